@@ -1,0 +1,199 @@
+"""CPU oracle for the KDA gated delta-rule step (decode, verify+fold, prefill).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, by the smoke check and by
+the benchmark's CPU-baseline leg, never by the GPU library or its binding.
+
+The arithmetic lives in ``kda_oracle.cpp`` (plain C++17 loops, built with g++,
+no HIP). This module builds it, loads it with ctypes and passes dense numpy
+arrays. Every array argument is a C-contiguous numpy array of the working
+precision (float32 = parity target, float64 = invariants and drift); bf16
+tensors are passed as their exact float values. Functions update the arrays
+they document as outputs in place.
+
+Readings that are "parity unpinned" (the oracle encodes them; no page fixes
+them): the gate formula, the L2-norm epsilon, the ring addressing through
+cache_base, the state orientation [V][K] and A_log being per head.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+def build(force: bool = True) -> str:
+    """Compile kda_oracle.cpp into liboracle.so with g++ (OpenMP, IEEE math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = ["g++", "-std=c++17", "-O2", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+               "-ffp-contract=off", _SRC, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = ctypes.CDLL(_LIB)
+    return _lib
+
+
+def _suffix(real) -> str:
+    real = np.dtype(real)
+    if real == np.float32:
+        return "f32"
+    if real == np.float64:
+        return "f64"
+    raise TypeError(f"oracle precision must be float32 or float64, got {real}")
+
+
+def _rp(a: np.ndarray, real):
+    assert a.dtype == np.dtype(real) and a.flags["C_CONTIGUOUS"], (a.dtype, real)
+    ctype = ctypes.c_float if np.dtype(real) == np.float32 else ctypes.c_double
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _ip(a: np.ndarray):
+    assert a.dtype == np.int32 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(_I32P)
+
+
+def _rs(x, real):
+    return (ctypes.c_float if np.dtype(real) == np.float32 else ctypes.c_double)(float(x))
+
+
+def threads() -> int:
+    return int(lib().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    lib().orc_set_threads(int(n))
+
+
+def bf16_round_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bits, round-to-nearest-even (uint16 array of x's shape)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().orc_bf16_round(ctypes.c_int64(x.size), x.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                         out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)))
+    return out
+
+
+def prologue(q, k, graw, beta_logit, a_log_h, dt_bias_h, lower_bound, real=np.float64):
+    """One head's per-token prologue -> (q_hat, k_hat, g, beta)."""
+    K = q.shape[0]
+    qh, kh, g = (np.zeros(K, real) for _ in range(3))
+    beta = np.zeros(1, real)
+    f = getattr(lib(), "orc_prologue_" + _suffix(real))
+    f(ctypes.c_int(K), _rp(q, real), _rp(k, real), _rp(graw, real), _rs(beta_logit, real),
+      _rs(a_log_h, real), _rp(dt_bias_h, real), _rs(lower_bound, real),
+      _rp(qh, real), _rp(kh, real), _rp(g, real), _rp(beta, real))
+    return qh, kh, g, float(beta[0])
+
+
+def step(S, qh, kh, v, g, beta, scale, real=np.float64):
+    """One step on S ([V][K], updated in place) -> (o, u)."""
+    V, K = S.shape
+    o = np.zeros(V, real)
+    u = np.zeros(V, real)
+    f = getattr(lib(), "orc_step_" + _suffix(real))
+    f(ctypes.c_int(K), ctypes.c_int(V), _rp(S, real), _rp(qh, real), _rp(kh, real), _rp(v, real),
+      _rp(g, real), _rs(beta, real), _rs(scale, real), _rp(o, real), _rp(u, real))
+    return o, u
+
+
+def replay(ckpt, kc, uc, gc, base, hist, real=np.float64):
+    """Ring replay for one (slot, head): ckpt [V][K], kc/gc [R][K], uc [R][V] -> S_cur."""
+    V, K = ckpt.shape
+    R = kc.shape[0]
+    S = np.zeros((V, K), real)
+    f = getattr(lib(), "orc_replay_" + _suffix(real))
+    f(ctypes.c_int(K), ctypes.c_int(V), _rp(ckpt, real), _rp(kc, real), _rp(uc, real),
+      _rp(gc, real), ctypes.c_int(R), ctypes.c_int(base), ctypes.c_int(hist), _rp(S, real))
+    return S
+
+
+def decode(q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,
+           bf16_storage=True, real=np.float32):
+    """T=1 decode. q/k/graw [B,H,K], v [B,H,V], beta_logit [B,H], pool [N,H,V,K]
+    (updated in place), idx int32 [B]. Returns out [B,H,V]."""
+    B, H, K = q.shape
+    V = v.shape[2]
+    N = pool.shape[0]
+    out = np.zeros((B, H, V), real)
+    f = getattr(lib(), "orc_decode_" + _suffix(real))
+    f(B, H, K, V, _rp(q, real), _rp(k, real), _rp(v, real), _rp(graw, real),
+      _rp(beta_logit, real), _rp(a_log, real), _rp(dt_bias, real), _rs(lower_bound, real),
+      _rs(scale, real), _rp(pool, real), ctypes.c_int64(N), _ip(idx), _rp(out, real),
+      ctypes.c_int(1 if bf16_storage else 0))
+    return out
+
+
+def verify(q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,
+           k_cache, u_cache, g_cache, hist_len, cache_base, flush_min, w_ring,
+           bf16_storage=True, real=np.float32):
+    """Verify+fold. q/k/graw [B,T,H,K], v [B,T,H,V], beta_logit [B,T,H]; pool [N,H,V,K],
+    k_cache/g_cache [N,H,R,K], u_cache [N,H,R,V] all updated in place. Returns out [B,T,H,V]."""
+    B, T, H, K = q.shape
+    V = v.shape[3]
+    N = pool.shape[0]
+    R = k_cache.shape[2]
+    out = np.zeros((B, T, H, V), real)
+    f = getattr(lib(), "orc_verify_" + _suffix(real))
+    f(B, T, H, K, V, _rp(q, real), _rp(k, real), _rp(v, real), _rp(graw, real),
+      _rp(beta_logit, real), _rp(a_log, real), _rp(dt_bias, real), _rs(lower_bound, real),
+      _rs(scale, real), _rp(pool, real), ctypes.c_int64(N), _ip(idx), _rp(k_cache, real),
+      _rp(u_cache, real), _rp(g_cache, real), ctypes.c_int(R), _ip(hist_len), _ip(cache_base),
+      ctypes.c_int(flush_min), ctypes.c_int(w_ring), _rp(out, real),
+      ctypes.c_int(1 if bf16_storage else 0))
+    return out
+
+
+def _prefill_args(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,
+                  use_initial_state, out, real):
+    n_docs = cu.shape[0] - 1
+    Ttot, H, K = q.shape
+    V = v.shape[2]
+    N = pool.shape[0]
+    return (n_docs, H, K, V, _ip(cu), _rp(q, real), _rp(k, real), _rp(v, real), _rp(graw, real),
+            _rp(beta_logit, real), _rp(a_log, real), _rp(dt_bias, real), _rs(lower_bound, real),
+            _rs(scale, real), _rp(pool, real), ctypes.c_int64(N), _ip(idx),
+            ctypes.c_int(1 if use_initial_state else 0), _rp(out, real))
+
+
+def prefill(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,
+            use_initial_state=True, bf16_storage=True, real=np.float32):
+    """Token-by-token varlen prefill. q/k/graw [Ttot,H,K], v [Ttot,H,V], beta_logit [Ttot,H],
+    cu int32 [n_docs+1], idx int32 [n_docs], pool [N,H,V,K] updated in place. -> out [Ttot,H,V]."""
+    out = np.zeros((q.shape[0], q.shape[1], v.shape[2]), real)
+    f = getattr(lib(), "orc_prefill_tbt_" + _suffix(real))
+    f(*_prefill_args(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool,
+                     idx, use_initial_state, out, real), ctypes.c_int(1 if bf16_storage else 0))
+    return out
+
+
+def prefill_chunked(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,
+                    chunk, use_initial_state=True, real=np.float64):
+    """Chunkwise (WY/UT) model of the same prefill, no storage rounding. -> out [Ttot,H,V]."""
+    out = np.zeros((q.shape[0], q.shape[1], v.shape[2]), real)
+    f = getattr(lib(), "orc_prefill_chunked_" + _suffix(real))
+    f(*_prefill_args(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool,
+                     idx, use_initial_state, out, real), ctypes.c_int(int(chunk)))
+    return out
+
+
+if __name__ == "__main__":  # pragma: no cover
+    print(build(force=True), file=sys.stderr)

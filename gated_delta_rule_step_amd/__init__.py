@@ -1,0 +1,223 @@
+"""Python binding of the KDA step library (libkda.so, HIP for gfx950).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, checks dtype/device/contiguity of the innermost dimension,
+and passes raw pointers, element strides and the current HIP stream to the C
+ABI declared in include/kda.h. All arithmetic runs in the library's kernels;
+there is no fallback. If libkda.so is missing the first call raises.
+
+bf16 tensors are torch.bfloat16; A_log and dt_bias are float32; indices and
+ring metadata are int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkda.so")
+HEAD_DIM = 128
+
+_lib = None
+
+_c = ctypes
+_P = _c.c_void_p
+_I32 = _c.c_int32
+_I64 = _c.c_int64
+_F = _c.c_float
+
+_SIGS = {
+    "kda_status_string": (_c.c_char_p, [_c.c_int]),
+    "kda_decode": (_c.c_int, [_I32, _I32, _I32, _I32,
+                              _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
+                              _P, _P, _F, _F, _P, _I64, _I64, _P, _P, _I64, _P]),
+    "kda_verify_ucache_flush": (_c.c_int, [_I32, _I32, _I32, _I32, _I32,
+                                           _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
+                                           _P, _I64, _I64, _P, _I64, _I64,
+                                           _P, _P, _F, _F, _P, _I64, _I64, _P,
+                                           _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32,
+                                           _P, _I64, _I64, _P]),
+    "kda_prefill_workspace_size": (_c.c_size_t, [_I32, _I64, _I32, _I32, _I32]),
+    "kda_prefill_varlen": (_c.c_int, [_I32, _I64, _I32, _I32, _I32, _P, _P,
+                                      _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
+                                      _P, _P, _F, _F, _P, _I64, _I64, _P, _I32,
+                                      _P, _I64, _P, _c.c_size_t, _P]),
+}
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {kda_status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkda.so (built in-tree by __graft_entry__.build()); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def kda_status_string(status: int) -> str:
+    return lib().kda_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise KdaError(fn, status)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _P(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return _P(t.data_ptr()) if t is not None else _P(0)
+
+
+def _bf16(name, t, last_contig=True):
+    import torch
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if last_contig and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the innermost dimension must be contiguous")
+
+
+def _f32(name, t):
+    import torch
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+
+
+def _i32(name, t):
+    import torch
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+
+
+def _pool_geometry(state_pool, H):
+    """Pool: bf16 tensor whose dim 0 indexes slots; each slot's first
+    H*128*128 elements are contiguous. Returns (num_slots, slot_stride)."""
+    _bf16("state_pool", state_pool)
+    n = state_pool.shape[0]
+    inner = state_pool[0] if n > 0 else None
+    if n > 0 and not inner.is_contiguous():
+        raise ValueError("state_pool: each slot must be contiguous")
+    if n > 0 and inner.numel() < H * HEAD_DIM * HEAD_DIM:
+        raise ValueError("state_pool: slot smaller than H*128*128")
+    return n, (state_pool.stride(0) if n > 0 else H * HEAD_DIM * HEAD_DIM)
+
+
+def kda_decode(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_indices, out,
+               lower_bound: float = -5.0, scale: float = 1.0, stream=None) -> None:
+    """T=1 decode. q, k, v, g_raw, out: bf16 [B, H*128] (row-strided views
+    allowed); beta_raw bf16 [B, H]; A_log fp32 [H]; dt_bias fp32 [H*128];
+    state_pool bf16 [N, ...] (slot-major); state_indices int32 [B]."""
+    B, W = q.shape
+    H = W // HEAD_DIM
+    for n, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta_raw", beta_raw),
+                 ("out", out)):
+        _bf16(n, t)
+    _f32("A_log", A_log)
+    _f32("dt_bias", dt_bias)
+    _i32("state_indices", state_indices)
+    N, slot_stride = _pool_geometry(state_pool, H)
+    st = lib().kda_decode(B, H, HEAD_DIM, HEAD_DIM,
+                          _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
+                          _ptr(g_raw), g_raw.stride(0), _ptr(beta_raw), beta_raw.stride(0),
+                          _ptr(A_log), _ptr(dt_bias), float(lower_bound), float(scale),
+                          _ptr(state_pool) if N else _P(0), N, slot_stride,
+                          _ptr(state_indices), _ptr(out), out.stride(0), _stream(stream))
+    _check("kda_decode", st)
+
+
+def kda_verify_ucache_flush(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool,
+                            state_indices, k_cache, u_cache, g_cache, hist_len, cache_base,
+                            out, flush_min: int, w_ring: int = 16,
+                            restart_hist_on_flush: bool = True, lower_bound: float = -5.0,
+                            scale: float = 1.0, stream=None) -> None:
+    """Verify+fold. q, k, v, g_raw, out: bf16 [B, T, H*128]; beta_raw bf16
+    [B, T, H]; k_cache/u_cache bf16 [N, H, R, 128]; g_cache fp32 [N, H, R, 128];
+    hist_len, cache_base int32 [B]."""
+    B, T, W = q.shape
+    H = W // HEAD_DIM
+    for n, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta_raw", beta_raw),
+                 ("out", out), ("k_cache", k_cache), ("u_cache", u_cache)):
+        _bf16(n, t)
+    for n, t in (("A_log", A_log), ("dt_bias", dt_bias), ("g_cache", g_cache)):
+        _f32(n, t)
+    for n, t in (("state_indices", state_indices), ("hist_len", hist_len),
+                 ("cache_base", cache_base)):
+        _i32(n, t)
+    if not (k_cache.is_contiguous() and u_cache.is_contiguous()):
+        raise ValueError("ring caches must be contiguous")
+    N, slot_stride = _pool_geometry(state_pool, H)
+    if N and (k_cache.shape[:2] != (N, H) or u_cache.shape[:2] != (N, H) or
+              g_cache.shape[:2] != (N, H)):
+        raise ValueError("ring caches must be [N, H, R, 128]")
+    R = k_cache.shape[2]
+    st = lib().kda_verify_ucache_flush(
+        B, T, H, HEAD_DIM, HEAD_DIM,
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1),
+        _ptr(v), v.stride(0), v.stride(1), _ptr(g_raw), g_raw.stride(0), g_raw.stride(1),
+        _ptr(beta_raw), beta_raw.stride(0), beta_raw.stride(1),
+        _ptr(A_log), _ptr(dt_bias), float(lower_bound), float(scale),
+        _ptr(state_pool) if N else _P(0), N, slot_stride, _ptr(state_indices),
+        _ptr(k_cache), _ptr(u_cache), _ptr(g_cache), R, _ptr(hist_len), _ptr(cache_base),
+        int(flush_min), int(w_ring), 1 if restart_hist_on_flush else 0,
+        _ptr(out), out.stride(0), out.stride(1), _stream(stream))
+    _check("kda_verify_ucache_flush", st)
+
+
+def kda_prefill_workspace_size(n_docs: int, total_tokens: int, H: int) -> int:
+    return int(lib().kda_prefill_workspace_size(n_docs, total_tokens, H, HEAD_DIM, HEAD_DIM))
+
+
+def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_log, dt_bias,
+                       state_pool, state_indices, out, workspace=None,
+                       use_initial_state: bool = True, lower_bound: float = -5.0,
+                       scale: float = 1.0, stream=None) -> None:
+    """Varlen prefill. cu_seqlens_host: CPU int32 [n_docs+1]; cu_seqlens: the
+    same on the GPU; q, k, v, g_raw, out: bf16 [Ttot, H*128] (token-strided);
+    beta_raw bf16 [Ttot, H]; state_indices int32 [n_docs]; workspace: uint8
+    GPU tensor of >= kda_prefill_workspace_size(...) bytes (or None)."""
+    import torch
+    if cu_seqlens_host.dtype != torch.int32 or cu_seqlens_host.is_cuda or \
+            not cu_seqlens_host.is_contiguous():
+        raise ValueError("cu_seqlens_host must be a contiguous int32 CPU tensor")
+    _i32("cu_seqlens", cu_seqlens)
+    _i32("state_indices", state_indices)
+    n_docs = cu_seqlens_host.shape[0] - 1
+    Ttot, W = q.shape
+    H = W // HEAD_DIM
+    for n, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta_raw", beta_raw),
+                 ("out", out)):
+        _bf16(n, t)
+    _f32("A_log", A_log)
+    _f32("dt_bias", dt_bias)
+    N, slot_stride = _pool_geometry(state_pool, H)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    cu_h = _P(cu_seqlens_host.data_ptr())
+    st = lib().kda_prefill_varlen(
+        n_docs, Ttot, H, HEAD_DIM, HEAD_DIM, cu_h, _ptr(cu_seqlens),
+        _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
+        _ptr(g_raw), g_raw.stride(0), _ptr(beta_raw), beta_raw.stride(0),
+        _ptr(A_log), _ptr(dt_bias), float(lower_bound), float(scale),
+        _ptr(state_pool) if N else _P(0), N, slot_stride, _ptr(state_indices),
+        1 if use_initial_state else 0, _ptr(out), out.stride(0),
+        _ptr(workspace), ws_bytes, _stream(stream))
+    _check("kda_prefill_varlen", st)

@@ -1,0 +1,250 @@
+// C ABI of the KDA step library: host-side validation, variant choice and
+// kernel launch. Nothing here allocates, synchronises or keeps state.
+
+#include <stdint.h>
+
+#include "../../include/kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+constexpr int64_t D = 128;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool mult8(int64_t s) { return (s & 7) == 0; }
+
+// An output tensor indexed by (row, token) must not write one element twice:
+// either row-major over tokens or token-major over rows.
+bool out_layout_ok(int64_t rows, int64_t toks, int64_t row_stride, int64_t tok_stride,
+                   int64_t width) {
+  if (row_stride < 0 || tok_stride < 0) return false;
+  const bool r_ok = rows <= 1 || row_stride >= width;
+  const bool t_ok = toks <= 1 || tok_stride >= width;
+  if (rows <= 1 || toks <= 1) return r_ok && t_ok;
+  const bool row_major = tok_stride >= width && row_stride >= toks * tok_stride;
+  const bool tok_major = row_stride >= width && tok_stride >= rows * row_stride;
+  return row_major || tok_major;
+}
+
+kda_status launch_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case KDA_ERR_BAD_SHAPE: return "invalid shape argument";
+    case KDA_ERR_BAD_STRIDE: return "invalid stride argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KDA_ERR_BAD_SEQLENS: return "cu_seqlens must start at 0, never decrease and end at total_tokens";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than kda_prefill_workspace_size()";
+    case KDA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+  }
+  return "unknown status";
+}
+
+extern "C" kda_status kda_decode(int32_t B, int32_t H, int32_t K, int32_t V, const void* q,
+                                 int64_t q_row_stride, const void* k, int64_t k_row_stride,
+                                 const void* v, int64_t v_row_stride, const void* g_raw,
+                                 int64_t g_row_stride, const void* beta_raw,
+                                 int64_t beta_row_stride, const float* A_log,
+                                 const float* dt_bias, float lower_bound, float scale,
+                                 void* state_pool, int64_t num_slots, int64_t slot_stride,
+                                 const int32_t* state_indices, void* out,
+                                 int64_t out_row_stride, hipStream_t stream) {
+  if (B < 0 || H < 1 || num_slots < 0) return KDA_ERR_BAD_SHAPE;
+  if (K != D || V != D) return KDA_ERR_UNSUPPORTED;
+  if (B == 0) return KDA_OK;
+  if (!q || !k || !v || !g_raw || !beta_raw || !A_log || !dt_bias || !state_indices || !out)
+    return KDA_ERR_NULL_POINTER;
+  if (num_slots > 0 && !state_pool) return KDA_ERR_NULL_POINTER;
+  const int64_t W = int64_t(H) * D;
+  if (q_row_stride < 0 || k_row_stride < 0 || v_row_stride < 0 || g_row_stride < 0 ||
+      beta_row_stride < 0 || out_row_stride < 0 || slot_stride < 0)
+    return KDA_ERR_BAD_STRIDE;
+  if (B > 1 && out_row_stride < W) return KDA_ERR_BAD_STRIDE;
+  if (num_slots > 1 && slot_stride < W * D) return KDA_ERR_BAD_STRIDE;
+
+  kda::DecodeParams p;
+  p.B = B;
+  p.H = H;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.g = static_cast<const uint16_t*>(g_raw);
+  p.beta = static_cast<const uint16_t*>(beta_raw);
+  p.q_row_stride = q_row_stride;
+  p.k_row_stride = k_row_stride;
+  p.v_row_stride = v_row_stride;
+  p.g_row_stride = g_row_stride;
+  p.beta_row_stride = beta_row_stride;
+  p.A_log = A_log;
+  p.dt_bias = dt_bias;
+  p.lower_bound = lower_bound;
+  p.scale = scale;
+  p.state_pool = static_cast<uint16_t*>(state_pool);
+  p.num_slots = num_slots;
+  p.slot_stride = slot_stride;
+  p.state_indices = state_indices;
+  p.out = static_cast<uint16_t*>(out);
+  p.out_row_stride = out_row_stride;
+  const bool vec = aligned16(q) && aligned16(k) && aligned16(g_raw) && aligned16(dt_bias) &&
+                   (num_slots == 0 || aligned16(state_pool)) && mult8(q_row_stride) &&
+                   mult8(k_row_stride) && mult8(g_row_stride) && mult8(slot_stride);
+  return launch_status(kda::launch_decode(p, vec, stream));
+}
+
+extern "C" kda_status kda_verify_ucache_flush(
+    int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, const void* q, int64_t q_row_stride,
+    int64_t q_tok_stride, const void* k, int64_t k_row_stride, int64_t k_tok_stride,
+    const void* v, int64_t v_row_stride, int64_t v_tok_stride, const void* g_raw,
+    int64_t g_row_stride, int64_t g_tok_stride, const void* beta_raw, int64_t beta_row_stride,
+    int64_t beta_tok_stride, const float* A_log, const float* dt_bias, float lower_bound,
+    float scale, void* state_pool, int64_t num_slots, int64_t slot_stride,
+    const int32_t* state_indices, void* k_cache, void* u_cache, float* g_cache,
+    int32_t ring_rows, const int32_t* hist_len, const int32_t* cache_base, int32_t flush_min,
+    int32_t w_ring, int32_t restart_hist_on_flush, void* out, int64_t out_row_stride,
+    int64_t out_tok_stride, hipStream_t stream) {
+  if (B < 0 || H < 1 || num_slots < 0 || ring_rows < 1) return KDA_ERR_BAD_SHAPE;
+  if (K != D || V != D || T < 1 || T > 8) return KDA_ERR_UNSUPPORTED;
+  if (w_ring != 16 && w_ring != 32) return KDA_ERR_UNSUPPORTED;
+  if (ring_rows < w_ring || restart_hist_on_flush != 1 || flush_min < 1) return KDA_ERR_UNSUPPORTED;
+  if (flush_min - 1 + T > w_ring) return KDA_ERR_UNSUPPORTED;  // ring capacity
+  if (w_ring == 32 && flush_min <= 16) return KDA_ERR_UNSUPPORTED;
+  if (B == 0) return KDA_OK;
+  if (!q || !k || !v || !g_raw || !beta_raw || !A_log || !dt_bias || !state_indices || !out ||
+      !hist_len || !cache_base)
+    return KDA_ERR_NULL_POINTER;
+  if (num_slots > 0 && (!state_pool || !k_cache || !u_cache || !g_cache))
+    return KDA_ERR_NULL_POINTER;
+  const int64_t W = int64_t(H) * D;
+  const int64_t in_strides[] = {q_row_stride, q_tok_stride, k_row_stride, k_tok_stride,
+                                v_row_stride, v_tok_stride, g_row_stride, g_tok_stride,
+                                beta_row_stride, beta_tok_stride, slot_stride};
+  for (int64_t s : in_strides)
+    if (s < 0) return KDA_ERR_BAD_STRIDE;
+  if (!out_layout_ok(B, T, out_row_stride, out_tok_stride, W)) return KDA_ERR_BAD_STRIDE;
+  if (num_slots > 1 && slot_stride < W * D) return KDA_ERR_BAD_STRIDE;
+
+  kda::VerifyParams p;
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.g = static_cast<const uint16_t*>(g_raw);
+  p.beta = static_cast<const uint16_t*>(beta_raw);
+  p.q_row_stride = q_row_stride;
+  p.q_tok_stride = q_tok_stride;
+  p.k_row_stride = k_row_stride;
+  p.k_tok_stride = k_tok_stride;
+  p.v_row_stride = v_row_stride;
+  p.v_tok_stride = v_tok_stride;
+  p.g_row_stride = g_row_stride;
+  p.g_tok_stride = g_tok_stride;
+  p.beta_row_stride = beta_row_stride;
+  p.beta_tok_stride = beta_tok_stride;
+  p.A_log = A_log;
+  p.dt_bias = dt_bias;
+  p.lower_bound = lower_bound;
+  p.scale = scale;
+  p.state_pool = static_cast<uint16_t*>(state_pool);
+  p.num_slots = num_slots;
+  p.slot_stride = slot_stride;
+  p.state_indices = state_indices;
+  p.k_cache = static_cast<uint16_t*>(k_cache);
+  p.u_cache = static_cast<uint16_t*>(u_cache);
+  p.g_cache = g_cache;
+  p.ring_rows = ring_rows;
+  p.hist_len = hist_len;
+  p.cache_base = cache_base;
+  p.flush_min = flush_min;
+  p.w_ring = w_ring;
+  p.out = static_cast<uint16_t*>(out);
+  p.out_row_stride = out_row_stride;
+  p.out_tok_stride = out_tok_stride;
+  const bool vec = aligned16(q) && aligned16(k) && aligned16(v) && aligned16(g_raw) &&
+                   aligned16(dt_bias) && aligned16(out) &&
+                   (num_slots == 0 || (aligned16(state_pool) && aligned16(k_cache) &&
+                                       aligned16(u_cache) && aligned16(g_cache))) &&
+                   mult8(q_row_stride) && mult8(q_tok_stride) && mult8(k_row_stride) &&
+                   mult8(k_tok_stride) && mult8(v_row_stride) && mult8(v_tok_stride) &&
+                   mult8(g_row_stride) && mult8(g_tok_stride) && mult8(out_row_stride) &&
+                   mult8(out_tok_stride) && mult8(slot_stride);
+  return launch_status(kda::launch_verify(p, vec, stream));
+}
+
+extern "C" size_t kda_prefill_workspace_size(int32_t n_docs, int64_t total_tokens, int32_t H,
+                                             int32_t K, int32_t V) {
+  if (n_docs < 0 || total_tokens < 0 || H < 1 || K != D || V != D) return 0;
+  return kda::prefill_workspace_bytes(n_docs, total_tokens, H);
+}
+
+extern "C" kda_status kda_prefill_varlen(
+    int32_t n_docs, int64_t total_tokens, int32_t H, int32_t K, int32_t V,
+    const int32_t* cu_seqlens_host, const int32_t* cu_seqlens, const void* q,
+    int64_t q_tok_stride, const void* k, int64_t k_tok_stride, const void* v,
+    int64_t v_tok_stride, const void* g_raw, int64_t g_tok_stride, const void* beta_raw,
+    int64_t beta_tok_stride, const float* A_log, const float* dt_bias, float lower_bound,
+    float scale, void* state_pool, int64_t num_slots, int64_t slot_stride,
+    const int32_t* state_indices, int32_t use_initial_state, void* out, int64_t out_tok_stride,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (n_docs < 0 || total_tokens < 0 || H < 1 || num_slots < 0) return KDA_ERR_BAD_SHAPE;
+  if (K != D || V != D) return KDA_ERR_UNSUPPORTED;
+  if (!cu_seqlens_host) return KDA_ERR_NULL_POINTER;
+  if (cu_seqlens_host[0] != 0) return KDA_ERR_BAD_SEQLENS;
+  for (int32_t d = 0; d < n_docs; ++d)
+    if (cu_seqlens_host[d + 1] < cu_seqlens_host[d]) return KDA_ERR_BAD_SEQLENS;
+  if (int64_t(cu_seqlens_host[n_docs]) != total_tokens) return KDA_ERR_BAD_SEQLENS;
+  if (n_docs == 0) return KDA_OK;
+  if (!cu_seqlens || !state_indices || !A_log || !dt_bias) return KDA_ERR_NULL_POINTER;
+  if (total_tokens > 0 && (!q || !k || !v || !g_raw || !beta_raw || !out))
+    return KDA_ERR_NULL_POINTER;
+  if (num_slots > 0 && !state_pool) return KDA_ERR_NULL_POINTER;
+  const int64_t W = int64_t(H) * D;
+  if (q_tok_stride < 0 || k_tok_stride < 0 || v_tok_stride < 0 || g_tok_stride < 0 ||
+      beta_tok_stride < 0 || out_tok_stride < 0 || slot_stride < 0)
+    return KDA_ERR_BAD_STRIDE;
+  if (total_tokens > 1 && out_tok_stride < W) return KDA_ERR_BAD_STRIDE;
+  if (num_slots > 1 && slot_stride < W * D) return KDA_ERR_BAD_STRIDE;
+  const size_t need = kda::prefill_workspace_bytes(n_docs, total_tokens, H);
+  if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+    return workspace ? KDA_ERR_UNSUPPORTED : KDA_ERR_NULL_POINTER;
+
+  kda::PrefillParams p;
+  p.n_docs = n_docs;
+  p.H = H;
+  p.total_tokens = total_tokens;
+  p.cu_seqlens = cu_seqlens;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.g = static_cast<const uint16_t*>(g_raw);
+  p.beta = static_cast<const uint16_t*>(beta_raw);
+  p.q_tok_stride = q_tok_stride;
+  p.k_tok_stride = k_tok_stride;
+  p.v_tok_stride = v_tok_stride;
+  p.g_tok_stride = g_tok_stride;
+  p.beta_tok_stride = beta_tok_stride;
+  p.A_log = A_log;
+  p.dt_bias = dt_bias;
+  p.lower_bound = lower_bound;
+  p.scale = scale;
+  p.state_pool = static_cast<uint16_t*>(state_pool);
+  p.num_slots = num_slots;
+  p.slot_stride = slot_stride;
+  p.state_indices = state_indices;
+  p.use_initial_state = use_initial_state ? 1 : 0;
+  p.out = static_cast<uint16_t*>(out);
+  p.out_tok_stride = out_tok_stride;
+  p.workspace = workspace;
+  const bool vec = aligned16(q) && aligned16(k) && aligned16(v) && aligned16(g_raw) &&
+                   aligned16(dt_bias) && aligned16(out) &&
+                   (num_slots == 0 || aligned16(state_pool)) && mult8(q_tok_stride) &&
+                   mult8(k_tok_stride) && mult8(v_tok_stride) && mult8(g_tok_stride) &&
+                   mult8(out_tok_stride) && mult8(slot_stride);
+  return launch_status(kda::launch_prefill(p, cu_seqlens_host, vec, stream));
+}

@@ -1,0 +1,151 @@
+// T = 1 KDA decode against an in-place bf16 state pool (gfx950).
+//
+// Operation: "feat(kda): add packed-input CuTe decode kernel" (opening
+// description and "T=1 fast path inside recurrent_kda"): per (row, head),
+// decay the state per key channel, form u = beta (v - S' k_hat), write
+// S = S' + k_hat u^T back in place and read out o = scale S q_hat. Rows whose
+// slot index is outside [0, N) write zero output and touch nothing else.
+//
+// The kernel is HBM-bound (32 KiB read + 32 KiB written per head for ~115
+// kflop), so the design is about streaming the state:
+//  * one wave owns a tile of ROWS = 4 * LOADS value rows of one (row, head);
+//    a 256-thread workgroup holds 4 waves, so the (row, head) inputs are
+//    fetched into one L2;
+//  * lane l covers key channels 8*(l%16) .. +7 of value rows
+//    vbase + 4*i + l/16 (i < LOADS): every state access is a 128-bit load or
+//    store and one load instruction covers four full 256-byte rows;
+//  * all LOADS state loads are issued before any prologue math;
+//  * the two dot products S'k_hat and S'q_hat of a row are reduced over the
+//    16 lanes of a DPP row (no LDS, no barrier); the decay is folded into the
+//    reduction operands (S' x = S (alpha * x)), so the state is touched by
+//    exactly two FMAs for the reductions and one multiply + one FMA for the
+//    update, and the read-out uses o = scale (S' q_hat + u (k_hat . q_hat));
+//  * fp32 math, bf16 storage: unpack by shift/mask, repack with the hardware
+//    round-to-nearest-even conversion; state traffic uses non-temporal hints.
+
+#include "kda_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <int LOADS, bool VEC>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+  constexpr int ROWS = 4 * LOADS;
+  constexpr int VBLOCKS = D / ROWS;
+  const int lane = threadIdx.x & 63;
+  const int64_t tile = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int vb = int(tile % VBLOCKS);
+  const int64_t bh = tile / VBLOCKS;
+  if (bh >= int64_t(p.B) * p.H) return;
+  const int h = int(bh % p.H);
+  const int64_t b = bh / p.H;
+  const int kb = lane & 15;  // key channels 8*kb .. 8*kb+7
+  const int rg = lane >> 4;  // row group: rows vbase + 4*i + rg
+  const int vbase = vb * ROWS;
+
+  uint16_t* outp = p.out + b * p.out_row_stride + int64_t(h) * D + vbase;
+  const int32_t slot = p.state_indices[b];
+  if (!(slot >= 0 && int64_t(slot) < p.num_slots)) {
+    if (lane < ROWS) outp[lane] = 0;
+    return;
+  }
+
+  // Issue every state load first.
+  uint16_t* sp = p.state_pool + int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS +
+                 int64_t(vbase + rg) * D + kb * 8;
+  u32x4 s[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) s[i] = load8_raw<VEC>(sp + i * 4 * D);
+
+  // Per-token prologue for this lane's 8 key channels.
+  float q[8], k[8], gr[8], dtb[8];
+  load8_bf16<VEC>(p.q + b * p.q_row_stride + h * D + kb * 8, q);
+  load8_bf16<VEC>(p.k + b * p.k_row_stride + h * D + kb * 8, k);
+  load8_bf16<VEC>(p.g + b * p.g_row_stride + h * D + kb * 8, gr);
+  load8_f32<VEC>(p.dt_bias + h * D + kb * 8, dtb);
+  const float neg_ea = -expf(p.A_log[h]);
+  const float beta = sigmoidf(bf1(p.beta[b * p.beta_row_stride + h]));
+  float vrow[LOADS];
+  const uint16_t* vp = p.v + b * p.v_row_stride + h * D + vbase + rg;
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) vrow[i] = bf1(vp[4 * i]);
+
+  float sq = 0.f, sk = 0.f, sqk = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    sq = fmaf(q[c], q[c], sq);
+    sk = fmaf(k[c], k[c], sk);
+    sqk = fmaf(q[c], k[c], sqk);
+  }
+  sq = row16_sum(sq);
+  sk = row16_sum(sk);
+  sqk = row16_sum(sqk);
+  const float rq = 1.0f / sqrtf(sq + 1e-6f);
+  const float rk = 1.0f / sqrtf(sk + 1e-6f);
+  const float kq = sqk * rq * rk;  // k_hat . q_hat
+  float al[8], kh[8], ka[8], qa[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    al[c] = expf(gate_logdecay(gr[c] + dtb[c], neg_ea, p.lower_bound));
+    kh[c] = k[c] * rk;
+    ka[c] = al[c] * kh[c];
+    qa[c] = al[c] * (q[c] * rq);
+  }
+
+  float osel = 0.f;
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf_lo(s[i][j]);
+      x[2 * j + 1] = bf_hi(s[i][j]);
+    }
+    float dk = 0.f, dq = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      dk = fmaf(x[c], ka[c], dk);
+      dq = fmaf(x[c], qa[c], dq);
+    }
+    dk = row16_sum(dk);
+    dq = row16_sum(dq);
+    const float u = beta * (vrow[i] - dk);
+    const float o = p.scale * fmaf(u, kq, dq);
+    if (kb == i) osel = o;
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a0 = fmaf(al[2 * j], x[2 * j], kh[2 * j] * u);
+      const float a1 = fmaf(al[2 * j + 1], x[2 * j + 1], kh[2 * j + 1] * u);
+      w[j] = pack_bf16x2(a0, a1);
+    }
+    s[i] = w;
+  }
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) store8_raw<VEC>(sp + i * 4 * D, s[i]);
+  if (kb < LOADS) outp[4 * kb + rg] = to_bf16(osel);
+}
+
+// Launch shape: 256-thread workgroups of four independent waves. Large
+// batches use 32-row tiles (8 loads per lane, four waves = one head); small
+// batches use 8-row tiles so that a few heads still spread over many CUs.
+hipError_t launch_decode(const DecodeParams& p, bool vec, hipStream_t stream) {
+  const int64_t heads = int64_t(p.B) * p.H;
+  const bool small = heads < 1024;
+  const int loads = small ? 2 : 8;
+  const int64_t tiles = heads * (D / (4 * loads));
+  const int64_t blocks = (tiles + 3) / 4;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  if (small) {
+    if (vec) hipLaunchKernelGGL((decode_kernel<2, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<2, false>), grid, block, 0, stream, p);
+  } else {
+    if (vec) hipLaunchKernelGGL((decode_kernel<8, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<8, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kda

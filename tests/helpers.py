@@ -1,0 +1,106 @@
+"""Shared helpers for the GPU parity tests: device transfer of bf16 bit arrays,
+the parity criteria, and oracle runs over the touched pool slots only."""
+from __future__ import annotations
+
+import numpy as np
+
+from gated_delta_rule_step_amd import synth
+
+f32 = synth.f32_from_bits
+HD = 128
+
+# Parity criteria for floating-point results:
+#  * outputs: |got - ref| <= 1e-2 + 1.6e-2 |ref| element-wise;
+#  * stored bf16 state / ring rows: |got - ref| <= 2 bf16 ulps of
+#    max(|ref|, 2^-12) (the floor covers elements that cancel to ~0);
+#  * cumulative log-decay (fp32): |got - ref| <= 1e-5 + 1e-5 |ref|.
+OUT_ATOL, OUT_RTOL = 1e-2, 1.6e-2
+STATE_ULPS, STATE_FLOOR = 2, 2.0 ** -12
+
+
+def dev_bf16(a, device="cuda"):
+    import torch
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def dev(a, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def bits(t) -> np.ndarray:
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_ulp(x):
+    return np.exp2(np.floor(np.log2(np.maximum(np.abs(x), STATE_FLOOR))) - 7)
+
+
+def check_out(got_bits, ref, what="output"):
+    got = f32(got_bits).astype(np.float64).reshape(ref.shape)
+    ref = ref.astype(np.float64)
+    excess = np.abs(got - ref) - (OUT_ATOL + OUT_RTOL * np.abs(ref))
+    bad = ~(excess <= 0)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, excess, -np.inf)), ref.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements out of tolerance; "
+                             f"worst at {i}: got {got[i]!r} ref {ref[i]!r}")
+
+
+def check_state(got_bits, ref, what="state"):
+    got = f32(got_bits).astype(np.float64).reshape(ref.shape)
+    ref = ref.astype(np.float64)
+    tol = STATE_ULPS * bf16_ulp(ref)
+    bad = ~(np.abs(got - ref) <= tol)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, np.abs(got - ref) / tol, -np.inf)),
+                             ref.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements beyond "
+                             f"{STATE_ULPS} bf16 ulps; worst at {i}: got {got[i]!r} "
+                             f"ref {ref[i]!r}")
+
+
+def check_gcache(got, ref, what="g_cache"):
+    got = got.astype(np.float64)
+    ref = ref.astype(np.float64)
+    bad = ~(np.abs(got - ref) <= 1e-5 + 1e-5 * np.abs(ref))
+    if bad.any():
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements out of tolerance")
+
+
+def compact_slots(idx, N):
+    """Map the active rows' slots onto a compact pool: returns (slots, cidx)
+    where slots lists the distinct active slots and cidx indexes them (-1 for
+    inactive rows)."""
+    idx = np.asarray(idx, np.int64)
+    active = (idx >= 0) & (idx < N)
+    slots = idx[active]
+    cidx = np.full(idx.shape, -1, np.int32)
+    cidx[active] = np.arange(slots.size, dtype=np.int32)
+    return slots, cidx
+
+
+def split_qkv(qkv_bits, H):
+    """Packed [..., 3*H*128] rows -> float32 q, k, v of shape [..., H, 128]."""
+    W = H * HD
+    q = f32(qkv_bits[..., :W]).reshape(*qkv_bits.shape[:-1], H, HD)
+    k = f32(qkv_bits[..., W:2 * W]).reshape(*qkv_bits.shape[:-1], H, HD)
+    v = f32(qkv_bits[..., 2 * W:]).reshape(*qkv_bits.shape[:-1], H, HD)
+    return np.ascontiguousarray(q), np.ascontiguousarray(k), np.ascontiguousarray(v)
+
+
+def oracle_decode(orc, case, pool_bits=None):
+    """Run the fp32 oracle on a decode case over its touched slots.
+    Returns (out [B,H,128] f32, slots, new_state[len(slots),H,128,128] f32)."""
+    H, N = case["H"], case["N"]
+    pool_bits = case["pool"] if pool_bits is None else pool_bits
+    slots, cidx = compact_slots(case["idx"], N)
+    cpool = np.ascontiguousarray(f32(pool_bits[slots]))
+    q, k, v = split_qkv(case["qkv"], H)
+    out = orc.decode(q, k, v, np.ascontiguousarray(f32(case["gate"]).reshape(-1, H, HD)),
+                     np.ascontiguousarray(f32(case["beta"])), case["a_log"], case["dt_bias"],
+                     case["lower_bound"], case["scale"], cpool, cidx, bf16_storage=True,
+                     real=np.float32)
+    return out, slots, cpool

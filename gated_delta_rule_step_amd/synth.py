@@ -8,7 +8,8 @@ CPU oracle consume the same arrays.
 Distributions (all workloads): q, k, v, raw gate and beta logits ~ N(0, 1) in
 bf16; A_log ~ U(-1, 1) fp32 per head; dt_bias ~ N(0, 0.1) fp32 per key
 channel; pool state ~ N(0, 0.05) in bf16. Seeds follow
-seed = 20261202 + 1000 * workload + 10 * B + T.
+seed = 20261202 + 1000 * workload + 10 * B + T; pools of more than 64 slots
+come from one seeded pool per (N, H), cached within a process.
 
 Layouts (all C-contiguous; bf16 tensors are uint16 arrays of bf16 bits):
   decode  qkv [B, 3*H*128] = [q | k | v] per row, gate [B, H*128], beta [B, H]
@@ -17,6 +18,8 @@ Layouts (all C-contiguous; bf16 tensors are uint16 arrays of bf16 bits):
   pool [N, H, 128 (V), 128 (K)]; rings k/g [N, H, R, 128], u [N, H, R, 128].
 """
 from __future__ import annotations
+
+import functools
 
 import numpy as np
 import torch
@@ -64,6 +67,27 @@ def pool_bits(rng, N: int, H: int, std: float = 0.05, chunk_slots: int = 64) -> 
     return out
 
 
+@functools.lru_cache(maxsize=2)
+def _pool_cached(N: int, H: int, seed: int) -> np.ndarray:
+    p = pool_bits(np.random.Generator(np.random.PCG64(seed)), N, H)
+    p.setflags(write=False)
+    return p
+
+
+def shared_pool(N: int, H: int) -> np.ndarray:
+    """A seeded N(0, 0.05) bf16 pool of N slots (a fresh writable copy of a
+    per-process cached array; the pool's seed depends on N and H only)."""
+    return _pool_cached(N, H, BASE_SEED + 7 * N + H).copy()
+
+
+def filler_bits(shape, salt: int = 0) -> np.ndarray:
+    """Cheap deterministic bf16 bit patterns for memory that must stay
+    untouched (any values, including NaN and inf encodings)."""
+    n = int(np.prod(shape))
+    x = (np.arange(n, dtype=np.uint64) * np.uint64(2654435761) + np.uint64(salt)) >> np.uint64(13)
+    return (x & np.uint64(0xFFFF)).astype(np.uint16).reshape(shape)
+
+
 def state_indices(rng, B: int, N: int, inactive_frac: float = 0.05) -> np.ndarray:
     """First B entries of a seeded permutation of 0..N-1 (B <= N); then
     round(inactive_frac * B) seeded positions set alternately to -1 and N + r."""
@@ -88,7 +112,7 @@ def decode_case(B: int, N: int = 1024, H: int = 12, seed: int | None = None,
     case["gate"] = _normal_bf16(rng, (B, W))
     case["beta"] = _normal_bf16(rng, (B, H))
     case["a_log"], case["dt_bias"] = gate_params(rng, H)
-    case["pool"] = pool_bits(rng, N, H)
+    case["pool"] = pool_bits(rng, N, H) if N <= 64 else shared_pool(N, H)
     case["idx"] = state_indices(rng, B, N, inactive_frac) if idx is None else np.asarray(idx, np.int32)
     return case
 
@@ -111,7 +135,7 @@ def verify_case(B: int, T: int, N: int = 1024, H: int = 12, R: int = 32, w_ring:
     case["gate"] = _normal_bf16(rng, (B, T, W))
     case["beta"] = _normal_bf16(rng, (B, T, H))
     case["a_log"], case["dt_bias"] = gate_params(rng, H)
-    case["pool"] = pool_bits(rng, N, H)
+    case["pool"] = pool_bits(rng, N, H) if N <= 64 else shared_pool(N, H)
     case["idx"] = state_indices(rng, B, N, inactive_frac)
     # Fold rows draw hist in [max(0, fm - T), min(fm - 1, w_ring - T)]; the rest
     # draw hist in [0, fm - T - 1] (empty when fm <= T: then every row folds).

@@ -4,16 +4,20 @@
 Headline (one JSON line on stdout): T = 1 decode at B = 512, H = 12,
 K = V = 128, bf16 pool of 1024 slots with 5% inactive rows, microseconds per
 call. A step is one kda_decode call over one batch. Calls rotate over four
-disjoint (pool, slot set, input) combinations so that one call's state
-(~190 MiB) is not left in the 256 MiB Infinity Cache for the next call that
-reads it; the timed region is K back-to-back calls bracketed by device
-synchronisation. Kernel durations come from HIP events recorded on the
-launch stream around every timed call.
+(pool, slot set, inputs) combinations -- two 1024-slot pools times two
+disjoint slot sets -- so the state a call reads (~190 MiB) was last touched
+three calls earlier, past the 256 MiB Infinity Cache. The K timed calls are
+replayed from HIP graphs (K launches exactly), bracketed by device
+synchronisation; HIP events on the launch stream around the timed region
+give the average kernel duration.
 
-The same line carries the roofline of the decode kernel (algorithmic bytes /
-event-timed duration against 8 TB/s), a CPU baseline (the CPU oracle timed on
-this host), and further measured points (decode batch sweep, verify, prefill)
-under "points".
+The line also carries the roofline of the decode kernel (algorithmic bytes
+per call / average duration, against 8 TB/s), the CPU oracle timed on this
+host, and further measured points under "points": the decode batch sweep and
+the verify workloads (T = 8 / 4, bare checkpoint, fold rates, deep window).
+
+--mode profile runs a short fixed sequence (decode B = 512, verify T = 8
+B = 512, and a known-size device copy for counter calibration) for rocprofv3.
 """
 from __future__ import annotations
 
@@ -30,6 +34,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+H = 12
+N_SLOTS = 1024
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -41,7 +48,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--points", choices=["all", "none"], default="all",
-                    help="also measure the decode sweep / verify / prefill points")
+                    help="also measure the decode sweep and the verify points")
+    ap.add_argument("--mode", choices=["bench", "profile"], default="bench")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     return ap.parse_args()
@@ -50,74 +58,96 @@ def parse():
 # ---------------------------------------------------------------------------
 # timing
 
-def time_calls(calls, steps, warmup, torch):
-    """Run `warmup` then `steps` calls (rotating through `calls`). Returns
-    (wall_seconds, per-call event durations in ms)."""
+def time_graphs(calls, steps, warmup, torch):
+    """Replay exactly `steps` launches (rotating through `calls`) from HIP
+    graphs after `warmup` eager launches. Returns (wall seconds, event ms)."""
     n = len(calls)
-    for i in range(warmup):
+    for i in range(max(warmup, n)):
         calls[i % n]()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    per = n * max(1, 32 // n)
+    reps, rem = divmod(steps, per)
+
+    def capture(count):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(count):
+                    calls[i % n]()
+        torch.cuda.current_stream().wait_stream(s)
+        return g
+
+    g_main = capture(per) if reps else None
+    g_rem = capture(rem) if rem else None
+    if g_main is not None:
+        g_main.replay()
+    if g_rem is not None:
+        g_rem.replay()
     torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record()
-        calls[i % n]()
-        ends[i].record()
+    e0.record()
+    for _ in range(reps):
+        g_main.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    return wall, e0.elapsed_time(e1)
 
 
 # ---------------------------------------------------------------------------
-# decode
+# workloads
 
-def make_pools(torch, synth, H=12, N=1024):
-    """Two bf16 pools of N slots (seeded N(0, 0.05) state)."""
+def bf16_dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def make_pools(torch, synth):
+    """Two bf16 pools of 1024 slots (seeded N(0, 0.05) state)."""
     pools = []
     for p in range(2):
         rng = np.random.Generator(np.random.PCG64(synth.seed_for(1, 0, p)))
-        bits = synth.pool_bits(rng, N, H)
-        pools.append(torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16))
-        del bits
+        pools.append(bf16_dev(torch, synth.pool_bits(rng, N_SLOTS, H)))
     return pools
 
 
-class DecodeSetup:
-    """Four rotating (pool, index set, inputs) combinations for batch B: two
-    pools x two disjoint index sets, each with its own seeded inputs."""
+def index_sets(synth, B, tag, inactive_frac=0.05):
+    """Two disjoint slot sets of B rows (when 2B <= 1024), each with
+    round(inactive_frac * B) rows set to -1 or >= 1024."""
+    rng = np.random.Generator(np.random.PCG64(synth.seed_for(1, B, tag)))
+    perm = rng.permutation(N_SLOTS)
+    sets = []
+    for s in range(2):
+        idx = (perm[s * B:(s + 1) * B] if 2 * B <= N_SLOTS else perm[:B]).astype(np.int64)
+        n_bad = int(round(inactive_frac * B))
+        for i, pos in enumerate(sorted(rng.choice(B, size=n_bad, replace=False))):
+            idx[pos] = -1 if i % 2 == 0 else N_SLOTS + int(rng.integers(0, 1000))
+        sets.append(idx.astype(np.int32))
+    return sets
 
-    def __init__(self, B, torch, kda, synth, pools, H=12, N=1024):
-        self.B, self.H = B, H
-        self.kda, self.torch = kda, torch
+
+class DecodeSetup:
+    def __init__(self, B, torch, kda, synth, pools):
+        self.B = B
         W = H * 128
-        self.W = W
-        rng = np.random.Generator(np.random.PCG64(synth.seed_for(1, B, 99)))
-        perm = rng.permutation(N)
-        sets = []
-        for s in range(2):
-            chosen = perm[s * B:(s + 1) * B] if 2 * B <= N else perm[:B]
-            idx = chosen.astype(np.int64)
-            n_bad = int(round(0.05 * B))
-            for i, pos in enumerate(sorted(rng.choice(B, size=n_bad, replace=False))):
-                idx[pos] = -1 if i % 2 == 0 else N + int(rng.integers(0, 1000))
-            sets.append(idx.astype(np.int32))
-        self.n_active = int(((sets[0] >= 0) & (sets[0] < N)).sum())
+        sets = index_sets(synth, B, 99)
+        self.n_active = int(((sets[0] >= 0) & (sets[0] < N_SLOTS)).sum())
         self.combos = []
         for j in range(4):
             c = synth.decode_case(B=B, N=1, H=H, seed=synth.seed_for(1, B) + j)
-            qkv = self._bf16(c["qkv"])
+            qkv = bf16_dev(torch, c["qkv"])
             self.combos.append(dict(
-                q=qkv[:, :W], k=qkv[:, W:2 * W], v=qkv[:, 2 * W:], g=self._bf16(c["gate"]),
-                b=self._bf16(c["beta"]), a_log=torch.from_numpy(c["a_log"]).cuda(),
+                q=qkv[:, :W], k=qkv[:, W:2 * W], v=qkv[:, 2 * W:], g=bf16_dev(torch, c["gate"]),
+                b=bf16_dev(torch, c["beta"]), a_log=torch.from_numpy(c["a_log"]).cuda(),
                 dtb=torch.from_numpy(c["dt_bias"]).cuda(), pool=pools[j % 2],
                 idx=torch.from_numpy(sets[(j // 2) % 2]).cuda(),
                 out=torch.empty((B, W), dtype=torch.bfloat16, device="cuda")))
-
-    def _bf16(self, a):
-        t = self.torch
-        return t.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(t.bfloat16)
+        self.kda = kda
 
     def calls(self):
         kda = self.kda
@@ -128,16 +158,67 @@ class DecodeSetup:
         return [mk(c) for c in self.combos]
 
 
+class VerifySetup:
+    """Verify workload: T draft tokens per row, pools shared with decode,
+    one synthetic ring set per pool; per-row hist_len / cache_base drawn as in
+    the tests (fold probability p, or hist ~ U{0..hist_max})."""
+
+    def __init__(self, B, T, torch, kda, synth, pools, rings, w_ring=16, flush_min=None,
+                 fold_p=0.0, hist_max=None):
+        self.B, self.T, self.w_ring = B, T, w_ring
+        W = H * 128
+        sets = index_sets(synth, B, 77, inactive_frac=0.0)
+        self.combos = []
+        for j in range(4):
+            c = synth.verify_case(B=B, T=T, N=1, H=H, w_ring=w_ring, flush_min=flush_min,
+                                  fold_p=fold_p, hist_max=hist_max,
+                                  seed=synth.seed_for(3, B, T) + j)
+            self.flush_min = c["flush_min"]
+            if j == 0:
+                self.hist = c["hist_len"].copy()
+                self.fold = (c["hist_len"] + T >= c["flush_min"])
+            qkv = bf16_dev(torch, c["qkv"])
+            kc, uc, gc = rings[j % 2]
+            self.combos.append(dict(
+                q=qkv[..., :W], k=qkv[..., W:2 * W], v=qkv[..., 2 * W:],
+                g=bf16_dev(torch, c["gate"]), b=bf16_dev(torch, c["beta"]),
+                a_log=torch.from_numpy(c["a_log"]).cuda(),
+                dtb=torch.from_numpy(c["dt_bias"]).cuda(), pool=pools[j % 2],
+                idx=torch.from_numpy(sets[(j // 2) % 2]).cuda(), kc=kc, uc=uc, gc=gc,
+                hist=torch.from_numpy(self.hist).cuda(),
+                base=torch.from_numpy(c["cache_base"]).cuda(),
+                out=torch.empty((B, T, W), dtype=torch.bfloat16, device="cuda")))
+        self.kda = kda
+
+    def calls(self):
+        kda, fm, w = self.kda, self.flush_min, self.w_ring
+
+        def mk(c):
+            return lambda: kda.kda_verify_ucache_flush(
+                c["q"], c["k"], c["v"], c["g"], c["b"], c["a_log"], c["dtb"], c["pool"],
+                c["idx"], c["kc"], c["uc"], c["gc"], c["hist"], c["base"], c["out"],
+                flush_min=fm, w_ring=w)
+        return [mk(c) for c in self.combos]
+
+
+def make_rings(torch, synth):
+    rings = []
+    for p in range(2):
+        kc, uc, gc = synth.synthetic_rings((N_SLOTS, H, 32, 128), synth.seed_for(3, 0, p))
+        rings.append((bf16_dev(torch, kc), bf16_dev(torch, uc), torch.from_numpy(gc).cuda()))
+    return rings
+
+
 def cpu_baseline_decode(B, budget_s, synth):
-    """Time the CPU oracle on the same decode workload (one full B-row call
-    per run; runs repeat until the budget is used, at least once)."""
+    """The CPU oracle on the same decode workload: one full B-row call per
+    run; runs repeat until the budget is used (at least one)."""
     import oracle
-    case = synth.decode_case(B=B, N=1024, H=12)
-    H, W = 12, 12 * 128
+    case = synth.decode_case(B=B, N=N_SLOTS, H=H)
+    W = H * 128
     f32 = synth.f32_from_bits
     # gather the active rows' slots into a compact pool (inactive rows -> -1)
     idx = case["idx"].astype(np.int64)
-    active = (idx >= 0) & (idx < case["N"])
+    active = (idx >= 0) & (idx < N_SLOTS)
     slots = idx[active]
     cidx = np.full(B, -1, np.int32)
     cidx[active] = np.arange(slots.size, dtype=np.int32)
@@ -157,19 +238,37 @@ def cpu_baseline_decode(B, budget_s, synth):
             break
     return dict(value=round(float(np.median(times)) * 1e6, 1), unit="us_per_call",
                 cores=oracle.threads(), kind="oracle",
-                sample=f"full T=1 decode call, B={B}, H=12, N=1024 pool (5% inactive), "
-                       f"fp32 oracle, median of {len(times)} runs, "
-                       f"{platform.processor() or platform.machine()}")
+                sample=f"full T=1 decode call, B={B}, H=12, 1024-slot pool (5% inactive), "
+                       f"fp32 oracle with OpenMP over (row, head), median of {len(times)} runs, "
+                       f"host {platform.machine()} with {os.cpu_count()} logical CPUs")
 
 
 # ---------------------------------------------------------------------------
+
+def run_profile(torch, kda, synth, pools):
+    """Fixed short sequence for rocprofv3: 8 decode calls (B = 512), 8 verify
+    calls (T = 8, B = 512, bare checkpoint), 4 device copies of 402,653,184 B."""
+    dec = DecodeSetup(512, torch, kda, synth, pools)
+    for c in dec.calls() * 2:
+        c()
+    torch.cuda.synchronize()
+    rings = make_rings(torch, synth)
+    ver = VerifySetup(512, 8, torch, kda, synth, pools, rings, hist_max=0)
+    for c in ver.calls() * 2:
+        c()
+    torch.cuda.synchronize()
+    src, dst = pools
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("profile: 8 x decode B=512, 8 x verify T=8 B=512 bare, 4 x copy 402653184 B")
+
 
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the KDA step shards by rows and heads with no exchange; see the design notes).",
-              file=sys.stderr)
+              "(the KDA step shards by rows and heads with no exchange).", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -180,31 +279,67 @@ def main():
     torch.cuda.init()
     dev_name = torch.cuda.get_device_name(0)
     log(f"bench: device {dev_name}")
+    pools = make_pools(torch, synth)
+
+    if args.mode == "profile":
+        run_profile(torch, kda, synth, pools)
+        return
 
     B = 512
-    pools = make_pools(torch, synth)
     setup = DecodeSetup(B, torch, kda, synth, pools)
     log(f"bench: decode B={B} set up ({setup.n_active} active rows)")
-    wall, ev = time_calls(setup.calls(), args.steps, args.warmup, torch)
+    wall, ev_ms = time_graphs(setup.calls(), args.steps, args.warmup, torch)
     us_wall = wall / args.steps * 1e6
-    us_ev = float(ev.mean()) * 1e3
+    us_ev = ev_ms * 1e3 / args.steps
     nbytes = wm.decode_bytes(setup.n_active, B - setup.n_active)
     gbs = nbytes / (us_ev * 1e-6) / 1e9
-    log(f"bench: decode B={B}: {us_wall:.2f} us/step wall, {us_ev:.2f} us kernel avg, "
+    log(f"bench: decode B={B}: {us_wall:.2f} us/step wall, {us_ev:.2f} us/call (events), "
         f"{gbs:.0f} GB/s")
 
     points = []
     if args.points == "all":
         for Bp in (1, 8, 32, 128):
             sp = DecodeSetup(Bp, torch, kda, synth, pools)
-            st = max(args.steps, 200)
-            w, e = time_calls(sp.calls(), st, args.warmup, torch)
+            st = max(args.steps, 256)
+            _, e = time_graphs(sp.calls(), st, args.warmup, torch)
+            us = e * 1e3 / st
             nb = wm.decode_bytes(sp.n_active, Bp - sp.n_active)
-            points.append(dict(kind="decode", B=Bp, us_per_call=round(float(e.mean()) * 1e3, 2),
-                               us_median=round(float(np.median(e)) * 1e3, 2),
-                               GBps=round(nb / (float(e.mean()) * 1e-3) / 1e9, 1)))
-            log(f"bench: decode B={Bp}: {points[-1]}")
-            del sp
+            points.append(dict(kind="decode", B=Bp, T=1, us_per_call=round(us, 3),
+                               GBps=round(nb / (us * 1e-6) / 1e9, 1),
+                               hbm_frac=round(nb / (us * 1e-6) / 1e9 / wm.HBM_PEAK_GBS, 4)))
+            log(f"bench: {points[-1]}")
+        points.append(dict(kind="decode", B=B, T=1, us_per_call=round(us_ev, 3),
+                           GBps=round(gbs, 1), hbm_frac=round(gbs / wm.HBM_PEAK_GBS, 4)))
+        rings = make_rings(torch, synth)
+        vcfgs = [
+            dict(label="T=8 bare (0% fold)", T=8, hist_max=0),
+            dict(label="T=4 bare (0% fold)", T=4, hist_max=0),
+            dict(label="T=8 fm=9 50% fold", T=8, fold_p=0.5),
+            dict(label="T=8 fm=9 100% fold", T=8, fold_p=1.0),
+            dict(label="T=4 fm=13 100% fold", T=4, fold_p=1.0),
+            dict(label="T=8 W32 fm=25 hist~U{0..24}", T=8, w_ring=32, flush_min=25, hist_max=24),
+        ]
+        for Bv in (1, 32, 512):
+            for cfg in vcfgs:
+                if Bv != 512 and cfg["label"] not in ("T=8 bare (0% fold)", "T=8 fm=9 100% fold"):
+                    continue
+                kw = {k: v for k, v in cfg.items() if k not in ("label", "T")}
+                vs = VerifySetup(Bv, cfg["T"], torch, kda, synth, pools, rings, **kw)
+                st = max(args.steps, 256 if Bv < 512 else 100)
+                _, e = time_graphs(vs.calls(), st, args.warmup, torch)
+                us = e * 1e3 / st
+                nb = wm.verify_bytes(cfg["T"], vs.hist, vs.fold)
+                fl = wm.verify_flops(cfg["T"], vs.hist)
+                points.append(dict(kind="verify", B=Bv, label=cfg["label"],
+                                   fold_frac=round(float(np.mean(vs.fold)), 3),
+                                   mean_hist=round(float(np.mean(vs.hist)), 2),
+                                   us_per_call=round(us, 3),
+                                   GBps=round(nb / (us * 1e-6) / 1e9, 1),
+                                   hbm_frac=round(nb / (us * 1e-6) / 1e9 / wm.HBM_PEAK_GBS, 4),
+                                   TFLOPs=round(fl / (us * 1e-6) / 1e12, 2)))
+                log(f"bench: {points[-1]}")
+                del vs
+        del rings
         torch.cuda.empty_cache()
 
     cpu = None
@@ -226,12 +361,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16 storage, fp32 math",
         "data": "synthetic (seeded N(0,1) q/k/v/gate/beta, N(0,0.05) state)",
-        "config": {"workload": "kda_decode T=1, B=512, H=12, K=V=128, bf16 pool N=1024, "
-                               "5% inactive rows, packed q/k/v views",
-                   "B": B, "H": 12, "T": 1, "pool_slots": 1024, "device": dev_name},
+        "config": {"workload": "kda_decode T=1, B=512, H=12, K=V=128, bf16 pool of 1024 slots, "
+                               "5% inactive rows, q/k/v strided views of packed rows",
+                   "B": B, "H": H, "T": 1, "pool_slots": N_SLOTS, "device": dev_name},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": wm.HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / wm.HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "decode_kernel<8,true>",
+                     "traffic": None, "kernel": "kda::decode_kernel<8, true>",
                      "kernel_us_avg": round(us_ev, 3), "algorithmic_bytes": nbytes},
         "cpu_baseline": cpu,
         "points": points,

@@ -5,8 +5,8 @@
 // (KDA)", sections "What it does", "API" and "Caching". One workgroup (four
 // waves) owns one (row, head). With S_cur the state the ring stands for,
 //   S_cur = diag(exp(G_L)) S_ckpt + sum_{j<hist} diag(exp(G_L - G_j)) k_j u_j^T,
-// the T draft tokens are processed as one chunk of the chunkwise (WY)
-// form of the recurrence instead of T sequential state updates:
+// the T draft tokens are processed as one chunk of the chunkwise (WY) form of
+// the recurrence instead of T sequential state updates:
 //   Gam_t  = g_0 + ... + g_t                        (per key channel)
 //   A[r,j] = sum_c k_r k_j exp(Gam_r - Gam_j)        (j < r)
 //   P[r,j] = sum_c q_r k_j exp(Gam_r - Gam_j)        (j <= r)
@@ -14,9 +14,9 @@
 //   U0     = (I + diag(beta) A)^-1 diag(beta) V
 //   u_t    = U0_t - (W S_cur)_t                      (the per-token corrections)
 //   o_t    = scale * ((exp(Gam_t) * q_t) S_cur + sum_{j<=t} P[t,j] u_j)
-// (S k means the state applied to a key vector, as in u = beta (v - S k)).
-// Because S_cur only enters through X S_cur with X = [W; exp(Gam) * Q], the
-// replay never needs to be materialised for the outputs:
+// ("S k" is the state applied to a key vector, as in u = beta (v - S k).)
+// S_cur only enters through X S_cur with X = [W; exp(Gam) * Q], so the replay
+// is never materialised for the outputs:
 //   X S_cur = (X * exp(G_L)) S_ckpt + C U_hist,  C[m,j] = X_m . (exp(G_L - G_j) * k_j).
 // (X * exp(G_L)) S_ckpt is the only product with the full 128 x 128 state. The
 // checkpoint is exact in bf16, so it feeds v_mfma_f32_16x16x32_bf16 directly
@@ -25,6 +25,17 @@
 // accumulator, ~2^-17 relative error). Everything else is small and runs on
 // the VALU in fp32. A folding row also materialises S_cur element-wise (fp32)
 // and stores it in bf16 over the checkpoint.
+//
+// Prologue cost matters as much as the state stream here, so:
+//  * transcendentals use the hardware v_exp_f32 / v_log_f32;
+//  * when T * |lower_bound| < 80 every exp(Gam_r - Gam_j) factors into
+//    exp(Gam_r) * exp(-Gam_j) (both finite in fp32), so the Gram products are
+//    plain FMAs over precomputed rows (FACT); otherwise each weight is one
+//    exp of a difference;
+//  * a 16-lane group reads 4 + 4 channels per lane (two 256-byte runs per
+//    row), which keeps LDS accesses free of bank conflicts;
+//  * ring rows wrap by one conditional subtraction (base < R and
+//    hist + T <= R).
 
 #include "kda_common.h"
 #include "kda_launch.h"
@@ -33,53 +44,53 @@ namespace kda {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TMAX = 8;
 constexpr int XLD = D + 8;  // padded bf16 row of the MFMA left operand (bank spread)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 
-// Dynamic LDS carve-up (floats unless noted). hm = history capacity of the
-// launch (w_ring - T).
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
+
+// max(lb, -exp(A_log) * softplus(x)) with hardware exp / log.
+__device__ __forceinline__ float fgate(float x, float neg_exp_alog, float lb) {
+  const float sp = x > 20.0f ? x : LN2 * __builtin_amdgcn_logf(1.0f + fexp(x));
+  return fmaxf(lb, neg_exp_alog * sp);
+}
+
+// LDS layout (floats unless noted); hm = history capacity (w_ring - T).
 struct Smem {
-  float* qh;    // [TMAX][D] q_hat; aliased by y after the left operand is built
-  float* kh;    // [TMAX][D] k_hat
-  float* y;     // [2*TMAX][D] MFMA result rows (aliases qh, kh)
-  float* gam;   // [TMAX][D] g_t, then Gam_t in place
-  float* vv;    // [TMAX][D] v_t, then U0_t in place
-  float* xf;    // [2*TMAX][D] X rows in fp32 (for C)
+  float* qa;      // [TMAX][D] q_hat, then exp(Gam) * q_hat           (X rows T..2T-1)
+  float* ka;      // [TMAX][D] k_hat, then exp(Gam) * k_hat, then W    (X rows 0..T-1)
+  float* kb;      // [TMAX][D] g, then Gam, then exp(-Gam) * k_hat (FACT)
+  float* vv;      // [TMAX][D] v, then U0
+  float* y;       // [2*TMAX][D] MFMA result rows (aliases qa, ka)
+  float* am;      // [TMAX][TMAX]
+  float* pm;      // [TMAX][TMAX]
+  float* beta;    // [TMAX]
+  float* egl;     // [D] exp(G_L)
+  float* cm;      // [2*TMAX][hm]
+  float* dh;      // [hm][D] exp(G_L - G_j) * k_j
   uint16_t* xop;  // [2][2*TMAX][XLD] bf16 hi / lo of X * exp(G_L)
-  float* am;    // [TMAX][TMAX]
-  float* pm;    // [TMAX][TMAX]
-  float* beta;  // [TMAX]
-  float* egl;   // [D] exp(G_L)
-  float* cm;    // [2*TMAX][hm]
-  float* dh;    // [hm][D] exp(G_L - G_j) * k_j
-  uint16_t* uh;  // [hm][D] u_j (bf16 bits)
+  uint16_t* uh;   // [hm][D] u_j (bf16 bits)
 };
 
 __host__ __device__ inline size_t smem_bytes(int hm) {
-  size_t f = 0;
-  f += 2 * TMAX * D;          // qh, kh (y)
-  f += TMAX * D;              // gam
-  f += TMAX * D;              // vv
-  f += 2 * TMAX * D;          // xf
-  f += 2 * TMAX * TMAX + TMAX + D;
-  f += size_t(2 * TMAX) * hm;  // cm
-  f += size_t(hm) * D;         // dh
-  size_t bytes = f * 4;
-  bytes += size_t(2) * 2 * TMAX * XLD * 2;  // xop
-  bytes += size_t(hm) * D * 2;               // uh
+  size_t f = size_t(4) * TMAX * D + 2 * TMAX * TMAX + TMAX + D + size_t(2 * TMAX) * hm +
+             size_t(hm) * D;
+  size_t bytes = f * 4 + size_t(2) * 2 * TMAX * XLD * 2 + size_t(hm) * D * 2;
   return (bytes + 15) & ~size_t(15);
 }
 
 __device__ inline Smem carve(float* base, int hm) {
   Smem s;
   float* p = base;
-  s.qh = p; p += TMAX * D;
-  s.kh = p; p += TMAX * D;
-  s.y = s.qh;
-  s.gam = p; p += TMAX * D;
+  s.qa = p; p += TMAX * D;
+  s.ka = p; p += TMAX * D;
+  s.y = s.qa;
+  s.kb = p; p += TMAX * D;
   s.vv = p; p += TMAX * D;
-  s.xf = p; p += 2 * TMAX * D;
   s.am = p; p += TMAX * TMAX;
   s.pm = p; p += TMAX * TMAX;
   s.beta = p; p += TMAX;
@@ -91,15 +102,57 @@ __device__ inline Smem carve(float* base, int hm) {
   return s;
 }
 
+// Four consecutive bf16 -> floats (VEC: one 8-byte load).
 template <bool VEC>
-__device__ __forceinline__ void load_bfrag(const uint16_t* p, u32x4& w) {
-  w = load8_raw<VEC>(p);
+__device__ __forceinline__ void load4_bf16(const uint16_t* p, float* x) {
+  if constexpr (VEC) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    x[0] = bf_lo(w[0]);
+    x[1] = bf_hi(w[0]);
+    x[2] = bf_lo(w[1]);
+    x[3] = bf_hi(w[1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = bf1(p[i]);
+  }
+}
+
+template <bool VEC>
+__device__ __forceinline__ void store4_bf16(uint16_t* p, const float* x) {
+  const uint32_t w0 = pack_bf16x2(x[0], x[1]), w1 = pack_bf16x2(x[2], x[3]);
+  if constexpr (VEC) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{w0, w1};
+  } else {
+    p[0] = uint16_t(w0 & 0xffffu);
+    p[1] = uint16_t(w0 >> 16);
+    p[2] = uint16_t(w1 & 0xffffu);
+    p[3] = uint16_t(w1 >> 16);
+  }
+}
+
+// The 8 channels of lane kb (0..15) inside a 16-lane group: 4kb..4kb+3 and
+// 64+4kb..64+4kb+3.
+__device__ __forceinline__ int chan(int kb, int half) { return half * 64 + 4 * kb; }
+
+__device__ __forceinline__ void lds_read8(const float* row, int kb, float* x) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(row + chan(kb, 0));
+  const f32x4 b = *reinterpret_cast<const f32x4*>(row + chan(kb, 1));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
+}
+
+__device__ __forceinline__ void lds_write8(float* row, int kb, const float* x) {
+  *reinterpret_cast<f32x4*>(row + chan(kb, 0)) = f32x4{x[0], x[1], x[2], x[3]};
+  *reinterpret_cast<f32x4*>(row + chan(kb, 1)) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
 }  // namespace
 
 // Grid: one 256-thread workgroup per (row, head), row-major over heads.
-template <bool VEC>
+template <bool VEC, bool FACT>
 __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   extern __shared__ __align__(16) float smem_raw[];
   const int tid = threadIdx.x;
@@ -117,7 +170,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
                       hist + T <= p.w_ring && base >= 0 && base < R;
   uint16_t* outb = p.out + b * p.out_row_stride + int64_t(h) * D;
   if (!active) {
-    for (int e = tid; e < T * D; e += 256) outb[int64_t(e / D) * p.out_tok_stride + (e % D)] = 0;
+    for (int e = tid; e < T * D; e += 256) outb[int64_t(e >> 7) * p.out_tok_stride + (e & 127)] = 0;
     return;
   }
   const bool fold = hist + T >= p.flush_min;
@@ -127,31 +180,39 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   uint16_t* kc = p.k_cache + sh * R * D;
   uint16_t* uc = p.u_cache + sh * R * D;
   float* gc = p.g_cache + sh * R * D;
+  // ring row of history / draft position j (0 <= j < hist + T <= R, base < R)
+  auto ring_row = [&](int j) { const int r = base + j; return r >= R ? r - R : r; };
 
   // ---- 1. checkpoint B fragments: wave w owns value columns 32w .. 32w+31
-  // (two 16-column blocks); fragment (blk, s): v = 32w + 16*blk + lane%16,
-  // key channels 32*s + 8*(lane/16) .. +7.
+  // (two 16-column blocks); fragment (blk, st): v = 32w + 16*blk + lane%16,
+  // key channels 32*st + 8*(lane/16) .. +7.
   const int fv = lane & 15, fk = (lane >> 4) * 8;
   u32x4 sf[2][4];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
     for (int st = 0; st < 4; ++st)
-      load_bfrag<VEC>(ckpt + int64_t(32 * wave + 16 * blk + fv) * D + 32 * st + fk, sf[blk][st]);
+      sf[blk][st] = load8_raw<VEC>(ckpt + int64_t(32 * wave + 16 * blk + fv) * D + 32 * st + fk);
 
-  // ---- 2. per-token prologue: token t on wave t/4, lanes 16*(t%4) .. +15,
-  // key channels 8*(lane%16) .. +7.
+  // ---- 2. per-token prologue: token t on wave t/4, lanes 16*(t%4) .. +15.
+  const int kb = lane & 15;
   {
     const int t = wave * 4 + (lane >> 4);
-    const int c0 = (lane & 15) * 8;
     if (t < T) {
-      float q[8], k[8], gr[8], vv[8], dtb[8];
-      load8_bf16<VEC>(p.q + b * p.q_row_stride + t * p.q_tok_stride + h * D + c0, q);
-      load8_bf16<VEC>(p.k + b * p.k_row_stride + t * p.k_tok_stride + h * D + c0, k);
-      load8_bf16<VEC>(p.g + b * p.g_row_stride + t * p.g_tok_stride + h * D + c0, gr);
-      load8_bf16<VEC>(p.v + b * p.v_row_stride + t * p.v_tok_stride + h * D + c0, vv);
-      load8_f32<VEC>(p.dt_bias + h * D + c0, dtb);
-      const float neg_ea = -expf(p.A_log[h]);
+      float q[8], k[8], gr[8], vv[8];
+      const int64_t qo = b * p.q_row_stride + t * p.q_tok_stride + h * D;
+      const int64_t ko = b * p.k_row_stride + t * p.k_tok_stride + h * D;
+      const int64_t go = b * p.g_row_stride + t * p.g_tok_stride + h * D;
+      const int64_t vo = b * p.v_row_stride + t * p.v_tok_stride + h * D;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int c = chan(kb, hf);
+        load4_bf16<VEC>(p.q + qo + c, q + 4 * hf);
+        load4_bf16<VEC>(p.k + ko + c, k + 4 * hf);
+        load4_bf16<VEC>(p.g + go + c, gr + 4 * hf);
+        load4_bf16<VEC>(p.v + vo + c, vv + 4 * hf);
+      }
+      const float neg_ea = -fexp(p.A_log[h]);
       float sq = 0.f, sk = 0.f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
@@ -162,48 +223,58 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
       sk = row16_sum(sk);
       const float rq = 1.0f / sqrtf(sq + 1e-6f);
       const float rk = 1.0f / sqrtf(sk + 1e-6f);
-      u32x4 kb16;
+      float g[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        s.qh[t * D + c0 + c] = q[c] * rq;
-        s.kh[t * D + c0 + c] = k[c] * rk;
-        s.gam[t * D + c0 + c] = gate_logdecay(gr[c] + dtb[c], neg_ea, p.lower_bound);
-        s.vv[t * D + c0 + c] = vv[c];
+        q[c] *= rq;
+        k[c] *= rk;
+        g[c] = fgate(gr[c] + p.dt_bias[h * D + chan(kb, c >> 2) + (c & 3)], neg_ea,
+                     p.lower_bound);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kb16[j] = pack_bf16x2(k[2 * j] * rk, k[2 * j + 1] * rk);
-      const int row = (base + hist + t) % R;
-      store8_raw<VEC>(kc + int64_t(row) * D + c0, kb16);
-      if ((lane & 15) == 0)
-        s.beta[t] = sigmoidf(bf1(p.beta[b * p.beta_row_stride + t * p.beta_tok_stride + h]));
+      lds_write8(s.qa + t * D, kb, q);
+      lds_write8(s.ka + t * D, kb, k);
+      lds_write8(s.kb + t * D, kb, g);
+      lds_write8(s.vv + t * D, kb, vv);
+      uint16_t* kr = kc + int64_t(ring_row(hist + t)) * D;
+      store4_bf16<VEC>(kr + chan(kb, 0), k);
+      store4_bf16<VEC>(kr + chan(kb, 1), k + 4);
+      if (kb == 0)
+        s.beta[t] = 1.0f / (1.0f + fexp(-bf1(p.beta[b * p.beta_row_stride + t * p.beta_tok_stride + h])));
     }
   }
   __syncthreads();
 
-  // ---- 3. cumulative decays and ring history. Threads 0..127 own key
-  // channel c: Gam_t = g_0 + ... + g_t (from 0, in place over g_t) and the
-  // ring's G_t = G_base + g_0 + ... + g_t (token order; G_base = 0 when
-  // folding, else G_{hist-1}), plus exp(G_L). Threads 128..255 stage the live
-  // history rows: D_j = exp(G_L - G_j) * k_j (fp32) and u_j (bf16). History
-  // rows j < hist and the draft rows hist .. hist+T-1 never coincide because
-  // hist + T <= w_ring <= R.
+  // ---- 3. threads 0..127 own key channel c: Gam_t (from 0) and the ring's
+  // G_t = G_base + g_0 + ... + g_t in token order (G_base = 0 when folding,
+  // else G_{hist-1}); exp(G_L); with FACT the rows exp(Gam) * q, exp(Gam) * k
+  // and exp(-Gam) * k. Threads 128..255 stage the live history rows:
+  // D_j = exp(G_L - G_j) * k_j (fp32) and u_j (bf16). History rows
+  // (j < hist) and draft rows (hist .. hist+T-1) never coincide.
   {
     const int c = tid & 127;
-    const float gl = hist > 0 ? gc[int64_t((base + hist - 1) % R) * D + c] : 0.f;
+    const float gl = hist > 0 ? gc[int64_t(ring_row(hist - 1)) * D + c] : 0.f;
     if (tid < 128) {
-      s.egl[c] = expf(gl);
+      s.egl[c] = fexp(gl);
       float gam = 0.f, gacc = fold ? 0.f : gl;
       for (int t = 0; t < T; ++t) {
-        const float g = s.gam[t * D + c];
+        const float g = s.kb[t * D + c];
         gam += g;
         gacc += g;
-        s.gam[t * D + c] = gam;
-        gc[int64_t((base + hist + t) % R) * D + c] = gacc;
+        gc[int64_t(ring_row(hist + t)) * D + c] = gacc;
+        if constexpr (FACT) {
+          const float ea = fexp(gam), eb = fexp(-gam);
+          const float kh = s.ka[t * D + c];
+          s.qa[t * D + c] *= ea;
+          s.ka[t * D + c] = kh * ea;
+          s.kb[t * D + c] = kh * eb;
+        } else {
+          s.kb[t * D + c] = gam;
+        }
       }
     } else {
       for (int j = 0; j < hist; ++j) {
-        const int64_t row = (base + j) % R;
-        s.dh[j * D + c] = expf(gl - gc[row * D + c]) * bf1(kc[row * D + c]);
+        const int64_t row = ring_row(j);
+        s.dh[j * D + c] = fexp(gl - gc[row * D + c]) * bf1(kc[row * D + c]);
         s.uh[j * D + c] = uc[row * D + c];
       }
     }
@@ -213,23 +284,40 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   // ---- 4. A and P: one (r, j) pair per 16-lane group, 8 channels per lane.
   {
     const int grp = tid >> 4;
-    const int c0 = (tid & 15) * 8;
     const int npairs = T * (T + 1) / 2;
     for (int pi = grp; pi < npairs; pi += 16) {
-      int r = 0;
-      while ((r + 1) * (r + 2) / 2 <= pi) ++r;
+      // r = floor((sqrt(8 pi + 1) - 1) / 2); the true value is at least 0.1
+      // below r + 1 for pi < 36, so a 0.01 margin absorbs sqrt rounding.
+      const int r = int((sqrtf(8.0f * pi + 1.0f) - 1.0f) * 0.5f + 0.01f);
       const int j = pi - r * (r + 1) / 2;
       float a = 0.f, pp = 0.f;
+      if constexpr (FACT) {
+        float x[8], y[8], z[8];
+        lds_read8(s.ka + r * D, kb, x);
+        lds_read8(s.qa + r * D, kb, y);
+        lds_read8(s.kb + j * D, kb, z);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float e = expf(s.gam[r * D + c0 + c] - s.gam[j * D + c0 + c]);
-        const float kj = s.kh[j * D + c0 + c] * e;
-        a = fmaf(s.kh[r * D + c0 + c], kj, a);
-        pp = fmaf(s.qh[r * D + c0 + c], kj, pp);
+        for (int c = 0; c < 8; ++c) {
+          a = fmaf(x[c], z[c], a);
+          pp = fmaf(y[c], z[c], pp);
+        }
+      } else {
+        float gr_[8], gj[8], kr[8], kj[8], qr[8];
+        lds_read8(s.kb + r * D, kb, gr_);
+        lds_read8(s.kb + j * D, kb, gj);
+        lds_read8(s.ka + r * D, kb, kr);
+        lds_read8(s.ka + j * D, kb, kj);
+        lds_read8(s.qa + r * D, kb, qr);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float w = kj[c] * fexp(gr_[c] - gj[c]);
+          a = fmaf(kr[c], w, a);
+          pp = fmaf(qr[c], w, pp);
+        }
       }
       a = row16_sum(a);
       pp = row16_sum(pp);
-      if ((tid & 15) == 0) {
+      if (kb == 0) {
         s.am[r * TMAX + j] = j < r ? a : 0.f;
         s.pm[r * TMAX + j] = pp;
       }
@@ -237,60 +325,80 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   }
   __syncthreads();
 
-  // ---- 5. forward substitution. Threads 0..127 own key channel c of W and
-  // build X = [W; exp(Gam) * Q] (fp32 copy for C, bf16 hi/lo of X * exp(G_L)
-  // for the MFMA); threads 128..255 own value channel c of U0 (in place).
+  // ---- 5. forward substitution. Threads 0..127 own key channel c of W
+  // (written over row r of ka; X rows T.. are the exp(Gam) * q rows in qa) and
+  // store the bf16 hi/lo parts of X * exp(G_L); threads 128..255 own value
+  // channel c of U0 (in place in vv).
   {
     const int c = tid & 127;
     if (tid < 128) {
       float w[TMAX];
       const float eg = s.egl[c];
-      for (int r = 0; r < T; ++r) {
-        float x = expf(s.gam[r * D + c]) * s.kh[r * D + c];
-        for (int j = 0; j < r; ++j) x = fmaf(-s.am[r * TMAX + j], w[j], x);
-        w[r] = s.beta[r] * x;
+#pragma unroll
+      for (int r = 0; r < TMAX; ++r) {
+        if (r < T) {
+          float x;
+          if constexpr (FACT) {
+            x = s.ka[r * D + c];
+          } else {
+            const float ea = fexp(s.kb[r * D + c]);
+            x = ea * s.ka[r * D + c];
+            s.qa[r * D + c] *= ea;
+          }
+#pragma unroll
+          for (int j = 0; j < r; ++j) x = fmaf(-s.am[r * TMAX + j], w[j], x);
+          w[r] = s.beta[r] * x;
+          s.ka[r * D + c] = w[r];
+        }
       }
+#pragma unroll
       for (int m = 0; m < 2 * TMAX; ++m) {
         float x = 0.f;
         if (m < T) x = w[m];
-        else if (m < 2 * T) x = expf(s.gam[(m - T) * D + c]) * s.qh[(m - T) * D + c];
-        s.xf[m * D + c] = x;
+        else if (m < 2 * T) x = s.qa[(m - T) * D + c];
         const float xs = x * eg;
         const uint16_t hi = to_bf16(xs);
-        const uint16_t lo = to_bf16(xs - bf1(hi));
         s.xop[m * XLD + c] = hi;
-        s.xop[2 * TMAX * XLD + m * XLD + c] = lo;
+        s.xop[2 * TMAX * XLD + m * XLD + c] = to_bf16(xs - bf1(hi));
       }
     } else {
       float u0[TMAX];
-      for (int r = 0; r < T; ++r) {
-        float x = s.vv[r * D + c];
-        for (int j = 0; j < r; ++j) x = fmaf(-s.am[r * TMAX + j], u0[j], x);
-        u0[r] = s.beta[r] * x;
-        s.vv[r * D + c] = u0[r];
+#pragma unroll
+      for (int r = 0; r < TMAX; ++r) {
+        if (r < T) {
+          float x = s.vv[r * D + c];
+#pragma unroll
+          for (int j = 0; j < r; ++j) x = fmaf(-s.am[r * TMAX + j], u0[j], x);
+          u0[r] = s.beta[r] * x;
+          s.vv[r * D + c] = u0[r];
+        }
       }
     }
   }
   __syncthreads();
 
-  // ---- 5b. C[m, j] = X_m . D_j (history correction), one pair per group.
+  // ---- 5b. C[m, j] = X_m . D_j (history correction); group grp owns row m.
   if (hist > 0) {
     const int grp = tid >> 4;
-    const int c0 = (tid & 15) * 8;
-    const int npairs = 2 * T * hist;
-    for (int pi = grp; pi < npairs; pi += 16) {
-      const int m = pi / hist, j = pi % hist;
-      float a = 0.f;
+    if (grp < 2 * T) {
+      const float* xrow = grp < T ? s.ka + grp * D : s.qa + (grp - T) * D;
+      float x[8];
+      lds_read8(xrow, kb, x);
+      for (int j = 0; j < hist; ++j) {
+        float d[8];
+        lds_read8(s.dh + j * D, kb, d);
+        float a = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) a = fmaf(s.xf[m * D + c0 + c], s.dh[j * D + c0 + c], a);
-      a = row16_sum(a);
-      if ((tid & 15) == 0) s.cm[m * hm + j] = a;
+        for (int c = 0; c < 8; ++c) a = fmaf(x[c], d[c], a);
+        a = row16_sum(a);
+        if (kb == 0) s.cm[grp * hm + j] = a;
+      }
     }
   }
+  __syncthreads();  // X rows (qa / ka) are dead from here on: y may overwrite them
 
   // ---- 6. Y = (X * exp(G_L)) S_ckpt on MFMA: per 16-column block, four
-  // 32-channel steps, hi and lo parts into one accumulator. y aliases qh/kh,
-  // whose last reads were in phase 5 (before the barrier above).
+  // 32-channel steps, hi and lo parts into one accumulator.
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -313,18 +421,22 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   if (tid < 128) {
     const int v = tid;
     float u[TMAX];
-    for (int t = 0; t < T; ++t) {
-      float yw = s.y[t * D + v];
-      float yq = s.y[(T + t) * D + v];
-      for (int j = 0; j < hist; ++j) {
-        const float uj = bf1(s.uh[j * D + v]);
-        yw = fmaf(s.cm[t * hm + j], uj, yw);
-        yq = fmaf(s.cm[(T + t) * hm + j], uj, yq);
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if (t < T) {
+        float yw = s.y[t * D + v];
+        float yq = s.y[(T + t) * D + v];
+        for (int j = 0; j < hist; ++j) {
+          const float uj = bf1(s.uh[j * D + v]);
+          yw = fmaf(s.cm[t * hm + j], uj, yw);
+          yq = fmaf(s.cm[(T + t) * hm + j], uj, yq);
+        }
+        u[t] = s.vv[t * D + v] - yw;
+#pragma unroll
+        for (int j = 0; j <= t; ++j) yq = fmaf(s.pm[t * TMAX + j], u[j], yq);
+        outb[int64_t(t) * p.out_tok_stride + v] = to_bf16(p.scale * yq);
+        uc[int64_t(ring_row(hist + t)) * D + v] = to_bf16(u[t]);
       }
-      u[t] = s.vv[t * D + v] - yw;
-      for (int j = 0; j <= t; ++j) yq = fmaf(s.pm[t * TMAX + j], u[j], yq);
-      outb[int64_t(t) * p.out_tok_stride + v] = to_bf16(p.scale * yq);
-      uc[int64_t((base + hist + t) % R) * D + v] = to_bf16(u[t]);
     }
   }
 
@@ -364,9 +476,16 @@ hipError_t launch_verify(const VerifyParams& p, bool vec, hipStream_t stream) {
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const int hm = p.w_ring - p.T;  // history capacity: hist + T <= w_ring
   const size_t lds = smem_bytes(hm);
+  // exp(Gam_r) * exp(-Gam_j) stays finite when |Gam| <= T * |lower_bound| < 80.
+  const bool fact = p.lower_bound > -80.0f / float(p.T);
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
-  if (vec) hipLaunchKernelGGL((verify_kernel<true>), grid, block, lds, stream, p, hm);
-  else hipLaunchKernelGGL((verify_kernel<false>), grid, block, lds, stream, p, hm);
+  if (vec) {
+    if (fact) hipLaunchKernelGGL((verify_kernel<true, true>), grid, block, lds, stream, p, hm);
+    else hipLaunchKernelGGL((verify_kernel<true, false>), grid, block, lds, stream, p, hm);
+  } else {
+    if (fact) hipLaunchKernelGGL((verify_kernel<false, true>), grid, block, lds, stream, p, hm);
+    else hipLaunchKernelGGL((verify_kernel<false, false>), grid, block, lds, stream, p, hm);
+  }
   return hipGetLastError();
 }
 

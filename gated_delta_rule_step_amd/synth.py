@@ -159,18 +159,24 @@ def verify_case(B: int, T: int, N: int = 1024, H: int = 12, R: int = 32, w_ring:
     return case
 
 
-def synthetic_rings(case: dict, seed: int) -> None:
-    """Fill every ring row with plausible magnitudes (unit-scale keys, small
-    corrections, decreasing cumulative log-decay). Timing only: the values are
-    not the result of stepping any state."""
+def synthetic_rings(shape, seed: int):
+    """Ring arrays (k_cache, u_cache bf16 bits; g_cache fp32) of `shape`
+    [N, H, R, 128] with plausible magnitudes: keys ~ U(-0.15, 0.15),
+    corrections ~ U(-0.5, 0.5), cumulative log-decay decreasing along the ring
+    by U(0, 2) per row. For timing only: no state was stepped to make them."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    N, H, R = case["N"], case["H"], case["R"]
+    N = shape[0]
+    kc = np.empty(shape, np.uint16)
+    uc = np.empty(shape, np.uint16)
+    gc = np.empty(shape, np.float32)
     for s in range(0, N, 64):
         e = min(N, s + 64)
-        case["k_cache"][s:e] = _normal_bf16(rng, (e - s, H, R, HEAD_DIM), HEAD_DIM ** -0.5)
-        case["u_cache"][s:e] = _normal_bf16(rng, (e - s, H, R, HEAD_DIM), 0.3)
-        steps = rng.uniform(0.0, 2.0, size=(e - s, H, R, HEAD_DIM)).astype(np.float32)
-        case["g_cache"][s:e] = -np.cumsum(steps, axis=2, dtype=np.float32)
+        sub = (e - s,) + tuple(shape[1:])
+        kc[s:e] = bf16_bits(rng.random(sub, dtype=np.float32) * np.float32(0.3) - np.float32(0.15))
+        uc[s:e] = bf16_bits(rng.random(sub, dtype=np.float32) - np.float32(0.5))
+        gc[s:e] = -np.cumsum(rng.random(sub, dtype=np.float32) * np.float32(2.0), axis=2,
+                             dtype=np.float32)
+    return kc, uc, gc
 
 
 def history_tokens(case: dict, n_tok: int) -> dict:

@@ -47,7 +47,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TMAX = 8;
-constexpr int XLD = D + 8;  // padded bf16 row of the MFMA left operand (bank spread)
+constexpr int YLD = D + 4;  // padded fp32 row of the MFMA result (rows 4 apart hit other banks)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -65,21 +65,21 @@ struct Smem {
   float* ka;      // [TMAX][D] k_hat, then exp(Gam) * k_hat, then W    (X rows 0..T-1)
   float* kb;      // [TMAX][D] g, then Gam, then exp(-Gam) * k_hat (FACT)
   float* vv;      // [TMAX][D] v, then U0
-  float* y;       // [2*TMAX][D] MFMA result rows (aliases qa, ka)
+  float* y;       // [2*TMAX][YLD] MFMA result rows (aliases qa, ka and the head of kb)
   float* am;      // [TMAX][TMAX]
   float* pm;      // [TMAX][TMAX]
   float* beta;    // [TMAX]
   float* egl;     // [D] exp(G_L)
   float* cm;      // [2*TMAX][hm]
   float* dh;      // [hm][D] exp(G_L - G_j) * k_j
-  uint16_t* xop;  // [2][2*TMAX][XLD] bf16 hi / lo of X * exp(G_L)
+  uint16_t* xop;  // [2][2*TMAX][D] bf16 hi / lo of X * exp(G_L), chunk-swizzled
   uint16_t* uh;   // [hm][D] u_j (bf16 bits)
 };
 
 __host__ __device__ inline size_t smem_bytes(int hm) {
   size_t f = size_t(4) * TMAX * D + 2 * TMAX * TMAX + TMAX + D + size_t(2 * TMAX) * hm +
              size_t(hm) * D;
-  size_t bytes = f * 4 + size_t(2) * 2 * TMAX * XLD * 2 + size_t(hm) * D * 2;
+  size_t bytes = f * 4 + size_t(2) * 2 * TMAX * D * 2 + size_t(hm) * D * 2;
   return (bytes + 15) & ~size_t(15);
 }
 
@@ -98,7 +98,7 @@ __device__ inline Smem carve(float* base, int hm) {
   s.cm = p; p += 2 * TMAX * hm;
   s.dh = p; p += size_t(hm) * D;
   s.xop = reinterpret_cast<uint16_t*>(p);
-  s.uh = s.xop + 2 * 2 * TMAX * XLD;
+  s.uh = s.xop + 2 * 2 * TMAX * D;
   return s;
 }
 
@@ -118,6 +118,21 @@ __device__ __forceinline__ void load4_bf16(const uint16_t* p, float* x) {
 }
 
 template <bool VEC>
+__device__ __forceinline__ u32x2 load4_raw(const uint16_t* p) {
+  if constexpr (VEC) {
+    return *reinterpret_cast<const u32x2*>(p);
+  } else {
+    return u32x2{uint32_t(p[0]) | (uint32_t(p[1]) << 16), uint32_t(p[2]) | (uint32_t(p[3]) << 16)};
+  }
+}
+
+template <bool VEC>
+__device__ __forceinline__ f32x4 load4_f32(const float* p) {
+  if constexpr (VEC) return *reinterpret_cast<const f32x4*>(p);
+  else return f32x4{p[0], p[1], p[2], p[3]};
+}
+
+template <bool VEC>
 __device__ __forceinline__ void store4_bf16(uint16_t* p, const float* x) {
   const uint32_t w0 = pack_bf16x2(x[0], x[1]), w1 = pack_bf16x2(x[2], x[3]);
   if constexpr (VEC) {
@@ -128,6 +143,13 @@ __device__ __forceinline__ void store4_bf16(uint16_t* p, const float* x) {
     p[2] = uint16_t(w1 & 0xffffu);
     p[3] = uint16_t(w1 >> 16);
   }
+}
+
+// Left-operand tile (bf16, 16 rows x 128 channels): the 16-byte chunk c of
+// row m is stored at chunk c ^ (m % 16), so the 16 lanes that read one chunk
+// column of 16 rows hit 16 different bank groups.
+__device__ __forceinline__ int xsw(int m, int c) {
+  return m * D + ((((c >> 3) ^ (m & 15))) << 3) + (c & 7);
 }
 
 // The 8 channels of lane kb (0..15) inside a 16-lane group: 4kb..4kb+3 and
@@ -183,23 +205,22 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   // ring row of history / draft position j (0 <= j < hist + T <= R, base < R)
   auto ring_row = [&](int j) { const int r = base + j; return r >= R ? r - R : r; };
 
-  // ---- 1. checkpoint B fragments: wave w owns value columns 32w .. 32w+31
-  // (two 16-column blocks); fragment (blk, st): v = 32w + 16*blk + lane%16,
-  // key channels 32*st + 8*(lane/16) .. +7.
   const int fv = lane & 15, fk = (lane >> 4) * 8;
   u32x4 sf[2][4];
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-      sf[blk][st] = load8_raw<VEC>(ckpt + int64_t(32 * wave + 16 * blk + fv) * D + 32 * st + fk);
-
   // ---- 2. per-token prologue: token t on wave t/4, lanes 16*(t%4) .. +15.
+  // The token loads are issued first, then the checkpoint B fragments (wave
+  // w owns value columns 32w .. 32w+31 in two 16-column blocks; fragment
+  // (blk, st) holds v = 32w + 16*blk + lane%16, key channels
+  // 32*st + 8*(lane/16) .. +7): waiting for the token inputs then does not
+  // also wait for the 32 KiB state read, which streams in under the prologue.
   const int kb = lane & 15;
   {
     const int t = wave * 4 + (lane >> 4);
+    // raw words first (no use of the loaded values before the state loads)
+    u32x2 qw[2], kw[2], gw[2], vw[2];
+    f32x4 dw[2];
+    float alog = 0.f;
     if (t < T) {
-      float q[8], k[8], gr[8], vv[8];
       const int64_t qo = b * p.q_row_stride + t * p.q_tok_stride + h * D;
       const int64_t ko = b * p.k_row_stride + t * p.k_tok_stride + h * D;
       const int64_t go = b * p.g_row_stride + t * p.g_tok_stride + h * D;
@@ -207,12 +228,40 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int c = chan(kb, hf);
-        load4_bf16<VEC>(p.q + qo + c, q + 4 * hf);
-        load4_bf16<VEC>(p.k + ko + c, k + 4 * hf);
-        load4_bf16<VEC>(p.g + go + c, gr + 4 * hf);
-        load4_bf16<VEC>(p.v + vo + c, vv + 4 * hf);
+        qw[hf] = load4_raw<VEC>(p.q + qo + c);
+        kw[hf] = load4_raw<VEC>(p.k + ko + c);
+        gw[hf] = load4_raw<VEC>(p.g + go + c);
+        vw[hf] = load4_raw<VEC>(p.v + vo + c);
+        dw[hf] = load4_f32<VEC>(p.dt_bias + h * D + c);
       }
-      const float neg_ea = -fexp(p.A_log[h]);
+      alog = p.A_log[h];
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        sf[blk][st] = load8_raw<VEC>(ckpt + int64_t(32 * wave + 16 * blk + fv) * D + 32 * st + fk);
+    // keep the state loads issued here, ahead of any wait on the token loads
+    __builtin_amdgcn_sched_barrier(0);
+    if (t < T) {
+      float q[8], k[8], gr[8], vv[8], dtb[8];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          q[4 * hf + 2 * i] = bf_lo(qw[hf][i]);
+          q[4 * hf + 2 * i + 1] = bf_hi(qw[hf][i]);
+          k[4 * hf + 2 * i] = bf_lo(kw[hf][i]);
+          k[4 * hf + 2 * i + 1] = bf_hi(kw[hf][i]);
+          gr[4 * hf + 2 * i] = bf_lo(gw[hf][i]);
+          gr[4 * hf + 2 * i + 1] = bf_hi(gw[hf][i]);
+          vv[4 * hf + 2 * i] = bf_lo(vw[hf][i]);
+          vv[4 * hf + 2 * i + 1] = bf_hi(vw[hf][i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dtb[4 * hf + i] = dw[hf][i];
+      }
+      const float neg_ea = -fexp(alog);
       float sq = 0.f, sk = 0.f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
@@ -228,8 +277,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
       for (int c = 0; c < 8; ++c) {
         q[c] *= rq;
         k[c] *= rk;
-        g[c] = fgate(gr[c] + p.dt_bias[h * D + chan(kb, c >> 2) + (c & 3)], neg_ea,
-                     p.lower_bound);
+        g[c] = fgate(gr[c] + dtb[c], neg_ea, p.lower_bound);
       }
       lds_write8(s.qa + t * D, kb, q);
       lds_write8(s.ka + t * D, kb, k);
@@ -238,8 +286,6 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
       uint16_t* kr = kc + int64_t(ring_row(hist + t)) * D;
       store4_bf16<VEC>(kr + chan(kb, 0), k);
       store4_bf16<VEC>(kr + chan(kb, 1), k + 4);
-      if (kb == 0)
-        s.beta[t] = 1.0f / (1.0f + fexp(-bf1(p.beta[b * p.beta_row_stride + t * p.beta_tok_stride + h])));
     }
   }
   __syncthreads();
@@ -247,7 +293,8 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   // ---- 3. threads 0..127 own key channel c: Gam_t (from 0) and the ring's
   // G_t = G_base + g_0 + ... + g_t in token order (G_base = 0 when folding,
   // else G_{hist-1}); exp(G_L); with FACT the rows exp(Gam) * q, exp(Gam) * k
-  // and exp(-Gam) * k. Threads 128..255 stage the live history rows:
+  // and exp(-Gam) * k. Threads 128..255 compute beta_t = sigmoid(logit) and
+  // stage the live history rows:
   // D_j = exp(G_L - G_j) * k_j (fp32) and u_j (bf16). History rows
   // (j < hist) and draft rows (hist .. hist+T-1) never coincide.
   {
@@ -272,6 +319,9 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
         }
       }
     } else {
+      if (c < T)
+        s.beta[c] = 1.0f / (1.0f + fexp(-bf1(p.beta[b * p.beta_row_stride +
+                                                    c * p.beta_tok_stride + h])));
       for (int j = 0; j < hist; ++j) {
         const int64_t row = ring_row(j);
         s.dh[j * D + c] = fexp(gl - gc[row * D + c]) * bf1(kc[row * D + c]);
@@ -358,8 +408,8 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
         else if (m < 2 * T) x = s.qa[(m - T) * D + c];
         const float xs = x * eg;
         const uint16_t hi = to_bf16(xs);
-        s.xop[m * XLD + c] = hi;
-        s.xop[2 * TMAX * XLD + m * XLD + c] = to_bf16(xs - bf1(hi));
+        s.xop[xsw(m, c)] = hi;
+        s.xop[2 * TMAX * D + xsw(m, c)] = to_bf16(xs - bf1(hi));
       }
     } else {
       float u0[TMAX];
@@ -395,7 +445,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
       }
     }
   }
-  __syncthreads();  // X rows (qa / ka) are dead from here on: y may overwrite them
+  __syncthreads();  // X rows (qa / ka) and kb are dead from here on: y may overwrite them
 
   // ---- 6. Y = (X * exp(G_L)) S_ckpt on MFMA: per 16-column block, four
   // 32-channel steps, hi and lo parts into one accumulator.
@@ -405,15 +455,15 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const bf16x8 bfr = __builtin_bit_cast(bf16x8, sf[blk][st]);
-      const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(s.xop + fv * XLD + 32 * st + fk);
-      const bf16x8 alo =
-          *reinterpret_cast<const bf16x8*>(s.xop + 2 * TMAX * XLD + fv * XLD + 32 * st + fk);
+      const int ax = xsw(fv, 32 * st + fk);
+      const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(s.xop + ax);
+      const bf16x8 alo = *reinterpret_cast<const bf16x8*>(s.xop + 2 * TMAX * D + ax);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bfr, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfr, acc, 0, 0, 0);
     }
     const int v = 32 * wave + 16 * blk + fv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s.y[((lane >> 4) * 4 + i) * D + v] = acc[i];
+    for (int i = 0; i < 4; ++i) s.y[((lane >> 4) * 4 + i) * YLD + v] = acc[i];
   }
   __syncthreads();
 
@@ -424,8 +474,8 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       if (t < T) {
-        float yw = s.y[t * D + v];
-        float yq = s.y[(T + t) * D + v];
+        float yw = s.y[t * YLD + v];
+        float yq = s.y[(T + t) * YLD + v];
         for (int j = 0; j < hist; ++j) {
           const float uj = bf1(s.uh[j * D + v]);
           yw = fmaf(s.cm[t * hm + j], uj, yw);

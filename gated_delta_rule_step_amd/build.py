@@ -20,6 +20,7 @@ FLAGS = [
     # Compiler-generated packed FP32 (v_pk_*_f32) is switched off for all
     # device code; every FP32 operation runs as a plain VALU instruction.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xclang", "-flax-vector-conversions=none",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),
 ]

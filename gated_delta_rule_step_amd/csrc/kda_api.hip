@@ -193,6 +193,8 @@ extern "C" kda_status kda_prefill_varlen(
     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (n_docs < 0 || total_tokens < 0 || H < 1 || num_slots < 0) return KDA_ERR_BAD_SHAPE;
   if (K != D || V != D) return KDA_ERR_UNSUPPORTED;
+  // 16-token chunks factor each decay weight into two exps of at most 8 |lb|.
+  if (!(lower_bound >= -5.5f && lower_bound <= 5.5f)) return KDA_ERR_UNSUPPORTED;
   if (!cu_seqlens_host) return KDA_ERR_NULL_POINTER;
   if (cu_seqlens_host[0] != 0) return KDA_ERR_BAD_SEQLENS;
   for (int32_t d = 0; d < n_docs; ++d)

@@ -1,8 +1,500 @@
+// Chunked varlen prefill of the KDA recurrence (gfx950).
+//
+// Operation: "feat(kda): add CuTe DSL recurrent prefill backend" -- packed
+// documents delimited by cu_seqlens, each (document, head) chain runs the
+// gated delta-rule recurrence over its tokens from an optional initial state
+// and leaves its final state in the pool; the work is chunked (BT = 16 on
+// that page) into an intra-chunk preparation and a sequential chain over
+// chunks. The result equals the token-by-token recurrence.
+//
+// Chunkwise form used here (WY representation of the delta rule with the
+// decay carried per key channel; Yang et al., "Parallelizing Linear
+// Transformers with the Delta Rule over Sequence Length", 2024). For a chunk
+// of c <= 16 tokens r entering with state S (S[v][k]: value channel v, key
+// channel k), Gam_r = g_0 + ... + g_r per key channel:
+//   A[r,j] = sum_k k_r k_j exp(Gam_r - Gam_j)         (j < r)
+//   P[r,j] = sum_k q_r k_j exp(Gam_r - Gam_j)         (j <= r)
+//   W_r    = beta_r (exp(Gam_r) k_r - sum_{j<r} A[r,j] W_j)
+//   U0_r   = beta_r (v_r - sum_{j<r} A[r,j] U0_j)
+//   U      = U0 - W S^T         (rows are the per-token corrections u_r)
+//   O      = scale ((exp(Gam) q) S^T + P U)
+//   S      = S diag(exp(Gam_c)) + U^T (exp(Gam_c - Gam) k)
+// Every weight exp(Gam_r - Gam_j) of A and P factors into
+// exp(Gam_r - m) * exp(m - Gam_j) with m = Gam_last / 2 per key channel: over
+// 16 tokens |Gam_r - m| <= 8 |lower_bound| <= 44 (the host requires
+// |lower_bound| <= 5.5), so both factors, and a key channel scaled by either,
+// stay far from fp32 overflow and from denormals. W is solved for the
+// right-hand side exp(Gam_r - m) k_r and scaled by exp(m) afterwards (the solve
+// is linear per key channel).
+//
+// One 256-thread workgroup owns one (document, head) chain; documents are
+// taken longest first. Wave w owns value channels 32w .. 32w+31 of the
+// fp32 state, kept in registers in the MFMA accumulator layout (16 tiles of
+// 16 x 16, tile (mt, nt) holding key channels 16mt + 4*(lane/16) + i and
+// value channel 32w + 16nt + lane%16). Per chunk:
+//  * the token prologue (norms, gate, beta) and the prefix / exp rows run on
+//    the VALU in fp32, A and P on v_mfma_f32_16x16x32_bf16 with bf16 hi/lo
+//    operand splits, the two 16 x 16 triangular solves on the VALU in fp32;
+//  * the chain multiplies W and exp(Gam) q by the state on
+//    v_mfma_f32_16x16x32_bf16 reading the state straight from the
+//    accumulators (the B fragment's 8 key channels are taken as two runs of
+//    4 from two accumulator tiles; the A fragments use the same order), with
+//    three hi/lo terms for W S^T and one for the read-out; U comes out in the
+//    accumulator layout, which is exactly the B fragment of
+//    v_mfma_f32_16x16x16_bf16 with the chunk's tokens as the contraction, so
+//    P U and the state update U^T K~ take it without any data movement;
+//  * the next chunk's token inputs are loaded into registers while the
+//    current chunk runs.
+
 #include "kda_common.h"
 #include "kda_launch.h"
+
 namespace kda {
-size_t prefill_workspace_bytes(int32_t, int64_t, int32_t) { return 0; }
-hipError_t launch_prefill(const PrefillParams&, const int32_t*, bool, hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));  // bf16 operands of the K = 16 MFMA
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int C = 16;          // tokens per chunk
+constexpr int XLD = D + 8;     // padded row (bf16) of the [token][key] operand tiles
+constexpr int TLD = C + 4;     // padded row (bf16) of the [key][token] operand tile
+constexpr int kMaxOrderedDocs = 256;
+
+struct DocOrder {
+  int32_t n;  // 0: natural order
+  int32_t doc[kMaxOrderedDocs];
+};
+
+struct PSmem {
+  float* qh;     // [C][D] q_hat, then exp(Gam - m) q_hat
+  float* kh;     // [C][D] k_hat, then exp(Gam - m) k_hat
+  float* gg;     // [C][D] g, then exp(m - Gam) k_hat
+  float* vv;     // [C][D] v
+  float* u0;     // [C][D] U0
+  float* am;     // [C][C] A
+  float* beta;   // [C]
+  float* egl;    // [D] exp(Gam_last)
+  float* em;     // [D] exp(Gam_last / 2)
+  uint16_t* wop;   // [2][C][XLD] W, bf16 hi / lo
+  uint16_t* qop;   // [C][XLD] exp(Gam) q_hat, bf16
+  uint16_t* ktop;  // [2][D][TLD] (exp(Gam_last - Gam) k_hat)^T, bf16 hi / lo
+  uint16_t* pop;   // [C][C] P, bf16
+};
+
+constexpr size_t kPrefillLds =
+    size_t(5 * C * D + C * C + C + 2 * D) * 4 + size_t(2 * C * XLD + C * XLD + 2 * D * TLD + C * C) * 2;
+
+__device__ inline PSmem pcarve(float* base) {
+  PSmem s;
+  float* p = base;
+  s.qh = p; p += C * D;
+  s.kh = p; p += C * D;
+  s.gg = p; p += C * D;
+  s.vv = p; p += C * D;
+  s.u0 = p; p += C * D;
+  s.am = p; p += C * C;
+  s.beta = p; p += C;
+  s.egl = p; p += D;
+  s.em = p; p += D;
+  uint16_t* b = reinterpret_cast<uint16_t*>(p);
+  s.wop = b; b += 2 * C * XLD;
+  s.qop = b; b += C * XLD;
+  s.ktop = b; b += 2 * D * TLD;
+  s.pop = b;
+  return s;
 }
+
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = to_bf16(x);
+  lo = to_bf16(x - bf1(hi));
+}
+
+// 8 fp32 -> bf16x8 hi and lo parts.
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+    const float r0 = x[2 * e] - bf_lo(h[e]);
+    const float r1 = x[2 * e + 1] - bf_hi(h[e]);
+    l[e] = pack_bf16x2(r0, r1);
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
+__device__ __forceinline__ void split4(const f32x4 x, s16x4& hi, s16x4& lo) {
+  u32x2 h, l;
+  h[0] = pack_bf16x2(x[0], x[1]);
+  h[1] = pack_bf16x2(x[2], x[3]);
+  l[0] = pack_bf16x2(x[0] - bf_lo(h[0]), x[1] - bf_hi(h[0]));
+  l[1] = pack_bf16x2(x[2] - bf_lo(h[1]), x[3] - bf_hi(h[1]));
+  hi = __builtin_bit_cast(s16x4, h);
+  lo = __builtin_bit_cast(s16x4, l);
+}
+
+__device__ __forceinline__ bf16x8 lds_bf16x8_2runs(const uint16_t* p0, const uint16_t* p1) {
+  const u32x2 a = *reinterpret_cast<const u32x2*>(p0);
+  const u32x2 b = *reinterpret_cast<const u32x2*>(p1);
+  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+
+template <bool VEC>
+__device__ __forceinline__ u32x2 gload4(const uint16_t* p) {
+  if constexpr (VEC) {
+    return *reinterpret_cast<const u32x2*>(p);
+  } else {
+    return u32x2{uint32_t(p[0]) | (uint32_t(p[1]) << 16), uint32_t(p[2]) | (uint32_t(p[3]) << 16)};
+  }
+}
+
+template <bool VEC>
+__device__ __forceinline__ void gstore4(uint16_t* p, u32x2 w) {
+  if constexpr (VEC) {
+    *reinterpret_cast<u32x2*>(p) = w;
+  } else {
+    p[0] = uint16_t(w[0] & 0xffffu);
+    p[1] = uint16_t(w[0] >> 16);
+    p[2] = uint16_t(w[1] & 0xffffu);
+    p[3] = uint16_t(w[1] >> 16);
+  }
+}
+
+// Raw token inputs of one lane: 8 channels of q, k, g, v and the beta logit.
+struct TokRaw {
+  u32x4 q, k, g, v;
+  uint16_t b;
+};
+
+template <bool VEC>
+__device__ __forceinline__ TokRaw load_tok(const PrefillParams& p, int64_t t, int h, int c0,
+                                           bool valid) {
+  TokRaw r;
+  if (valid) {
+    r.q = load8_raw<VEC>(p.q + t * p.q_tok_stride + h * D + c0);
+    r.k = load8_raw<VEC>(p.k + t * p.k_tok_stride + h * D + c0);
+    r.g = load8_raw<VEC>(p.g + t * p.g_tok_stride + h * D + c0);
+    r.v = load8_raw<VEC>(p.v + t * p.v_tok_stride + h * D + c0);
+    r.b = p.beta[t * p.beta_tok_stride + h];
+  } else {
+    r.q = r.k = r.g = r.v = u32x4{0u, 0u, 0u, 0u};
+    r.b = 0;
+  }
+  return r;
+}
+
+}  // namespace
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder ord) {
+  extern __shared__ __align__(16) float psmem_raw[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g4 = lane >> 4;     // lane group inside a wave
+  const int n16 = lane & 15;
+  const int h = int(blockIdx.x % p.H);
+  const int rank = int(blockIdx.x / p.H);
+  const int doc = ord.n > 0 ? ord.doc[rank] : rank;
+  const int64_t t0 = p.cu_seqlens[doc];
+  const int64_t len = int64_t(p.cu_seqlens[doc + 1]) - t0;
+  const int32_t slot = p.state_indices[doc];
+  const bool active = slot >= 0 && int64_t(slot) < p.num_slots;
+
+  if (!active) {  // zero outputs, no state access
+    for (int64_t e = tid; e < len * D; e += 256)
+      p.out[(t0 + e / D) * p.out_tok_stride + h * D + (e % D)] = 0;
+    return;
+  }
+  uint16_t* sp = p.state_pool + int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS;
+  if (len == 0) {  // final state = initial state: untouched, or zeros without one
+    if (!p.use_initial_state)
+      for (int e = tid; e < HEAD_ELEMS; e += 256) sp[e] = 0;
+    return;
+  }
+  PSmem s = pcarve(psmem_raw);
+
+  // ---- initial state into the accumulator layout
+  f32x4 acc[8][2];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      if (p.use_initial_state) {
+        const int v = 32 * wave + 16 * nt + n16;
+        const u32x2 w = gload4<VEC>(sp + v * D + 16 * mt + 4 * g4);
+        acc[mt][nt] = f32x4{bf_lo(w[0]), bf_hi(w[0]), bf_lo(w[1]), bf_hi(w[1])};
+      } else {
+        acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+
+  const float neg_ea = -expf(p.A_log[h]);
+  const int tt = tid >> 4;           // prologue: token of this lane
+  const int c0 = (tid & 15) * 8;     // prologue: 8 key / value channels of this lane
+  float dtb[8];
+  load8_f32<VEC>(p.dt_bias + h * D + c0, dtb);
+  const int nchunks = int((len + C - 1) / C);
+  TokRaw raw = load_tok<VEC>(p, t0 + tt, h, c0, tt < len);
+
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int64_t tc0 = t0 + int64_t(ch) * C;
+    const int c = int(min<int64_t>(C, len - int64_t(ch) * C));
+
+    // ---- P2: token prologue -> q_hat, k_hat, g, v, beta (rows >= c are zeros)
+    {
+      float q[8], k[8], gr[8], vv[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        q[2 * e] = bf_lo(raw.q[e]);  q[2 * e + 1] = bf_hi(raw.q[e]);
+        k[2 * e] = bf_lo(raw.k[e]);  k[2 * e + 1] = bf_hi(raw.k[e]);
+        gr[2 * e] = bf_lo(raw.g[e]); gr[2 * e + 1] = bf_hi(raw.g[e]);
+        vv[2 * e] = bf_lo(raw.v[e]); vv[2 * e + 1] = bf_hi(raw.v[e]);
+      }
+      const uint16_t braw = raw.b;
+      // prefetch the next chunk's inputs while this one runs
+      if (ch + 1 < nchunks) {
+        const int64_t tn = tc0 + C + tt;
+        raw = load_tok<VEC>(p, tn, h, c0, tn < t0 + len);
+      }
+      const bool valid = tt < c;
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sq = fmaf(q[e], q[e], sq);
+        sk = fmaf(k[e], k[e], sk);
+      }
+      sq = row16_sum(sq);
+      sk = row16_sum(sk);
+      const float rq = 1.0f / sqrtf(sq + 1e-6f);
+      const float rk = 1.0f / sqrtf(sk + 1e-6f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s.qh[tt * D + c0 + e] = q[e] * rq;
+        s.kh[tt * D + c0 + e] = k[e] * rk;
+        s.gg[tt * D + c0 + e] = valid ? gate_logdecay(gr[e] + dtb[e], neg_ea, p.lower_bound) : 0.f;
+        s.vv[tt * D + c0 + e] = vv[e];
+      }
+      if ((tid & 15) == 0) s.beta[tt] = valid ? sigmoidf(bf1(braw)) : 0.f;
+    }
+    __syncthreads();
+
+    // ---- P3: threads 0..127 own key channel c: Gam prefix, the scaled rows
+    // for A and P, and the chain's bf16 operands exp(Gam) q_hat and
+    // (exp(Gam_last - Gam) k_hat)^T.
+    if (tid < 128) {
+      const int cc = tid;
+      float gam[C];
+      float acc_g = 0.f;
+#pragma unroll
+      for (int r = 0; r < C; ++r) {
+        acc_g += s.gg[r * D + cc];
+        gam[r] = acc_g;
+      }
+      const float mid = 0.5f * acc_g;  // padded rows carry g = 0
+      const float em = expf(mid);
+      s.egl[cc] = expf(acc_g);
+      s.em[cc] = em;
+#pragma unroll
+      for (int r = 0; r < C; ++r) {
+        const float ea = expf(gam[r] - mid), eb = expf(mid - gam[r]);
+        const float kh = s.kh[r * D + cc];
+        const float qh = s.qh[r * D + cc];
+        const float kb = kh * eb;
+        s.qh[r * D + cc] = qh * ea;
+        s.kh[r * D + cc] = kh * ea;
+        s.gg[r * D + cc] = kb;
+        s.qop[r * XLD + cc] = to_bf16(qh * ea * em);
+        uint16_t hi, lo;
+        split_bf16(em * kb, hi, lo);  // exp(Gam_last - m) = exp(m)
+        s.ktop[cc * TLD + r] = hi;
+        s.ktop[D * TLD + cc * TLD + r] = lo;
+      }
+    }
+    __syncthreads();
+
+    // ---- P4: A = (e^(Gam-m) k)(e^(m-Gam) k)^T on wave 0, P = (e^(Gam-m) q)(e^(m-Gam) k)^T on
+    // wave 1 (three hi/lo terms each); lane (row m = lane%16, group g4).
+    if (wave < 2) {
+      const float* left = wave == 0 ? s.kh : s.qh;
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        float x[8], y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[e] = left[n16 * D + 32 * kt + 8 * g4 + e];
+          y[e] = s.gg[n16 * D + 32 * kt + 8 * g4 + e];
+        }
+        bf16x8 xh, xl, yh, yl;
+        split8(x, xh, xl);
+        split8(y, yh, yl);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yh, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yl, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, yh, a, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i, j = n16;
+        if (wave == 0) s.am[r * C + j] = j < r ? a[i] : 0.f;
+        else s.pop[r * C + j] = to_bf16(j <= r ? a[i] : 0.f);
+      }
+    }
+    __syncthreads();
+
+    // ---- P5: forward substitution. Threads 0..127: W (key channel c),
+    // stored as bf16 hi / lo; threads 128..255: U0 (value channel v).
+    {
+      const int cc = tid & 127;
+      const float* rhs = tid < 128 ? s.kh : s.vv;
+      float x[C];
+#pragma unroll
+      for (int r = 0; r < C; ++r) {
+        float y = rhs[r * D + cc];
+#pragma unroll
+        for (int j = 0; j < r; ++j) y = fmaf(-s.am[r * C + j], x[j], y);
+        x[r] = s.beta[r] * y;
+      }
+      if (tid < 128) {
+        const float em = s.em[cc];
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+          uint16_t hi, lo;
+          split_bf16(x[r] * em, hi, lo);
+          s.wop[r * XLD + cc] = hi;
+          s.wop[C * XLD + r * XLD + cc] = lo;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < C; ++r) s.u0[r * D + cc] = x[r];
+      }
+    }
+    __syncthreads();
+
+    // ---- chain for this wave's 32 value channels
+    f32x4 yw[2], yq[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      yw[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      yq[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int ka = 32 * kt + 4 * g4, kb2 = ka + 16;
+      const bf16x8 whi = lds_bf16x8_2runs(s.wop + n16 * XLD + ka, s.wop + n16 * XLD + kb2);
+      const bf16x8 wlo = lds_bf16x8_2runs(s.wop + C * XLD + n16 * XLD + ka,
+                                          s.wop + C * XLD + n16 * XLD + kb2);
+      const bf16x8 qhi = lds_bf16x8_2runs(s.qop + n16 * XLD + ka, s.qop + n16 * XLD + kb2);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const f32x4 s0 = acc[2 * kt][nt], s1 = acc[2 * kt + 1][nt];
+        const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+        bf16x8 shi, slo;
+        split8(sv, shi, slo);
+        yw[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, shi, yw[nt], 0, 0, 0);
+        yw[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, slo, yw[nt], 0, 0, 0);
+        yw[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, shi, yw[nt], 0, 0, 0);
+        yq[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi, shi, yq[nt], 0, 0, 0);
+      }
+    }
+    // U = U0 - W S^T (accumulator layout: rows 4*g4 + i, value channel of the lane)
+    s16x4 uhi[2], ulo[2];
+    const s16x4 pfr = __builtin_bit_cast(
+        s16x4, *reinterpret_cast<const u32x2*>(s.pop + n16 * C + 4 * g4));
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int v = 32 * wave + 16 * nt + n16;
+      f32x4 u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[i] = s.u0[(4 * g4 + i) * D + v] - yw[nt][i];
+      split4(u, uhi[nt], ulo[nt]);
+      // O = scale ((e^Gam q) S^T + P U)
+      f32x4 o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pfr, uhi[nt], yq[nt], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i;
+        if (r < c) p.out[(tc0 + r) * p.out_tok_stride + h * D + v] = to_bf16(p.scale * o[i]);
+      }
+    }
+    // S = S diag(e^Gam_last) + U^T K~  (contraction over the chunk's tokens)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const int kr = 16 * mt + n16;  // key channel of this lane's A-fragment row
+      const s16x4 khi = __builtin_bit_cast(
+          s16x4, *reinterpret_cast<const u32x2*>(s.ktop + kr * TLD + 4 * g4));
+      const s16x4 klo = __builtin_bit_cast(
+          s16x4, *reinterpret_cast<const u32x2*>(s.ktop + D * TLD + kr * TLD + 4 * g4));
+      float e4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e4[i] = s.egl[16 * mt + 4 * g4 + i];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        f32x4 a = acc[mt][nt];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] *= e4[i];
+        a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(khi, uhi[nt], a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(khi, ulo[nt], a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(klo, uhi[nt], a, 0, 0, 0);
+        acc[mt][nt] = a;
+      }
+    }
+    // the next chunk's P2 rewrites only qh / kh / gg / vv / beta, which the
+    // chain does not read; its P3 (after the next barrier) rewrites the chain's
+    // operands.
+  }
+
+  // ---- final state
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int v = 32 * wave + 16 * nt + n16;
+      const f32x4 a = acc[mt][nt];
+      gstore4<VEC>(sp + v * D + 16 * mt + 4 * g4,
+                   u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])});
+    }
+}
+
+size_t prefill_workspace_bytes(int32_t, int64_t, int32_t) { return 0; }
+
+hipError_t launch_prefill(const PrefillParams& p, const int32_t* cu_host, bool vec,
+                          hipStream_t stream) {
+  const int64_t blocks = int64_t(p.n_docs) * p.H;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  // Longest documents first: their chains bound the makespan.
+  DocOrder ord;
+  ord.n = 0;
+  if (p.n_docs <= kMaxOrderedDocs) {
+    ord.n = p.n_docs;
+    for (int d = 0; d < p.n_docs; ++d) ord.doc[d] = d;
+    for (int i = 1; i < p.n_docs; ++i) {  // stable insertion sort, descending length
+      const int d = ord.doc[i];
+      const int32_t ld = cu_host[d + 1] - cu_host[d];
+      int j = i - 1;
+      while (j >= 0 && cu_host[ord.doc[j] + 1] - cu_host[ord.doc[j]] < ld) {
+        ord.doc[j + 1] = ord.doc[j];
+        --j;
+      }
+      ord.doc[j + 1] = d;
+    }
+  }
+  static const hipError_t attr = [] {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(kPrefillLds));
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(kPrefillLds));
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
+  dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  if (vec) hipLaunchKernelGGL((prefill_kernel<true>), grid, block, kPrefillLds, stream, p, ord);
+  else hipLaunchKernelGGL((prefill_kernel<false>), grid, block, kPrefillLds, stream, p, ord);
+  return hipGetLastError();
+}
+
 }  // namespace kda

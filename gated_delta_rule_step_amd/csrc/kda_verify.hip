@@ -527,7 +527,7 @@ hipError_t launch_verify(const VerifyParams& p, bool vec, hipStream_t stream) {
   const int hm = p.w_ring - p.T;  // history capacity: hist + T <= w_ring
   const size_t lds = smem_bytes(hm);
   // exp(Gam_r) * exp(-Gam_j) stays finite when |Gam| <= T * |lower_bound| < 80.
-  const bool fact = p.lower_bound > -80.0f / float(p.T);
+  const bool fact = p.lower_bound > -80.0f / float(p.T) && p.lower_bound <= 0.0f;
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
   if (vec) {
     if (fact) hipLaunchKernelGGL((verify_kernel<true, true>), grid, block, lds, stream, p, hm);

@@ -126,12 +126,12 @@ def test_prefill_workspace_and_validation(lib):
     assert lib.kda_prefill_workspace_size(4, 13888, 64, 64, 128) == 0
 
     def call(cu, total, **kw):
-        a = dict(n=len(cu) - 1, H=2, K=128, ws=1 << 40, ots=256)
+        a = dict(n=len(cu) - 1, H=2, K=128, ws=1 << 40, ots=256, lb=-5.0)
         a.update(kw)
         arr = (ctypes.c_int32 * len(cu))(*cu)
         p = P(1 << 20)
         return lib.kda_prefill_varlen(a["n"], total, a["H"], a["K"], 128, arr, p, p, 256, p,
-                                      256, p, 256, p, 256, p, 2, p, p, -5.0, 1.0, p, 4,
+                                      256, p, 256, p, 256, p, 2, p, p, a["lb"], 1.0, p, 4,
                                       2 * 128 * 128, p, 1, p, a["ots"], p, a["ws"], P(0))
 
     assert call([1, 5], 5) == SEQ       # must start at 0
@@ -139,4 +139,7 @@ def test_prefill_workspace_and_validation(lib):
     assert call([0, 5, 7], 9) == SEQ    # must end at total_tokens
     assert call([0, 5], 5, K=64) == UNSUP
     assert call([0, 5], 5, ots=8) == STRIDE
+    # 16-token chunks need |lower_bound| <= 5.5 (each decay factor within e^44)
+    assert call([0, 5], 5, lb=-5.6) == UNSUP
+    assert call([0, 5], 5, lb=float("nan")) == UNSUP
     assert call([0], 0) == OK           # no documents: nothing to do

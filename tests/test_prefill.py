@@ -1,0 +1,202 @@
+"""GPU parity of kda_prefill_varlen against the CPU oracle's token-by-token
+recurrence, through the C ABI.
+
+Operation: "feat(kda): add CuTe DSL recurrent prefill backend" -- packed
+documents delimited by cu_seqlens, optional initial states from a bf16 pool
+addressed by state indices, per-token outputs and final states; the chunked
+result must equal the token-by-token recurrence.
+"""
+import numpy as np
+import pytest
+
+from gated_delta_rule_step_amd import synth
+from tests.helpers import HD, bits, check_out, check_state, dev, dev_bf16, f32
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _kda():
+    import gated_delta_rule_step_amd as kda
+    return kda
+
+
+def run_prefill(case, pool=None, packed=False, use_initial_state=None, lower_bound=None):
+    """Launch kda_prefill_varlen on a case. packed: q/k/v are strided views of
+    one [Ttot, 3*H*128] buffer and out is a view with a padded row."""
+    H, Ttot = case["H"], case["Ttot"]
+    W = H * HD
+    if packed:
+        qkv = np.concatenate([case["q"].reshape(Ttot, W), case["k"].reshape(Ttot, W),
+                              case["v"].reshape(Ttot, W)], axis=1)
+        qkv_d = dev_bf16(qkv)
+        q, k, v = qkv_d[:, :W], qkv_d[:, W:2 * W], qkv_d[:, 2 * W:]
+        out_buf = torch.full((Ttot, W + 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+        out = out_buf[:, :W]
+    else:
+        q, k, v = (dev_bf16(case[n].reshape(Ttot, W)) for n in ("q", "k", "v"))
+        out = torch.full((Ttot, W), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pool = dev_bf16(case["pool"]) if pool is None else pool
+    cu_h = torch.from_numpy(case["cu_seqlens"].copy())
+    uis = case["use_initial_state"] if use_initial_state is None else use_initial_state
+    _kda().kda_prefill_varlen(cu_h, dev(case["cu_seqlens"]), q, k, v, dev_bf16(case["gate"]),
+                              dev_bf16(case["beta"]), dev(case["a_log"]), dev(case["dt_bias"]),
+                              pool, dev(case["idx"]), out, use_initial_state=uis,
+                              lower_bound=case["lower_bound"] if lower_bound is None
+                              else lower_bound, scale=case["scale"])
+    return pool, out
+
+
+def oracle_prefill(orc, case, heads=None, use_initial_state=None, lower_bound=None):
+    """fp32 token-by-token oracle over the heads listed (all by default).
+    Returns (out [Ttot, nh, 128], pool [N, nh, 128, 128] float32 after the run)."""
+    H, Ttot = case["H"], case["Ttot"]
+    hs = np.arange(H) if heads is None else np.asarray(heads)
+    q = f32(case["q"])[:, hs]
+    k = f32(case["k"])[:, hs]
+    v = f32(case["v"])[:, hs]
+    g = f32(case["gate"]).reshape(Ttot, H, HD)[:, hs]
+    b = f32(case["beta"])[:, hs]
+    pool = f32(case["pool"])[:, hs]
+    uis = case["use_initial_state"] if use_initial_state is None else use_initial_state
+    lb = case["lower_bound"] if lower_bound is None else lower_bound
+    c = np.ascontiguousarray
+    pool = c(pool)
+    out = orc.prefill(case["cu_seqlens"], c(q), c(k), c(v), c(g), c(b), c(case["a_log"][hs]),
+                      c(case["dt_bias"].reshape(H, HD)[hs]), lb, case["scale"], pool,
+                      case["idx"], use_initial_state=uis, bf16_storage=True, real=np.float32)
+    return out, pool
+
+
+def check_prefill(orc, case, pool_dev, out_dev, heads=None, use_initial_state=None,
+                  lower_bound=None):
+    H, Ttot, N = case["H"], case["Ttot"], case["N"]
+    hs = np.arange(H) if heads is None else np.asarray(heads)
+    ref_out, ref_pool = oracle_prefill(orc, case, heads, use_initial_state, lower_bound)
+    torch.cuda.synchronize()
+    got_out = bits(out_dev).reshape(Ttot, H, HD)[:, hs]
+    got_pool = bits(pool_dev)
+    idx = case["idx"].astype(np.int64)
+    active = (idx >= 0) & (idx < N)
+    cu = case["cu_seqlens"]
+    for d in range(case["n_docs"]):
+        t0, t1 = cu[d], cu[d + 1]
+        if active[d]:
+            if t1 > t0:
+                check_out(got_out[t0:t1], ref_out[t0:t1], f"prefill output doc {d}")
+            check_state(got_pool[idx[d]][hs], ref_pool[idx[d]], f"prefill state doc {d}")
+        else:
+            assert np.all(got_out[t0:t1] == 0), f"inactive doc {d} must output +0.0"
+    touched = np.zeros(N, bool)
+    touched[idx[active]] = True
+    assert np.array_equal(got_pool[~touched], case["pool"][~touched]), \
+        "slots of inactive documents or unused slots changed"
+
+
+# ---------------------------------------------------------------------------
+# small cases: every chunk boundary, ragged tails, zero-length documents
+
+SMALL_DOCS = (1, 15, 16, 17, 0, 33, 50, 2, 64, 31)
+
+
+@pytest.mark.parametrize("H", [1, 3])
+def test_small_docs_ragged(orc, H):
+    case = synth.prefill_case(SMALL_DOCS, H=H, seed=synth.seed_for(4, H, 1))
+    pool, out = run_prefill(case)
+    check_prefill(orc, case, pool, out)
+
+
+def test_single_token_doc(orc):
+    """One token, one head: the prefill equals one decode step."""
+    case = synth.prefill_case((1,), H=1, seed=synth.seed_for(4, 1, 2))
+    pool, out = run_prefill(case)
+    check_prefill(orc, case, pool, out)
+
+
+def test_no_initial_state(orc):
+    """use_initial_state = 0: chains start from zeros; a zero-length document
+    leaves a zero state in its slot."""
+    case = synth.prefill_case((20, 0, 37, 16), H=2, seed=synth.seed_for(4, 2, 3),
+                              use_initial_state=False)
+    pool, out = run_prefill(case)
+    check_prefill(orc, case, pool, out)
+    z = case["idx"][1]
+    assert np.all(bits(pool)[z] == 0), "zero-length document without initial state: zeros"
+
+
+def test_zero_length_keeps_state(orc):
+    """use_initial_state = 1: a zero-length document leaves its slot bitwise."""
+    case = synth.prefill_case((0, 5, 0), H=2, seed=synth.seed_for(4, 2, 4))
+    pool, out = run_prefill(case)
+    check_prefill(orc, case, pool, out)
+    for d in (0, 2):
+        s = case["idx"][d]
+        assert np.array_equal(bits(pool)[s], case["pool"][s])
+
+
+def test_inactive_docs(orc):
+    """Documents whose slot is -1 or >= N: zero outputs, pool untouched."""
+    case = synth.prefill_case((18, 40, 7, 23), H=2, seed=synth.seed_for(4, 2, 5),
+                              inactive_docs=(1,))
+    case["idx"][3] = case["N"] + 5
+    pool, out = run_prefill(case)
+    check_prefill(orc, case, pool, out)
+
+
+def test_packed_views_and_padded_out(orc):
+    """q / k / v as strided views of one packed row, out with a padded row."""
+    case = synth.prefill_case((29, 16, 3), H=2, seed=synth.seed_for(4, 2, 6))
+    pool, out = run_prefill(case, packed=True)
+    check_prefill(orc, case, pool, out)
+
+
+def test_many_docs_natural_order(orc):
+    """More documents than the launch orders by length (300)."""
+    rng = np.random.Generator(np.random.PCG64(synth.seed_for(4, 1, 7)))
+    lens = tuple(int(x) for x in rng.integers(0, 24, size=300))
+    case = synth.prefill_case(lens, H=1, seed=synth.seed_for(4, 1, 8))
+    pool, out = run_prefill(case)
+    check_prefill(orc, case, pool, out)
+
+
+@pytest.mark.parametrize("lb", [-5.5, -1.0, 0.0])
+def test_lower_bound_range(orc, lb):
+    """The accepted range of lower_bound, including its end (|lb| = 5.5)."""
+    case = synth.prefill_case((40, 9), H=2, seed=synth.seed_for(4, 2, 9))
+    case["a_log"] = np.full_like(case["a_log"], 1.0)  # strong decay: the clamp is active
+    pool, out = run_prefill(case, lower_bound=lb)
+    check_prefill(orc, case, pool, out, lower_bound=lb)
+
+
+def test_lower_bound_rejected():
+    case = synth.prefill_case((4,), H=1, seed=synth.seed_for(4, 1, 10))
+    with pytest.raises(_kda().KdaError):
+        run_prefill(case, lower_bound=-6.0)
+
+
+def test_deterministic(orc):
+    case = synth.prefill_case((70, 33), H=2, seed=synth.seed_for(4, 2, 11))
+    _, out1 = run_prefill(case)
+    pool2, out2 = run_prefill(case)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out1), bits(out2))
+
+
+# ---------------------------------------------------------------------------
+# full sizes: 4 documents (3840, 3776, 3200, 3072) and the 14-document mix
+# (16384 tokens each), H = 12 (all heads) and H = 64 (sampled heads)
+
+@pytest.mark.parametrize("docs", ["docs4", "docs14"])
+def test_full_h12(orc, docs):
+    lens = synth.DOCS_4 if docs == "docs4" else synth.DOCS_14
+    case = synth.prefill_case(lens, H=12)
+    pool, out = run_prefill(case)
+    check_prefill(orc, case, pool, out)
+
+
+@pytest.mark.parametrize("docs", ["docs4", "docs14"])
+def test_full_h64_sampled_heads(orc, docs):
+    lens = synth.DOCS_4 if docs == "docs4" else synth.DOCS_14
+    case = synth.prefill_case(lens, H=64)
+    pool, out = run_prefill(case)
+    check_prefill(orc, case, pool, out, heads=[0, 9, 21, 33, 47, 63])

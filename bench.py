@@ -16,10 +16,13 @@ milliseconds of sustained load ~10-15% slower.
 The line also carries the roofline of the decode kernel (algorithmic bytes
 per call / average duration, against 8 TB/s), the CPU oracle timed on this
 host, and further measured points under "points": the decode batch sweep and
-the verify workloads (T = 8 / 4, bare checkpoint, fold rates, deep window).
+the verify workloads (T = 8 / 4, bare checkpoint, fold rates, deep window)
+and the varlen prefill workloads (4 documents and the 14-document mix of
+16384 tokens, H = 64 and 12).
 
 --mode profile runs a short fixed sequence (decode B = 512, verify T = 8
-B = 512, and a known-size device copy for counter calibration) for rocprofv3.
+B = 512, and a known-size device copy for counter calibration) for rocprofv3;
+--mode profile-prefill runs 4 prefill calls on each H = 64 document set.
 """
 from __future__ import annotations
 
@@ -80,7 +83,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--points", choices=["all", "none"], default="all",
                     help="also measure the decode sweep and the verify points")
-    ap.add_argument("--mode", choices=["bench", "profile"], default="bench")
+    ap.add_argument("--mode", choices=["bench", "profile", "profile-prefill"], default="bench")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     return ap.parse_args()
@@ -247,6 +250,45 @@ def make_rings(torch, synth):
     return rings
 
 
+class PrefillSetup:
+    """Prefill workload: packed documents of the given lengths, H heads,
+    inputs drawn on the device from a seeded generator with the same
+    distributions as the test cases (q, k, v, gate, beta logits N(0, 1),
+    A_log U(-1, 1), dt_bias N(0, 0.1), initial states N(0, 0.05) in a pool of
+    2 slots per document)."""
+
+    def __init__(self, lens, H, torch, kda, synth):
+        self.lens, self.H = tuple(lens), H
+        n_docs, T, W = len(lens), int(sum(lens)), H * 128
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(synth.seed_for(4, H, n_docs))
+
+        def randn(*shape, std=1.0):
+            x = torch.randn(*shape, generator=gen, device="cuda", dtype=torch.float32)
+            return (x * std).to(torch.bfloat16)
+        self.q, self.k, self.v, self.g = (randn(T, W) for _ in range(4))
+        self.beta = randn(T, H)
+        self.a_log = torch.rand(H, generator=gen, device="cuda") * 2.0 - 1.0
+        self.dtb = torch.randn(H * 128, generator=gen, device="cuda") * 0.1
+        N = 2 * n_docs
+        self.pool = randn(N, H, 128, 128, std=0.05)
+        self.idx = torch.randperm(N, generator=gen, device="cuda")[:n_docs].to(torch.int32)
+        cu = np.zeros(n_docs + 1, np.int32)
+        cu[1:] = np.cumsum(lens)
+        self.cu_h = torch.from_numpy(cu)
+        self.cu_d = self.cu_h.cuda()
+        self.out = torch.empty((T, W), dtype=torch.bfloat16, device="cuda")
+        self.kda = kda
+
+    def calls(self):
+        s = self
+
+        def call():
+            s.kda.kda_prefill_varlen(s.cu_h, s.cu_d, s.q, s.k, s.v, s.g, s.beta, s.a_log, s.dtb,
+                                     s.pool, s.idx, s.out)
+        return [call]
+
+
 def cpu_baseline_decode(B, budget_s, synth):
     """The CPU oracle on the same decode workload: one full B-row call per
     run; runs repeat until the budget is used (at least one)."""
@@ -322,6 +364,15 @@ def main():
     if args.mode == "profile":
         run_profile(torch, kda, synth, pools)
         return
+    if args.mode == "profile-prefill":
+        for lens in (synth.DOCS_4, synth.DOCS_14):
+            ps = PrefillSetup(lens, 64, torch, kda, synth)
+            for c in ps.calls() * 4:
+                c()
+            torch.cuda.synchronize()
+            del ps
+        log("profile: 4 x prefill H=64 4 docs, 4 x prefill H=64 14-doc mix")
+        return
 
     B = 512
     setup = DecodeSetup(B, torch, kda, synth, pools)
@@ -379,6 +430,26 @@ def main():
                 del vs
         del rings
         torch.cuda.empty_cache()
+        for name, lens in (("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4),
+                           ("14-doc mix, 16384 tokens", synth.DOCS_14)):
+            for Hp in (64, 12):
+                ps = PrefillSetup(lens, Hp, torch, kda, synth)
+                st = max(10, min(args.steps, 50))
+                _, e = time_graphs(ps.calls(), st, 2, torch, min_warm_s=0.3)
+                us = e * 1e3 / st
+                nb = wm.prefill_bytes(lens, Hp)
+                fl = wm.prefill_flops(lens, Hp)
+                points.append(dict(kind="prefill", H=Hp, docs=name, tokens=int(sum(lens)),
+                                   us_per_call=round(us, 1),
+                                   Mtok_per_s=round(sum(lens) / (us * 1e-6) / 1e6, 2),
+                                   GBps=round(nb / (us * 1e-6) / 1e9, 1),
+                                   hbm_frac=round(nb / (us * 1e-6) / 1e9 / wm.HBM_PEAK_GBS, 4),
+                                   TFLOPs=round(fl / (us * 1e-6) / 1e12, 2),
+                                   mfma_frac=round(fl / (us * 1e-6) / 1e12
+                                                   / wm.BF16_MFMA_PEAK_TFLOPS, 4)))
+                log(f"bench: {points[-1]}")
+                del ps
+                torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:

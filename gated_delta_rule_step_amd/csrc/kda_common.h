@@ -115,4 +115,15 @@ __device__ __forceinline__ float gate_logdecay(float x, float neg_exp_alog, floa
 }
 __device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// The same pieces on the hardware transcendentals (v_exp_f32 / v_log_f32,
+// base 2, ~1 ulp), for the kernels whose prologue sits on the critical path.
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
+__device__ __forceinline__ float fgate(float x, float neg_exp_alog, float lb) {
+  const float sp = x > 20.0f ? x : LN2 * __builtin_amdgcn_logf(1.0f + fexp(x));
+  return fmaxf(lb, neg_exp_alog * sp);
+}
+__device__ __forceinline__ float fsigmoid(float x) { return 1.0f / (1.0f + fexp(-x)); }
+
 }  // namespace kda

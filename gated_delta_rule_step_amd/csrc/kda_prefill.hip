@@ -69,9 +69,10 @@ struct DocOrder {
 struct PSmem {
   float* qh;     // [C][D] q_hat, then exp(Gam - m) q_hat
   float* kh;     // [C][D] k_hat, then exp(Gam - m) k_hat
-  float* gg;     // [C][D] g, then exp(m - Gam) k_hat
+  float* gg;     // [C][D] g
   float* vv;     // [C][D] v
   float* u0;     // [C][D] U0
+  float* kb;     // [C][D] exp(m - Gam) k_hat, in the U0 rows (dead by the time U0 is solved)
   float* am;     // [C][C] A
   float* beta;   // [C]
   float* egl;    // [D] exp(Gam_last)
@@ -93,6 +94,7 @@ __device__ inline PSmem pcarve(float* base) {
   s.gg = p; p += C * D;
   s.vv = p; p += C * D;
   s.u0 = p; p += C * D;
+  s.kb = s.u0;
   s.am = p; p += C * C;
   s.beta = p; p += C;
   s.egl = p; p += D;
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
       }
     }
 
-  const float neg_ea = -expf(p.A_log[h]);
+  const float neg_ea = -fexp(p.A_log[h]);
   const int tt = tid >> 4;           // prologue: token of this lane
   const int c0 = (tid & 15) * 8;     // prologue: 8 key / value channels of this lane
   float dtb[8];
@@ -273,18 +275,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
       for (int e = 0; e < 8; ++e) {
         s.qh[tt * D + c0 + e] = q[e] * rq;
         s.kh[tt * D + c0 + e] = k[e] * rk;
-        s.gg[tt * D + c0 + e] = valid ? gate_logdecay(gr[e] + dtb[e], neg_ea, p.lower_bound) : 0.f;
+        s.gg[tt * D + c0 + e] = valid ? fgate(gr[e] + dtb[e], neg_ea, p.lower_bound) : 0.f;
         s.vv[tt * D + c0 + e] = vv[e];
       }
-      if ((tid & 15) == 0) s.beta[tt] = valid ? sigmoidf(bf1(braw)) : 0.f;
+      if ((tid & 15) == 0) s.beta[tt] = valid ? fsigmoid(bf1(braw)) : 0.f;
     }
     __syncthreads();
 
-    // ---- P3: threads 0..127 own key channel c: Gam prefix, the scaled rows
-    // for A and P, and the chain's bf16 operands exp(Gam) q_hat and
-    // (exp(Gam_last - Gam) k_hat)^T.
-    if (tid < 128) {
-      const int cc = tid;
+    // ---- P3: thread (c, half) owns key channel c = tid % 128 and tokens
+    // 8 half .. 8 half + 7: Gam prefix (every thread sums all 16 gates of its
+    // channel), the scaled rows for A and P, and the chain's bf16 operands
+    // exp(Gam) q_hat and (exp(Gam_last - Gam) k_hat)^T.
+    {
+      const int cc = tid & 127;
+      const int r0 = (tid >> 7) * 8;
       float gam[C];
       float acc_g = 0.f;
 #pragma unroll
@@ -293,18 +297,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
         gam[r] = acc_g;
       }
       const float mid = 0.5f * acc_g;  // padded rows carry g = 0
-      const float em = expf(mid);
-      s.egl[cc] = expf(acc_g);
-      s.em[cc] = em;
+      const float em = fexp(mid);
+      if (r0 == 0) {
+        s.egl[cc] = fexp(acc_g);
+        s.em[cc] = em;
+      }
 #pragma unroll
-      for (int r = 0; r < C; ++r) {
-        const float ea = expf(gam[r] - mid), eb = expf(mid - gam[r]);
+      for (int i = 0; i < 8; ++i) {
+        const int r = r0 + i;
+        const float gr_ = r0 == 0 ? gam[i] : gam[8 + i];
+        const float ea = fexp(gr_ - mid), eb = fexp(mid - gr_);
         const float kh = s.kh[r * D + cc];
         const float qh = s.qh[r * D + cc];
         const float kb = kh * eb;
         s.qh[r * D + cc] = qh * ea;
         s.kh[r * D + cc] = kh * ea;
-        s.gg[r * D + cc] = kb;
+        s.kb[r * D + cc] = kb;
         s.qop[r * XLD + cc] = to_bf16(qh * ea * em);
         uint16_t hi, lo;
         split_bf16(em * kb, hi, lo);  // exp(Gam_last - m) = exp(m)
@@ -325,7 +333,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           x[e] = left[n16 * D + 32 * kt + 8 * g4 + e];
-          y[e] = s.gg[n16 * D + 32 * kt + 8 * g4 + e];
+          y[e] = s.kb[n16 * D + 32 * kt + 8 * g4 + e];
         }
         bf16x8 xh, xl, yh, yl;
         split8(x, xh, xl);

@@ -48,16 +48,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TMAX = 8;
 constexpr int YLD = D + 4;  // padded fp32 row of the MFMA result (rows 4 apart hit other banks)
-constexpr float LOG2E = 1.4426950408889634f;
-constexpr float LN2 = 0.6931471805599453f;
-
-__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
-
-// max(lb, -exp(A_log) * softplus(x)) with hardware exp / log.
-__device__ __forceinline__ float fgate(float x, float neg_exp_alog, float lb) {
-  const float sp = x > 20.0f ? x : LN2 * __builtin_amdgcn_logf(1.0f + fexp(x));
-  return fmaxf(lb, neg_exp_alog * sp);
-}
 
 // LDS layout (floats unless noted); hm = history capacity (w_ring - T).
 struct Smem {

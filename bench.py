@@ -54,8 +54,8 @@ COUNTED_TRAFFIC = {
         sources=("gated_delta_rule_step_amd/csrc/kda_decode.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h"),
         sha256=("779051e40ebca063e86ddd83f1ed6ed3c5742ee6e5c7f7998eaacfa6ebd2a385",
-                "f4d3b86e655ef4c7e210d1c69ea020bedcc69fc38160058f93dda401a235e509"),
-        fetch_kib=96395.640625, write_kib=188165.890625, fetch_scale=2.0, write_scale=1.0),
+                "34b8100422cba3857f715dc728116de3c64c225b97154059cd0d5945ac5a48f0"),
+        fetch_kib=96395.6484375, write_kib=188166.1875, fetch_scale=2.0, write_scale=1.0),
 }
 
 

@@ -21,6 +21,10 @@ FLAGS = [
     # device code; every FP32 operation runs as a plain VALU instruction.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Xclang", "-flax-vector-conversions=none",
+    # MFMA accumulators live in ordinary VGPRs, not AGPRs: the register file
+    # is shared, and the AGPR block otherwise rounds a kernel's allocation up
+    # past an occupancy step.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),
 ]

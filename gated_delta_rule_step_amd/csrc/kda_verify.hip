@@ -47,64 +47,56 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TMAX = 8;
-constexpr int YLD = D + 4;  // padded fp32 row of the MFMA result (rows 4 apart hit other banks)
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8) for vmcnt(8), the other counters unconstrained: all but
+// the newest 8 vector-memory operations (the checkpoint loads) have completed.
+constexpr int kVmcntBehindCheckpoint = 8 | (7 << 4) | (15 << 8);
+// Token rows (and the MFMA result rows that reuse them) are padded to XS
+// floats: rows 4 apart, or 16 rows read by one fragment load, then fall on
+// different banks.
+constexpr int XS = D + 4;
 
 // LDS layout (floats unless noted); hm = history capacity (w_ring - T).
 struct Smem {
-  float* qa;      // [TMAX][D] q_hat, then exp(Gam) * q_hat           (X rows T..2T-1)
-  float* ka;      // [TMAX][D] k_hat, then exp(Gam) * k_hat, then W    (X rows 0..T-1)
-  float* kb;      // [TMAX][D] g, then Gam, then exp(-Gam) * k_hat (FACT)
-  float* vv;      // [TMAX][D] v, then U0
-  float* y;       // [2*TMAX][YLD] MFMA result rows (aliases qa, ka and the head of kb)
+  float* qa;      // [TMAX][XS] q_hat, then exp(Gam) * q_hat           (X rows T..2T-1)
+  float* ka;      // [TMAX][XS] k_hat, then exp(Gam) * k_hat, then W    (X rows 0..T-1)
+  float* kb;      // [TMAX][XS] g, then Gam, then exp(-Gam) * k_hat (FACT)
+  float* vv;      // [TMAX][XS] v, then U0
+  float* y;       // [2*TMAX][XS] MFMA result rows (over qa and ka)
   float* am;      // [TMAX][TMAX]
   float* pm;      // [TMAX][TMAX]
   float* beta;    // [TMAX]
   float* egl;     // [D] exp(G_L)
   float* cm;      // [2*TMAX][hm]
   float* dh;      // [hm][D] exp(G_L - G_j) * k_j
-  uint16_t* xop;  // [2][2*TMAX][D] bf16 hi / lo of X * exp(G_L), chunk-swizzled
   uint16_t* uh;   // [hm][D] u_j (bf16 bits)
+  uint16_t* kr;   // [hm][D] k_j (bf16 bits) as read from the ring
 };
 
 __host__ __device__ inline size_t smem_bytes(int hm) {
-  size_t f = size_t(4) * TMAX * D + 2 * TMAX * TMAX + TMAX + D + size_t(2 * TMAX) * hm +
-             size_t(hm) * D;
-  size_t bytes = f * 4 + size_t(2) * 2 * TMAX * D * 2 + size_t(hm) * D * 2;
+  const size_t f = size_t(4) * TMAX * XS + 2 * TMAX * TMAX + TMAX + D + size_t(2 * TMAX) * hm +
+                   size_t(hm) * D;
+  const size_t bytes = f * 4 + size_t(2) * hm * D * 2;
   return (bytes + 15) & ~size_t(15);
 }
 
 __device__ inline Smem carve(float* base, int hm) {
   Smem s;
   float* p = base;
-  s.qa = p; p += TMAX * D;
-  s.ka = p; p += TMAX * D;
+  s.qa = p; p += TMAX * XS;
+  s.ka = p; p += TMAX * XS;
   s.y = s.qa;
-  s.kb = p; p += TMAX * D;
-  s.vv = p; p += TMAX * D;
+  s.kb = p; p += TMAX * XS;
+  s.vv = p; p += TMAX * XS;
   s.am = p; p += TMAX * TMAX;
   s.pm = p; p += TMAX * TMAX;
   s.beta = p; p += TMAX;
   s.egl = p; p += D;
   s.cm = p; p += 2 * TMAX * hm;
   s.dh = p; p += size_t(hm) * D;
-  s.xop = reinterpret_cast<uint16_t*>(p);
-  s.uh = s.xop + 2 * 2 * TMAX * D;
+  s.uh = reinterpret_cast<uint16_t*>(p);
+  s.kr = s.uh + size_t(hm) * D;
   return s;
-}
-
-// Four consecutive bf16 -> floats (VEC: one 8-byte load).
-template <bool VEC>
-__device__ __forceinline__ void load4_bf16(const uint16_t* p, float* x) {
-  if constexpr (VEC) {
-    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-    x[0] = bf_lo(w[0]);
-    x[1] = bf_hi(w[0]);
-    x[2] = bf_lo(w[1]);
-    x[3] = bf_hi(w[1]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = bf1(p[i]);
-  }
 }
 
 template <bool VEC>
@@ -122,26 +114,6 @@ __device__ __forceinline__ f32x4 load4_f32(const float* p) {
   else return f32x4{p[0], p[1], p[2], p[3]};
 }
 
-template <bool VEC>
-__device__ __forceinline__ void store4_bf16(uint16_t* p, const float* x) {
-  const uint32_t w0 = pack_bf16x2(x[0], x[1]), w1 = pack_bf16x2(x[2], x[3]);
-  if constexpr (VEC) {
-    *reinterpret_cast<u32x2*>(p) = u32x2{w0, w1};
-  } else {
-    p[0] = uint16_t(w0 & 0xffffu);
-    p[1] = uint16_t(w0 >> 16);
-    p[2] = uint16_t(w1 & 0xffffu);
-    p[3] = uint16_t(w1 >> 16);
-  }
-}
-
-// Left-operand tile (bf16, 16 rows x 128 channels): the 16-byte chunk c of
-// row m is stored at chunk c ^ (m % 16), so the 16 lanes that read one chunk
-// column of 16 rows hit 16 different bank groups.
-__device__ __forceinline__ int xsw(int m, int c) {
-  return m * D + ((((c >> 3) ^ (m & 15))) << 3) + (c & 7);
-}
-
 // The 8 channels of lane kb (0..15) inside a 16-lane group: 4kb..4kb+3 and
 // 64+4kb..64+4kb+3.
 __device__ __forceinline__ int chan(int kb, int half) { return half * 64 + 4 * kb; }
@@ -156,24 +128,46 @@ __device__ __forceinline__ void lds_read8(const float* row, int kb, float* x) {
   }
 }
 
-__device__ __forceinline__ void lds_write8(float* row, int kb, const float* x) {
-  *reinterpret_cast<f32x4*>(row + chan(kb, 0)) = f32x4{x[0], x[1], x[2], x[3]};
-  *reinterpret_cast<f32x4*>(row + chan(kb, 1)) = f32x4{x[4], x[5], x[6], x[7]};
-}
-
 }  // namespace
 
-// Grid: one 256-thread workgroup per (row, head), row-major over heads.
+// Raw token inputs of one item: thread tid covers token tid / 32 (T <= 8),
+// channels 4 (tid % 32) .. +3.
+struct TokRegs {
+  u32x2 q, k, g, v;
+  f32x4 dtb;
+  uint32_t braw;
+};
+
+template <bool VEC>
+__device__ __forceinline__ void load_tokens(const VerifyParams& p, int64_t item, int tid,
+                                            TokRegs& r) {
+  const int h = int(item % p.H);
+  const int64_t b = item / p.H;
+  const int t = tid >> 5, c = 4 * (tid & 31);
+  if (t < p.T) {
+    r.q = load4_raw<VEC>(p.q + b * p.q_row_stride + t * p.q_tok_stride + h * D + c);
+    r.k = load4_raw<VEC>(p.k + b * p.k_row_stride + t * p.k_tok_stride + h * D + c);
+    r.g = load4_raw<VEC>(p.g + b * p.g_row_stride + t * p.g_tok_stride + h * D + c);
+    r.v = load4_raw<VEC>(p.v + b * p.v_row_stride + t * p.v_tok_stride + h * D + c);
+    r.dtb = load4_f32<VEC>(p.dt_bias + h * D + c);
+    r.braw = p.beta[b * p.beta_row_stride + t * p.beta_tok_stride + h];
+  }
+}
+
+// Grid: one 256-thread workgroup per item (row, head), item = row * H + head.
 template <bool VEC, bool FACT>
 __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   extern __shared__ __align__(16) float smem_raw[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int h = int(blockIdx.x % p.H);
-  const int64_t b = blockIdx.x / p.H;
   const int T = p.T;
   const int R = p.ring_rows;
+  const int64_t item = blockIdx.x;
+  const int h = int(item % p.H);
+  const int64_t b = item / p.H;
+  const int fv = lane & 15, fk = (lane >> 4) * 8;
+  const int kb = lane & 15;
 
   const int32_t slot = p.state_indices[b];
   const int hist = p.hist_len[b];
@@ -185,8 +179,14 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
     for (int e = tid; e < T * D; e += 256) outb[int64_t(e >> 7) * p.out_tok_stride + (e & 127)] = 0;
     return;
   }
-  const bool fold = hist + T >= p.flush_min;
   Smem s = carve(smem_raw, hm);
+  const float neg_ea = -fexp(p.A_log[h]);
+  // Token words first; every global load phases 2-5 need is issued before
+  // the checkpoint loads (the memory counter is in order: waiting on a load
+  // issued after them would also wait for the 32 KiB checkpoint read).
+  TokRegs tk;
+  load_tokens<VEC>(p, item, tid, tk);
+  const bool fold = hist + T >= p.flush_min;
   const int64_t sh = int64_t(slot) * p.H + h;
   uint16_t* ckpt = p.state_pool + int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS;
   uint16_t* kc = p.k_cache + sh * R * D;
@@ -195,127 +195,159 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   // ring row of history / draft position j (0 <= j < hist + T <= R, base < R)
   auto ring_row = [&](int j) { const int r = base + j; return r >= R ? r - R : r; };
 
-  const int fv = lane & 15, fk = (lane >> 4) * 8;
   u32x4 sf[2][4];
-  // ---- 2. per-token prologue: token t on wave t/4, lanes 16*(t%4) .. +15.
-  // The token loads are issued first, then the checkpoint B fragments (wave
+  // ---- 2. per-token prologue (token t on lanes 32 t .. 32 t + 31, four
+  // channels per lane), run while the checkpoint B fragments stream in (wave
   // w owns value columns 32w .. 32w+31 in two 16-column blocks; fragment
   // (blk, st) holds v = 32w + 16*blk + lane%16, key channels
-  // 32*st + 8*(lane/16) .. +7): waiting for the token inputs then does not
-  // also wait for the 32 KiB state read, which streams in under the prologue.
-  const int kb = lane & 15;
-  {
-    const int t = wave * 4 + (lane >> 4);
-    // raw words first (no use of the loaded values before the state loads)
-    u32x2 qw[2], kw[2], gw[2], vw[2];
-    f32x4 dw[2];
-    float alog = 0.f;
-    if (t < T) {
-      const int64_t qo = b * p.q_row_stride + t * p.q_tok_stride + h * D;
-      const int64_t ko = b * p.k_row_stride + t * p.k_tok_stride + h * D;
-      const int64_t go = b * p.g_row_stride + t * p.g_tok_stride + h * D;
-      const int64_t vo = b * p.v_row_stride + t * p.v_tok_stride + h * D;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int c = chan(kb, hf);
-        qw[hf] = load4_raw<VEC>(p.q + qo + c);
-        kw[hf] = load4_raw<VEC>(p.k + ko + c);
-        gw[hf] = load4_raw<VEC>(p.g + go + c);
-        vw[hf] = load4_raw<VEC>(p.v + vo + c);
-        dw[hf] = load4_f32<VEC>(p.dt_bias + h * D + c);
+  // 32*st + 8*(lane/16) .. +7).
+  // History rows j < hist go straight from the ring into LDS (no register
+  // destinations) in waves 2 and 3. Wave 2 + half owns key / value channels
+  // 64 half .. +63: G_j (64 lanes x 4 B) into dh, k_j and u_j (32 lanes x
+  // 4 B each) into kr and uh. Like every other load of the item they are
+  // issued before the checkpoint loads and covered by the explicit vmcnt(8)
+  // at the start of the prologue math.
+  if constexpr (VEC) {
+    if (hist > 0 && wave >= 2) {
+      const int half = wave - 2;
+      for (int j = 0; j < hist; ++j) {
+        const int64_t row = ring_row(j);
+        __builtin_amdgcn_global_load_lds(gc + row * D + 64 * half + lane, s.dh + j * D + 64 * half,
+                                         4, 0, 0);
+        if (lane < 32) {
+          __builtin_amdgcn_global_load_lds(kc + row * D + 64 * half + 2 * lane,
+                                           s.kr + j * D + 64 * half, 4, 0, 0);
+          __builtin_amdgcn_global_load_lds(uc + row * D + 64 * half + 2 * lane,
+                                           s.uh + j * D + 64 * half, 4, 0, 0);
+        }
       }
-      alog = p.A_log[h];
+    }
+  }
+  // G_{hist-1} of key channel tid % 128 (phase 3).
+  float gl = 0.f;
+  if (hist > 0) gl = gc[int64_t(ring_row(hist - 1)) * D + (tid & 127)];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      sf[blk][st] = load8_raw<VEC>(ckpt + int64_t(32 * wave + 16 * blk + fv) * D + 32 * st + fk);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const int t = tid >> 5, c0 = 4 * (tid & 31);
+    // Every load but the 8 checkpoint loads is complete from here on. The
+    // token words are used only through an OR with an opaque zero defined
+    // here, so no use of them is hoisted above the checkpoint loads (where
+    // waiting for them would delay that read).
+    __builtin_amdgcn_s_waitcnt(kVmcntBehindCheckpoint);
+    uint32_t zero = 0;
+    __asm__ volatile("" : "+v"(zero));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      tk.q[i] |= zero;
+      tk.k[i] |= zero;
+      tk.g[i] |= zero;
+      tk.v[i] |= zero;
     }
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        sf[blk][st] = load8_raw<VEC>(ckpt + int64_t(32 * wave + 16 * blk + fv) * D + 32 * st + fk);
-    // keep the state loads issued here, ahead of any wait on the token loads
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < 4; ++i) tk.dtb[i] = __uint_as_float(__float_as_uint(tk.dtb[i]) | zero);
+    tk.braw |= zero;
     if (t < T) {
-      float q[8], k[8], gr[8], vv[8], dtb[8];
+      float q[4], k[4], gr[4], vv[4];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          q[4 * hf + 2 * i] = bf_lo(qw[hf][i]);
-          q[4 * hf + 2 * i + 1] = bf_hi(qw[hf][i]);
-          k[4 * hf + 2 * i] = bf_lo(kw[hf][i]);
-          k[4 * hf + 2 * i + 1] = bf_hi(kw[hf][i]);
-          gr[4 * hf + 2 * i] = bf_lo(gw[hf][i]);
-          gr[4 * hf + 2 * i + 1] = bf_hi(gw[hf][i]);
-          vv[4 * hf + 2 * i] = bf_lo(vw[hf][i]);
-          vv[4 * hf + 2 * i + 1] = bf_hi(vw[hf][i]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dtb[4 * hf + i] = dw[hf][i];
+      for (int i = 0; i < 2; ++i) {
+        q[2 * i] = bf_lo(tk.q[i]);
+        q[2 * i + 1] = bf_hi(tk.q[i]);
+        k[2 * i] = bf_lo(tk.k[i]);
+        k[2 * i + 1] = bf_hi(tk.k[i]);
+        gr[2 * i] = bf_lo(tk.g[i]);
+        gr[2 * i + 1] = bf_hi(tk.g[i]);
+        vv[2 * i] = bf_lo(tk.v[i]);
+        vv[2 * i + 1] = bf_hi(tk.v[i]);
       }
-      const float neg_ea = -fexp(alog);
       float sq = 0.f, sk = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
+      for (int c = 0; c < 4; ++c) {
         sq = fmaf(q[c], q[c], sq);
         sk = fmaf(k[c], k[c], sk);
       }
       sq = row16_sum(sq);
       sk = row16_sum(sk);
+      sq += __shfl_xor(sq, 16);
+      sk += __shfl_xor(sk, 16);
       const float rq = 1.0f / sqrtf(sq + 1e-6f);
       const float rk = 1.0f / sqrtf(sk + 1e-6f);
-      float g[8];
+      f32x4 qn, kn, gn, vn;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        q[c] *= rq;
-        k[c] *= rk;
-        g[c] = fgate(gr[c] + dtb[c], neg_ea, p.lower_bound);
+      for (int c = 0; c < 4; ++c) {
+        qn[c] = q[c] * rq;
+        kn[c] = k[c] * rk;
+        gn[c] = fgate(gr[c] + tk.dtb[c], neg_ea, p.lower_bound);
+        vn[c] = vv[c];
       }
-      lds_write8(s.qa + t * D, kb, q);
-      lds_write8(s.ka + t * D, kb, k);
-      lds_write8(s.kb + t * D, kb, g);
-      lds_write8(s.vv + t * D, kb, vv);
-      uint16_t* kr = kc + int64_t(ring_row(hist + t)) * D;
-      store4_bf16<VEC>(kr + chan(kb, 0), k);
-      store4_bf16<VEC>(kr + chan(kb, 1), k + 4);
+      *reinterpret_cast<f32x4*>(s.qa + t * XS + c0) = qn;
+      *reinterpret_cast<f32x4*>(s.ka + t * XS + c0) = kn;
+      *reinterpret_cast<f32x4*>(s.kb + t * XS + c0) = gn;
+      *reinterpret_cast<f32x4*>(s.vv + t * XS + c0) = vn;
+      if ((tid & 31) == 0) s.beta[t] = fsigmoid(bf1(uint16_t(tk.braw)));
     }
   }
   __syncthreads();
 
-  // ---- 3. threads 0..127 own key channel c: Gam_t (from 0) and the ring's
+  // ---- 3. two threads own key channel c (tokens split by parity): the
+  // ring's k_hat rows, Gam_t (from 0) and the ring's
   // G_t = G_base + g_0 + ... + g_t in token order (G_base = 0 when folding,
   // else G_{hist-1}); exp(G_L); with FACT the rows exp(Gam) * q, exp(Gam) * k
-  // and exp(-Gam) * k. Threads 128..255 compute beta_t = sigmoid(logit) and
-  // stage the live history rows:
+  // and exp(-Gam) * k. Threads 128..255 also stage the live history rows:
   // D_j = exp(G_L - G_j) * k_j (fp32) and u_j (bf16). History rows
-  // (j < hist) and draft rows (hist .. hist+T-1) never coincide.
+  // (j < hist) and draft rows (hist .. hist+T-1) never coincide. (These
+  // history loads come after the checkpoint read, so a row with history
+  // waits for it here.)
   {
     const int c = tid & 127;
-    const float gl = hist > 0 ? gc[int64_t(ring_row(hist - 1)) * D + c] : 0.f;
-    if (tid < 128) {
-      s.egl[c] = fexp(gl);
-      float gam = 0.f, gacc = fold ? 0.f : gl;
-      for (int t = 0; t < T; ++t) {
-        const float g = s.kb[t * D + c];
-        gam += g;
-        gacc += g;
-        gc[int64_t(ring_row(hist + t)) * D + c] = gacc;
-        if constexpr (FACT) {
-          const float ea = fexp(gam), eb = fexp(-gam);
-          const float kh = s.ka[t * D + c];
-          s.qa[t * D + c] *= ea;
-          s.ka[t * D + c] = kh * ea;
-          s.kb[t * D + c] = kh * eb;
-        } else {
-          s.kb[t * D + c] = gam;
+    const int half = tid >> 7;  // tokens t with t % 2 == half
+    // Both threads of a channel read its whole gate column before either
+    // rewrites the rows (barrier below).
+    float gcol[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) gcol[t] = t < T ? s.kb[t * XS + c] : 0.f;
+    if (half == 1 && hist > 0) {
+      if constexpr (VEC) {
+        // this wave's history rows are in LDS (waited for in phase 2)
+        for (int j = 0; j < hist; ++j)
+          s.dh[j * D + c] = fexp(gl - s.dh[j * D + c]) * bf1(s.kr[j * D + c]);
+      } else {
+        for (int j = 0; j < hist; ++j) {
+          const int64_t row = ring_row(j);
+          s.dh[j * D + c] = fexp(gl - gc[row * D + c]) * bf1(kc[row * D + c]);
+          s.uh[j * D + c] = uc[row * D + c];
         }
       }
-    } else {
-      if (c < T)
-        s.beta[c] = 1.0f / (1.0f + fexp(-bf1(p.beta[b * p.beta_row_stride +
-                                                    c * p.beta_tok_stride + h])));
-      for (int j = 0; j < hist; ++j) {
-        const int64_t row = ring_row(j);
-        s.dh[j * D + c] = fexp(gl - gc[row * D + c]) * bf1(kc[row * D + c]);
-        s.uh[j * D + c] = uc[row * D + c];
+    }
+    __syncthreads();
+    if (half == 0) s.egl[c] = fexp(gl);
+    float gam = 0.f, gacc = fold ? 0.f : gl;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if (t < T) {
+        gam += gcol[t];
+        gacc += gcol[t];
+        if ((t & 1) == half) {
+          const int64_t row = ring_row(hist + t);
+          const float kh = s.ka[t * XS + c];
+          __builtin_nontemporal_store(gacc, gc + row * D + c);
+          // (stored here rather than in phase 2: a store there makes the
+          // compiler wait on the checkpoint loads before the next barrier)
+          __builtin_nontemporal_store(to_bf16(kh), kc + row * D + c);
+          if constexpr (FACT) {
+            const float ea = fexp(gam), eb = fexp(-gam);
+            s.qa[t * XS + c] *= ea;
+            s.ka[t * XS + c] = kh * ea;
+            s.kb[t * XS + c] = kh * eb;
+          } else {
+            s.kb[t * XS + c] = gam;
+          }
+        }
       }
     }
   }
@@ -333,9 +365,9 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
       float a = 0.f, pp = 0.f;
       if constexpr (FACT) {
         float x[8], y[8], z[8];
-        lds_read8(s.ka + r * D, kb, x);
-        lds_read8(s.qa + r * D, kb, y);
-        lds_read8(s.kb + j * D, kb, z);
+        lds_read8(s.ka + r * XS, kb, x);
+        lds_read8(s.qa + r * XS, kb, y);
+        lds_read8(s.kb + j * XS, kb, z);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           a = fmaf(x[c], z[c], a);
@@ -343,11 +375,11 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
         }
       } else {
         float gr_[8], gj[8], kr[8], kj[8], qr[8];
-        lds_read8(s.kb + r * D, kb, gr_);
-        lds_read8(s.kb + j * D, kb, gj);
-        lds_read8(s.ka + r * D, kb, kr);
-        lds_read8(s.ka + j * D, kb, kj);
-        lds_read8(s.qa + r * D, kb, qr);
+        lds_read8(s.kb + r * XS, kb, gr_);
+        lds_read8(s.kb + j * XS, kb, gj);
+        lds_read8(s.ka + r * XS, kb, kr);
+        lds_read8(s.ka + j * XS, kb, kj);
+        lds_read8(s.qa + r * XS, kb, qr);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const float w = kj[c] * fexp(gr_[c] - gj[c]);
@@ -366,51 +398,39 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   __syncthreads();
 
   // ---- 5. forward substitution. Threads 0..127 own key channel c of W
-  // (written over row r of ka; X rows T.. are the exp(Gam) * q rows in qa) and
-  // store the bf16 hi/lo parts of X * exp(G_L); threads 128..255 own value
-  // channel c of U0 (in place in vv).
+  // (written over row r of ka; X rows T.. are the exp(Gam) * q rows in qa);
+  // threads 128..255 own value channel c of U0 (in place in vv).
   {
     const int c = tid & 127;
     if (tid < 128) {
       float w[TMAX];
-      const float eg = s.egl[c];
 #pragma unroll
       for (int r = 0; r < TMAX; ++r) {
         if (r < T) {
           float x;
           if constexpr (FACT) {
-            x = s.ka[r * D + c];
+            x = s.ka[r * XS + c];
           } else {
-            const float ea = fexp(s.kb[r * D + c]);
-            x = ea * s.ka[r * D + c];
-            s.qa[r * D + c] *= ea;
+            const float ea = fexp(s.kb[r * XS + c]);
+            x = ea * s.ka[r * XS + c];
+            s.qa[r * XS + c] *= ea;
           }
 #pragma unroll
           for (int j = 0; j < r; ++j) x = fmaf(-s.am[r * TMAX + j], w[j], x);
           w[r] = s.beta[r] * x;
-          s.ka[r * D + c] = w[r];
+          s.ka[r * XS + c] = w[r];
         }
-      }
-#pragma unroll
-      for (int m = 0; m < 2 * TMAX; ++m) {
-        float x = 0.f;
-        if (m < T) x = w[m];
-        else if (m < 2 * T) x = s.qa[(m - T) * D + c];
-        const float xs = x * eg;
-        const uint16_t hi = to_bf16(xs);
-        s.xop[xsw(m, c)] = hi;
-        s.xop[2 * TMAX * D + xsw(m, c)] = to_bf16(xs - bf1(hi));
       }
     } else {
       float u0[TMAX];
 #pragma unroll
       for (int r = 0; r < TMAX; ++r) {
         if (r < T) {
-          float x = s.vv[r * D + c];
+          float x = s.vv[r * XS + c];
 #pragma unroll
           for (int j = 0; j < r; ++j) x = fmaf(-s.am[r * TMAX + j], u0[j], x);
           u0[r] = s.beta[r] * x;
-          s.vv[r * D + c] = u0[r];
+          s.vv[r * XS + c] = u0[r];
         }
       }
     }
@@ -421,7 +441,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   if (hist > 0) {
     const int grp = tid >> 4;
     if (grp < 2 * T) {
-      const float* xrow = grp < T ? s.ka + grp * D : s.qa + (grp - T) * D;
+      const float* xrow = grp < T ? s.ka + grp * XS : s.qa + (grp - T) * XS;
       float x[8];
       lds_read8(xrow, kb, x);
       for (int j = 0; j < hist; ++j) {
@@ -435,47 +455,77 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
       }
     }
   }
-  __syncthreads();  // X rows (qa / ka) and kb are dead from here on: y may overwrite them
+  __syncthreads();
 
-  // ---- 6. Y = (X * exp(G_L)) S_ckpt on MFMA: per 16-column block, four
-  // 32-channel steps, hi and lo parts into one accumulator.
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // ---- 6. Y = (X * exp(G_L)) S_ckpt on MFMA. Lane (g, m) builds its A
+  // fragment from X row m (W rows in ka, exp(Gam) q rows in qa, zero rows
+  // from 2T on): 8 fp32 channels scaled by exp(G_L) and split into bf16 hi
+  // and lo parts, shared by both 16-column blocks; four 32-channel steps.
+  {
+    const float* xrow = fv < T ? s.ka + fv * XS : s.qa + (fv - T) * XS;
+    const bool xzero = fv >= 2 * T;
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const bf16x8 bfr = __builtin_bit_cast(bf16x8, sf[blk][st]);
-      const int ax = xsw(fv, 32 * st + fk);
-      const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(s.xop + ax);
-      const bf16x8 alo = *reinterpret_cast<const bf16x8*>(s.xop + 2 * TMAX * D + ax);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bfr, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfr, acc, 0, 0, 0);
-    }
-    const int v = 32 * wave + 16 * blk + fv;
+      const int k0 = 32 * st + fk;
+      f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+      if (!xzero) {
+        x0 = *reinterpret_cast<const f32x4*>(xrow + k0);
+        x1 = *reinterpret_cast<const f32x4*>(xrow + k0 + 4);
+      }
+      const f32x4 e0 = *reinterpret_cast<const f32x4*>(s.egl + k0);
+      const f32x4 e1 = *reinterpret_cast<const f32x4*>(s.egl + k0 + 4);
+      u32x4 hi, lo;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s.y[((lane >> 4) * 4 + i) * YLD + v] = acc[i];
+      for (int i = 0; i < 2; ++i) {
+        const float a = x0[2 * i] * e0[2 * i], b = x0[2 * i + 1] * e0[2 * i + 1];
+        const float c = x1[2 * i] * e1[2 * i], d = x1[2 * i + 1] * e1[2 * i + 1];
+        hi[i] = pack_bf16x2(a, b);
+        hi[2 + i] = pack_bf16x2(c, d);
+        lo[i] = pack_bf16x2(a - bf_lo(hi[i]), b - bf_hi(hi[i]));
+        lo[2 + i] = pack_bf16x2(c - bf_lo(hi[2 + i]), d - bf_hi(hi[2 + i]));
+      }
+      const bf16x8 ahi = __builtin_bit_cast(bf16x8, hi);
+      const bf16x8 alo = __builtin_bit_cast(bf16x8, lo);
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const bf16x8 bfr = __builtin_bit_cast(bf16x8, sf[blk][st]);
+        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bfr, acc[blk], 0, 0, 0);
+        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfr, acc[blk], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave has read its X rows: Y may overwrite them
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int v = 32 * wave + 16 * blk + fv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s.y[((lane >> 4) * 4 + i) * XS + v] = acc[blk][i];
+    }
   }
   __syncthreads();
 
-  // ---- 7. threads 0..127 own value channel v: u_t, o_t, ring u rows, outputs.
-  if (tid < 128) {
-    const int v = tid;
+  // ---- 7. two threads own value channel v (tokens split by parity): u_t,
+  // o_t, ring u rows, outputs. Each computes every u_j it needs (u_t only
+  // depends on Y and U0).
+  {
+    const int v = tid & 127;
+    const int half = tid >> 7;
     float u[TMAX];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       if (t < T) {
-        float yw = s.y[t * YLD + v];
-        float yq = s.y[(T + t) * YLD + v];
-        for (int j = 0; j < hist; ++j) {
-          const float uj = bf1(s.uh[j * D + v]);
-          yw = fmaf(s.cm[t * hm + j], uj, yw);
-          yq = fmaf(s.cm[(T + t) * hm + j], uj, yq);
-        }
-        u[t] = s.vv[t * D + v] - yw;
+        float yw = s.y[t * XS + v];
+        for (int j = 0; j < hist; ++j) yw = fmaf(s.cm[t * hm + j], bf1(s.uh[j * D + v]), yw);
+        u[t] = s.vv[t * XS + v] - yw;
+        if ((t & 1) == half) {
+          float yq = s.y[(T + t) * XS + v];
+          for (int j = 0; j < hist; ++j)
+            yq = fmaf(s.cm[(T + t) * hm + j], bf1(s.uh[j * D + v]), yq);
 #pragma unroll
-        for (int j = 0; j <= t; ++j) yq = fmaf(s.pm[t * TMAX + j], u[j], yq);
-        outb[int64_t(t) * p.out_tok_stride + v] = to_bf16(p.scale * yq);
-        uc[int64_t(ring_row(hist + t)) * D + v] = to_bf16(u[t]);
+          for (int j = 0; j <= t; ++j) yq = fmaf(s.pm[t * TMAX + j], u[j], yq);
+          __builtin_nontemporal_store(to_bf16(p.scale * yq), outb + int64_t(t) * p.out_tok_stride + v);
+          __builtin_nontemporal_store(to_bf16(u[t]), uc + int64_t(ring_row(hist + t)) * D + v);
+        }
       }
     }
   }

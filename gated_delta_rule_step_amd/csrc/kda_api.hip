@@ -210,6 +210,8 @@ extern "C" kda_status kda_prefill_varlen(
       beta_tok_stride < 0 || out_tok_stride < 0 || slot_stride < 0)
     return KDA_ERR_BAD_STRIDE;
   if (total_tokens > 1 && out_tok_stride < W) return KDA_ERR_BAD_STRIDE;
+  // a 16-token chunk of outputs is stored through one 32-bit buffer range
+  if (out_tok_stride > (int64_t(1) << 25)) return KDA_ERR_UNSUPPORTED;
   if (num_slots > 1 && slot_stride < W * D) return KDA_ERR_BAD_STRIDE;
   const size_t need = kda::prefill_workspace_bytes(n_docs, total_tokens, H);
   if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;

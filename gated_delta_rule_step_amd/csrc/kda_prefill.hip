@@ -60,6 +60,8 @@ constexpr int C = 16;          // tokens per chunk
 constexpr int XLD = D + 8;     // padded row (bf16) of the [token][key] operand tiles
 constexpr int TLD = C + 4;     // padded row (bf16) of the [key][token] operand tile
 constexpr int kMaxOrderedDocs = 256;
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
+constexpr int kStoreNontemporal = 2;      // cache-policy bits of a buffer store: nt
 
 struct DocOrder {
   int32_t n;  // 0: natural order
@@ -154,7 +156,7 @@ __device__ __forceinline__ u32x2 gload4(const uint16_t* p) {
 template <bool VEC>
 __device__ __forceinline__ void gstore4(uint16_t* p, u32x2 w) {
   if constexpr (VEC) {
-    *reinterpret_cast<u32x2*>(p) = w;
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
   } else {
     p[0] = uint16_t(w[0] & 0xffffu);
     p[1] = uint16_t(w[0] >> 16);
@@ -217,20 +219,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
   }
   PSmem s = pcarve(psmem_raw);
 
-  // ---- initial state into the accumulator layout
+  // ---- initial state into the accumulator layout (all 16 loads issued
+  // before any is waited for)
   f32x4 acc[8][2];
+  if (p.use_initial_state) {
+    u32x2 w[8][2];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      if (p.use_initial_state) {
-        const int v = 32 * wave + 16 * nt + n16;
-        const u32x2 w = gload4<VEC>(sp + v * D + 16 * mt + 4 * g4);
-        acc[mt][nt] = f32x4{bf_lo(w[0]), bf_hi(w[0]), bf_lo(w[1]), bf_hi(w[1])};
-      } else {
-        acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
+      for (int nt = 0; nt < 2; ++nt)
+        w[mt][nt] = gload4<VEC>(sp + (32 * wave + 16 * nt + n16) * D + 16 * mt + 4 * g4);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        acc[mt][nt] = f32x4{bf_lo(w[mt][nt][0]), bf_hi(w[mt][nt][0]), bf_lo(w[mt][nt][1]),
+                            bf_hi(w[mt][nt][1])};
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const float neg_ea = -fexp(p.A_log[h]);
   const int tt = tid >> 4;           // prologue: token of this lane
@@ -238,6 +248,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
   float dtb[8];
   load8_f32<VEC>(p.dt_bias + h * D + c0, dtb);
   const int nchunks = int((len + C - 1) / C);
+  const int ots32 = static_cast<int>(p.out_tok_stride);  // host-checked to fit a buffer range
   TokRaw raw = load_tok<VEC>(p, t0 + tt, h, c0, tt < len);
 
   for (int ch = 0; ch < nchunks; ++ch) {
@@ -381,6 +392,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
     __syncthreads();
 
     // ---- chain for this wave's 32 value channels
+    // Output rows of this chunk as a buffer range of exactly c rows: a store
+    // to a padded row (r >= c) is out of range and discarded, so the number
+    // of store instructions does not depend on c (the compiler can then count
+    // them and never waits for them before the next chunk's token words).
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        p.out + tc0 * p.out_tok_stride + h * D, 0,
+        static_cast<int>(((c - 1) * p.out_tok_stride + D) * 2), kBufferWord3);
     f32x4 yw[2], yq[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -417,12 +435,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
 #pragma unroll
       for (int i = 0; i < 4; ++i) u[i] = s.u0[(4 * g4 + i) * D + v] - yw[nt][i];
       split4(u, uhi[nt], ulo[nt]);
-      // O = scale ((e^Gam q) S^T + P U)
+      // O = scale ((e^Gam q) S^T + P U); rows r >= c fall outside the
+      // buffer range and are dropped by the store itself
       f32x4 o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pfr, uhi[nt], yq[nt], 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g4 + i;
-        if (r < c) p.out[(tc0 + r) * p.out_tok_stride + h * D + v] = to_bf16(p.scale * o[i]);
+        __builtin_amdgcn_raw_buffer_store_b16(to_bf16(p.scale * o[i]), orsrc,
+                                              (r * ots32 + v) * 2, 0, kStoreNontemporal);
       }
     }
     // S = S diag(e^Gam_last) + U^T K~  (contraction over the chunk's tokens)

@@ -229,7 +229,9 @@ size_t kda_prefill_workspace_size(int32_t n_docs, int64_t total_tokens, int32_t 
  * with use_initial_state = 0).
  * KDA_ERR_BAD_SEQLENS when cu_seqlens_host[0] != 0, it decreases, or its last
  * entry differs from total_tokens; KDA_ERR_WORKSPACE_TOO_SMALL when
- * workspace_bytes is short; KDA_ERR_UNSUPPORTED when |lower_bound| > 5.5 (the
+ * workspace_bytes is short; KDA_ERR_UNSUPPORTED when out_tok_stride exceeds
+ * 2^25 elements (16 output rows must span less than 2^31 bytes) or when
+ * |lower_bound| > 5.5 (the
  * 16-token chunks factor each decay weight exp(G_r - G_j) into two exps of at
  * most 8 |lower_bound| each, which must stay well inside the fp32 range).
  * Outputs are written in bf16 (round to nearest even); the final states are

@@ -52,10 +52,21 @@ N_SLOTS = 1024
 COUNTED_TRAFFIC = {
     "kda::decode_kernel<8, true>": dict(
         sources=("gated_delta_rule_step_amd/csrc/kda_decode.hip",
-                 "gated_delta_rule_step_amd/csrc/kda_common.h"),
+                 "gated_delta_rule_step_amd/csrc/kda_common.h",
+                 "gated_delta_rule_step_amd/build.py"),
         sha256=("779051e40ebca063e86ddd83f1ed6ed3c5742ee6e5c7f7998eaacfa6ebd2a385",
-                "34b8100422cba3857f715dc728116de3c64c225b97154059cd0d5945ac5a48f0"),
-        fetch_kib=96395.6484375, write_kib=188166.1875, fetch_scale=2.0, write_scale=1.0),
+                "34b8100422cba3857f715dc728116de3c64c225b97154059cd0d5945ac5a48f0",
+                "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
+        fetch_kib=96395.711, write_kib=188168.320, fetch_scale=2.0, write_scale=1.0),
+    # T = 8 verify, B = 512, bare checkpoint (the --mode profile sequence)
+    "kda::verify_kernel<true, true>": dict(
+        sources=("gated_delta_rule_step_amd/csrc/kda_verify.hip",
+                 "gated_delta_rule_step_amd/csrc/kda_common.h",
+                 "gated_delta_rule_step_amd/build.py"),
+        sha256=("951f9c1628aa4ef54ed7fa7199806b4f8d66caf89035296f88da587354cfc959",
+                "34b8100422cba3857f715dc728116de3c64c225b97154059cd0d5945ac5a48f0",
+                "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
+        fetch_kib=123927.266, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),
 }
 
 
@@ -419,13 +430,16 @@ def main():
                 us = e * 1e3 / st
                 nb = wm.verify_bytes(cfg["T"], vs.hist, vs.fold)
                 fl = wm.verify_flops(cfg["T"], vs.hist)
+                extra = {}
+                if Bv == 512 and cfg["label"] == "T=8 bare (0% fold)":
+                    extra["traffic_bytes"] = counted_traffic("kda::verify_kernel<true, true>")
                 points.append(dict(kind="verify", B=Bv, label=cfg["label"],
                                    fold_frac=round(float(np.mean(vs.fold)), 3),
                                    mean_hist=round(float(np.mean(vs.hist)), 2),
                                    us_per_call=round(us, 3),
                                    GBps=round(nb / (us * 1e-6) / 1e9, 1),
                                    hbm_frac=round(nb / (us * 1e-6) / 1e9 / wm.HBM_PEAK_GBS, 4),
-                                   TFLOPs=round(fl / (us * 1e-6) / 1e12, 2)))
+                                   TFLOPs=round(fl / (us * 1e-6) / 1e12, 2), **extra))
                 log(f"bench: {points[-1]}")
                 del vs
         del rings

@@ -57,6 +57,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));  // bf16 operands of th
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int C = 16;          // tokens per chunk
+constexpr int RS = D + 4;      // padded row (fp32) of the [token][channel] LDS arrays: the
+                               // 16 rows read by one MFMA fragment load hit different banks
 constexpr int XLD = D + 8;     // padded row (bf16) of the [token][key] operand tiles
 constexpr int TLD = C + 4;     // padded row (bf16) of the [key][token] operand tile
 constexpr int kMaxOrderedDocs = 256;
@@ -69,12 +71,12 @@ struct DocOrder {
 };
 
 struct PSmem {
-  float* qh;     // [C][D] q_hat, then exp(Gam - m) q_hat
-  float* kh;     // [C][D] k_hat, then exp(Gam - m) k_hat
-  float* gg;     // [C][D] g
-  float* vv;     // [C][D] v
-  float* u0;     // [C][D] U0
-  float* kb;     // [C][D] exp(m - Gam) k_hat, in the U0 rows (dead by the time U0 is solved)
+  float* qh;     // [C][RS] q_hat, then exp(Gam - m) q_hat
+  float* kh;     // [C][RS] k_hat, then exp(Gam - m) k_hat
+  float* gg;     // [C][RS] g
+  float* vv;     // [C][RS] v
+  float* u0;     // [C][RS] U0
+  float* kb;     // [C][RS] exp(m - Gam) k_hat, in the U0 rows (dead by the time U0 is solved)
   float* am;     // [C][C] A
   float* beta;   // [C]
   float* egl;    // [D] exp(Gam_last)
@@ -86,16 +88,16 @@ struct PSmem {
 };
 
 constexpr size_t kPrefillLds =
-    size_t(5 * C * D + C * C + C + 2 * D) * 4 + size_t(2 * C * XLD + C * XLD + 2 * D * TLD + C * C) * 2;
+    size_t(5 * C * RS + C * C + C + 2 * D) * 4 + size_t(2 * C * XLD + C * XLD + 2 * D * TLD + C * C) * 2;
 
 __device__ inline PSmem pcarve(float* base) {
   PSmem s;
   float* p = base;
-  s.qh = p; p += C * D;
-  s.kh = p; p += C * D;
-  s.gg = p; p += C * D;
-  s.vv = p; p += C * D;
-  s.u0 = p; p += C * D;
+  s.qh = p; p += C * RS;
+  s.kh = p; p += C * RS;
+  s.gg = p; p += C * RS;
+  s.vv = p; p += C * RS;
+  s.u0 = p; p += C * RS;
   s.kb = s.u0;
   s.am = p; p += C * C;
   s.beta = p; p += C;
@@ -284,10 +286,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
       const float rk = 1.0f / sqrtf(sk + 1e-6f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        s.qh[tt * D + c0 + e] = q[e] * rq;
-        s.kh[tt * D + c0 + e] = k[e] * rk;
-        s.gg[tt * D + c0 + e] = valid ? fgate(gr[e] + dtb[e], neg_ea, p.lower_bound) : 0.f;
-        s.vv[tt * D + c0 + e] = vv[e];
+        s.qh[tt * RS + c0 + e] = q[e] * rq;
+        s.kh[tt * RS + c0 + e] = k[e] * rk;
+        s.gg[tt * RS + c0 + e] = valid ? fgate(gr[e] + dtb[e], neg_ea, p.lower_bound) : 0.f;
+        s.vv[tt * RS + c0 + e] = vv[e];
       }
       if ((tid & 15) == 0) s.beta[tt] = valid ? fsigmoid(bf1(braw)) : 0.f;
     }
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
       float acc_g = 0.f;
 #pragma unroll
       for (int r = 0; r < C; ++r) {
-        acc_g += s.gg[r * D + cc];
+        acc_g += s.gg[r * RS + cc];
         gam[r] = acc_g;
       }
       const float mid = 0.5f * acc_g;  // padded rows carry g = 0
@@ -318,12 +320,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
         const int r = r0 + i;
         const float gr_ = r0 == 0 ? gam[i] : gam[8 + i];
         const float ea = fexp(gr_ - mid), eb = fexp(mid - gr_);
-        const float kh = s.kh[r * D + cc];
-        const float qh = s.qh[r * D + cc];
+        const float kh = s.kh[r * RS + cc];
+        const float qh = s.qh[r * RS + cc];
         const float kb = kh * eb;
-        s.qh[r * D + cc] = qh * ea;
-        s.kh[r * D + cc] = kh * ea;
-        s.kb[r * D + cc] = kb;
+        s.qh[r * RS + cc] = qh * ea;
+        s.kh[r * RS + cc] = kh * ea;
+        s.kb[r * RS + cc] = kb;
         s.qop[r * XLD + cc] = to_bf16(qh * ea * em);
         uint16_t hi, lo;
         split_bf16(em * kb, hi, lo);  // exp(Gam_last - m) = exp(m)
@@ -343,8 +345,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
         float x[8], y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          x[e] = left[n16 * D + 32 * kt + 8 * g4 + e];
-          y[e] = s.kb[n16 * D + 32 * kt + 8 * g4 + e];
+          x[e] = left[n16 * RS + 32 * kt + 8 * g4 + e];
+          y[e] = s.kb[n16 * RS + 32 * kt + 8 * g4 + e];
         }
         bf16x8 xh, xl, yh, yl;
         split8(x, xh, xl);
@@ -367,13 +369,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
     {
       const int cc = tid & 127;
       const float* rhs = tid < 128 ? s.kh : s.vv;
+      // Right-looking: once x_j is known it is taken off every later row's
+      // remainder, so the updates of one step are independent and the chain
+      // of dependent operations is two per row; each row still accumulates
+      // its terms in the order j = 0, 1, ...
       float x[C];
 #pragma unroll
-      for (int r = 0; r < C; ++r) {
-        float y = rhs[r * D + cc];
+      for (int r = 0; r < C; ++r) x[r] = rhs[r * RS + cc];
 #pragma unroll
-        for (int j = 0; j < r; ++j) y = fmaf(-s.am[r * C + j], x[j], y);
-        x[r] = s.beta[r] * y;
+      for (int j = 0; j < C; ++j) {
+        x[j] *= s.beta[j];
+#pragma unroll
+        for (int r = j + 1; r < C; ++r) x[r] = fmaf(-s.am[r * C + j], x[j], x[r]);
       }
       if (tid < 128) {
         const float em = s.em[cc];
@@ -386,7 +393,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < C; ++r) s.u0[r * D + cc] = x[r];
+        for (int r = 0; r < C; ++r) s.u0[r * RS + cc] = x[r];
       }
     }
     __syncthreads();
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
       const int v = 32 * wave + 16 * nt + n16;
       f32x4 u;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = s.u0[(4 * g4 + i) * D + v] - yw[nt][i];
+      for (int i = 0; i < 4; ++i) u[i] = s.u0[(4 * g4 + i) * RS + v] - yw[nt][i];
       split4(u, uhi[nt], ulo[nt]);
       // O = scale ((e^Gam q) S^T + P U); rows r >= c fall outside the
       // buffer range and are dropped by the store itself

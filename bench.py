@@ -289,6 +289,8 @@ class PrefillSetup:
         self.cu_h = torch.from_numpy(cu)
         self.cu_d = self.cu_h.cuda()
         self.out = torch.empty((T, W), dtype=torch.bfloat16, device="cuda")
+        self.ws = torch.empty(kda.kda_prefill_workspace_size(n_docs, T, H), dtype=torch.uint8,
+                              device="cuda")
         self.kda = kda
 
     def calls(self):
@@ -296,7 +298,7 @@ class PrefillSetup:
 
         def call():
             s.kda.kda_prefill_varlen(s.cu_h, s.cu_d, s.q, s.k, s.v, s.g, s.beta, s.a_log, s.dtb,
-                                     s.pool, s.idx, s.out)
+                                     s.pool, s.idx, s.out, workspace=s.ws)
         return [call]
 
 

@@ -194,7 +194,8 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
     """Varlen prefill. cu_seqlens_host: CPU int32 [n_docs+1]; cu_seqlens: the
     same on the GPU; q, k, v, g_raw, out: bf16 [Ttot, H*128] (token-strided);
     beta_raw bf16 [Ttot, H]; state_indices int32 [n_docs]; workspace: uint8
-    GPU tensor of >= kda_prefill_workspace_size(...) bytes (or None)."""
+    GPU tensor of >= kda_prefill_workspace_size(...) bytes, or None to have
+    one allocated here for this call."""
     import torch
     if cu_seqlens_host.dtype != torch.int32 or cu_seqlens_host.is_cuda or \
             not cu_seqlens_host.is_contiguous():
@@ -210,6 +211,10 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
     _f32("A_log", A_log)
     _f32("dt_bias", dt_bias)
     N, slot_stride = _pool_geometry(state_pool, H)
+    if workspace is None:
+        need = kda_prefill_workspace_size(n_docs, Ttot, H)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     cu_h = _P(cu_seqlens_host.data_ptr())
     st = lib().kda_prefill_varlen(

@@ -1,11 +1,14 @@
-// Chunked varlen prefill of the KDA recurrence (gfx950).
+// Chunked varlen prefill of the KDA recurrence (gfx950): a preparation
+// kernel over every (chunk, head) and a chain kernel over every
+// (document, head).
 //
 // Operation: "feat(kda): add CuTe DSL recurrent prefill backend" -- packed
 // documents delimited by cu_seqlens, each (document, head) chain runs the
 // gated delta-rule recurrence over its tokens from an optional initial state
 // and leaves its final state in the pool; the work is chunked (BT = 16 on
 // that page) into an intra-chunk preparation and a sequential chain over
-// chunks. The result equals the token-by-token recurrence.
+// chunks, the two stages of that page's prefill. The result equals the
+// token-by-token recurrence.
 //
 // Chunkwise form used here (WY representation of the delta rule with the
 // decay carried per key channel; Yang et al., "Parallelizing Linear
@@ -19,6 +22,10 @@
 //   U      = U0 - W S^T         (rows are the per-token corrections u_r)
 //   O      = scale ((exp(Gam) q) S^T + P U)
 //   S      = S diag(exp(Gam_c)) + U^T (exp(Gam_c - Gam) k)
+// Everything but the last three lines is independent of the state, so it runs
+// for all chunks of all documents at once (prep_kernel); only the last three
+// lines are sequential (chain_kernel).
+//
 // Every weight exp(Gam_r - Gam_j) of A and P factors into
 // exp(Gam_r - m) * exp(m - Gam_j) with m = Gam_last / 2 per key channel: over
 // 16 tokens |Gam_r - m| <= 8 |lower_bound| <= 44 (the host requires
@@ -27,24 +34,29 @@
 // right-hand side exp(Gam_r - m) k_r and scaled by exp(m) afterwards (the solve
 // is linear per key channel).
 //
-// One 256-thread workgroup owns one (document, head) chain; documents are
-// taken longest first. Wave w owns value channels 32w .. 32w+31 of the
-// fp32 state, kept in registers in the MFMA accumulator layout (16 tiles of
-// 16 x 16, tile (mt, nt) holding key channels 16mt + 4*(lane/16) + i and
-// value channel 32w + 16nt + lane%16). Per chunk:
-//  * the token prologue (norms, gate, beta) and the prefix / exp rows run on
-//    the VALU in fp32, A and P on v_mfma_f32_16x16x32_bf16 with bf16 hi/lo
-//    operand splits, the two 16 x 16 triangular solves on the VALU in fp32;
-//  * the chain multiplies W and exp(Gam) q by the state on
-//    v_mfma_f32_16x16x32_bf16 reading the state straight from the
-//    accumulators (the B fragment's 8 key channels are taken as two runs of
-//    4 from two accumulator tiles; the A fragments use the same order), with
-//    three hi/lo terms for W S^T and one for the read-out; U comes out in the
-//    accumulator layout, which is exactly the B fragment of
-//    v_mfma_f32_16x16x16_bf16 with the chunk's tokens as the contraction, so
-//    P U and the state update U^T K~ take it without any data movement;
-//  * the next chunk's token inputs are loaded into registers while the
-//    current chunk runs.
+// Chunk record. The preparation leaves, per (chunk, head), the chain's
+// operands in the workspace already in MFMA fragment order, so the chain
+// moves them with 16-byte loads and reads them with one LDS read per
+// fragment. Lane l = n16 + 16 g4 of a wave:
+//   W   [kt 4][hi, lo][lane][8 bf16]  W[n16][32kt + 4g4 + 0..3, 32kt + 16 + 4g4 + 0..3]
+//   Q   [kt 4][lane][8 bf16]          (exp(Gam) q_hat) at the same positions, bf16
+//   KT  [mt 8][lane][4 hi, 4 lo bf16] (exp(Gam_c - Gam) k_hat)[4g4 + 0..3][16mt + n16]
+//   U0  [vt 8][lane][4 fp32]          U0[4g4 + 0..3][16vt + n16]
+//   P   [lane][4 bf16]                P[n16][4g4 + 0..3]
+//   EG  [128 fp32]                    exp(Gam_c)
+// The chain's state S[v][k] sits in the MFMA accumulator layout: wave w, tile
+// (mt, nt) holds key channels 16mt + 4g4 + i and value channel 32w + 16nt + n16,
+// so the B fragment of v_mfma_f32_16x16x32_bf16 takes its 8 key channels as two
+// runs of 4 from accumulator tiles 2kt and 2kt+1 (the order the W and Q
+// fragments are written in), and U = U0 - W S^T comes out in the accumulator
+// layout, which is the B fragment of v_mfma_f32_16x16x16_bf16 with the chunk's
+// tokens as the contraction.
+//
+// Chunk slots. Chunk j of document d (first token t0) has slot
+// d + floor(t0 / 16) + j: strictly increasing over (d, j), fewer than
+// n_docs + floor(Ttot / 16) in all, and computable by the chain from (d, j)
+// alone; the preparation finds (d, j) from its slot by a search over
+// cu_seqlens.
 
 #include "kda_common.h"
 #include "kda_launch.h"
@@ -59,11 +71,24 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int C = 16;          // tokens per chunk
 constexpr int RS = D + 4;      // padded row (fp32) of the [token][channel] LDS arrays: the
                                // 16 rows read by one MFMA fragment load hit different banks
-constexpr int XLD = D + 8;     // padded row (bf16) of the [token][key] operand tiles
-constexpr int TLD = C + 4;     // padded row (bf16) of the [key][token] operand tile
+constexpr int XLD = D + 4;     // padded row (bf16) of W as bf16 hi / lo
 constexpr int kMaxOrderedDocs = 256;
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
 constexpr int kStoreNontemporal = 2;      // cache-policy bits of a buffer store: nt
+
+// chunk record, bytes
+constexpr int kRecW = 0;
+constexpr int kRecQ = 8192;
+constexpr int kRecKT = 12288;
+constexpr int kRecU0 = 20480;
+constexpr int kRecP = 28672;
+constexpr int kRecEG = 29184;
+constexpr int kRecBytes = 29696;
+constexpr int kRecUnits = kRecBytes / 16;  // 16-byte units
+constexpr int kThreads = 256;
+constexpr int kRecRounds = (kRecUnits + kThreads - 1) / kThreads;  // 8
+static_assert(kRecEG + 4 * D == kRecBytes, "record layout");
+static_assert(kRecUnits > (kRecRounds - 1) * kThreads, "every round has work");
 
 struct DocOrder {
   int32_t n;  // 0: natural order
@@ -71,24 +96,31 @@ struct DocOrder {
 };
 
 struct PSmem {
-  float* qh;     // [C][RS] q_hat, then exp(Gam - m) q_hat
-  float* kh;     // [C][RS] k_hat, then exp(Gam - m) k_hat
-  float* gg;     // [C][RS] g
-  float* vv;     // [C][RS] v
+  float* qh;     // [C][RS] q_hat, then exp(Gam - m) q_hat as bf16 hi / lo pairs, then W
+  float* kh;     // [C][RS] k_hat, then exp(Gam - m) k_hat as bf16 hi / lo pairs
+  float* gg;     // [C][RS] g, then exp(Gam_last - Gam) k_hat
   float* u0;     // [C][RS] U0
-  float* kb;     // [C][RS] exp(m - Gam) k_hat, in the U0 rows (dead by the time U0 is solved)
+  float* kb;     // [C][RS] exp(m - Gam) k_hat as bf16 hi / lo pairs, in the U0 rows
+                 // (dead by the time U0 is solved)
+  float* kw;     // [C][RS] exp(Gam - m) k_hat in fp32: right-hand side of W
   float* am;     // [C][C] A
   float* beta;   // [C]
   float* egl;    // [D] exp(Gam_last)
   float* em;     // [D] exp(Gam_last / 2)
-  uint16_t* wop;   // [2][C][XLD] W, bf16 hi / lo
-  uint16_t* qop;   // [C][XLD] exp(Gam) q_hat, bf16
-  uint16_t* ktop;  // [2][D][TLD] (exp(Gam_last - Gam) k_hat)^T, bf16 hi / lo
+  uint16_t* vv;    // [C][VLD] v (bf16, as loaded)
+  uint16_t* wop;   // [2][C][XLD] W, bf16 hi / lo, in the q rows (dead after A and P)
+  uint16_t* qop;   // [C][QLD] exp(Gam) q_hat, bf16
+  uint16_t* ktop;  // [2][C][D] exp(Gam_last - Gam) k_hat, bf16 hi / lo, in the g rows
+                   // (dead once the prefix sums are taken)
   uint16_t* pop;   // [C][C] P, bf16
 };
 
-constexpr size_t kPrefillLds =
-    size_t(5 * C * RS + C * C + C + 2 * D) * 4 + size_t(2 * C * XLD + C * XLD + 2 * D * TLD + C * C) * 2;
+constexpr int VLD = D + 8;  // row (bf16) of v: 16-byte aligned rows
+constexpr int QLD = D + 4;  // row (bf16) of exp(Gam) q_hat
+static_assert(2 * C * XLD * 2 <= C * RS * 4, "W fits in the q rows");
+static_assert(2 * C * D * 2 <= C * RS * 4, "K~ fits in the g rows");
+constexpr size_t kPrepLds = size_t(5 * C * RS + C * C + C + 2 * D) * 4 +
+                            size_t(C * VLD + C * QLD + C * C) * 2;
 
 __device__ inline PSmem pcarve(float* base) {
   PSmem s;
@@ -96,18 +128,19 @@ __device__ inline PSmem pcarve(float* base) {
   s.qh = p; p += C * RS;
   s.kh = p; p += C * RS;
   s.gg = p; p += C * RS;
-  s.vv = p; p += C * RS;
   s.u0 = p; p += C * RS;
   s.kb = s.u0;
+  s.kw = p; p += C * RS;
   s.am = p; p += C * C;
   s.beta = p; p += C;
   s.egl = p; p += D;
   s.em = p; p += D;
   uint16_t* b = reinterpret_cast<uint16_t*>(p);
-  s.wop = b; b += 2 * C * XLD;
-  s.qop = b; b += C * XLD;
-  s.ktop = b; b += 2 * D * TLD;
+  s.vv = b; b += C * VLD;
+  s.qop = b; b += C * QLD;
   s.pop = b;
+  s.wop = reinterpret_cast<uint16_t*>(s.qh);
+  s.ktop = reinterpret_cast<uint16_t*>(s.gg);
   return s;
 }
 
@@ -140,10 +173,11 @@ __device__ __forceinline__ void split4(const f32x4 x, s16x4& hi, s16x4& lo) {
   lo = __builtin_bit_cast(s16x4, l);
 }
 
-__device__ __forceinline__ bf16x8 lds_bf16x8_2runs(const uint16_t* p0, const uint16_t* p1) {
+// Two runs of 4 bf16 (8 bytes each, 8-byte aligned) as one 16-byte unit.
+__device__ __forceinline__ u32x4 lds_2runs(const uint16_t* p0, const uint16_t* p1) {
   const u32x2 a = *reinterpret_cast<const u32x2*>(p0);
   const u32x2 b = *reinterpret_cast<const u32x2*>(p1);
-  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+  return u32x4{a[0], a[1], b[0], b[1]};
 }
 
 template <bool VEC>
@@ -190,90 +224,83 @@ __device__ __forceinline__ TokRaw load_tok(const PrefillParams& p, int64_t t, in
   return r;
 }
 
+// First chunk slot of document i (i = n_docs gives the slot count).
+__device__ __forceinline__ int64_t doc_slot0(const int32_t* cu, int i) {
+  return int64_t(i) + (int64_t(cu[i]) >> 4);
+}
+
+// The document owning chunk slot sigma: the largest i in [0, n_docs] with
+// doc_slot0(i) <= sigma (doc_slot0 is strictly increasing and doc_slot0(0) = 0).
+// Every thread of the workgroup calls it; each step narrows the window
+// 256-fold with one load per thread.
+__device__ int find_doc(const int32_t* cu, int n_docs, int64_t sigma, int tid) {
+  int lo = 0;
+  int len = n_docs + 1;  // window [lo, lo + len), doc_slot0(lo) <= sigma
+  while (len > kThreads) {
+    const int stride = (len + kThreads - 1) / kThreads;
+    const int off = tid * stride;
+    const bool le = off < len && doc_slot0(cu, lo + off) <= sigma;
+    const int cnt = __syncthreads_count(le);
+    lo += (cnt - 1) * stride;
+    len = min(stride, n_docs + 1 - lo);
+  }
+  const bool le = tid < len && doc_slot0(cu, lo + tid) <= sigma;
+  return lo + __syncthreads_count(le) - 1;
+}
+
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Preparation: one 256-thread workgroup per (chunk slot, group of up to
+// kPrepHeads heads). Everything of the chunk that does not depend on the
+// state, written to the chunk record of each head; the next head's token
+// inputs are loaded while the current head is processed.
+constexpr int kPrepHeads = 4;
+
 template <bool VEC>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder ord) {
+__global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillParams p) {
   extern __shared__ __align__(16) float psmem_raw[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int g4 = lane >> 4;     // lane group inside a wave
+  const int g4 = lane >> 4;
   const int n16 = lane & 15;
-  const int h = int(blockIdx.x % p.H);
-  const int rank = int(blockIdx.x / p.H);
-  const int doc = ord.n > 0 ? ord.doc[rank] : rank;
+  const int64_t sigma = blockIdx.x;
+  const int h0 = int(blockIdx.y) * kPrepHeads;
+  const int h1 = min(h0 + kPrepHeads, p.H);
+
+  const int doc = find_doc(p.cu_seqlens, p.n_docs, sigma, tid);
+  if (doc >= p.n_docs) return;
   const int64_t t0 = p.cu_seqlens[doc];
   const int64_t len = int64_t(p.cu_seqlens[doc + 1]) - t0;
+  const int64_t j = sigma - doc_slot0(p.cu_seqlens, doc);
+  if (j * C >= len) return;  // a slot between documents
   const int32_t slot = p.state_indices[doc];
-  const bool active = slot >= 0 && int64_t(slot) < p.num_slots;
-
-  if (!active) {  // zero outputs, no state access
-    for (int64_t e = tid; e < len * D; e += 256)
-      p.out[(t0 + e / D) * p.out_tok_stride + h * D + (e % D)] = 0;
-    return;
-  }
-  uint16_t* sp = p.state_pool + int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS;
-  if (len == 0) {  // final state = initial state: untouched, or zeros without one
-    if (!p.use_initial_state)
-      for (int e = tid; e < HEAD_ELEMS; e += 256) sp[e] = 0;
-    return;
-  }
+  if (slot < 0 || int64_t(slot) >= p.num_slots) return;  // the chain writes zeros
+  const int64_t tc0 = t0 + j * C;
+  const int c = int(min<int64_t>(C, len - j * C));
   PSmem s = pcarve(psmem_raw);
 
-  // ---- initial state into the accumulator layout (all 16 loads issued
-  // before any is waited for)
-  f32x4 acc[8][2];
-  if (p.use_initial_state) {
-    u32x2 w[8][2];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        w[mt][nt] = gload4<VEC>(sp + (32 * wave + 16 * nt + n16) * D + 16 * mt + 4 * g4);
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        acc[mt][nt] = f32x4{bf_lo(w[mt][nt][0]), bf_hi(w[mt][nt][0]), bf_lo(w[mt][nt][1]),
-                            bf_hi(w[mt][nt][1])};
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  const int tt = tid >> 4;        // prologue: token of this lane
+  const int c0 = (tid & 15) * 8;  // prologue: 8 key / value channels of this lane
+  const bool valid = tt < c;
+  TokRaw raw = load_tok<VEC>(p, tc0 + tt, h0, c0, valid);
 
-  const float neg_ea = -fexp(p.A_log[h]);
-  const int tt = tid >> 4;           // prologue: token of this lane
-  const int c0 = (tid & 15) * 8;     // prologue: 8 key / value channels of this lane
-  float dtb[8];
-  load8_f32<VEC>(p.dt_bias + h * D + c0, dtb);
-  const int nchunks = int((len + C - 1) / C);
-  const int ots32 = static_cast<int>(p.out_tok_stride);  // host-checked to fit a buffer range
-  TokRaw raw = load_tok<VEC>(p, t0 + tt, h, c0, tt < len);
-
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int64_t tc0 = t0 + int64_t(ch) * C;
-    const int c = int(min<int64_t>(C, len - int64_t(ch) * C));
-
-    // ---- P2: token prologue -> q_hat, k_hat, g, v, beta (rows >= c are zeros)
+  for (int h = h0; h < h1; ++h) {
+    // ---- token prologue -> q_hat, k_hat, g, v, beta (rows >= c are zeros)
     {
-      float q[8], k[8], gr[8], vv[8];
+      const TokRaw cur = raw;
+      if (h + 1 < h1) raw = load_tok<VEC>(p, tc0 + tt, h + 1, c0, valid);
+      const float neg_ea = -fexp(p.A_log[h]);
+      float dtb[8];
+      load8_f32<VEC>(p.dt_bias + h * D + c0, dtb);
+      float q[8], k[8], gr[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        q[2 * e] = bf_lo(raw.q[e]);  q[2 * e + 1] = bf_hi(raw.q[e]);
-        k[2 * e] = bf_lo(raw.k[e]);  k[2 * e + 1] = bf_hi(raw.k[e]);
-        gr[2 * e] = bf_lo(raw.g[e]); gr[2 * e + 1] = bf_hi(raw.g[e]);
-        vv[2 * e] = bf_lo(raw.v[e]); vv[2 * e + 1] = bf_hi(raw.v[e]);
+        q[2 * e] = bf_lo(cur.q[e]);  q[2 * e + 1] = bf_hi(cur.q[e]);
+        k[2 * e] = bf_lo(cur.k[e]);  k[2 * e + 1] = bf_hi(cur.k[e]);
+        gr[2 * e] = bf_lo(cur.g[e]); gr[2 * e + 1] = bf_hi(cur.g[e]);
       }
-      const uint16_t braw = raw.b;
-      // prefetch the next chunk's inputs while this one runs
-      if (ch + 1 < nchunks) {
-        const int64_t tn = tc0 + C + tt;
-        raw = load_tok<VEC>(p, tn, h, c0, tn < t0 + len);
-      }
-      const bool valid = tt < c;
       float sq = 0.f, sk = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -289,16 +316,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
         s.qh[tt * RS + c0 + e] = q[e] * rq;
         s.kh[tt * RS + c0 + e] = k[e] * rk;
         s.gg[tt * RS + c0 + e] = valid ? fgate(gr[e] + dtb[e], neg_ea, p.lower_bound) : 0.f;
-        s.vv[tt * RS + c0 + e] = vv[e];
       }
-      if ((tid & 15) == 0) s.beta[tt] = valid ? fsigmoid(bf1(braw)) : 0.f;
+      *reinterpret_cast<u32x4*>(s.vv + tt * VLD + c0) = cur.v;
+      if ((tid & 15) == 0) s.beta[tt] = valid ? fsigmoid(bf1(cur.b)) : 0.f;
     }
     __syncthreads();
 
-    // ---- P3: thread (c, half) owns key channel c = tid % 128 and tokens
+    // ---- thread (c, half) owns key channel c = tid % 128 and tokens
     // 8 half .. 8 half + 7: Gam prefix (every thread sums all 16 gates of its
-    // channel), the scaled rows for A and P, and the chain's bf16 operands
-    // exp(Gam) q_hat and (exp(Gam_last - Gam) k_hat)^T.
+    // channel), the scaled rows for A and P as bf16 hi / lo pairs (MFMA
+    // operands, written over the fp32 rows they come from: hi in the first
+    // 128 bf16 of a row, lo in the next 128), the fp32 right-hand side of W,
+    // and the chain's bf16 operands exp(Gam) q_hat and exp(Gam_last - Gam) k_hat.
     {
       const int cc = tid & 127;
       const int r0 = (tid >> 7) * 8;
@@ -311,76 +340,93 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
       }
       const float mid = 0.5f * acc_g;  // padded rows carry g = 0
       const float em = fexp(mid);
+      float kq[8], qq[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        kq[i] = s.kh[(r0 + i) * RS + cc];
+        qq[i] = s.qh[(r0 + i) * RS + cc];
+      }
+      __syncthreads();  // every fp32 row and every gate is read before any is rewritten
       if (r0 == 0) {
         s.egl[cc] = fexp(acc_g);
         s.em[cc] = em;
       }
+      uint16_t* khp = reinterpret_cast<uint16_t*>(s.kh);
+      uint16_t* qhp = reinterpret_cast<uint16_t*>(s.qh);
+      uint16_t* kbp = reinterpret_cast<uint16_t*>(s.kb);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = r0 + i;
-        const float gr_ = r0 == 0 ? gam[i] : gam[8 + i];
+        const float g_first = gam[i], g_second = gam[8 + i];  // both loaded: a select of
+        const float gr_ = r0 == 0 ? g_first : g_second;         // values, not of addresses
         const float ea = fexp(gr_ - mid), eb = fexp(mid - gr_);
-        const float kh = s.kh[r * RS + cc];
-        const float qh = s.qh[r * RS + cc];
-        const float kb = kh * eb;
-        s.qh[r * RS + cc] = qh * ea;
-        s.kh[r * RS + cc] = kh * ea;
-        s.kb[r * RS + cc] = kb;
-        s.qop[r * XLD + cc] = to_bf16(qh * ea * em);
+        const float kb = kq[i] * eb;
         uint16_t hi, lo;
+        split_bf16(qq[i] * ea, hi, lo);
+        qhp[r * 2 * RS + cc] = hi;
+        qhp[r * 2 * RS + D + cc] = lo;
+        s.kw[r * RS + cc] = kq[i] * ea;
+        split_bf16(kq[i] * ea, hi, lo);
+        khp[r * 2 * RS + cc] = hi;
+        khp[r * 2 * RS + D + cc] = lo;
+        split_bf16(kb, hi, lo);
+        kbp[r * 2 * RS + cc] = hi;
+        kbp[r * 2 * RS + D + cc] = lo;
+        s.qop[r * QLD + cc] = to_bf16(qq[i] * ea * em);
         split_bf16(em * kb, hi, lo);  // exp(Gam_last - m) = exp(m)
-        s.ktop[cc * TLD + r] = hi;
-        s.ktop[D * TLD + cc * TLD + r] = lo;
+        s.ktop[r * D + cc] = hi;
+        s.ktop[C * D + r * D + cc] = lo;
       }
     }
     __syncthreads();
 
-    // ---- P4: A = (e^(Gam-m) k)(e^(m-Gam) k)^T on wave 0, P = (e^(Gam-m) q)(e^(m-Gam) k)^T on
-    // wave 1 (three hi/lo terms each); lane (row m = lane%16, group g4).
+    // ---- A = (e^(Gam-m) k)(e^(m-Gam) k)^T on wave 0, P = (e^(Gam-m) q)(e^(m-Gam) k)^T on
+    // wave 1 (three hi/lo terms each, fragments read straight from the bf16
+    // pairs; one accumulator per term so the products do not wait on each other).
     if (wave < 2) {
-      const float* left = wave == 0 ? s.kh : s.qh;
-      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* left = reinterpret_cast<const uint16_t*>(wave == 0 ? s.kh : s.qh);
+      const uint16_t* right = reinterpret_cast<const uint16_t*>(s.kb);
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        float x[8], y[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          x[e] = left[n16 * RS + 32 * kt + 8 * g4 + e];
-          y[e] = s.kb[n16 * RS + 32 * kt + 8 * g4 + e];
-        }
-        bf16x8 xh, xl, yh, yl;
-        split8(x, xh, xl);
-        split8(y, yh, yl);
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yh, a, 0, 0, 0);
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yl, a, 0, 0, 0);
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, yh, a, 0, 0, 0);
+        const int off = n16 * 2 * RS + 32 * kt + 8 * g4;
+        const bf16x8 xh = *reinterpret_cast<const bf16x8*>(left + off);
+        const bf16x8 xl = *reinterpret_cast<const bf16x8*>(left + off + D);
+        const bf16x8 yh = *reinterpret_cast<const bf16x8*>(right + off);
+        const bf16x8 yl = *reinterpret_cast<const bf16x8*>(right + off + D);
+        a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yh, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yl, a1, 0, 0, 0);
+        a2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, yh, a2, 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g4 + i, j = n16;
-        if (wave == 0) s.am[r * C + j] = j < r ? a[i] : 0.f;
-        else s.pop[r * C + j] = to_bf16(j <= r ? a[i] : 0.f);
+        const int r = 4 * g4 + i, jj = n16;
+        const float a = a0[i] + (a1[i] + a2[i]);
+        if (wave == 0) s.am[r * C + jj] = jj < r ? a : 0.f;
+        else s.pop[r * C + jj] = to_bf16(jj <= r ? a : 0.f);
       }
     }
     __syncthreads();
 
-    // ---- P5: forward substitution. Threads 0..127: W (key channel c),
-    // stored as bf16 hi / lo; threads 128..255: U0 (value channel v).
+    // ---- forward substitution. Threads 0..127: W (key channel c), stored as
+    // bf16 hi / lo; threads 128..255: U0 (value channel v).
     {
       const int cc = tid & 127;
-      const float* rhs = tid < 128 ? s.kh : s.vv;
       // Right-looking: once x_j is known it is taken off every later row's
-      // remainder, so the updates of one step are independent and the chain
-      // of dependent operations is two per row; each row still accumulates
-      // its terms in the order j = 0, 1, ...
+      // remainder; each row still accumulates its terms in the order j = 0, 1, ...
       float x[C];
+      if (tid < 128) {
 #pragma unroll
-      for (int r = 0; r < C; ++r) x[r] = rhs[r * RS + cc];
+        for (int r = 0; r < C; ++r) x[r] = s.kw[r * RS + cc];
+      } else {
 #pragma unroll
-      for (int j = 0; j < C; ++j) {
-        x[j] *= s.beta[j];
+        for (int r = 0; r < C; ++r) x[r] = bf1(s.vv[r * VLD + cc]);
+      }
 #pragma unroll
-        for (int r = j + 1; r < C; ++r) x[r] = fmaf(-s.am[r * C + j], x[j], x[r]);
+      for (int jj = 0; jj < C; ++jj) {
+        x[jj] *= s.beta[jj];
+#pragma unroll
+        for (int r = jj + 1; r < C; ++r) x[r] = fmaf(-s.am[r * C + jj], x[jj], x[r]);
       }
       if (tid < 128) {
         const float em = s.em[cc];
@@ -398,106 +444,223 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, DocOrder 
     }
     __syncthreads();
 
-    // ---- chain for this wave's 32 value channels
+    // ---- the chunk record, one 16-byte unit per thread and round
+    u32x4* rec = reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.workspace) +
+                                          (sigma * p.H + h) * int64_t(kRecBytes));
+#pragma unroll
+    for (int rd = 0; rd < kRecRounds; ++rd) {
+      const int u = tid + kThreads * rd;
+      u32x4 w;
+      if (u < kRecQ / 16) {  // W
+        const int kt = u >> 7, part = (u >> 6) & 1, l = u & 63;
+        const uint16_t* row = s.wop + part * C * XLD + (l & 15) * XLD + 32 * kt + 4 * (l >> 4);
+        w = lds_2runs(row, row + 16);
+      } else if (u < kRecKT / 16) {  // Q
+        const int kt = (u - kRecQ / 16) >> 6, l = u & 63;
+        const uint16_t* row = s.qop + (l & 15) * QLD + 32 * kt + 4 * (l >> 4);
+        w = lds_2runs(row, row + 16);
+      } else if (u < kRecU0 / 16) {  // KT: tokens 4g4 .. 4g4+3 of key channel 16mt + n16
+        const int mt = (u - kRecKT / 16) >> 6, l = u & 63;
+        const uint16_t* col = s.ktop + 4 * (l >> 4) * D + 16 * mt + (l & 15);
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          const uint16_t* cp = col + part * C * D;
+          w[2 * part] = uint32_t(cp[0]) | (uint32_t(cp[D]) << 16);
+          w[2 * part + 1] = uint32_t(cp[2 * D]) | (uint32_t(cp[3 * D]) << 16);
+        }
+      } else if (u < kRecP / 16) {  // U0
+        const int vt = (u - kRecU0 / 16) >> 6, l = u & 63;
+        const float* col = s.u0 + 4 * (l >> 4) * RS + 16 * vt + (l & 15);
+        w = u32x4{__float_as_uint(col[0]), __float_as_uint(col[RS]),
+                  __float_as_uint(col[2 * RS]), __float_as_uint(col[3 * RS])};
+      } else if (u < kRecEG / 16) {  // P: lanes 2q and 2q+1
+        const int l0 = 2 * (u - kRecP / 16);
+        w = lds_2runs(s.pop + (l0 & 15) * C + 4 * (l0 >> 4),
+                      s.pop + ((l0 + 1) & 15) * C + 4 * ((l0 + 1) >> 4));
+      } else if (u < kRecUnits) {  // EG
+        w = *reinterpret_cast<const u32x4*>(s.egl + 4 * (u - kRecEG / 16));
+      } else {
+        continue;
+      }
+      rec[u] = w;
+    }
+    __syncthreads();  // the record is read out before the next head rewrites the arrays
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chain: one 512-thread workgroup per (document, head), documents longest
+// first. Wave w keeps value channels 16w .. 16w+15 of the fp32 state in
+// registers (two waves per SIMD, so one wave's MFMA and LDS latencies overlap
+// the other's arithmetic). Chunk records move HBM -> registers one chunk
+// ahead of use and registers -> LDS (double buffer) one chunk ahead, so a
+// chunk's operands are in LDS when it starts and the next record's loads
+// overlap its arithmetic.
+constexpr int kChainThreads = 512;
+constexpr int kChainRounds = (kRecUnits + kChainThreads - 1) / kChainThreads;  // 4
+static_assert(kRecUnits > (kChainRounds - 1) * kChainThreads, "every round has work");
+
+template <bool VEC>
+__global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, DocOrder ord) {
+  __shared__ __align__(16) uint8_t rbuf[2][kRecBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g4 = lane >> 4;
+  const int n16 = lane & 15;
+  const int v = 16 * wave + n16;  // value channel of this lane
+  const int h = int(blockIdx.x % p.H);
+  const int rank = int(blockIdx.x / p.H);
+  const int doc = ord.n > 0 ? ord.doc[rank] : rank;
+  const int64_t t0 = p.cu_seqlens[doc];
+  const int64_t len = int64_t(p.cu_seqlens[doc + 1]) - t0;
+  const int32_t slot = p.state_indices[doc];
+  const bool active = slot >= 0 && int64_t(slot) < p.num_slots;
+
+  if (!active) {  // zero outputs, no state access
+    for (int64_t e = tid; e < len * D; e += kChainThreads)
+      p.out[(t0 + e / D) * p.out_tok_stride + h * D + (e % D)] = 0;
+    return;
+  }
+  uint16_t* sp = p.state_pool + int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS;
+  if (len == 0) {  // final state = initial state: untouched, or zeros without one
+    if (!p.use_initial_state)
+      for (int e = tid; e < HEAD_ELEMS; e += kChainThreads) sp[e] = 0;
+    return;
+  }
+
+  const int nchunks = int((len + C - 1) / C);
+  const int64_t sigma0 = doc_slot0(p.cu_seqlens, doc);
+  const uint8_t* ws = static_cast<const uint8_t*>(p.workspace);
+  auto rec_of = [&](int ch) {
+    return reinterpret_cast<const u32x4*>(ws + ((sigma0 + ch) * p.H + h) * int64_t(kRecBytes));
+  };
+  // Thread tid moves units tid + 512 rd; the units past the record's end in
+  // the last round load a unit of the record again (a fixed load count per
+  // chunk) and are not stored.
+  u32x4 pre[kChainRounds];
+  auto load_rec = [&](int ch) {
+    const u32x4* r = rec_of(ch);
+#pragma unroll
+    for (int rd = 0; rd < kChainRounds; ++rd) {
+      const int u = tid + kChainThreads * rd;
+      pre[rd] = __builtin_nontemporal_load(r + (u < kRecUnits ? u : u - kRecUnits));
+    }
+  };
+  auto store_rec = [&](int b) {
+    u32x4* d = reinterpret_cast<u32x4*>(&rbuf[b][0]);
+#pragma unroll
+    for (int rd = 0; rd < kChainRounds; ++rd) {
+      const int u = tid + kChainThreads * rd;
+      if (rd < kChainRounds - 1 || u < kRecUnits) d[u] = pre[rd];
+    }
+  };
+
+  load_rec(0);
+
+  // ---- initial state into the accumulator layout (all 8 loads issued
+  // before any is waited for)
+  f32x4 acc[8];
+  if (p.use_initial_state) {
+    u32x2 w[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) w[mt] = gload4<VEC>(sp + v * D + 16 * mt + 4 * g4);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+      acc[mt] = f32x4{bf_lo(w[mt][0]), bf_hi(w[mt][0]), bf_lo(w[mt][1]), bf_hi(w[mt][1])};
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  store_rec(0);
+  load_rec(min(1, nchunks - 1));
+  __syncthreads();
+
+  const int ots32 = static_cast<int>(p.out_tok_stride);  // host-checked to fit a buffer range
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int64_t tc0 = t0 + int64_t(ch) * C;
+    const int c = int(min<int64_t>(C, len - int64_t(ch) * C));
+    const uint8_t* R = &rbuf[ch & 1][0];
+
     // Output rows of this chunk as a buffer range of exactly c rows: a store
     // to a padded row (r >= c) is out of range and discarded, so the number
-    // of store instructions does not depend on c (the compiler can then count
-    // them and never waits for them before the next chunk's token words).
+    // of store instructions does not depend on c.
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
         p.out + tc0 * p.out_tok_stride + h * D, 0,
         static_cast<int>(((c - 1) * p.out_tok_stride + D) * 2), kBufferWord3);
-    f32x4 yw[2], yq[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      yw[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      yq[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    // W S^T in three hi/lo terms (one accumulator each, so the products do
+    // not wait on each other) and (e^Gam q) S^T in one
+    f32x4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = y0, y2 = y0, yq = y0;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      const int ka = 32 * kt + 4 * g4, kb2 = ka + 16;
-      const bf16x8 whi = lds_bf16x8_2runs(s.wop + n16 * XLD + ka, s.wop + n16 * XLD + kb2);
-      const bf16x8 wlo = lds_bf16x8_2runs(s.wop + C * XLD + n16 * XLD + ka,
-                                          s.wop + C * XLD + n16 * XLD + kb2);
-      const bf16x8 qhi = lds_bf16x8_2runs(s.qop + n16 * XLD + ka, s.qop + n16 * XLD + kb2);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const f32x4 s0 = acc[2 * kt][nt], s1 = acc[2 * kt + 1][nt];
-        const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-        bf16x8 shi, slo;
-        split8(sv, shi, slo);
-        yw[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, shi, yw[nt], 0, 0, 0);
-        yw[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, slo, yw[nt], 0, 0, 0);
-        yw[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, shi, yw[nt], 0, 0, 0);
-        yq[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi, shi, yq[nt], 0, 0, 0);
-      }
+      const bf16x8 whi = *reinterpret_cast<const bf16x8*>(R + kRecW + ((2 * kt) * 64 + lane) * 16);
+      const bf16x8 wlo =
+          *reinterpret_cast<const bf16x8*>(R + kRecW + ((2 * kt + 1) * 64 + lane) * 16);
+      const bf16x8 qhi = *reinterpret_cast<const bf16x8*>(R + kRecQ + (kt * 64 + lane) * 16);
+      const f32x4 s0 = acc[2 * kt], s1 = acc[2 * kt + 1];
+      const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      bf16x8 shi, slo;
+      split8(sv, shi, slo);
+      y0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, shi, y0, 0, 0, 0);
+      y1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, slo, y1, 0, 0, 0);
+      y2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, shi, y2, 0, 0, 0);
+      yq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi, shi, yq, 0, 0, 0);
     }
     // U = U0 - W S^T (accumulator layout: rows 4*g4 + i, value channel of the lane)
-    s16x4 uhi[2], ulo[2];
-    const s16x4 pfr = __builtin_bit_cast(
-        s16x4, *reinterpret_cast<const u32x2*>(s.pop + n16 * C + 4 * g4));
+    const f32x4 u0 = *reinterpret_cast<const f32x4*>(R + kRecU0 + (wave * 64 + lane) * 16);
+    s16x4 uhi, ulo;
+    split4(u0 - (y0 + (y1 + y2)), uhi, ulo);
+    // O = scale ((e^Gam q) S^T + P U); rows r >= c fall outside the buffer
+    // range and are dropped by the store itself
+    const s16x4 pfr = *reinterpret_cast<const s16x4*>(R + kRecP + lane * 8);
+    const f32x4 o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pfr, uhi, yq, 0, 0, 0);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int v = 32 * wave + 16 * nt + n16;
-      f32x4 u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = s.u0[(4 * g4 + i) * RS + v] - yw[nt][i];
-      split4(u, uhi[nt], ulo[nt]);
-      // O = scale ((e^Gam q) S^T + P U); rows r >= c fall outside the
-      // buffer range and are dropped by the store itself
-      f32x4 o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pfr, uhi[nt], yq[nt], 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g4 + i;
-        __builtin_amdgcn_raw_buffer_store_b16(to_bf16(p.scale * o[i]), orsrc,
-                                              (r * ots32 + v) * 2, 0, kStoreNontemporal);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g4 + i;
+      __builtin_amdgcn_raw_buffer_store_b16(to_bf16(p.scale * o[i]), orsrc, (r * ots32 + v) * 2,
+                                            0, kStoreNontemporal);
     }
     // S = S diag(e^Gam_last) + U^T K~  (contraction over the chunk's tokens)
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      const int kr = 16 * mt + n16;  // key channel of this lane's A-fragment row
-      const s16x4 khi = __builtin_bit_cast(
-          s16x4, *reinterpret_cast<const u32x2*>(s.ktop + kr * TLD + 4 * g4));
-      const s16x4 klo = __builtin_bit_cast(
-          s16x4, *reinterpret_cast<const u32x2*>(s.ktop + D * TLD + kr * TLD + 4 * g4));
-      float e4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) e4[i] = s.egl[16 * mt + 4 * g4 + i];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        f32x4 a = acc[mt][nt];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] *= e4[i];
-        a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(khi, uhi[nt], a, 0, 0, 0);
-        a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(khi, ulo[nt], a, 0, 0, 0);
-        a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(klo, uhi[nt], a, 0, 0, 0);
-        acc[mt][nt] = a;
-      }
+      const u32x4 kk = *reinterpret_cast<const u32x4*>(R + kRecKT + (mt * 64 + lane) * 16);
+      const s16x4 khi = __builtin_bit_cast(s16x4, u32x2{kk[0], kk[1]});
+      const s16x4 klo = __builtin_bit_cast(s16x4, u32x2{kk[2], kk[3]});
+      const f32x4 e4 = *reinterpret_cast<const f32x4*>(R + kRecEG + (16 * mt + 4 * g4) * 4);
+      f32x4 a = acc[mt] * e4;
+      a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(khi, uhi, a, 0, 0, 0);
+      a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(khi, ulo, a, 0, 0, 0);
+      a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(klo, uhi, a, 0, 0, 0);
+      acc[mt] = a;
     }
-    // the next chunk's P2 rewrites only qh / kh / gg / vv / beta, which the
-    // chain does not read; its P3 (after the next barrier) rewrites the chain's
-    // operands.
+    // record ch+1 (its loads were issued a chunk ago) into the other buffer,
+    // last read before the previous barrier; then the loads of record ch+2
+    store_rec((ch + 1) & 1);
+    load_rec(min(ch + 2, nchunks - 1));
+    __syncthreads();  // this chunk's buffer is read; the next one is written
   }
 
   // ---- final state
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int v = 32 * wave + 16 * nt + n16;
-      const f32x4 a = acc[mt][nt];
-      gstore4<VEC>(sp + v * D + 16 * mt + 4 * g4,
-                   u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])});
-    }
+  for (int mt = 0; mt < 8; ++mt) {
+    const f32x4 a = acc[mt];
+    gstore4<VEC>(sp + v * D + 16 * mt + 4 * g4,
+                 u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])});
+  }
 }
 
-size_t prefill_workspace_bytes(int32_t, int64_t, int32_t) { return 0; }
+size_t prefill_workspace_bytes(int32_t n_docs, int64_t total_tokens, int32_t H) {
+  if (n_docs <= 0 || total_tokens <= 0 || H <= 0) return 0;
+  return size_t(int64_t(n_docs) + (total_tokens >> 4)) * size_t(H) * size_t(kRecBytes);
+}
 
 hipError_t launch_prefill(const PrefillParams& p, const int32_t* cu_host, bool vec,
                           hipStream_t stream) {
   const int64_t blocks = int64_t(p.n_docs) * p.H;
   if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (blocks > 0x7fffffff || p.H > 65535) return hipErrorInvalidValue;
+  const int64_t slots = int64_t(p.n_docs) + (p.total_tokens >> 4);
+  if (slots > 0x7fffffff) return hipErrorInvalidValue;
   // Longest documents first: their chains bound the makespan.
   DocOrder ord;
   ord.n = 0;
@@ -516,19 +679,28 @@ hipError_t launch_prefill(const PrefillParams& p, const int32_t* cu_host, bool v
     }
   }
   static const hipError_t attr = [] {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<true>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<true>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(kPrefillLds));
+                                       static_cast<int>(kPrepLds));
     if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<false>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<false>),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(kPrefillLds));
+                              static_cast<int>(kPrepLds));
     return e;
   }();
   if (attr != hipSuccess) return attr;
-  dim3 grid(static_cast<unsigned>(blocks)), block(256);
-  if (vec) hipLaunchKernelGGL((prefill_kernel<true>), grid, block, kPrefillLds, stream, p, ord);
-  else hipLaunchKernelGGL((prefill_kernel<false>), grid, block, kPrefillLds, stream, p, ord);
+  if (p.total_tokens > 0) {
+    dim3 pgrid(static_cast<unsigned>(slots),
+               static_cast<unsigned>((p.H + kPrepHeads - 1) / kPrepHeads)),
+        block(kThreads);
+    if (vec) hipLaunchKernelGGL((prep_kernel<true>), pgrid, block, kPrepLds, stream, p);
+    else hipLaunchKernelGGL((prep_kernel<false>), pgrid, block, kPrepLds, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(static_cast<unsigned>(blocks)), block(kChainThreads);
+  if (vec) hipLaunchKernelGGL((chain_kernel<true>), grid, block, 0, stream, p, ord);
+  else hipLaunchKernelGGL((chain_kernel<false>), grid, block, 0, stream, p, ord);
   return hipGetLastError();
 }
 

@@ -193,7 +193,10 @@ kda_status kda_verify_ucache_flush(int32_t B, int32_t T, int32_t H, int32_t K, i
 
 /*
  * kda_prefill_workspace_size -- bytes of device workspace kda_prefill_varlen
- * needs for these sizes (0 when nothing is needed). Pure host arithmetic.
+ * needs for these sizes (0 when nothing is needed, or when K or V is not 128).
+ * Pure host arithmetic: one 29,696-byte chunk record per (chunk slot, head),
+ * with (n_docs + floor(total_tokens / 16)) chunk slots, since a document's
+ * 16-token chunks are numbered from its index plus floor(first token / 16).
  */
 size_t kda_prefill_workspace_size(int32_t n_docs, int64_t total_tokens, int32_t H, int32_t K,
                                   int32_t V);
@@ -223,17 +226,22 @@ size_t kda_prefill_workspace_size(int32_t n_docs, int64_t total_tokens, int32_t 
  *  use_initial_state  1: start each chain from its slot; 0: from zeros
  *  out                bf16, element (t, h*128 + v) at t*out_tok_stride + h*128 + v
  *  workspace          device buffer of >= kda_prefill_workspace_size(...) bytes,
- *                     256-byte aligned (may be NULL when that size is 0)
+ *                     256-byte aligned (may be NULL when that size is 0); the
+ *                     per-chunk operands pass through it from the preparation
+ *                     kernel to the chain kernel, and its contents are
+ *                     meaningless after the call
  * A zero-length document writes no output; its final state equals its
  * initial state (left untouched with use_initial_state = 1, written as zeros
  * with use_initial_state = 0).
  * KDA_ERR_BAD_SEQLENS when cu_seqlens_host[0] != 0, it decreases, or its last
  * entry differs from total_tokens; KDA_ERR_WORKSPACE_TOO_SMALL when
- * workspace_bytes is short; KDA_ERR_UNSUPPORTED when out_tok_stride exceeds
- * 2^25 elements (16 output rows must span less than 2^31 bytes) or when
- * |lower_bound| > 5.5 (the
- * 16-token chunks factor each decay weight exp(G_r - G_j) into two exps of at
- * most 8 |lower_bound| each, which must stay well inside the fp32 range).
+ * workspace_bytes is short; KDA_ERR_NULL_POINTER when a workspace is needed
+ * and NULL; KDA_ERR_UNSUPPORTED when the workspace is not 256-byte aligned,
+ * when out_tok_stride exceeds 2^25 elements (16 output rows must span less
+ * than 2^31 bytes) or when |lower_bound| > 5.5 (the 16-token chunks factor
+ * each decay weight exp(G_r - G_j) into two exps of at most 8 |lower_bound|
+ * each, which must stay well inside the fp32 range). The call launches a
+ * preparation kernel and then a chain kernel on the stream.
  * Outputs are written in bf16 (round to nearest even); the final states are
  * rounded to bf16 once, at the end of each chain.
  */

@@ -122,17 +122,23 @@ def test_verify_host_validation(lib):
 
 def test_prefill_workspace_and_validation(lib):
     P = ctypes.c_void_p
-    assert lib.kda_prefill_workspace_size(4, 13888, 64, 128, 128) >= 0
+    # one 29,696-byte chunk record per (chunk slot, head); chunk slots number
+    # fewer than n_docs + floor(total_tokens / 16)
+    rec = 29696
+    assert lib.kda_prefill_workspace_size(4, 13888, 64, 128, 128) == (4 + 868) * 64 * rec
+    assert lib.kda_prefill_workspace_size(14, 16384, 12, 128, 128) == (14 + 1024) * 12 * rec
+    assert lib.kda_prefill_workspace_size(3, 0, 12, 128, 128) == 0
     assert lib.kda_prefill_workspace_size(4, 13888, 64, 64, 128) == 0
 
     def call(cu, total, **kw):
-        a = dict(n=len(cu) - 1, H=2, K=128, ws=1 << 40, ots=256, lb=-5.0)
+        p = P(1 << 20)
+        a = dict(n=len(cu) - 1, H=2, K=128, ws=1 << 40, ots=256, lb=-5.0, ws_ptr=p)
         a.update(kw)
         arr = (ctypes.c_int32 * len(cu))(*cu)
-        p = P(1 << 20)
         return lib.kda_prefill_varlen(a["n"], total, a["H"], a["K"], 128, arr, p, p, 256, p,
                                       256, p, 256, p, 256, p, 2, p, p, a["lb"], 1.0, p, 4,
-                                      2 * 128 * 128, p, 1, p, a["ots"], p, a["ws"], P(0))
+                                      2 * 128 * 128, p, 1, p, a["ots"], a["ws_ptr"], a["ws"],
+                                      P(0))
 
     assert call([1, 5], 5) == SEQ       # must start at 0
     assert call([0, 5, 3], 3) == SEQ    # must not decrease
@@ -143,3 +149,6 @@ def test_prefill_workspace_and_validation(lib):
     assert call([0, 5], 5, lb=-5.6) == UNSUP
     assert call([0, 5], 5, lb=float("nan")) == UNSUP
     assert call([0], 0) == OK           # no documents: nothing to do
+    assert call([0, 5], 5, ws=2 * rec - 1) == WS   # one slot, two heads
+    assert call([0, 5], 5, ws=2 * rec, ws_ptr=P(0)) == NULLP
+    assert call([0, 5], 5, ws=2 * rec, ws_ptr=P((1 << 20) + 128)) == UNSUP  # 256-byte aligned

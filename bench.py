@@ -379,12 +379,13 @@ def main():
         return
     if args.mode == "profile-prefill":
         for lens in (synth.DOCS_4, synth.DOCS_14):
-            ps = PrefillSetup(lens, 64, torch, kda, synth)
-            for c in ps.calls() * 4:
-                c()
-            torch.cuda.synchronize()
-            del ps
-        log("profile: 4 x prefill H=64 4 docs, 4 x prefill H=64 14-doc mix")
+            for Hp in (64, 12):
+                ps = PrefillSetup(lens, Hp, torch, kda, synth)
+                for c in ps.calls() * 4:
+                    c()
+                torch.cuda.synchronize()
+                del ps
+        log("profile: 4 x prefill at H=64 then H=12, on the 4-document set, then the 14-doc mix")
         return
 
     B = 512

@@ -13,6 +13,10 @@ they document as outputs in place.
 Readings that are "parity unpinned" (the oracle encodes them; no page fixes
 them): the gate formula, the L2-norm epsilon, the ring addressing through
 cache_base, the state orientation [V][K] and A_log being per head.
+
+gate_mode (every entry): 0 takes raw gate and beta logits; bit GATE_PRECOMPUTED
+takes the log-decay g itself (clamped into [lower_bound, 0]; a_log and dt_bias
+may be None); bit BETA_PRESIGMOID takes beta itself.
 """
 from __future__ import annotations
 
@@ -60,9 +64,11 @@ def _suffix(real) -> str:
     raise TypeError(f"oracle precision must be float32 or float64, got {real}")
 
 
-def _rp(a: np.ndarray, real):
-    assert a.dtype == np.dtype(real) and a.flags["C_CONTIGUOUS"], (a.dtype, real)
+def _rp(a, real):
     ctype = ctypes.c_float if np.dtype(real) == np.float32 else ctypes.c_double
+    if a is None:  # an input the chosen gate mode does not read
+        return ctypes.POINTER(ctype)()
+    assert a.dtype == np.dtype(real) and a.flags["C_CONTIGUOUS"], (a.dtype, real)
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
 
@@ -92,15 +98,20 @@ def bf16_round_bits(x: np.ndarray) -> np.ndarray:
     return out
 
 
-def prologue(q, k, graw, beta_logit, a_log_h, dt_bias_h, lower_bound, real=np.float64):
+GATE_PRECOMPUTED = 1  # gate_mode bit: graw holds the log-decay g itself
+BETA_PRESIGMOID = 2   # gate_mode bit: beta_logit holds beta itself
+
+
+def prologue(q, k, graw, beta_logit, a_log_h, dt_bias_h, lower_bound, real=np.float64,
+             gate_mode=0):
     """One head's per-token prologue -> (q_hat, k_hat, g, beta)."""
     K = q.shape[0]
     qh, kh, g = (np.zeros(K, real) for _ in range(3))
     beta = np.zeros(1, real)
     f = getattr(lib(), "orc_prologue_" + _suffix(real))
     f(ctypes.c_int(K), _rp(q, real), _rp(k, real), _rp(graw, real), _rs(beta_logit, real),
-      _rs(a_log_h, real), _rp(dt_bias_h, real), _rs(lower_bound, real),
-      _rp(qh, real), _rp(kh, real), _rp(g, real), _rp(beta, real))
+      _rs(a_log_h or 0.0, real), _rp(dt_bias_h, real), _rs(lower_bound, real),
+      ctypes.c_int(gate_mode), _rp(qh, real), _rp(kh, real), _rp(g, real), _rp(beta, real))
     return qh, kh, g, float(beta[0])
 
 
@@ -127,7 +138,7 @@ def replay(ckpt, kc, uc, gc, base, hist, real=np.float64):
 
 
 def decode(q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,
-           bf16_storage=True, real=np.float32):
+           bf16_storage=True, real=np.float32, gate_mode=0):
     """T=1 decode. q/k/graw [B,H,K], v [B,H,V], beta_logit [B,H], pool [N,H,V,K]
     (updated in place), idx int32 [B]. Returns out [B,H,V]."""
     B, H, K = q.shape
@@ -138,13 +149,13 @@ def decode(q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, 
     f(B, H, K, V, _rp(q, real), _rp(k, real), _rp(v, real), _rp(graw, real),
       _rp(beta_logit, real), _rp(a_log, real), _rp(dt_bias, real), _rs(lower_bound, real),
       _rs(scale, real), _rp(pool, real), ctypes.c_int64(N), _ip(idx), _rp(out, real),
-      ctypes.c_int(1 if bf16_storage else 0))
+      ctypes.c_int(1 if bf16_storage else 0), ctypes.c_int(gate_mode))
     return out
 
 
 def verify(q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,
            k_cache, u_cache, g_cache, hist_len, cache_base, flush_min, w_ring,
-           bf16_storage=True, real=np.float32):
+           bf16_storage=True, real=np.float32, gate_mode=0):
     """Verify+fold. q/k/graw [B,T,H,K], v [B,T,H,V], beta_logit [B,T,H]; pool [N,H,V,K],
     k_cache/g_cache [N,H,R,K], u_cache [N,H,R,V] all updated in place. Returns out [B,T,H,V]."""
     B, T, H, K = q.shape
@@ -158,7 +169,7 @@ def verify(q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, 
       _rs(scale, real), _rp(pool, real), ctypes.c_int64(N), _ip(idx), _rp(k_cache, real),
       _rp(u_cache, real), _rp(g_cache, real), ctypes.c_int(R), _ip(hist_len), _ip(cache_base),
       ctypes.c_int(flush_min), ctypes.c_int(w_ring), _rp(out, real),
-      ctypes.c_int(1 if bf16_storage else 0))
+      ctypes.c_int(1 if bf16_storage else 0), ctypes.c_int(gate_mode))
     return out
 
 
@@ -175,23 +186,25 @@ def _prefill_args(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, sc
 
 
 def prefill(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,
-            use_initial_state=True, bf16_storage=True, real=np.float32):
+            use_initial_state=True, bf16_storage=True, real=np.float32, gate_mode=0):
     """Token-by-token varlen prefill. q/k/graw [Ttot,H,K], v [Ttot,H,V], beta_logit [Ttot,H],
     cu int32 [n_docs+1], idx int32 [n_docs], pool [N,H,V,K] updated in place. -> out [Ttot,H,V]."""
     out = np.zeros((q.shape[0], q.shape[1], v.shape[2]), real)
     f = getattr(lib(), "orc_prefill_tbt_" + _suffix(real))
     f(*_prefill_args(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool,
-                     idx, use_initial_state, out, real), ctypes.c_int(1 if bf16_storage else 0))
+                     idx, use_initial_state, out, real), ctypes.c_int(1 if bf16_storage else 0),
+      ctypes.c_int(gate_mode))
     return out
 
 
 def prefill_chunked(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,
-                    chunk, use_initial_state=True, real=np.float64):
+                    chunk, use_initial_state=True, real=np.float64, gate_mode=0):
     """Chunkwise (WY/UT) model of the same prefill, no storage rounding. -> out [Ttot,H,V]."""
     out = np.zeros((q.shape[0], q.shape[1], v.shape[2]), real)
     f = getattr(lib(), "orc_prefill_chunked_" + _suffix(real))
     f(*_prefill_args(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool,
-                     idx, use_initial_state, out, real), ctypes.c_int(int(chunk)))
+                     idx, use_initial_state, out, real), ctypes.c_int(int(chunk)),
+      ctypes.c_int(gate_mode))
     return out
 
 

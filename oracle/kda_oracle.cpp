@@ -95,9 +95,19 @@ Real store(Real x, int bf16_storage) {
 //   for Kimi K3 (KDA)", section "API"). Reading: the Mamba-style softplus gate
 //   clamped at lower_bound. softplus(x) = log1p(exp(x)), or x when x > 20.
 // * beta = sigmoid(beta logit) (beta_is_logit in the fast-path section).
+// * gate_mode (same page, same section: the raw form, where the kernel computes
+//   the decay and the sigmoid, and the API-default pre-computed form, log-space
+//   g and pre-sigmoided beta, with decay = exp(g)):
+//     bit 0 (pre-computed gate): graw holds the log-decay itself; it is used
+//       clamped into [lower_bound, 0], the range the raw gate lands in
+//       (reading); a_log and dt_bias are not read and may be null;
+//     bit 1 (pre-sigmoided beta): beta_logit holds beta itself.
+constexpr int kGatePrecomputed = 1;
+constexpr int kBetaPresigmoid = 2;
+
 template <class Real>
 void prologue(int K, const Real* q, const Real* k, const Real* graw, Real beta_logit,
-              Real a_log, const Real* dt_bias, Real lower_bound,
+              Real a_log, const Real* dt_bias, Real lower_bound, int gate_mode,
               Real* qh, Real* kh, Real* g, Real* beta) {
   Real sq = 0, sk = 0;
   for (int c = 0; c < K; ++c) {
@@ -110,13 +120,30 @@ void prologue(int K, const Real* q, const Real* k, const Real* graw, Real beta_l
     qh[c] = q[c] / nq;
     kh[c] = k[c] / nk;
   }
-  const Real ea = std::exp(a_log);
-  for (int c = 0; c < K; ++c) {
-    const Real x = graw[c] + dt_bias[c];
-    const Real sp = x > static_cast<Real>(20) ? x : std::log1p(std::exp(x));
-    g[c] = std::max(lower_bound, -ea * sp);
+  if (gate_mode & kGatePrecomputed) {
+    for (int c = 0; c < K; ++c)
+      g[c] = std::min(static_cast<Real>(0), std::max(lower_bound, graw[c]));
+  } else {
+    const Real ea = std::exp(a_log);
+    for (int c = 0; c < K; ++c) {
+      const Real x = graw[c] + dt_bias[c];
+      const Real sp = x > static_cast<Real>(20) ? x : std::log1p(std::exp(x));
+      g[c] = std::max(lower_bound, -ea * sp);
+    }
   }
-  *beta = static_cast<Real>(1) / (static_cast<Real>(1) + std::exp(-beta_logit));
+  *beta = (gate_mode & kBetaPresigmoid)
+              ? beta_logit
+              : static_cast<Real>(1) / (static_cast<Real>(1) + std::exp(-beta_logit));
+}
+
+// The per-head gate parameters, or nothing in the pre-computed gate mode.
+template <class Real>
+Real alog_of(const Real* a_log, int h, int gate_mode) {
+  return (gate_mode & kGatePrecomputed) ? static_cast<Real>(0) : a_log[h];
+}
+template <class Real>
+const Real* dtb_of(const Real* dt_bias, int h, int K, int gate_mode) {
+  return (gate_mode & kGatePrecomputed) ? nullptr : dt_bias + static_cast<int64_t>(h) * K;
 }
 
 // ---------------------------------------------------------------------------
@@ -170,7 +197,7 @@ template <class Real>
 void decode(int B, int H, int K, int V, const Real* q, const Real* k, const Real* v,
             const Real* graw, const Real* beta_logit, const Real* a_log, const Real* dt_bias,
             Real lower_bound, Real scale, Real* pool, int64_t N, const int32_t* idx,
-            Real* out, int bf16_storage) {
+            Real* out, int bf16_storage, int gate_mode) {
   const int64_t KV = i64(K) * V;
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int b = 0; b < B; ++b) {
@@ -183,8 +210,9 @@ void decode(int B, int H, int K, int V, const Real* q, const Real* k, const Real
       const int64_t tk = (i64(b) * H + h) * K;
       std::vector<Real> qh(K), kh(K), g(K), S(KV);
       Real beta;
-      prologue<Real>(K, q + tk, k + tk, graw + tk, beta_logit[i64(b) * H + h], a_log[h],
-                     dt_bias + i64(h) * K, lower_bound, qh.data(), kh.data(), g.data(), &beta);
+      prologue<Real>(K, q + tk, k + tk, graw + tk, beta_logit[i64(b) * H + h],
+                     alog_of(a_log, h, gate_mode), dtb_of(dt_bias, h, K, gate_mode),
+                     lower_bound, gate_mode, qh.data(), kh.data(), g.data(), &beta);
       Real* slot = pool + (i64(idx[b]) * H + h) * KV;
       std::copy(slot, slot + KV, S.begin());
       step<Real>(K, V, S.data(), qh.data(), kh.data(), v + (i64(b) * H + h) * V, g.data(),
@@ -250,7 +278,7 @@ void verify(int B, int T, int H, int K, int V, const Real* q, const Real* k, con
             const Real* graw, const Real* beta_logit, const Real* a_log, const Real* dt_bias,
             Real lower_bound, Real scale, Real* pool, int64_t N, const int32_t* idx, Real* kc,
             Real* uc, Real* gc, int R, const int32_t* hist_len, const int32_t* cache_base,
-            int flush_min, int w_ring, Real* out, int bf16_storage) {
+            int flush_min, int w_ring, Real* out, int bf16_storage, int gate_mode) {
   const int64_t KV = i64(K) * V;
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int b = 0; b < B; ++b) {
@@ -283,8 +311,8 @@ void verify(int B, int T, int H, int K, int V, const Real* q, const Real* k, con
         const int64_t tv = ((i64(b) * T + t) * H + h) * V;
         Real beta;
         prologue<Real>(K, q + tk, k + tk, graw + tk, beta_logit[(i64(b) * T + t) * H + h],
-                       a_log[h], dt_bias + i64(h) * K, lower_bound, qh.data(), kh.data(),
-                       g.data(), &beta);
+                       alog_of(a_log, h, gate_mode), dtb_of(dt_bias, h, K, gate_mode),
+                       lower_bound, gate_mode, qh.data(), kh.data(), g.data(), &beta);
         Real* o = out + tv;
         step<Real>(K, V, S.data(), qh.data(), kh.data(), v + tv, g.data(), beta, scale, o,
                    u.data());
@@ -320,7 +348,7 @@ void prefill_tbt(int n_docs, int H, int K, int V, const int32_t* cu, const Real*
                  const Real* k, const Real* v, const Real* graw, const Real* beta_logit,
                  const Real* a_log, const Real* dt_bias, Real lower_bound, Real scale,
                  Real* pool, int64_t N, const int32_t* idx, int use_initial_state, Real* out,
-                 int bf16_storage) {
+                 int bf16_storage, int gate_mode) {
   const int64_t KV = i64(K) * V;
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int d = 0; d < n_docs; ++d) {
@@ -339,8 +367,9 @@ void prefill_tbt(int n_docs, int H, int K, int V, const int32_t* cu, const Real*
       for (int t = t0; t < t1; ++t) {
         const int64_t tk = (i64(t) * H + h) * K;
         Real beta;
-        prologue<Real>(K, q + tk, k + tk, graw + tk, beta_logit[i64(t) * H + h], a_log[h],
-                       dt_bias + i64(h) * K, lower_bound, qh.data(), kh.data(), g.data(), &beta);
+        prologue<Real>(K, q + tk, k + tk, graw + tk, beta_logit[i64(t) * H + h],
+                       alog_of(a_log, h, gate_mode), dtb_of(dt_bias, h, K, gate_mode),
+                       lower_bound, gate_mode, qh.data(), kh.data(), g.data(), &beta);
         Real* o = out + (i64(t) * H + h) * V;
         step<Real>(K, V, S.data(), qh.data(), kh.data(), v + (i64(t) * H + h) * V, g.data(),
                    beta, scale, o, nullptr);
@@ -375,7 +404,7 @@ void prefill_chunked(int n_docs, int H, int K, int V, const int32_t* cu, const R
                      const Real* k, const Real* v, const Real* graw, const Real* beta_logit,
                      const Real* a_log, const Real* dt_bias, Real lower_bound, Real scale,
                      Real* pool, int64_t N, const int32_t* idx, int use_initial_state,
-                     Real* out, int chunk) {
+                     Real* out, int chunk, int gate_mode) {
   const int64_t KV = i64(K) * V;
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int d = 0; d < n_docs; ++d) {
@@ -401,9 +430,10 @@ void prefill_chunked(int n_docs, int H, int K, int V, const int32_t* cu, const R
         for (int r = 0; r < n; ++r) {
           const int t = c0 + r;
           const int64_t tk = (i64(t) * H + h) * K;
-          prologue<Real>(K, q + tk, k + tk, graw + tk, beta_logit[i64(t) * H + h], a_log[h],
-                         dt_bias + i64(h) * K, lower_bound, &Q[i64(r) * K], &Kh[i64(r) * K],
-                         g.data(), &be[r]);
+          prologue<Real>(K, q + tk, k + tk, graw + tk, beta_logit[i64(t) * H + h],
+                         alog_of(a_log, h, gate_mode), dtb_of(dt_bias, h, K, gate_mode),
+                         lower_bound, gate_mode, &Q[i64(r) * K], &Kh[i64(r) * K], g.data(),
+                         &be[r]);
           for (int c = 0; c < K; ++c)
             Gm[i64(r) * K + c] = (r ? Gm[i64(r - 1) * K + c] : static_cast<Real>(0)) + g[c];
           for (int x = 0; x < V; ++x) Vv[i64(r) * V + x] = v[(i64(t) * H + h) * V + x];
@@ -474,9 +504,10 @@ void prefill_chunked(int n_docs, int H, int K, int V, const int32_t* cu, const R
 #define ORC_INSTANTIATE(SUF, Real)                                                            \
   extern "C" void orc_prologue_##SUF(int K, const Real* q, const Real* k, const Real* graw,   \
                                      Real beta_logit, Real a_log, const Real* dt_bias,        \
-                                     Real lower_bound, Real* qh, Real* kh, Real* g,           \
-                                     Real* beta) {                                            \
-    prologue<Real>(K, q, k, graw, beta_logit, a_log, dt_bias, lower_bound, qh, kh, g, beta);  \
+                                     Real lower_bound, int gate_mode, Real* qh, Real* kh,     \
+                                     Real* g, Real* beta) {                                   \
+    prologue<Real>(K, q, k, graw, beta_logit, a_log, dt_bias, lower_bound, gate_mode, qh, kh, \
+                   g, beta);                                                                  \
   }                                                                                           \
   extern "C" void orc_step_##SUF(int K, int V, Real* S, const Real* qh, const Real* kh,       \
                                  const Real* v, const Real* g, Real beta, Real scale,         \
@@ -492,35 +523,38 @@ void prefill_chunked(int n_docs, int H, int K, int V, const int32_t* cu, const R
                                    const Real* v, const Real* graw, const Real* beta_logit,   \
                                    const Real* a_log, const Real* dt_bias, Real lower_bound,  \
                                    Real scale, Real* pool, int64_t N, const int32_t* idx,     \
-                                   Real* out, int bf16_storage) {                             \
+                                   Real* out, int bf16_storage, int gate_mode) {              \
     decode<Real>(B, H, K, V, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale,   \
-                 pool, N, idx, out, bf16_storage);                                            \
+                 pool, N, idx, out, bf16_storage, gate_mode);                                 \
   }                                                                                           \
   extern "C" void orc_verify_##SUF(                                                           \
       int B, int T, int H, int K, int V, const Real* q, const Real* k, const Real* v,         \
       const Real* graw, const Real* beta_logit, const Real* a_log, const Real* dt_bias,       \
       Real lower_bound, Real scale, Real* pool, int64_t N, const int32_t* idx, Real* kc,      \
       Real* uc, Real* gc, int R, const int32_t* hist_len, const int32_t* cache_base,          \
-      int flush_min, int w_ring, Real* out, int bf16_storage) {                               \
+      int flush_min, int w_ring, Real* out, int bf16_storage, int gate_mode) {                \
     verify<Real>(B, T, H, K, V, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound,       \
                  scale, pool, N, idx, kc, uc, gc, R, hist_len, cache_base, flush_min, w_ring, \
-                 out, bf16_storage);                                                          \
+                 out, bf16_storage, gate_mode);                                               \
   }                                                                                           \
   extern "C" void orc_prefill_tbt_##SUF(                                                      \
       int n_docs, int H, int K, int V, const int32_t* cu, const Real* q, const Real* k,       \
       const Real* v, const Real* graw, const Real* beta_logit, const Real* a_log,             \
       const Real* dt_bias, Real lower_bound, Real scale, Real* pool, int64_t N,               \
-      const int32_t* idx, int use_initial_state, Real* out, int bf16_storage) {               \
+      const int32_t* idx, int use_initial_state, Real* out, int bf16_storage,                 \
+      int gate_mode) {                                                                        \
     prefill_tbt<Real>(n_docs, H, K, V, cu, q, k, v, graw, beta_logit, a_log, dt_bias,         \
-                      lower_bound, scale, pool, N, idx, use_initial_state, out, bf16_storage); \
+                      lower_bound, scale, pool, N, idx, use_initial_state, out, bf16_storage, \
+                      gate_mode);                                                             \
   }                                                                                           \
   extern "C" void orc_prefill_chunked_##SUF(                                                  \
       int n_docs, int H, int K, int V, const int32_t* cu, const Real* q, const Real* k,       \
       const Real* v, const Real* graw, const Real* beta_logit, const Real* a_log,             \
       const Real* dt_bias, Real lower_bound, Real scale, Real* pool, int64_t N,               \
-      const int32_t* idx, int use_initial_state, Real* out, int chunk) {                      \
+      const int32_t* idx, int use_initial_state, Real* out, int chunk, int gate_mode) {       \
     prefill_chunked<Real>(n_docs, H, K, V, cu, q, k, v, graw, beta_logit, a_log, dt_bias,     \
-                          lower_bound, scale, pool, N, idx, use_initial_state, out, chunk);   \
+                          lower_bound, scale, pool, N, idx, use_initial_state, out, chunk,    \
+                          gate_mode);                                                         \
   }
 
 ORC_INSTANTIATE(f32, float)

@@ -596,3 +596,131 @@ def test_prefill_document_isolation_and_inactive(orc):
     for s in range(d["pool"].shape[0]):
         if s not in used:
             assert np.array_equal(p1[s].view(np.uint32), d["pool"][s].view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# Pre-computed gate convention ([decode] "T=1 fast path inside recurrent_kda":
+# the raw form computes decay and sigmoid in-kernel; the API-default form takes
+# log-space g and pre-sigmoided beta, decay = exp(g)).
+
+PRE = 1 | 2  # pre-computed gate and pre-sigmoided beta
+
+
+def _gate_np(graw, a_log, dt_bias, lb):
+    """The raw gate written out with numpy's own routines (fp64): softplus as
+    log(1 + e^x) through logaddexp, then the clamp."""
+    H = a_log.shape[0]
+    x = graw.reshape(graw.shape[:-2] + (H, 128)) + dt_bias.reshape(H, 128)
+    g = -np.exp(a_log)[:, None] * np.logaddexp(0.0, x)
+    return np.maximum(lb, g)
+
+
+def test_precomputed_mode_equals_raw_mode_fed_the_gate(orc):
+    """Decode, verify and prefill in the pre-computed mode, given g and beta
+    computed independently from the raw inputs, reproduce the raw mode."""
+    rng = _rng(200)
+    lb = -5.0
+    B, H, N = 3, 2, 4
+    d = _decode_inputs(rng, B, H, N, F64)
+    g = _gate_np(d["graw"], d["a_log"], d["dt_bias"], lb)
+    beta = scipy.special.expit(d["beta_logit"])
+    idx = np.array([3, 0, 1], np.int32)
+    p_raw, p_pre = d["pool"].copy(), d["pool"].copy()
+    o_raw = orc.decode(d["q"], d["k"], d["v"], d["graw"], d["beta_logit"], d["a_log"],
+                       d["dt_bias"], lb, 1.0, p_raw, idx, bf16_storage=False, real=F64)
+    o_pre = orc.decode(d["q"], d["k"], d["v"], np.ascontiguousarray(g), beta, None, None, lb,
+                       1.0, p_pre, idx, bf16_storage=False, real=F64, gate_mode=PRE)
+    np.testing.assert_allclose(o_pre, o_raw, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(p_pre, p_raw, rtol=1e-12, atol=1e-14)
+
+    toks = _tok(rng, 4, H)
+    toks = {n: a.astype(F64) for n, a in toks.items()}
+    a_log, dt_bias = rng.uniform(-1, 1, H), rng.standard_normal(H * 128) * 0.1
+    R = 32
+    res = []
+    for mode in (0, PRE):
+        pool = d["pool"][:2].copy()
+        kc, uc, gc = (np.zeros((2, H, R, 128)) for _ in range(3))
+        hist = np.zeros(1, np.int32)
+        base = np.array([5], np.int32)
+        if mode:
+            gr = np.ascontiguousarray(_gate_np(toks["graw"], a_log, dt_bias, lb))
+            bl = scipy.special.expit(toks["beta_logit"])
+            al = db = None
+        else:
+            gr, bl, al, db = toks["graw"], toks["beta_logit"], a_log, dt_bias
+        out = orc.verify(toks["q"], toks["k"], toks["v"], gr, bl, al, db, lb, 1.0, pool,
+                         np.array([1], np.int32), kc, uc, gc, hist, base, 5, 16,
+                         bf16_storage=False, real=F64, gate_mode=mode)
+        res.append((out, pool, kc, uc, gc))
+    for a, b in zip(res[0], res[1]):
+        np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-14)
+
+    p = _prefill_inputs(rng, (21, 0, 9), H=2)
+    gp = np.ascontiguousarray(_gate_np(p["graw"], p["a_log"], p["dt_bias"], lb))
+    bp = scipy.special.expit(p["beta_logit"])
+    q1, q2 = p["pool"].copy(), p["pool"].copy()
+    o1 = orc.prefill(*_pf_args(p), q1, p["idx"], bf16_storage=False, real=F64)
+    o2 = orc.prefill(p["cu"], p["q"], p["k"], p["v"], gp, bp, None, None, lb, 1.0, q2, p["idx"],
+                     bf16_storage=False, real=F64, gate_mode=PRE)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(q2, q1, rtol=1e-12, atol=1e-14)
+    # and its chunked form agrees with it
+    q3 = p["pool"].copy()
+    o3 = orc.prefill_chunked(p["cu"], p["q"], p["k"], p["v"], gp, bp, None, None, lb, 1.0, q3,
+                             p["idx"], 16, real=F64, gate_mode=PRE)
+    np.testing.assert_allclose(o3, o1, rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(q3, q1, rtol=1e-10, atol=1e-11)
+
+
+def test_precomputed_prologue_uses_g_and_beta_as_given(orc):
+    """The pre-computed prologue passes g through inside [lb, 0], clamps it
+    outside, and passes beta through; each bit acts alone."""
+    rng = _rng(201)
+    K = 128
+    lb = -3.0
+    q, k = rng.standard_normal(K), rng.standard_normal(K)
+    g_in = np.concatenate([rng.uniform(lb, 0, K - 4), [lb - 1.0, -1e30, 0.5, 0.0]])
+    _, _, g, beta = orc.prologue(q, k, g_in, 0.37, 0.0, np.zeros(K), lb, real=F64, gate_mode=3)
+    np.testing.assert_array_equal(g[:K - 4], g_in[:K - 4])
+    np.testing.assert_array_equal(g[K - 4:], [lb, lb, 0.0, 0.0])
+    assert beta == 0.37
+    # gate bit only: beta still goes through the sigmoid
+    _, _, g1, beta1 = orc.prologue(q, k, g_in, 0.37, 0.0, np.zeros(K), lb, real=F64, gate_mode=1)
+    np.testing.assert_array_equal(g1, g)
+    assert beta1 == pytest.approx(float(scipy.special.expit(0.37)), rel=1e-15)
+    # beta bit only: the gate is still the raw formula (A_log = 0, dt_bias = 0)
+    graw = rng.standard_normal(K)
+    _, _, g2, beta2 = orc.prologue(q, k, graw, 0.37, 0.0, np.zeros(K), -1e30, real=F64,
+                                   gate_mode=2)
+    np.testing.assert_allclose(g2, -np.logaddexp(0.0, graw), rtol=1e-12, atol=1e-15)
+    assert beta2 == 0.37
+
+
+def test_precomputed_beta1_exact_retrieval_and_beta0_pure_decay(orc):
+    """With beta = 1 given exactly, decode writes v under k_hat (S_new k_hat = v);
+    with beta = 0 and g given, the state is exp(g)-decayed and nothing else."""
+    rng = _rng(202)
+    B, H, N = 2, 2, 3
+    d = _decode_inputs(rng, B, H, N, F64)
+    g = -rng.uniform(0, 5, (B, H, 128))
+    idx = np.array([2, 0], np.int32)
+    pool = d["pool"].copy()
+    orc.decode(d["q"], d["k"], d["v"], g, np.ones((B, H)), None, None, -5.0, 1.0, pool, idx,
+               bf16_storage=False, real=F64, gate_mode=PRE)
+    for b in range(B):
+        for h in range(H):
+            kk = d["k"][b, h]
+            got = pool[idx[b], h] @ (kk / np.sqrt(kk @ kk + 1e-6))
+            # |k_hat|^2 = 1 - 1e-6 / |k|^2 (the norm's epsilon): retrieval to ~1e-8
+            np.testing.assert_allclose(got, d["v"][b, h], rtol=1e-7, atol=1e-7)
+    pool = d["pool"].copy()
+    out = orc.decode(d["q"], d["k"], d["v"], g, np.zeros((B, H)), None, None, -5.0, 0.5, pool,
+                     idx, bf16_storage=False, real=F64, gate_mode=PRE)
+    for b in range(B):
+        for h in range(H):
+            ref = d["pool"][idx[b], h] * np.exp(g[b, h])[None, :]
+            np.testing.assert_allclose(pool[idx[b], h], ref, rtol=1e-14, atol=1e-300)
+            qq = d["q"][b, h]
+            np.testing.assert_allclose(out[b, h], 0.5 * ref @ (qq / np.sqrt(qq @ qq + 1e-6)),
+                                       rtol=1e-12, atol=1e-14)

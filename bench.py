@@ -50,7 +50,7 @@ N_SLOTS = 1024
 # only for the kernel sources the counters were taken on: the digest below
 # turns it into null once those sources change.
 COUNTED_TRAFFIC = {
-    "kda::decode_kernel<8, true>": dict(
+    "kda::decode_kernel<8, true, true>": dict(
         sources=("gated_delta_rule_step_amd/csrc/kda_decode.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
@@ -59,7 +59,7 @@ COUNTED_TRAFFIC = {
                 "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
         fetch_kib=96395.711, write_kib=188168.320, fetch_scale=2.0, write_scale=1.0),
     # T = 8 verify, B = 512, bare checkpoint (the --mode profile sequence)
-    "kda::verify_kernel<true, true>": dict(
+    "kda::verify_kernel<true, true, true>": dict(
         sources=("gated_delta_rule_step_amd/csrc/kda_verify.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
@@ -184,14 +184,16 @@ def index_sets(synth, B, tag, inactive_frac=0.05):
 
 
 class DecodeSetup:
-    def __init__(self, B, torch, kda, synth, pools):
-        self.B = B
+    def __init__(self, B, torch, kda, synth, pools, gate_mode=0):
+        self.B, self.gate_mode = B, gate_mode
         W = H * 128
         sets = index_sets(synth, B, 99)
         self.n_active = int(((sets[0] >= 0) & (sets[0] < N_SLOTS)).sum())
         self.combos = []
         for j in range(4):
             c = synth.decode_case(B=B, N=1, H=H, seed=synth.seed_for(1, B) + j)
+            if gate_mode:
+                c = synth.precomputed_gate(c, gate_mode, synth.seed_for(1, B, 100) + j)
             qkv = bf16_dev(torch, c["qkv"])
             self.combos.append(dict(
                 q=qkv[:, :W], k=qkv[:, W:2 * W], v=qkv[:, 2 * W:], g=bf16_dev(torch, c["gate"]),
@@ -204,9 +206,13 @@ class DecodeSetup:
     def calls(self):
         kda = self.kda
 
+        gm = self.gate_mode
+        pre = bool(gm & 1)
+
         def mk(c):
-            return lambda: kda.kda_decode(c["q"], c["k"], c["v"], c["g"], c["b"], c["a_log"],
-                                          c["dtb"], c["pool"], c["idx"], c["out"])
+            return lambda: kda.kda_decode(c["q"], c["k"], c["v"], c["g"], c["b"],
+                                          None if pre else c["a_log"], None if pre else c["dtb"],
+                                          c["pool"], c["idx"], c["out"], gate_mode=gm)
         return [mk(c) for c in self.combos]
 
 
@@ -216,8 +222,8 @@ class VerifySetup:
     the tests (fold probability p, or hist ~ U{0..hist_max})."""
 
     def __init__(self, B, T, torch, kda, synth, pools, rings, w_ring=16, flush_min=None,
-                 fold_p=0.0, hist_max=None):
-        self.B, self.T, self.w_ring = B, T, w_ring
+                 fold_p=0.0, hist_max=None, gate_mode=0):
+        self.B, self.T, self.w_ring, self.gate_mode = B, T, w_ring, gate_mode
         W = H * 128
         sets = index_sets(synth, B, 77, inactive_frac=0.0)
         self.combos = []
@@ -225,6 +231,8 @@ class VerifySetup:
             c = synth.verify_case(B=B, T=T, N=1, H=H, w_ring=w_ring, flush_min=flush_min,
                                   fold_p=fold_p, hist_max=hist_max,
                                   seed=synth.seed_for(3, B, T) + j)
+            if gate_mode:
+                c = synth.precomputed_gate(c, gate_mode, synth.seed_for(3, B, 100 + T) + j)
             self.flush_min = c["flush_min"]
             if j == 0:
                 self.hist = c["hist_len"].copy()
@@ -243,13 +251,15 @@ class VerifySetup:
         self.kda = kda
 
     def calls(self):
-        kda, fm, w = self.kda, self.flush_min, self.w_ring
+        kda, fm, w, gm = self.kda, self.flush_min, self.w_ring, self.gate_mode
+        pre = bool(gm & 1)
 
         def mk(c):
             return lambda: kda.kda_verify_ucache_flush(
-                c["q"], c["k"], c["v"], c["g"], c["b"], c["a_log"], c["dtb"], c["pool"],
+                c["q"], c["k"], c["v"], c["g"], c["b"], None if pre else c["a_log"],
+                None if pre else c["dtb"], c["pool"],
                 c["idx"], c["kc"], c["uc"], c["gc"], c["hist"], c["base"], c["out"],
-                flush_min=fm, w_ring=w)
+                flush_min=fm, w_ring=w, gate_mode=gm)
         return [mk(c) for c in self.combos]
 
 
@@ -268,8 +278,8 @@ class PrefillSetup:
     A_log U(-1, 1), dt_bias N(0, 0.1), initial states N(0, 0.05) in a pool of
     2 slots per document)."""
 
-    def __init__(self, lens, H, torch, kda, synth):
-        self.lens, self.H = tuple(lens), H
+    def __init__(self, lens, H, torch, kda, synth, gate_mode=0):
+        self.lens, self.H, self.gate_mode = tuple(lens), H, gate_mode
         n_docs, T, W = len(lens), int(sum(lens)), H * 128
         gen = torch.Generator(device="cuda")
         gen.manual_seed(synth.seed_for(4, H, n_docs))
@@ -279,6 +289,11 @@ class PrefillSetup:
             return (x * std).to(torch.bfloat16)
         self.q, self.k, self.v, self.g = (randn(T, W) for _ in range(4))
         self.beta = randn(T, H)
+        if gate_mode & 1:  # the log-decay itself, U(-6, 0.5) (clamped into [-5, 0])
+            u = torch.rand(T, W, generator=gen, device="cuda")
+            self.g = (u * 6.5 - 6.0).to(torch.bfloat16)
+        if gate_mode & 2:  # beta itself, U(0, 1)
+            self.beta = torch.rand(T, H, generator=gen, device="cuda").to(torch.bfloat16)
         self.a_log = torch.rand(H, generator=gen, device="cuda") * 2.0 - 1.0
         self.dtb = torch.randn(H * 128, generator=gen, device="cuda") * 0.1
         N = 2 * n_docs
@@ -296,9 +311,13 @@ class PrefillSetup:
     def calls(self):
         s = self
 
+        pre = bool(s.gate_mode & 1)
+
         def call():
-            s.kda.kda_prefill_varlen(s.cu_h, s.cu_d, s.q, s.k, s.v, s.g, s.beta, s.a_log, s.dtb,
-                                     s.pool, s.idx, s.out, workspace=s.ws)
+            s.kda.kda_prefill_varlen(s.cu_h, s.cu_d, s.q, s.k, s.v, s.g, s.beta,
+                                     None if pre else s.a_log, None if pre else s.dtb,
+                                     s.pool, s.idx, s.out, workspace=s.ws,
+                                     gate_mode=s.gate_mode)
         return [call]
 
 
@@ -413,6 +432,15 @@ def main():
             log(f"bench: {points[-1]}")
         points.append(dict(kind="decode", B=B, T=1, us_per_call=round(us_ev, 3),
                            GBps=round(gbs, 1), hbm_frac=round(gbs / wm.HBM_PEAK_GBS, 4)))
+        # the pre-computed gate and beta convention at the headline size
+        sp = DecodeSetup(B, torch, kda, synth, pools, gate_mode=3)
+        _, e = time_graphs(sp.calls(), args.steps, args.warmup, torch, min_warm_s=0.3)
+        us = e * 1e3 / args.steps
+        nb = wm.decode_bytes(sp.n_active, B - sp.n_active)
+        points.append(dict(kind="decode", B=B, T=1, gate="pre-computed g and beta",
+                           us_per_call=round(us, 3), GBps=round(nb / (us * 1e-6) / 1e9, 1),
+                           hbm_frac=round(nb / (us * 1e-6) / 1e9 / wm.HBM_PEAK_GBS, 4)))
+        log(f"bench: {points[-1]}")
         rings = make_rings(torch, synth)
         vcfgs = [
             dict(label="T=8 bare (0% fold)", T=8, hist_max=0),
@@ -421,6 +449,7 @@ def main():
             dict(label="T=8 fm=9 100% fold", T=8, fold_p=1.0),
             dict(label="T=4 fm=13 100% fold", T=4, fold_p=1.0),
             dict(label="T=8 W32 fm=25 hist~U{0..24}", T=8, w_ring=32, flush_min=25, hist_max=24),
+            dict(label="T=8 bare, pre-computed gate and beta", T=8, hist_max=0, gate_mode=3),
         ]
         for Bv in (1, 32, 512):
             for cfg in vcfgs:
@@ -435,7 +464,7 @@ def main():
                 fl = wm.verify_flops(cfg["T"], vs.hist)
                 extra = {}
                 if Bv == 512 and cfg["label"] == "T=8 bare (0% fold)":
-                    extra["traffic_bytes"] = counted_traffic("kda::verify_kernel<true, true>")
+                    extra["traffic_bytes"] = counted_traffic("kda::verify_kernel<true, true, true>")
                 points.append(dict(kind="verify", B=Bv, label=cfg["label"],
                                    fold_frac=round(float(np.mean(vs.fold)), 3),
                                    mean_hist=round(float(np.mean(vs.hist)), 2),
@@ -447,26 +476,30 @@ def main():
                 del vs
         del rings
         torch.cuda.empty_cache()
-        for name, lens in (("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4),
-                           ("14-doc mix, 16384 tokens", synth.DOCS_14)):
-            for Hp in (64, 12):
-                ps = PrefillSetup(lens, Hp, torch, kda, synth)
-                st = max(10, min(args.steps, 50))
-                _, e = time_graphs(ps.calls(), st, 2, torch, min_warm_s=0.3)
-                us = e * 1e3 / st
-                nb = wm.prefill_bytes(lens, Hp)
-                fl = wm.prefill_flops(lens, Hp)
-                points.append(dict(kind="prefill", H=Hp, docs=name, tokens=int(sum(lens)),
-                                   us_per_call=round(us, 1),
-                                   Mtok_per_s=round(sum(lens) / (us * 1e-6) / 1e6, 2),
-                                   GBps=round(nb / (us * 1e-6) / 1e9, 1),
-                                   hbm_frac=round(nb / (us * 1e-6) / 1e9 / wm.HBM_PEAK_GBS, 4),
-                                   TFLOPs=round(fl / (us * 1e-6) / 1e12, 2),
-                                   mfma_frac=round(fl / (us * 1e-6) / 1e12
-                                                   / wm.BF16_MFMA_PEAK_TFLOPS, 4)))
-                log(f"bench: {points[-1]}")
-                del ps
-                torch.cuda.empty_cache()
+        pcfgs = [(name, lens, Hp, 0)
+                 for name, lens in (("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4),
+                                    ("14-doc mix, 16384 tokens", synth.DOCS_14))
+                 for Hp in (64, 12)]
+        pcfgs.append(("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4, 12, 3))
+        for name, lens, Hp, gm in pcfgs:
+            ps = PrefillSetup(lens, Hp, torch, kda, synth, gate_mode=gm)
+            st = max(10, min(args.steps, 50))
+            _, e = time_graphs(ps.calls(), st, 2, torch, min_warm_s=0.3)
+            us = e * 1e3 / st
+            nb = wm.prefill_bytes(lens, Hp)
+            fl = wm.prefill_flops(lens, Hp)
+            extra = {"gate": "pre-computed g and beta"} if gm else {}
+            points.append(dict(kind="prefill", H=Hp, docs=name, tokens=int(sum(lens)),
+                               **extra, us_per_call=round(us, 1),
+                               Mtok_per_s=round(sum(lens) / (us * 1e-6) / 1e6, 2),
+                               GBps=round(nb / (us * 1e-6) / 1e9, 1),
+                               hbm_frac=round(nb / (us * 1e-6) / 1e9 / wm.HBM_PEAK_GBS, 4),
+                               TFLOPs=round(fl / (us * 1e-6) / 1e12, 2),
+                               mfma_frac=round(fl / (us * 1e-6) / 1e12
+                                               / wm.BF16_MFMA_PEAK_TFLOPS, 4)))
+            log(f"bench: {points[-1]}")
+            del ps
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -492,8 +525,8 @@ def main():
                    "B": B, "H": H, "T": 1, "pool_slots": N_SLOTS, "device": dev_name},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": wm.HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / wm.HBM_PEAK_GBS, 4),
-                     "traffic": counted_traffic("kda::decode_kernel<8, true>"),
-                     "kernel": "kda::decode_kernel<8, true>",
+                     "traffic": counted_traffic("kda::decode_kernel<8, true, true>"),
+                     "kernel": "kda::decode_kernel<8, true, true>",
                      "kernel_us_avg": round(us_ev, 3), "algorithmic_bytes": nbytes},
         "cpu_baseline": cpu,
         "points": points,

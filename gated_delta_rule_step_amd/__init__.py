@@ -30,19 +30,25 @@ _SIGS = {
     "kda_status_string": (_c.c_char_p, [_c.c_int]),
     "kda_decode": (_c.c_int, [_I32, _I32, _I32, _I32,
                               _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
-                              _P, _P, _F, _F, _P, _I64, _I64, _P, _P, _I64, _P]),
+                              _P, _P, _F, _F, _I32, _P, _I64, _I64, _P, _P, _I64, _P]),
     "kda_verify_ucache_flush": (_c.c_int, [_I32, _I32, _I32, _I32, _I32,
                                            _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
                                            _P, _I64, _I64, _P, _I64, _I64,
-                                           _P, _P, _F, _F, _P, _I64, _I64, _P,
+                                           _P, _P, _F, _F, _I32, _P, _I64, _I64, _P,
                                            _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32,
                                            _P, _I64, _I64, _P]),
     "kda_prefill_workspace_size": (_c.c_size_t, [_I32, _I64, _I32, _I32, _I32]),
     "kda_prefill_varlen": (_c.c_int, [_I32, _I64, _I32, _I32, _I32, _P, _P,
                                       _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
-                                      _P, _P, _F, _F, _P, _I64, _I64, _P, _I32,
+                                      _P, _P, _F, _F, _I32, _P, _I64, _I64, _P, _I32,
                                       _P, _I64, _P, _c.c_size_t, _P]),
 }
+
+
+# gate_mode bits (include/kda.h): g_raw holds the log-decay g itself (A_log and
+# dt_bias may then be None); beta_raw holds beta itself.
+GATE_PRECOMPUTED = 1
+BETA_PRESIGMOID = 2
 
 
 class KdaError(RuntimeError):
@@ -97,8 +103,10 @@ def _bf16(name, t, last_contig=True):
         raise ValueError(f"{name}: the innermost dimension must be contiguous")
 
 
-def _f32(name, t):
+def _f32(name, t, optional=False):
     import torch
+    if optional and t is None:
+        return
     if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
 
@@ -123,7 +131,8 @@ def _pool_geometry(state_pool, H):
 
 
 def kda_decode(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_indices, out,
-               lower_bound: float = -5.0, scale: float = 1.0, stream=None) -> None:
+               lower_bound: float = -5.0, scale: float = 1.0, gate_mode: int = 0,
+               stream=None) -> None:
     """T=1 decode. q, k, v, g_raw, out: bf16 [B, H*128] (row-strided views
     allowed); beta_raw bf16 [B, H]; A_log fp32 [H]; dt_bias fp32 [H*128];
     state_pool bf16 [N, ...] (slot-major); state_indices int32 [B]."""
@@ -132,15 +141,16 @@ def kda_decode(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_indic
     for n, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta_raw", beta_raw),
                  ("out", out)):
         _bf16(n, t)
-    _f32("A_log", A_log)
-    _f32("dt_bias", dt_bias)
+    pre = bool(gate_mode & GATE_PRECOMPUTED)
+    _f32("A_log", A_log, optional=pre)
+    _f32("dt_bias", dt_bias, optional=pre)
     _i32("state_indices", state_indices)
     N, slot_stride = _pool_geometry(state_pool, H)
     st = lib().kda_decode(B, H, HEAD_DIM, HEAD_DIM,
                           _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
                           _ptr(g_raw), g_raw.stride(0), _ptr(beta_raw), beta_raw.stride(0),
                           _ptr(A_log), _ptr(dt_bias), float(lower_bound), float(scale),
-                          _ptr(state_pool) if N else _P(0), N, slot_stride,
+                          int(gate_mode), _ptr(state_pool) if N else _P(0), N, slot_stride,
                           _ptr(state_indices), _ptr(out), out.stride(0), _stream(stream))
     _check("kda_decode", st)
 
@@ -149,7 +159,7 @@ def kda_verify_ucache_flush(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool
                             state_indices, k_cache, u_cache, g_cache, hist_len, cache_base,
                             out, flush_min: int, w_ring: int = 16,
                             restart_hist_on_flush: bool = True, lower_bound: float = -5.0,
-                            scale: float = 1.0, stream=None) -> None:
+                            scale: float = 1.0, gate_mode: int = 0, stream=None) -> None:
     """Verify+fold. q, k, v, g_raw, out: bf16 [B, T, H*128]; beta_raw bf16
     [B, T, H]; k_cache/u_cache bf16 [N, H, R, 128]; g_cache fp32 [N, H, R, 128];
     hist_len, cache_base int32 [B]."""
@@ -158,8 +168,10 @@ def kda_verify_ucache_flush(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool
     for n, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta_raw", beta_raw),
                  ("out", out), ("k_cache", k_cache), ("u_cache", u_cache)):
         _bf16(n, t)
-    for n, t in (("A_log", A_log), ("dt_bias", dt_bias), ("g_cache", g_cache)):
-        _f32(n, t)
+    pre = bool(gate_mode & GATE_PRECOMPUTED)
+    _f32("A_log", A_log, optional=pre)
+    _f32("dt_bias", dt_bias, optional=pre)
+    _f32("g_cache", g_cache)
     for n, t in (("state_indices", state_indices), ("hist_len", hist_len),
                  ("cache_base", cache_base)):
         _i32(n, t)
@@ -175,7 +187,7 @@ def kda_verify_ucache_flush(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool
         _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1),
         _ptr(v), v.stride(0), v.stride(1), _ptr(g_raw), g_raw.stride(0), g_raw.stride(1),
         _ptr(beta_raw), beta_raw.stride(0), beta_raw.stride(1),
-        _ptr(A_log), _ptr(dt_bias), float(lower_bound), float(scale),
+        _ptr(A_log), _ptr(dt_bias), float(lower_bound), float(scale), int(gate_mode),
         _ptr(state_pool) if N else _P(0), N, slot_stride, _ptr(state_indices),
         _ptr(k_cache), _ptr(u_cache), _ptr(g_cache), R, _ptr(hist_len), _ptr(cache_base),
         int(flush_min), int(w_ring), 1 if restart_hist_on_flush else 0,
@@ -190,7 +202,7 @@ def kda_prefill_workspace_size(n_docs: int, total_tokens: int, H: int) -> int:
 def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_log, dt_bias,
                        state_pool, state_indices, out, workspace=None,
                        use_initial_state: bool = True, lower_bound: float = -5.0,
-                       scale: float = 1.0, stream=None) -> None:
+                       scale: float = 1.0, gate_mode: int = 0, stream=None) -> None:
     """Varlen prefill. cu_seqlens_host: CPU int32 [n_docs+1]; cu_seqlens: the
     same on the GPU; q, k, v, g_raw, out: bf16 [Ttot, H*128] (token-strided);
     beta_raw bf16 [Ttot, H]; state_indices int32 [n_docs]; workspace: uint8
@@ -208,8 +220,9 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
     for n, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta_raw", beta_raw),
                  ("out", out)):
         _bf16(n, t)
-    _f32("A_log", A_log)
-    _f32("dt_bias", dt_bias)
+    pre = bool(gate_mode & GATE_PRECOMPUTED)
+    _f32("A_log", A_log, optional=pre)
+    _f32("dt_bias", dt_bias, optional=pre)
     N, slot_stride = _pool_geometry(state_pool, H)
     if workspace is None:
         need = kda_prefill_workspace_size(n_docs, Ttot, H)
@@ -221,7 +234,7 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
         n_docs, Ttot, H, HEAD_DIM, HEAD_DIM, cu_h, _ptr(cu_seqlens),
         _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
         _ptr(g_raw), g_raw.stride(0), _ptr(beta_raw), beta_raw.stride(0),
-        _ptr(A_log), _ptr(dt_bias), float(lower_bound), float(scale),
+        _ptr(A_log), _ptr(dt_bias), float(lower_bound), float(scale), int(gate_mode),
         _ptr(state_pool) if N else _P(0), N, slot_stride, _ptr(state_indices),
         1 if use_initial_state else 0, _ptr(out), out.stride(0),
         _ptr(workspace), ws_bytes, _stream(stream))

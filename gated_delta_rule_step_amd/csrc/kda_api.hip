@@ -28,6 +28,19 @@ bool out_layout_ok(int64_t rows, int64_t toks, int64_t row_stride, int64_t tok_s
 
 kda_status launch_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH; }
 
+// gate_mode: only the two documented bits; the pre-computed gate clamps into
+// [lower_bound, 0], so lower_bound must be <= 0 (not NaN) there. A_log and
+// dt_bias are read only for raw gate logits.
+kda_status check_gate(int32_t gate_mode, float lower_bound, const float* A_log,
+                      const float* dt_bias) {
+  if (gate_mode & ~(KDA_GATE_PRECOMPUTED | KDA_BETA_PRESIGMOID)) return KDA_ERR_UNSUPPORTED;
+  if (gate_mode & KDA_GATE_PRECOMPUTED) {
+    if (!(lower_bound <= 0.0f)) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+  }
+  return (A_log && dt_bias) ? KDA_OK : KDA_ERR_NULL_POINTER;
+}
+
 }  // namespace
 
 extern "C" const char* kda_status_string(kda_status s) {
@@ -50,13 +63,16 @@ extern "C" kda_status kda_decode(int32_t B, int32_t H, int32_t K, int32_t V, con
                                  int64_t g_row_stride, const void* beta_raw,
                                  int64_t beta_row_stride, const float* A_log,
                                  const float* dt_bias, float lower_bound, float scale,
-                                 void* state_pool, int64_t num_slots, int64_t slot_stride,
-                                 const int32_t* state_indices, void* out,
+                                 int32_t gate_mode, void* state_pool, int64_t num_slots,
+                                 int64_t slot_stride, const int32_t* state_indices, void* out,
                                  int64_t out_row_stride, hipStream_t stream) {
   if (B < 0 || H < 1 || num_slots < 0) return KDA_ERR_BAD_SHAPE;
   if (K != D || V != D) return KDA_ERR_UNSUPPORTED;
+  if (const kda_status gs = check_gate(gate_mode, lower_bound, A_log, dt_bias)) {
+    if (gs == KDA_ERR_UNSUPPORTED || B > 0) return gs;
+  }
   if (B == 0) return KDA_OK;
-  if (!q || !k || !v || !g_raw || !beta_raw || !A_log || !dt_bias || !state_indices || !out)
+  if (!q || !k || !v || !g_raw || !beta_raw || !state_indices || !out)
     return KDA_ERR_NULL_POINTER;
   if (num_slots > 0 && !state_pool) return KDA_ERR_NULL_POINTER;
   const int64_t W = int64_t(H) * D;
@@ -83,6 +99,7 @@ extern "C" kda_status kda_decode(int32_t B, int32_t H, int32_t K, int32_t V, con
   p.dt_bias = dt_bias;
   p.lower_bound = lower_bound;
   p.scale = scale;
+  p.gate_mode = gate_mode;
   p.state_pool = static_cast<uint16_t*>(state_pool);
   p.num_slots = num_slots;
   p.slot_stride = slot_stride;
@@ -101,7 +118,7 @@ extern "C" kda_status kda_verify_ucache_flush(
     const void* v, int64_t v_row_stride, int64_t v_tok_stride, const void* g_raw,
     int64_t g_row_stride, int64_t g_tok_stride, const void* beta_raw, int64_t beta_row_stride,
     int64_t beta_tok_stride, const float* A_log, const float* dt_bias, float lower_bound,
-    float scale, void* state_pool, int64_t num_slots, int64_t slot_stride,
+    float scale, int32_t gate_mode, void* state_pool, int64_t num_slots, int64_t slot_stride,
     const int32_t* state_indices, void* k_cache, void* u_cache, float* g_cache,
     int32_t ring_rows, const int32_t* hist_len, const int32_t* cache_base, int32_t flush_min,
     int32_t w_ring, int32_t restart_hist_on_flush, void* out, int64_t out_row_stride,
@@ -112,9 +129,12 @@ extern "C" kda_status kda_verify_ucache_flush(
   if (ring_rows < w_ring || restart_hist_on_flush != 1 || flush_min < 1) return KDA_ERR_UNSUPPORTED;
   if (flush_min - 1 + T > w_ring) return KDA_ERR_UNSUPPORTED;  // ring capacity
   if (w_ring == 32 && flush_min <= 16) return KDA_ERR_UNSUPPORTED;
+  if (const kda_status gs = check_gate(gate_mode, lower_bound, A_log, dt_bias)) {
+    if (gs == KDA_ERR_UNSUPPORTED || B > 0) return gs;
+  }
   if (B == 0) return KDA_OK;
-  if (!q || !k || !v || !g_raw || !beta_raw || !A_log || !dt_bias || !state_indices || !out ||
-      !hist_len || !cache_base)
+  if (!q || !k || !v || !g_raw || !beta_raw || !state_indices || !out || !hist_len ||
+      !cache_base)
     return KDA_ERR_NULL_POINTER;
   if (num_slots > 0 && (!state_pool || !k_cache || !u_cache || !g_cache))
     return KDA_ERR_NULL_POINTER;
@@ -150,6 +170,7 @@ extern "C" kda_status kda_verify_ucache_flush(
   p.dt_bias = dt_bias;
   p.lower_bound = lower_bound;
   p.scale = scale;
+  p.gate_mode = gate_mode;
   p.state_pool = static_cast<uint16_t*>(state_pool);
   p.num_slots = num_slots;
   p.slot_stride = slot_stride;
@@ -188,7 +209,7 @@ extern "C" kda_status kda_prefill_varlen(
     int64_t q_tok_stride, const void* k, int64_t k_tok_stride, const void* v,
     int64_t v_tok_stride, const void* g_raw, int64_t g_tok_stride, const void* beta_raw,
     int64_t beta_tok_stride, const float* A_log, const float* dt_bias, float lower_bound,
-    float scale, void* state_pool, int64_t num_slots, int64_t slot_stride,
+    float scale, int32_t gate_mode, void* state_pool, int64_t num_slots, int64_t slot_stride,
     const int32_t* state_indices, int32_t use_initial_state, void* out, int64_t out_tok_stride,
     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (n_docs < 0 || total_tokens < 0 || H < 1 || num_slots < 0) return KDA_ERR_BAD_SHAPE;
@@ -200,8 +221,11 @@ extern "C" kda_status kda_prefill_varlen(
   for (int32_t d = 0; d < n_docs; ++d)
     if (cu_seqlens_host[d + 1] < cu_seqlens_host[d]) return KDA_ERR_BAD_SEQLENS;
   if (int64_t(cu_seqlens_host[n_docs]) != total_tokens) return KDA_ERR_BAD_SEQLENS;
+  if (const kda_status gs = check_gate(gate_mode, lower_bound, A_log, dt_bias)) {
+    if (gs == KDA_ERR_UNSUPPORTED || n_docs > 0) return gs;
+  }
   if (n_docs == 0) return KDA_OK;
-  if (!cu_seqlens || !state_indices || !A_log || !dt_bias) return KDA_ERR_NULL_POINTER;
+  if (!cu_seqlens || !state_indices) return KDA_ERR_NULL_POINTER;
   if (total_tokens > 0 && (!q || !k || !v || !g_raw || !beta_raw || !out))
     return KDA_ERR_NULL_POINTER;
   if (num_slots > 0 && !state_pool) return KDA_ERR_NULL_POINTER;
@@ -237,6 +261,7 @@ extern "C" kda_status kda_prefill_varlen(
   p.dt_bias = dt_bias;
   p.lower_bound = lower_bound;
   p.scale = scale;
+  p.gate_mode = gate_mode;
   p.state_pool = static_cast<uint16_t*>(state_pool);
   p.num_slots = num_slots;
   p.slot_stride = slot_stride;

@@ -126,4 +126,10 @@ __device__ __forceinline__ float fgate(float x, float neg_exp_alog, float lb) {
 }
 __device__ __forceinline__ float fsigmoid(float x) { return 1.0f / (1.0f + fexp(-x)); }
 
+// Pre-computed gate: the given log-decay, clamped into [lb, 0] (the range the
+// raw gate lands in).
+__device__ __forceinline__ float gate_given(float g, float lb) {
+  return fminf(0.0f, fmaxf(lb, g));
+}
+
 }  // namespace kda

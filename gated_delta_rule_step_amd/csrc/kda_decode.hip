@@ -30,7 +30,9 @@
 
 namespace kda {
 
-template <int LOADS, bool VEC>
+// GRAW: raw gate logits (log-decay from A_log, dt_bias, lower_bound); else
+// the gate input is the log-decay itself.
+template <int LOADS, bool VEC, bool GRAW>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr int ROWS = 4 * LOADS;
   constexpr int VBLOCKS = D / ROWS;
@@ -60,13 +62,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   for (int i = 0; i < LOADS; ++i) s[i] = load8_raw<VEC>(sp + i * 4 * D);
 
   // Per-token prologue for this lane's 8 key channels.
-  float q[8], k[8], gr[8], dtb[8];
+  float q[8], k[8], gr[8], dtb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   load8_bf16<VEC>(p.q + b * p.q_row_stride + h * D + kb * 8, q);
   load8_bf16<VEC>(p.k + b * p.k_row_stride + h * D + kb * 8, k);
   load8_bf16<VEC>(p.g + b * p.g_row_stride + h * D + kb * 8, gr);
-  load8_f32<VEC>(p.dt_bias + h * D + kb * 8, dtb);
-  const float neg_ea = -expf(p.A_log[h]);
-  const float beta = sigmoidf(bf1(p.beta[b * p.beta_row_stride + h]));
+  float neg_ea = 0.f;
+  if constexpr (GRAW) {
+    load8_f32<VEC>(p.dt_bias + h * D + kb * 8, dtb);
+    neg_ea = -expf(p.A_log[h]);
+  }
+  const float braw = bf1(p.beta[b * p.beta_row_stride + h]);
+  const float beta = (p.gate_mode & kBetaPresigmoid) ? braw : sigmoidf(braw);
   float vrow[LOADS];
   const uint16_t* vp = p.v + b * p.v_row_stride + h * D + vbase + rg;
 #pragma unroll
@@ -88,7 +94,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   float al[8], kh[8], ka[8], qa[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    al[c] = expf(gate_logdecay(gr[c] + dtb[c], neg_ea, p.lower_bound));
+    al[c] = expf(GRAW ? gate_logdecay(gr[c] + dtb[c], neg_ea, p.lower_bound)
+                      : gate_given(gr[c], p.lower_bound));
     kh[c] = k[c] * rk;
     ka[c] = al[c] * kh[c];
     qa[c] = al[c] * (q[c] * rq);
@@ -138,13 +145,20 @@ hipError_t launch_decode(const DecodeParams& p, bool vec, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  const bool graw = !(p.gate_mode & kGatePrecomputed);
+#define KDA_DECODE_LAUNCH(L, V)                                                        \
+  do {                                                                                 \
+    if (graw) hipLaunchKernelGGL((decode_kernel<L, V, true>), grid, block, 0, stream, p); \
+    else hipLaunchKernelGGL((decode_kernel<L, V, false>), grid, block, 0, stream, p);  \
+  } while (0)
   if (small) {
-    if (vec) hipLaunchKernelGGL((decode_kernel<2, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel<2, false>), grid, block, 0, stream, p);
+    if (vec) KDA_DECODE_LAUNCH(2, true);
+    else KDA_DECODE_LAUNCH(2, false);
   } else {
-    if (vec) hipLaunchKernelGGL((decode_kernel<8, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel<8, false>), grid, block, 0, stream, p);
+    if (vec) KDA_DECODE_LAUNCH(8, true);
+    else KDA_DECODE_LAUNCH(8, false);
   }
+#undef KDA_DECODE_LAUNCH
   return hipGetLastError();
 }
 

@@ -7,6 +7,11 @@
 
 namespace kda {
 
+// gate_mode bits (kda.h): the gate input holds the log-decay itself; the beta
+// input holds beta itself.
+constexpr int32_t kGatePrecomputed = 1;
+constexpr int32_t kBetaPresigmoid = 2;
+
 // All strides in elements. bf16 tensors are uint16_t bit patterns.
 struct DecodeParams {
   int32_t B, H;
@@ -19,6 +24,7 @@ struct DecodeParams {
   const float* A_log;
   const float* dt_bias;
   float lower_bound, scale;
+  int32_t gate_mode;
   uint16_t* state_pool;
   int64_t num_slots, slot_stride;
   const int32_t* state_indices;
@@ -38,6 +44,7 @@ struct VerifyParams {
   const float* A_log;
   const float* dt_bias;
   float lower_bound, scale;
+  int32_t gate_mode;
   uint16_t* state_pool;
   int64_t num_slots, slot_stride;
   const int32_t* state_indices;
@@ -65,6 +72,7 @@ struct PrefillParams {
   const float* A_log;
   const float* dt_bias;
   float lower_bound, scale;
+  int32_t gate_mode;
   uint16_t* state_pool;
   int64_t num_slots, slot_stride;
   const int32_t* state_indices;

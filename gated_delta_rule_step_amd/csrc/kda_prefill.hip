@@ -257,7 +257,8 @@ __device__ int find_doc(const int32_t* cu, int n_docs, int64_t sigma, int tid) {
 // inputs are loaded while the current head is processed.
 constexpr int kPrepHeads = 4;
 
-template <bool VEC>
+// GRAW: raw gate logits; else the gate input is the log-decay itself.
+template <bool VEC, bool GRAW>
 __global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillParams p) {
   extern __shared__ __align__(16) float psmem_raw[];
   const int tid = threadIdx.x;
@@ -291,9 +292,12 @@ __global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillParams p) {
     {
       const TokRaw cur = raw;
       if (h + 1 < h1) raw = load_tok<VEC>(p, tc0 + tt, h + 1, c0, valid);
-      const float neg_ea = -fexp(p.A_log[h]);
-      float dtb[8];
-      load8_f32<VEC>(p.dt_bias + h * D + c0, dtb);
+      float neg_ea = 0.f;
+      float dtb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if constexpr (GRAW) {
+        neg_ea = -fexp(p.A_log[h]);
+        load8_f32<VEC>(p.dt_bias + h * D + c0, dtb);
+      }
       float q[8], k[8], gr[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -315,10 +319,16 @@ __global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillParams p) {
       for (int e = 0; e < 8; ++e) {
         s.qh[tt * RS + c0 + e] = q[e] * rq;
         s.kh[tt * RS + c0 + e] = k[e] * rk;
-        s.gg[tt * RS + c0 + e] = valid ? fgate(gr[e] + dtb[e], neg_ea, p.lower_bound) : 0.f;
+        const float ge = GRAW ? fgate(gr[e] + dtb[e], neg_ea, p.lower_bound)
+                              : gate_given(gr[e], p.lower_bound);
+        s.gg[tt * RS + c0 + e] = valid ? ge : 0.f;
       }
       *reinterpret_cast<u32x4*>(s.vv + tt * VLD + c0) = cur.v;
-      if ((tid & 15) == 0) s.beta[tt] = valid ? fsigmoid(bf1(cur.b)) : 0.f;
+      if ((tid & 15) == 0) {
+        const float braw = bf1(cur.b);
+        const float be = (p.gate_mode & kBetaPresigmoid) ? braw : fsigmoid(braw);
+        s.beta[tt] = valid ? be : 0.f;
+      }
     }
     __syncthreads();
 
@@ -679,22 +689,30 @@ hipError_t launch_prefill(const PrefillParams& p, const int32_t* cu_host, bool v
     }
   }
   static const hipError_t attr = [] {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(kPrepLds));
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(kPrepLds));
-    return e;
+    const void* fns[] = {reinterpret_cast<const void*>(&prep_kernel<true, true>),
+                         reinterpret_cast<const void*>(&prep_kernel<true, false>),
+                         reinterpret_cast<const void*>(&prep_kernel<false, true>),
+                         reinterpret_cast<const void*>(&prep_kernel<false, false>)};
+    for (const void* f : fns) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               static_cast<int>(kPrepLds));
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }();
   if (attr != hipSuccess) return attr;
   if (p.total_tokens > 0) {
     dim3 pgrid(static_cast<unsigned>(slots),
                static_cast<unsigned>((p.H + kPrepHeads - 1) / kPrepHeads)),
         block(kThreads);
-    if (vec) hipLaunchKernelGGL((prep_kernel<true>), pgrid, block, kPrepLds, stream, p);
-    else hipLaunchKernelGGL((prep_kernel<false>), pgrid, block, kPrepLds, stream, p);
+    const bool graw = !(p.gate_mode & kGatePrecomputed);
+    if (vec) {
+      if (graw) hipLaunchKernelGGL((prep_kernel<true, true>), pgrid, block, kPrepLds, stream, p);
+      else hipLaunchKernelGGL((prep_kernel<true, false>), pgrid, block, kPrepLds, stream, p);
+    } else {
+      if (graw) hipLaunchKernelGGL((prep_kernel<false, true>), pgrid, block, kPrepLds, stream, p);
+      else hipLaunchKernelGGL((prep_kernel<false, false>), pgrid, block, kPrepLds, stream, p);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -138,7 +138,7 @@ struct TokRegs {
   uint32_t braw;
 };
 
-template <bool VEC>
+template <bool VEC, bool GRAW>
 __device__ __forceinline__ void load_tokens(const VerifyParams& p, int64_t item, int tid,
                                             TokRegs& r) {
   const int h = int(item % p.H);
@@ -149,13 +149,15 @@ __device__ __forceinline__ void load_tokens(const VerifyParams& p, int64_t item,
     r.k = load4_raw<VEC>(p.k + b * p.k_row_stride + t * p.k_tok_stride + h * D + c);
     r.g = load4_raw<VEC>(p.g + b * p.g_row_stride + t * p.g_tok_stride + h * D + c);
     r.v = load4_raw<VEC>(p.v + b * p.v_row_stride + t * p.v_tok_stride + h * D + c);
-    r.dtb = load4_f32<VEC>(p.dt_bias + h * D + c);
+    if constexpr (GRAW) r.dtb = load4_f32<VEC>(p.dt_bias + h * D + c);
+    else r.dtb = f32x4{0.f, 0.f, 0.f, 0.f};
     r.braw = p.beta[b * p.beta_row_stride + t * p.beta_tok_stride + h];
   }
 }
 
 // Grid: one 256-thread workgroup per item (row, head), item = row * H + head.
-template <bool VEC, bool FACT>
+// GRAW: raw gate logits; else the gate input is the log-decay itself.
+template <bool VEC, bool FACT, bool GRAW>
 __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   extern __shared__ __align__(16) float smem_raw[];
   const int tid = threadIdx.x;
@@ -180,12 +182,12 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
     return;
   }
   Smem s = carve(smem_raw, hm);
-  const float neg_ea = -fexp(p.A_log[h]);
+  const float neg_ea = GRAW ? -fexp(p.A_log[h]) : 0.f;
   // Token words first; every global load phases 2-5 need is issued before
   // the checkpoint loads (the memory counter is in order: waiting on a load
   // issued after them would also wait for the 32 KiB checkpoint read).
   TokRegs tk;
-  load_tokens<VEC>(p, item, tid, tk);
+  load_tokens<VEC, GRAW>(p, item, tid, tk);
   const bool fold = hist + T >= p.flush_min;
   const int64_t sh = int64_t(slot) * p.H + h;
   uint16_t* ckpt = p.state_pool + int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS;
@@ -282,14 +284,18 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
       for (int c = 0; c < 4; ++c) {
         qn[c] = q[c] * rq;
         kn[c] = k[c] * rk;
-        gn[c] = fgate(gr[c] + tk.dtb[c], neg_ea, p.lower_bound);
+        gn[c] = GRAW ? fgate(gr[c] + tk.dtb[c], neg_ea, p.lower_bound)
+                     : gate_given(gr[c], p.lower_bound);
         vn[c] = vv[c];
       }
       *reinterpret_cast<f32x4*>(s.qa + t * XS + c0) = qn;
       *reinterpret_cast<f32x4*>(s.ka + t * XS + c0) = kn;
       *reinterpret_cast<f32x4*>(s.kb + t * XS + c0) = gn;
       *reinterpret_cast<f32x4*>(s.vv + t * XS + c0) = vn;
-      if ((tid & 31) == 0) s.beta[t] = fsigmoid(bf1(uint16_t(tk.braw)));
+      if ((tid & 31) == 0) {
+        const float braw = bf1(uint16_t(tk.braw));
+        s.beta[t] = (p.gate_mode & kBetaPresigmoid) ? braw : fsigmoid(braw);
+      }
     }
   }
   __syncthreads();
@@ -569,13 +575,20 @@ hipError_t launch_verify(const VerifyParams& p, bool vec, hipStream_t stream) {
   // exp(Gam_r) * exp(-Gam_j) stays finite when |Gam| <= T * |lower_bound| < 80.
   const bool fact = p.lower_bound > -80.0f / float(p.T) && p.lower_bound <= 0.0f;
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  const bool graw = !(p.gate_mode & kGatePrecomputed);
+#define KDA_VERIFY_LAUNCH(V, F)                                                           \
+  do {                                                                                    \
+    if (graw) hipLaunchKernelGGL((verify_kernel<V, F, true>), grid, block, lds, stream, p, hm); \
+    else hipLaunchKernelGGL((verify_kernel<V, F, false>), grid, block, lds, stream, p, hm);   \
+  } while (0)
   if (vec) {
-    if (fact) hipLaunchKernelGGL((verify_kernel<true, true>), grid, block, lds, stream, p, hm);
-    else hipLaunchKernelGGL((verify_kernel<true, false>), grid, block, lds, stream, p, hm);
+    if (fact) KDA_VERIFY_LAUNCH(true, true);
+    else KDA_VERIFY_LAUNCH(true, false);
   } else {
-    if (fact) hipLaunchKernelGGL((verify_kernel<false, true>), grid, block, lds, stream, p, hm);
-    else hipLaunchKernelGGL((verify_kernel<false, false>), grid, block, lds, stream, p, hm);
+    if (fact) KDA_VERIFY_LAUNCH(false, true);
+    else KDA_VERIFY_LAUNCH(false, false);
   }
+#undef KDA_VERIFY_LAUNCH
   return hipGetLastError();
 }
 

@@ -18,6 +18,18 @@
  * lower_bound = -5, beta as a logit, in-kernel QK L2 norm) but print no
  * formula; the gate formula and the epsilon are this library's reading.
  *
+ * Gate convention (argument gate_mode of every entry point; "feat(kda): add
+ * packed-input CuTe decode kernel", section "T=1 fast path inside
+ * recurrent_kda": the raw form above, and the API-default pre-computed form
+ * with log-space g and pre-sigmoided beta, decay = exp(g)):
+ *  - 0: g_raw holds gate logits and beta_raw beta logits (the formulas above);
+ *  - KDA_GATE_PRECOMPUTED: g_raw holds the log-decay g_c itself, used as
+ *    min(0, max(lower_bound, g_c)) -- the range the raw gate lands in (a
+ *    reading); A_log and dt_bias are not read and may be NULL; lower_bound
+ *    must be <= 0 (-INFINITY: no floor), else KDA_ERR_UNSUPPORTED;
+ *  - KDA_BETA_PRESIGMOID: beta_raw holds beta itself, used as given.
+ * The two bits combine; any other bit gives KDA_ERR_UNSUPPORTED.
+ *
  * Conventions common to every entry point
  *  - Every pointer is a DEVICE pointer, except those whose name ends in _host.
  *  - bf16 tensors are passed as `const void*` / `void*` holding raw bf16 bits.
@@ -61,6 +73,11 @@
 extern "C" {
 #endif
 
+enum {
+  KDA_GATE_PRECOMPUTED = 1,  /* gate_mode bit: g_raw is the log-decay itself */
+  KDA_BETA_PRESIGMOID = 2    /* gate_mode bit: beta_raw is beta itself */
+};
+
 typedef enum {
   KDA_OK = 0,
   KDA_ERR_NULL_POINTER = 1,
@@ -92,12 +109,14 @@ const char* kda_status_string(kda_status s);
  *  q, k, v            bf16 [B, H*128] views with row strides q_row_stride,
  *                     k_row_stride, v_row_stride (may be three views into one
  *                     packed [B, 3*H*128] row)
- *  g_raw              bf16 [B, H*128] raw gate logits, row stride g_row_stride
- *  beta_raw           bf16 [B, H] beta logits, row stride beta_row_stride
- *  A_log              fp32 [H]
- *  dt_bias            fp32 [H*128]
+ *  g_raw              bf16 [B, H*128] raw gate logits (or the log-decay, see
+ *                     gate_mode), row stride g_row_stride
+ *  beta_raw           bf16 [B, H] beta logits (or beta), row stride beta_row_stride
+ *  A_log              fp32 [H] (not read with KDA_GATE_PRECOMPUTED)
+ *  dt_bias            fp32 [H*128] (not read with KDA_GATE_PRECOMPUTED)
  *  lower_bound        clamp of the log-decay (the pages use -5.0)
  *  scale              read-out scale
+ *  gate_mode          0, or KDA_GATE_PRECOMPUTED and/or KDA_BETA_PRESIGMOID
  *  state_pool         bf16 pool, num_slots slots of slot_stride elements
  *                     (may be NULL only when num_slots == 0)
  *  state_indices      int32 [B]: the pool slot of each row
@@ -113,7 +132,7 @@ kda_status kda_decode(int32_t B, int32_t H, int32_t K, int32_t V,
                       const void* g_raw, int64_t g_row_stride,
                       const void* beta_raw, int64_t beta_row_stride,
                       const float* A_log, const float* dt_bias,
-                      float lower_bound, float scale,
+                      float lower_bound, float scale, int32_t gate_mode,
                       void* state_pool, int64_t num_slots, int64_t slot_stride,
                       const int32_t* state_indices,
                       void* out, int64_t out_row_stride,
@@ -156,8 +175,8 @@ kda_status kda_decode(int32_t B, int32_t H, int32_t K, int32_t V,
  *  q, k, v, g_raw     bf16, element (b, t, h*128 + c) at
  *                     b*row_stride + t*tok_stride + h*128 + c
  *  beta_raw           bf16, element (b, t, h) at b*row_stride + t*tok_stride + h
- *  A_log, dt_bias, lower_bound, scale, state_pool, num_slots, slot_stride,
- *  state_indices      as for kda_decode (the pool holds the checkpoints)
+ *  A_log, dt_bias, lower_bound, scale, gate_mode, state_pool, num_slots,
+ *  slot_stride, state_indices  as for kda_decode (the pool holds the checkpoints)
  *  k_cache, u_cache   bf16 [num_slots, H, ring_rows, 128]
  *  g_cache            fp32 [num_slots, H, ring_rows, 128]
  *  ring_rows          R, physical ring rows per (slot, head) (>= w_ring)
@@ -180,7 +199,7 @@ kda_status kda_verify_ucache_flush(int32_t B, int32_t T, int32_t H, int32_t K, i
                                    const void* beta_raw, int64_t beta_row_stride,
                                    int64_t beta_tok_stride,
                                    const float* A_log, const float* dt_bias,
-                                   float lower_bound, float scale,
+                                   float lower_bound, float scale, int32_t gate_mode,
                                    void* state_pool, int64_t num_slots, int64_t slot_stride,
                                    const int32_t* state_indices,
                                    void* k_cache, void* u_cache, float* g_cache,
@@ -218,7 +237,7 @@ size_t kda_prefill_workspace_size(int32_t n_docs, int64_t total_tokens, int32_t 
  *  cu_seqlens         int32 [n_docs + 1], device copy with the same contents
  *  q, k, v, g_raw     bf16, element (t, h*128 + c) at t*tok_stride + h*128 + c
  *  beta_raw           bf16, element (t, h) at t*beta_tok_stride + h
- *  A_log, dt_bias, lower_bound, scale  as for kda_decode
+ *  A_log, dt_bias, lower_bound, scale, gate_mode  as for kda_decode
  *  state_pool, num_slots, slot_stride  as for kda_decode
  *  state_indices      int32 [n_docs]: slot of each document (initial and final
  *                     state); a document whose slot is outside [0, num_slots)
@@ -254,7 +273,7 @@ kda_status kda_prefill_varlen(int32_t n_docs, int64_t total_tokens, int32_t H, i
                               const void* g_raw, int64_t g_tok_stride,
                               const void* beta_raw, int64_t beta_tok_stride,
                               const float* A_log, const float* dt_bias,
-                              float lower_bound, float scale,
+                              float lower_bound, float scale, int32_t gate_mode,
                               void* state_pool, int64_t num_slots, int64_t slot_stride,
                               const int32_t* state_indices, int32_t use_initial_state,
                               void* out, int64_t out_tok_stride,

@@ -99,8 +99,10 @@ def oracle_decode(orc, case, pool_bits=None):
     slots, cidx = compact_slots(case["idx"], N)
     cpool = np.ascontiguousarray(f32(pool_bits[slots]))
     q, k, v = split_qkv(case["qkv"], H)
+    gm = case.get("gate_mode", 0)
+    a_log, dt_bias = (None, None) if gm & 1 else (case["a_log"], case["dt_bias"])
     out = orc.decode(q, k, v, np.ascontiguousarray(f32(case["gate"]).reshape(-1, H, HD)),
-                     np.ascontiguousarray(f32(case["beta"])), case["a_log"], case["dt_bias"],
+                     np.ascontiguousarray(f32(case["beta"])), a_log, dt_bias,
                      case["lower_bound"], case["scale"], cpool, cidx, bf16_storage=True,
-                     real=np.float32)
+                     real=np.float32, gate_mode=gm)
     return out, slots, cpool

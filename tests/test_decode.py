@@ -31,11 +31,14 @@ def run_decode(case, pool=None, out=None, scale=None, lower_bound=None, stream=N
     B = case["B"]
     if out is None:
         out = torch.full((B, W), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gm = case.get("gate_mode", 0)
+    a_log, dt_bias = (None, None) if gm & 1 else (dev(case["a_log"]), dev(case["dt_bias"]))
     _kda().kda_decode(qkv[:, :W], qkv[:, W:2 * W], qkv[:, 2 * W:], dev_bf16(case["gate"]),
-                      dev_bf16(case["beta"]), dev(case["a_log"]), dev(case["dt_bias"]), pool,
+                      dev_bf16(case["beta"]), a_log, dt_bias, pool,
                       dev(case["idx"]), out,
                       lower_bound=case["lower_bound"] if lower_bound is None else lower_bound,
-                      scale=case["scale"] if scale is None else scale, stream=stream)
+                      scale=case["scale"] if scale is None else scale, gate_mode=gm,
+                      stream=stream)
     return pool, out
 
 
@@ -53,6 +56,18 @@ def check_case(orc, case, pool_dev, out_dev):
         (case["idx"] >= 0) & (case["idx"] < case["N"]))[0])
     ob = bits(out_dev).reshape(case["B"], -1)
     assert np.all(ob[~active] == 0), "inactive rows must output +0.0"
+
+
+@pytest.mark.parametrize("gate_mode", [1, 2, 3])
+def test_precomputed_gate_conventions(orc, gate_mode):
+    """[decode] "T=1 fast path inside recurrent_kda": the pre-computed form
+    (log-space g, decay = exp(g); pre-sigmoided beta), alone or together, at
+    B = 512 with 5 % inactive rows; A_log and dt_bias are not passed when the
+    gate is pre-computed."""
+    case = synth.precomputed_gate(synth.decode_case(B=512, H=12), gate_mode,
+                                  synth.seed_for(1, 512, 100 + gate_mode))
+    pool, out = run_decode(case)
+    check_case(orc, case, pool, out)
 
 
 def test_single_row_slot2_of_4(orc):

@@ -22,6 +22,7 @@ def _kda():
 
 
 def run_prefill(case, pool=None, packed=False, use_initial_state=None, lower_bound=None):
+    gm = case.get("gate_mode", 0)
     """Launch kda_prefill_varlen on a case. packed: q/k/v are strided views of
     one [Ttot, 3*H*128] buffer and out is a view with a padded row."""
     H, Ttot = case["H"], case["Ttot"]
@@ -40,10 +41,11 @@ def run_prefill(case, pool=None, packed=False, use_initial_state=None, lower_bou
     cu_h = torch.from_numpy(case["cu_seqlens"].copy())
     uis = case["use_initial_state"] if use_initial_state is None else use_initial_state
     _kda().kda_prefill_varlen(cu_h, dev(case["cu_seqlens"]), q, k, v, dev_bf16(case["gate"]),
-                              dev_bf16(case["beta"]), dev(case["a_log"]), dev(case["dt_bias"]),
+                              dev_bf16(case["beta"]), None if gm & 1 else dev(case["a_log"]),
+                              None if gm & 1 else dev(case["dt_bias"]),
                               pool, dev(case["idx"]), out, use_initial_state=uis,
                               lower_bound=case["lower_bound"] if lower_bound is None
-                              else lower_bound, scale=case["scale"])
+                              else lower_bound, scale=case["scale"], gate_mode=gm)
     return pool, out
 
 
@@ -62,9 +64,13 @@ def oracle_prefill(orc, case, heads=None, use_initial_state=None, lower_bound=No
     lb = case["lower_bound"] if lower_bound is None else lower_bound
     c = np.ascontiguousarray
     pool = c(pool)
-    out = orc.prefill(case["cu_seqlens"], c(q), c(k), c(v), c(g), c(b), c(case["a_log"][hs]),
-                      c(case["dt_bias"].reshape(H, HD)[hs]), lb, case["scale"], pool,
-                      case["idx"], use_initial_state=uis, bf16_storage=True, real=np.float32)
+    gm = case.get("gate_mode", 0)
+    pre = bool(gm & 1)
+    out = orc.prefill(case["cu_seqlens"], c(q), c(k), c(v), c(g), c(b),
+                      None if pre else c(case["a_log"][hs]),
+                      None if pre else c(case["dt_bias"].reshape(H, HD)[hs]), lb,
+                      case["scale"], pool, case["idx"], use_initial_state=uis,
+                      bf16_storage=True, real=np.float32, gate_mode=gm)
     return out, pool
 
 
@@ -155,6 +161,23 @@ def test_many_docs_natural_order(orc):
     rng = np.random.Generator(np.random.PCG64(synth.seed_for(4, 1, 7)))
     lens = tuple(int(x) for x in rng.integers(0, 24, size=300))
     case = synth.prefill_case(lens, H=1, seed=synth.seed_for(4, 1, 8))
+    pool, out = run_prefill(case)
+    check_prefill(orc, case, pool, out)
+
+
+@pytest.mark.parametrize("gate_mode", [1, 2, 3])
+def test_precomputed_gate_conventions(orc, gate_mode):
+    """The pre-computed gate and / or beta convention over ragged documents."""
+    case = synth.prefill_case(SMALL_DOCS, H=3, seed=synth.seed_for(4, 3, 12))
+    case = synth.precomputed_gate(case, gate_mode, synth.seed_for(4, 3, 100 + gate_mode))
+    pool, out = run_prefill(case)
+    check_prefill(orc, case, pool, out)
+
+
+def test_precomputed_gate_full_h12(orc):
+    """Both pre-computed conventions on the 4-document set at H = 12."""
+    case = synth.precomputed_gate(synth.prefill_case(synth.DOCS_4, H=12), 3,
+                                  synth.seed_for(4, 12, 103))
     pool, out = run_prefill(case)
     check_prefill(orc, case, pool, out)
 

@@ -91,13 +91,15 @@ def run_gpu(case, flush_min=None, qkv=None, gate=None, beta=None, T=None, hist=N
     _kda().kda_verify_ucache_flush(
         qkv[..., :W], qkv[..., W:2 * W], qkv[..., 2 * W:],
         dev_bf16(case["gate"] if gate is None else gate),
-        dev_bf16(case["beta"] if beta is None else beta), dev(case["a_log"]),
-        dev(case["dt_bias"]), dev_state["pool"], dev(case["idx"]), dev_state["kc"],
+        dev_bf16(case["beta"] if beta is None else beta),
+        None if case.get("gate_mode", 0) & 1 else dev(case["a_log"]),
+        None if case.get("gate_mode", 0) & 1 else dev(case["dt_bias"]),
+        dev_state["pool"], dev(case["idx"]), dev_state["kc"],
         dev_state["uc"], dev_state["gc"],
         dev(case["hist_len"] if hist is None else hist),
         dev(case["cache_base"] if base is None else base), out,
         flush_min=case["flush_min"] if flush_min is None else flush_min, w_ring=case["w_ring"],
-        lower_bound=case["lower_bound"], scale=case["scale"])
+        lower_bound=case["lower_bound"], scale=case["scale"], gate_mode=case.get("gate_mode", 0))
     dev_state["out"] = out
     return dev_state
 
@@ -107,12 +109,14 @@ def run_oracle(orc, case, flush_min=None, qkv=None, gate=None, beta=None, hist=N
     q, k, v, g, be = _tok_arrays(case["qkv"] if qkv is None else qkv,
                                  case["gate"] if gate is None else gate,
                                  case["beta"] if beta is None else beta, H)
-    return orc.verify(q, k, v, g, be, case["a_log"], case["dt_bias"], case["lower_bound"],
+    gm = case.get("gate_mode", 0)
+    a_log, dt_bias = (None, None) if gm & 1 else (case["a_log"], case["dt_bias"])
+    return orc.verify(q, k, v, g, be, a_log, dt_bias, case["lower_bound"],
                       case["scale"], case["opool"], case["cidx"], case["okc"], case["ouc"],
                       case["ogc"], case["hist_len"] if hist is None else hist,
                       case["cache_base"] if base is None else base,
                       case["flush_min"] if flush_min is None else flush_min, case["w_ring"],
-                      bf16_storage=True, real=np.float32)
+                      bf16_storage=True, real=np.float32, gate_mode=gm)
 
 
 def check_all(case, st, ref_out, pool0, kc0, uc0, gc0, T=None, hist=None, base=None,
@@ -183,6 +187,16 @@ def test_bare_checkpoint_no_history(orc, T, B):
 @pytest.mark.parametrize("B", [1, 32, 512])
 def test_ring_history_and_fold(orc, T, fm, p, B):
     case = build_case(orc, B, T, w_ring=16, flush_min=fm, fold_p=p)
+    verify_roundtrip(orc, case)
+
+
+@pytest.mark.parametrize("T,fm,p,gate_mode", [(8, 9, 0.5, 3), (4, 13, 1.0, 1), (8, 9, 0.0, 2)])
+def test_precomputed_gate_conventions(orc, T, fm, p, gate_mode):
+    """The pre-computed gate and / or beta convention on the draft tokens, with
+    ring history and folding rows, B = 512 (the history itself was written
+    under the raw convention, as a caller switching conventions would see)."""
+    case = build_case(orc, 512, T, w_ring=16, flush_min=fm, fold_p=p)
+    case = synth.precomputed_gate(case, gate_mode, synth.seed_for(3, 512, 100 + gate_mode))
     verify_roundtrip(orc, case)
 
 

@@ -186,14 +186,24 @@ def _prefill_args(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, sc
 
 
 def prefill(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,
-            use_initial_state=True, bf16_storage=True, real=np.float32, gate_mode=0):
+            use_initial_state=True, bf16_storage=True, real=np.float32, gate_mode=0,
+            checkpoints=None, checkpoint_starts=None, checkpoint_interval=16):
     """Token-by-token varlen prefill. q/k/graw [Ttot,H,K], v [Ttot,H,V], beta_logit [Ttot,H],
-    cu int32 [n_docs+1], idx int32 [n_docs], pool [N,H,V,K] updated in place. -> out [Ttot,H,V]."""
+    cu int32 [n_docs+1], idx int32 [n_docs], pool [N,H,V,K] updated in place. -> out [Ttot,H,V].
+    checkpoints [rows,H,V,K] (updated in place) with checkpoint_starts int64 [n_docs]: the
+    state after every checkpoint_interval tokens of each active document."""
     out = np.zeros((q.shape[0], q.shape[1], v.shape[2]), real)
     f = getattr(lib(), "orc_prefill_tbt_" + _suffix(real))
+    if checkpoints is None:
+        ck, rows, starts = _rp(None, real), 0, ctypes.POINTER(ctypes.c_int64)()
+    else:
+        assert checkpoint_starts.dtype == np.int64 and checkpoint_starts.flags["C_CONTIGUOUS"]
+        ck, rows = _rp(checkpoints, real), checkpoints.shape[0]
+        starts = checkpoint_starts.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
     f(*_prefill_args(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool,
                      idx, use_initial_state, out, real), ctypes.c_int(1 if bf16_storage else 0),
-      ctypes.c_int(gate_mode))
+      ctypes.c_int(gate_mode), ck, ctypes.c_int64(rows), starts,
+      ctypes.c_int(int(checkpoint_interval)))
     return out
 
 

@@ -341,14 +341,22 @@ void verify(int B, int T, int H, int K, int V, const Real* q, const Real* k, con
 // document whose slot index is outside [0, N) writes zero outputs and leaves
 // the pool untouched. A zero-length document with an initial state writes
 // nothing.
+// Intermediate checkpoints (same page: the prefill returns "output, final
+// state, checkpoints", with checkpoint_cu_starts, int64; the positions are a
+// reading): when ckpt is not null, an active document also stores its state
+// after its first i * interval tokens, i = 1 .. floor(len / interval), into
+// checkpoint row ckpt_starts[d] + i - 1 (rows outside [0, ckpt_rows) are
+// skipped), rounded like the final state.
 // q, k, graw: [Ttot][H][K]; v: [Ttot][H][V]; beta_logit: [Ttot][H];
-// cu: [n_docs + 1]; idx: [n_docs]; pool: [N][H][V][K]; out: [Ttot][H][V].
+// cu: [n_docs + 1]; idx: [n_docs]; pool: [N][H][V][K]; out: [Ttot][H][V];
+// ckpt: [ckpt_rows][H][V][K]; ckpt_starts: [n_docs].
 template <class Real>
 void prefill_tbt(int n_docs, int H, int K, int V, const int32_t* cu, const Real* q,
                  const Real* k, const Real* v, const Real* graw, const Real* beta_logit,
                  const Real* a_log, const Real* dt_bias, Real lower_bound, Real scale,
                  Real* pool, int64_t N, const int32_t* idx, int use_initial_state, Real* out,
-                 int bf16_storage, int gate_mode) {
+                 int bf16_storage, int gate_mode, Real* ckpt, int64_t ckpt_rows,
+                 const int64_t* ckpt_starts, int interval) {
   const int64_t KV = i64(K) * V;
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int d = 0; d < n_docs; ++d) {
@@ -374,6 +382,14 @@ void prefill_tbt(int n_docs, int H, int K, int V, const int32_t* cu, const Real*
         step<Real>(K, V, S.data(), qh.data(), kh.data(), v + (i64(t) * H + h) * V, g.data(),
                    beta, scale, o, nullptr);
         for (int r = 0; r < V; ++r) o[r] = store(o[r], bf16_storage);
+        const int done = t - t0 + 1;  // tokens of the document consumed
+        if (ckpt && done % interval == 0) {
+          const int64_t row = ckpt_starts[d] + done / interval - 1;
+          if (row >= 0 && row < ckpt_rows) {
+            Real* c = ckpt + (row * H + h) * KV;
+            for (int64_t e = 0; e < KV; ++e) c[e] = store(S[e], bf16_storage);
+          }
+        }
       }
       for (int64_t e = 0; e < KV; ++e) slot[e] = store(S[e], bf16_storage);
     }
@@ -542,10 +558,11 @@ void prefill_chunked(int n_docs, int H, int K, int V, const int32_t* cu, const R
       const Real* v, const Real* graw, const Real* beta_logit, const Real* a_log,             \
       const Real* dt_bias, Real lower_bound, Real scale, Real* pool, int64_t N,               \
       const int32_t* idx, int use_initial_state, Real* out, int bf16_storage,                 \
-      int gate_mode) {                                                                        \
+      int gate_mode, Real* ckpt, int64_t ckpt_rows, const int64_t* ckpt_starts,               \
+      int interval) {                                                                         \
     prefill_tbt<Real>(n_docs, H, K, V, cu, q, k, v, graw, beta_logit, a_log, dt_bias,         \
                       lower_bound, scale, pool, N, idx, use_initial_state, out, bf16_storage, \
-                      gate_mode);                                                             \
+                      gate_mode, ckpt, ckpt_rows, ckpt_starts, interval);                     \
   }                                                                                           \
   extern "C" void orc_prefill_chunked_##SUF(                                                  \
       int n_docs, int H, int K, int V, const int32_t* cu, const Real* q, const Real* k,       \

@@ -724,3 +724,53 @@ def test_precomputed_beta1_exact_retrieval_and_beta0_pure_decay(orc):
             qq = d["q"][b, h]
             np.testing.assert_allclose(out[b, h], 0.5 * ref @ (qq / np.sqrt(qq @ qq + 1e-6)),
                                        rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Prefill intermediate checkpoints ([prefill]: output, final state,
+# checkpoints; checkpoint_cu_starts). Reading: the state after every
+# `interval` tokens of a document.
+
+def test_prefill_checkpoints_equal_truncated_prefills(orc):
+    """Checkpoint i of document d equals the final state of the same prefill
+    run on d's first i * interval tokens; the final state is unchanged by
+    asking for checkpoints; rows outside the buffer and inactive documents
+    write nothing."""
+    rng = _rng(210)
+    lens = (40, 0, 64, 15, 33)
+    interval = 16
+    d = _prefill_inputs(rng, lens, H=2)
+    d["idx"][3] = -1  # inactive: no checkpoints
+    counts = [n // interval for n in lens]          # 2, 0, 4, 0, 2
+    starts = np.array([0, 2, 2, 6, 7], np.int64)    # row 6 is a gap; doc 4 takes 7 and 8
+    rows = 8                                        # doc 4's row 8 lies outside: skipped
+    ck = np.full((rows, 2, 128, 128), -7.0)
+    p1 = d["pool"].copy()
+    o1 = orc.prefill(*_pf_args(d), p1, d["idx"], bf16_storage=False, real=F64,
+                     checkpoints=ck, checkpoint_starts=starts, checkpoint_interval=interval)
+    p0 = d["pool"].copy()
+    o0 = orc.prefill(*_pf_args(d), p0, d["idx"], bf16_storage=False, real=F64)
+    np.testing.assert_array_equal(o1, o0)
+    np.testing.assert_array_equal(p1, p0)
+    written = np.zeros(rows, bool)
+    for doc, n in enumerate(lens):
+        if d["idx"][doc] < 0:
+            continue
+        for i in range(1, counts[doc] + 1):
+            row = starts[doc] + i - 1
+            if row >= rows:
+                continue
+            # the same document truncated to its first i * interval tokens
+            t0 = int(d["cu"][doc])
+            sl = slice(t0, t0 + i * interval)
+            sub = dict(cu=np.array([0, i * interval], np.int32),
+                       **{n_: np.ascontiguousarray(d[n_][sl])
+                          for n_ in ("q", "k", "v", "graw", "beta_logit")})
+            pool = d["pool"].copy()
+            orc.prefill(sub["cu"], sub["q"], sub["k"], sub["v"], sub["graw"],
+                        sub["beta_logit"], d["a_log"], d["dt_bias"], -5.0, 1.0, pool,
+                        d["idx"][doc:doc + 1].copy(), bf16_storage=False, real=F64)
+            np.testing.assert_array_equal(ck[row], pool[d["idx"][doc]])
+            written[row] = True
+    assert written.tolist() == [True] * 6 + [False, True]
+    assert np.all(ck[~written] == -7.0)

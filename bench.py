@@ -278,7 +278,7 @@ class PrefillSetup:
     A_log U(-1, 1), dt_bias N(0, 0.1), initial states N(0, 0.05) in a pool of
     2 slots per document)."""
 
-    def __init__(self, lens, H, torch, kda, synth, gate_mode=0):
+    def __init__(self, lens, H, torch, kda, synth, gate_mode=0, ckpt_interval=0):
         self.lens, self.H, self.gate_mode = tuple(lens), H, gate_mode
         n_docs, T, W = len(lens), int(sum(lens)), H * 128
         gen = torch.Generator(device="cuda")
@@ -306,6 +306,16 @@ class PrefillSetup:
         self.out = torch.empty((T, W), dtype=torch.bfloat16, device="cuda")
         self.ws = torch.empty(kda.kda_prefill_workspace_size(n_docs, T, H), dtype=torch.uint8,
                               device="cuda")
+        # intermediate checkpoints every ckpt_interval tokens (0: none)
+        self.ck = self.ck_starts = None
+        self.ck_interval, self.ck_rows = max(ckpt_interval, 16), 0
+        if ckpt_interval:
+            counts = np.asarray(lens) // ckpt_interval
+            self.ck_rows = int(counts.sum())
+            starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
+            self.ck_starts = torch.from_numpy(starts).cuda()
+            self.ck = torch.empty((self.ck_rows, H, 128, 128), dtype=torch.bfloat16,
+                                  device="cuda")
         self.kda = kda
 
     def calls(self):
@@ -317,7 +327,9 @@ class PrefillSetup:
             s.kda.kda_prefill_varlen(s.cu_h, s.cu_d, s.q, s.k, s.v, s.g, s.beta,
                                      None if pre else s.a_log, None if pre else s.dtb,
                                      s.pool, s.idx, s.out, workspace=s.ws,
-                                     gate_mode=s.gate_mode)
+                                     gate_mode=s.gate_mode, checkpoints=s.ck,
+                                     checkpoint_cu_starts=s.ck_starts,
+                                     checkpoint_interval=s.ck_interval)
         return [call]
 
 
@@ -476,19 +488,23 @@ def main():
                 del vs
         del rings
         torch.cuda.empty_cache()
-        pcfgs = [(name, lens, Hp, 0)
+        pcfgs = [(name, lens, Hp, 0, 0)
                  for name, lens in (("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4),
                                     ("14-doc mix, 16384 tokens", synth.DOCS_14))
                  for Hp in (64, 12)]
-        pcfgs.append(("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4, 12, 3))
-        for name, lens, Hp, gm in pcfgs:
-            ps = PrefillSetup(lens, Hp, torch, kda, synth, gate_mode=gm)
+        pcfgs.append(("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4, 12, 3, 0))
+        pcfgs.append(("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4, 12, 0, 64))
+        for name, lens, Hp, gm, cki in pcfgs:
+            ps = PrefillSetup(lens, Hp, torch, kda, synth, gate_mode=gm, ckpt_interval=cki)
             st = max(10, min(args.steps, 50))
             _, e = time_graphs(ps.calls(), st, 2, torch, min_warm_s=0.3)
             us = e * 1e3 / st
-            nb = wm.prefill_bytes(lens, Hp)
+            # each checkpoint row writes H bf16 states
+            nb = wm.prefill_bytes(lens, Hp) + ps.ck_rows * Hp * 128 * 128 * 2
             fl = wm.prefill_flops(lens, Hp)
             extra = {"gate": "pre-computed g and beta"} if gm else {}
+            if cki:
+                extra["checkpoints"] = f"every {cki} tokens ({ps.ck_rows} rows)"
             points.append(dict(kind="prefill", H=Hp, docs=name, tokens=int(sum(lens)),
                                **extra, us_per_call=round(us, 1),
                                Mtok_per_s=round(sum(lens) / (us * 1e-6) / 1e6, 2),

@@ -41,7 +41,7 @@ _SIGS = {
     "kda_prefill_varlen": (_c.c_int, [_I32, _I64, _I32, _I32, _I32, _P, _P,
                                       _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
                                       _P, _P, _F, _F, _I32, _P, _I64, _I64, _P, _I32,
-                                      _P, _I64, _P, _c.c_size_t, _P]),
+                                      _P, _I64, _P, _I64, _P, _I32, _P, _c.c_size_t, _P]),
 }
 
 
@@ -202,12 +202,17 @@ def kda_prefill_workspace_size(n_docs: int, total_tokens: int, H: int) -> int:
 def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_log, dt_bias,
                        state_pool, state_indices, out, workspace=None,
                        use_initial_state: bool = True, lower_bound: float = -5.0,
-                       scale: float = 1.0, gate_mode: int = 0, stream=None) -> None:
+                       scale: float = 1.0, gate_mode: int = 0, checkpoints=None,
+                       checkpoint_cu_starts=None, checkpoint_interval: int = 16,
+                       stream=None) -> None:
     """Varlen prefill. cu_seqlens_host: CPU int32 [n_docs+1]; cu_seqlens: the
     same on the GPU; q, k, v, g_raw, out: bf16 [Ttot, H*128] (token-strided);
     beta_raw bf16 [Ttot, H]; state_indices int32 [n_docs]; workspace: uint8
     GPU tensor of >= kda_prefill_workspace_size(...) bytes, or None to have
-    one allocated here for this call."""
+    one allocated here for this call. checkpoints: bf16 [rows, H, 128, 128]
+    (contiguous) receiving the state after every checkpoint_interval tokens of
+    each document at rows checkpoint_cu_starts[d] + i (int64 GPU tensor
+    [n_docs]), or None."""
     import torch
     if cu_seqlens_host.dtype != torch.int32 or cu_seqlens_host.is_cuda or \
             not cu_seqlens_host.is_contiguous():
@@ -229,6 +234,16 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ck_rows = 0
+    if checkpoints is not None:
+        _bf16("checkpoints", checkpoints)
+        if not checkpoints.is_contiguous() or \
+                checkpoints.numel() != checkpoints.shape[0] * H * HEAD_DIM * HEAD_DIM:
+            raise ValueError("checkpoints must be a contiguous bf16 [rows, H, 128, 128] tensor")
+        if checkpoint_cu_starts is None or checkpoint_cu_starts.dtype != torch.int64 or \
+                not checkpoint_cu_starts.is_cuda or not checkpoint_cu_starts.is_contiguous():
+            raise ValueError("checkpoint_cu_starts must be a contiguous int64 GPU tensor")
+        ck_rows = checkpoints.shape[0]
     cu_h = _P(cu_seqlens_host.data_ptr())
     st = lib().kda_prefill_varlen(
         n_docs, Ttot, H, HEAD_DIM, HEAD_DIM, cu_h, _ptr(cu_seqlens),
@@ -237,5 +252,6 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
         _ptr(A_log), _ptr(dt_bias), float(lower_bound), float(scale), int(gate_mode),
         _ptr(state_pool) if N else _P(0), N, slot_stride, _ptr(state_indices),
         1 if use_initial_state else 0, _ptr(out), out.stride(0),
+        _ptr(checkpoints), ck_rows, _ptr(checkpoint_cu_starts), int(checkpoint_interval),
         _ptr(workspace), ws_bytes, _stream(stream))
     _check("kda_prefill_varlen", st)

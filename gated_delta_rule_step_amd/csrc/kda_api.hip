@@ -211,7 +211,8 @@ extern "C" kda_status kda_prefill_varlen(
     int64_t beta_tok_stride, const float* A_log, const float* dt_bias, float lower_bound,
     float scale, int32_t gate_mode, void* state_pool, int64_t num_slots, int64_t slot_stride,
     const int32_t* state_indices, int32_t use_initial_state, void* out, int64_t out_tok_stride,
-    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    void* checkpoints, int64_t checkpoint_rows, const int64_t* checkpoint_cu_starts,
+    int32_t checkpoint_interval, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (n_docs < 0 || total_tokens < 0 || H < 1 || num_slots < 0) return KDA_ERR_BAD_SHAPE;
   if (K != D || V != D) return KDA_ERR_UNSUPPORTED;
   // 16-token chunks factor each decay weight into two exps of at most 8 |lb|.
@@ -224,8 +225,14 @@ extern "C" kda_status kda_prefill_varlen(
   if (const kda_status gs = check_gate(gate_mode, lower_bound, A_log, dt_bias)) {
     if (gs == KDA_ERR_UNSUPPORTED || n_docs > 0) return gs;
   }
+  if (checkpoints) {
+    if (checkpoint_rows < 0) return KDA_ERR_BAD_SHAPE;
+    // checkpoints sit on 16-token chunk boundaries
+    if (checkpoint_interval < 16 || checkpoint_interval % 16 != 0) return KDA_ERR_UNSUPPORTED;
+  }
   if (n_docs == 0) return KDA_OK;
   if (!cu_seqlens || !state_indices) return KDA_ERR_NULL_POINTER;
+  if (checkpoints && !checkpoint_cu_starts) return KDA_ERR_NULL_POINTER;
   if (total_tokens > 0 && (!q || !k || !v || !g_raw || !beta_raw || !out))
     return KDA_ERR_NULL_POINTER;
   if (num_slots > 0 && !state_pool) return KDA_ERR_NULL_POINTER;
@@ -269,11 +276,15 @@ extern "C" kda_status kda_prefill_varlen(
   p.use_initial_state = use_initial_state ? 1 : 0;
   p.out = static_cast<uint16_t*>(out);
   p.out_tok_stride = out_tok_stride;
+  p.ckpt = static_cast<uint16_t*>(checkpoints);
+  p.ckpt_rows = checkpoints ? checkpoint_rows : 0;
+  p.ckpt_starts = checkpoint_cu_starts;
+  p.ckpt_interval = checkpoints ? checkpoint_interval : 16;
   p.workspace = workspace;
   const bool vec = aligned16(q) && aligned16(k) && aligned16(v) && aligned16(g_raw) &&
                    aligned16(dt_bias) && aligned16(out) &&
-                   (num_slots == 0 || aligned16(state_pool)) && mult8(q_tok_stride) &&
-                   mult8(k_tok_stride) && mult8(v_tok_stride) && mult8(g_tok_stride) &&
-                   mult8(out_tok_stride) && mult8(slot_stride);
+                   (num_slots == 0 || aligned16(state_pool)) && aligned16(checkpoints) &&
+                   mult8(q_tok_stride) && mult8(k_tok_stride) && mult8(v_tok_stride) &&
+                   mult8(g_tok_stride) && mult8(out_tok_stride) && mult8(slot_stride);
   return launch_status(kda::launch_prefill(p, cu_seqlens_host, vec, stream));
 }

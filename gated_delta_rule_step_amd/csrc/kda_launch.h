@@ -79,6 +79,10 @@ struct PrefillParams {
   int32_t use_initial_state;
   uint16_t* out;
   int64_t out_tok_stride;
+  uint16_t* ckpt;              // NULL: no intermediate checkpoints
+  int64_t ckpt_rows;
+  const int64_t* ckpt_starts;  // [n_docs]
+  int32_t ckpt_interval;       // tokens, a multiple of 16
   void* workspace;
 };
 

@@ -541,6 +541,10 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
 
   const int nchunks = int((len + C - 1) / C);
   const int64_t sigma0 = doc_slot0(p.cu_seqlens, doc);
+  // first checkpoint row of this document (checkpoints after every
+  // ckpt_interval tokens, a multiple of the chunk)
+  const int64_t ckpt_row0 = p.ckpt ? p.ckpt_starts[doc] : 0;
+  const int ckpt_every = p.ckpt_interval / C;
   const uint8_t* ws = static_cast<const uint8_t*>(p.workspace);
   auto rec_of = [&](int ch) {
     return reinterpret_cast<const u32x4*>(ws + ((sigma0 + ch) * p.H + h) * int64_t(kRecBytes));
@@ -642,6 +646,19 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
       a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(khi, ulo, a, 0, 0, 0);
       a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(klo, uhi, a, 0, 0, 0);
       acc[mt] = a;
+    }
+    // intermediate checkpoint after this chunk
+    if (p.ckpt && (ch + 1) % ckpt_every == 0 && int64_t(ch + 1) * C <= len) {
+      const int64_t row = ckpt_row0 + (ch + 1) / ckpt_every - 1;
+      if (row >= 0 && row < p.ckpt_rows) {
+        uint16_t* cp = p.ckpt + (row * p.H + h) * int64_t(HEAD_ELEMS);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const f32x4 a = acc[mt];
+          gstore4<VEC>(cp + v * D + 16 * mt + 4 * g4,
+                       u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])});
+        }
+      }
     }
     // record ch+1 (its loads were issued a chunk ago) into the other buffer,
     // last read before the previous barrier; then the loads of record ch+2

@@ -244,6 +244,22 @@ size_t kda_prefill_workspace_size(int32_t n_docs, int64_t total_tokens, int32_t 
  *                     gets zero outputs and no state write
  *  use_initial_state  1: start each chain from its slot; 0: from zeros
  *  out                bf16, element (t, h*128 + v) at t*out_tok_stride + h*128 + v
+ *  checkpoints        NULL (no intermediate checkpoints), or bf16 rows of H
+ *                     states laid out like a pool slot (row r, head h at
+ *                     (r*H + h)*16384, element (v, c) at v*128 + c). The page
+ *                     returns "output, final state, checkpoints" with an int64
+ *                     checkpoint_cu_starts; the positions are this library's
+ *                     reading: an active document d stores its state after its
+ *                     first i*checkpoint_interval tokens, i = 1 ..
+ *                     floor(len_d / checkpoint_interval), into row
+ *                     checkpoint_cu_starts[d] + i - 1; rows outside
+ *                     [0, checkpoint_rows) are skipped; inactive documents store
+ *                     none. Rounded to bf16 like the final state.
+ *  checkpoint_rows    rows of `checkpoints` (>= 0)
+ *  checkpoint_cu_starts  int64 [n_docs] device array (read only when
+ *                     checkpoints is not NULL)
+ *  checkpoint_interval  tokens between checkpoints: a positive multiple of 16
+ *                     (the chunk), else KDA_ERR_UNSUPPORTED
  *  workspace          device buffer of >= kda_prefill_workspace_size(...) bytes,
  *                     256-byte aligned (may be NULL when that size is 0); the
  *                     per-chunk operands pass through it from the preparation
@@ -277,6 +293,8 @@ kda_status kda_prefill_varlen(int32_t n_docs, int64_t total_tokens, int32_t H, i
                               void* state_pool, int64_t num_slots, int64_t slot_stride,
                               const int32_t* state_indices, int32_t use_initial_state,
                               void* out, int64_t out_tok_stride,
+                              void* checkpoints, int64_t checkpoint_rows,
+                              const int64_t* checkpoint_cu_starts, int32_t checkpoint_interval,
                               void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 

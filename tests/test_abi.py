@@ -152,13 +152,14 @@ def test_prefill_workspace_and_validation(lib):
 
     def call(cu, total, **kw):
         p = P(1 << 20)
-        a = dict(n=len(cu) - 1, H=2, K=128, ws=1 << 40, ots=256, lb=-5.0, ws_ptr=p, gm=0)
+        a = dict(n=len(cu) - 1, H=2, K=128, ws=1 << 40, ots=256, lb=-5.0, ws_ptr=p, gm=0,
+                 ck=P(0), ck_rows=0, ck_starts=P(0), ck_int=16)
         a.update(kw)
         arr = (ctypes.c_int32 * len(cu))(*cu)
         return lib.kda_prefill_varlen(a["n"], total, a["H"], a["K"], 128, arr, p, p, 256, p,
                                       256, p, 256, p, 256, p, 2, p, p, a["lb"], 1.0, a["gm"], p, 4,
-                                      2 * 128 * 128, p, 1, p, a["ots"], a["ws_ptr"], a["ws"],
-                                      P(0))
+                                      2 * 128 * 128, p, 1, p, a["ots"], a["ck"], a["ck_rows"],
+                                      a["ck_starts"], a["ck_int"], a["ws_ptr"], a["ws"], P(0))
 
     assert call([1, 5], 5) == SEQ       # must start at 0
     assert call([0, 5, 3], 3) == SEQ    # must not decrease
@@ -170,6 +171,13 @@ def test_prefill_workspace_and_validation(lib):
     assert call([0, 5], 5, lb=float("nan")) == UNSUP
     assert call([0], 0) == OK           # no documents: nothing to do
     assert call([0, 5], 5, gm=4) == UNSUP
+    # intermediate checkpoints: on chunk boundaries, a row count, a starts array
+    q = P(1 << 20)
+    assert call([0, 5], 5, ck=q, ck_rows=3, ck_starts=q, ck_int=24) == UNSUP
+    assert call([0, 5], 5, ck=q, ck_rows=3, ck_starts=q, ck_int=0) == UNSUP
+    assert call([0, 5], 5, ck=q, ck_rows=-1, ck_starts=q) == SHAPE
+    assert call([0, 5], 5, ck=q, ck_rows=3) == NULLP
+    assert call([0], 0, ck=q, ck_rows=3, ck_starts=q, ck_int=32) == OK
     assert call([0, 5], 5, gm=1, lb=0.5) == UNSUP  # also outside the prefill's |lb| <= 5.5
     assert call([0, 5], 5, ws=2 * rec - 1) == WS   # one slot, two heads
     assert call([0, 5], 5, ws=2 * rec, ws_ptr=P(0)) == NULLP

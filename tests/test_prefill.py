@@ -21,7 +21,8 @@ def _kda():
     return kda
 
 
-def run_prefill(case, pool=None, packed=False, use_initial_state=None, lower_bound=None):
+def run_prefill(case, pool=None, packed=False, use_initial_state=None, lower_bound=None,
+                checkpoints=None, ckpt_starts=None, ckpt_interval=16):
     gm = case.get("gate_mode", 0)
     """Launch kda_prefill_varlen on a case. packed: q/k/v are strided views of
     one [Ttot, 3*H*128] buffer and out is a view with a padded row."""
@@ -45,11 +46,15 @@ def run_prefill(case, pool=None, packed=False, use_initial_state=None, lower_bou
                               None if gm & 1 else dev(case["dt_bias"]),
                               pool, dev(case["idx"]), out, use_initial_state=uis,
                               lower_bound=case["lower_bound"] if lower_bound is None
-                              else lower_bound, scale=case["scale"], gate_mode=gm)
+                              else lower_bound, scale=case["scale"], gate_mode=gm,
+                              checkpoints=checkpoints,
+                              checkpoint_cu_starts=None if ckpt_starts is None
+                              else dev(ckpt_starts), checkpoint_interval=ckpt_interval)
     return pool, out
 
 
-def oracle_prefill(orc, case, heads=None, use_initial_state=None, lower_bound=None):
+def oracle_prefill(orc, case, heads=None, use_initial_state=None, lower_bound=None,
+                   ckpt=None, ckpt_starts=None, ckpt_interval=16):
     """fp32 token-by-token oracle over the heads listed (all by default).
     Returns (out [Ttot, nh, 128], pool [N, nh, 128, 128] float32 after the run)."""
     H, Ttot = case["H"], case["Ttot"]
@@ -70,7 +75,8 @@ def oracle_prefill(orc, case, heads=None, use_initial_state=None, lower_bound=No
                       None if pre else c(case["a_log"][hs]),
                       None if pre else c(case["dt_bias"].reshape(H, HD)[hs]), lb,
                       case["scale"], pool, case["idx"], use_initial_state=uis,
-                      bf16_storage=True, real=np.float32, gate_mode=gm)
+                      bf16_storage=True, real=np.float32, gate_mode=gm, checkpoints=ckpt,
+                      checkpoint_starts=ckpt_starts, checkpoint_interval=ckpt_interval)
     return out, pool
 
 
@@ -180,6 +186,66 @@ def test_precomputed_gate_full_h12(orc):
                                   synth.seed_for(4, 12, 103))
     pool, out = run_prefill(case)
     check_prefill(orc, case, pool, out)
+
+
+def _ckpt_roundtrip(orc, case, interval, starts, rows, heads=None):
+    """Prefill with intermediate checkpoints; compare written rows with the
+    oracle's, check that every other row is untouched and that outputs and
+    final states match as without checkpoints."""
+    H = case["H"]
+    hs = np.arange(H) if heads is None else np.asarray(heads)
+    fill = synth.filler_bits((rows, H, HD, HD), 7)
+    ck = dev_bf16(fill)
+    pool, out = run_prefill(case, checkpoints=ck, ckpt_starts=starts, ckpt_interval=interval)
+    check_prefill(orc, case, pool, out, heads=heads)
+    ref_ck = np.zeros((rows, len(hs), HD, HD), np.float32)
+    oracle_prefill(orc, case, heads=heads, ckpt=ref_ck, ckpt_starts=starts,
+                   ckpt_interval=interval)
+    got = bits(ck)
+    lens = np.diff(case["cu_seqlens"])
+    active = (case["idx"] >= 0) & (case["idx"] < case["N"])
+    written = np.zeros(rows, bool)
+    for d, n in enumerate(lens):
+        if not active[d]:
+            continue
+        for i in range(1, n // interval + 1):
+            r = int(starts[d]) + i - 1
+            if 0 <= r < rows:
+                written[r] = True
+                check_state(got[r][hs], ref_ck[r], f"checkpoint row {r} (doc {d}, i {i})")
+    assert np.array_equal(got[~written], fill[~written]), "rows that are not checkpoints changed"
+    return written
+
+
+def test_checkpoints_small_docs(orc):
+    """Checkpoints every 16 tokens over ragged documents: one inactive
+    document, a gap row, and a last row outside the buffer (skipped)."""
+    case = synth.prefill_case(SMALL_DOCS, H=3, seed=synth.seed_for(4, 3, 20))
+    case["idx"][5] = -1  # the 33-token document: inactive, no checkpoints
+    lens = np.diff(case["cu_seqlens"])
+    counts = lens // 16
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
+    starts[6:] += 1          # a gap row before the 50-token document
+    rows = int(starts[-1] + counts[-1]) - 1   # the last checkpoint falls outside
+    written = _ckpt_roundtrip(orc, case, 16, starts, rows)
+    assert written.sum() == counts[np.arange(len(lens)) != 5].sum() - 1
+
+
+@pytest.mark.parametrize("interval", [48, 64])
+def test_checkpoints_longer_interval(orc, interval):
+    case = synth.prefill_case((100, 47, 96, 130), H=2, seed=synth.seed_for(4, 2, 21),
+                              use_initial_state=False)
+    counts = np.diff(case["cu_seqlens"]) // interval
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
+    _ckpt_roundtrip(orc, case, interval, starts, int(counts.sum()))
+
+
+def test_checkpoints_full_h12(orc):
+    """The 4-document set at H = 12 with a checkpoint every 256 tokens (53 rows)."""
+    case = synth.prefill_case(synth.DOCS_4, H=12)
+    counts = np.diff(case["cu_seqlens"]) // 256
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
+    _ckpt_roundtrip(orc, case, 256, starts, int(counts.sum()))
 
 
 @pytest.mark.parametrize("lb", [-5.5, -1.0, 0.0])

@@ -359,6 +359,38 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   }
   __syncthreads();
 
+  // ---- 3b. fold: S_cur = exp(G_L) * S_ckpt + sum_j u_j D_j over this wave's
+  // fragments, stored in bf16 over the checkpoint. It needs only the
+  // checkpoint fragments, exp(G_L), D_j and u_j, all ready here, so its stores
+  // drain while phases 4-7 run. (The checkpoint fragments stay in registers
+  // for phase 6.) With no history S_cur is the checkpoint itself and nothing
+  // is rewritten.
+  if (fold && hist > 0) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int v = 32 * wave + 16 * blk + fv;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int k0 = 32 * st + fk;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = bf_lo(sf[blk][st][e]) * s.egl[k0 + 2 * e];
+          x[2 * e + 1] = bf_hi(sf[blk][st][e]) * s.egl[k0 + 2 * e + 1];
+        }
+        for (int j = 0; j < hist; ++j) {
+          const float uj = bf1(s.uh[j * D + v]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = fmaf(uj, s.dh[j * D + k0 + e], x[e]);
+        }
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+        store8_raw<VEC>(ckpt + int64_t(v) * D + k0, w);
+      }
+    }
+  }
+
   // ---- 4. A and P: one (r, j) pair per 16-lane group, 8 channels per lane.
   {
     const int grp = tid >> 4;
@@ -500,6 +532,41 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
         acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfr, acc[blk], 0, 0, 0);
       }
     }
+    // History correction C U_hist (C = X D^T from phase 5b, 2T x hist; U_hist
+    // the ring's bf16 u rows, exact as B operands): one more K = 32
+    // contraction over history entries j = 8 (lane / 16) + e, with C split into
+    // bf16 hi and lo; entries j >= hist are zero on both sides.
+    if (hist > 0) {
+      float cr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = fk + e;
+        cr[e] = (!xzero && j < hist) ? s.cm[fv * hm + j] : 0.f;
+      }
+      u32x4 hi, lo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = pack_bf16x2(cr[2 * i], cr[2 * i + 1]);
+        lo[i] = pack_bf16x2(cr[2 * i] - bf_lo(hi[i]), cr[2 * i + 1] - bf_hi(hi[i]));
+      }
+      const bf16x8 chi = __builtin_bit_cast(bf16x8, hi);
+      const bf16x8 clo = __builtin_bit_cast(bf16x8, lo);
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int v = 32 * wave + 16 * blk + fv;
+        u32x4 ub;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = fk + 2 * i;
+          const uint32_t u0 = j < hist ? s.uh[j * D + v] : 0u;
+          const uint32_t u1 = j + 1 < hist ? s.uh[(j + 1) * D + v] : 0u;
+          ub[i] = u0 | (u1 << 16);
+        }
+        const bf16x8 bu = __builtin_bit_cast(bf16x8, ub);
+        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(chi, bu, acc[blk], 0, 0, 0);
+        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(clo, bu, acc[blk], 0, 0, 0);
+      }
+    }
     __syncthreads();  // every wave has read its X rows: Y may overwrite them
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -520,47 +587,14 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       if (t < T) {
-        float yw = s.y[t * XS + v];
-        for (int j = 0; j < hist; ++j) yw = fmaf(s.cm[t * hm + j], bf1(s.uh[j * D + v]), yw);
-        u[t] = s.vv[t * XS + v] - yw;
+        u[t] = s.vv[t * XS + v] - s.y[t * XS + v];
         if ((t & 1) == half) {
           float yq = s.y[(T + t) * XS + v];
-          for (int j = 0; j < hist; ++j)
-            yq = fmaf(s.cm[(T + t) * hm + j], bf1(s.uh[j * D + v]), yq);
 #pragma unroll
           for (int j = 0; j <= t; ++j) yq = fmaf(s.pm[t * TMAX + j], u[j], yq);
           __builtin_nontemporal_store(to_bf16(p.scale * yq), outb + int64_t(t) * p.out_tok_stride + v);
           __builtin_nontemporal_store(to_bf16(u[t]), uc + int64_t(ring_row(hist + t)) * D + v);
         }
-      }
-    }
-  }
-
-  // ---- 8. fold: S_cur = exp(G_L) * S_ckpt + sum_j u_j D_j over this wave's
-  // fragments, stored in bf16 over the checkpoint. With no history S_cur is
-  // the checkpoint itself and nothing is rewritten.
-  if (fold && hist > 0) {
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int v = 32 * wave + 16 * blk + fv;
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int k0 = 32 * st + fk;
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[2 * e] = bf_lo(sf[blk][st][e]) * s.egl[k0 + 2 * e];
-          x[2 * e + 1] = bf_hi(sf[blk][st][e]) * s.egl[k0 + 2 * e + 1];
-        }
-        for (int j = 0; j < hist; ++j) {
-          const float uj = bf1(s.uh[j * D + v]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = fmaf(uj, s.dh[j * D + k0 + e], x[e]);
-        }
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
-        store8_raw<VEC>(ckpt + int64_t(v) * D + k0, w);
       }
     }
   }

@@ -54,19 +54,19 @@ COUNTED_TRAFFIC = {
         sources=("gated_delta_rule_step_amd/csrc/kda_decode.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
-        sha256=("779051e40ebca063e86ddd83f1ed6ed3c5742ee6e5c7f7998eaacfa6ebd2a385",
-                "34b8100422cba3857f715dc728116de3c64c225b97154059cd0d5945ac5a48f0",
+        sha256=("a629490627c39e46695ab5c0e93098d616ab9c1a1e2ba39e18dbfc59c4904ace",
+                "9263cc848eebfe534d02cd8eacff54653d6af454b497328dc8bab1bf3291a3fb",
                 "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
-        fetch_kib=96395.711, write_kib=188168.320, fetch_scale=2.0, write_scale=1.0),
+        fetch_kib=96394.250, write_kib=188166.664, fetch_scale=2.0, write_scale=1.0),
     # T = 8 verify, B = 512, bare checkpoint (the --mode profile sequence)
     "kda::verify_kernel<true, true, true>": dict(
         sources=("gated_delta_rule_step_amd/csrc/kda_verify.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
-        sha256=("951f9c1628aa4ef54ed7fa7199806b4f8d66caf89035296f88da587354cfc959",
-                "34b8100422cba3857f715dc728116de3c64c225b97154059cd0d5945ac5a48f0",
+        sha256=("fa43b79cc9794d35c8cfcf862aabef1f65bb4d3db80f24eaac8070016e837897",
+                "9263cc848eebfe534d02cd8eacff54653d6af454b497328dc8bab1bf3291a3fb",
                 "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
-        fetch_kib=123927.266, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),
+        fetch_kib=123763.406, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),
 }
 
 

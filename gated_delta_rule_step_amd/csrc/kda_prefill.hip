@@ -189,10 +189,12 @@ __device__ __forceinline__ u32x2 gload4(const uint16_t* p) {
   }
 }
 
+// State rows leave in 32-byte pieces (16 rows per instruction): plain
+// stores, so that L2 merges the pieces of a row into whole lines.
 template <bool VEC>
 __device__ __forceinline__ void gstore4(uint16_t* p, u32x2 w) {
   if constexpr (VEC) {
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+    *reinterpret_cast<u32x2*>(p) = w;
   } else {
     p[0] = uint16_t(w[0] & 0xffffu);
     p[1] = uint16_t(w[0] >> 16);

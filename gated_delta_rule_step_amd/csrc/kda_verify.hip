@@ -386,7 +386,12 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
-        store8_raw<VEC>(ckpt + int64_t(v) * D + k0, w);
+        // A plain (cached) store: one instruction covers 64 of the 128 bytes of
+        // each of 16 checkpoint rows, and the st + 1 store fills the other
+        // half; in L2 the halves merge into whole lines before they reach
+        // memory (non-temporal stores measured 9 % slower at 100 % fold).
+        if constexpr (VEC) *reinterpret_cast<u32x4*>(ckpt + int64_t(v) * D + k0) = w;
+        else store8_raw<VEC>(ckpt + int64_t(v) * D + k0, w);
       }
     }
   }

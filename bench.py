@@ -63,10 +63,10 @@ COUNTED_TRAFFIC = {
         sources=("gated_delta_rule_step_amd/csrc/kda_verify.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
-        sha256=("fa43b79cc9794d35c8cfcf862aabef1f65bb4d3db80f24eaac8070016e837897",
+        sha256=("f6d95bf4a17745085762d0d5d02fd4308b206fda5736651a4546c44cb95dee91",
                 "9263cc848eebfe534d02cd8eacff54653d6af454b497328dc8bab1bf3291a3fb",
                 "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
-        fetch_kib=123763.406, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),
+        fetch_kib=123754.672, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),
 }
 
 

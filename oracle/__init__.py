@@ -16,7 +16,9 @@ cache_base, the state orientation [V][K] and A_log being per head.
 
 gate_mode (every entry): 0 takes raw gate and beta logits; bit GATE_PRECOMPUTED
 takes the log-decay g itself (clamped into [lower_bound, 0]; a_log and dt_bias
-may be None); bit BETA_PRESIGMOID takes beta itself.
+may be None); bit BETA_PRESIGMOID takes beta itself; bit GATE_PER_HEAD takes one
+gate value per token and head (graw [..., H], dt_bias [H]), applied to every key
+channel.
 """
 from __future__ import annotations
 
@@ -100,6 +102,7 @@ def bf16_round_bits(x: np.ndarray) -> np.ndarray:
 
 GATE_PRECOMPUTED = 1  # gate_mode bit: graw holds the log-decay g itself
 BETA_PRESIGMOID = 2   # gate_mode bit: beta_logit holds beta itself
+GATE_PER_HEAD = 4     # gate_mode bit: one gate value (and dt_bias) per head
 
 
 def prologue(q, k, graw, beta_logit, a_log_h, dt_bias_h, lower_bound, real=np.float64,

@@ -101,9 +101,14 @@ Real store(Real x, int bf16_storage) {
 //     bit 0 (pre-computed gate): graw holds the log-decay itself; it is used
 //       clamped into [lower_bound, 0], the range the raw gate lands in
 //       (reading); a_log and dt_bias are not read and may be null;
-//     bit 1 (pre-sigmoided beta): beta_logit holds beta itself.
+//     bit 1 (pre-sigmoided beta): beta_logit holds beta itself;
+//     bit 2 (per-head gate, the scalar decay of GDN, which that page contrasts
+//       with KDA's per-key-channel gate): graw holds one value per head and
+//       dt_bias one per head; the resulting log-decay applies to every key
+//       channel (reading: the same gate formula on the per-head inputs).
 constexpr int kGatePrecomputed = 1;
 constexpr int kBetaPresigmoid = 2;
+constexpr int kGatePerHead = 4;
 
 template <class Real>
 void prologue(int K, const Real* q, const Real* k, const Real* graw, Real beta_logit,
@@ -120,13 +125,16 @@ void prologue(int K, const Real* q, const Real* k, const Real* graw, Real beta_l
     qh[c] = q[c] / nq;
     kh[c] = k[c] / nk;
   }
+  const bool per_head = gate_mode & kGatePerHead;
   if (gate_mode & kGatePrecomputed) {
-    for (int c = 0; c < K; ++c)
-      g[c] = std::min(static_cast<Real>(0), std::max(lower_bound, graw[c]));
+    for (int c = 0; c < K; ++c) {
+      const Real gc = per_head ? graw[0] : graw[c];
+      g[c] = std::min(static_cast<Real>(0), std::max(lower_bound, gc));
+    }
   } else {
     const Real ea = std::exp(a_log);
     for (int c = 0; c < K; ++c) {
-      const Real x = graw[c] + dt_bias[c];
+      const Real x = per_head ? graw[0] + dt_bias[0] : graw[c] + dt_bias[c];
       const Real sp = x > static_cast<Real>(20) ? x : std::log1p(std::exp(x));
       g[c] = std::max(lower_bound, -ea * sp);
     }
@@ -143,8 +151,11 @@ Real alog_of(const Real* a_log, int h, int gate_mode) {
 }
 template <class Real>
 const Real* dtb_of(const Real* dt_bias, int h, int K, int gate_mode) {
-  return (gate_mode & kGatePrecomputed) ? nullptr : dt_bias + static_cast<int64_t>(h) * K;
+  if (gate_mode & kGatePrecomputed) return nullptr;
+  return dt_bias + static_cast<int64_t>(h) * ((gate_mode & kGatePerHead) ? 1 : K);
 }
+// Gate values per token and head: K per-channel values, or one per head.
+inline int gate_width(int K, int gate_mode) { return (gate_mode & kGatePerHead) ? 1 : K; }
 
 // ---------------------------------------------------------------------------
 // One gated delta-rule step for one head, the plain definition, in the order
@@ -208,9 +219,10 @@ void decode(int B, int H, int K, int V, const Real* q, const Real* k, const Real
         continue;
       }
       const int64_t tk = (i64(b) * H + h) * K;
+      const int64_t tg = (i64(b) * H + h) * gate_width(K, gate_mode);
       std::vector<Real> qh(K), kh(K), g(K), S(KV);
       Real beta;
-      prologue<Real>(K, q + tk, k + tk, graw + tk, beta_logit[i64(b) * H + h],
+      prologue<Real>(K, q + tk, k + tk, graw + tg, beta_logit[i64(b) * H + h],
                      alog_of(a_log, h, gate_mode), dtb_of(dt_bias, h, K, gate_mode),
                      lower_bound, gate_mode, qh.data(), kh.data(), g.data(), &beta);
       Real* slot = pool + (i64(idx[b]) * H + h) * KV;
@@ -309,8 +321,9 @@ void verify(int B, int T, int H, int K, int V, const Real* q, const Real* k, con
       for (int t = 0; t < T; ++t) {
         const int64_t tk = ((i64(b) * T + t) * H + h) * K;
         const int64_t tv = ((i64(b) * T + t) * H + h) * V;
+        const int64_t tg = ((i64(b) * T + t) * H + h) * gate_width(K, gate_mode);
         Real beta;
-        prologue<Real>(K, q + tk, k + tk, graw + tk, beta_logit[(i64(b) * T + t) * H + h],
+        prologue<Real>(K, q + tk, k + tk, graw + tg, beta_logit[(i64(b) * T + t) * H + h],
                        alog_of(a_log, h, gate_mode), dtb_of(dt_bias, h, K, gate_mode),
                        lower_bound, gate_mode, qh.data(), kh.data(), g.data(), &beta);
         Real* o = out + tv;
@@ -374,8 +387,9 @@ void prefill_tbt(int n_docs, int H, int K, int V, const int32_t* cu, const Real*
       std::vector<Real> qh(K), kh(K), g(K);
       for (int t = t0; t < t1; ++t) {
         const int64_t tk = (i64(t) * H + h) * K;
+        const int64_t tg = (i64(t) * H + h) * gate_width(K, gate_mode);
         Real beta;
-        prologue<Real>(K, q + tk, k + tk, graw + tk, beta_logit[i64(t) * H + h],
+        prologue<Real>(K, q + tk, k + tk, graw + tg, beta_logit[i64(t) * H + h],
                        alog_of(a_log, h, gate_mode), dtb_of(dt_bias, h, K, gate_mode),
                        lower_bound, gate_mode, qh.data(), kh.data(), g.data(), &beta);
         Real* o = out + (i64(t) * H + h) * V;
@@ -446,7 +460,8 @@ void prefill_chunked(int n_docs, int H, int K, int V, const int32_t* cu, const R
         for (int r = 0; r < n; ++r) {
           const int t = c0 + r;
           const int64_t tk = (i64(t) * H + h) * K;
-          prologue<Real>(K, q + tk, k + tk, graw + tk, beta_logit[i64(t) * H + h],
+          const int64_t tg = (i64(t) * H + h) * gate_width(K, gate_mode);
+          prologue<Real>(K, q + tk, k + tk, graw + tg, beta_logit[i64(t) * H + h],
                          alog_of(a_log, h, gate_mode), dtb_of(dt_bias, h, K, gate_mode),
                          lower_bound, gate_mode, &Q[i64(r) * K], &Kh[i64(r) * K], g.data(),
                          &be[r]);

@@ -774,3 +774,70 @@ def test_prefill_checkpoints_equal_truncated_prefills(orc):
             written[row] = True
     assert written.tolist() == [True] * 6 + [False, True]
     assert np.all(ck[~written] == -7.0)
+
+
+# ---------------------------------------------------------------------------
+# Per-head (scalar) gate: GDN's decay, which [verify] "What it does" contrasts
+# with KDA's per-key-channel gate. Reading: the same gate formula on per-head
+# inputs, applied to every key channel.
+
+PER_HEAD = 4
+
+
+@pytest.mark.parametrize("pre", [0, 1])
+def test_per_head_gate_equals_broadcast_channel_gate(orc, pre):
+    """Decode, verify and prefill with one gate value per head reproduce,
+    bit for bit, the per-channel mode given that value (and dt_bias)
+    repeated over the 128 key channels; raw and pre-computed forms."""
+    rng = _rng(220 + pre)
+    lb = -5.0
+    B, H, N = 3, 2, 4
+    d = _decode_inputs(rng, B, H, N, F64)
+    gh = rng.standard_normal((B, H)) if not pre else rng.uniform(-6, 0.5, (B, H))
+    dth = rng.standard_normal(H) * 0.1
+    g_bc = np.ascontiguousarray(np.repeat(gh[:, :, None], 128, axis=2))
+    dt_bc = np.ascontiguousarray(np.repeat(dth, 128))
+    al, dhd, dbc = (None, None, None) if pre else (d["a_log"], dth, dt_bc)
+    idx = np.array([3, 0, 1], np.int32)
+    p1, p2 = d["pool"].copy(), d["pool"].copy()
+    o1 = orc.decode(d["q"], d["k"], d["v"], np.ascontiguousarray(gh), d["beta_logit"], al, dhd,
+                    lb, 1.0, p1, idx, bf16_storage=False, real=F64, gate_mode=PER_HEAD | pre)
+    o2 = orc.decode(d["q"], d["k"], d["v"], g_bc, d["beta_logit"], al, dbc, lb, 1.0, p2, idx,
+                    bf16_storage=False, real=F64, gate_mode=pre)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(p1, p2)
+    # the per-head decay really is one value across the key channels
+    assert not np.array_equal(p1, d["pool"])
+
+    toks = {n: a.astype(F64) for n, a in _tok(rng, 4, H).items()}
+    gt = rng.standard_normal((1, 4, H)) if not pre else rng.uniform(-6, 0.5, (1, 4, H))
+    gt_bc = np.ascontiguousarray(np.repeat(gt[..., None], 128, axis=3))
+    res = []
+    for gm, gr, db in ((PER_HEAD | pre, np.ascontiguousarray(gt), dhd), (pre, gt_bc, dbc)):
+        pool = d["pool"][:2].copy()
+        kc, uc, gc = (np.zeros((2, H, 32, 128)) for _ in range(3))
+        out = orc.verify(toks["q"], toks["k"], toks["v"], gr, toks["beta_logit"], al, db, lb,
+                         1.0, pool, np.array([1], np.int32), kc, uc, gc,
+                         np.zeros(1, np.int32), np.array([30], np.int32), 5, 16,
+                         bf16_storage=False, real=F64, gate_mode=gm)
+        res.append((out, pool, kc, uc, gc))
+    for a, b in zip(*res):
+        np.testing.assert_array_equal(a, b)
+
+    p = _prefill_inputs(rng, (21, 0, 9), H=2)
+    T = p["q"].shape[0]
+    gp = rng.standard_normal((T, 2)) if not pre else rng.uniform(-6, 0.5, (T, 2))
+    gp_bc = np.ascontiguousarray(np.repeat(gp[..., None], 128, axis=2))
+    outs = []
+    for gm, gr, db in ((PER_HEAD | pre, np.ascontiguousarray(gp), dhd), (pre, gp_bc, dbc)):
+        pool = p["pool"].copy()
+        o = orc.prefill(p["cu"], p["q"], p["k"], p["v"], gr, p["beta_logit"],
+                        None if pre else p["a_log"], db, lb, 1.0, pool, p["idx"],
+                        bf16_storage=False, real=F64, gate_mode=gm)
+        oc = orc.prefill_chunked(p["cu"], p["q"], p["k"], p["v"], gr, p["beta_logit"],
+                                 None if pre else p["a_log"], db, lb, 1.0, p["pool"].copy(),
+                                 p["idx"], 16, real=F64, gate_mode=gm)
+        outs.append((o, pool, oc))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+    np.testing.assert_allclose(outs[0][2], outs[0][0], rtol=1e-10, atol=1e-11)

@@ -28,12 +28,19 @@ bool out_layout_ok(int64_t rows, int64_t toks, int64_t row_stride, int64_t tok_s
 
 kda_status launch_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH; }
 
+// The gate input joins the vectorised-path test only when it is read as
+// 128-channel rows (a per-head gate is one value per token and head).
+bool gate_vec_ok(int32_t gate_mode, const void* g, int64_t s0, int64_t s1) {
+  return (gate_mode & KDA_GATE_PER_HEAD) || (aligned16(g) && mult8(s0) && mult8(s1));
+}
+
 // gate_mode: only the two documented bits; the pre-computed gate clamps into
 // [lower_bound, 0], so lower_bound must be <= 0 (not NaN) there. A_log and
 // dt_bias are read only for raw gate logits.
 kda_status check_gate(int32_t gate_mode, float lower_bound, const float* A_log,
                       const float* dt_bias) {
-  if (gate_mode & ~(KDA_GATE_PRECOMPUTED | KDA_BETA_PRESIGMOID)) return KDA_ERR_UNSUPPORTED;
+  if (gate_mode & ~(KDA_GATE_PRECOMPUTED | KDA_BETA_PRESIGMOID | KDA_GATE_PER_HEAD))
+    return KDA_ERR_UNSUPPORTED;
   if (gate_mode & KDA_GATE_PRECOMPUTED) {
     if (!(lower_bound <= 0.0f)) return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
@@ -106,9 +113,10 @@ extern "C" kda_status kda_decode(int32_t B, int32_t H, int32_t K, int32_t V, con
   p.state_indices = state_indices;
   p.out = static_cast<uint16_t*>(out);
   p.out_row_stride = out_row_stride;
-  const bool vec = aligned16(q) && aligned16(k) && aligned16(g_raw) && aligned16(dt_bias) &&
+  const bool vec = aligned16(q) && aligned16(k) &&
+                   gate_vec_ok(gate_mode, g_raw, g_row_stride, 0) && aligned16(dt_bias) &&
                    (num_slots == 0 || aligned16(state_pool)) && mult8(q_row_stride) &&
-                   mult8(k_row_stride) && mult8(g_row_stride) && mult8(slot_stride);
+                   mult8(k_row_stride) && mult8(slot_stride);
   return launch_status(kda::launch_decode(p, vec, stream));
 }
 
@@ -186,14 +194,14 @@ extern "C" kda_status kda_verify_ucache_flush(
   p.out = static_cast<uint16_t*>(out);
   p.out_row_stride = out_row_stride;
   p.out_tok_stride = out_tok_stride;
-  const bool vec = aligned16(q) && aligned16(k) && aligned16(v) && aligned16(g_raw) &&
+  const bool vec = aligned16(q) && aligned16(k) && aligned16(v) &&
+                   gate_vec_ok(gate_mode, g_raw, g_row_stride, g_tok_stride) &&
                    aligned16(dt_bias) && aligned16(out) &&
                    (num_slots == 0 || (aligned16(state_pool) && aligned16(k_cache) &&
                                        aligned16(u_cache) && aligned16(g_cache))) &&
                    mult8(q_row_stride) && mult8(q_tok_stride) && mult8(k_row_stride) &&
                    mult8(k_tok_stride) && mult8(v_row_stride) && mult8(v_tok_stride) &&
-                   mult8(g_row_stride) && mult8(g_tok_stride) && mult8(out_row_stride) &&
-                   mult8(out_tok_stride) && mult8(slot_stride);
+                   mult8(out_row_stride) && mult8(out_tok_stride) && mult8(slot_stride);
   return launch_status(kda::launch_verify(p, vec, stream));
 }
 
@@ -281,10 +289,10 @@ extern "C" kda_status kda_prefill_varlen(
   p.ckpt_starts = checkpoint_cu_starts;
   p.ckpt_interval = checkpoints ? checkpoint_interval : 16;
   p.workspace = workspace;
-  const bool vec = aligned16(q) && aligned16(k) && aligned16(v) && aligned16(g_raw) &&
-                   aligned16(dt_bias) && aligned16(out) &&
-                   (num_slots == 0 || aligned16(state_pool)) && aligned16(checkpoints) &&
-                   mult8(q_tok_stride) && mult8(k_tok_stride) && mult8(v_tok_stride) &&
-                   mult8(g_tok_stride) && mult8(out_tok_stride) && mult8(slot_stride);
+  const bool vec = aligned16(q) && aligned16(k) && aligned16(v) &&
+                   gate_vec_ok(gate_mode, g_raw, g_tok_stride, 0) && aligned16(dt_bias) &&
+                   aligned16(out) && (num_slots == 0 || aligned16(state_pool)) &&
+                   aligned16(checkpoints) && mult8(q_tok_stride) && mult8(k_tok_stride) &&
+                   mult8(v_tok_stride) && mult8(out_tok_stride) && mult8(slot_stride);
   return launch_status(kda::launch_prefill(p, cu_seqlens_host, vec, stream));
 }

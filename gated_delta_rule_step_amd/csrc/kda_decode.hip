@@ -30,10 +30,13 @@
 
 namespace kda {
 
-// GRAW: raw gate logits (log-decay from A_log, dt_bias, lower_bound); else
-// the gate input is the log-decay itself.
-template <int LOADS, bool VEC, bool GRAW>
+// GK, the gate kind: kGatePrecomputed clear = raw gate logits (log-decay from
+// A_log, dt_bias, lower_bound), set = the log-decay itself; kGatePerHead set =
+// one gate value (and dt_bias) per head for all key channels.
+template <int LOADS, bool VEC, int GK>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+  constexpr bool GRAW = !(GK & kGatePrecomputed);
+  constexpr bool GHEAD = (GK & kGatePerHead) != 0;
   constexpr int ROWS = 4 * LOADS;
   constexpr int VBLOCKS = D / ROWS;
   const int lane = threadIdx.x & 63;
@@ -65,10 +68,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   float q[8], k[8], gr[8], dtb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   load8_bf16<VEC>(p.q + b * p.q_row_stride + h * D + kb * 8, q);
   load8_bf16<VEC>(p.k + b * p.k_row_stride + h * D + kb * 8, k);
-  load8_bf16<VEC>(p.g + b * p.g_row_stride + h * D + kb * 8, gr);
+  if constexpr (GHEAD) {
+    const float gh = bf1(p.g[b * p.g_row_stride + h]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) gr[c] = gh;
+  } else {
+    load8_bf16<VEC>(p.g + b * p.g_row_stride + h * D + kb * 8, gr);
+  }
   float neg_ea = 0.f;
   if constexpr (GRAW) {
-    load8_f32<VEC>(p.dt_bias + h * D + kb * 8, dtb);
+    if constexpr (GHEAD) {
+      const float dh = p.dt_bias[h];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dtb[c] = dh;
+    } else {
+      load8_f32<VEC>(p.dt_bias + h * D + kb * 8, dtb);
+    }
     neg_ea = -expf(p.A_log[h]);
   }
   const float braw = bf1(p.beta[b * p.beta_row_stride + h]);
@@ -145,11 +160,15 @@ hipError_t launch_decode(const DecodeParams& p, bool vec, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
-  const bool graw = !(p.gate_mode & kGatePrecomputed);
-#define KDA_DECODE_LAUNCH(L, V)                                                        \
-  do {                                                                                 \
-    if (graw) hipLaunchKernelGGL((decode_kernel<L, V, true>), grid, block, 0, stream, p); \
-    else hipLaunchKernelGGL((decode_kernel<L, V, false>), grid, block, 0, stream, p);  \
+  const int gk = p.gate_mode & kGateKindMask;
+#define KDA_DECODE_LAUNCH(L, V)                                                              \
+  do {                                                                                       \
+    switch (gk) {                                                                            \
+      case 0: hipLaunchKernelGGL((decode_kernel<L, V, 0>), grid, block, 0, stream, p); break; \
+      case 1: hipLaunchKernelGGL((decode_kernel<L, V, 1>), grid, block, 0, stream, p); break; \
+      case 4: hipLaunchKernelGGL((decode_kernel<L, V, 4>), grid, block, 0, stream, p); break; \
+      default: hipLaunchKernelGGL((decode_kernel<L, V, 5>), grid, block, 0, stream, p);      \
+    }                                                                                        \
   } while (0)
   if (small) {
     if (vec) KDA_DECODE_LAUNCH(2, true);

@@ -11,6 +11,9 @@ namespace kda {
 // input holds beta itself.
 constexpr int32_t kGatePrecomputed = 1;
 constexpr int32_t kBetaPresigmoid = 2;
+constexpr int32_t kGatePerHead = 4;  // one gate value (and dt_bias) per head
+// The kernels are compiled per gate kind: gate_mode & (kGatePrecomputed | kGatePerHead).
+constexpr int32_t kGateKindMask = kGatePrecomputed | kGatePerHead;
 
 // All strides in elements. bf16 tensors are uint16_t bit patterns.
 struct DecodeParams {

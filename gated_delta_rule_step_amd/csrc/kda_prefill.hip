@@ -209,14 +209,19 @@ struct TokRaw {
   uint16_t b;
 };
 
-template <bool VEC>
+template <bool VEC, bool GHEAD>
 __device__ __forceinline__ TokRaw load_tok(const PrefillParams& p, int64_t t, int h, int c0,
                                            bool valid) {
   TokRaw r;
   if (valid) {
     r.q = load8_raw<VEC>(p.q + t * p.q_tok_stride + h * D + c0);
     r.k = load8_raw<VEC>(p.k + t * p.k_tok_stride + h * D + c0);
-    r.g = load8_raw<VEC>(p.g + t * p.g_tok_stride + h * D + c0);
+    if constexpr (GHEAD) {  // one gate value per head, in all eight channel slots
+      const uint32_t gh = p.g[t * p.g_tok_stride + h];
+      r.g = u32x4{gh | (gh << 16), gh | (gh << 16), gh | (gh << 16), gh | (gh << 16)};
+    } else {
+      r.g = load8_raw<VEC>(p.g + t * p.g_tok_stride + h * D + c0);
+    }
     r.v = load8_raw<VEC>(p.v + t * p.v_tok_stride + h * D + c0);
     r.b = p.beta[t * p.beta_tok_stride + h];
   } else {
@@ -259,9 +264,12 @@ __device__ int find_doc(const int32_t* cu, int n_docs, int64_t sigma, int tid) {
 // inputs are loaded while the current head is processed.
 constexpr int kPrepHeads = 4;
 
-// GRAW: raw gate logits; else the gate input is the log-decay itself.
-template <bool VEC, bool GRAW>
+// GK, the gate kind: kGatePrecomputed clear = raw gate logits, set = the
+// log-decay itself; kGatePerHead set = one gate value per head.
+template <bool VEC, int GK>
 __global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillParams p) {
+  constexpr bool GRAW = !(GK & kGatePrecomputed);
+  constexpr bool GHEAD = (GK & kGatePerHead) != 0;
   extern __shared__ __align__(16) float psmem_raw[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -287,18 +295,24 @@ __global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillParams p) {
   const int tt = tid >> 4;        // prologue: token of this lane
   const int c0 = (tid & 15) * 8;  // prologue: 8 key / value channels of this lane
   const bool valid = tt < c;
-  TokRaw raw = load_tok<VEC>(p, tc0 + tt, h0, c0, valid);
+  TokRaw raw = load_tok<VEC, GHEAD>(p, tc0 + tt, h0, c0, valid);
 
   for (int h = h0; h < h1; ++h) {
     // ---- token prologue -> q_hat, k_hat, g, v, beta (rows >= c are zeros)
     {
       const TokRaw cur = raw;
-      if (h + 1 < h1) raw = load_tok<VEC>(p, tc0 + tt, h + 1, c0, valid);
+      if (h + 1 < h1) raw = load_tok<VEC, GHEAD>(p, tc0 + tt, h + 1, c0, valid);
       float neg_ea = 0.f;
       float dtb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       if constexpr (GRAW) {
         neg_ea = -fexp(p.A_log[h]);
-        load8_f32<VEC>(p.dt_bias + h * D + c0, dtb);
+        if constexpr (GHEAD) {
+          const float dh = p.dt_bias[h];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dtb[e] = dh;
+        } else {
+          load8_f32<VEC>(p.dt_bias + h * D + c0, dtb);
+        }
       }
       float q[8], k[8], gr[8];
 #pragma unroll
@@ -708,10 +722,14 @@ hipError_t launch_prefill(const PrefillParams& p, const int32_t* cu_host, bool v
     }
   }
   static const hipError_t attr = [] {
-    const void* fns[] = {reinterpret_cast<const void*>(&prep_kernel<true, true>),
-                         reinterpret_cast<const void*>(&prep_kernel<true, false>),
-                         reinterpret_cast<const void*>(&prep_kernel<false, true>),
-                         reinterpret_cast<const void*>(&prep_kernel<false, false>)};
+    const void* fns[] = {reinterpret_cast<const void*>(&prep_kernel<true, 0>),
+                         reinterpret_cast<const void*>(&prep_kernel<true, 1>),
+                         reinterpret_cast<const void*>(&prep_kernel<true, 4>),
+                         reinterpret_cast<const void*>(&prep_kernel<true, 5>),
+                         reinterpret_cast<const void*>(&prep_kernel<false, 0>),
+                         reinterpret_cast<const void*>(&prep_kernel<false, 1>),
+                         reinterpret_cast<const void*>(&prep_kernel<false, 4>),
+                         reinterpret_cast<const void*>(&prep_kernel<false, 5>)};
     for (const void* f : fns) {
       const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                static_cast<int>(kPrepLds));
@@ -724,14 +742,19 @@ hipError_t launch_prefill(const PrefillParams& p, const int32_t* cu_host, bool v
     dim3 pgrid(static_cast<unsigned>(slots),
                static_cast<unsigned>((p.H + kPrepHeads - 1) / kPrepHeads)),
         block(kThreads);
-    const bool graw = !(p.gate_mode & kGatePrecomputed);
-    if (vec) {
-      if (graw) hipLaunchKernelGGL((prep_kernel<true, true>), pgrid, block, kPrepLds, stream, p);
-      else hipLaunchKernelGGL((prep_kernel<true, false>), pgrid, block, kPrepLds, stream, p);
-    } else {
-      if (graw) hipLaunchKernelGGL((prep_kernel<false, true>), pgrid, block, kPrepLds, stream, p);
-      else hipLaunchKernelGGL((prep_kernel<false, false>), pgrid, block, kPrepLds, stream, p);
-    }
+    const int gk = p.gate_mode & kGateKindMask;
+#define KDA_PREP_LAUNCH(V)                                                                    \
+  do {                                                                                        \
+    switch (gk) {                                                                             \
+      case 0: hipLaunchKernelGGL((prep_kernel<V, 0>), pgrid, block, kPrepLds, stream, p); break; \
+      case 1: hipLaunchKernelGGL((prep_kernel<V, 1>), pgrid, block, kPrepLds, stream, p); break; \
+      case 4: hipLaunchKernelGGL((prep_kernel<V, 4>), pgrid, block, kPrepLds, stream, p); break; \
+      default: hipLaunchKernelGGL((prep_kernel<V, 5>), pgrid, block, kPrepLds, stream, p);      \
+    }                                                                                         \
+  } while (0)
+    if (vec) KDA_PREP_LAUNCH(true);
+    else KDA_PREP_LAUNCH(false);
+#undef KDA_PREP_LAUNCH
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -138,27 +138,42 @@ struct TokRegs {
   uint32_t braw;
 };
 
-template <bool VEC, bool GRAW>
+template <bool VEC, int GK>
 __device__ __forceinline__ void load_tokens(const VerifyParams& p, int64_t item, int tid,
                                             TokRegs& r) {
+  constexpr bool GRAW = !(GK & kGatePrecomputed);
+  constexpr bool GHEAD = (GK & kGatePerHead) != 0;
   const int h = int(item % p.H);
   const int64_t b = item / p.H;
   const int t = tid >> 5, c = 4 * (tid & 31);
   if (t < p.T) {
     r.q = load4_raw<VEC>(p.q + b * p.q_row_stride + t * p.q_tok_stride + h * D + c);
     r.k = load4_raw<VEC>(p.k + b * p.k_row_stride + t * p.k_tok_stride + h * D + c);
-    r.g = load4_raw<VEC>(p.g + b * p.g_row_stride + t * p.g_tok_stride + h * D + c);
+    if constexpr (GHEAD) {  // one gate value per head, in all four channel slots
+      const uint32_t gh = p.g[b * p.g_row_stride + t * p.g_tok_stride + h];
+      r.g = u32x2{gh | (gh << 16), gh | (gh << 16)};
+    } else {
+      r.g = load4_raw<VEC>(p.g + b * p.g_row_stride + t * p.g_tok_stride + h * D + c);
+    }
     r.v = load4_raw<VEC>(p.v + b * p.v_row_stride + t * p.v_tok_stride + h * D + c);
-    if constexpr (GRAW) r.dtb = load4_f32<VEC>(p.dt_bias + h * D + c);
-    else r.dtb = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (!GRAW) {
+      r.dtb = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else if constexpr (GHEAD) {
+      const float dh = p.dt_bias[h];
+      r.dtb = f32x4{dh, dh, dh, dh};
+    } else {
+      r.dtb = load4_f32<VEC>(p.dt_bias + h * D + c);
+    }
     r.braw = p.beta[b * p.beta_row_stride + t * p.beta_tok_stride + h];
   }
 }
 
 // Grid: one 256-thread workgroup per item (row, head), item = row * H + head.
-// GRAW: raw gate logits; else the gate input is the log-decay itself.
-template <bool VEC, bool FACT, bool GRAW>
+// GK, the gate kind: kGatePrecomputed clear = raw gate logits, set = the
+// log-decay itself; kGatePerHead set = one gate value per head.
+template <bool VEC, bool FACT, int GK>
 __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
+  constexpr bool GRAW = !(GK & kGatePrecomputed);
   extern __shared__ __align__(16) float smem_raw[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -187,7 +202,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   // the checkpoint loads (the memory counter is in order: waiting on a load
   // issued after them would also wait for the 32 KiB checkpoint read).
   TokRegs tk;
-  load_tokens<VEC, GRAW>(p, item, tid, tk);
+  load_tokens<VEC, GK>(p, item, tid, tk);
   const bool fold = hist + T >= p.flush_min;
   const int64_t sh = int64_t(slot) * p.H + h;
   uint16_t* ckpt = p.state_pool + int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS;
@@ -614,11 +629,15 @@ hipError_t launch_verify(const VerifyParams& p, bool vec, hipStream_t stream) {
   // exp(Gam_r) * exp(-Gam_j) stays finite when |Gam| <= T * |lower_bound| < 80.
   const bool fact = p.lower_bound > -80.0f / float(p.T) && p.lower_bound <= 0.0f;
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
-  const bool graw = !(p.gate_mode & kGatePrecomputed);
-#define KDA_VERIFY_LAUNCH(V, F)                                                           \
-  do {                                                                                    \
-    if (graw) hipLaunchKernelGGL((verify_kernel<V, F, true>), grid, block, lds, stream, p, hm); \
-    else hipLaunchKernelGGL((verify_kernel<V, F, false>), grid, block, lds, stream, p, hm);   \
+  const int gk = p.gate_mode & kGateKindMask;
+#define KDA_VERIFY_LAUNCH(V, F)                                                                    \
+  do {                                                                                             \
+    switch (gk) {                                                                                  \
+      case 0: hipLaunchKernelGGL((verify_kernel<V, F, 0>), grid, block, lds, stream, p, hm); break; \
+      case 1: hipLaunchKernelGGL((verify_kernel<V, F, 1>), grid, block, lds, stream, p, hm); break; \
+      case 4: hipLaunchKernelGGL((verify_kernel<V, F, 4>), grid, block, lds, stream, p, hm); break; \
+      default: hipLaunchKernelGGL((verify_kernel<V, F, 5>), grid, block, lds, stream, p, hm);      \
+    }                                                                                              \
   } while (0)
   if (vec) {
     if (fact) KDA_VERIFY_LAUNCH(true, true);

@@ -118,6 +118,23 @@ def precomputed_gate(case: dict, gate_mode: int, seed: int) -> dict:
     return c
 
 
+def per_head_gate(case: dict, precomputed: bool, seed: int) -> dict:
+    """A copy of a decode, verify or prefill case with one gate value per token
+    and head (gate_mode bit 4): raw logits N(0, 1) with dt_bias N(0, 0.1) per
+    head, or pre-computed log-decays U(-6, 0.5) (gate_mode bit 1 as well)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    c = dict(case)
+    H = case["H"]
+    shape = case["gate"].shape[:-1] + (H,)
+    if precomputed:
+        c["gate"] = bf16_bits(rng.uniform(-6.0, 0.5, shape).astype(np.float32))
+    else:
+        c["gate"] = _normal_bf16(rng, shape)
+        c["dt_bias"] = (rng.standard_normal(H) * 0.1).astype(np.float32)
+    c["gate_mode"] = case.get("gate_mode", 0) | 4 | (1 if precomputed else 0)
+    return c
+
+
 def decode_case(B: int, N: int = 1024, H: int = 12, seed: int | None = None,
                 inactive_frac: float = 0.05, idx: np.ndarray | None = None) -> dict:
     rng = np.random.Generator(np.random.PCG64(seed_for(1, B) if seed is None else seed))

@@ -27,8 +27,15 @@
  *    min(0, max(lower_bound, g_c)) -- the range the raw gate lands in (a
  *    reading); A_log and dt_bias are not read and may be NULL; lower_bound
  *    must be <= 0 (-INFINITY: no floor), else KDA_ERR_UNSUPPORTED;
- *  - KDA_BETA_PRESIGMOID: beta_raw holds beta itself, used as given.
- * The two bits combine; any other bit gives KDA_ERR_UNSUPPORTED.
+ *  - KDA_BETA_PRESIGMOID: beta_raw holds beta itself, used as given;
+ *  - KDA_GATE_PER_HEAD: the scalar (per-head) decay of GDN, which "feat(kda):
+ *    ReplaySSM verify+flush decode kernel for Kimi K3 (KDA)" ("What it does")
+ *    contrasts with KDA's per-key-channel gate: g_raw holds ONE value per
+ *    token and head, at the offset a beta value has (h, not h*128), and
+ *    dt_bias holds H values; the gate formula above (or the pre-computed
+ *    value) is applied to that value and the result decays every key channel
+ *    of the head (a reading).
+ * The bits combine; any other bit gives KDA_ERR_UNSUPPORTED.
  *
  * Conventions common to every entry point
  *  - Every pointer is a DEVICE pointer, except those whose name ends in _host.
@@ -75,7 +82,8 @@ extern "C" {
 
 enum {
   KDA_GATE_PRECOMPUTED = 1,  /* gate_mode bit: g_raw is the log-decay itself */
-  KDA_BETA_PRESIGMOID = 2    /* gate_mode bit: beta_raw is beta itself */
+  KDA_BETA_PRESIGMOID = 2,   /* gate_mode bit: beta_raw is beta itself */
+  KDA_GATE_PER_HEAD = 4      /* gate_mode bit: one gate value (and dt_bias) per head */
 };
 
 typedef enum {
@@ -110,13 +118,16 @@ const char* kda_status_string(kda_status s);
  *                     k_row_stride, v_row_stride (may be three views into one
  *                     packed [B, 3*H*128] row)
  *  g_raw              bf16 [B, H*128] raw gate logits (or the log-decay, see
- *                     gate_mode), row stride g_row_stride
+ *                     gate_mode; [B, H] with KDA_GATE_PER_HEAD), row stride
+ *                     g_row_stride
  *  beta_raw           bf16 [B, H] beta logits (or beta), row stride beta_row_stride
  *  A_log              fp32 [H] (not read with KDA_GATE_PRECOMPUTED)
- *  dt_bias            fp32 [H*128] (not read with KDA_GATE_PRECOMPUTED)
+ *  dt_bias            fp32 [H*128], or [H] with KDA_GATE_PER_HEAD (not read
+ *                     with KDA_GATE_PRECOMPUTED)
  *  lower_bound        clamp of the log-decay (the pages use -5.0)
  *  scale              read-out scale
- *  gate_mode          0, or KDA_GATE_PRECOMPUTED and/or KDA_BETA_PRESIGMOID
+ *  gate_mode          0, or any of KDA_GATE_PRECOMPUTED, KDA_BETA_PRESIGMOID,
+ *                     KDA_GATE_PER_HEAD
  *  state_pool         bf16 pool, num_slots slots of slot_stride elements
  *                     (may be NULL only when num_slots == 0)
  *  state_indices      int32 [B]: the pool slot of each row

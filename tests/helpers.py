@@ -101,7 +101,8 @@ def oracle_decode(orc, case, pool_bits=None):
     q, k, v = split_qkv(case["qkv"], H)
     gm = case.get("gate_mode", 0)
     a_log, dt_bias = (None, None) if gm & 1 else (case["a_log"], case["dt_bias"])
-    out = orc.decode(q, k, v, np.ascontiguousarray(f32(case["gate"]).reshape(-1, H, HD)),
+    gshape = (-1, H) if gm & 4 else (-1, H, HD)  # per-head gate: one value per head
+    out = orc.decode(q, k, v, np.ascontiguousarray(f32(case["gate"]).reshape(gshape)),
                      np.ascontiguousarray(f32(case["beta"])), a_log, dt_bias,
                      case["lower_bound"], case["scale"], cpool, cidx, bf16_storage=True,
                      real=np.float32, gate_mode=gm)

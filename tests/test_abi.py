@@ -95,13 +95,14 @@ def test_gate_mode_validation(lib):
     assert _decode(lib, alog=0) == NULLP
     assert _decode(lib, dtb=0) == NULLP
     assert _decode(lib, gm=2, alog=0) == NULLP        # pre-sigmoided beta alone: raw gate
-    assert _decode(lib, gm=4) == UNSUP
+    assert _decode(lib, gm=8) == UNSUP
     assert _decode(lib, gm=-1) == UNSUP
     assert _decode(lib, gm=1, lb=0.5) == UNSUP
     assert _decode(lib, gm=1, lb=float("nan")) == UNSUP
     # B = 0: nothing is launched, so the NULL checks pass (unknown bits do not)
     assert _decode(lib, B=0, gm=1, alog=0, dtb=0, lb=float("-inf")) == OK
     assert _decode(lib, B=0, gm=8) == UNSUP
+    assert _decode(lib, gm=4 | 1, lb=0.5) == UNSUP   # per-head pre-computed: same rule
     assert _verify(lib, gm=1, lb=0.25) == UNSUP
     assert _verify(lib, gm=16) == UNSUP
     assert _verify(lib, B=0, gm=3) == OK
@@ -170,7 +171,7 @@ def test_prefill_workspace_and_validation(lib):
     assert call([0, 5], 5, lb=-5.6) == UNSUP
     assert call([0, 5], 5, lb=float("nan")) == UNSUP
     assert call([0], 0) == OK           # no documents: nothing to do
-    assert call([0, 5], 5, gm=4) == UNSUP
+    assert call([0, 5], 5, gm=8) == UNSUP
     # intermediate checkpoints: on chunk boundaries, a row count, a starts array
     q = P(1 << 20)
     assert call([0, 5], 5, ck=q, ck_rows=3, ck_starts=q, ck_int=24) == UNSUP

@@ -70,6 +70,16 @@ def test_precomputed_gate_conventions(orc, gate_mode):
     check_case(orc, case, pool, out)
 
 
+@pytest.mark.parametrize("pre", [False, True])
+def test_per_head_gate(orc, pre):
+    """The per-head (scalar, GDN-style) gate, raw and pre-computed, at B = 512:
+    gate [B, H] and dt_bias [H]."""
+    case = synth.per_head_gate(synth.decode_case(B=512, H=12), pre,
+                               synth.seed_for(1, 512, 120 + int(pre)))
+    pool, out = run_decode(case)
+    check_case(orc, case, pool, out)
+
+
 def test_single_row_slot2_of_4(orc):
     """One row, a 4-slot pool, index 2: slots 0, 1, 3 stay bitwise untouched."""
     case = synth.decode_case(B=1, N=4, H=12, seed=synth.seed_for(0, 1), idx=[2])

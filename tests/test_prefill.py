@@ -62,18 +62,21 @@ def oracle_prefill(orc, case, heads=None, use_initial_state=None, lower_bound=No
     q = f32(case["q"])[:, hs]
     k = f32(case["k"])[:, hs]
     v = f32(case["v"])[:, hs]
-    g = f32(case["gate"]).reshape(Ttot, H, HD)[:, hs]
+    gm = case.get("gate_mode", 0)
+    if gm & 4:  # per-head gate: one value per token and head
+        g = f32(case["gate"]).reshape(Ttot, H)[:, hs]
+    else:
+        g = f32(case["gate"]).reshape(Ttot, H, HD)[:, hs]
     b = f32(case["beta"])[:, hs]
     pool = f32(case["pool"])[:, hs]
     uis = case["use_initial_state"] if use_initial_state is None else use_initial_state
     lb = case["lower_bound"] if lower_bound is None else lower_bound
     c = np.ascontiguousarray
     pool = c(pool)
-    gm = case.get("gate_mode", 0)
     pre = bool(gm & 1)
     out = orc.prefill(case["cu_seqlens"], c(q), c(k), c(v), c(g), c(b),
                       None if pre else c(case["a_log"][hs]),
-                      None if pre else c(case["dt_bias"].reshape(H, HD)[hs]), lb,
+                      None if pre else c(case["dt_bias"].reshape(H, -1)[hs]), lb,
                       case["scale"], pool, case["idx"], use_initial_state=uis,
                       bf16_storage=True, real=np.float32, gate_mode=gm, checkpoints=ckpt,
                       checkpoint_starts=ckpt_starts, checkpoint_interval=ckpt_interval)
@@ -176,6 +179,15 @@ def test_precomputed_gate_conventions(orc, gate_mode):
     """The pre-computed gate and / or beta convention over ragged documents."""
     case = synth.prefill_case(SMALL_DOCS, H=3, seed=synth.seed_for(4, 3, 12))
     case = synth.precomputed_gate(case, gate_mode, synth.seed_for(4, 3, 100 + gate_mode))
+    pool, out = run_prefill(case)
+    check_prefill(orc, case, pool, out)
+
+
+@pytest.mark.parametrize("pre", [False, True])
+def test_per_head_gate(orc, pre):
+    """The per-head (scalar) gate, raw and pre-computed, over ragged documents."""
+    case = synth.prefill_case(SMALL_DOCS, H=3, seed=synth.seed_for(4, 3, 13))
+    case = synth.per_head_gate(case, pre, synth.seed_for(4, 3, 120 + int(pre)))
     pool, out = run_prefill(case)
     check_prefill(orc, case, pool, out)
 

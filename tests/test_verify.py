@@ -27,7 +27,10 @@ def _kda():
 
 def _tok_arrays(qkv, gate, beta, H):
     q, k, v = split_qkv(qkv, H)
-    g = np.ascontiguousarray(f32(gate).reshape(*gate.shape[:-1], H, HD))
+    if gate.shape[-1] == H:  # per-head gate: one value per token and head
+        g = np.ascontiguousarray(f32(gate))
+    else:
+        g = np.ascontiguousarray(f32(gate).reshape(*gate.shape[:-1], H, HD))
     return q, k, v, g, np.ascontiguousarray(f32(beta))
 
 
@@ -197,6 +200,16 @@ def test_precomputed_gate_conventions(orc, T, fm, p, gate_mode):
     under the raw convention, as a caller switching conventions would see)."""
     case = build_case(orc, 512, T, w_ring=16, flush_min=fm, fold_p=p)
     case = synth.precomputed_gate(case, gate_mode, synth.seed_for(3, 512, 100 + gate_mode))
+    verify_roundtrip(orc, case)
+
+
+@pytest.mark.parametrize("pre", [False, True])
+def test_per_head_gate(orc, pre):
+    """The per-head (scalar) gate on the draft tokens, raw and pre-computed, with
+    ring history and folding rows, B = 512; the history was written under the
+    per-channel gate (the ring keeps only cumulative G rows)."""
+    case = build_case(orc, 512, 8, w_ring=16, flush_min=9, fold_p=0.5)
+    case = synth.per_head_gate(case, pre, synth.seed_for(3, 512, 120 + int(pre)))
     verify_roundtrip(orc, case)
 
 

@@ -192,7 +192,9 @@ class DecodeSetup:
         self.combos = []
         for j in range(4):
             c = synth.decode_case(B=B, N=1, H=H, seed=synth.seed_for(1, B) + j)
-            if gate_mode:
+            if gate_mode & 4:
+                c = synth.per_head_gate(c, bool(gate_mode & 1), synth.seed_for(1, B, 120) + j)
+            elif gate_mode:
                 c = synth.precomputed_gate(c, gate_mode, synth.seed_for(1, B, 100) + j)
             qkv = bf16_dev(torch, c["qkv"])
             self.combos.append(dict(
@@ -231,7 +233,9 @@ class VerifySetup:
             c = synth.verify_case(B=B, T=T, N=1, H=H, w_ring=w_ring, flush_min=flush_min,
                                   fold_p=fold_p, hist_max=hist_max,
                                   seed=synth.seed_for(3, B, T) + j)
-            if gate_mode:
+            if gate_mode & 4:
+                c = synth.per_head_gate(c, bool(gate_mode & 1), synth.seed_for(3, B, 120 + T) + j)
+            elif gate_mode:
                 c = synth.precomputed_gate(c, gate_mode, synth.seed_for(3, B, 100 + T) + j)
             self.flush_min = c["flush_min"]
             if j == 0:
@@ -294,6 +298,9 @@ class PrefillSetup:
             self.g = (u * 6.5 - 6.0).to(torch.bfloat16)
         if gate_mode & 2:  # beta itself, U(0, 1)
             self.beta = torch.rand(T, H, generator=gen, device="cuda").to(torch.bfloat16)
+        if gate_mode & 4:  # one gate value per token and head
+            self.g = randn(T, H)
+            self.dtb = torch.randn(H, generator=gen, device="cuda") * 0.1
         self.a_log = torch.rand(H, generator=gen, device="cuda") * 2.0 - 1.0
         self.dtb = torch.randn(H * 128, generator=gen, device="cuda") * 0.1
         N = 2 * n_docs
@@ -444,15 +451,16 @@ def main():
             log(f"bench: {points[-1]}")
         points.append(dict(kind="decode", B=B, T=1, us_per_call=round(us_ev, 3),
                            GBps=round(gbs, 1), hbm_frac=round(gbs / wm.HBM_PEAK_GBS, 4)))
-        # the pre-computed gate and beta convention at the headline size
-        sp = DecodeSetup(B, torch, kda, synth, pools, gate_mode=3)
-        _, e = time_graphs(sp.calls(), args.steps, args.warmup, torch, min_warm_s=0.3)
-        us = e * 1e3 / args.steps
-        nb = wm.decode_bytes(sp.n_active, B - sp.n_active)
-        points.append(dict(kind="decode", B=B, T=1, gate="pre-computed g and beta",
-                           us_per_call=round(us, 3), GBps=round(nb / (us * 1e-6) / 1e9, 1),
-                           hbm_frac=round(nb / (us * 1e-6) / 1e9 / wm.HBM_PEAK_GBS, 4)))
-        log(f"bench: {points[-1]}")
+        # the other gate conventions at the headline size
+        for gm, gname in ((3, "pre-computed g and beta"), (4, "per-head gate (GDN-style)")):
+            sp = DecodeSetup(B, torch, kda, synth, pools, gate_mode=gm)
+            _, e = time_graphs(sp.calls(), args.steps, args.warmup, torch, min_warm_s=0.3)
+            us = e * 1e3 / args.steps
+            nb = wm.decode_bytes(sp.n_active, B - sp.n_active)
+            points.append(dict(kind="decode", B=B, T=1, gate=gname,
+                               us_per_call=round(us, 3), GBps=round(nb / (us * 1e-6) / 1e9, 1),
+                               hbm_frac=round(nb / (us * 1e-6) / 1e9 / wm.HBM_PEAK_GBS, 4)))
+            log(f"bench: {points[-1]}")
         rings = make_rings(torch, synth)
         vcfgs = [
             dict(label="T=8 bare (0% fold)", T=8, hist_max=0),
@@ -462,6 +470,7 @@ def main():
             dict(label="T=4 fm=13 100% fold", T=4, fold_p=1.0),
             dict(label="T=8 W32 fm=25 hist~U{0..24}", T=8, w_ring=32, flush_min=25, hist_max=24),
             dict(label="T=8 bare, pre-computed gate and beta", T=8, hist_max=0, gate_mode=3),
+            dict(label="T=8 fm=9 50% fold, per-head gate", T=8, fold_p=0.5, gate_mode=4),
         ]
         for Bv in (1, 32, 512):
             for cfg in vcfgs:
@@ -493,6 +502,7 @@ def main():
                                     ("14-doc mix, 16384 tokens", synth.DOCS_14))
                  for Hp in (64, 12)]
         pcfgs.append(("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4, 12, 3, 0))
+        pcfgs.append(("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4, 12, 4, 0))
         pcfgs.append(("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4, 12, 0, 64))
         for name, lens, Hp, gm, cki in pcfgs:
             ps = PrefillSetup(lens, Hp, torch, kda, synth, gate_mode=gm, ckpt_interval=cki)
@@ -502,7 +512,8 @@ def main():
             # each checkpoint row writes H bf16 states
             nb = wm.prefill_bytes(lens, Hp) + ps.ck_rows * Hp * 128 * 128 * 2
             fl = wm.prefill_flops(lens, Hp)
-            extra = {"gate": "pre-computed g and beta"} if gm else {}
+            extra = {"gate": {3: "pre-computed g and beta", 4: "per-head gate (GDN-style)"}[gm]} \
+                if gm else {}
             if cki:
                 extra["checkpoints"] = f"every {cki} tokens ({ps.ck_rows} rows)"
             points.append(dict(kind="prefill", H=Hp, docs=name, tokens=int(sum(lens)),

@@ -19,6 +19,11 @@ takes the log-decay g itself (clamped into [lower_bound, 0]; a_log and dt_bias
 may be None); bit BETA_PRESIGMOID takes beta itself; bit GATE_PER_HEAD takes one
 gate value per token and head (graw [..., H], dt_bias [H]), applied to every key
 channel.
+
+state_dtype (decode, verify, prefill): 0 stores the state (pool write-back, fold
+checkpoint, prefill final and intermediate states) in bf16, 1 in fp16 (round to
+nearest even, written from the binary16 definition); outputs and ring rows stay
+bf16. Pool inputs are passed as their exact values either way.
 """
 from __future__ import annotations
 
@@ -91,6 +96,24 @@ def set_threads(n: int) -> None:
     lib().orc_set_threads(int(n))
 
 
+def f16_round_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> fp16 bits, round-to-nearest-even (uint16 array of x's shape)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().orc_f16_round(ctypes.c_int64(x.size), x.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                        out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)))
+    return out
+
+
+def f16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """fp16 bits -> fp32 values (exact)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float32)
+    lib().orc_f16_to_float(ctypes.c_int64(b.size), b.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                           out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    return out
+
+
 def bf16_round_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bits, round-to-nearest-even (uint16 array of x's shape)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
@@ -141,7 +164,7 @@ def replay(ckpt, kc, uc, gc, base, hist, real=np.float64):
 
 
 def decode(q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,
-           bf16_storage=True, real=np.float32, gate_mode=0):
+           bf16_storage=True, real=np.float32, gate_mode=0, state_dtype=0):
     """T=1 decode. q/k/graw [B,H,K], v [B,H,V], beta_logit [B,H], pool [N,H,V,K]
     (updated in place), idx int32 [B]. Returns out [B,H,V]."""
     B, H, K = q.shape
@@ -152,13 +175,14 @@ def decode(q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, 
     f(B, H, K, V, _rp(q, real), _rp(k, real), _rp(v, real), _rp(graw, real),
       _rp(beta_logit, real), _rp(a_log, real), _rp(dt_bias, real), _rs(lower_bound, real),
       _rs(scale, real), _rp(pool, real), ctypes.c_int64(N), _ip(idx), _rp(out, real),
-      ctypes.c_int(1 if bf16_storage else 0), ctypes.c_int(gate_mode))
+      ctypes.c_int(1 if bf16_storage else 0), ctypes.c_int(gate_mode),
+      ctypes.c_int(1 if state_dtype == 1 else 0))
     return out
 
 
 def verify(q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,
            k_cache, u_cache, g_cache, hist_len, cache_base, flush_min, w_ring,
-           bf16_storage=True, real=np.float32, gate_mode=0):
+           bf16_storage=True, real=np.float32, gate_mode=0, state_dtype=0):
     """Verify+fold. q/k/graw [B,T,H,K], v [B,T,H,V], beta_logit [B,T,H]; pool [N,H,V,K],
     k_cache/g_cache [N,H,R,K], u_cache [N,H,R,V] all updated in place. Returns out [B,T,H,V]."""
     B, T, H, K = q.shape
@@ -172,7 +196,8 @@ def verify(q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, 
       _rs(scale, real), _rp(pool, real), ctypes.c_int64(N), _ip(idx), _rp(k_cache, real),
       _rp(u_cache, real), _rp(g_cache, real), ctypes.c_int(R), _ip(hist_len), _ip(cache_base),
       ctypes.c_int(flush_min), ctypes.c_int(w_ring), _rp(out, real),
-      ctypes.c_int(1 if bf16_storage else 0), ctypes.c_int(gate_mode))
+      ctypes.c_int(1 if bf16_storage else 0), ctypes.c_int(gate_mode),
+      ctypes.c_int(1 if state_dtype == 1 else 0))
     return out
 
 
@@ -190,7 +215,7 @@ def _prefill_args(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, sc
 
 def prefill(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,
             use_initial_state=True, bf16_storage=True, real=np.float32, gate_mode=0,
-            checkpoints=None, checkpoint_starts=None, checkpoint_interval=16):
+            checkpoints=None, checkpoint_starts=None, checkpoint_interval=16, state_dtype=0):
     """Token-by-token varlen prefill. q/k/graw [Ttot,H,K], v [Ttot,H,V], beta_logit [Ttot,H],
     cu int32 [n_docs+1], idx int32 [n_docs], pool [N,H,V,K] updated in place. -> out [Ttot,H,V].
     checkpoints [rows,H,V,K] (updated in place) with checkpoint_starts int64 [n_docs]: the
@@ -206,7 +231,7 @@ def prefill(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, p
     f(*_prefill_args(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool,
                      idx, use_initial_state, out, real), ctypes.c_int(1 if bf16_storage else 0),
       ctypes.c_int(gate_mode), ck, ctypes.c_int64(rows), starts,
-      ctypes.c_int(int(checkpoint_interval)))
+      ctypes.c_int(int(checkpoint_interval)), ctypes.c_int(1 if state_dtype == 1 else 0))
     return out
 
 

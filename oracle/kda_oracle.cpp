@@ -80,6 +80,70 @@ Real store(Real x, int bf16_storage) {
 }
 
 // ---------------------------------------------------------------------------
+// binary16 (fp16) round-to-nearest-even from binary32, for the fp16 state
+// option (the pages' GDN kernel offers "an optional fp16 checkpoint-state
+// mode"; "feat(kda): ReplaySSM verify+flush decode kernel for Kimi K3 (KDA)",
+// "Caching"). Written from the IEEE-754 binary16 format: 1 sign, 5 exponent
+// (bias 15) and 10 fraction bits; values from 65520 up overflow to infinity;
+// below 2^-14 the result is a subnormal m * 2^-24; ties go to the even result.
+uint16_t f16_rne_bits(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return static_cast<uint16_t>(sign | 0x7e00u | ((a >> 13) & 0x3ffu));
+  if (a >= 0x477ff000u) return static_cast<uint16_t>(sign | 0x7c00u);  // 65520 and up: inf
+  uint32_t r;
+  if (a >= 0x38800000u) {  // normal binary16
+    const uint32_t e = (a >> 23) - 127 + 15;
+    const uint32_t m = a & 0x7fffffu;
+    r = (e << 10) | (m >> 13);
+    const uint32_t rem = m & 0x1fffu;
+    if (rem > 0x1000u || (rem == 0x1000u && (r & 1u))) r += 1;  // may carry into the exponent
+  } else {
+    const uint32_t e = a >> 23;
+    if (e == 0) return static_cast<uint16_t>(sign);  // binary32 subnormal: far below 2^-25
+    const uint32_t m = (a & 0x7fffffu) | 0x800000u;  // value = m * 2^(e - 150)
+    const uint32_t shift = 126 - e;                  // value * 2^24 = m >> shift
+    if (shift > 24) return static_cast<uint16_t>(sign);  // below 2^-25: rounds to zero
+    r = m >> shift;
+    const uint32_t rem = m & ((1u << shift) - 1u), half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (r & 1u))) r += 1;  // 1024 is the smallest normal
+  }
+  return static_cast<uint16_t>(sign | r);
+}
+
+float f16_bits_to_float(uint16_t b) {
+  const uint32_t sign = static_cast<uint32_t>(b & 0x8000u) << 16;
+  const uint32_t e = (b >> 10) & 0x1fu, m = b & 0x3ffu;
+  float f;
+  if (e == 0) {
+    f = std::ldexp(static_cast<float>(m), -24);
+  } else if (e == 31) {
+    const uint32_t u = 0x7f800000u | (m << 13);
+    std::memcpy(&f, &u, 4);
+  } else {
+    const uint32_t u = ((e - 15 + 127) << 23) | (m << 13);
+    std::memcpy(&f, &u, 4);
+  }
+  uint32_t v;
+  std::memcpy(&v, &f, 4);
+  v |= sign;
+  std::memcpy(&f, &v, 4);
+  return f;
+}
+
+// State storage points (pool write-back, fold checkpoint, prefill final and
+// intermediate states): bf16, or fp16 when state_fp16 is set.
+template <class Real>
+Real store_state(Real x, int bf16_storage, int state_fp16) {
+  if (!bf16_storage) return x;
+  if (state_fp16)
+    return static_cast<Real>(f16_bits_to_float(f16_rne_bits(static_cast<float>(x))));
+  return to_bf16(x);
+}
+
+// ---------------------------------------------------------------------------
 // Per-token prologue for one head.
 //
 // * L2 normalisation of q and k over the K key channels, in the working
@@ -208,7 +272,7 @@ template <class Real>
 void decode(int B, int H, int K, int V, const Real* q, const Real* k, const Real* v,
             const Real* graw, const Real* beta_logit, const Real* a_log, const Real* dt_bias,
             Real lower_bound, Real scale, Real* pool, int64_t N, const int32_t* idx,
-            Real* out, int bf16_storage, int gate_mode) {
+            Real* out, int bf16_storage, int gate_mode, int state_fp16) {
   const int64_t KV = i64(K) * V;
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int b = 0; b < B; ++b) {
@@ -229,7 +293,7 @@ void decode(int B, int H, int K, int V, const Real* q, const Real* k, const Real
       std::copy(slot, slot + KV, S.begin());
       step<Real>(K, V, S.data(), qh.data(), kh.data(), v + (i64(b) * H + h) * V, g.data(),
                  beta, scale, o, nullptr);
-      for (int64_t e = 0; e < KV; ++e) slot[e] = store(S[e], bf16_storage);
+      for (int64_t e = 0; e < KV; ++e) slot[e] = store_state(S[e], bf16_storage, state_fp16);
       for (int r = 0; r < V; ++r) o[r] = store(o[r], bf16_storage);
     }
   }
@@ -290,7 +354,8 @@ void verify(int B, int T, int H, int K, int V, const Real* q, const Real* k, con
             const Real* graw, const Real* beta_logit, const Real* a_log, const Real* dt_bias,
             Real lower_bound, Real scale, Real* pool, int64_t N, const int32_t* idx, Real* kc,
             Real* uc, Real* gc, int R, const int32_t* hist_len, const int32_t* cache_base,
-            int flush_min, int w_ring, Real* out, int bf16_storage, int gate_mode) {
+            int flush_min, int w_ring, Real* out, int bf16_storage, int gate_mode,
+            int state_fp16) {
   const int64_t KV = i64(K) * V;
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int b = 0; b < B; ++b) {
@@ -339,7 +404,7 @@ void verify(int B, int T, int H, int K, int V, const Real* q, const Real* k, con
         for (int r = 0; r < V; ++r) ucs[row * V + r] = store(u[r], bf16_storage);
       }
       if (fold)
-        for (int64_t e = 0; e < KV; ++e) ckpt[e] = store(Scur[e], bf16_storage);
+        for (int64_t e = 0; e < KV; ++e) ckpt[e] = store_state(Scur[e], bf16_storage, state_fp16);
     }
   }
 }
@@ -369,7 +434,7 @@ void prefill_tbt(int n_docs, int H, int K, int V, const int32_t* cu, const Real*
                  const Real* a_log, const Real* dt_bias, Real lower_bound, Real scale,
                  Real* pool, int64_t N, const int32_t* idx, int use_initial_state, Real* out,
                  int bf16_storage, int gate_mode, Real* ckpt, int64_t ckpt_rows,
-                 const int64_t* ckpt_starts, int interval) {
+                 const int64_t* ckpt_starts, int interval, int state_fp16) {
   const int64_t KV = i64(K) * V;
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int d = 0; d < n_docs; ++d) {
@@ -401,11 +466,11 @@ void prefill_tbt(int n_docs, int H, int K, int V, const int32_t* cu, const Real*
           const int64_t row = ckpt_starts[d] + done / interval - 1;
           if (row >= 0 && row < ckpt_rows) {
             Real* c = ckpt + (row * H + h) * KV;
-            for (int64_t e = 0; e < KV; ++e) c[e] = store(S[e], bf16_storage);
+            for (int64_t e = 0; e < KV; ++e) c[e] = store_state(S[e], bf16_storage, state_fp16);
           }
         }
       }
-      for (int64_t e = 0; e < KV; ++e) slot[e] = store(S[e], bf16_storage);
+      for (int64_t e = 0; e < KV; ++e) slot[e] = store_state(S[e], bf16_storage, state_fp16);
     }
   }
 }
@@ -554,19 +619,21 @@ void prefill_chunked(int n_docs, int H, int K, int V, const int32_t* cu, const R
                                    const Real* v, const Real* graw, const Real* beta_logit,   \
                                    const Real* a_log, const Real* dt_bias, Real lower_bound,  \
                                    Real scale, Real* pool, int64_t N, const int32_t* idx,     \
-                                   Real* out, int bf16_storage, int gate_mode) {              \
+                                   Real* out, int bf16_storage, int gate_mode,                \
+                                   int state_fp16) {                                          \
     decode<Real>(B, H, K, V, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale,   \
-                 pool, N, idx, out, bf16_storage, gate_mode);                                 \
+                 pool, N, idx, out, bf16_storage, gate_mode, state_fp16);                     \
   }                                                                                           \
   extern "C" void orc_verify_##SUF(                                                           \
       int B, int T, int H, int K, int V, const Real* q, const Real* k, const Real* v,         \
       const Real* graw, const Real* beta_logit, const Real* a_log, const Real* dt_bias,       \
       Real lower_bound, Real scale, Real* pool, int64_t N, const int32_t* idx, Real* kc,      \
       Real* uc, Real* gc, int R, const int32_t* hist_len, const int32_t* cache_base,          \
-      int flush_min, int w_ring, Real* out, int bf16_storage, int gate_mode) {                \
+      int flush_min, int w_ring, Real* out, int bf16_storage, int gate_mode,                  \
+      int state_fp16) {                                                                       \
     verify<Real>(B, T, H, K, V, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound,       \
                  scale, pool, N, idx, kc, uc, gc, R, hist_len, cache_base, flush_min, w_ring, \
-                 out, bf16_storage, gate_mode);                                               \
+                 out, bf16_storage, gate_mode, state_fp16);                                   \
   }                                                                                           \
   extern "C" void orc_prefill_tbt_##SUF(                                                      \
       int n_docs, int H, int K, int V, const int32_t* cu, const Real* q, const Real* k,       \
@@ -574,10 +641,10 @@ void prefill_chunked(int n_docs, int H, int K, int V, const int32_t* cu, const R
       const Real* dt_bias, Real lower_bound, Real scale, Real* pool, int64_t N,               \
       const int32_t* idx, int use_initial_state, Real* out, int bf16_storage,                 \
       int gate_mode, Real* ckpt, int64_t ckpt_rows, const int64_t* ckpt_starts,               \
-      int interval) {                                                                         \
+      int interval, int state_fp16) {                                                         \
     prefill_tbt<Real>(n_docs, H, K, V, cu, q, k, v, graw, beta_logit, a_log, dt_bias,         \
                       lower_bound, scale, pool, N, idx, use_initial_state, out, bf16_storage, \
-                      gate_mode, ckpt, ckpt_rows, ckpt_starts, interval);                     \
+                      gate_mode, ckpt, ckpt_rows, ckpt_starts, interval, state_fp16);         \
   }                                                                                           \
   extern "C" void orc_prefill_chunked_##SUF(                                                  \
       int n_docs, int H, int K, int V, const int32_t* cu, const Real* q, const Real* k,       \
@@ -594,6 +661,14 @@ ORC_INSTANTIATE(f64, double)
 
 extern "C" void orc_bf16_round(int64_t n, const float* in, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = bf16_rne_bits(in[i]);
+}
+
+extern "C" void orc_f16_round(int64_t n, const float* in, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f16_rne_bits(in[i]);
+}
+
+extern "C" void orc_f16_to_float(int64_t n, const uint16_t* in, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f16_bits_to_float(in[i]);
 }
 
 extern "C" int orc_max_threads() {

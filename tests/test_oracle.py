@@ -841,3 +841,97 @@ def test_per_head_gate_equals_broadcast_channel_gate(orc, pre):
     np.testing.assert_array_equal(outs[0][0], outs[1][0])
     np.testing.assert_array_equal(outs[0][1], outs[1][1])
     np.testing.assert_allclose(outs[0][2], outs[0][0], rtol=1e-10, atol=1e-11)
+
+
+# ---------------------------------------------------------------------------
+# fp16 state option ([verify] "Caching": the GDN kernel offers an fp16
+# checkpoint-state mode). The rounding is written from the binary16 format;
+# torch's float32 -> float16 cast is the independent reference.
+
+def test_f16_rne_matches_torch(orc):
+    rng = _rng(230)
+    bits = rng.integers(0, 2 ** 32, 4_000_000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[~np.isnan(x)]
+    # every class near the binary16 range: ties, subnormals, overflow edge
+    special = []
+    for e in range(-26, 17):
+        base = np.float32(2.0 ** e)
+        for k in range(0, 1 << 11, 37):
+            m = np.float32(1 + k / 2048.0)
+            special.append(base * m)
+            special.append(base * (m + np.float32(2.0 ** -11)))  # exact binary16 ties
+    special += [65504.0, 65519.996, 65520.0, 65536.0, 2.0 ** -24, 2.0 ** -25, 2.0 ** -25 * 1.5,
+                6.0e-8, 5.96e-8, 0.0, -0.0, np.inf, -np.inf]
+    sp = np.array(special, np.float32)
+    x = np.concatenate([x, sp, -sp])
+    ours = orc.f16_round_bits(x)
+    ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    # and back: fp16 bits -> fp32 is exact (torch's widening)
+    allb = np.arange(65536, dtype=np.uint16)
+    allb = allb[(allb & 0x7c00) != 0x7c00]  # finite encodings
+    back = orc.f16_bits_to_f32(allb)
+    np.testing.assert_array_equal(back, torch.from_numpy(allb.view(np.int16)).view(
+        torch.float16).to(torch.float32).numpy())
+
+
+def _f16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float16).to(
+        torch.float32).numpy()
+
+
+def test_fp16_state_rounds_only_the_state_storage_points(orc):
+    """Decode, verify (fold) and prefill with fp16 state equal the same run
+    without state rounding followed by torch's fp16 cast of the stored states;
+    outputs keep their bf16 rounding."""
+    rng = _rng(231)
+    B, H, N = 3, 2, 4
+    d = _decode_inputs(rng, B, H, N, F32)
+    d["pool"] = _f16(d["pool"])
+    idx = np.array([3, 0, 1], np.int32)
+    pa, pb = d["pool"].copy(), d["pool"].copy()
+    args = (d["q"], d["k"], d["v"], d["graw"], d["beta_logit"], d["a_log"], d["dt_bias"], -5.0,
+            1.0)
+    oa = orc.decode(*args, pa, idx, bf16_storage=True, real=F32, state_dtype=1)
+    ob = orc.decode(*args, pb, idx, bf16_storage=False, real=F32)
+    np.testing.assert_array_equal(pa[idx], _f16(pb[idx]))
+    np.testing.assert_array_equal(oa, synth.f32_from_bits(synth.bf16_bits(ob)))
+    assert not np.array_equal(pa[idx], synth.f32_from_bits(synth.bf16_bits(pb[idx])))
+
+    toks = {n: synth.f32_from_bits(synth.bf16_bits(a)) for n, a in _tok(rng, 4, H).items()}
+    R = 32
+    res = []
+    for st, bf in ((1, True), (0, False)):
+        pool = d["pool"][:2].copy()
+        kc = np.zeros((2, H, R, 128), np.float32)
+        uc = np.zeros_like(kc)
+        gc = np.zeros_like(kc)
+        # three history rows written by an earlier call, then a folding call
+        h0 = {n: a[:, :3].copy() for n, a in toks.items()}
+        orc.verify(h0["q"], h0["k"], h0["v"], h0["graw"], h0["beta_logit"], d["a_log"],
+                   d["dt_bias"], -5.0, 1.0, pool, np.array([1], np.int32), kc, uc, gc,
+                   np.zeros(1, np.int32), np.array([30], np.int32), 10, 16,
+                   bf16_storage=True, real=F32, state_dtype=st)
+        h1 = {n: a[:, 3:].copy() for n, a in toks.items()}
+        out = orc.verify(h1["q"], h1["k"], h1["v"], h1["graw"], h1["beta_logit"], d["a_log"],
+                         d["dt_bias"], -5.0, 1.0, pool, np.array([1], np.int32), kc, uc, gc,
+                         np.array([3], np.int32), np.array([30], np.int32), 4, 16,
+                         bf16_storage=bf, real=F32, state_dtype=st)
+        res.append((out, pool))
+    np.testing.assert_array_equal(res[0][1][1], _f16(res[1][1][1]))  # the folded checkpoint
+
+    p = _prefill_inputs(rng, (21, 0, 40), H=2, real=F32)
+    for n in ("q", "k", "v", "graw", "beta_logit"):
+        p[n] = synth.f32_from_bits(synth.bf16_bits(p[n]))
+    p["pool"] = _f16(p["pool"])
+    ck_a = np.zeros((3, 2, 128, 128), np.float32)
+    ck_b = np.zeros_like(ck_a)
+    starts = np.array([0, 1, 1], np.int64)
+    qa, qb = p["pool"].copy(), p["pool"].copy()
+    orc.prefill(*_pf_args(p), qa, p["idx"], real=F32, state_dtype=1, checkpoints=ck_a,
+                checkpoint_starts=starts, checkpoint_interval=16)
+    orc.prefill(*_pf_args(p), qb, p["idx"], bf16_storage=False, real=F32, checkpoints=ck_b,
+                checkpoint_starts=starts, checkpoint_interval=16)
+    np.testing.assert_array_equal(qa[p["idx"]], _f16(qb[p["idx"]]))
+    np.testing.assert_array_equal(ck_a, _f16(ck_b))

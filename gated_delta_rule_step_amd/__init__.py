@@ -30,17 +30,17 @@ _SIGS = {
     "kda_status_string": (_c.c_char_p, [_c.c_int]),
     "kda_decode": (_c.c_int, [_I32, _I32, _I32, _I32,
                               _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
-                              _P, _P, _F, _F, _I32, _P, _I64, _I64, _P, _P, _I64, _P]),
+                              _P, _P, _F, _F, _I32, _I32, _P, _I64, _I64, _P, _P, _I64, _P]),
     "kda_verify_ucache_flush": (_c.c_int, [_I32, _I32, _I32, _I32, _I32,
                                            _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
                                            _P, _I64, _I64, _P, _I64, _I64,
-                                           _P, _P, _F, _F, _I32, _P, _I64, _I64, _P,
+                                           _P, _P, _F, _F, _I32, _I32, _P, _I64, _I64, _P,
                                            _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32,
                                            _P, _I64, _I64, _P]),
     "kda_prefill_workspace_size": (_c.c_size_t, [_I32, _I64, _I32, _I32, _I32]),
     "kda_prefill_varlen": (_c.c_int, [_I32, _I64, _I32, _I32, _I32, _P, _P,
                                       _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
-                                      _P, _P, _F, _F, _I32, _P, _I64, _I64, _P, _I32,
+                                      _P, _P, _F, _F, _I32, _I32, _P, _I64, _I64, _P, _I32,
                                       _P, _I64, _P, _I64, _P, _I32, _P, _c.c_size_t, _P]),
 }
 
@@ -117,10 +117,20 @@ def _i32(name, t):
         raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
 
 
-def _pool_geometry(state_pool, H):
-    """Pool: bf16 tensor whose dim 0 indexes slots; each slot's first
-    H*128*128 elements are contiguous. Returns (num_slots, slot_stride)."""
+def _state_dtype(state_pool) -> int:
+    """KDA_STATE_BF16 (0) or KDA_STATE_FP16 (1), from the pool tensor's dtype."""
+    import torch
+    if state_pool.dtype == torch.float16:
+        return 1
     _bf16("state_pool", state_pool)
+    return 0
+
+
+def _pool_geometry(state_pool, H):
+    """Pool: bf16 or fp16 tensor whose dim 0 indexes slots; each slot's first
+    H*128*128 elements are contiguous. Returns (num_slots, slot_stride)."""
+    if not state_pool.is_cuda or state_pool.stride(-1) != 1:
+        raise ValueError("state_pool must be a GPU tensor with a contiguous last dimension")
     n = state_pool.shape[0]
     inner = state_pool[0] if n > 0 else None
     if n > 0 and not inner.is_contiguous():
@@ -135,7 +145,8 @@ def kda_decode(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_indic
                stream=None) -> None:
     """T=1 decode. q, k, v, g_raw, out: bf16 [B, H*128] (row-strided views
     allowed); beta_raw bf16 [B, H]; A_log fp32 [H]; dt_bias fp32 [H*128];
-    state_pool bf16 [N, ...] (slot-major); state_indices int32 [B]."""
+    state_pool bf16 or fp16 [N, ...] (slot-major; its dtype selects the state
+    element type); state_indices int32 [B]."""
     B, W = q.shape
     H = W // HEAD_DIM
     for n, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta_raw", beta_raw),
@@ -150,7 +161,8 @@ def kda_decode(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_indic
                           _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
                           _ptr(g_raw), g_raw.stride(0), _ptr(beta_raw), beta_raw.stride(0),
                           _ptr(A_log), _ptr(dt_bias), float(lower_bound), float(scale),
-                          int(gate_mode), _ptr(state_pool) if N else _P(0), N, slot_stride,
+                          int(gate_mode), _state_dtype(state_pool),
+                          _ptr(state_pool) if N else _P(0), N, slot_stride,
                           _ptr(state_indices), _ptr(out), out.stride(0), _stream(stream))
     _check("kda_decode", st)
 
@@ -188,8 +200,8 @@ def kda_verify_ucache_flush(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool
         _ptr(v), v.stride(0), v.stride(1), _ptr(g_raw), g_raw.stride(0), g_raw.stride(1),
         _ptr(beta_raw), beta_raw.stride(0), beta_raw.stride(1),
         _ptr(A_log), _ptr(dt_bias), float(lower_bound), float(scale), int(gate_mode),
-        _ptr(state_pool) if N else _P(0), N, slot_stride, _ptr(state_indices),
-        _ptr(k_cache), _ptr(u_cache), _ptr(g_cache), R, _ptr(hist_len), _ptr(cache_base),
+        _state_dtype(state_pool), _ptr(state_pool) if N else _P(0), N, slot_stride,
+        _ptr(state_indices), _ptr(k_cache), _ptr(u_cache), _ptr(g_cache), R, _ptr(hist_len), _ptr(cache_base),
         int(flush_min), int(w_ring), 1 if restart_hist_on_flush else 0,
         _ptr(out), out.stride(0), out.stride(1), _stream(stream))
     _check("kda_verify_ucache_flush", st)
@@ -236,7 +248,8 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     ck_rows = 0
     if checkpoints is not None:
-        _bf16("checkpoints", checkpoints)
+        if checkpoints.dtype != state_pool.dtype or not checkpoints.is_cuda:
+            raise ValueError("checkpoints must be a GPU tensor of the state pool's dtype")
         if not checkpoints.is_contiguous() or \
                 checkpoints.numel() != checkpoints.shape[0] * H * HEAD_DIM * HEAD_DIM:
             raise ValueError("checkpoints must be a contiguous bf16 [rows, H, 128, 128] tensor")
@@ -250,8 +263,8 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
         _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
         _ptr(g_raw), g_raw.stride(0), _ptr(beta_raw), beta_raw.stride(0),
         _ptr(A_log), _ptr(dt_bias), float(lower_bound), float(scale), int(gate_mode),
-        _ptr(state_pool) if N else _P(0), N, slot_stride, _ptr(state_indices),
-        1 if use_initial_state else 0, _ptr(out), out.stride(0),
+        _state_dtype(state_pool), _ptr(state_pool) if N else _P(0), N, slot_stride,
+        _ptr(state_indices), 1 if use_initial_state else 0, _ptr(out), out.stride(0),
         _ptr(checkpoints), ck_rows, _ptr(checkpoint_cu_starts), int(checkpoint_interval),
         _ptr(workspace), ws_bytes, _stream(stream))
     _check("kda_prefill_varlen", st)

@@ -70,11 +70,13 @@ extern "C" kda_status kda_decode(int32_t B, int32_t H, int32_t K, int32_t V, con
                                  int64_t g_row_stride, const void* beta_raw,
                                  int64_t beta_row_stride, const float* A_log,
                                  const float* dt_bias, float lower_bound, float scale,
-                                 int32_t gate_mode, void* state_pool, int64_t num_slots,
+                                 int32_t gate_mode, int32_t state_dtype, void* state_pool,
+                                 int64_t num_slots,
                                  int64_t slot_stride, const int32_t* state_indices, void* out,
                                  int64_t out_row_stride, hipStream_t stream) {
   if (B < 0 || H < 1 || num_slots < 0) return KDA_ERR_BAD_SHAPE;
   if (K != D || V != D) return KDA_ERR_UNSUPPORTED;
+  if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP16) return KDA_ERR_UNSUPPORTED;
   if (const kda_status gs = check_gate(gate_mode, lower_bound, A_log, dt_bias)) {
     if (gs == KDA_ERR_UNSUPPORTED || B > 0) return gs;
   }
@@ -107,6 +109,7 @@ extern "C" kda_status kda_decode(int32_t B, int32_t H, int32_t K, int32_t V, con
   p.lower_bound = lower_bound;
   p.scale = scale;
   p.gate_mode = gate_mode;
+  p.state_fp16 = state_dtype == KDA_STATE_FP16 ? 1 : 0;
   p.state_pool = static_cast<uint16_t*>(state_pool);
   p.num_slots = num_slots;
   p.slot_stride = slot_stride;
@@ -117,6 +120,8 @@ extern "C" kda_status kda_decode(int32_t B, int32_t H, int32_t K, int32_t V, con
                    gate_vec_ok(gate_mode, g_raw, g_row_stride, 0) && aligned16(dt_bias) &&
                    (num_slots == 0 || aligned16(state_pool)) && mult8(q_row_stride) &&
                    mult8(k_row_stride) && mult8(slot_stride);
+  // fp16 state: the vectorised path only (16-byte aligned bases, strides in multiples of 8)
+  if (p.state_fp16 && !vec) return KDA_ERR_UNSUPPORTED;
   return launch_status(kda::launch_decode(p, vec, stream));
 }
 
@@ -126,8 +131,8 @@ extern "C" kda_status kda_verify_ucache_flush(
     const void* v, int64_t v_row_stride, int64_t v_tok_stride, const void* g_raw,
     int64_t g_row_stride, int64_t g_tok_stride, const void* beta_raw, int64_t beta_row_stride,
     int64_t beta_tok_stride, const float* A_log, const float* dt_bias, float lower_bound,
-    float scale, int32_t gate_mode, void* state_pool, int64_t num_slots, int64_t slot_stride,
-    const int32_t* state_indices, void* k_cache, void* u_cache, float* g_cache,
+    float scale, int32_t gate_mode, int32_t state_dtype, void* state_pool, int64_t num_slots,
+    int64_t slot_stride, const int32_t* state_indices, void* k_cache, void* u_cache, float* g_cache,
     int32_t ring_rows, const int32_t* hist_len, const int32_t* cache_base, int32_t flush_min,
     int32_t w_ring, int32_t restart_hist_on_flush, void* out, int64_t out_row_stride,
     int64_t out_tok_stride, hipStream_t stream) {
@@ -137,6 +142,7 @@ extern "C" kda_status kda_verify_ucache_flush(
   if (ring_rows < w_ring || restart_hist_on_flush != 1 || flush_min < 1) return KDA_ERR_UNSUPPORTED;
   if (flush_min - 1 + T > w_ring) return KDA_ERR_UNSUPPORTED;  // ring capacity
   if (w_ring == 32 && flush_min <= 16) return KDA_ERR_UNSUPPORTED;
+  if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP16) return KDA_ERR_UNSUPPORTED;
   if (const kda_status gs = check_gate(gate_mode, lower_bound, A_log, dt_bias)) {
     if (gs == KDA_ERR_UNSUPPORTED || B > 0) return gs;
   }
@@ -179,6 +185,7 @@ extern "C" kda_status kda_verify_ucache_flush(
   p.lower_bound = lower_bound;
   p.scale = scale;
   p.gate_mode = gate_mode;
+  p.state_fp16 = state_dtype == KDA_STATE_FP16 ? 1 : 0;
   p.state_pool = static_cast<uint16_t*>(state_pool);
   p.num_slots = num_slots;
   p.slot_stride = slot_stride;
@@ -202,6 +209,8 @@ extern "C" kda_status kda_verify_ucache_flush(
                    mult8(q_row_stride) && mult8(q_tok_stride) && mult8(k_row_stride) &&
                    mult8(k_tok_stride) && mult8(v_row_stride) && mult8(v_tok_stride) &&
                    mult8(out_row_stride) && mult8(out_tok_stride) && mult8(slot_stride);
+  // fp16 state: the vectorised path only (16-byte aligned bases, strides in multiples of 8)
+  if (p.state_fp16 && !vec) return KDA_ERR_UNSUPPORTED;
   return launch_status(kda::launch_verify(p, vec, stream));
 }
 
@@ -217,8 +226,8 @@ extern "C" kda_status kda_prefill_varlen(
     int64_t q_tok_stride, const void* k, int64_t k_tok_stride, const void* v,
     int64_t v_tok_stride, const void* g_raw, int64_t g_tok_stride, const void* beta_raw,
     int64_t beta_tok_stride, const float* A_log, const float* dt_bias, float lower_bound,
-    float scale, int32_t gate_mode, void* state_pool, int64_t num_slots, int64_t slot_stride,
-    const int32_t* state_indices, int32_t use_initial_state, void* out, int64_t out_tok_stride,
+    float scale, int32_t gate_mode, int32_t state_dtype, void* state_pool, int64_t num_slots,
+    int64_t slot_stride, const int32_t* state_indices, int32_t use_initial_state, void* out, int64_t out_tok_stride,
     void* checkpoints, int64_t checkpoint_rows, const int64_t* checkpoint_cu_starts,
     int32_t checkpoint_interval, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (n_docs < 0 || total_tokens < 0 || H < 1 || num_slots < 0) return KDA_ERR_BAD_SHAPE;
@@ -230,6 +239,7 @@ extern "C" kda_status kda_prefill_varlen(
   for (int32_t d = 0; d < n_docs; ++d)
     if (cu_seqlens_host[d + 1] < cu_seqlens_host[d]) return KDA_ERR_BAD_SEQLENS;
   if (int64_t(cu_seqlens_host[n_docs]) != total_tokens) return KDA_ERR_BAD_SEQLENS;
+  if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP16) return KDA_ERR_UNSUPPORTED;
   if (const kda_status gs = check_gate(gate_mode, lower_bound, A_log, dt_bias)) {
     if (gs == KDA_ERR_UNSUPPORTED || n_docs > 0) return gs;
   }
@@ -277,6 +287,7 @@ extern "C" kda_status kda_prefill_varlen(
   p.lower_bound = lower_bound;
   p.scale = scale;
   p.gate_mode = gate_mode;
+  p.state_fp16 = state_dtype == KDA_STATE_FP16 ? 1 : 0;
   p.state_pool = static_cast<uint16_t*>(state_pool);
   p.num_slots = num_slots;
   p.slot_stride = slot_stride;
@@ -294,5 +305,7 @@ extern "C" kda_status kda_prefill_varlen(
                    aligned16(out) && (num_slots == 0 || aligned16(state_pool)) &&
                    aligned16(checkpoints) && mult8(q_tok_stride) && mult8(k_tok_stride) &&
                    mult8(v_tok_stride) && mult8(out_tok_stride) && mult8(slot_stride);
+  // fp16 state: the vectorised path only (16-byte aligned bases, strides in multiples of 8)
+  if (p.state_fp16 && !vec) return KDA_ERR_UNSUPPORTED;
   return launch_status(kda::launch_prefill(p, cu_seqlens_host, vec, stream));
 }

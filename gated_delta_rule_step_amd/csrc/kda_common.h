@@ -31,6 +31,30 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
   return static_cast<uint16_t>(pack_bf16x2(x, 0.0f) & 0xffffu);
 }
 
+// fp16 (binary16) state elements: widening is exact (v_cvt_f32_f16);
+// narrowing is v_cvt_pk_f16_f32, round to nearest even.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+}
+
+// A state word of two elements, bf16 or (SF16) fp16.
+template <bool SF16>
+__device__ __forceinline__ float st_lo(uint32_t w) { return SF16 ? f16_lo(w) : bf_lo(w); }
+template <bool SF16>
+__device__ __forceinline__ float st_hi(uint32_t w) { return SF16 ? f16_hi(w) : bf_hi(w); }
+template <bool SF16>
+__device__ __forceinline__ uint32_t st_pack(float lo, float hi) {
+  return SF16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+}
+
 // 8 consecutive bf16 -> 8 floats; VEC: one 128-bit load (16-byte aligned).
 template <bool VEC>
 __device__ __forceinline__ void load8_bf16(const uint16_t* p, float (&x)[8]) {

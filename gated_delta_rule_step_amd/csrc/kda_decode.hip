@@ -33,7 +33,8 @@ namespace kda {
 // GK, the gate kind: kGatePrecomputed clear = raw gate logits (log-decay from
 // A_log, dt_bias, lower_bound), set = the log-decay itself; kGatePerHead set =
 // one gate value (and dt_bias) per head for all key channels.
-template <int LOADS, bool VEC, int GK>
+// SF16: the pool holds fp16 state (else bf16).
+template <int LOADS, bool VEC, int GK, bool SF16>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr bool GRAW = !(GK & kGatePrecomputed);
   constexpr bool GHEAD = (GK & kGatePerHead) != 0;
@@ -122,8 +123,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     float x[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      x[2 * j] = bf_lo(s[i][j]);
-      x[2 * j + 1] = bf_hi(s[i][j]);
+      x[2 * j] = st_lo<SF16>(s[i][j]);
+      x[2 * j + 1] = st_hi<SF16>(s[i][j]);
     }
     float dk = 0.f, dq = 0.f;
 #pragma unroll
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     for (int j = 0; j < 4; ++j) {
       const float a0 = fmaf(al[2 * j], x[2 * j], kh[2 * j] * u);
       const float a1 = fmaf(al[2 * j + 1], x[2 * j + 1], kh[2 * j + 1] * u);
-      w[j] = pack_bf16x2(a0, a1);
+      w[j] = st_pack<SF16>(a0, a1);
     }
     store8_raw<VEC>(sp + i * 4 * D, w);
   }
@@ -161,21 +162,26 @@ hipError_t launch_decode(const DecodeParams& p, bool vec, hipStream_t stream) {
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
   const int gk = p.gate_mode & kGateKindMask;
-#define KDA_DECODE_LAUNCH(L, V)                                                              \
-  do {                                                                                       \
-    switch (gk) {                                                                            \
-      case 0: hipLaunchKernelGGL((decode_kernel<L, V, 0>), grid, block, 0, stream, p); break; \
-      case 1: hipLaunchKernelGGL((decode_kernel<L, V, 1>), grid, block, 0, stream, p); break; \
-      case 4: hipLaunchKernelGGL((decode_kernel<L, V, 4>), grid, block, 0, stream, p); break; \
-      default: hipLaunchKernelGGL((decode_kernel<L, V, 5>), grid, block, 0, stream, p);      \
-    }                                                                                        \
+#define KDA_DECODE_LAUNCH(L, V, F)                                                              \
+  do {                                                                                          \
+    switch (gk) {                                                                               \
+      case 0: hipLaunchKernelGGL((decode_kernel<L, V, 0, F>), grid, block, 0, stream, p); break; \
+      case 1: hipLaunchKernelGGL((decode_kernel<L, V, 1, F>), grid, block, 0, stream, p); break; \
+      case 4: hipLaunchKernelGGL((decode_kernel<L, V, 4, F>), grid, block, 0, stream, p); break; \
+      default: hipLaunchKernelGGL((decode_kernel<L, V, 5, F>), grid, block, 0, stream, p);      \
+    }                                                                                           \
   } while (0)
-  if (small) {
-    if (vec) KDA_DECODE_LAUNCH(2, true);
-    else KDA_DECODE_LAUNCH(2, false);
+  // fp16 state runs on the vectorised path only (the host requires it)
+  if (p.state_fp16) {
+    if (!vec) return hipErrorInvalidValue;
+    if (small) KDA_DECODE_LAUNCH(2, true, true);
+    else KDA_DECODE_LAUNCH(8, true, true);
+  } else if (small) {
+    if (vec) KDA_DECODE_LAUNCH(2, true, false);
+    else KDA_DECODE_LAUNCH(2, false, false);
   } else {
-    if (vec) KDA_DECODE_LAUNCH(8, true);
-    else KDA_DECODE_LAUNCH(8, false);
+    if (vec) KDA_DECODE_LAUNCH(8, true, false);
+    else KDA_DECODE_LAUNCH(8, false, false);
   }
 #undef KDA_DECODE_LAUNCH
   return hipGetLastError();

@@ -28,6 +28,7 @@ struct DecodeParams {
   const float* dt_bias;
   float lower_bound, scale;
   int32_t gate_mode;
+  int32_t state_fp16;  // pool elements are fp16 (else bf16)
   uint16_t* state_pool;
   int64_t num_slots, slot_stride;
   const int32_t* state_indices;
@@ -48,6 +49,7 @@ struct VerifyParams {
   const float* dt_bias;
   float lower_bound, scale;
   int32_t gate_mode;
+  int32_t state_fp16;  // checkpoint elements are fp16 (else bf16); rings stay bf16
   uint16_t* state_pool;
   int64_t num_slots, slot_stride;
   const int32_t* state_indices;
@@ -76,6 +78,7 @@ struct PrefillParams {
   const float* dt_bias;
   float lower_bound, scale;
   int32_t gate_mode;
+  int32_t state_fp16;  // pool and checkpoint elements are fp16 (else bf16)
   uint16_t* state_pool;
   int64_t num_slots, slot_stride;
   const int32_t* state_indices;

@@ -526,7 +526,8 @@ constexpr int kChainThreads = 512;
 constexpr int kChainRounds = (kRecUnits + kChainThreads - 1) / kChainThreads;  // 4
 static_assert(kRecUnits > (kChainRounds - 1) * kChainThreads, "every round has work");
 
-template <bool VEC>
+// SF16: the pool (initial and final states) and the checkpoints hold fp16.
+template <bool VEC, bool SF16>
 __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, DocOrder ord) {
   __shared__ __align__(16) uint8_t rbuf[2][kRecBytes];
   const int tid = threadIdx.x;
@@ -597,7 +598,8 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
     for (int mt = 0; mt < 8; ++mt) w[mt] = gload4<VEC>(sp + v * D + 16 * mt + 4 * g4);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
-      acc[mt] = f32x4{bf_lo(w[mt][0]), bf_hi(w[mt][0]), bf_lo(w[mt][1]), bf_hi(w[mt][1])};
+      acc[mt] = f32x4{st_lo<SF16>(w[mt][0]), st_hi<SF16>(w[mt][0]), st_lo<SF16>(w[mt][1]),
+                      st_hi<SF16>(w[mt][1])};
   } else {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -672,7 +674,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
         for (int mt = 0; mt < 8; ++mt) {
           const f32x4 a = acc[mt];
           gstore4<VEC>(cp + v * D + 16 * mt + 4 * g4,
-                       u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])});
+                       u32x2{st_pack<SF16>(a[0], a[1]), st_pack<SF16>(a[2], a[3])});
         }
       }
     }
@@ -688,7 +690,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
   for (int mt = 0; mt < 8; ++mt) {
     const f32x4 a = acc[mt];
     gstore4<VEC>(sp + v * D + 16 * mt + 4 * g4,
-                 u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])});
+                 u32x2{st_pack<SF16>(a[0], a[1]), st_pack<SF16>(a[2], a[3])});
   }
 }
 
@@ -759,8 +761,15 @@ hipError_t launch_prefill(const PrefillParams& p, const int32_t* cu_host, bool v
     if (e != hipSuccess) return e;
   }
   dim3 grid(static_cast<unsigned>(blocks)), block(kChainThreads);
-  if (vec) hipLaunchKernelGGL((chain_kernel<true>), grid, block, 0, stream, p, ord);
-  else hipLaunchKernelGGL((chain_kernel<false>), grid, block, 0, stream, p, ord);
+  // fp16 states run on the vectorised path only (the host requires it)
+  if (p.state_fp16) {
+    if (!vec) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((chain_kernel<true, true>), grid, block, 0, stream, p, ord);
+  } else if (vec) {
+    hipLaunchKernelGGL((chain_kernel<true, false>), grid, block, 0, stream, p, ord);
+  } else {
+    hipLaunchKernelGGL((chain_kernel<false, false>), grid, block, 0, stream, p, ord);
+  }
   return hipGetLastError();
 }
 

@@ -44,6 +44,7 @@ namespace kda {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __fp16 f16x8 __attribute__((__vector_size__(8 * sizeof(__fp16))));  // MFMA f16 operand
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TMAX = 8;
@@ -170,8 +171,10 @@ __device__ __forceinline__ void load_tokens(const VerifyParams& p, int64_t item,
 
 // Grid: one 256-thread workgroup per item (row, head), item = row * H + head.
 // GK, the gate kind: kGatePrecomputed clear = raw gate logits, set = the
-// log-decay itself; kGatePerHead set = one gate value per head.
-template <bool VEC, bool FACT, int GK>
+// log-decay itself; kGatePerHead set = one gate value per head. SF16: fp16
+// checkpoints (the product below then runs on v_mfma_f32_16x16x32_f16 with
+// fp16 hi / lo A fragments); the rings stay bf16.
+template <bool VEC, bool FACT, int GK, bool SF16>
 __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   constexpr bool GRAW = !(GK & kGatePrecomputed);
   extern __shared__ __align__(16) float smem_raw[];
@@ -390,8 +393,8 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
         float x[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[2 * e] = bf_lo(sf[blk][st][e]) * s.egl[k0 + 2 * e];
-          x[2 * e + 1] = bf_hi(sf[blk][st][e]) * s.egl[k0 + 2 * e + 1];
+          x[2 * e] = st_lo<SF16>(sf[blk][st][e]) * s.egl[k0 + 2 * e];
+          x[2 * e + 1] = st_hi<SF16>(sf[blk][st][e]) * s.egl[k0 + 2 * e + 1];
         }
         for (int j = 0; j < hist; ++j) {
           const float uj = bf1(s.uh[j * D + v]);
@@ -400,7 +403,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
         }
         u32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+        for (int e = 0; e < 4; ++e) w[e] = st_pack<SF16>(x[2 * e], x[2 * e + 1]);
         // A plain (cached) store: one instruction covers 64 of the 128 bytes of
         // each of 16 checkpoint rows, and the st + 1 store fills the other
         // half; in L2 the halves merge into whole lines before they reach
@@ -538,18 +541,27 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
       for (int i = 0; i < 2; ++i) {
         const float a = x0[2 * i] * e0[2 * i], b = x0[2 * i + 1] * e0[2 * i + 1];
         const float c = x1[2 * i] * e1[2 * i], d = x1[2 * i + 1] * e1[2 * i + 1];
-        hi[i] = pack_bf16x2(a, b);
-        hi[2 + i] = pack_bf16x2(c, d);
-        lo[i] = pack_bf16x2(a - bf_lo(hi[i]), b - bf_hi(hi[i]));
-        lo[2 + i] = pack_bf16x2(c - bf_lo(hi[2 + i]), d - bf_hi(hi[2 + i]));
+        // hi / lo split in the checkpoint's own format
+        hi[i] = st_pack<SF16>(a, b);
+        hi[2 + i] = st_pack<SF16>(c, d);
+        lo[i] = st_pack<SF16>(a - st_lo<SF16>(hi[i]), b - st_hi<SF16>(hi[i]));
+        lo[2 + i] = st_pack<SF16>(c - st_lo<SF16>(hi[2 + i]), d - st_hi<SF16>(hi[2 + i]));
       }
-      const bf16x8 ahi = __builtin_bit_cast(bf16x8, hi);
-      const bf16x8 alo = __builtin_bit_cast(bf16x8, lo);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const bf16x8 bfr = __builtin_bit_cast(bf16x8, sf[blk][st]);
-        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bfr, acc[blk], 0, 0, 0);
-        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfr, acc[blk], 0, 0, 0);
+        if constexpr (SF16) {
+          const f16x8 ahi = __builtin_bit_cast(f16x8, hi);
+          const f16x8 alo = __builtin_bit_cast(f16x8, lo);
+          const f16x8 bfr = __builtin_bit_cast(f16x8, sf[blk][st]);
+          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bfr, acc[blk], 0, 0, 0);
+          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bfr, acc[blk], 0, 0, 0);
+        } else {
+          const bf16x8 ahi = __builtin_bit_cast(bf16x8, hi);
+          const bf16x8 alo = __builtin_bit_cast(bf16x8, lo);
+          const bf16x8 bfr = __builtin_bit_cast(bf16x8, sf[blk][st]);
+          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bfr, acc[blk], 0, 0, 0);
+          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfr, acc[blk], 0, 0, 0);
+        }
       }
     }
     // History correction C U_hist (C = X D^T from phase 5b, 2T x hist; U_hist
@@ -630,21 +642,32 @@ hipError_t launch_verify(const VerifyParams& p, bool vec, hipStream_t stream) {
   const bool fact = p.lower_bound > -80.0f / float(p.T) && p.lower_bound <= 0.0f;
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
   const int gk = p.gate_mode & kGateKindMask;
-#define KDA_VERIFY_LAUNCH(V, F)                                                                    \
-  do {                                                                                             \
-    switch (gk) {                                                                                  \
-      case 0: hipLaunchKernelGGL((verify_kernel<V, F, 0>), grid, block, lds, stream, p, hm); break; \
-      case 1: hipLaunchKernelGGL((verify_kernel<V, F, 1>), grid, block, lds, stream, p, hm); break; \
-      case 4: hipLaunchKernelGGL((verify_kernel<V, F, 4>), grid, block, lds, stream, p, hm); break; \
-      default: hipLaunchKernelGGL((verify_kernel<V, F, 5>), grid, block, lds, stream, p, hm);      \
-    }                                                                                              \
+#define KDA_VERIFY_LAUNCH(V, F, S)                                                            \
+  do {                                                                                        \
+    switch (gk) {                                                                             \
+      case 0:                                                                                 \
+        hipLaunchKernelGGL((verify_kernel<V, F, 0, S>), grid, block, lds, stream, p, hm);     \
+        break;                                                                                \
+      case 1:                                                                                 \
+        hipLaunchKernelGGL((verify_kernel<V, F, 1, S>), grid, block, lds, stream, p, hm);     \
+        break;                                                                                \
+      case 4:                                                                                 \
+        hipLaunchKernelGGL((verify_kernel<V, F, 4, S>), grid, block, lds, stream, p, hm);     \
+        break;                                                                                \
+      default: hipLaunchKernelGGL((verify_kernel<V, F, 5, S>), grid, block, lds, stream, p, hm); \
+    }                                                                                         \
   } while (0)
-  if (vec) {
-    if (fact) KDA_VERIFY_LAUNCH(true, true);
-    else KDA_VERIFY_LAUNCH(true, false);
+  // fp16 checkpoints run on the vectorised path only (the host requires it)
+  if (p.state_fp16) {
+    if (!vec) return hipErrorInvalidValue;
+    if (fact) KDA_VERIFY_LAUNCH(true, true, true);
+    else KDA_VERIFY_LAUNCH(true, false, true);
+  } else if (vec) {
+    if (fact) KDA_VERIFY_LAUNCH(true, true, false);
+    else KDA_VERIFY_LAUNCH(true, false, false);
   } else {
-    if (fact) KDA_VERIFY_LAUNCH(false, true);
-    else KDA_VERIFY_LAUNCH(false, false);
+    if (fact) KDA_VERIFY_LAUNCH(false, true, false);
+    else KDA_VERIFY_LAUNCH(false, false, false);
   }
 #undef KDA_VERIFY_LAUNCH
   return hipGetLastError();

@@ -135,6 +135,15 @@ def per_head_gate(case: dict, precomputed: bool, seed: int) -> dict:
     return c
 
 
+def fp16_state(case: dict) -> dict:
+    """A copy of a decode, verify or prefill case whose pool holds fp16 state
+    (state_dtype 1): the same state values, stored as binary16 bits."""
+    c = dict(case)
+    c["pool"] = f32_from_bits(case["pool"]).astype(np.float16).view(np.uint16)
+    c["state_dtype"] = 1
+    return c
+
+
 def decode_case(B: int, N: int = 1024, H: int = 12, seed: int | None = None,
                 inactive_frac: float = 0.05, idx: np.ndarray | None = None) -> dict:
     rng = np.random.Generator(np.random.PCG64(seed_for(1, B) if seed is None else seed))

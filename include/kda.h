@@ -37,6 +37,17 @@
  *    of the head (a reading).
  * The bits combine; any other bit gives KDA_ERR_UNSUPPORTED.
  *
+ * State element type (argument state_dtype of every entry point): the pages'
+ * GDN verify kernel offers "an optional fp16 checkpoint-state mode"
+ * ("feat(kda): ReplaySSM verify+flush decode kernel for Kimi K3 (KDA)",
+ * "Caching"). KDA_STATE_BF16 (0) keeps the pool, the verify checkpoints and the
+ * prefill states in bf16; KDA_STATE_FP16 (1) keeps them in fp16 (IEEE binary16,
+ * rounded to nearest even), the same 2 bytes with 3 more fraction bits and a
+ * range of +-65504. Token inputs, outputs and the verify rings stay bf16 and
+ * g_cache fp32. fp16 state needs the vectorised layout (16-byte aligned bases,
+ * strides in multiples of 8), else KDA_ERR_UNSUPPORTED; any other value also
+ * gives KDA_ERR_UNSUPPORTED.
+ *
  * Conventions common to every entry point
  *  - Every pointer is a DEVICE pointer, except those whose name ends in _host.
  *  - bf16 tensors are passed as `const void*` / `void*` holding raw bf16 bits.
@@ -86,6 +97,11 @@ enum {
   KDA_GATE_PER_HEAD = 4      /* gate_mode bit: one gate value (and dt_bias) per head */
 };
 
+enum {
+  KDA_STATE_BF16 = 0,  /* state_dtype: pool / checkpoint elements are bf16 */
+  KDA_STATE_FP16 = 1   /* state_dtype: pool / checkpoint elements are fp16 */
+};
+
 typedef enum {
   KDA_OK = 0,
   KDA_ERR_NULL_POINTER = 1,
@@ -128,6 +144,7 @@ const char* kda_status_string(kda_status s);
  *  scale              read-out scale
  *  gate_mode          0, or any of KDA_GATE_PRECOMPUTED, KDA_BETA_PRESIGMOID,
  *                     KDA_GATE_PER_HEAD
+ *  state_dtype        KDA_STATE_BF16 or KDA_STATE_FP16 (the pool's elements)
  *  state_pool         bf16 pool, num_slots slots of slot_stride elements
  *                     (may be NULL only when num_slots == 0)
  *  state_indices      int32 [B]: the pool slot of each row
@@ -144,6 +161,7 @@ kda_status kda_decode(int32_t B, int32_t H, int32_t K, int32_t V,
                       const void* beta_raw, int64_t beta_row_stride,
                       const float* A_log, const float* dt_bias,
                       float lower_bound, float scale, int32_t gate_mode,
+                      int32_t state_dtype,
                       void* state_pool, int64_t num_slots, int64_t slot_stride,
                       const int32_t* state_indices,
                       void* out, int64_t out_row_stride,
@@ -186,8 +204,9 @@ kda_status kda_decode(int32_t B, int32_t H, int32_t K, int32_t V,
  *  q, k, v, g_raw     bf16, element (b, t, h*128 + c) at
  *                     b*row_stride + t*tok_stride + h*128 + c
  *  beta_raw           bf16, element (b, t, h) at b*row_stride + t*tok_stride + h
- *  A_log, dt_bias, lower_bound, scale, gate_mode, state_pool, num_slots,
- *  slot_stride, state_indices  as for kda_decode (the pool holds the checkpoints)
+ *  A_log, dt_bias, lower_bound, scale, gate_mode, state_dtype, state_pool,
+ *  num_slots, slot_stride, state_indices  as for kda_decode (the pool holds the
+ *                     checkpoints)
  *  k_cache, u_cache   bf16 [num_slots, H, ring_rows, 128]
  *  g_cache            fp32 [num_slots, H, ring_rows, 128]
  *  ring_rows          R, physical ring rows per (slot, head) (>= w_ring)
@@ -211,6 +230,7 @@ kda_status kda_verify_ucache_flush(int32_t B, int32_t T, int32_t H, int32_t K, i
                                    int64_t beta_tok_stride,
                                    const float* A_log, const float* dt_bias,
                                    float lower_bound, float scale, int32_t gate_mode,
+                                   int32_t state_dtype,
                                    void* state_pool, int64_t num_slots, int64_t slot_stride,
                                    const int32_t* state_indices,
                                    void* k_cache, void* u_cache, float* g_cache,
@@ -248,14 +268,16 @@ size_t kda_prefill_workspace_size(int32_t n_docs, int64_t total_tokens, int32_t 
  *  cu_seqlens         int32 [n_docs + 1], device copy with the same contents
  *  q, k, v, g_raw     bf16, element (t, h*128 + c) at t*tok_stride + h*128 + c
  *  beta_raw           bf16, element (t, h) at t*beta_tok_stride + h
- *  A_log, dt_bias, lower_bound, scale, gate_mode  as for kda_decode
+ *  A_log, dt_bias, lower_bound, scale, gate_mode, state_dtype  as for kda_decode
+ *                     (checkpoints, below, use the state element type too)
  *  state_pool, num_slots, slot_stride  as for kda_decode
  *  state_indices      int32 [n_docs]: slot of each document (initial and final
  *                     state); a document whose slot is outside [0, num_slots)
  *                     gets zero outputs and no state write
  *  use_initial_state  1: start each chain from its slot; 0: from zeros
  *  out                bf16, element (t, h*128 + v) at t*out_tok_stride + h*128 + v
- *  checkpoints        NULL (no intermediate checkpoints), or bf16 rows of H
+ *  checkpoints        NULL (no intermediate checkpoints), or rows (of the state
+ *                     element type, see state_dtype) of H
  *                     states laid out like a pool slot (row r, head h at
  *                     (r*H + h)*16384, element (v, c) at v*128 + c). The page
  *                     returns "output, final state, checkpoints" with an int64
@@ -265,7 +287,7 @@ size_t kda_prefill_workspace_size(int32_t n_docs, int64_t total_tokens, int32_t 
  *                     floor(len_d / checkpoint_interval), into row
  *                     checkpoint_cu_starts[d] + i - 1; rows outside
  *                     [0, checkpoint_rows) are skipped; inactive documents store
- *                     none. Rounded to bf16 like the final state.
+ *                     none. Rounded like the final state.
  *  checkpoint_rows    rows of `checkpoints` (>= 0)
  *  checkpoint_cu_starts  int64 [n_docs] device array (read only when
  *                     checkpoints is not NULL)
@@ -301,6 +323,7 @@ kda_status kda_prefill_varlen(int32_t n_docs, int64_t total_tokens, int32_t H, i
                               const void* beta_raw, int64_t beta_tok_stride,
                               const float* A_log, const float* dt_bias,
                               float lower_bound, float scale, int32_t gate_mode,
+                              int32_t state_dtype,
                               void* state_pool, int64_t num_slots, int64_t slot_stride,
                               const int32_t* state_indices, int32_t use_initial_state,
                               void* out, int64_t out_tok_stride,

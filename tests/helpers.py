@@ -38,6 +38,50 @@ def bf16_ulp(x):
     return np.exp2(np.floor(np.log2(np.maximum(np.abs(x), STATE_FLOOR))) - 7)
 
 
+# fp16 state (state_dtype 1): 2 fp16 ulps of max(|ref|, 2^-9). The floor gives
+# the same absolute allowance near zero as the bf16 criterion (2 * 2^-12 *
+# 2^-7 = 2^-18): that allowance covers the arithmetic's error, which does not
+# depend on the storage format; above 2^-9 the check is 8 times tighter than
+# the bf16 one.
+STATE_FLOOR_F16 = 2.0 ** -9
+
+
+def f16_ulp(x):
+    return np.exp2(np.floor(np.log2(np.maximum(np.abs(x), STATE_FLOOR_F16))) - 10)
+
+
+# Pools of either state element type (case["state_dtype"]: 0 bf16, 1 fp16).
+def pool_vals(case, pool_bits):
+    """The values a pool's bit patterns hold, as float32."""
+    if case.get("state_dtype", 0):
+        return np.ascontiguousarray(pool_bits).view(np.float16).astype(np.float32)
+    return f32(pool_bits)
+
+
+def pool_dev(case, pool_bits, device="cuda"):
+    import torch
+    if case.get("state_dtype", 0):
+        a = np.ascontiguousarray(pool_bits)
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.float16)
+    return dev_bf16(pool_bits, device)
+
+
+def check_pool(case, got_bits, ref, what="state"):
+    """check_state in the pool's element type (2 ulps of that type, same floor)."""
+    if not case.get("state_dtype", 0):
+        return check_state(got_bits, ref, what)
+    got = pool_vals(case, got_bits).astype(np.float64).reshape(ref.shape)
+    ref = ref.astype(np.float64)
+    tol = STATE_ULPS * f16_ulp(ref)
+    bad = ~(np.abs(got - ref) <= tol)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, np.abs(got - ref) / tol, -np.inf)),
+                             ref.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements beyond "
+                             f"{STATE_ULPS} fp16 ulps; worst at {i}: got {got[i]!r} "
+                             f"ref {ref[i]!r}")
+
+
 def check_out(got_bits, ref, what="output"):
     got = f32(got_bits).astype(np.float64).reshape(ref.shape)
     ref = ref.astype(np.float64)
@@ -97,7 +141,7 @@ def oracle_decode(orc, case, pool_bits=None):
     H, N = case["H"], case["N"]
     pool_bits = case["pool"] if pool_bits is None else pool_bits
     slots, cidx = compact_slots(case["idx"], N)
-    cpool = np.ascontiguousarray(f32(pool_bits[slots]))
+    cpool = np.ascontiguousarray(pool_vals(case, pool_bits[slots]))
     q, k, v = split_qkv(case["qkv"], H)
     gm = case.get("gate_mode", 0)
     a_log, dt_bias = (None, None) if gm & 1 else (case["a_log"], case["dt_bias"])
@@ -105,5 +149,5 @@ def oracle_decode(orc, case, pool_bits=None):
     out = orc.decode(q, k, v, np.ascontiguousarray(f32(case["gate"]).reshape(gshape)),
                      np.ascontiguousarray(f32(case["beta"])), a_log, dt_bias,
                      case["lower_bound"], case["scale"], cpool, cidx, bf16_storage=True,
-                     real=np.float32, gate_mode=gm)
+                     real=np.float32, gate_mode=gm, state_dtype=case.get("state_dtype", 0))
     return out, slots, cpool

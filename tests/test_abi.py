@@ -60,13 +60,14 @@ def test_status_strings(lib):
 def _decode(lib, **kw):
     a = dict(B=2, H=12, K=128, V=128, q=1 << 20, qs=4608, k=1 << 20, ks=4608, v=1 << 20,
              vs=4608, g=1 << 20, gs=1536, b=1 << 20, bs=12, alog=1 << 20, dtb=1 << 20,
-             lb=-5.0, scale=1.0, gm=0, pool=1 << 20, N=4, ss=12 * 128 * 128, idx=1 << 20,
+             lb=-5.0, scale=1.0, gm=0, sd=0, pool=1 << 20, N=4, ss=12 * 128 * 128, idx=1 << 20,
              out=1 << 20, os=1536)
     a.update(kw)
     P = ctypes.c_void_p
     return lib.kda_decode(a["B"], a["H"], a["K"], a["V"], P(a["q"]), a["qs"], P(a["k"]),
                           a["ks"], P(a["v"]), a["vs"], P(a["g"]), a["gs"], P(a["b"]), a["bs"],
-                          P(a["alog"]), P(a["dtb"]), a["lb"], a["scale"], a["gm"], P(a["pool"]),
+                          P(a["alog"]), P(a["dtb"]), a["lb"], a["scale"], a["gm"], a["sd"],
+                          P(a["pool"]),
                           a["N"], a["ss"], P(a["idx"]), P(a["out"]), a["os"], P(0))
 
 
@@ -108,17 +109,31 @@ def test_gate_mode_validation(lib):
     assert _verify(lib, B=0, gm=3) == OK
 
 
+def test_state_dtype_validation(lib):
+    """state_dtype: bf16 (0) or fp16 (1), and fp16 only on the vectorised
+    layout (16-byte aligned bases, strides in multiples of 8)."""
+    assert _decode(lib, sd=2) == UNSUP
+    assert _decode(lib, sd=-1) == UNSUP
+    assert _decode(lib, sd=1, q=(1 << 20) + 2) == UNSUP   # unaligned q: no vectorised path
+    assert _decode(lib, sd=1, qs=4610) == UNSUP
+    assert _decode(lib, B=0, sd=1) == OK
+    assert _verify(lib, sd=5) == UNSUP
+    assert _verify(lib, sd=1, rs=8 * 4608 + 2) == UNSUP
+
+
 def _verify(lib, **kw):
     a = dict(B=2, T=8, H=12, K=128, V=128, ptr=1 << 20, rs=8 * 4608, ts=4608, brs=96, bts=12,
              grs=8 * 1536, gts=1536, lb=-5.0, scale=1.0, N=4, ss=12 * 128 * 128, R=32,
-             fm=9, w=16, restart=1, ors=8 * 1536, ots=1536, kc=1 << 20, hist=1 << 20, gm=0)
+             fm=9, w=16, restart=1, ors=8 * 1536, ots=1536, kc=1 << 20, hist=1 << 20, gm=0,
+             sd=0)
     a.update(kw)
     P = ctypes.c_void_p
     p = P(a["ptr"])
     return lib.kda_verify_ucache_flush(
         a["B"], a["T"], a["H"], a["K"], a["V"], p, a["rs"], a["ts"], p, a["rs"], a["ts"],
         p, a["rs"], a["ts"], p, a["grs"], a["gts"], p, a["brs"], a["bts"], p, p, a["lb"],
-        a["scale"], a["gm"], p, a["N"], a["ss"], p, P(a["kc"]), p, p, a["R"], P(a["hist"]), p,
+        a["scale"], a["gm"], a["sd"], p, a["N"], a["ss"], p, P(a["kc"]), p, p, a["R"],
+        P(a["hist"]), p,
         a["fm"],
         a["w"], a["restart"], p, a["ors"], a["ots"], P(0))
 
@@ -153,12 +168,13 @@ def test_prefill_workspace_and_validation(lib):
 
     def call(cu, total, **kw):
         p = P(1 << 20)
-        a = dict(n=len(cu) - 1, H=2, K=128, ws=1 << 40, ots=256, lb=-5.0, ws_ptr=p, gm=0,
+        a = dict(n=len(cu) - 1, H=2, K=128, ws=1 << 40, ots=256, lb=-5.0, ws_ptr=p, gm=0, sd=0,
                  ck=P(0), ck_rows=0, ck_starts=P(0), ck_int=16)
         a.update(kw)
         arr = (ctypes.c_int32 * len(cu))(*cu)
         return lib.kda_prefill_varlen(a["n"], total, a["H"], a["K"], 128, arr, p, p, 256, p,
-                                      256, p, 256, p, 256, p, 2, p, p, a["lb"], 1.0, a["gm"], p, 4,
+                                      256, p, 256, p, 256, p, 2, p, p, a["lb"], 1.0, a["gm"],
+                                      a["sd"], p, 4,
                                       2 * 128 * 128, p, 1, p, a["ots"], a["ck"], a["ck_rows"],
                                       a["ck_starts"], a["ck_int"], a["ws_ptr"], a["ws"], P(0))
 
@@ -172,6 +188,7 @@ def test_prefill_workspace_and_validation(lib):
     assert call([0, 5], 5, lb=float("nan")) == UNSUP
     assert call([0], 0) == OK           # no documents: nothing to do
     assert call([0, 5], 5, gm=8) == UNSUP
+    assert call([0, 5], 5, sd=3) == UNSUP
     # intermediate checkpoints: on chunk boundaries, a row count, a starts array
     q = P(1 << 20)
     assert call([0, 5], 5, ck=q, ck_rows=3, ck_starts=q, ck_int=24) == UNSUP

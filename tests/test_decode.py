@@ -8,8 +8,8 @@ import numpy as np
 import pytest
 
 from gated_delta_rule_step_amd import synth
-from tests.helpers import (HD, bits, check_out, check_state, dev, dev_bf16, f32,
-                           oracle_decode, split_qkv)
+from tests.helpers import (HD, bits, check_out, check_pool, check_state, dev, dev_bf16, f32,
+                           oracle_decode, pool_dev, split_qkv)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -27,7 +27,7 @@ def run_decode(case, pool=None, out=None, scale=None, lower_bound=None, stream=N
     H = case["H"]
     W = H * HD
     qkv = dev_bf16(case["qkv"])
-    pool = dev_bf16(case["pool"]) if pool is None else pool
+    pool = pool_dev(case, case["pool"]) if pool is None else pool
     B = case["B"]
     if out is None:
         out = torch.full((B, W), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -47,7 +47,7 @@ def check_case(orc, case, pool_dev, out_dev):
     torch.cuda.synchronize()
     got_pool = bits(pool_dev)
     check_out(bits(out_dev), ref_out, "decode output")
-    check_state(got_pool[slots], ref_state, "decode state")
+    check_pool(case, got_pool[slots], ref_state, "decode state")
     untouched = np.ones(case["N"], bool)
     untouched[slots] = False
     assert np.array_equal(got_pool[untouched], case["pool"][untouched]), \
@@ -66,6 +66,15 @@ def test_precomputed_gate_conventions(orc, gate_mode):
     gate is pre-computed."""
     case = synth.precomputed_gate(synth.decode_case(B=512, H=12), gate_mode,
                                   synth.seed_for(1, 512, 100 + gate_mode))
+    pool, out = run_decode(case)
+    check_case(orc, case, pool, out)
+
+
+@pytest.mark.parametrize("B", [1, 512])
+def test_fp16_state(orc, B):
+    """An fp16 state pool (state_dtype 1), B = 1 and 512 with inactive rows:
+    the state is read and written as binary16, outputs stay bf16."""
+    case = synth.fp16_state(synth.decode_case(B=B, H=12))
     pool, out = run_decode(case)
     check_case(orc, case, pool, out)
 

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 from gated_delta_rule_step_amd import synth
-from tests.helpers import HD, bits, check_out, check_state, dev, dev_bf16, f32
+from tests.helpers import (HD, bits, check_out, check_pool, dev, dev_bf16, f32, pool_dev,
+                           pool_vals)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -38,7 +39,7 @@ def run_prefill(case, pool=None, packed=False, use_initial_state=None, lower_bou
     else:
         q, k, v = (dev_bf16(case[n].reshape(Ttot, W)) for n in ("q", "k", "v"))
         out = torch.full((Ttot, W), float("nan"), dtype=torch.bfloat16, device="cuda")
-    pool = dev_bf16(case["pool"]) if pool is None else pool
+    pool = pool_dev(case, case["pool"]) if pool is None else pool
     cu_h = torch.from_numpy(case["cu_seqlens"].copy())
     uis = case["use_initial_state"] if use_initial_state is None else use_initial_state
     _kda().kda_prefill_varlen(cu_h, dev(case["cu_seqlens"]), q, k, v, dev_bf16(case["gate"]),
@@ -68,7 +69,7 @@ def oracle_prefill(orc, case, heads=None, use_initial_state=None, lower_bound=No
     else:
         g = f32(case["gate"]).reshape(Ttot, H, HD)[:, hs]
     b = f32(case["beta"])[:, hs]
-    pool = f32(case["pool"])[:, hs]
+    pool = pool_vals(case, case["pool"])[:, hs]
     uis = case["use_initial_state"] if use_initial_state is None else use_initial_state
     lb = case["lower_bound"] if lower_bound is None else lower_bound
     c = np.ascontiguousarray
@@ -79,7 +80,8 @@ def oracle_prefill(orc, case, heads=None, use_initial_state=None, lower_bound=No
                       None if pre else c(case["dt_bias"].reshape(H, -1)[hs]), lb,
                       case["scale"], pool, case["idx"], use_initial_state=uis,
                       bf16_storage=True, real=np.float32, gate_mode=gm, checkpoints=ckpt,
-                      checkpoint_starts=ckpt_starts, checkpoint_interval=ckpt_interval)
+                      checkpoint_starts=ckpt_starts, checkpoint_interval=ckpt_interval,
+                      state_dtype=case.get("state_dtype", 0))
     return out, pool
 
 
@@ -99,7 +101,7 @@ def check_prefill(orc, case, pool_dev, out_dev, heads=None, use_initial_state=No
         if active[d]:
             if t1 > t0:
                 check_out(got_out[t0:t1], ref_out[t0:t1], f"prefill output doc {d}")
-            check_state(got_pool[idx[d]][hs], ref_pool[idx[d]], f"prefill state doc {d}")
+            check_pool(case, got_pool[idx[d]][hs], ref_pool[idx[d]], f"prefill state doc {d}")
         else:
             assert np.all(got_out[t0:t1] == 0), f"inactive doc {d} must output +0.0"
     touched = np.zeros(N, bool)
@@ -207,7 +209,7 @@ def _ckpt_roundtrip(orc, case, interval, starts, rows, heads=None):
     H = case["H"]
     hs = np.arange(H) if heads is None else np.asarray(heads)
     fill = synth.filler_bits((rows, H, HD, HD), 7)
-    ck = dev_bf16(fill)
+    ck = pool_dev(case, fill)
     pool, out = run_prefill(case, checkpoints=ck, ckpt_starts=starts, ckpt_interval=interval)
     check_prefill(orc, case, pool, out, heads=heads)
     ref_ck = np.zeros((rows, len(hs), HD, HD), np.float32)
@@ -224,7 +226,7 @@ def _ckpt_roundtrip(orc, case, interval, starts, rows, heads=None):
             r = int(starts[d]) + i - 1
             if 0 <= r < rows:
                 written[r] = True
-                check_state(got[r][hs], ref_ck[r], f"checkpoint row {r} (doc {d}, i {i})")
+                check_pool(case, got[r][hs], ref_ck[r], f"checkpoint row {r} (doc {d}, i {i})")
     assert np.array_equal(got[~written], fill[~written]), "rows that are not checkpoints changed"
     return written
 
@@ -250,6 +252,21 @@ def test_checkpoints_longer_interval(orc, interval):
     counts = np.diff(case["cu_seqlens"]) // interval
     starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
     _ckpt_roundtrip(orc, case, interval, starts, int(counts.sum()))
+
+
+@pytest.mark.parametrize("docs", ["small", "docs4"])
+def test_fp16_state(orc, docs):
+    """fp16 initial and final states (state_dtype 1): ragged documents with
+    checkpoints every 16 tokens, and the 4-document set at H = 12."""
+    if docs == "small":
+        case = synth.fp16_state(synth.prefill_case(SMALL_DOCS, H=3, seed=synth.seed_for(4, 3, 22)))
+        counts = np.diff(case["cu_seqlens"]) // 16
+        starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
+        _ckpt_roundtrip(orc, case, 16, starts, int(counts.sum()))
+    else:
+        case = synth.fp16_state(synth.prefill_case(synth.DOCS_4, H=12))
+        pool, out = run_prefill(case)
+        check_prefill(orc, case, pool, out)
 
 
 def test_checkpoints_full_h12(orc):

@@ -11,8 +11,8 @@ import numpy as np
 import pytest
 
 from gated_delta_rule_step_amd import synth
-from tests.helpers import (HD, bits, check_gcache, check_out, check_state, compact_slots, dev,
-                           dev_bf16, f32, split_qkv)
+from tests.helpers import (HD, bits, check_gcache, check_out, check_pool, check_state,
+                           compact_slots, dev, dev_bf16, f32, pool_dev, pool_vals, split_qkv)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -35,16 +35,19 @@ def _tok_arrays(qkv, gate, beta, H):
 
 
 def build_case(orc, B, T, w_ring=16, flush_min=None, fold_p=0.0, hist_max=None, N=1024, H=12,
-               workload=3, inactive_frac=0.0, seed=None):
-    """A verify case whose live ring history comes from the oracle."""
+               workload=3, inactive_frac=0.0, seed=None, state_dtype=0):
+    """A verify case whose live ring history comes from the oracle (state_dtype
+    1: fp16 checkpoints)."""
     case = synth.verify_case(B=B, T=T, N=N, H=H, w_ring=w_ring, flush_min=flush_min,
                              fold_p=fold_p, hist_max=hist_max, workload=workload,
                              inactive_frac=inactive_frac, seed=seed)
+    if state_dtype:
+        case = synth.fp16_state(case)
     R = case["R"]
     slots, cidx = compact_slots(case["idx"], N)
     case["slots"], case["cidx"] = slots, cidx
     # Oracle view: compact pool / rings over the active rows' slots.
-    cpool = np.ascontiguousarray(f32(case["pool"][slots]))
+    cpool = np.ascontiguousarray(pool_vals(case, case["pool"][slots]))
     n = len(slots)
     kc = np.zeros((n, H, R, HD), np.float32)
     uc = np.zeros((n, H, R, HD), np.float32)
@@ -88,7 +91,7 @@ def run_gpu(case, flush_min=None, qkv=None, gate=None, beta=None, T=None, hist=N
     W = H * HD
     qkv = dev_bf16(case["qkv"] if qkv is None else qkv)
     if dev_state is None:
-        dev_state = dict(pool=dev_bf16(case["pool"]), kc=dev_bf16(case["k_cache"]),
+        dev_state = dict(pool=pool_dev(case, case["pool"]), kc=dev_bf16(case["k_cache"]),
                          uc=dev_bf16(case["u_cache"]), gc=dev(case["g_cache"]))
     out = torch.full((B, T, W), float("nan"), dtype=torch.bfloat16, device="cuda")
     _kda().kda_verify_ucache_flush(
@@ -119,7 +122,8 @@ def run_oracle(orc, case, flush_min=None, qkv=None, gate=None, beta=None, hist=N
                       case["ogc"], case["hist_len"] if hist is None else hist,
                       case["cache_base"] if base is None else base,
                       case["flush_min"] if flush_min is None else flush_min, case["w_ring"],
-                      bf16_storage=True, real=np.float32, gate_mode=gm)
+                      bf16_storage=True, real=np.float32, gate_mode=gm,
+                      state_dtype=case.get("state_dtype", 0))
 
 
 def check_all(case, st, ref_out, pool0, kc0, uc0, gc0, T=None, hist=None, base=None,
@@ -148,7 +152,7 @@ def check_all(case, st, ref_out, pool0, kc0, uc0, gc0, T=None, hist=None, base=N
         check_state(uc[s][:, rows], case["ouc"][c][:, rows], f"u_cache row {b}")
         check_gcache(gc[s][:, rows], case["ogc"][c][:, rows], f"g_cache row {b}")
         if hist[b] + T >= fm:
-            check_state(pool[s], case["opool"][c], f"folded checkpoint row {b}")
+            check_pool(case, pool[s], case["opool"][c], f"folded checkpoint row {b}")
         else:
             assert np.array_equal(pool[s], pool0[s]), f"checkpoint of row {b} must not change"
     untouched = ~written
@@ -200,6 +204,16 @@ def test_precomputed_gate_conventions(orc, T, fm, p, gate_mode):
     under the raw convention, as a caller switching conventions would see)."""
     case = build_case(orc, 512, T, w_ring=16, flush_min=fm, fold_p=p)
     case = synth.precomputed_gate(case, gate_mode, synth.seed_for(3, 512, 100 + gate_mode))
+    verify_roundtrip(orc, case)
+
+
+@pytest.mark.parametrize("T,fm,p,hist_max,w", [(8, 9, 0.5, None, 16), (8, 9, 0.0, 0, 16),
+                                              (8, 25, 0.0, 24, 32)])
+def test_fp16_checkpoints(orc, T, fm, p, hist_max, w):
+    """fp16 checkpoints (state_dtype 1) at B = 512: the checkpoint product on
+    fp16 MFMA operands, folds stored as binary16, rings still bf16."""
+    case = build_case(orc, 512, T, w_ring=w, flush_min=fm, fold_p=p, hist_max=hist_max,
+                      state_dtype=1)
     verify_roundtrip(orc, case)
 
 

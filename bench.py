@@ -50,23 +50,23 @@ N_SLOTS = 1024
 # only for the kernel sources the counters were taken on: the digest below
 # turns it into null once those sources change.
 COUNTED_TRAFFIC = {
-    "kda::decode_kernel<8, true, true>": dict(
+    "kda::decode_kernel<8, true, 0, false>": dict(
         sources=("gated_delta_rule_step_amd/csrc/kda_decode.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
-        sha256=("a629490627c39e46695ab5c0e93098d616ab9c1a1e2ba39e18dbfc59c4904ace",
-                "9263cc848eebfe534d02cd8eacff54653d6af454b497328dc8bab1bf3291a3fb",
+        sha256=("9b97d6492c4a548912fabff38b0dd8b97a2d11609c57edece98326fbd0ea49f8",
+                "6f2f73dc89b2f8219a4424f049b380789f8f175496a5af2d45a2e2c54e5fb750",
                 "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
-        fetch_kib=96394.250, write_kib=188166.664, fetch_scale=2.0, write_scale=1.0),
+        fetch_kib=96395.945, write_kib=188166.828, fetch_scale=2.0, write_scale=1.0),
     # T = 8 verify, B = 512, bare checkpoint (the --mode profile sequence)
-    "kda::verify_kernel<true, true, true>": dict(
+    "kda::verify_kernel<true, true, 0, false>": dict(
         sources=("gated_delta_rule_step_amd/csrc/kda_verify.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
-        sha256=("f6d95bf4a17745085762d0d5d02fd4308b206fda5736651a4546c44cb95dee91",
-                "9263cc848eebfe534d02cd8eacff54653d6af454b497328dc8bab1bf3291a3fb",
+        sha256=("78dc39bd714cef50017ef31fc73f42b2888d0c2c2d3b61853749b2e600bc97b1",
+                "6f2f73dc89b2f8219a4424f049b380789f8f175496a5af2d45a2e2c54e5fb750",
                 "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
-        fetch_kib=123754.672, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),
+        fetch_kib=123782.234, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),
 }
 
 
@@ -157,6 +157,11 @@ def time_graphs(calls, steps, warmup, torch, min_warm_s=0.0):
 
 def bf16_dev(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def fp16_pools(torch, pools):
+    """The same two pools with fp16 state elements (state_dtype 1)."""
+    return [p.to(torch.float16) for p in pools]
 
 
 def make_pools(torch, synth):
@@ -282,7 +287,7 @@ class PrefillSetup:
     A_log U(-1, 1), dt_bias N(0, 0.1), initial states N(0, 0.05) in a pool of
     2 slots per document)."""
 
-    def __init__(self, lens, H, torch, kda, synth, gate_mode=0, ckpt_interval=0):
+    def __init__(self, lens, H, torch, kda, synth, gate_mode=0, ckpt_interval=0, state_fp16=False):
         self.lens, self.H, self.gate_mode = tuple(lens), H, gate_mode
         n_docs, T, W = len(lens), int(sum(lens)), H * 128
         gen = torch.Generator(device="cuda")
@@ -305,6 +310,8 @@ class PrefillSetup:
         self.dtb = torch.randn(H * 128, generator=gen, device="cuda") * 0.1
         N = 2 * n_docs
         self.pool = randn(N, H, 128, 128, std=0.05)
+        if state_fp16:
+            self.pool = self.pool.to(torch.float16)
         self.idx = torch.randperm(N, generator=gen, device="cuda")[:n_docs].to(torch.int32)
         cu = np.zeros(n_docs + 1, np.int32)
         cu[1:] = np.cumsum(lens)
@@ -321,7 +328,7 @@ class PrefillSetup:
             self.ck_rows = int(counts.sum())
             starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
             self.ck_starts = torch.from_numpy(starts).cuda()
-            self.ck = torch.empty((self.ck_rows, H, 128, 128), dtype=torch.bfloat16,
+            self.ck = torch.empty((self.ck_rows, H, 128, 128), dtype=self.pool.dtype,
                                   device="cuda")
         self.kda = kda
 
@@ -451,16 +458,20 @@ def main():
             log(f"bench: {points[-1]}")
         points.append(dict(kind="decode", B=B, T=1, us_per_call=round(us_ev, 3),
                            GBps=round(gbs, 1), hbm_frac=round(gbs / wm.HBM_PEAK_GBS, 4)))
-        # the other gate conventions at the headline size
-        for gm, gname in ((3, "pre-computed g and beta"), (4, "per-head gate (GDN-style)")):
-            sp = DecodeSetup(B, torch, kda, synth, pools, gate_mode=gm)
+        # the other gate conventions and the fp16 state at the headline size
+        f16 = fp16_pools(torch, pools)
+        for gm, variant, pp in ((3, dict(gate="pre-computed g and beta"), pools),
+                                (4, dict(gate="per-head gate (GDN-style)"), pools),
+                                (0, dict(state="fp16"), f16)):
+            sp = DecodeSetup(B, torch, kda, synth, pp, gate_mode=gm)
             _, e = time_graphs(sp.calls(), args.steps, args.warmup, torch, min_warm_s=0.3)
             us = e * 1e3 / args.steps
             nb = wm.decode_bytes(sp.n_active, B - sp.n_active)
-            points.append(dict(kind="decode", B=B, T=1, gate=gname,
+            points.append(dict(kind="decode", B=B, T=1, **variant,
                                us_per_call=round(us, 3), GBps=round(nb / (us * 1e-6) / 1e9, 1),
                                hbm_frac=round(nb / (us * 1e-6) / 1e9 / wm.HBM_PEAK_GBS, 4)))
             log(f"bench: {points[-1]}")
+        del f16
         rings = make_rings(torch, synth)
         vcfgs = [
             dict(label="T=8 bare (0% fold)", T=8, hist_max=0),
@@ -471,13 +482,17 @@ def main():
             dict(label="T=8 W32 fm=25 hist~U{0..24}", T=8, w_ring=32, flush_min=25, hist_max=24),
             dict(label="T=8 bare, pre-computed gate and beta", T=8, hist_max=0, gate_mode=3),
             dict(label="T=8 fm=9 50% fold, per-head gate", T=8, fold_p=0.5, gate_mode=4),
+            dict(label="T=8 bare, fp16 checkpoints", T=8, hist_max=0, fp16=True),
+            dict(label="T=8 fm=9 100% fold, fp16 checkpoints", T=8, fold_p=1.0, fp16=True),
         ]
+        f16 = fp16_pools(torch, pools)
         for Bv in (1, 32, 512):
             for cfg in vcfgs:
                 if Bv != 512 and cfg["label"] not in ("T=8 bare (0% fold)", "T=8 fm=9 100% fold"):
                     continue
-                kw = {k: v for k, v in cfg.items() if k not in ("label", "T")}
-                vs = VerifySetup(Bv, cfg["T"], torch, kda, synth, pools, rings, **kw)
+                kw = {k: v for k, v in cfg.items() if k not in ("label", "T", "fp16")}
+                vs = VerifySetup(Bv, cfg["T"], torch, kda, synth, f16 if cfg.get("fp16") else pools,
+                                 rings, **kw)
                 st = max(args.steps, 256 if Bv < 512 else 100)
                 _, e = time_graphs(vs.calls(), st, args.warmup, torch, min_warm_s=0.3)
                 us = e * 1e3 / st
@@ -485,7 +500,7 @@ def main():
                 fl = wm.verify_flops(cfg["T"], vs.hist)
                 extra = {}
                 if Bv == 512 and cfg["label"] == "T=8 bare (0% fold)":
-                    extra["traffic_bytes"] = counted_traffic("kda::verify_kernel<true, true, true>")
+                    extra["traffic_bytes"] = counted_traffic("kda::verify_kernel<true, true, 0, false>")
                 points.append(dict(kind="verify", B=Bv, label=cfg["label"],
                                    fold_frac=round(float(np.mean(vs.fold)), 3),
                                    mean_hist=round(float(np.mean(vs.hist)), 2),
@@ -495,17 +510,17 @@ def main():
                                    TFLOPs=round(fl / (us * 1e-6) / 1e12, 2), **extra))
                 log(f"bench: {points[-1]}")
                 del vs
-        del rings
+        del rings, f16
         torch.cuda.empty_cache()
-        pcfgs = [(name, lens, Hp, 0, 0)
-                 for name, lens in (("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4),
-                                    ("14-doc mix, 16384 tokens", synth.DOCS_14))
+        d4 = ("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4)
+        pcfgs = [(name, lens, Hp, 0, 0, False)
+                 for name, lens in (d4, ("14-doc mix, 16384 tokens", synth.DOCS_14))
                  for Hp in (64, 12)]
-        pcfgs.append(("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4, 12, 3, 0))
-        pcfgs.append(("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4, 12, 4, 0))
-        pcfgs.append(("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4, 12, 0, 64))
-        for name, lens, Hp, gm, cki in pcfgs:
-            ps = PrefillSetup(lens, Hp, torch, kda, synth, gate_mode=gm, ckpt_interval=cki)
+        pcfgs += [(*d4, 12, 3, 0, False), (*d4, 12, 4, 0, False), (*d4, 12, 0, 64, False),
+                  (*d4, 12, 0, 0, True)]
+        for name, lens, Hp, gm, cki, sf16 in pcfgs:
+            ps = PrefillSetup(lens, Hp, torch, kda, synth, gate_mode=gm, ckpt_interval=cki,
+                              state_fp16=sf16)
             st = max(10, min(args.steps, 50))
             _, e = time_graphs(ps.calls(), st, 2, torch, min_warm_s=0.3)
             us = e * 1e3 / st
@@ -516,6 +531,8 @@ def main():
                 if gm else {}
             if cki:
                 extra["checkpoints"] = f"every {cki} tokens ({ps.ck_rows} rows)"
+            if sf16:
+                extra["state"] = "fp16"
             points.append(dict(kind="prefill", H=Hp, docs=name, tokens=int(sum(lens)),
                                **extra, us_per_call=round(us, 1),
                                Mtok_per_s=round(sum(lens) / (us * 1e-6) / 1e6, 2),
@@ -552,8 +569,8 @@ def main():
                    "B": B, "H": H, "T": 1, "pool_slots": N_SLOTS, "device": dev_name},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": wm.HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / wm.HBM_PEAK_GBS, 4),
-                     "traffic": counted_traffic("kda::decode_kernel<8, true, true>"),
-                     "kernel": "kda::decode_kernel<8, true, true>",
+                     "traffic": counted_traffic("kda::decode_kernel<8, true, 0, false>"),
+                     "kernel": "kda::decode_kernel<8, true, 0, false>",
                      "kernel_us_avg": round(us_ev, 3), "algorithmic_bytes": nbytes},
         "cpu_baseline": cpu,
         "points": points,

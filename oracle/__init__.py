@@ -24,6 +24,11 @@ state_dtype (decode, verify, prefill): 0 stores the state (pool write-back, fold
 checkpoint, prefill final and intermediate states) in bf16, 1 in fp16 (round to
 nearest even, written from the binary16 definition); outputs and ring rows stay
 bf16. Pool inputs are passed as their exact values either way.
+
+Prefill hand-off (ring_tail > 0, a reading): a document's last tokens, at most
+those after its last 16-token boundary and at most ring_tail, go to the verify
+ring as history entries (k_hat, u, cumulative G from the stored state), and the
+pool slot receives the state before them.
 """
 from __future__ import annotations
 
@@ -215,11 +220,16 @@ def _prefill_args(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, sc
 
 def prefill(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,
             use_initial_state=True, bf16_storage=True, real=np.float32, gate_mode=0,
-            checkpoints=None, checkpoint_starts=None, checkpoint_interval=16, state_dtype=0):
+            checkpoints=None, checkpoint_starts=None, checkpoint_interval=16, state_dtype=0,
+            ring=None, cache_base=None, ring_tail=0):
     """Token-by-token varlen prefill. q/k/graw [Ttot,H,K], v [Ttot,H,V], beta_logit [Ttot,H],
     cu int32 [n_docs+1], idx int32 [n_docs], pool [N,H,V,K] updated in place. -> out [Ttot,H,V].
     checkpoints [rows,H,V,K] (updated in place) with checkpoint_starts int64 [n_docs]: the
-    state after every checkpoint_interval tokens of each active document."""
+    state after every checkpoint_interval tokens of each active document.
+    ring = (k_cache [N,H,R,K], u_cache [N,H,R,V], g_cache [N,H,R,K]), updated in place, with
+    cache_base int32 [n_docs] and ring_tail > 0: each active document hands its last
+    min(ring_tail, tokens after its last 16-token boundary) tokens to the ring as history
+    entries, and the pool receives the state before them (see handoff_tail)."""
     out = np.zeros((q.shape[0], q.shape[1], v.shape[2]), real)
     f = getattr(lib(), "orc_prefill_tbt_" + _suffix(real))
     if checkpoints is None:
@@ -231,8 +241,26 @@ def prefill(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, p
     f(*_prefill_args(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool,
                      idx, use_initial_state, out, real), ctypes.c_int(1 if bf16_storage else 0),
       ctypes.c_int(gate_mode), ck, ctypes.c_int64(rows), starts,
-      ctypes.c_int(int(checkpoint_interval)), ctypes.c_int(1 if state_dtype == 1 else 0))
+      ctypes.c_int(int(checkpoint_interval)), ctypes.c_int(1 if state_dtype == 1 else 0),
+      *_ring_args(ring, cache_base, ring_tail, real))
     return out
+
+
+def _ring_args(ring, cache_base, ring_tail, real):
+    if not ring_tail:
+        return (_rp(None, real), _rp(None, real), _rp(None, real), ctypes.c_int(0), _I32P(),
+                ctypes.c_int(0))
+    kc, uc, gc = ring
+    return (_rp(kc, real), _rp(uc, real), _rp(gc, real), ctypes.c_int(kc.shape[2]),
+            _ip(cache_base), ctypes.c_int(int(ring_tail)))
+
+
+def handoff_tail(length, ring_tail):
+    """Tokens a document of `length` tokens hands to the ring: at most those after
+    its last 16-token boundary, and at most ring_tail."""
+    if length <= 0 or ring_tail <= 0:
+        return 0
+    return min(ring_tail, length - 16 * ((length - 1) // 16))
 
 
 def prefill_chunked(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, idx,

@@ -425,31 +425,52 @@ void verify(int B, int T, int H, int K, int V, const Real* q, const Real* k, con
 // after its first i * interval tokens, i = 1 .. floor(len / interval), into
 // checkpoint row ckpt_starts[d] + i - 1 (rows outside [0, ckpt_rows) are
 // skipped), rounded like the final state.
+// Hand-off to speculative decoding (a reading: the prefill leaves each
+// document in the form the verify step resumes from, a checkpoint plus ring
+// history, as in "feat(kda): ReplaySSM verify+flush decode kernel for Kimi K3
+// (KDA)", "Caching"): with ring_tail > 0 an active document of length len hands
+// its last r = min(ring_tail, len - 16 * floor((len - 1) / 16)) tokens (at most
+// the tokens after its last 16-token boundary, the prefill's chunk) to the
+// ring: the slot receives the state after the first len - r tokens, and tail
+// token j = 0 .. r-1 writes history entry j into ring row (cache_base[d] + j)
+// mod R of the slot: k_hat, u (the token's correction) and G, the cumulative
+// log-decay of tail tokens 0..j. Outputs are unchanged; checkpoints only cover
+// the first len - r tokens. A document whose cache_base lies outside [0, R) is
+// inactive when ring_tail > 0.
 // q, k, graw: [Ttot][H][K]; v: [Ttot][H][V]; beta_logit: [Ttot][H];
 // cu: [n_docs + 1]; idx: [n_docs]; pool: [N][H][V][K]; out: [Ttot][H][V];
-// ckpt: [ckpt_rows][H][V][K]; ckpt_starts: [n_docs].
+// ckpt: [ckpt_rows][H][V][K]; ckpt_starts: [n_docs]; kc, gc: [N][H][R][K];
+// uc: [N][H][R][V]; cache_base: [n_docs].
 template <class Real>
 void prefill_tbt(int n_docs, int H, int K, int V, const int32_t* cu, const Real* q,
                  const Real* k, const Real* v, const Real* graw, const Real* beta_logit,
                  const Real* a_log, const Real* dt_bias, Real lower_bound, Real scale,
                  Real* pool, int64_t N, const int32_t* idx, int use_initial_state, Real* out,
                  int bf16_storage, int gate_mode, Real* ckpt, int64_t ckpt_rows,
-                 const int64_t* ckpt_starts, int interval, int state_fp16) {
+                 const int64_t* ckpt_starts, int interval, int state_fp16, Real* kc, Real* uc,
+                 Real* gc, int R, const int32_t* cache_base, int ring_tail) {
   const int64_t KV = i64(K) * V;
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int d = 0; d < n_docs; ++d) {
     for (int h = 0; h < H; ++h) {
       const int t0 = cu[d], t1 = cu[d + 1];
-      if (!slot_active(idx[d], N)) {
+      const int len = t1 - t0;
+      const bool ring_ok = ring_tail == 0 || (cache_base[d] >= 0 && cache_base[d] < R);
+      if (!slot_active(idx[d], N) || !ring_ok) {
         for (int t = t0; t < t1; ++t)
           for (int r = 0; r < V; ++r) out[(i64(t) * H + h) * V + r] = 0;
         continue;
       }
       Real* slot = pool + (i64(idx[d]) * H + h) * KV;
       if (t1 == t0 && use_initial_state) continue;
+      const int last = len > 0 ? len - 16 * ((len - 1) / 16) : 0;
+      const int tail = std::min(ring_tail, last);
+      const int kept = len - tail;  // tokens whose state the slot receives
       std::vector<Real> S(KV, static_cast<Real>(0));
       if (use_initial_state) std::copy(slot, slot + KV, S.begin());
-      std::vector<Real> qh(K), kh(K), g(K);
+      if (kept == 0)
+        for (int64_t e = 0; e < KV; ++e) slot[e] = store_state(S[e], bf16_storage, state_fp16);
+      std::vector<Real> qh(K), kh(K), g(K), u(V), G(K, static_cast<Real>(0));
       for (int t = t0; t < t1; ++t) {
         const int64_t tk = (i64(t) * H + h) * K;
         const int64_t tg = (i64(t) * H + h) * gate_width(K, gate_mode);
@@ -459,18 +480,32 @@ void prefill_tbt(int n_docs, int H, int K, int V, const int32_t* cu, const Real*
                        lower_bound, gate_mode, qh.data(), kh.data(), g.data(), &beta);
         Real* o = out + (i64(t) * H + h) * V;
         step<Real>(K, V, S.data(), qh.data(), kh.data(), v + (i64(t) * H + h) * V, g.data(),
-                   beta, scale, o, nullptr);
+                   beta, scale, o, u.data());
         for (int r = 0; r < V; ++r) o[r] = store(o[r], bf16_storage);
         const int done = t - t0 + 1;  // tokens of the document consumed
-        if (ckpt && done % interval == 0) {
+        if (ckpt && done % interval == 0 && done <= kept) {
           const int64_t row = ckpt_starts[d] + done / interval - 1;
           if (row >= 0 && row < ckpt_rows) {
             Real* c = ckpt + (row * H + h) * KV;
             for (int64_t e = 0; e < KV; ++e) c[e] = store_state(S[e], bf16_storage, state_fp16);
           }
         }
+        if (done == kept)
+          for (int64_t e = 0; e < KV; ++e) slot[e] = store_state(S[e], bf16_storage, state_fp16);
+        if (done > kept) {  // a tail token: ring history entry done - kept - 1
+          const int64_t sh = i64(idx[d]) * H + h;
+          const int64_t row = (cache_base[d] + (done - kept - 1)) % R;
+          Real* kr = kc + (sh * R + row) * K;
+          Real* gr = gc + (sh * R + row) * K;
+          Real* ur = uc + (sh * R + row) * V;
+          for (int c = 0; c < K; ++c) {
+            G[c] += g[c];
+            kr[c] = store(kh[c], bf16_storage);
+            gr[c] = G[c];
+          }
+          for (int r = 0; r < V; ++r) ur[r] = store(u[r], bf16_storage);
+        }
       }
-      for (int64_t e = 0; e < KV; ++e) slot[e] = store_state(S[e], bf16_storage, state_fp16);
     }
   }
 }
@@ -641,10 +676,12 @@ void prefill_chunked(int n_docs, int H, int K, int V, const int32_t* cu, const R
       const Real* dt_bias, Real lower_bound, Real scale, Real* pool, int64_t N,               \
       const int32_t* idx, int use_initial_state, Real* out, int bf16_storage,                 \
       int gate_mode, Real* ckpt, int64_t ckpt_rows, const int64_t* ckpt_starts,               \
-      int interval, int state_fp16) {                                                         \
+      int interval, int state_fp16, Real* kc, Real* uc, Real* gc, int R,                      \
+      const int32_t* cache_base, int ring_tail) {                                             \
     prefill_tbt<Real>(n_docs, H, K, V, cu, q, k, v, graw, beta_logit, a_log, dt_bias,         \
                       lower_bound, scale, pool, N, idx, use_initial_state, out, bf16_storage, \
-                      gate_mode, ckpt, ckpt_rows, ckpt_starts, interval, state_fp16);         \
+                      gate_mode, ckpt, ckpt_rows, ckpt_starts, interval, state_fp16, kc, uc,  \
+                      gc, R, cache_base, ring_tail);                                          \
   }                                                                                           \
   extern "C" void orc_prefill_chunked_##SUF(                                                  \
       int n_docs, int H, int K, int V, const int32_t* cu, const Real* q, const Real* k,       \

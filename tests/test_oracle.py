@@ -935,3 +935,149 @@ def test_fp16_state_rounds_only_the_state_storage_points(orc):
                 checkpoint_starts=starts, checkpoint_interval=16)
     np.testing.assert_array_equal(qa[p["idx"]], _f16(qb[p["idx"]]))
     np.testing.assert_array_equal(ck_a, _f16(ck_b))
+
+
+# ---------------------------------------------------------------------------
+# Prefill hand-off to speculative decoding (reading): a document's last
+# min(ring_tail, tokens after its last 16-token boundary) tokens become ring
+# history entries ([verify] "Caching": k_hat, u and the cumulative log-decay G)
+# and the pool receives the state before them.
+
+def _ring_nan(N, H, R=32):
+    return tuple(np.full((N, H, R, 128), np.nan) for _ in range(3))
+
+
+@pytest.mark.parametrize("ring_tail,expect", [(16, [0, 5, 16, 1, 8, 4]),
+                                              (7, [0, 5, 7, 1, 7, 4]),
+                                              (3, [0, 3, 3, 1, 3, 3])])
+def test_handoff_ring_replays_to_the_full_prefill_state(orc, ring_tail, expect):
+    """The checkpoint plus the handed-off ring rows replay to the final state
+    of the same prefill without hand-off; outputs are bitwise unchanged; each
+    (slot, head) ring holds exactly the expected number of rows, at
+    cache_base onwards (wrapping), and nothing else is written."""
+    rng = _rng(240 + ring_tail)
+    lens = (0, 5, 16, 17, 40, 100)
+    H = 2
+    d = _prefill_inputs(rng, lens, H=H)
+    N = d["pool"].shape[0]
+    base = np.array([3, 30, 25, 0, 31, 17], np.int32)
+    p0 = d["pool"].copy()
+    o0 = orc.prefill(*_pf_args(d), p0, d["idx"], bf16_storage=False, real=F64)
+    p1 = d["pool"].copy()
+    ring = _ring_nan(N, H)
+    o1 = orc.prefill(*_pf_args(d), p1, d["idx"], bf16_storage=False, real=F64, ring=ring,
+                     cache_base=base, ring_tail=ring_tail)
+    np.testing.assert_array_equal(o1, o0)
+    kc, uc, gc = ring
+    for doc, n in enumerate(lens):
+        s = d["idx"][doc]
+        r = expect[doc]
+        assert orc.handoff_tail(n, ring_tail) == r
+        for h in range(H):
+            rows = [(int(base[doc]) + j) % 32 for j in range(r)]
+            filled = ~np.isnan(kc[s, h, :, 0])
+            assert sorted(np.nonzero(filled)[0].tolist()) == sorted(rows)
+            assert np.array_equal(filled, ~np.isnan(uc[s, h, :, 0]))
+            assert np.array_equal(filled, ~np.isnan(gc[s, h, :, 0]))
+            S = orc.replay(p1[s, h], np.nan_to_num(kc[s, h]), np.nan_to_num(uc[s, h]),
+                           np.nan_to_num(gc[s, h]), int(base[doc]), r, real=F64)
+            np.testing.assert_allclose(S, p0[s, h], rtol=1e-10, atol=1e-12)
+            if r:  # G is a cumulative log-decay: non-increasing over the entries
+                G = gc[s, h, rows]
+                assert np.all(np.diff(G, axis=0) <= 0) and np.all(G <= 0)
+    untouched = np.setdiff1d(np.arange(N), d["idx"])
+    assert np.all(np.isnan(kc[untouched]))
+    np.testing.assert_array_equal(p1[untouched], d["pool"][untouched])
+
+
+@pytest.mark.parametrize("T,fm,ring_tail", [(8, 9, 8), (4, 13, 8)])
+def test_handoff_then_verify_equals_the_longer_prefill(orc, T, fm, ring_tail):
+    """Prefill with hand-off, then a verify call on T draft tokens from the
+    handed-off ring (hist = the tail, W16), gives the outputs the prefill of
+    the documents with the draft tokens appended gives at those positions;
+    a folding call commits the no-hand-off final state, and a non-folding
+    call leaves a ring that replays to the longer prefill's final state."""
+    rng = _rng(250 + T)
+    lens = (40, 37, 3, 16, 0, 32)
+    H = 2
+    n_docs = len(lens)
+    d = _prefill_inputs(rng, lens, H=H)
+    dr = _prefill_inputs(rng, (T,) * n_docs, H=H)  # draft tokens, doc by doc
+    base = np.array([5, 31, 0, 12, 7, 20], np.int32)
+    hist = np.array([orc.handoff_tail(n, ring_tail) for n in lens], np.int32)
+    pool = d["pool"].copy()
+    ring = tuple(np.zeros((pool.shape[0], H, 32, 128)) for _ in range(3))
+    orc.prefill(*_pf_args(d), pool, d["idx"], bf16_storage=False, real=F64, ring=ring,
+                cache_base=base, ring_tail=ring_tail)
+    drafts = {n: np.ascontiguousarray(dr[n].reshape((n_docs, T) + dr[n].shape[1:]))
+              for n in ("q", "k", "v", "graw", "beta_logit")}
+    out_v = orc.verify(drafts["q"], drafts["k"], drafts["v"], drafts["graw"],
+                       drafts["beta_logit"], d["a_log"], d["dt_bias"], -5.0, 1.0, pool,
+                       d["idx"], *ring, hist, base, fm, 16, bf16_storage=False, real=F64)
+    # the longer prefill: each document followed by its draft tokens
+    cu = np.zeros(n_docs + 1, np.int32)
+    cu[1:] = np.cumsum(np.array(lens) + T)
+    cat = {}
+    for n in ("q", "k", "v", "graw", "beta_logit"):
+        parts = []
+        for doc in range(n_docs):
+            parts.append(d[n][d["cu"][doc]:d["cu"][doc + 1]])
+            parts.append(drafts[n][doc])
+        cat[n] = np.ascontiguousarray(np.concatenate(parts))
+    long_pool = d["pool"].copy()
+    o_long = orc.prefill(cu, cat["q"], cat["k"], cat["v"], cat["graw"], cat["beta_logit"],
+                         d["a_log"], d["dt_bias"], -5.0, 1.0, long_pool, d["idx"],
+                         bf16_storage=False, real=F64)
+    short_pool = d["pool"].copy()
+    orc.prefill(*_pf_args(d), short_pool, d["idx"], bf16_storage=False, real=F64)
+    for doc in range(n_docs):
+        s = d["idx"][doc]
+        np.testing.assert_allclose(out_v[doc], o_long[cu[doc] + lens[doc]:cu[doc + 1]],
+                                   rtol=1e-9, atol=1e-11)
+        fold = hist[doc] + T >= fm
+        for h in range(H):
+            if fold:
+                np.testing.assert_allclose(pool[s, h], short_pool[s, h], rtol=1e-10, atol=1e-12)
+            else:
+                S = orc.replay(pool[s, h], ring[0][s, h], ring[1][s, h], ring[2][s, h],
+                               int(base[doc]), int(hist[doc]) + T, real=F64)
+                np.testing.assert_allclose(S, long_pool[s, h], rtol=1e-9, atol=1e-11)
+    # both branches are exercised: every document folds at (8, 9) but the
+    # empty one, none at (4, 13)
+    assert np.sum(hist + T >= fm) == (n_docs - 1 if fm == 9 else 0)
+
+
+def test_handoff_checkpoints_stop_before_the_tail_and_bad_base_is_inactive(orc):
+    """Checkpoints cover only the tokens before the tail (a checkpoint at the
+    document's end is not written when tokens were handed off); a document
+    whose cache_base lies outside [0, R) writes zero outputs and nothing
+    else."""
+    rng = _rng(260)
+    lens = (64, 20, 33)
+    H = 2
+    d = _prefill_inputs(rng, lens, H=H)
+    N = d["pool"].shape[0]
+    starts = np.array([0, 4, 5], np.int64)
+    ck0 = np.full((8, H, 128, 128), -3.0)
+    ck1 = ck0.copy()
+    p0, p1 = d["pool"].copy(), d["pool"].copy()
+    base = np.array([0, 9, -1], np.int32)  # doc 2: bad base
+    o0 = orc.prefill(*_pf_args(d), p0, d["idx"], bf16_storage=False, real=F64, checkpoints=ck0,
+                     checkpoint_starts=starts, checkpoint_interval=16)
+    ring = _ring_nan(N, H)
+    o1 = orc.prefill(*_pf_args(d), p1, d["idx"], bf16_storage=False, real=F64, checkpoints=ck1,
+                     checkpoint_starts=starts, checkpoint_interval=16, ring=ring,
+                     cache_base=base, ring_tail=16)
+    # doc 0 (64 tokens, tail 16): rows 0..2 as before, row 3 (token 64) not written
+    np.testing.assert_array_equal(ck1[0:3], ck0[0:3])
+    assert np.all(ck0[3] != -3.0) and np.all(ck1[3] == -3.0)
+    # doc 1 (20 tokens, tail 4): row 4 (token 16) as before
+    np.testing.assert_array_equal(ck1[4], ck0[4])
+    # doc 2: inactive
+    t0, t1 = d["cu"][2], d["cu"][3]
+    assert np.all(o1[t0:t1] == 0) and np.any(o0[t0:t1] != 0)
+    assert np.all(ck1[5:] == -3.0)
+    s2 = d["idx"][2]
+    np.testing.assert_array_equal(p1[s2], d["pool"][s2])
+    assert np.all(np.isnan(ring[0][s2]))
+    np.testing.assert_array_equal(o1[:t0], o0[:t0])

@@ -287,7 +287,8 @@ class PrefillSetup:
     A_log U(-1, 1), dt_bias N(0, 0.1), initial states N(0, 0.05) in a pool of
     2 slots per document)."""
 
-    def __init__(self, lens, H, torch, kda, synth, gate_mode=0, ckpt_interval=0, state_fp16=False):
+    def __init__(self, lens, H, torch, kda, synth, gate_mode=0, ckpt_interval=0, state_fp16=False,
+                 ring_tail=0):
         self.lens, self.H, self.gate_mode = tuple(lens), H, gate_mode
         n_docs, T, W = len(lens), int(sum(lens)), H * 128
         gen = torch.Generator(device="cuda")
@@ -303,11 +304,11 @@ class PrefillSetup:
             self.g = (u * 6.5 - 6.0).to(torch.bfloat16)
         if gate_mode & 2:  # beta itself, U(0, 1)
             self.beta = torch.rand(T, H, generator=gen, device="cuda").to(torch.bfloat16)
-        if gate_mode & 4:  # one gate value per token and head
-            self.g = randn(T, H)
-            self.dtb = torch.randn(H, generator=gen, device="cuda") * 0.1
         self.a_log = torch.rand(H, generator=gen, device="cuda") * 2.0 - 1.0
         self.dtb = torch.randn(H * 128, generator=gen, device="cuda") * 0.1
+        if gate_mode & 4:  # one gate value (and dt_bias) per token and head
+            self.g = randn(T, H)
+            self.dtb = torch.randn(H, generator=gen, device="cuda") * 0.1
         N = 2 * n_docs
         self.pool = randn(N, H, 128, 128, std=0.05)
         if state_fp16:
@@ -330,6 +331,14 @@ class PrefillSetup:
             self.ck_starts = torch.from_numpy(starts).cuda()
             self.ck = torch.empty((self.ck_rows, H, 128, 128), dtype=self.pool.dtype,
                                   device="cuda")
+        # hand-off of each document's last tokens to a 32-row verify ring
+        self.ring_tail, self.ring, self.base = ring_tail, None, None
+        if ring_tail:
+            self.ring = (torch.zeros((N, H, 32, 128), dtype=torch.bfloat16, device="cuda"),
+                         torch.zeros((N, H, 32, 128), dtype=torch.bfloat16, device="cuda"),
+                         torch.zeros((N, H, 32, 128), dtype=torch.float32, device="cuda"))
+            self.base = torch.randint(0, 32, (n_docs,), generator=gen, device="cuda",
+                                      dtype=torch.int32)
         self.kda = kda
 
     def calls(self):
@@ -343,7 +352,8 @@ class PrefillSetup:
                                      s.pool, s.idx, s.out, workspace=s.ws,
                                      gate_mode=s.gate_mode, checkpoints=s.ck,
                                      checkpoint_cu_starts=s.ck_starts,
-                                     checkpoint_interval=s.ck_interval)
+                                     checkpoint_interval=s.ck_interval, ring=s.ring,
+                                     cache_base=s.base, ring_tail=s.ring_tail)
         return [call]
 
 
@@ -513,14 +523,14 @@ def main():
         del rings, f16
         torch.cuda.empty_cache()
         d4 = ("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4)
-        pcfgs = [(name, lens, Hp, 0, 0, False)
+        pcfgs = [(name, lens, Hp, 0, 0, False, 0)
                  for name, lens in (d4, ("14-doc mix, 16384 tokens", synth.DOCS_14))
                  for Hp in (64, 12)]
-        pcfgs += [(*d4, 12, 3, 0, False), (*d4, 12, 4, 0, False), (*d4, 12, 0, 64, False),
-                  (*d4, 12, 0, 0, True)]
-        for name, lens, Hp, gm, cki, sf16 in pcfgs:
+        pcfgs += [(*d4, 12, 3, 0, False, 0), (*d4, 12, 4, 0, False, 0),
+                  (*d4, 12, 0, 64, False, 0), (*d4, 12, 0, 0, True, 0), (*d4, 12, 0, 0, False, 8)]
+        for name, lens, Hp, gm, cki, sf16, rt in pcfgs:
             ps = PrefillSetup(lens, Hp, torch, kda, synth, gate_mode=gm, ckpt_interval=cki,
-                              state_fp16=sf16)
+                              state_fp16=sf16, ring_tail=rt)
             st = max(10, min(args.steps, 50))
             _, e = time_graphs(ps.calls(), st, 2, torch, min_warm_s=0.3)
             us = e * 1e3 / st
@@ -533,6 +543,8 @@ def main():
                 extra["checkpoints"] = f"every {cki} tokens ({ps.ck_rows} rows)"
             if sf16:
                 extra["state"] = "fp16"
+            if rt:
+                extra["handoff"] = f"last {rt} tokens of each document to the verify ring"
             points.append(dict(kind="prefill", H=Hp, docs=name, tokens=int(sum(lens)),
                                **extra, us_per_call=round(us, 1),
                                Mtok_per_s=round(sum(lens) / (us * 1e-6) / 1e6, 2),

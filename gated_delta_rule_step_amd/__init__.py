@@ -41,7 +41,8 @@ _SIGS = {
     "kda_prefill_varlen": (_c.c_int, [_I32, _I64, _I32, _I32, _I32, _P, _P,
                                       _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
                                       _P, _P, _F, _F, _I32, _I32, _P, _I64, _I64, _P, _I32,
-                                      _P, _I64, _P, _I64, _P, _I32, _P, _c.c_size_t, _P]),
+                                      _P, _I64, _P, _I64, _P, _I32, _P, _P, _P, _I32, _P,
+                                      _I32, _P, _c.c_size_t, _P]),
 }
 
 
@@ -216,6 +217,7 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
                        use_initial_state: bool = True, lower_bound: float = -5.0,
                        scale: float = 1.0, gate_mode: int = 0, checkpoints=None,
                        checkpoint_cu_starts=None, checkpoint_interval: int = 16,
+                       ring=None, cache_base=None, ring_tail: int = 0,
                        stream=None) -> None:
     """Varlen prefill. cu_seqlens_host: CPU int32 [n_docs+1]; cu_seqlens: the
     same on the GPU; q, k, v, g_raw, out: bf16 [Ttot, H*128] (token-strided);
@@ -224,7 +226,10 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
     one allocated here for this call. checkpoints: bf16 [rows, H, 128, 128]
     (contiguous) receiving the state after every checkpoint_interval tokens of
     each document at rows checkpoint_cu_starts[d] + i (int64 GPU tensor
-    [n_docs]), or None."""
+    [n_docs]), or None. ring = (k_cache bf16, u_cache bf16, g_cache fp32, each
+    [N, H, R, 128]) with cache_base int32 [n_docs] and ring_tail in 1..16: each
+    document hands its last prefill_handoff_hist(...)[d] tokens to the ring at
+    rows cache_base[d] onwards, and its slot receives the state before them."""
     import torch
     if cu_seqlens_host.dtype != torch.int32 or cu_seqlens_host.is_cuda or \
             not cu_seqlens_host.is_contiguous():
@@ -257,6 +262,19 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
                 not checkpoint_cu_starts.is_cuda or not checkpoint_cu_starts.is_contiguous():
             raise ValueError("checkpoint_cu_starts must be a contiguous int64 GPU tensor")
         ck_rows = checkpoints.shape[0]
+    kc = uc = gc = None
+    R = 0
+    if ring_tail:
+        kc, uc, gc = ring
+        _bf16("k_cache", kc)
+        _bf16("u_cache", uc)
+        _f32("g_cache", gc)
+        _i32("cache_base", cache_base)
+        if not (kc.is_contiguous() and uc.is_contiguous() and gc.is_contiguous()):
+            raise ValueError("ring caches must be contiguous")
+        if N and (kc.shape[:2] != (N, H) or uc.shape[:2] != (N, H) or gc.shape[:2] != (N, H)):
+            raise ValueError("ring caches must be [N, H, R, 128]")
+        R = kc.shape[2]
     cu_h = _P(cu_seqlens_host.data_ptr())
     st = lib().kda_prefill_varlen(
         n_docs, Ttot, H, HEAD_DIM, HEAD_DIM, cu_h, _ptr(cu_seqlens),
@@ -266,5 +284,17 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
         _state_dtype(state_pool), _ptr(state_pool) if N else _P(0), N, slot_stride,
         _ptr(state_indices), 1 if use_initial_state else 0, _ptr(out), out.stride(0),
         _ptr(checkpoints), ck_rows, _ptr(checkpoint_cu_starts), int(checkpoint_interval),
+        _ptr(kc), _ptr(uc), _ptr(gc), R, _ptr(cache_base), int(ring_tail),
         _ptr(workspace), ws_bytes, _stream(stream))
     _check("kda_prefill_varlen", st)
+
+
+def prefill_handoff_hist(cu_seqlens_host, ring_tail: int):
+    """Ring history entries each document hands off (the hist_len of its next
+    verify call): min(ring_tail, tokens after its last 16-token boundary), 0 for
+    an empty document. CPU int32 tensor [n_docs]."""
+    import torch
+    lens = (cu_seqlens_host[1:] - cu_seqlens_host[:-1]).to(torch.int64)
+    last = lens - 16 * torch.div(lens - 1, 16, rounding_mode="floor")
+    return torch.where(lens > 0, torch.clamp(last, max=int(ring_tail)),
+                       torch.zeros_like(lens)).to(torch.int32)

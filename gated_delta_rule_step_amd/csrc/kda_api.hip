@@ -229,7 +229,9 @@ extern "C" kda_status kda_prefill_varlen(
     float scale, int32_t gate_mode, int32_t state_dtype, void* state_pool, int64_t num_slots,
     int64_t slot_stride, const int32_t* state_indices, int32_t use_initial_state, void* out, int64_t out_tok_stride,
     void* checkpoints, int64_t checkpoint_rows, const int64_t* checkpoint_cu_starts,
-    int32_t checkpoint_interval, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int32_t checkpoint_interval, void* k_cache, void* u_cache, float* g_cache, int32_t ring_rows,
+    const int32_t* cache_base, int32_t ring_tail, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
   if (n_docs < 0 || total_tokens < 0 || H < 1 || num_slots < 0) return KDA_ERR_BAD_SHAPE;
   if (K != D || V != D) return KDA_ERR_UNSUPPORTED;
   // 16-token chunks factor each decay weight into two exps of at most 8 |lb|.
@@ -248,7 +250,12 @@ extern "C" kda_status kda_prefill_varlen(
     // checkpoints sit on 16-token chunk boundaries
     if (checkpoint_interval < 16 || checkpoint_interval % 16 != 0) return KDA_ERR_UNSUPPORTED;
   }
+  // the hand-off tail lies inside a document's last 16-token chunk
+  if (ring_tail < 0 || ring_tail > 16) return KDA_ERR_UNSUPPORTED;
+  if (ring_tail > 0 && ring_rows < ring_tail) return KDA_ERR_BAD_SHAPE;
   if (n_docs == 0) return KDA_OK;
+  if (ring_tail > 0 && (!k_cache || !u_cache || !g_cache || !cache_base))
+    return KDA_ERR_NULL_POINTER;
   if (!cu_seqlens || !state_indices) return KDA_ERR_NULL_POINTER;
   if (checkpoints && !checkpoint_cu_starts) return KDA_ERR_NULL_POINTER;
   if (total_tokens > 0 && (!q || !k || !v || !g_raw || !beta_raw || !out))
@@ -299,6 +306,12 @@ extern "C" kda_status kda_prefill_varlen(
   p.ckpt_rows = checkpoints ? checkpoint_rows : 0;
   p.ckpt_starts = checkpoint_cu_starts;
   p.ckpt_interval = checkpoints ? checkpoint_interval : 16;
+  p.k_cache = static_cast<uint16_t*>(k_cache);
+  p.u_cache = static_cast<uint16_t*>(u_cache);
+  p.g_cache = g_cache;
+  p.ring_rows = ring_tail > 0 ? ring_rows : 0;
+  p.cache_base = cache_base;
+  p.ring_tail = ring_tail;
   p.workspace = workspace;
   const bool vec = aligned16(q) && aligned16(k) && aligned16(v) &&
                    gate_vec_ok(gate_mode, g_raw, g_tok_stride, 0) && aligned16(dt_bias) &&

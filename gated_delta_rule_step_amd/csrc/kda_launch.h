@@ -89,6 +89,15 @@ struct PrefillParams {
   int64_t ckpt_rows;
   const int64_t* ckpt_starts;  // [n_docs]
   int32_t ckpt_interval;       // tokens, a multiple of 16
+  // hand-off to the verify ring: each active document's last
+  // min(ring_tail, tokens of its last chunk) tokens become ring history rows
+  // ([num_slots][H][ring_rows][128]) and the pool gets the state before them
+  uint16_t* k_cache;
+  uint16_t* u_cache;
+  float* g_cache;
+  int32_t ring_rows;
+  const int32_t* cache_base;   // [n_docs]
+  int32_t ring_tail;           // 0: no hand-off
   void* workspace;
 };
 

@@ -515,6 +515,121 @@ __global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Hand-off to the verify ring: one 256-thread workgroup per (document, head),
+// run between the preparation and the chain when ring_tail > 0. In a
+// document's last chunk (c tokens, of which the last `tail` are handed off,
+// pe = c - tail) only tokens 0 .. pe-1 may enter the state the chain passes
+// on, so this kernel rewrites that chunk record's state-update operands,
+//   K~_r = exp(Gam_e - Gam_r) k_hat_r (r < pe, else 0),  EG = exp(Gam_e),
+// with Gam_e = Gam_{pe-1} (0 when pe = 0), and writes the tail tokens' ring
+// rows: k_hat (bf16) and G, the log-decay summed from the first tail token.
+// The chain then leaves S after pe tokens, and writes the tail's u rows.
+// k_hat and the gate are computed as the preparation computes them.
+template <bool VEC, int GK>
+__global__ __launch_bounds__(kThreads) void handoff_kernel(PrefillParams p) {
+  constexpr bool GRAW = !(GK & kGatePrecomputed);
+  constexpr bool GHEAD = (GK & kGatePerHead) != 0;
+  __shared__ float kh[C][D];
+  __shared__ float gg[C][D];
+  const int tid = threadIdx.x;
+  const int doc = blockIdx.x;
+  const int h = blockIdx.y;
+  const int64_t t0 = p.cu_seqlens[doc];
+  const int64_t len = int64_t(p.cu_seqlens[doc + 1]) - t0;
+  const int32_t slot = p.state_indices[doc];
+  const int32_t rbase = p.cache_base[doc];
+  if (len == 0 || slot < 0 || int64_t(slot) >= p.num_slots || rbase < 0 ||
+      rbase >= p.ring_rows)
+    return;  // nothing to hand off, or an inactive document
+  const int nchunks = int((len + C - 1) / C);
+  const int c = int(len - int64_t(nchunks - 1) * C);
+  const int tail = min(p.ring_tail, c);
+  const int pe = c - tail;
+
+  // ---- k_hat and g of the chunk's tokens (rows >= c: zeros)
+  {
+    const int tt = tid >> 4;
+    const int c0 = (tid & 15) * 8;
+    const bool valid = tt < c;
+    const TokRaw raw =
+        load_tok<VEC, GHEAD>(p, t0 + int64_t(nchunks - 1) * C + tt, h, c0, valid);
+    float neg_ea = 0.f;
+    float dtb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if constexpr (GRAW) {
+      neg_ea = -fexp(p.A_log[h]);
+      if constexpr (GHEAD) {
+        const float dh = p.dt_bias[h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dtb[e] = dh;
+      } else {
+        load8_f32<VEC>(p.dt_bias + h * D + c0, dtb);
+      }
+    }
+    float k[8], gr[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      k[2 * e] = bf_lo(raw.k[e]);  k[2 * e + 1] = bf_hi(raw.k[e]);
+      gr[2 * e] = bf_lo(raw.g[e]); gr[2 * e + 1] = bf_hi(raw.g[e]);
+    }
+    float sk = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sk = fmaf(k[e], k[e], sk);
+    sk = row16_sum(sk);
+    const float rk = 1.0f / sqrtf(sk + 1e-6f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kh[tt][c0 + e] = k[e] * rk;
+      const float ge = GRAW ? fgate(gr[e] + dtb[e], neg_ea, p.lower_bound)
+                            : gate_given(gr[e], p.lower_bound);
+      gg[tt][c0 + e] = valid ? ge : 0.f;
+    }
+  }
+  __syncthreads();
+  if (tid >= D) return;
+
+  // ---- thread cc: one key channel
+  const int cc = tid;
+  float gam_e = 0.f, acc = 0.f;
+  for (int r = 0; r < pe; ++r) {
+    acc += gg[r][cc];
+    gam_e = acc;
+  }
+  uint8_t* rec = static_cast<uint8_t*>(p.workspace) +
+                 ((doc_slot0(p.cu_seqlens, doc) + nchunks - 1) * p.H + h) * int64_t(kRecBytes);
+  // KT unit (mt, lane = n16 + 16 g4): tokens 4 g4 .. 4 g4 + 3 of key channel
+  // 16 mt + n16, four bf16 hi then four bf16 lo
+  const int mt = cc >> 4, n16 = cc & 15;
+  float gam = 0.f;
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g4 + i;
+      gam += gg[r][cc];
+      const float x = r < pe ? fexp(gam_e - gam) * kh[r][cc] : 0.f;
+      split_bf16(x, hi[i], lo[i]);
+    }
+    const u32x4 w = {uint32_t(hi[0]) | (uint32_t(hi[1]) << 16),
+                     uint32_t(hi[2]) | (uint32_t(hi[3]) << 16),
+                     uint32_t(lo[0]) | (uint32_t(lo[1]) << 16),
+                     uint32_t(lo[2]) | (uint32_t(lo[3]) << 16)};
+    *reinterpret_cast<u32x4*>(rec + kRecKT + (mt * 64 + n16 + 16 * g4) * 16) = w;
+  }
+  reinterpret_cast<float*>(rec + kRecEG)[cc] = fexp(gam_e);
+
+  // ---- ring rows of the tail tokens
+  const int64_t ring0 = (int64_t(slot) * p.H + h) * p.ring_rows;
+  float gt = 0.f;
+  for (int r = pe; r < c; ++r) {
+    gt += gg[r][cc];
+    const int64_t row = ring0 + (rbase + r - pe) % p.ring_rows;
+    p.k_cache[row * D + cc] = to_bf16(kh[r][cc]);
+    p.g_cache[row * D + cc] = gt;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Chain: one 512-thread workgroup per (document, head), documents longest
 // first. Wave w keeps value channels 16w .. 16w+15 of the fp32 state in
 // registers (two waves per SIMD, so one wave's MFMA and LDS latencies overlap
@@ -542,7 +657,9 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
   const int64_t t0 = p.cu_seqlens[doc];
   const int64_t len = int64_t(p.cu_seqlens[doc + 1]) - t0;
   const int32_t slot = p.state_indices[doc];
-  const bool active = slot >= 0 && int64_t(slot) < p.num_slots;
+  const int32_t rbase = p.ring_tail > 0 ? p.cache_base[doc] : 0;
+  const bool active = slot >= 0 && int64_t(slot) < p.num_slots && rbase >= 0 &&
+                      (p.ring_tail == 0 || rbase < p.ring_rows);
 
   if (!active) {  // zero outputs, no state access
     for (int64_t e = tid; e < len * D; e += kChainThreads)
@@ -557,6 +674,11 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
   }
 
   const int nchunks = int((len + C - 1) / C);
+  // hand-off: the last chunk's last `tail` tokens go to the ring; the state
+  // passed on (checkpoints, final) covers the first `kept` tokens
+  const int c_last = int(len - int64_t(nchunks - 1) * C);
+  const int tail = p.ring_tail > 0 ? min(p.ring_tail, c_last) : 0;
+  const int64_t kept = len - tail;
   const int64_t sigma0 = doc_slot0(p.cu_seqlens, doc);
   // first checkpoint row of this document (checkpoints after every
   // ckpt_interval tokens, a multiple of the chunk)
@@ -609,6 +731,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
   __syncthreads();
 
   const int ots32 = static_cast<int>(p.out_tok_stride);  // host-checked to fit a buffer range
+  f32x4 u_last = {0.f, 0.f, 0.f, 0.f};  // U of the last chunk (rows 4 g4 + i)
   for (int ch = 0; ch < nchunks; ++ch) {
     const int64_t tc0 = t0 + int64_t(ch) * C;
     const int c = int(min<int64_t>(C, len - int64_t(ch) * C));
@@ -640,8 +763,10 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
     }
     // U = U0 - W S^T (accumulator layout: rows 4*g4 + i, value channel of the lane)
     const f32x4 u0 = *reinterpret_cast<const f32x4*>(R + kRecU0 + (wave * 64 + lane) * 16);
+    const f32x4 uf = u0 - (y0 + (y1 + y2));
     s16x4 uhi, ulo;
-    split4(u0 - (y0 + (y1 + y2)), uhi, ulo);
+    split4(uf, uhi, ulo);
+    u_last = uf;
     // O = scale ((e^Gam q) S^T + P U); rows r >= c fall outside the buffer
     // range and are dropped by the store itself
     const s16x4 pfr = *reinterpret_cast<const s16x4*>(R + kRecP + lane * 8);
@@ -666,7 +791,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
       acc[mt] = a;
     }
     // intermediate checkpoint after this chunk
-    if (p.ckpt && (ch + 1) % ckpt_every == 0 && int64_t(ch + 1) * C <= len) {
+    if (p.ckpt && (ch + 1) % ckpt_every == 0 && int64_t(ch + 1) * C <= kept) {
       const int64_t row = ckpt_row0 + (ch + 1) / ckpt_every - 1;
       if (row >= 0 && row < p.ckpt_rows) {
         uint16_t* cp = p.ckpt + (row * p.H + h) * int64_t(HEAD_ELEMS);
@@ -685,7 +810,18 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
     __syncthreads();  // this chunk's buffer is read; the next one is written
   }
 
-  // ---- final state
+  if (tail > 0) {  // hand-off: ring rows of the tail tokens receive u (bf16)
+    uint16_t* ur = p.u_cache + (int64_t(slot) * p.H + h) * p.ring_rows * int64_t(D) + v;
+    const int pe = c_last - tail;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g4 + i;
+      if (r >= pe && r < c_last)
+        ur[int64_t((rbase + r - pe) % p.ring_rows) * D] = to_bf16(u_last[i]);
+    }
+  }
+
+  // ---- final state (the state after the first `kept` tokens)
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
     const f32x4 a = acc[mt];
@@ -757,6 +893,24 @@ hipError_t launch_prefill(const PrefillParams& p, const int32_t* cu_host, bool v
     if (vec) KDA_PREP_LAUNCH(true);
     else KDA_PREP_LAUNCH(false);
 #undef KDA_PREP_LAUNCH
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.ring_tail > 0) {
+    dim3 hgrid(static_cast<unsigned>(p.n_docs), static_cast<unsigned>(p.H)), hblock(kThreads);
+    const int gk = p.gate_mode & kGateKindMask;
+#define KDA_HANDOFF_LAUNCH(V)                                                                  \
+  do {                                                                                         \
+    switch (gk) {                                                                              \
+      case 0: hipLaunchKernelGGL((handoff_kernel<V, 0>), hgrid, hblock, 0, stream, p); break; \
+      case 1: hipLaunchKernelGGL((handoff_kernel<V, 1>), hgrid, hblock, 0, stream, p); break; \
+      case 4: hipLaunchKernelGGL((handoff_kernel<V, 4>), hgrid, hblock, 0, stream, p); break; \
+      default: hipLaunchKernelGGL((handoff_kernel<V, 5>), hgrid, hblock, 0, stream, p);       \
+    }                                                                                          \
+  } while (0)
+    if (vec) KDA_HANDOFF_LAUNCH(true);
+    else KDA_HANDOFF_LAUNCH(false);
+#undef KDA_HANDOFF_LAUNCH
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -293,6 +293,33 @@ size_t kda_prefill_workspace_size(int32_t n_docs, int64_t total_tokens, int32_t 
  *                     checkpoints is not NULL)
  *  checkpoint_interval  tokens between checkpoints: a positive multiple of 16
  *                     (the chunk), else KDA_ERR_UNSUPPORTED
+ *  k_cache, u_cache, g_cache, ring_rows, cache_base, ring_tail
+ *                     hand-off to speculative decoding (this library's reading
+ *                     of a prefill that leaves each sequence in the form
+ *                     kda_verify_ucache_flush resumes from: a checkpoint plus
+ *                     ring history, "feat(kda): ReplaySSM verify+flush decode
+ *                     kernel for Kimi K3 (KDA)", "Caching"). ring_tail = 0: off,
+ *                     the ring arguments are not read (may be NULL). 1..16: an
+ *                     active document d of len_d > 0 tokens hands its last
+ *                     r_d = min(ring_tail, len_d - 16*floor((len_d - 1)/16))
+ *                     tokens (never more than those after its last 16-token
+ *                     boundary) to the ring of its slot s = state_indices[d]:
+ *                     its slot receives the state after its first len_d - r_d
+ *                     tokens instead of the final state, and tail token j
+ *                     (0 <= j < r_d) writes ring row (cache_base[d] + j) mod
+ *                     ring_rows with k_hat_j and u_j (bf16) and G_j (fp32, the
+ *                     log-decay summed over tail tokens 0..j), exactly the rows
+ *                     a verify call would have appended. The next verify call
+ *                     for d takes hist_len = r_d and the same cache_base.
+ *                     Outputs are unchanged; checkpoints cover only the first
+ *                     len_d - r_d tokens. k_cache and u_cache are bf16 and
+ *                     g_cache fp32, each [num_slots, H, ring_rows, 128];
+ *                     cache_base is int32 [n_docs]; a document whose
+ *                     cache_base lies outside [0, ring_rows) is inactive (zero
+ *                     outputs, nothing written). ring_tail outside 0..16 gives
+ *                     KDA_ERR_UNSUPPORTED, ring_rows < ring_tail
+ *                     KDA_ERR_BAD_SHAPE, a NULL ring pointer with ring_tail > 0
+ *                     KDA_ERR_NULL_POINTER.
  *  workspace          device buffer of >= kda_prefill_workspace_size(...) bytes,
  *                     256-byte aligned (may be NULL when that size is 0); the
  *                     per-chunk operands pass through it from the preparation
@@ -329,6 +356,8 @@ kda_status kda_prefill_varlen(int32_t n_docs, int64_t total_tokens, int32_t H, i
                               void* out, int64_t out_tok_stride,
                               void* checkpoints, int64_t checkpoint_rows,
                               const int64_t* checkpoint_cu_starts, int32_t checkpoint_interval,
+                              void* k_cache, void* u_cache, float* g_cache, int32_t ring_rows,
+                              const int32_t* cache_base, int32_t ring_tail,
                               void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 

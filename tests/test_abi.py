@@ -169,14 +169,16 @@ def test_prefill_workspace_and_validation(lib):
     def call(cu, total, **kw):
         p = P(1 << 20)
         a = dict(n=len(cu) - 1, H=2, K=128, ws=1 << 40, ots=256, lb=-5.0, ws_ptr=p, gm=0, sd=0,
-                 ck=P(0), ck_rows=0, ck_starts=P(0), ck_int=16)
+                 ck=P(0), ck_rows=0, ck_starts=P(0), ck_int=16, kc=P(0), uc=P(0), gc=P(0),
+                 R=0, base=P(0), tail=0)
         a.update(kw)
         arr = (ctypes.c_int32 * len(cu))(*cu)
         return lib.kda_prefill_varlen(a["n"], total, a["H"], a["K"], 128, arr, p, p, 256, p,
                                       256, p, 256, p, 256, p, 2, p, p, a["lb"], 1.0, a["gm"],
                                       a["sd"], p, 4,
                                       2 * 128 * 128, p, 1, p, a["ots"], a["ck"], a["ck_rows"],
-                                      a["ck_starts"], a["ck_int"], a["ws_ptr"], a["ws"], P(0))
+                                      a["ck_starts"], a["ck_int"], a["kc"], a["uc"], a["gc"],
+                                      a["R"], a["base"], a["tail"], a["ws_ptr"], a["ws"], P(0))
 
     assert call([1, 5], 5) == SEQ       # must start at 0
     assert call([0, 5, 3], 3) == SEQ    # must not decrease
@@ -197,6 +199,16 @@ def test_prefill_workspace_and_validation(lib):
     assert call([0, 5], 5, ck=q, ck_rows=3) == NULLP
     assert call([0], 0, ck=q, ck_rows=3, ck_starts=q, ck_int=32) == OK
     assert call([0, 5], 5, gm=1, lb=0.5) == UNSUP  # also outside the prefill's |lb| <= 5.5
+    # hand-off to the verify ring: at most one chunk's tokens, distinct rows,
+    # every ring pointer
+    assert call([0, 5], 5, tail=17, kc=q, uc=q, gc=q, R=32, base=q) == UNSUP
+    assert call([0, 5], 5, tail=-1) == UNSUP
+    assert call([0, 5], 5, tail=4, kc=q, uc=q, gc=q, R=3, base=q) == SHAPE
+    for miss in ("kc", "uc", "gc", "base"):
+        kw = dict(tail=4, kc=q, uc=q, gc=q, R=32, base=q)
+        kw[miss] = P(0)
+        assert call([0, 5], 5, **kw) == NULLP, miss
+    assert call([0], 0, tail=4, R=32) == OK  # no documents: nothing read
     assert call([0, 5], 5, ws=2 * rec - 1) == WS   # one slot, two heads
     assert call([0, 5], 5, ws=2 * rec, ws_ptr=P(0)) == NULLP
     assert call([0, 5], 5, ws=2 * rec, ws_ptr=P((1 << 20) + 128)) == UNSUP  # 256-byte aligned

@@ -10,8 +10,8 @@ import numpy as np
 import pytest
 
 from gated_delta_rule_step_amd import synth
-from tests.helpers import (HD, bits, check_out, check_pool, dev, dev_bf16, f32, pool_dev,
-                           pool_vals)
+from tests.helpers import (HD, bits, check_gcache, check_out, check_pool, check_state, dev,
+                           dev_bf16, f32, pool_dev, pool_vals)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -23,7 +23,8 @@ def _kda():
 
 
 def run_prefill(case, pool=None, packed=False, use_initial_state=None, lower_bound=None,
-                checkpoints=None, ckpt_starts=None, ckpt_interval=16):
+                checkpoints=None, ckpt_starts=None, ckpt_interval=16, ring=None, cache_base=None,
+                ring_tail=0):
     gm = case.get("gate_mode", 0)
     """Launch kda_prefill_varlen on a case. packed: q/k/v are strided views of
     one [Ttot, 3*H*128] buffer and out is a view with a padded row."""
@@ -50,12 +51,15 @@ def run_prefill(case, pool=None, packed=False, use_initial_state=None, lower_bou
                               else lower_bound, scale=case["scale"], gate_mode=gm,
                               checkpoints=checkpoints,
                               checkpoint_cu_starts=None if ckpt_starts is None
-                              else dev(ckpt_starts), checkpoint_interval=ckpt_interval)
+                              else dev(ckpt_starts), checkpoint_interval=ckpt_interval,
+                              ring=ring, cache_base=None if cache_base is None
+                              else dev(cache_base), ring_tail=ring_tail)
     return pool, out
 
 
 def oracle_prefill(orc, case, heads=None, use_initial_state=None, lower_bound=None,
-                   ckpt=None, ckpt_starts=None, ckpt_interval=16):
+                   ckpt=None, ckpt_starts=None, ckpt_interval=16, ring=None, cache_base=None,
+                   ring_tail=0):
     """fp32 token-by-token oracle over the heads listed (all by default).
     Returns (out [Ttot, nh, 128], pool [N, nh, 128, 128] float32 after the run)."""
     H, Ttot = case["H"], case["Ttot"]
@@ -81,7 +85,8 @@ def oracle_prefill(orc, case, heads=None, use_initial_state=None, lower_bound=No
                       case["scale"], pool, case["idx"], use_initial_state=uis,
                       bf16_storage=True, real=np.float32, gate_mode=gm, checkpoints=ckpt,
                       checkpoint_starts=ckpt_starts, checkpoint_interval=ckpt_interval,
-                      state_dtype=case.get("state_dtype", 0))
+                      state_dtype=case.get("state_dtype", 0), ring=ring, cache_base=cache_base,
+                      ring_tail=ring_tail)
     return out, pool
 
 
@@ -318,3 +323,188 @@ def test_full_h64_sampled_heads(orc, docs):
     case = synth.prefill_case(lens, H=64)
     pool, out = run_prefill(case)
     check_prefill(orc, case, pool, out, heads=[0, 9, 21, 33, 47, 63])
+
+
+# ---------------------------------------------------------------------------
+# hand-off to the verify ring: a document's last min(ring_tail, tokens after
+# its last 16-token boundary) tokens become ring history rows (k_hat, u, G)
+# and its slot receives the state before them
+
+RING_R = 32
+
+
+def _ring_fill(N, H, R=RING_R):
+    kc = synth.filler_bits((N, H, R, HD), 11)
+    uc = synth.filler_bits((N, H, R, HD), 12)
+    gc = (synth.filler_bits((N, H, R, HD), 13).astype(np.uint32) << 16).view(np.float32)
+    return kc, uc, gc
+
+
+def _handoff_check(orc, case, ring_tail, base, ckpt_interval=None):
+    """Prefill with hand-off on the GPU and in the oracle; compare outputs,
+    slot states, every handed-off ring row and (optionally) checkpoints, and
+    check that nothing else was written."""
+    H, N, Ttot = case["H"], case["N"], case["Ttot"]
+    kc0, uc0, gc0 = _ring_fill(N, H)
+    ring_d = (dev_bf16(kc0), dev_bf16(uc0), dev(gc0))
+    lens = np.diff(case["cu_seqlens"])
+    ck = starts = fill = ref_ck = None
+    rows = 0
+    if ckpt_interval:
+        counts = lens // ckpt_interval
+        starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
+        rows = int(counts.sum())
+        fill = synth.filler_bits((rows, H, HD, HD), 14)
+        ck = pool_dev(case, fill)
+        ref_ck = np.zeros((rows, H, HD, HD), np.float32)
+    pool, out = run_prefill(case, ring=ring_d, cache_base=base, ring_tail=ring_tail,
+                            checkpoints=ck, ckpt_starts=starts,
+                            ckpt_interval=ckpt_interval or 16)
+    ring_o = tuple(np.full((N, H, RING_R, HD), np.nan, np.float32) for _ in range(3))
+    ref_out, ref_pool = oracle_prefill(orc, case, ckpt=ref_ck, ckpt_starts=starts,
+                                       ckpt_interval=ckpt_interval or 16, ring=ring_o,
+                                       cache_base=base, ring_tail=ring_tail)
+    torch.cuda.synchronize()
+    got_out = bits(out).reshape(Ttot, H, HD)
+    got_pool = bits(pool)
+    gk, gu = bits(ring_d[0]), bits(ring_d[1])
+    gg = ring_d[2].cpu().numpy()
+    idx = case["idx"].astype(np.int64)
+    active = (idx >= 0) & (idx < N) & (base >= 0) & (base < RING_R)
+    cu = case["cu_seqlens"]
+    written = np.zeros((N, RING_R), bool)
+    n_rows = 0
+    for d in range(case["n_docs"]):
+        t0, t1 = cu[d], cu[d + 1]
+        if not active[d]:
+            assert np.all(got_out[t0:t1] == 0), f"inactive doc {d} must output +0.0"
+            continue
+        if t1 > t0:
+            check_out(got_out[t0:t1], ref_out[t0:t1], f"hand-off output doc {d}")
+        s_ = idx[d]
+        check_pool(case, got_pool[s_], ref_pool[s_], f"hand-off state doc {d}")
+        r = orc.handoff_tail(int(t1 - t0), ring_tail)
+        for j in range(r):
+            row = (int(base[d]) + j) % RING_R
+            written[s_, row] = True
+            check_state(gk[s_, :, row], ring_o[0][s_, :, row], f"k_hat row {j} doc {d}")
+            check_state(gu[s_, :, row], ring_o[1][s_, :, row], f"u row {j} doc {d}")
+            check_gcache(gg[s_, :, row], ring_o[2][s_, :, row], f"G row {j} doc {d}")
+        n_rows += r
+    def others(a):  # [N, H, R, 128] -> [N, R, H, 128], indexed by (slot, ring row)
+        return a.transpose(0, 2, 1, 3)[~written]
+    assert np.array_equal(others(gk), others(kc0)), "k_cache rows outside the hand-off changed"
+    assert np.array_equal(others(gu), others(uc0)), "u_cache rows outside the hand-off changed"
+    assert np.array_equal(others(gg.view(np.uint32)), others(gc0.view(np.uint32))), \
+        "g_cache rows outside the hand-off changed"
+    touched = np.zeros(N, bool)
+    touched[idx[active]] = True
+    assert np.array_equal(got_pool[~touched], case["pool"][~touched])
+    if ckpt_interval:
+        got_ck = bits(ck)
+        ck_written = np.zeros(rows, bool)
+        for d, n in enumerate(lens):
+            if not active[d]:
+                continue
+            kept = n - orc.handoff_tail(int(n), ring_tail)
+            for i in range(1, kept // ckpt_interval + 1):
+                row = int(starts[d]) + i - 1
+                ck_written[row] = True
+                check_pool(case, got_ck[row], ref_ck[row], f"checkpoint {row} doc {d}")
+        assert np.array_equal(got_ck[~ck_written], fill[~ck_written])
+        return n_rows, int((~ck_written).sum())
+    return n_rows, 0
+
+
+@pytest.mark.parametrize("ring_tail", [16, 5, 1])
+def test_handoff_small_docs(orc, ring_tail):
+    """Ragged documents (every chunk-boundary case, a zero-length document),
+    ring rows wrapping past the ring's end, one document with a ring base
+    out of range (inactive)."""
+    case = synth.prefill_case(SMALL_DOCS, H=3, seed=synth.seed_for(4, 3, 30 + ring_tail))
+    base = np.array([0, 31, 20, 17, 5, 30, -1, 9, 28, 3], np.int32)
+    n_rows, _ = _handoff_check(orc, case, ring_tail, base)
+    expect = sum(min(ring_tail, n - 16 * ((n - 1) // 16)) for i, n in enumerate(SMALL_DOCS)
+                 if n > 0 and i != 6)
+    assert n_rows == expect
+
+
+def test_handoff_with_checkpoints_fp16_and_no_initial_state(orc):
+    """Hand-off with checkpoints every 16 tokens (a checkpoint at a
+    document's end is not written when tokens were handed off), fp16
+    states, chains from zeros, a ring base of R (inactive)."""
+    case = synth.fp16_state(synth.prefill_case(SMALL_DOCS, H=2, seed=synth.seed_for(4, 2, 40),
+                                               use_initial_state=False))
+    base = np.array([4, 8, 12, 16, 20, 24, 28, RING_R, 1, 2], np.int32)
+    _, skipped = _handoff_check(orc, case, 16, base, ckpt_interval=16)
+    # skipped rows: the 64-token document's last (its tail is 16 tokens), the
+    # 16-token document's only one, and the inactive 2-token document has none
+    assert skipped == 2
+
+
+def test_handoff_full_h12(orc):
+    """The 4-document set at H = 12 with an 8-token hand-off."""
+    case = synth.prefill_case(synth.DOCS_4, H=12)
+    base = np.array([0, 8, 16, 24], np.int32)
+    n_rows, _ = _handoff_check(orc, case, 8, base)
+    assert n_rows == 8 * 4
+
+
+def test_handoff_then_verify(orc):
+    """Prefill hands off to the ring, then a verify call of 8 draft tokens
+    (flush_min 9, 16-row window) resumes from it with hist_len = the tail:
+    GPU prefill + GPU verify against oracle prefill + oracle verify."""
+    kda = _kda()
+    lens = (40, 37, 3, 16, 0, 32, 7)
+    H, T, fm = 3, 8, 9
+    case = synth.prefill_case(lens, H=H, seed=synth.seed_for(4, H, 50))
+    N = case["N"]
+    base = np.array([5, 31, 0, 12, 7, 20, 27], np.int32)
+    hist = kda.prefill_handoff_hist(torch.from_numpy(case["cu_seqlens"].copy()), 8).numpy()
+    assert hist.tolist() == [8, 5, 3, 8, 0, 8, 7]
+    kc0, uc0, gc0 = _ring_fill(N, H)
+    ring_d = (dev_bf16(kc0), dev_bf16(uc0), dev(gc0))
+    pool, _ = run_prefill(case, ring=ring_d, cache_base=base, ring_tail=8)
+    torch.cuda.synchronize()
+    # what the GPU prefill left, for the teacher-forced check of the fold
+    pre_pool = f32(bits(pool))
+    pre_k, pre_u = f32(bits(ring_d[0])), f32(bits(ring_d[1]))
+    pre_g = ring_d[2].cpu().numpy()
+    ring_o = tuple(np.full((N, H, RING_R, HD), np.nan, np.float32) for _ in range(3))
+    _, ref_pool = oracle_prefill(orc, case, ring=ring_o, cache_base=base, ring_tail=8)
+    # draft tokens, one row per document
+    rng = np.random.Generator(np.random.PCG64(synth.seed_for(4, H, 51)))
+    B, W = len(lens), H * HD
+    qkv = synth.bf16_bits(rng.standard_normal((B, T, 3 * W)).astype(np.float32))
+    gate = synth.bf16_bits(rng.standard_normal((B, T, W)).astype(np.float32))
+    beta = synth.bf16_bits(rng.standard_normal((B, T, H)).astype(np.float32))
+    qkv_d = dev_bf16(qkv)
+    out = torch.full((B, T, W), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kda.kda_verify_ucache_flush(qkv_d[..., :W], qkv_d[..., W:2 * W], qkv_d[..., 2 * W:],
+                                dev_bf16(gate), dev_bf16(beta), dev(case["a_log"]),
+                                dev(case["dt_bias"]), pool, dev(case["idx"]), *ring_d,
+                                dev(hist), dev(base), out, flush_min=fm, w_ring=16,
+                                lower_bound=case["lower_bound"], scale=case["scale"])
+    q = np.ascontiguousarray(f32(qkv[..., :W]).reshape(B, T, H, HD))
+    k = np.ascontiguousarray(f32(qkv[..., W:2 * W]).reshape(B, T, H, HD))
+    v = np.ascontiguousarray(f32(qkv[..., 2 * W:]).reshape(B, T, H, HD))
+    g = np.ascontiguousarray(f32(gate).reshape(B, T, H, HD))
+    ref_out = orc.verify(q, k, v, g, np.ascontiguousarray(f32(beta)), case["a_log"],
+                         case["dt_bias"], case["lower_bound"], case["scale"], ref_pool,
+                         case["idx"], *ring_o, hist, base, fm, 16, bf16_storage=True,
+                         real=np.float32)
+    torch.cuda.synchronize()
+    check_out(bits(out).reshape(B, T, H, HD), ref_out, "verify after hand-off")
+    got_pool = bits(pool)
+    folded = 0
+    for d in range(B):
+        s_ = case["idx"][d]
+        if hist[d] + T < fm:
+            continue
+        folded += 1
+        # the fold commits the replay of what the prefill handed off
+        for h in range(H):
+            S = orc.replay(np.ascontiguousarray(pre_pool[s_, h]), pre_k[s_, h], pre_u[s_, h],
+                           pre_g[s_, h], int(base[d]), int(hist[d]), real=np.float32)
+            check_state(got_pool[s_, h], S, f"folded checkpoint doc {d} head {h}")
+    assert folded == B - 1  # every document but the empty one

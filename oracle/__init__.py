@@ -22,8 +22,9 @@ channel.
 
 state_dtype (decode, verify, prefill): 0 stores the state (pool write-back, fold
 checkpoint, prefill final and intermediate states) in bf16, 1 in fp16 (round to
-nearest even, written from the binary16 definition); outputs and ring rows stay
-bf16. Pool inputs are passed as their exact values either way.
+nearest even, written from the binary16 definition), 2 in fp8 e4m3 (the OCP
+e4m3fn format, round to nearest even, saturating at +-448); outputs and ring
+rows stay bf16. Pool inputs are passed as their exact values either way.
 
 Prefill hand-off (ring_tail > 0, a reading): a document's last tokens, at most
 those after its last 16-token boundary and at most ring_tail, go to the verify
@@ -110,6 +111,24 @@ def f16_round_bits(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def f8_round_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> fp8 e4m3 bits, round-to-nearest-even, saturating at +-448 (uint8)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().orc_f8_round(ctypes.c_int64(x.size), x.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                       out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    return out
+
+
+def f8_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """fp8 e4m3 bits -> fp32 values (exact)."""
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    out = np.empty(b.shape, dtype=np.float32)
+    lib().orc_f8_to_float(ctypes.c_int64(b.size), b.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                          out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    return out
+
+
 def f16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """fp16 bits -> fp32 values (exact)."""
     b = np.ascontiguousarray(b, dtype=np.uint16)
@@ -181,7 +200,7 @@ def decode(q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, 
       _rp(beta_logit, real), _rp(a_log, real), _rp(dt_bias, real), _rs(lower_bound, real),
       _rs(scale, real), _rp(pool, real), ctypes.c_int64(N), _ip(idx), _rp(out, real),
       ctypes.c_int(1 if bf16_storage else 0), ctypes.c_int(gate_mode),
-      ctypes.c_int(1 if state_dtype == 1 else 0))
+      ctypes.c_int(int(state_dtype)))
     return out
 
 
@@ -202,7 +221,7 @@ def verify(q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool, 
       _rp(u_cache, real), _rp(g_cache, real), ctypes.c_int(R), _ip(hist_len), _ip(cache_base),
       ctypes.c_int(flush_min), ctypes.c_int(w_ring), _rp(out, real),
       ctypes.c_int(1 if bf16_storage else 0), ctypes.c_int(gate_mode),
-      ctypes.c_int(1 if state_dtype == 1 else 0))
+      ctypes.c_int(int(state_dtype)))
     return out
 
 
@@ -241,7 +260,7 @@ def prefill(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, p
     f(*_prefill_args(cu, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale, pool,
                      idx, use_initial_state, out, real), ctypes.c_int(1 if bf16_storage else 0),
       ctypes.c_int(gate_mode), ck, ctypes.c_int64(rows), starts,
-      ctypes.c_int(int(checkpoint_interval)), ctypes.c_int(1 if state_dtype == 1 else 0),
+      ctypes.c_int(int(checkpoint_interval)), ctypes.c_int(int(state_dtype)),
       *_ring_args(ring, cache_base, ring_tail, real))
     return out
 

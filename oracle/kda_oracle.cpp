@@ -30,6 +30,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <limits>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -133,13 +134,63 @@ float f16_bits_to_float(uint16_t b) {
   return f;
 }
 
+// ---------------------------------------------------------------------------
+// FP8 E4M3 (the OCP 8-bit format "e4m3fn": 1 sign, 4 exponent bits with bias
+// 7, 3 fraction bits; no infinities, S.1111.111 is NaN, so the largest finite
+// value is 448 = 1.75 * 2^8; below 2^-6 the value is a subnormal m * 2^-9)
+// for the fp8 state option, the byte reduction the decode page names as the
+// remaining lever ("feat(kda): add packed-input CuTe decode kernel"). Written
+// from that definition: round to nearest, ties to even; magnitudes beyond 448
+// saturate to 448 (a reading: a stored state must stay finite).
+uint8_t f8_rne_bits(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return static_cast<uint8_t>(sign | 0x7fu);  // NaN
+  if (a > 0x43e00000u) a = 0x43e00000u;                              // saturate at 448
+  uint32_t r;
+  if (a >= 0x3c800000u) {  // normal: |x| >= 2^-6
+    const uint32_t e = (a >> 23) - 127 + 7;
+    const uint32_t m = a & 0x7fffffu;
+    r = (e << 3) | (m >> 20);
+    const uint32_t rem = m & 0xfffffu, half = 0x80000u;
+    if (rem > half || (rem == half && (r & 1u))) r += 1;  // may carry into the exponent
+  } else {
+    const uint32_t e = a >> 23;
+    if (e == 0) return static_cast<uint8_t>(sign);  // binary32 subnormal: rounds to zero
+    const uint32_t m = (a & 0x7fffffu) | 0x800000u;  // value = m * 2^(e - 150)
+    const uint32_t shift = 141 - e;                  // value * 2^9 = m >> shift
+    if (shift > 24) return static_cast<uint8_t>(sign);  // below 2^-10: rounds to zero
+    r = m >> shift;
+    const uint32_t rem = m & ((1u << shift) - 1u), half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (r & 1u))) r += 1;  // 8 is the smallest normal
+  }
+  return static_cast<uint8_t>(sign | r);
+}
+
+float f8_bits_to_float(uint8_t b) {
+  const uint32_t e = (b >> 3) & 0xfu, m = b & 0x7u;
+  float f;
+  if (e == 15 && m == 7) {
+    f = std::numeric_limits<float>::quiet_NaN();
+  } else if (e == 0) {
+    f = std::ldexp(static_cast<float>(m), -9);
+  } else {
+    f = std::ldexp(static_cast<float>(8 + m), static_cast<int>(e) - 10);
+  }
+  return (b & 0x80u) ? -f : f;
+}
+
 // State storage points (pool write-back, fold checkpoint, prefill final and
-// intermediate states): bf16, or fp16 when state_fp16 is set.
+// intermediate states): bf16 (state_dtype 0), fp16 (1) or fp8 e4m3 (2).
 template <class Real>
-Real store_state(Real x, int bf16_storage, int state_fp16) {
+Real store_state(Real x, int bf16_storage, int state_dtype) {
   if (!bf16_storage) return x;
-  if (state_fp16)
+  if (state_dtype == 1)
     return static_cast<Real>(f16_bits_to_float(f16_rne_bits(static_cast<float>(x))));
+  if (state_dtype == 2)
+    return static_cast<Real>(f8_bits_to_float(f8_rne_bits(static_cast<float>(x))));
   return to_bf16(x);
 }
 
@@ -272,7 +323,7 @@ template <class Real>
 void decode(int B, int H, int K, int V, const Real* q, const Real* k, const Real* v,
             const Real* graw, const Real* beta_logit, const Real* a_log, const Real* dt_bias,
             Real lower_bound, Real scale, Real* pool, int64_t N, const int32_t* idx,
-            Real* out, int bf16_storage, int gate_mode, int state_fp16) {
+            Real* out, int bf16_storage, int gate_mode, int state_dtype) {
   const int64_t KV = i64(K) * V;
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int b = 0; b < B; ++b) {
@@ -293,7 +344,7 @@ void decode(int B, int H, int K, int V, const Real* q, const Real* k, const Real
       std::copy(slot, slot + KV, S.begin());
       step<Real>(K, V, S.data(), qh.data(), kh.data(), v + (i64(b) * H + h) * V, g.data(),
                  beta, scale, o, nullptr);
-      for (int64_t e = 0; e < KV; ++e) slot[e] = store_state(S[e], bf16_storage, state_fp16);
+      for (int64_t e = 0; e < KV; ++e) slot[e] = store_state(S[e], bf16_storage, state_dtype);
       for (int r = 0; r < V; ++r) o[r] = store(o[r], bf16_storage);
     }
   }
@@ -355,7 +406,7 @@ void verify(int B, int T, int H, int K, int V, const Real* q, const Real* k, con
             Real lower_bound, Real scale, Real* pool, int64_t N, const int32_t* idx, Real* kc,
             Real* uc, Real* gc, int R, const int32_t* hist_len, const int32_t* cache_base,
             int flush_min, int w_ring, Real* out, int bf16_storage, int gate_mode,
-            int state_fp16) {
+            int state_dtype) {
   const int64_t KV = i64(K) * V;
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int b = 0; b < B; ++b) {
@@ -404,7 +455,7 @@ void verify(int B, int T, int H, int K, int V, const Real* q, const Real* k, con
         for (int r = 0; r < V; ++r) ucs[row * V + r] = store(u[r], bf16_storage);
       }
       if (fold)
-        for (int64_t e = 0; e < KV; ++e) ckpt[e] = store_state(Scur[e], bf16_storage, state_fp16);
+        for (int64_t e = 0; e < KV; ++e) ckpt[e] = store_state(Scur[e], bf16_storage, state_dtype);
     }
   }
 }
@@ -447,7 +498,7 @@ void prefill_tbt(int n_docs, int H, int K, int V, const int32_t* cu, const Real*
                  const Real* a_log, const Real* dt_bias, Real lower_bound, Real scale,
                  Real* pool, int64_t N, const int32_t* idx, int use_initial_state, Real* out,
                  int bf16_storage, int gate_mode, Real* ckpt, int64_t ckpt_rows,
-                 const int64_t* ckpt_starts, int interval, int state_fp16, Real* kc, Real* uc,
+                 const int64_t* ckpt_starts, int interval, int state_dtype, Real* kc, Real* uc,
                  Real* gc, int R, const int32_t* cache_base, int ring_tail) {
   const int64_t KV = i64(K) * V;
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -469,7 +520,7 @@ void prefill_tbt(int n_docs, int H, int K, int V, const int32_t* cu, const Real*
       std::vector<Real> S(KV, static_cast<Real>(0));
       if (use_initial_state) std::copy(slot, slot + KV, S.begin());
       if (kept == 0)
-        for (int64_t e = 0; e < KV; ++e) slot[e] = store_state(S[e], bf16_storage, state_fp16);
+        for (int64_t e = 0; e < KV; ++e) slot[e] = store_state(S[e], bf16_storage, state_dtype);
       std::vector<Real> qh(K), kh(K), g(K), u(V), G(K, static_cast<Real>(0));
       for (int t = t0; t < t1; ++t) {
         const int64_t tk = (i64(t) * H + h) * K;
@@ -487,11 +538,11 @@ void prefill_tbt(int n_docs, int H, int K, int V, const int32_t* cu, const Real*
           const int64_t row = ckpt_starts[d] + done / interval - 1;
           if (row >= 0 && row < ckpt_rows) {
             Real* c = ckpt + (row * H + h) * KV;
-            for (int64_t e = 0; e < KV; ++e) c[e] = store_state(S[e], bf16_storage, state_fp16);
+            for (int64_t e = 0; e < KV; ++e) c[e] = store_state(S[e], bf16_storage, state_dtype);
           }
         }
         if (done == kept)
-          for (int64_t e = 0; e < KV; ++e) slot[e] = store_state(S[e], bf16_storage, state_fp16);
+          for (int64_t e = 0; e < KV; ++e) slot[e] = store_state(S[e], bf16_storage, state_dtype);
         if (done > kept) {  // a tail token: ring history entry done - kept - 1
           const int64_t sh = i64(idx[d]) * H + h;
           const int64_t row = (cache_base[d] + (done - kept - 1)) % R;
@@ -655,9 +706,9 @@ void prefill_chunked(int n_docs, int H, int K, int V, const int32_t* cu, const R
                                    const Real* a_log, const Real* dt_bias, Real lower_bound,  \
                                    Real scale, Real* pool, int64_t N, const int32_t* idx,     \
                                    Real* out, int bf16_storage, int gate_mode,                \
-                                   int state_fp16) {                                          \
+                                   int state_dtype) {                                          \
     decode<Real>(B, H, K, V, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound, scale,   \
-                 pool, N, idx, out, bf16_storage, gate_mode, state_fp16);                     \
+                 pool, N, idx, out, bf16_storage, gate_mode, state_dtype);                     \
   }                                                                                           \
   extern "C" void orc_verify_##SUF(                                                           \
       int B, int T, int H, int K, int V, const Real* q, const Real* k, const Real* v,         \
@@ -665,10 +716,10 @@ void prefill_chunked(int n_docs, int H, int K, int V, const int32_t* cu, const R
       Real lower_bound, Real scale, Real* pool, int64_t N, const int32_t* idx, Real* kc,      \
       Real* uc, Real* gc, int R, const int32_t* hist_len, const int32_t* cache_base,          \
       int flush_min, int w_ring, Real* out, int bf16_storage, int gate_mode,                  \
-      int state_fp16) {                                                                       \
+      int state_dtype) {                                                                       \
     verify<Real>(B, T, H, K, V, q, k, v, graw, beta_logit, a_log, dt_bias, lower_bound,       \
                  scale, pool, N, idx, kc, uc, gc, R, hist_len, cache_base, flush_min, w_ring, \
-                 out, bf16_storage, gate_mode, state_fp16);                                   \
+                 out, bf16_storage, gate_mode, state_dtype);                                   \
   }                                                                                           \
   extern "C" void orc_prefill_tbt_##SUF(                                                      \
       int n_docs, int H, int K, int V, const int32_t* cu, const Real* q, const Real* k,       \
@@ -676,11 +727,11 @@ void prefill_chunked(int n_docs, int H, int K, int V, const int32_t* cu, const R
       const Real* dt_bias, Real lower_bound, Real scale, Real* pool, int64_t N,               \
       const int32_t* idx, int use_initial_state, Real* out, int bf16_storage,                 \
       int gate_mode, Real* ckpt, int64_t ckpt_rows, const int64_t* ckpt_starts,               \
-      int interval, int state_fp16, Real* kc, Real* uc, Real* gc, int R,                      \
+      int interval, int state_dtype, Real* kc, Real* uc, Real* gc, int R,                      \
       const int32_t* cache_base, int ring_tail) {                                             \
     prefill_tbt<Real>(n_docs, H, K, V, cu, q, k, v, graw, beta_logit, a_log, dt_bias,         \
                       lower_bound, scale, pool, N, idx, use_initial_state, out, bf16_storage, \
-                      gate_mode, ckpt, ckpt_rows, ckpt_starts, interval, state_fp16, kc, uc,  \
+                      gate_mode, ckpt, ckpt_rows, ckpt_starts, interval, state_dtype, kc, uc,  \
                       gc, R, cache_base, ring_tail);                                          \
   }                                                                                           \
   extern "C" void orc_prefill_chunked_##SUF(                                                  \
@@ -706,6 +757,14 @@ extern "C" void orc_f16_round(int64_t n, const float* in, uint16_t* out) {
 
 extern "C" void orc_f16_to_float(int64_t n, const uint16_t* in, float* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = f16_bits_to_float(in[i]);
+}
+
+extern "C" void orc_f8_round(int64_t n, const float* in, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f8_rne_bits(in[i]);
+}
+
+extern "C" void orc_f8_to_float(int64_t n, const uint8_t* in, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f8_bits_to_float(in[i]);
 }
 
 extern "C" int orc_max_threads() {

@@ -881,28 +881,65 @@ def _f16(x):
         torch.float32).numpy()
 
 
-def test_fp16_state_rounds_only_the_state_storage_points(orc):
-    """Decode, verify (fold) and prefill with fp16 state equal the same run
-    without state rounding followed by torch's fp16 cast of the stored states;
-    outputs keep their bf16 rounding."""
+# fp8 e4m3 state option (the decode page names byte reduction as the lever that
+# remains; the format is OCP e4m3fn, saturating at +-448). torch's float8_e4m3fn
+# cast of the clamped value is the independent reference.
+
+def _f8(x):
+    x = np.clip(np.ascontiguousarray(x, np.float32), -448.0, 448.0)
+    return torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
+def test_f8_rne_matches_torch(orc):
+    rng = _rng(232)
+    bits = rng.integers(0, 2 ** 32, 4_000_000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[~np.isnan(x)]
+    allv = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(
+        torch.float32).numpy()
+    fin = np.unique(allv[np.isfinite(allv)])
+    mids = ((fin[1:].astype(np.float64) + fin[:-1]) / 2).astype(np.float32)  # exact ties
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(-np.inf))
+    sp = np.concatenate([fin, mids, up, dn, rng.standard_normal(100_000).astype(np.float32) * 0.05,
+                         np.array([447, 449, 464, 465, 480, 1e4, np.inf, 2.0 ** -10,
+                                   2.0 ** -11, 1.5 * 2.0 ** -10, 1e-30, 0.0], np.float32)])
+    x = np.concatenate([x, sp, -sp])
+    ours = orc.f8_round_bits(x)
+    ref = torch.from_numpy(np.clip(x, -448.0, 448.0)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+    np.testing.assert_array_equal(ours, ref)
+    # and back: every finite encoding widens exactly
+    allb = np.arange(256, dtype=np.uint8)
+    finite = np.isfinite(allv)
+    np.testing.assert_array_equal(orc.f8_bits_to_f32(allb)[finite], allv[finite])
+    assert np.all(np.isnan(orc.f8_bits_to_f32(allb)[~finite]))
+
+
+@pytest.mark.parametrize("state_dtype", [1, 2])
+def test_low_byte_state_rounds_only_the_state_storage_points(orc, state_dtype):
+    """Decode, verify (fold) and prefill with fp16 (1) or fp8 (2) state equal
+    the same run without state rounding followed by torch's cast of the stored
+    states; outputs keep their bf16 rounding."""
+    cast = {1: _f16, 2: _f8}[state_dtype]
     rng = _rng(231)
     B, H, N = 3, 2, 4
     d = _decode_inputs(rng, B, H, N, F32)
-    d["pool"] = _f16(d["pool"])
+    d["pool"] = cast(d["pool"])
     idx = np.array([3, 0, 1], np.int32)
     pa, pb = d["pool"].copy(), d["pool"].copy()
     args = (d["q"], d["k"], d["v"], d["graw"], d["beta_logit"], d["a_log"], d["dt_bias"], -5.0,
             1.0)
-    oa = orc.decode(*args, pa, idx, bf16_storage=True, real=F32, state_dtype=1)
+    oa = orc.decode(*args, pa, idx, bf16_storage=True, real=F32, state_dtype=state_dtype)
     ob = orc.decode(*args, pb, idx, bf16_storage=False, real=F32)
-    np.testing.assert_array_equal(pa[idx], _f16(pb[idx]))
+    np.testing.assert_array_equal(pa[idx], cast(pb[idx]))
     np.testing.assert_array_equal(oa, synth.f32_from_bits(synth.bf16_bits(ob)))
     assert not np.array_equal(pa[idx], synth.f32_from_bits(synth.bf16_bits(pb[idx])))
 
     toks = {n: synth.f32_from_bits(synth.bf16_bits(a)) for n, a in _tok(rng, 4, H).items()}
     R = 32
     res = []
-    for st, bf in ((1, True), (0, False)):
+    for st, bf in ((state_dtype, True), (0, False)):
         pool = d["pool"][:2].copy()
         kc = np.zeros((2, H, R, 128), np.float32)
         uc = np.zeros_like(kc)
@@ -919,22 +956,22 @@ def test_fp16_state_rounds_only_the_state_storage_points(orc):
                          np.array([3], np.int32), np.array([30], np.int32), 4, 16,
                          bf16_storage=bf, real=F32, state_dtype=st)
         res.append((out, pool))
-    np.testing.assert_array_equal(res[0][1][1], _f16(res[1][1][1]))  # the folded checkpoint
+    np.testing.assert_array_equal(res[0][1][1], cast(res[1][1][1]))  # the folded checkpoint
 
     p = _prefill_inputs(rng, (21, 0, 40), H=2, real=F32)
     for n in ("q", "k", "v", "graw", "beta_logit"):
         p[n] = synth.f32_from_bits(synth.bf16_bits(p[n]))
-    p["pool"] = _f16(p["pool"])
+    p["pool"] = cast(p["pool"])
     ck_a = np.zeros((3, 2, 128, 128), np.float32)
     ck_b = np.zeros_like(ck_a)
     starts = np.array([0, 1, 1], np.int64)
     qa, qb = p["pool"].copy(), p["pool"].copy()
-    orc.prefill(*_pf_args(p), qa, p["idx"], real=F32, state_dtype=1, checkpoints=ck_a,
+    orc.prefill(*_pf_args(p), qa, p["idx"], real=F32, state_dtype=state_dtype, checkpoints=ck_a,
                 checkpoint_starts=starts, checkpoint_interval=16)
     orc.prefill(*_pf_args(p), qb, p["idx"], bf16_storage=False, real=F32, checkpoints=ck_b,
                 checkpoint_starts=starts, checkpoint_interval=16)
-    np.testing.assert_array_equal(qa[p["idx"]], _f16(qb[p["idx"]]))
-    np.testing.assert_array_equal(ck_a, _f16(ck_b))
+    np.testing.assert_array_equal(qa[p["idx"]], cast(qb[p["idx"]]))
+    np.testing.assert_array_equal(ck_a, cast(ck_b))
 
 
 # ---------------------------------------------------------------------------

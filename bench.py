@@ -164,6 +164,11 @@ def fp16_pools(torch, pools):
     return [p.to(torch.float16) for p in pools]
 
 
+def fp8_pools(torch, pools):
+    """The same two pools with fp8 e4m3 state elements (state_dtype 2)."""
+    return [p.to(torch.float8_e4m3fn) for p in pools]
+
+
 def make_pools(torch, synth):
     """Two bf16 pools of 1024 slots (seeded N(0, 0.05) state)."""
     pools = []
@@ -287,7 +292,7 @@ class PrefillSetup:
     A_log U(-1, 1), dt_bias N(0, 0.1), initial states N(0, 0.05) in a pool of
     2 slots per document)."""
 
-    def __init__(self, lens, H, torch, kda, synth, gate_mode=0, ckpt_interval=0, state_fp16=False,
+    def __init__(self, lens, H, torch, kda, synth, gate_mode=0, ckpt_interval=0, state="bf16",
                  ring_tail=0):
         self.lens, self.H, self.gate_mode = tuple(lens), H, gate_mode
         n_docs, T, W = len(lens), int(sum(lens)), H * 128
@@ -311,8 +316,8 @@ class PrefillSetup:
             self.dtb = torch.randn(H, generator=gen, device="cuda") * 0.1
         N = 2 * n_docs
         self.pool = randn(N, H, 128, 128, std=0.05)
-        if state_fp16:
-            self.pool = self.pool.to(torch.float16)
+        if state != "bf16":
+            self.pool = self.pool.to({"fp16": torch.float16, "fp8": torch.float8_e4m3fn}[state])
         self.idx = torch.randperm(N, generator=gen, device="cuda")[:n_docs].to(torch.int32)
         cu = np.zeros(n_docs + 1, np.int32)
         cu[1:] = np.cumsum(lens)
@@ -468,20 +473,21 @@ def main():
             log(f"bench: {points[-1]}")
         points.append(dict(kind="decode", B=B, T=1, us_per_call=round(us_ev, 3),
                            GBps=round(gbs, 1), hbm_frac=round(gbs / wm.HBM_PEAK_GBS, 4)))
-        # the other gate conventions and the fp16 state at the headline size
-        f16 = fp16_pools(torch, pools)
-        for gm, variant, pp in ((3, dict(gate="pre-computed g and beta"), pools),
-                                (4, dict(gate="per-head gate (GDN-style)"), pools),
-                                (0, dict(state="fp16"), f16)):
+        # the other gate conventions and the fp16 and fp8 states at the headline size
+        f16, f8 = fp16_pools(torch, pools), fp8_pools(torch, pools)
+        for gm, variant, pp, sbytes in ((3, dict(gate="pre-computed g and beta"), pools, 2),
+                                        (4, dict(gate="per-head gate (GDN-style)"), pools, 2),
+                                        (0, dict(state="fp16"), f16, 2),
+                                        (0, dict(state="fp8 e4m3"), f8, 1)):
             sp = DecodeSetup(B, torch, kda, synth, pp, gate_mode=gm)
             _, e = time_graphs(sp.calls(), args.steps, args.warmup, torch, min_warm_s=0.3)
             us = e * 1e3 / args.steps
-            nb = wm.decode_bytes(sp.n_active, B - sp.n_active)
+            nb = wm.decode_bytes(sp.n_active, B - sp.n_active, state_bytes=sbytes)
             points.append(dict(kind="decode", B=B, T=1, **variant,
                                us_per_call=round(us, 3), GBps=round(nb / (us * 1e-6) / 1e9, 1),
                                hbm_frac=round(nb / (us * 1e-6) / 1e9 / wm.HBM_PEAK_GBS, 4)))
             log(f"bench: {points[-1]}")
-        del f16
+        del f16, f8
         rings = make_rings(torch, synth)
         vcfgs = [
             dict(label="T=8 bare (0% fold)", T=8, hist_max=0),
@@ -492,21 +498,24 @@ def main():
             dict(label="T=8 W32 fm=25 hist~U{0..24}", T=8, w_ring=32, flush_min=25, hist_max=24),
             dict(label="T=8 bare, pre-computed gate and beta", T=8, hist_max=0, gate_mode=3),
             dict(label="T=8 fm=9 50% fold, per-head gate", T=8, fold_p=0.5, gate_mode=4),
-            dict(label="T=8 bare, fp16 checkpoints", T=8, hist_max=0, fp16=True),
-            dict(label="T=8 fm=9 100% fold, fp16 checkpoints", T=8, fold_p=1.0, fp16=True),
+            dict(label="T=8 bare, fp16 checkpoints", T=8, hist_max=0, state="fp16"),
+            dict(label="T=8 fm=9 100% fold, fp16 checkpoints", T=8, fold_p=1.0, state="fp16"),
+            dict(label="T=8 bare, fp8 checkpoints", T=8, hist_max=0, state="fp8"),
+            dict(label="T=8 fm=9 100% fold, fp8 checkpoints", T=8, fold_p=1.0, state="fp8"),
         ]
-        f16 = fp16_pools(torch, pools)
+        low = {"fp16": fp16_pools(torch, pools), "fp8": fp8_pools(torch, pools)}
         for Bv in (1, 32, 512):
             for cfg in vcfgs:
                 if Bv != 512 and cfg["label"] not in ("T=8 bare (0% fold)", "T=8 fm=9 100% fold"):
                     continue
-                kw = {k: v for k, v in cfg.items() if k not in ("label", "T", "fp16")}
-                vs = VerifySetup(Bv, cfg["T"], torch, kda, synth, f16 if cfg.get("fp16") else pools,
+                kw = {k: v for k, v in cfg.items() if k not in ("label", "T", "state")}
+                vs = VerifySetup(Bv, cfg["T"], torch, kda, synth, low.get(cfg.get("state"), pools),
                                  rings, **kw)
                 st = max(args.steps, 256 if Bv < 512 else 100)
                 _, e = time_graphs(vs.calls(), st, args.warmup, torch, min_warm_s=0.3)
                 us = e * 1e3 / st
-                nb = wm.verify_bytes(cfg["T"], vs.hist, vs.fold)
+                nb = wm.verify_bytes(cfg["T"], vs.hist, vs.fold,
+                                     state_bytes=1 if cfg.get("state") == "fp8" else 2)
                 fl = wm.verify_flops(cfg["T"], vs.hist)
                 extra = {}
                 if Bv == 512 and cfg["label"] == "T=8 bare (0% fold)":
@@ -520,29 +529,32 @@ def main():
                                    TFLOPs=round(fl / (us * 1e-6) / 1e12, 2), **extra))
                 log(f"bench: {points[-1]}")
                 del vs
-        del rings, f16
+        del rings, low
         torch.cuda.empty_cache()
         d4 = ("4 docs (3840, 3776, 3200, 3072)", synth.DOCS_4)
-        pcfgs = [(name, lens, Hp, 0, 0, False, 0)
+        pcfgs = [(name, lens, Hp, 0, 0, "bf16", 0)
                  for name, lens in (d4, ("14-doc mix, 16384 tokens", synth.DOCS_14))
                  for Hp in (64, 12)]
-        pcfgs += [(*d4, 12, 3, 0, False, 0), (*d4, 12, 4, 0, False, 0),
-                  (*d4, 12, 0, 64, False, 0), (*d4, 12, 0, 0, True, 0), (*d4, 12, 0, 0, False, 8)]
-        for name, lens, Hp, gm, cki, sf16, rt in pcfgs:
+        pcfgs += [(*d4, 12, 3, 0, "bf16", 0), (*d4, 12, 4, 0, "bf16", 0),
+                  (*d4, 12, 0, 64, "bf16", 0), (*d4, 12, 0, 0, "fp16", 0),
+                  (*d4, 12, 0, 0, "fp8", 0), (*d4, 12, 0, 0, "bf16", 8)]
+        for name, lens, Hp, gm, cki, sdt, rt in pcfgs:
             ps = PrefillSetup(lens, Hp, torch, kda, synth, gate_mode=gm, ckpt_interval=cki,
-                              state_fp16=sf16, ring_tail=rt)
+                              state=sdt, ring_tail=rt)
             st = max(10, min(args.steps, 50))
             _, e = time_graphs(ps.calls(), st, 2, torch, min_warm_s=0.3)
             us = e * 1e3 / st
-            # each checkpoint row writes H bf16 states
-            nb = wm.prefill_bytes(lens, Hp) + ps.ck_rows * Hp * 128 * 128 * 2
+            # each checkpoint row writes H states
+            sbytes = 1 if sdt == "fp8" else 2
+            nb = (wm.prefill_bytes(lens, Hp, state_bytes=sbytes) +
+                  ps.ck_rows * Hp * 128 * 128 * sbytes)
             fl = wm.prefill_flops(lens, Hp)
             extra = {"gate": {3: "pre-computed g and beta", 4: "per-head gate (GDN-style)"}[gm]} \
                 if gm else {}
             if cki:
                 extra["checkpoints"] = f"every {cki} tokens ({ps.ck_rows} rows)"
-            if sf16:
-                extra["state"] = "fp16"
+            if sdt != "bf16":
+                extra["state"] = sdt
             if rt:
                 extra["handoff"] = f"last {rt} tokens of each document to the verify ring"
             points.append(dict(kind="prefill", H=Hp, docs=name, tokens=int(sum(lens)),

@@ -119,16 +119,19 @@ def _i32(name, t):
 
 
 def _state_dtype(state_pool) -> int:
-    """KDA_STATE_BF16 (0) or KDA_STATE_FP16 (1), from the pool tensor's dtype."""
+    """KDA_STATE_BF16 (0), KDA_STATE_FP16 (1) or KDA_STATE_FP8 (2, torch's
+    float8_e4m3fn), from the pool tensor's dtype."""
     import torch
     if state_pool.dtype == torch.float16:
         return 1
+    if state_pool.dtype == torch.float8_e4m3fn:
+        return 2
     _bf16("state_pool", state_pool)
     return 0
 
 
 def _pool_geometry(state_pool, H):
-    """Pool: bf16 or fp16 tensor whose dim 0 indexes slots; each slot's first
+    """Pool: bf16, fp16 or fp8 e4m3 tensor whose dim 0 indexes slots; each slot's first
     H*128*128 elements are contiguous. Returns (num_slots, slot_stride)."""
     if not state_pool.is_cuda or state_pool.stride(-1) != 1:
         raise ValueError("state_pool must be a GPU tensor with a contiguous last dimension")

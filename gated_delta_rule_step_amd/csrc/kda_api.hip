@@ -5,6 +5,12 @@
 
 #include "../../include/kda.h"
 #include "kda_launch.h"
+#include "kda_common.h"
+
+// state_dtype values are the kernels' state format indices
+static_assert(KDA_STATE_BF16 == kda::kStateBf16 && KDA_STATE_FP16 == kda::kStateFp16 &&
+                  KDA_STATE_FP8 == kda::kStateFp8,
+              "state format numbering");
 
 namespace {
 
@@ -76,7 +82,7 @@ extern "C" kda_status kda_decode(int32_t B, int32_t H, int32_t K, int32_t V, con
                                  int64_t out_row_stride, hipStream_t stream) {
   if (B < 0 || H < 1 || num_slots < 0) return KDA_ERR_BAD_SHAPE;
   if (K != D || V != D) return KDA_ERR_UNSUPPORTED;
-  if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP16) return KDA_ERR_UNSUPPORTED;
+  if (state_dtype < KDA_STATE_BF16 || state_dtype > KDA_STATE_FP8) return KDA_ERR_UNSUPPORTED;
   if (const kda_status gs = check_gate(gate_mode, lower_bound, A_log, dt_bias)) {
     if (gs == KDA_ERR_UNSUPPORTED || B > 0) return gs;
   }
@@ -109,8 +115,8 @@ extern "C" kda_status kda_decode(int32_t B, int32_t H, int32_t K, int32_t V, con
   p.lower_bound = lower_bound;
   p.scale = scale;
   p.gate_mode = gate_mode;
-  p.state_fp16 = state_dtype == KDA_STATE_FP16 ? 1 : 0;
-  p.state_pool = static_cast<uint16_t*>(state_pool);
+  p.state_fmt = state_dtype;  // kda_state_dtype values are the kernels' format indices
+  p.state_pool = state_pool;
   p.num_slots = num_slots;
   p.slot_stride = slot_stride;
   p.state_indices = state_indices;
@@ -120,8 +126,9 @@ extern "C" kda_status kda_decode(int32_t B, int32_t H, int32_t K, int32_t V, con
                    gate_vec_ok(gate_mode, g_raw, g_row_stride, 0) && aligned16(dt_bias) &&
                    (num_slots == 0 || aligned16(state_pool)) && mult8(q_row_stride) &&
                    mult8(k_row_stride) && mult8(slot_stride);
-  // fp16 state: the vectorised path only (16-byte aligned bases, strides in multiples of 8)
-  if (p.state_fp16 && !vec) return KDA_ERR_UNSUPPORTED;
+  // fp16 and fp8 states: the vectorised path only (16-byte aligned bases, strides in
+  // multiples of 8)
+  if (p.state_fmt != KDA_STATE_BF16 && !vec) return KDA_ERR_UNSUPPORTED;
   return launch_status(kda::launch_decode(p, vec, stream));
 }
 
@@ -142,7 +149,7 @@ extern "C" kda_status kda_verify_ucache_flush(
   if (ring_rows < w_ring || restart_hist_on_flush != 1 || flush_min < 1) return KDA_ERR_UNSUPPORTED;
   if (flush_min - 1 + T > w_ring) return KDA_ERR_UNSUPPORTED;  // ring capacity
   if (w_ring == 32 && flush_min <= 16) return KDA_ERR_UNSUPPORTED;
-  if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP16) return KDA_ERR_UNSUPPORTED;
+  if (state_dtype < KDA_STATE_BF16 || state_dtype > KDA_STATE_FP8) return KDA_ERR_UNSUPPORTED;
   if (const kda_status gs = check_gate(gate_mode, lower_bound, A_log, dt_bias)) {
     if (gs == KDA_ERR_UNSUPPORTED || B > 0) return gs;
   }
@@ -185,8 +192,8 @@ extern "C" kda_status kda_verify_ucache_flush(
   p.lower_bound = lower_bound;
   p.scale = scale;
   p.gate_mode = gate_mode;
-  p.state_fp16 = state_dtype == KDA_STATE_FP16 ? 1 : 0;
-  p.state_pool = static_cast<uint16_t*>(state_pool);
+  p.state_fmt = state_dtype;  // kda_state_dtype values are the kernels' format indices
+  p.state_pool = state_pool;
   p.num_slots = num_slots;
   p.slot_stride = slot_stride;
   p.state_indices = state_indices;
@@ -209,8 +216,9 @@ extern "C" kda_status kda_verify_ucache_flush(
                    mult8(q_row_stride) && mult8(q_tok_stride) && mult8(k_row_stride) &&
                    mult8(k_tok_stride) && mult8(v_row_stride) && mult8(v_tok_stride) &&
                    mult8(out_row_stride) && mult8(out_tok_stride) && mult8(slot_stride);
-  // fp16 state: the vectorised path only (16-byte aligned bases, strides in multiples of 8)
-  if (p.state_fp16 && !vec) return KDA_ERR_UNSUPPORTED;
+  // fp16 and fp8 states: the vectorised path only (16-byte aligned bases, strides in
+  // multiples of 8)
+  if (p.state_fmt != KDA_STATE_BF16 && !vec) return KDA_ERR_UNSUPPORTED;
   return launch_status(kda::launch_verify(p, vec, stream));
 }
 
@@ -241,7 +249,7 @@ extern "C" kda_status kda_prefill_varlen(
   for (int32_t d = 0; d < n_docs; ++d)
     if (cu_seqlens_host[d + 1] < cu_seqlens_host[d]) return KDA_ERR_BAD_SEQLENS;
   if (int64_t(cu_seqlens_host[n_docs]) != total_tokens) return KDA_ERR_BAD_SEQLENS;
-  if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP16) return KDA_ERR_UNSUPPORTED;
+  if (state_dtype < KDA_STATE_BF16 || state_dtype > KDA_STATE_FP8) return KDA_ERR_UNSUPPORTED;
   if (const kda_status gs = check_gate(gate_mode, lower_bound, A_log, dt_bias)) {
     if (gs == KDA_ERR_UNSUPPORTED || n_docs > 0) return gs;
   }
@@ -294,15 +302,15 @@ extern "C" kda_status kda_prefill_varlen(
   p.lower_bound = lower_bound;
   p.scale = scale;
   p.gate_mode = gate_mode;
-  p.state_fp16 = state_dtype == KDA_STATE_FP16 ? 1 : 0;
-  p.state_pool = static_cast<uint16_t*>(state_pool);
+  p.state_fmt = state_dtype;  // kda_state_dtype values are the kernels' format indices
+  p.state_pool = state_pool;
   p.num_slots = num_slots;
   p.slot_stride = slot_stride;
   p.state_indices = state_indices;
   p.use_initial_state = use_initial_state ? 1 : 0;
   p.out = static_cast<uint16_t*>(out);
   p.out_tok_stride = out_tok_stride;
-  p.ckpt = static_cast<uint16_t*>(checkpoints);
+  p.ckpt = checkpoints;
   p.ckpt_rows = checkpoints ? checkpoint_rows : 0;
   p.ckpt_starts = checkpoint_cu_starts;
   p.ckpt_interval = checkpoints ? checkpoint_interval : 16;
@@ -318,7 +326,8 @@ extern "C" kda_status kda_prefill_varlen(
                    aligned16(out) && (num_slots == 0 || aligned16(state_pool)) &&
                    aligned16(checkpoints) && mult8(q_tok_stride) && mult8(k_tok_stride) &&
                    mult8(v_tok_stride) && mult8(out_tok_stride) && mult8(slot_stride);
-  // fp16 state: the vectorised path only (16-byte aligned bases, strides in multiples of 8)
-  if (p.state_fp16 && !vec) return KDA_ERR_UNSUPPORTED;
+  // fp16 and fp8 states: the vectorised path only (16-byte aligned bases, strides in
+  // multiples of 8)
+  if (p.state_fmt != KDA_STATE_BF16 && !vec) return KDA_ERR_UNSUPPORTED;
   return launch_status(kda::launch_prefill(p, cu_seqlens_host, vec, stream));
 }

@@ -4,11 +4,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kda {
 
 constexpr int D = 128;             // head dimension (K = V = 128)
 constexpr int HEAD_ELEMS = D * D;  // one head's state, elements
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -45,14 +48,105 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
 }
 
-// A state word of two elements, bf16 or (SF16) fp16.
-template <bool SF16>
-__device__ __forceinline__ float st_lo(uint32_t w) { return SF16 ? f16_lo(w) : bf_lo(w); }
-template <bool SF16>
-__device__ __forceinline__ float st_hi(uint32_t w) { return SF16 ? f16_hi(w) : bf_hi(w); }
-template <bool SF16>
+// fp8 e4m3 state elements (the OCP e4m3fn format: bias 7, largest finite
+// 448, no infinities). Widening is exact (v_cvt_pk_f32_fp8); narrowing is
+// v_cvt_pk_fp8_f32, round to nearest even, after a clamp to +-448 with
+// v_med3_f32, so that an out-of-range value saturates instead of becoming NaN.
+__device__ __forceinline__ f32x2 f8x2_lo(uint32_t w) {  // bytes 0, 1
+  return __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+}
+__device__ __forceinline__ f32x2 f8x2_hi(uint32_t w) {  // bytes 2, 3
+  return __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+}
+__device__ __forceinline__ float f8_sat(float x) { return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f); }
+__device__ __forceinline__ uint32_t pack_f8x4(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(f8_sat(a), f8_sat(b), 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(f8_sat(c), f8_sat(d), r, true);
+  return static_cast<uint32_t>(r);
+}
+// Two fp32 values that are exactly bf16 (e.g. widened fp8) as a bf16 pair:
+// the top halves of both words, one v_perm_b32.
+__device__ __forceinline__ uint32_t pack_bf16x2_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// ---------------------------------------------------------------------------
+// State element formats: bf16, fp16 or fp8 e4m3 (the state_dtype argument).
+constexpr int kStateBf16 = 0;
+constexpr int kStateFp16 = 1;
+constexpr int kStateFp8 = 2;
+template <int SF>
+constexpr int kStateBytes = SF == kStateFp8 ? 1 : 2;
+
+// A state word of two elements, bf16 or fp16.
+template <int SF>
+__device__ __forceinline__ float st_lo(uint32_t w) {
+  static_assert(SF != kStateFp8, "two-element words hold 16-bit formats");
+  return SF == kStateFp16 ? f16_lo(w) : bf_lo(w);
+}
+template <int SF>
+__device__ __forceinline__ float st_hi(uint32_t w) {
+  static_assert(SF != kStateFp8, "two-element words hold 16-bit formats");
+  return SF == kStateFp16 ? f16_hi(w) : bf_hi(w);
+}
+template <int SF>
 __device__ __forceinline__ uint32_t st_pack(float lo, float hi) {
-  return SF16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+  static_assert(SF != kStateFp8, "two-element words hold 16-bit formats");
+  return SF == kStateFp16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+}
+
+// Eight consecutive state elements: 16 bytes (bf16, fp16) or 8 bytes (fp8).
+template <int SF>
+using St8 = typename std::conditional<SF == kStateFp8, u32x2, u32x4>::type;
+
+template <int SF>
+__device__ __forceinline__ void st8_unpack(St8<SF> w, float (&x)[8]) {
+  if constexpr (SF == kStateFp8) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const f32x2 a = f8x2_lo(w[i]), b = f8x2_hi(w[i]);
+      x[4 * i] = a[0];
+      x[4 * i + 1] = a[1];
+      x[4 * i + 2] = b[0];
+      x[4 * i + 3] = b[1];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = st_lo<SF>(w[i]);
+      x[2 * i + 1] = st_hi<SF>(w[i]);
+    }
+  }
+}
+
+template <int SF>
+__device__ __forceinline__ St8<SF> st8_pack(const float (&x)[8]) {
+  St8<SF> w;
+  if constexpr (SF == kStateFp8) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) w[i] = pack_f8x4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = st_pack<SF>(x[2 * i], x[2 * i + 1]);
+  }
+  return w;
+}
+
+// Non-temporal loads and stores of 8 state elements at element offset `e`
+// (aligned to 8 elements: the vectorised layout).
+template <int SF>
+__device__ __forceinline__ St8<SF> st8_load_nt(const void* base, int64_t e) {
+  return __builtin_nontemporal_load(
+      reinterpret_cast<const St8<SF>*>(static_cast<const uint8_t*>(base) + e * kStateBytes<SF>));
+}
+template <int SF>
+__device__ __forceinline__ void st8_store_nt(void* base, int64_t e, St8<SF> w) {
+  __builtin_nontemporal_store(
+      w, reinterpret_cast<St8<SF>*>(static_cast<uint8_t*>(base) + e * kStateBytes<SF>));
+}
+template <int SF>
+__device__ __forceinline__ void st8_store(void* base, int64_t e, St8<SF> w) {
+  *reinterpret_cast<St8<SF>*>(static_cast<uint8_t*>(base) + e * kStateBytes<SF>) = w;
 }
 
 // 8 consecutive bf16 -> 8 floats; VEC: one 128-bit load (16-byte aligned).

@@ -1,4 +1,5 @@
-// T = 1 KDA decode against an in-place bf16 state pool (gfx950).
+// T = 1 KDA decode against an in-place state pool (gfx950): bf16, fp16 or fp8
+// e4m3 elements.
 //
 // Operation: "feat(kda): add packed-input CuTe decode kernel" (opening
 // description and "T=1 fast path inside recurrent_kda"): per (row, head),
@@ -13,7 +14,8 @@
 //    fetched into one L2;
 //  * lane l covers key channels 8*(l%16) .. +7 of value rows
 //    vbase + 4*i + l/16 (i < LOADS): every state access is a 128-bit load or
-//    store and one load instruction covers four full 256-byte rows;
+//    store (64-bit with fp8 elements) and one load instruction covers four
+//    full rows;
 //  * all LOADS state loads are issued before any prologue math, and each
 //    updated 4-row group is stored as soon as it is computed (holding all
 //    stores back to the end measured ~15% slower);
@@ -33,8 +35,9 @@ namespace kda {
 // GK, the gate kind: kGatePrecomputed clear = raw gate logits (log-decay from
 // A_log, dt_bias, lower_bound), set = the log-decay itself; kGatePerHead set =
 // one gate value (and dt_bias) per head for all key channels.
-// SF16: the pool holds fp16 state (else bf16).
-template <int LOADS, bool VEC, int GK, bool SF16>
+// SF: the pool's element format (kStateBf16, kStateFp16, kStateFp8); the
+// 16-bit formats move 8 elements per 128-bit access, fp8 per 64-bit access.
+template <int LOADS, bool VEC, int GK, int SF>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr bool GRAW = !(GK & kGatePrecomputed);
   constexpr bool GHEAD = (GK & kGatePerHead) != 0;
@@ -59,11 +62,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   }
 
   // Issue every state load first.
-  uint16_t* sp = p.state_pool + int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS +
-                 int64_t(vbase + rg) * D + kb * 8;
-  u32x4 s[LOADS];
+  static_assert(VEC || SF == kStateBf16, "fp16 and fp8 states use the vectorised layout");
+  const int64_t se = int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS +
+                     int64_t(vbase + rg) * D + kb * 8;  // element offset
+  uint16_t* sp = static_cast<uint16_t*>(p.state_pool) + se;  // 16-bit formats
+  St8<SF> s[LOADS];
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) s[i] = load8_raw<VEC>(sp + i * 4 * D);
+  for (int i = 0; i < LOADS; ++i) {
+    if constexpr (SF == kStateFp8) s[i] = st8_load_nt<SF>(p.state_pool, se + i * 4 * D);
+    else s[i] = load8_raw<VEC>(sp + i * 4 * D);
+  }
 
   // Per-token prologue for this lane's 8 key channels.
   float q[8], k[8], gr[8], dtb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -121,11 +129,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     float x[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = st_lo<SF16>(s[i][j]);
-      x[2 * j + 1] = st_hi<SF16>(s[i][j]);
-    }
+    st8_unpack<SF>(s[i], x);
     float dk = 0.f, dq = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -137,25 +141,35 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     const float u = beta * (vrow[i] - dk);
     const float o = p.scale * fmaf(u, kq, dq);
     if (kb == i) osel = o;
-    u32x4 w;
+    St8<SF> w;
+    if constexpr (SF == kStateFp8) {
+      float a[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float a0 = fmaf(al[2 * j], x[2 * j], kh[2 * j] * u);
-      const float a1 = fmaf(al[2 * j + 1], x[2 * j + 1], kh[2 * j + 1] * u);
-      w[j] = st_pack<SF16>(a0, a1);
+      for (int c = 0; c < 8; ++c) a[c] = fmaf(al[c], x[c], kh[c] * u);
+      w = st8_pack<SF>(a);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a0 = fmaf(al[2 * j], x[2 * j], kh[2 * j] * u);
+        const float a1 = fmaf(al[2 * j + 1], x[2 * j + 1], kh[2 * j + 1] * u);
+        w[j] = st_pack<SF>(a0, a1);
+      }
     }
-    store8_raw<VEC>(sp + i * 4 * D, w);
+    if constexpr (SF == kStateFp8) st8_store_nt<SF>(p.state_pool, se + i * 4 * D, w);
+    else store8_raw<VEC>(sp + i * 4 * D, w);
   }
   if (kb < LOADS) outp[4 * kb + rg] = to_bf16(osel);
 }
 
 // Launch shape: 256-thread workgroups of four independent waves. Large
-// batches use 32-row tiles (8 loads per lane, four waves = one head); small
-// batches use 8-row tiles so that a few heads still spread over many CUs.
+// batches use 32-row tiles (8 loads per lane, four waves = one head), or with
+// fp8 state 64-row tiles (16 loads of 8 bytes, the same 32 registers of state
+// and bytes in flight per wave); small batches use 8-row tiles so that a few
+// heads still spread over many CUs.
 hipError_t launch_decode(const DecodeParams& p, bool vec, hipStream_t stream) {
   const int64_t heads = int64_t(p.B) * p.H;
   const bool small = heads < 1024;
-  const int loads = small ? 2 : 8;
+  const int loads = small ? 2 : (p.state_fmt == kStateFp8 ? 16 : 8);
   const int64_t tiles = heads * (D / (4 * loads));
   const int64_t blocks = (tiles + 3) / 4;
   if (blocks == 0) return hipSuccess;
@@ -171,17 +185,20 @@ hipError_t launch_decode(const DecodeParams& p, bool vec, hipStream_t stream) {
       default: hipLaunchKernelGGL((decode_kernel<L, V, 5, F>), grid, block, 0, stream, p);      \
     }                                                                                           \
   } while (0)
-  // fp16 state runs on the vectorised path only (the host requires it)
-  if (p.state_fp16) {
-    if (!vec) return hipErrorInvalidValue;
-    if (small) KDA_DECODE_LAUNCH(2, true, true);
-    else KDA_DECODE_LAUNCH(8, true, true);
+  // fp16 and fp8 states run on the vectorised path only (the host requires it)
+  if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
+  if (p.state_fmt == kStateFp16) {
+    if (small) KDA_DECODE_LAUNCH(2, true, kStateFp16);
+    else KDA_DECODE_LAUNCH(8, true, kStateFp16);
+  } else if (p.state_fmt == kStateFp8) {
+    if (small) KDA_DECODE_LAUNCH(2, true, kStateFp8);
+    else KDA_DECODE_LAUNCH(16, true, kStateFp8);
   } else if (small) {
-    if (vec) KDA_DECODE_LAUNCH(2, true, false);
-    else KDA_DECODE_LAUNCH(2, false, false);
+    if (vec) KDA_DECODE_LAUNCH(2, true, kStateBf16);
+    else KDA_DECODE_LAUNCH(2, false, kStateBf16);
   } else {
-    if (vec) KDA_DECODE_LAUNCH(8, true, false);
-    else KDA_DECODE_LAUNCH(8, false, false);
+    if (vec) KDA_DECODE_LAUNCH(8, true, kStateBf16);
+    else KDA_DECODE_LAUNCH(8, false, kStateBf16);
   }
 #undef KDA_DECODE_LAUNCH
   return hipGetLastError();

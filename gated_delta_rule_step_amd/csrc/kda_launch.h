@@ -28,8 +28,8 @@ struct DecodeParams {
   const float* dt_bias;
   float lower_bound, scale;
   int32_t gate_mode;
-  int32_t state_fp16;  // pool elements are fp16 (else bf16)
-  uint16_t* state_pool;
+  int32_t state_fmt;  // pool element format: kStateBf16, kStateFp16, kStateFp8
+  void* state_pool;
   int64_t num_slots, slot_stride;
   const int32_t* state_indices;
   uint16_t* out;
@@ -49,8 +49,8 @@ struct VerifyParams {
   const float* dt_bias;
   float lower_bound, scale;
   int32_t gate_mode;
-  int32_t state_fp16;  // checkpoint elements are fp16 (else bf16); rings stay bf16
-  uint16_t* state_pool;
+  int32_t state_fmt;  // checkpoint element format (kStateBf16 ...); rings stay bf16
+  void* state_pool;
   int64_t num_slots, slot_stride;
   const int32_t* state_indices;
   uint16_t* k_cache;
@@ -78,14 +78,14 @@ struct PrefillParams {
   const float* dt_bias;
   float lower_bound, scale;
   int32_t gate_mode;
-  int32_t state_fp16;  // pool and checkpoint elements are fp16 (else bf16)
-  uint16_t* state_pool;
+  int32_t state_fmt;  // pool and checkpoint element format (kStateBf16 ...)
+  void* state_pool;
   int64_t num_slots, slot_stride;
   const int32_t* state_indices;
   int32_t use_initial_state;
   uint16_t* out;
   int64_t out_tok_stride;
-  uint16_t* ckpt;              // NULL: no intermediate checkpoints
+  void* ckpt;                  // NULL: no intermediate checkpoints
   int64_t ckpt_rows;
   const int64_t* ckpt_starts;  // [n_docs]
   int32_t ckpt_interval;       // tokens, a multiple of 16

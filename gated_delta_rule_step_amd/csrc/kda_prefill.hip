@@ -66,7 +66,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));  // bf16 operands of the K = 16 MFMA
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int C = 16;          // tokens per chunk
 constexpr int RS = D + 4;      // padded row (fp32) of the [token][channel] LDS arrays: the
@@ -200,6 +199,28 @@ __device__ __forceinline__ void gstore4(uint16_t* p, u32x2 w) {
     p[1] = uint16_t(w[0] >> 16);
     p[2] = uint16_t(w[1] & 0xffffu);
     p[3] = uint16_t(w[1] >> 16);
+  }
+}
+
+// Four consecutive state elements (the 4 key channels of one accumulator
+// entry), in the state format SF: 8 bytes (bf16, fp16) or 4 bytes (fp8).
+template <int SF, bool VEC>
+__device__ __forceinline__ f32x4 st4_load(const void* base, int64_t e) {
+  if constexpr (SF == kStateFp8) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(base) + e);
+    const f32x2 a = f8x2_lo(w), b = f8x2_hi(w);
+    return f32x4{a[0], a[1], b[0], b[1]};
+  } else {
+    const u32x2 w = gload4<VEC>(static_cast<const uint16_t*>(base) + e);
+    return f32x4{st_lo<SF>(w[0]), st_hi<SF>(w[0]), st_lo<SF>(w[1]), st_hi<SF>(w[1])};
+  }
+}
+template <int SF, bool VEC>
+__device__ __forceinline__ void st4_store(void* base, int64_t e, f32x4 a) {
+  if constexpr (SF == kStateFp8) {
+    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(base) + e) = pack_f8x4(a[0], a[1], a[2], a[3]);
+  } else {
+    gstore4<VEC>(static_cast<uint16_t*>(base) + e, u32x2{st_pack<SF>(a[0], a[1]), st_pack<SF>(a[2], a[3])});
   }
 }
 
@@ -641,8 +662,9 @@ constexpr int kChainThreads = 512;
 constexpr int kChainRounds = (kRecUnits + kChainThreads - 1) / kChainThreads;  // 4
 static_assert(kRecUnits > (kChainRounds - 1) * kChainThreads, "every round has work");
 
-// SF16: the pool (initial and final states) and the checkpoints hold fp16.
-template <bool VEC, bool SF16>
+// SF: the element format of the pool (initial and final states) and the
+// checkpoints (kStateBf16, kStateFp16, kStateFp8).
+template <bool VEC, int SF>
 __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, DocOrder ord) {
   __shared__ __align__(16) uint8_t rbuf[2][kRecBytes];
   const int tid = threadIdx.x;
@@ -666,10 +688,14 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
       p.out[(t0 + e / D) * p.out_tok_stride + h * D + (e % D)] = 0;
     return;
   }
-  uint16_t* sp = p.state_pool + int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS;
+  static_assert(VEC || SF == kStateBf16, "fp16 and fp8 states use the vectorised layout");
+  const int64_t se = int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS;  // element offset
   if (len == 0) {  // final state = initial state: untouched, or zeros without one
-    if (!p.use_initial_state)
-      for (int e = tid; e < HEAD_ELEMS; e += kChainThreads) sp[e] = 0;
+    if (!p.use_initial_state) {
+      uint16_t* z = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(p.state_pool) +
+                                                se * kStateBytes<SF>);
+      for (int e = tid; e < HEAD_ELEMS * kStateBytes<SF> / 2; e += kChainThreads) z[e] = 0;
+    }
     return;
   }
 
@@ -715,13 +741,20 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
   // before any is waited for)
   f32x4 acc[8];
   if (p.use_initial_state) {
-    u32x2 w[8];
+    if constexpr (SF == kStateFp8) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) w[mt] = gload4<VEC>(sp + v * D + 16 * mt + 4 * g4);
+      for (int mt = 0; mt < 8; ++mt)
+        acc[mt] = st4_load<SF, VEC>(p.state_pool, se + v * D + 16 * mt + 4 * g4);
+    } else {
+      const uint16_t* sp = static_cast<const uint16_t*>(p.state_pool) + se;
+      u32x2 w[8];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-      acc[mt] = f32x4{st_lo<SF16>(w[mt][0]), st_hi<SF16>(w[mt][0]), st_lo<SF16>(w[mt][1]),
-                      st_hi<SF16>(w[mt][1])};
+      for (int mt = 0; mt < 8; ++mt) w[mt] = gload4<VEC>(sp + v * D + 16 * mt + 4 * g4);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        acc[mt] = f32x4{st_lo<SF>(w[mt][0]), st_hi<SF>(w[mt][0]), st_lo<SF>(w[mt][1]),
+                        st_hi<SF>(w[mt][1])};
+    }
   } else {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -794,13 +827,10 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
     if (p.ckpt && (ch + 1) % ckpt_every == 0 && int64_t(ch + 1) * C <= kept) {
       const int64_t row = ckpt_row0 + (ch + 1) / ckpt_every - 1;
       if (row >= 0 && row < p.ckpt_rows) {
-        uint16_t* cp = p.ckpt + (row * p.H + h) * int64_t(HEAD_ELEMS);
+        const int64_t ce = (row * p.H + h) * int64_t(HEAD_ELEMS);
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-          const f32x4 a = acc[mt];
-          gstore4<VEC>(cp + v * D + 16 * mt + 4 * g4,
-                       u32x2{st_pack<SF16>(a[0], a[1]), st_pack<SF16>(a[2], a[3])});
-        }
+        for (int mt = 0; mt < 8; ++mt)
+          st4_store<SF, VEC>(p.ckpt, ce + v * D + 16 * mt + 4 * g4, acc[mt]);
       }
     }
     // record ch+1 (its loads were issued a chunk ago) into the other buffer,
@@ -823,11 +853,8 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
 
   // ---- final state (the state after the first `kept` tokens)
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    const f32x4 a = acc[mt];
-    gstore4<VEC>(sp + v * D + 16 * mt + 4 * g4,
-                 u32x2{st_pack<SF16>(a[0], a[1]), st_pack<SF16>(a[2], a[3])});
-  }
+  for (int mt = 0; mt < 8; ++mt)
+    st4_store<SF, VEC>(p.state_pool, se + v * D + 16 * mt + 4 * g4, acc[mt]);
 }
 
 size_t prefill_workspace_bytes(int32_t n_docs, int64_t total_tokens, int32_t H) {
@@ -915,14 +942,16 @@ hipError_t launch_prefill(const PrefillParams& p, const int32_t* cu_host, bool v
     if (e != hipSuccess) return e;
   }
   dim3 grid(static_cast<unsigned>(blocks)), block(kChainThreads);
-  // fp16 states run on the vectorised path only (the host requires it)
-  if (p.state_fp16) {
-    if (!vec) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((chain_kernel<true, true>), grid, block, 0, stream, p, ord);
+  // fp16 and fp8 states run on the vectorised path only (the host requires it)
+  if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
+  if (p.state_fmt == kStateFp16) {
+    hipLaunchKernelGGL((chain_kernel<true, kStateFp16>), grid, block, 0, stream, p, ord);
+  } else if (p.state_fmt == kStateFp8) {
+    hipLaunchKernelGGL((chain_kernel<true, kStateFp8>), grid, block, 0, stream, p, ord);
   } else if (vec) {
-    hipLaunchKernelGGL((chain_kernel<true, false>), grid, block, 0, stream, p, ord);
+    hipLaunchKernelGGL((chain_kernel<true, kStateBf16>), grid, block, 0, stream, p, ord);
   } else {
-    hipLaunchKernelGGL((chain_kernel<false, false>), grid, block, 0, stream, p, ord);
+    hipLaunchKernelGGL((chain_kernel<false, kStateBf16>), grid, block, 0, stream, p, ord);
   }
   return hipGetLastError();
 }

@@ -45,7 +45,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __fp16 f16x8 __attribute__((__vector_size__(8 * sizeof(__fp16))));  // MFMA f16 operand
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TMAX = 8;
 // s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
@@ -171,12 +170,16 @@ __device__ __forceinline__ void load_tokens(const VerifyParams& p, int64_t item,
 
 // Grid: one 256-thread workgroup per item (row, head), item = row * H + head.
 // GK, the gate kind: kGatePrecomputed clear = raw gate logits, set = the
-// log-decay itself; kGatePerHead set = one gate value per head. SF16: fp16
-// checkpoints (the product below then runs on v_mfma_f32_16x16x32_f16 with
-// fp16 hi / lo A fragments); the rings stay bf16.
-template <bool VEC, bool FACT, int GK, bool SF16>
+// log-decay itself; kGatePerHead set = one gate value per head. SF: the
+// checkpoint format. fp16 checkpoints make the product below run on
+// v_mfma_f32_16x16x32_f16 with fp16 hi / lo A fragments; fp8 checkpoints are
+// widened to bf16 (exactly) as B fragments of the bf16 product. The rings
+// stay bf16.
+template <bool VEC, bool FACT, int GK, int SF>
 __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   constexpr bool GRAW = !(GK & kGatePrecomputed);
+  constexpr int MF = SF == kStateFp16 ? kStateFp16 : kStateBf16;  // MFMA operand format
+  static_assert(VEC || SF == kStateBf16, "fp16 and fp8 checkpoints use the vectorised layout");
   extern __shared__ __align__(16) float smem_raw[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -208,14 +211,17 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   load_tokens<VEC, GK>(p, item, tid, tk);
   const bool fold = hist + T >= p.flush_min;
   const int64_t sh = int64_t(slot) * p.H + h;
-  uint16_t* ckpt = p.state_pool + int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS;
+  // the checkpoint: element offset ce; ckpt addresses the 16-bit formats
+  const int64_t ce = int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS;
+  uint16_t* ckpt = static_cast<uint16_t*>(p.state_pool) + int64_t(slot) * p.slot_stride +
+                   int64_t(h) * HEAD_ELEMS;
   uint16_t* kc = p.k_cache + sh * R * D;
   uint16_t* uc = p.u_cache + sh * R * D;
   float* gc = p.g_cache + sh * R * D;
   // ring row of history / draft position j (0 <= j < hist + T <= R, base < R)
   auto ring_row = [&](int j) { const int r = base + j; return r >= R ? r - R : r; };
 
-  u32x4 sf[2][4];
+  St8<SF> sf[2][4];
   // ---- 2. per-token prologue (token t on lanes 32 t .. 32 t + 31, four
   // channels per lane), run while the checkpoint B fragments stream in (wave
   // w owns value columns 32w .. 32w+31 in two 16-column blocks; fragment
@@ -251,7 +257,11 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
     for (int st = 0; st < 4; ++st)
-      sf[blk][st] = load8_raw<VEC>(ckpt + int64_t(32 * wave + 16 * blk + fv) * D + 32 * st + fk);
+      if constexpr (SF == kStateFp8)
+        sf[blk][st] = st8_load_nt<SF>(p.state_pool,
+                                      ce + int64_t(32 * wave + 16 * blk + fv) * D + 32 * st + fk);
+      else
+        sf[blk][st] = load8_raw<VEC>(ckpt + int64_t(32 * wave + 16 * blk + fv) * D + 32 * st + fk);
   __builtin_amdgcn_sched_barrier(0);
   {
     const int t = tid >> 5, c0 = 4 * (tid & 31);
@@ -391,24 +401,30 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
       for (int st = 0; st < 4; ++st) {
         const int k0 = 32 * st + fk;
         float x[8];
+        if constexpr (SF == kStateFp8) {
+          st8_unpack<SF>(sf[blk][st], x);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[2 * e] = st_lo<SF16>(sf[blk][st][e]) * s.egl[k0 + 2 * e];
-          x[2 * e + 1] = st_hi<SF16>(sf[blk][st][e]) * s.egl[k0 + 2 * e + 1];
+          for (int e = 0; e < 8; ++e) x[e] *= s.egl[k0 + e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[2 * e] = st_lo<SF>(sf[blk][st][e]) * s.egl[k0 + 2 * e];
+            x[2 * e + 1] = st_hi<SF>(sf[blk][st][e]) * s.egl[k0 + 2 * e + 1];
+          }
         }
         for (int j = 0; j < hist; ++j) {
           const float uj = bf1(s.uh[j * D + v]);
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = fmaf(uj, s.dh[j * D + k0 + e], x[e]);
         }
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = st_pack<SF16>(x[2 * e], x[2 * e + 1]);
+        const St8<SF> w = st8_pack<SF>(x);
         // A plain (cached) store: one instruction covers 64 of the 128 bytes of
-        // each of 16 checkpoint rows, and the st + 1 store fills the other
-        // half; in L2 the halves merge into whole lines before they reach
-        // memory (non-temporal stores measured 9 % slower at 100 % fold).
-        if constexpr (VEC) *reinterpret_cast<u32x4*>(ckpt + int64_t(v) * D + k0) = w;
+        // each of 16 checkpoint rows (32 of 64 for fp8), and the st + 1 store
+        // fills the other half; in L2 the halves merge into whole lines before
+        // they reach memory (non-temporal stores measured 9 % slower at 100 %
+        // fold).
+        if constexpr (SF == kStateFp8) st8_store<SF>(p.state_pool, ce + int64_t(v) * D + k0, w);
+        else if constexpr (VEC) *reinterpret_cast<u32x4*>(ckpt + int64_t(v) * D + k0) = w;
         else store8_raw<VEC>(ckpt + int64_t(v) * D + k0, w);
       }
     }
@@ -541,15 +557,15 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
       for (int i = 0; i < 2; ++i) {
         const float a = x0[2 * i] * e0[2 * i], b = x0[2 * i + 1] * e0[2 * i + 1];
         const float c = x1[2 * i] * e1[2 * i], d = x1[2 * i + 1] * e1[2 * i + 1];
-        // hi / lo split in the checkpoint's own format
-        hi[i] = st_pack<SF16>(a, b);
-        hi[2 + i] = st_pack<SF16>(c, d);
-        lo[i] = st_pack<SF16>(a - st_lo<SF16>(hi[i]), b - st_hi<SF16>(hi[i]));
-        lo[2 + i] = st_pack<SF16>(c - st_lo<SF16>(hi[2 + i]), d - st_hi<SF16>(hi[2 + i]));
+        // hi / lo split in the format of the checkpoint operand
+        hi[i] = st_pack<MF>(a, b);
+        hi[2 + i] = st_pack<MF>(c, d);
+        lo[i] = st_pack<MF>(a - st_lo<MF>(hi[i]), b - st_hi<MF>(hi[i]));
+        lo[2 + i] = st_pack<MF>(c - st_lo<MF>(hi[2 + i]), d - st_hi<MF>(hi[2 + i]));
       }
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        if constexpr (SF16) {
+        if constexpr (MF == kStateFp16) {
           const f16x8 ahi = __builtin_bit_cast(f16x8, hi);
           const f16x8 alo = __builtin_bit_cast(f16x8, lo);
           const f16x8 bfr = __builtin_bit_cast(f16x8, sf[blk][st]);
@@ -558,7 +574,18 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
         } else {
           const bf16x8 ahi = __builtin_bit_cast(bf16x8, hi);
           const bf16x8 alo = __builtin_bit_cast(bf16x8, lo);
-          const bf16x8 bfr = __builtin_bit_cast(bf16x8, sf[blk][st]);
+          u32x4 bw;
+          if constexpr (SF == kStateFp8) {  // fp8 -> bf16 is exact
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const f32x2 x01 = f8x2_lo(sf[blk][st][i]), x23 = f8x2_hi(sf[blk][st][i]);
+              bw[2 * i] = pack_bf16x2_exact(x01[0], x01[1]);
+              bw[2 * i + 1] = pack_bf16x2_exact(x23[0], x23[1]);
+            }
+          } else {
+            bw = sf[blk][st];
+          }
+          const bf16x8 bfr = __builtin_bit_cast(bf16x8, bw);
           acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bfr, acc[blk], 0, 0, 0);
           acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bfr, acc[blk], 0, 0, 0);
         }
@@ -657,17 +684,20 @@ hipError_t launch_verify(const VerifyParams& p, bool vec, hipStream_t stream) {
       default: hipLaunchKernelGGL((verify_kernel<V, F, 5, S>), grid, block, lds, stream, p, hm); \
     }                                                                                         \
   } while (0)
-  // fp16 checkpoints run on the vectorised path only (the host requires it)
-  if (p.state_fp16) {
-    if (!vec) return hipErrorInvalidValue;
-    if (fact) KDA_VERIFY_LAUNCH(true, true, true);
-    else KDA_VERIFY_LAUNCH(true, false, true);
+  // fp16 and fp8 checkpoints run on the vectorised path only (the host requires it)
+  if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
+  if (p.state_fmt == kStateFp16) {
+    if (fact) KDA_VERIFY_LAUNCH(true, true, kStateFp16);
+    else KDA_VERIFY_LAUNCH(true, false, kStateFp16);
+  } else if (p.state_fmt == kStateFp8) {
+    if (fact) KDA_VERIFY_LAUNCH(true, true, kStateFp8);
+    else KDA_VERIFY_LAUNCH(true, false, kStateFp8);
   } else if (vec) {
-    if (fact) KDA_VERIFY_LAUNCH(true, true, false);
-    else KDA_VERIFY_LAUNCH(true, false, false);
+    if (fact) KDA_VERIFY_LAUNCH(true, true, kStateBf16);
+    else KDA_VERIFY_LAUNCH(true, false, kStateBf16);
   } else {
-    if (fact) KDA_VERIFY_LAUNCH(false, true, false);
-    else KDA_VERIFY_LAUNCH(false, false, false);
+    if (fact) KDA_VERIFY_LAUNCH(false, true, kStateBf16);
+    else KDA_VERIFY_LAUNCH(false, false, kStateBf16);
   }
 #undef KDA_VERIFY_LAUNCH
   return hipGetLastError();

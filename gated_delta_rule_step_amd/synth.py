@@ -144,6 +144,18 @@ def fp16_state(case: dict) -> dict:
     return c
 
 
+def fp8_state(case: dict) -> dict:
+    """A copy of a decode, verify or prefill case whose pool holds fp8 e4m3
+    state (state_dtype 2): the state values cast with torch's float8_e4m3fn
+    conversion (the N(0, 0.05) values lie far inside its +-448 range), stored
+    as bytes."""
+    c = dict(case)
+    x = torch.from_numpy(np.ascontiguousarray(f32_from_bits(case["pool"])))
+    c["pool"] = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    c["state_dtype"] = 2
+    return c
+
+
 def decode_case(B: int, N: int = 1024, H: int = 12, seed: int | None = None,
                 inactive_frac: float = 0.05, idx: np.ndarray | None = None) -> dict:
     rng = np.random.Generator(np.random.PCG64(seed_for(1, B) if seed is None else seed))

@@ -43,10 +43,16 @@
  * "Caching"). KDA_STATE_BF16 (0) keeps the pool, the verify checkpoints and the
  * prefill states in bf16; KDA_STATE_FP16 (1) keeps them in fp16 (IEEE binary16,
  * rounded to nearest even), the same 2 bytes with 3 more fraction bits and a
- * range of +-65504. Token inputs, outputs and the verify rings stay bf16 and
- * g_cache fp32. fp16 state needs the vectorised layout (16-byte aligned bases,
- * strides in multiples of 8), else KDA_ERR_UNSUPPORTED; any other value also
- * gives KDA_ERR_UNSUPPORTED.
+ * range of +-65504. KDA_STATE_FP8 (2) keeps them in one byte, the OCP FP8
+ * E4M3 format ("e4m3fn": bias 7, 3 fraction bits, largest finite value 448, no
+ * infinities), rounded to nearest even with magnitudes beyond 448 saturated to
+ * 448: the byte reduction the decode page ("feat(kda): add packed-input CuTe
+ * decode kernel") names as the lever left at its measured HBM fraction; it
+ * halves the state traffic at the cost of a 2^-4 relative step. Token inputs,
+ * outputs and the verify rings stay bf16 and g_cache fp32. fp16 and fp8 states
+ * need the vectorised layout (16-byte aligned bases, strides in multiples of
+ * 8), else KDA_ERR_UNSUPPORTED; any other value also gives
+ * KDA_ERR_UNSUPPORTED.
  *
  * Conventions common to every entry point
  *  - Every pointer is a DEVICE pointer, except those whose name ends in _host.
@@ -99,7 +105,8 @@ enum {
 
 enum {
   KDA_STATE_BF16 = 0,  /* state_dtype: pool / checkpoint elements are bf16 */
-  KDA_STATE_FP16 = 1   /* state_dtype: pool / checkpoint elements are fp16 */
+  KDA_STATE_FP16 = 1,  /* state_dtype: pool / checkpoint elements are fp16 */
+  KDA_STATE_FP8 = 2    /* state_dtype: pool / checkpoint elements are fp8 e4m3 */
 };
 
 typedef enum {
@@ -144,8 +151,10 @@ const char* kda_status_string(kda_status s);
  *  scale              read-out scale
  *  gate_mode          0, or any of KDA_GATE_PRECOMPUTED, KDA_BETA_PRESIGMOID,
  *                     KDA_GATE_PER_HEAD
- *  state_dtype        KDA_STATE_BF16 or KDA_STATE_FP16 (the pool's elements)
- *  state_pool         bf16 pool, num_slots slots of slot_stride elements
+ *  state_dtype        KDA_STATE_BF16, KDA_STATE_FP16 or KDA_STATE_FP8 (the
+ *                     pool's elements)
+ *  state_pool         pool of state_dtype elements, num_slots slots of
+ *                     slot_stride elements
  *                     (may be NULL only when num_slots == 0)
  *  state_indices      int32 [B]: the pool slot of each row
  *  out                bf16 [B, H*128], row stride out_row_stride

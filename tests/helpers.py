@@ -30,7 +30,10 @@ def dev(a, device="cuda"):
 
 
 def bits(t) -> np.ndarray:
+    """A tensor's bit patterns: uint16 for 2-byte elements, uint8 for fp8."""
     import torch
+    if t.element_size() == 1:
+        return t.detach().contiguous().view(torch.uint8).cpu().numpy()
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
@@ -50,35 +53,58 @@ def f16_ulp(x):
     return np.exp2(np.floor(np.log2(np.maximum(np.abs(x), STATE_FLOOR_F16))) - 10)
 
 
-# Pools of either state element type (case["state_dtype"]: 0 bf16, 1 fp16).
+# fp8 e4m3 state (state_dtype 2): 2 fp8 ulps of max(|ref|, 2^-6), the smallest
+# normal (below it the spacing is the subnormal 2^-9). The fp32 arithmetic
+# differs between the two sides by far less than one fp8 step, so a stored
+# element differs by at most the one step a value near a rounding boundary
+# can fall either way.
+STATE_FLOOR_F8 = 2.0 ** -6
+
+
+def f8_ulp(x):
+    return np.exp2(np.floor(np.log2(np.maximum(np.abs(x), STATE_FLOOR_F8))) - 3)
+
+
+# Pools of any state element type (case["state_dtype"]: 0 bf16, 1 fp16, 2 fp8).
 def pool_vals(case, pool_bits):
     """The values a pool's bit patterns hold, as float32."""
-    if case.get("state_dtype", 0):
+    sd = case.get("state_dtype", 0)
+    if sd == 1:
         return np.ascontiguousarray(pool_bits).view(np.float16).astype(np.float32)
+    if sd == 2:
+        import torch
+        b = torch.from_numpy(np.ascontiguousarray(pool_bits, dtype=np.uint8))
+        return b.view(torch.float8_e4m3fn).to(torch.float32).numpy()
     return f32(pool_bits)
 
 
 def pool_dev(case, pool_bits, device="cuda"):
     import torch
-    if case.get("state_dtype", 0):
+    sd = case.get("state_dtype", 0)
+    if sd == 1:
         a = np.ascontiguousarray(pool_bits)
         return torch.from_numpy(a.view(np.int16)).to(device).view(torch.float16)
+    if sd == 2:
+        a = np.ascontiguousarray(pool_bits, dtype=np.uint8)
+        return torch.from_numpy(a).to(device).view(torch.float8_e4m3fn)
     return dev_bf16(pool_bits, device)
 
 
 def check_pool(case, got_bits, ref, what="state"):
-    """check_state in the pool's element type (2 ulps of that type, same floor)."""
-    if not case.get("state_dtype", 0):
+    """check_state in the pool's element type: 2 ulps of that type above its floor."""
+    sd = case.get("state_dtype", 0)
+    if not sd:
         return check_state(got_bits, ref, what)
     got = pool_vals(case, got_bits).astype(np.float64).reshape(ref.shape)
     ref = ref.astype(np.float64)
-    tol = STATE_ULPS * f16_ulp(ref)
+    tol = STATE_ULPS * (f16_ulp(ref) if sd == 1 else f8_ulp(ref))
     bad = ~(np.abs(got - ref) <= tol)
     if bad.any():
         i = np.unravel_index(np.argmax(np.where(bad, np.abs(got - ref) / tol, -np.inf)),
                              ref.shape)
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements beyond "
-                             f"{STATE_ULPS} fp16 ulps; worst at {i}: got {got[i]!r} "
+                             f"{STATE_ULPS} {'fp16' if sd == 1 else 'fp8'} ulps; worst at "
+                             f"{i}: got {got[i]!r} "
                              f"ref {ref[i]!r}")
 
 

@@ -110,9 +110,11 @@ def test_gate_mode_validation(lib):
 
 
 def test_state_dtype_validation(lib):
-    """state_dtype: bf16 (0) or fp16 (1), and fp16 only on the vectorised
-    layout (16-byte aligned bases, strides in multiples of 8)."""
-    assert _decode(lib, sd=2) == UNSUP
+    """state_dtype: bf16 (0), fp16 (1) or fp8 (2), and the last two only on
+    the vectorised layout (16-byte aligned bases, strides in multiples of 8)."""
+    assert _decode(lib, sd=3) == UNSUP
+    assert _decode(lib, sd=2, q=(1 << 20) + 2) == UNSUP
+    assert _decode(lib, sd=2, ss=12 * 128 * 128 + 4) == UNSUP
     assert _decode(lib, sd=-1) == UNSUP
     assert _decode(lib, sd=1, q=(1 << 20) + 2) == UNSUP   # unaligned q: no vectorised path
     assert _decode(lib, sd=1, qs=4610) == UNSUP

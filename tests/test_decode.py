@@ -79,6 +79,16 @@ def test_fp16_state(orc, B):
     check_case(orc, case, pool, out)
 
 
+@pytest.mark.parametrize("B", [1, 512])
+def test_fp8_state(orc, B):
+    """An fp8 e4m3 state pool (state_dtype 2), B = 1 and 512 with inactive
+    rows: the state is read and written as one byte per element (round to
+    nearest even, saturating), outputs stay bf16."""
+    case = synth.fp8_state(synth.decode_case(B=B, H=12))
+    pool, out = run_decode(case)
+    check_case(orc, case, pool, out)
+
+
 @pytest.mark.parametrize("pre", [False, True])
 def test_per_head_gate(orc, pre):
     """The per-head (scalar, GDN-style) gate, raw and pre-computed, at B = 512:

@@ -214,6 +214,8 @@ def _ckpt_roundtrip(orc, case, interval, starts, rows, heads=None):
     H = case["H"]
     hs = np.arange(H) if heads is None else np.asarray(heads)
     fill = synth.filler_bits((rows, H, HD, HD), 7)
+    if case.get("state_dtype", 0) == 2:  # one-byte elements
+        fill = (fill & 0xFF).astype(np.uint8)
     ck = pool_dev(case, fill)
     pool, out = run_prefill(case, checkpoints=ck, ckpt_starts=starts, ckpt_interval=interval)
     check_prefill(orc, case, pool, out, heads=heads)
@@ -270,6 +272,27 @@ def test_fp16_state(orc, docs):
         _ckpt_roundtrip(orc, case, 16, starts, int(counts.sum()))
     else:
         case = synth.fp16_state(synth.prefill_case(synth.DOCS_4, H=12))
+        pool, out = run_prefill(case)
+        check_prefill(orc, case, pool, out)
+
+
+@pytest.mark.parametrize("docs", ["small", "docs4"])
+def test_fp8_state(orc, docs):
+    """fp8 e4m3 initial and final states (state_dtype 2): ragged documents
+    with checkpoints every 16 tokens, a zero-length document started from
+    zeros, and the 4-document set at H = 12."""
+    if docs == "small":
+        case = synth.fp8_state(synth.prefill_case(SMALL_DOCS, H=3, seed=synth.seed_for(4, 3, 23)))
+        counts = np.diff(case["cu_seqlens"]) // 16
+        starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
+        _ckpt_roundtrip(orc, case, 16, starts, int(counts.sum()))
+        case = synth.fp8_state(synth.prefill_case((20, 0, 37), H=2, seed=synth.seed_for(4, 2, 24),
+                                                  use_initial_state=False))
+        pool, out = run_prefill(case)
+        check_prefill(orc, case, pool, out)
+        assert np.all(bits(pool)[case["idx"][1]] == 0)
+    else:
+        case = synth.fp8_state(synth.prefill_case(synth.DOCS_4, H=12))
         pool, out = run_prefill(case)
         check_prefill(orc, case, pool, out)
 

@@ -37,12 +37,14 @@ def _tok_arrays(qkv, gate, beta, H):
 def build_case(orc, B, T, w_ring=16, flush_min=None, fold_p=0.0, hist_max=None, N=1024, H=12,
                workload=3, inactive_frac=0.0, seed=None, state_dtype=0):
     """A verify case whose live ring history comes from the oracle (state_dtype
-    1: fp16 checkpoints)."""
+    1: fp16 checkpoints, 2: fp8 e4m3 checkpoints)."""
     case = synth.verify_case(B=B, T=T, N=N, H=H, w_ring=w_ring, flush_min=flush_min,
                              fold_p=fold_p, hist_max=hist_max, workload=workload,
                              inactive_frac=inactive_frac, seed=seed)
-    if state_dtype:
+    if state_dtype == 1:
         case = synth.fp16_state(case)
+    elif state_dtype == 2:
+        case = synth.fp8_state(case)
     R = case["R"]
     slots, cidx = compact_slots(case["idx"], N)
     case["slots"], case["cidx"] = slots, cidx
@@ -214,6 +216,16 @@ def test_fp16_checkpoints(orc, T, fm, p, hist_max, w):
     fp16 MFMA operands, folds stored as binary16, rings still bf16."""
     case = build_case(orc, 512, T, w_ring=w, flush_min=fm, fold_p=p, hist_max=hist_max,
                       state_dtype=1)
+    verify_roundtrip(orc, case)
+
+
+@pytest.mark.parametrize("T,fm,p,hist_max,w", [(8, 9, 0.5, None, 16), (8, 9, 0.0, 0, 16),
+                                              (8, 25, 0.0, 24, 32)])
+def test_fp8_checkpoints(orc, T, fm, p, hist_max, w):
+    """fp8 e4m3 checkpoints (state_dtype 2) at B = 512: the checkpoint widened
+    to bf16 B operands (exactly), folds stored as fp8, rings still bf16."""
+    case = build_case(orc, 512, T, w_ring=w, flush_min=fm, fold_p=p, hist_max=hist_max,
+                      state_dtype=2)
     verify_roundtrip(orc, case)
 
 

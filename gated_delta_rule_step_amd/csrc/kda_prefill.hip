@@ -823,7 +823,11 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
       a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(klo, uhi, a, 0, 0, 0);
       acc[mt] = a;
     }
-    // intermediate checkpoint after this chunk
+    // record ch+1 (its loads were issued a chunk ago) into the other buffer,
+    // last read before the previous barrier; then the loads of record ch+2
+    store_rec((ch + 1) & 1);
+    load_rec(min(ch + 2, nchunks - 1));
+    // intermediate checkpoint after this chunk, after the record loads
     if (p.ckpt && (ch + 1) % ckpt_every == 0 && int64_t(ch + 1) * C <= kept) {
       const int64_t row = ckpt_row0 + (ch + 1) / ckpt_every - 1;
       if (row >= 0 && row < p.ckpt_rows) {
@@ -833,10 +837,6 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
           st4_store<SF, VEC>(p.ckpt, ce + v * D + 16 * mt + 4 * g4, acc[mt]);
       }
     }
-    // record ch+1 (its loads were issued a chunk ago) into the other buffer,
-    // last read before the previous barrier; then the loads of record ch+2
-    store_rec((ch + 1) & 1);
-    load_rec(min(ch + 2, nchunks - 1));
     __syncthreads();  // this chunk's buffer is read; the next one is written
   }
 

@@ -658,23 +658,51 @@ __global__ __launch_bounds__(kThreads) void handoff_kernel(PrefillParams p) {
 // ahead of use and registers -> LDS (double buffer) one chunk ahead, so a
 // chunk's operands are in LDS when it starts and the next record's loads
 // overlap its arithmetic.
-constexpr int kChainThreads = 512;
-constexpr int kChainRounds = (kRecUnits + kChainThreads - 1) / kChainThreads;  // 4
-static_assert(kRecUnits > (kChainRounds - 1) * kChainThreads, "every round has work");
+//
+// With few chains (documents x heads below the CU count) each chain is split
+// by value channels over VS = 2 workgroups of 4 waves on different CUs: the
+// value channels of the state evolve independently, and a CU then holds one
+// wave per SIMD instead of two, so a chunk's VALU and MFMA issue per SIMD
+// halves. Each part stages the record's shared operands (W, Q, K~, P,
+// exp(Gam_c)) and only its own U0 tiles.
+template <int VS>
+struct ChainShape {
+  static constexpr int kThreads = 512 / VS;
+  static constexpr int kWaves = 8 / VS;                     // value tiles of 16 channels
+  static constexpr int kShared = kRecU0 / 16;               // W, Q, K~ units
+  static constexpr int kOwnU0 = kWaves * 64;                // this part's U0 units
+  static constexpr int kTail = kRecUnits - kRecP / 16;      // P, exp(Gam_c) units
+  static constexpr int kUnits = kShared + kOwnU0 + kTail;   // units staged per chunk
+  static constexpr int kRounds = (kUnits + kThreads - 1) / kThreads;
+  static_assert(kUnits > (kRounds - 1) * kThreads, "every round has work");
+  // record unit of staged unit i (< kUnits) of part `part`
+  __device__ static int unit(int i, int part) {
+    if (i < kShared) return i;
+    if (i < kShared + kOwnU0) return kRecU0 / 16 + part * kOwnU0 + (i - kShared);
+    return kRecP / 16 + (i - kShared - kOwnU0);
+  }
+};
+static_assert(ChainShape<1>::kUnits == kRecUnits, "the whole record");
 
 // SF: the element format of the pool (initial and final states) and the
-// checkpoints (kStateBf16, kStateFp16, kStateFp8).
-template <bool VEC, int SF>
-__global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, DocOrder ord) {
+// checkpoints (kStateBf16, kStateFp16, kStateFp8). VS: workgroups per chain.
+template <bool VEC, int SF, int VS>
+__global__ __launch_bounds__(ChainShape<VS>::kThreads) void chain_kernel(PrefillParams p,
+                                                                        DocOrder ord) {
+  using Shape = ChainShape<VS>;
+  constexpr int kChainThreads = Shape::kThreads;
+  constexpr int kChainRounds = Shape::kRounds;
   __shared__ __align__(16) uint8_t rbuf[2][kRecBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g4 = lane >> 4;
   const int n16 = lane & 15;
-  const int v = 16 * wave + n16;  // value channel of this lane
-  const int h = int(blockIdx.x % p.H);
-  const int rank = int(blockIdx.x / p.H);
+  const int part = int(blockIdx.x % VS);
+  const int vt = part * Shape::kWaves + wave;  // value tile of this wave
+  const int v = 16 * vt + n16;                 // value channel of this lane
+  const int h = int((blockIdx.x / VS) % p.H);
+  const int rank = int(blockIdx.x / VS / p.H);
   const int doc = ord.n > 0 ? ord.doc[rank] : rank;
   const int64_t t0 = p.cu_seqlens[doc];
   const int64_t len = int64_t(p.cu_seqlens[doc + 1]) - t0;
@@ -683,18 +711,19 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
   const bool active = slot >= 0 && int64_t(slot) < p.num_slots && rbase >= 0 &&
                       (p.ring_tail == 0 || rbase < p.ring_rows);
 
+  constexpr int kPartCh = D / VS;  // value channels (state rows) of this part
   if (!active) {  // zero outputs, no state access
-    for (int64_t e = tid; e < len * D; e += kChainThreads)
-      p.out[(t0 + e / D) * p.out_tok_stride + h * D + (e % D)] = 0;
+    for (int64_t e = tid; e < len * kPartCh; e += kChainThreads)
+      p.out[(t0 + e / kPartCh) * p.out_tok_stride + h * D + part * kPartCh + (e % kPartCh)] = 0;
     return;
   }
   static_assert(VEC || SF == kStateBf16, "fp16 and fp8 states use the vectorised layout");
   const int64_t se = int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS;  // element offset
   if (len == 0) {  // final state = initial state: untouched, or zeros without one
-    if (!p.use_initial_state) {
-      uint16_t* z = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(p.state_pool) +
-                                                se * kStateBytes<SF>);
-      for (int e = tid; e < HEAD_ELEMS * kStateBytes<SF> / 2; e += kChainThreads) z[e] = 0;
+    if (!p.use_initial_state) {  // this part's state rows
+      uint16_t* z = reinterpret_cast<uint16_t*>(
+          static_cast<uint8_t*>(p.state_pool) + (se + part * kPartCh * D) * kStateBytes<SF>);
+      for (int e = tid; e < kPartCh * D * kStateBytes<SF> / 2; e += kChainThreads) z[e] = 0;
     }
     return;
   }
@@ -714,24 +743,25 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
   auto rec_of = [&](int ch) {
     return reinterpret_cast<const u32x4*>(ws + ((sigma0 + ch) * p.H + h) * int64_t(kRecBytes));
   };
-  // Thread tid moves units tid + 512 rd; the units past the record's end in
-  // the last round load a unit of the record again (a fixed load count per
-  // chunk) and are not stored.
+  // Thread tid moves staged units tid + kChainThreads rd (to the record's
+  // own offsets in LDS); the units past the staged set in the last round load
+  // a staged unit again (a fixed load count per chunk) and are not stored.
   u32x4 pre[kChainRounds];
   auto load_rec = [&](int ch) {
     const u32x4* r = rec_of(ch);
 #pragma unroll
     for (int rd = 0; rd < kChainRounds; ++rd) {
-      const int u = tid + kChainThreads * rd;
-      pre[rd] = __builtin_nontemporal_load(r + (u < kRecUnits ? u : u - kRecUnits));
+      const int i = tid + kChainThreads * rd;
+      pre[rd] = __builtin_nontemporal_load(
+          r + Shape::unit(i < Shape::kUnits ? i : i - Shape::kUnits, part));
     }
   };
   auto store_rec = [&](int b) {
     u32x4* d = reinterpret_cast<u32x4*>(&rbuf[b][0]);
 #pragma unroll
     for (int rd = 0; rd < kChainRounds; ++rd) {
-      const int u = tid + kChainThreads * rd;
-      if (rd < kChainRounds - 1 || u < kRecUnits) d[u] = pre[rd];
+      const int i = tid + kChainThreads * rd;
+      if (rd < kChainRounds - 1 || i < Shape::kUnits) d[Shape::unit(i, part)] = pre[rd];
     }
   };
 
@@ -795,7 +825,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(PrefillParams p, D
       yq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi, shi, yq, 0, 0, 0);
     }
     // U = U0 - W S^T (accumulator layout: rows 4*g4 + i, value channel of the lane)
-    const f32x4 u0 = *reinterpret_cast<const f32x4*>(R + kRecU0 + (wave * 64 + lane) * 16);
+    const f32x4 u0 = *reinterpret_cast<const f32x4*>(R + kRecU0 + (vt * 64 + lane) * 16);
     const f32x4 uf = u0 - (y0 + (y1 + y2));
     s16x4 uhi, ulo;
     split4(uf, uhi, ulo);
@@ -866,7 +896,7 @@ hipError_t launch_prefill(const PrefillParams& p, const int32_t* cu_host, bool v
                           hipStream_t stream) {
   const int64_t blocks = int64_t(p.n_docs) * p.H;
   if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffff || p.H > 65535) return hipErrorInvalidValue;
+  if (2 * blocks > 0x7fffffff || p.H > 65535) return hipErrorInvalidValue;
   const int64_t slots = int64_t(p.n_docs) + (p.total_tokens >> 4);
   if (slots > 0x7fffffff) return hipErrorInvalidValue;
   // Longest documents first: their chains bound the makespan.
@@ -941,18 +971,28 @@ hipError_t launch_prefill(const PrefillParams& p, const int32_t* cu_host, bool v
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  dim3 grid(static_cast<unsigned>(blocks)), block(kChainThreads);
+  // Fewer chains than CUs: two workgroups per chain (by value channels).
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  const bool split = blocks < cus;
   // fp16 and fp8 states run on the vectorised path only (the host requires it)
   if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
-  if (p.state_fmt == kStateFp16) {
-    hipLaunchKernelGGL((chain_kernel<true, kStateFp16>), grid, block, 0, stream, p, ord);
-  } else if (p.state_fmt == kStateFp8) {
-    hipLaunchKernelGGL((chain_kernel<true, kStateFp8>), grid, block, 0, stream, p, ord);
-  } else if (vec) {
-    hipLaunchKernelGGL((chain_kernel<true, kStateBf16>), grid, block, 0, stream, p, ord);
-  } else {
-    hipLaunchKernelGGL((chain_kernel<false, kStateBf16>), grid, block, 0, stream, p, ord);
-  }
+#define KDA_CHAIN_LAUNCH(V, S)                                                              \
+  do {                                                                                      \
+    if (split)                                                                              \
+      hipLaunchKernelGGL((chain_kernel<V, S, 2>), dim3(static_cast<unsigned>(2 * blocks)),  \
+                         dim3(ChainShape<2>::kThreads), 0, stream, p, ord);                 \
+    else                                                                                    \
+      hipLaunchKernelGGL((chain_kernel<V, S, 1>), dim3(static_cast<unsigned>(blocks)),      \
+                         dim3(ChainShape<1>::kThreads), 0, stream, p, ord);                 \
+  } while (0)
+  if (p.state_fmt == kStateFp16) KDA_CHAIN_LAUNCH(true, kStateFp16);
+  else if (p.state_fmt == kStateFp8) KDA_CHAIN_LAUNCH(true, kStateFp8);
+  else if (vec) KDA_CHAIN_LAUNCH(true, kStateBf16);
+  else KDA_CHAIN_LAUNCH(false, kStateBf16);
+#undef KDA_CHAIN_LAUNCH
   return hipGetLastError();
 }
 

@@ -165,6 +165,27 @@ __device__ __forceinline__ void load8_bf16(const uint16_t* p, float (&x)[8]) {
   }
 }
 
+// 8 consecutive bf16 as raw bits (plain loads: token inputs, shared by the
+// waves of a head through L2), and their widening to fp32.
+template <bool VEC>
+__device__ __forceinline__ u32x4 load8_bits(const uint16_t* p) {
+  if constexpr (VEC) {
+    return *reinterpret_cast<const u32x4*>(p);
+  } else {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = uint32_t(p[2 * i]) | (uint32_t(p[2 * i + 1]) << 16);
+    return w;
+  }
+}
+__device__ __forceinline__ void unpack8_bf16(u32x4 w, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf_lo(w[i]);
+    x[2 * i + 1] = bf_hi(w[i]);
+  }
+}
+
 template <bool VEC>
 __device__ __forceinline__ u32x4 load8_raw(const uint16_t* p) {
   if constexpr (VEC) {

@@ -20,9 +20,8 @@
 //    updated 4-row group is stored as soon as it is computed (holding all
 //    stores back to the end measured ~15% slower);
 //  * the two dot products S'k_hat and S'q_hat of a row are reduced over the
-//    16 lanes of a DPP row (no LDS, no barrier); the decay is folded into the
-//    reduction operands (S' x = S (alpha * x)), so the state is touched by
-//    exactly two FMAs for the reductions and one multiply + one FMA for the
+//    16 lanes of a DPP row (no LDS, no barrier); each state element takes one
+//    multiply for the decay, two FMAs for the reductions and one FMA for the
 //    update, and the read-out uses o = scale (S' q_hat + u (k_hat . q_hat));
 //  * fp32 math, bf16 storage: unpack by shift/mask, repack with the hardware
 //    round-to-nearest-even conversion; state traffic uses non-temporal hints.
@@ -37,14 +36,25 @@ namespace kda {
 // one gate value (and dt_bias) per head for all key channels.
 // SF: the pool's element format (kStateBf16, kStateFp16, kStateFp8); the
 // 16-bit formats move 8 elements per 128-bit access, fp8 per 64-bit access.
+// Five waves per SIMD (at most 96 VGPRs: the register allocation rounds to 8,
+// so 97..104 would leave four); the fp8 64-row tile holds twice the state
+// words and keeps four.
+template <int LOADS, int SF>
+constexpr int kDecodeWaves = (SF == kStateFp8 && LOADS == 16) ? 4 : 5;
+
 template <int LOADS, bool VEC, int GK, int SF>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDecodeWaves<LOADS, SF>)))
+void decode_kernel(DecodeParams p) {
   constexpr bool GRAW = !(GK & kGatePrecomputed);
   constexpr bool GHEAD = (GK & kGatePerHead) != 0;
   constexpr int ROWS = 4 * LOADS;
   constexpr int VBLOCKS = D / ROWS;
   const int lane = threadIdx.x & 63;
-  const int64_t tile = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  // The tile, and with it the row, head and slot, is uniform over the wave:
+  // said so with readfirstlane, the address arithmetic runs on the scalar
+  // unit and the slot index is a scalar load.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t tile = int64_t(blockIdx.x) * (blockDim.x >> 6) + wave;
   const int vb = int(tile % VBLOCKS);
   const int64_t bh = tile / VBLOCKS;
   if (bh >= int64_t(p.B) * p.H) return;
@@ -56,12 +66,45 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 
   uint16_t* outp = p.out + b * p.out_row_stride + int64_t(h) * D + vbase;
   const int32_t slot = p.state_indices[b];
+
+  // The token inputs do not depend on the slot: their loads are issued before
+  // the slot index is waited on, and before the state loads, so that the
+  // prologue below runs while the state is still in flight (the memory
+  // counter completes loads in issue order).
+  const u32x4 qw = load8_bits<VEC>(p.q + b * p.q_row_stride + h * D + kb * 8);
+  const u32x4 kw = load8_bits<VEC>(p.k + b * p.k_row_stride + h * D + kb * 8);
+  u32x4 gw = {0u, 0u, 0u, 0u};
+  uint16_t gh = 0;
+  if constexpr (GHEAD) gh = p.g[b * p.g_row_stride + h];
+  else gw = load8_bits<VEC>(p.g + b * p.g_row_stride + h * D + kb * 8);
+  float dtb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float alog = 0.f;
+  if constexpr (GRAW) {
+    if constexpr (GHEAD) {
+      const float dh = p.dt_bias[h];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dtb[c] = dh;
+    } else {
+      load8_f32<VEC>(p.dt_bias + h * D + kb * 8, dtb);
+    }
+    alog = p.A_log[h];
+  }
+  const uint16_t bw = p.beta[b * p.beta_row_stride + h];
+  uint16_t vw[LOADS];
+  const uint16_t* vp = p.v + b * p.v_row_stride + h * D + vbase + rg;
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) vw[i] = vp[4 * i];
+
+  // Pin the token words in registers here: otherwise the compiler sinks their
+  // loads below the branch, behind the wait for the slot index.
+  asm volatile("" ::"v"(qw), "v"(kw), "v"(gw));
+
   if (!(slot >= 0 && int64_t(slot) < p.num_slots)) {
     if (lane < ROWS) outp[lane] = 0;
     return;
   }
 
-  // Issue every state load first.
+  // State loads.
   static_assert(VEC || SF == kStateBf16, "fp16 and fp8 states use the vectorised layout");
   const int64_t se = int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS +
                      int64_t(vbase + rg) * D + kb * 8;  // element offset
@@ -73,34 +116,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     else s[i] = load8_raw<VEC>(sp + i * 4 * D);
   }
 
-  // Per-token prologue for this lane's 8 key channels.
-  float q[8], k[8], gr[8], dtb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  load8_bf16<VEC>(p.q + b * p.q_row_stride + h * D + kb * 8, q);
-  load8_bf16<VEC>(p.k + b * p.k_row_stride + h * D + kb * 8, k);
+  // Per-token prologue for this lane's 8 key channels, on the hardware
+  // exponential and logarithm (about 1 ulp in fp32).
+  float q[8], k[8], gr[8];
+  unpack8_bf16(qw, q);
+  unpack8_bf16(kw, k);
   if constexpr (GHEAD) {
-    const float gh = bf1(p.g[b * p.g_row_stride + h]);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) gr[c] = gh;
+    for (int c = 0; c < 8; ++c) gr[c] = bf1(gh);
   } else {
-    load8_bf16<VEC>(p.g + b * p.g_row_stride + h * D + kb * 8, gr);
+    unpack8_bf16(gw, gr);
   }
-  float neg_ea = 0.f;
-  if constexpr (GRAW) {
-    if constexpr (GHEAD) {
-      const float dh = p.dt_bias[h];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) dtb[c] = dh;
-    } else {
-      load8_f32<VEC>(p.dt_bias + h * D + kb * 8, dtb);
-    }
-    neg_ea = -expf(p.A_log[h]);
-  }
-  const float braw = bf1(p.beta[b * p.beta_row_stride + h]);
-  const float beta = (p.gate_mode & kBetaPresigmoid) ? braw : sigmoidf(braw);
+  const float neg_ea = GRAW ? -fexp(alog) : 0.f;
+  const float braw = bf1(bw);
+  const float beta = (p.gate_mode & kBetaPresigmoid) ? braw : fsigmoid(braw);
   float vrow[LOADS];
-  const uint16_t* vp = p.v + b * p.v_row_stride + h * D + vbase + rg;
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) vrow[i] = bf1(vp[4 * i]);
+  for (int i = 0; i < LOADS; ++i) vrow[i] = bf1(vw[i]);
 
   float sq = 0.f, sk = 0.f, sqk = 0.f;
 #pragma unroll
@@ -115,14 +147,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   const float rq = 1.0f / sqrtf(sq + 1e-6f);
   const float rk = 1.0f / sqrtf(sk + 1e-6f);
   const float kq = sqk * rq * rk;  // k_hat . q_hat
-  float al[8], kh[8], ka[8], qa[8];
+  float al[8], kh[8], qh[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    al[c] = expf(GRAW ? gate_logdecay(gr[c] + dtb[c], neg_ea, p.lower_bound)
+    al[c] = fexp(GRAW ? fgate(gr[c] + dtb[c], neg_ea, p.lower_bound)
                       : gate_given(gr[c], p.lower_bound));
     kh[c] = k[c] * rk;
-    ka[c] = al[c] * kh[c];
-    qa[c] = al[c] * (q[c] * rq);
+    qh[c] = q[c] * rq;
   }
 
   float osel = 0.f;
@@ -130,46 +161,39 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   for (int i = 0; i < LOADS; ++i) {
     float x[8];
     st8_unpack<SF>(s[i], x);
+    // the decayed row S' = alpha * S, then both dot products from it
     float dk = 0.f, dq = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      dk = fmaf(x[c], ka[c], dk);
-      dq = fmaf(x[c], qa[c], dq);
+      x[c] *= al[c];
+      dk = fmaf(x[c], kh[c], dk);
+      dq = fmaf(x[c], qh[c], dq);
     }
     dk = row16_sum(dk);
     dq = row16_sum(dq);
     const float u = beta * (vrow[i] - dk);
     const float o = p.scale * fmaf(u, kq, dq);
     if (kb == i) osel = o;
-    St8<SF> w;
-    if constexpr (SF == kStateFp8) {
-      float a[8];
+    float a[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) a[c] = fmaf(al[c], x[c], kh[c] * u);
-      w = st8_pack<SF>(a);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a0 = fmaf(al[2 * j], x[2 * j], kh[2 * j] * u);
-        const float a1 = fmaf(al[2 * j + 1], x[2 * j + 1], kh[2 * j + 1] * u);
-        w[j] = st_pack<SF>(a0, a1);
-      }
-    }
+    for (int c = 0; c < 8; ++c) a[c] = fmaf(kh[c], u, x[c]);
+    const St8<SF> w = st8_pack<SF>(a);
     if constexpr (SF == kStateFp8) st8_store_nt<SF>(p.state_pool, se + i * 4 * D, w);
     else store8_raw<VEC>(sp + i * 4 * D, w);
   }
   if (kb < LOADS) outp[4 * kb + rg] = to_bf16(osel);
 }
 
-// Launch shape: 256-thread workgroups of four independent waves. Large
-// batches use 32-row tiles (8 loads per lane, four waves = one head), or with
-// fp8 state 64-row tiles (16 loads of 8 bytes, the same 32 registers of state
-// and bytes in flight per wave); small batches use 8-row tiles so that a few
-// heads still spread over many CUs.
+// Launch shape: 256-thread workgroups of four independent waves. The tile
+// shrinks with the batch so that a few heads still spread over many CUs:
+// up to 64 heads take 8-row tiles (2 loads per lane), up to 4095 heads
+// 16-row tiles (4 loads), larger batches 32-row tiles (8 loads, four waves =
+// one head), or with fp8 state 64-row tiles (16 loads of 8 bytes: the same
+// 32 registers of state and bytes in flight per wave).
 hipError_t launch_decode(const DecodeParams& p, bool vec, hipStream_t stream) {
   const int64_t heads = int64_t(p.B) * p.H;
-  const bool small = heads < 1024;
-  const int loads = small ? 2 : (p.state_fmt == kStateFp8 ? 16 : 8);
+  const int size = heads <= 64 ? 0 : (heads < 4096 ? 1 : 2);
+  const int loads = size == 0 ? 2 : size == 1 ? 4 : (p.state_fmt == kStateFp8 ? 16 : 8);
   const int64_t tiles = heads * (D / (4 * loads));
   const int64_t blocks = (tiles + 3) / 4;
   if (blocks == 0) return hipSuccess;
@@ -185,21 +209,19 @@ hipError_t launch_decode(const DecodeParams& p, bool vec, hipStream_t stream) {
       default: hipLaunchKernelGGL((decode_kernel<L, V, 5, F>), grid, block, 0, stream, p);      \
     }                                                                                           \
   } while (0)
+#define KDA_DECODE_SIZES(V, F, BIG)                 \
+  do {                                              \
+    if (size == 0) KDA_DECODE_LAUNCH(2, V, F);      \
+    else if (size == 1) KDA_DECODE_LAUNCH(4, V, F); \
+    else KDA_DECODE_LAUNCH(BIG, V, F);              \
+  } while (0)
   // fp16 and fp8 states run on the vectorised path only (the host requires it)
   if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
-  if (p.state_fmt == kStateFp16) {
-    if (small) KDA_DECODE_LAUNCH(2, true, kStateFp16);
-    else KDA_DECODE_LAUNCH(8, true, kStateFp16);
-  } else if (p.state_fmt == kStateFp8) {
-    if (small) KDA_DECODE_LAUNCH(2, true, kStateFp8);
-    else KDA_DECODE_LAUNCH(16, true, kStateFp8);
-  } else if (small) {
-    if (vec) KDA_DECODE_LAUNCH(2, true, kStateBf16);
-    else KDA_DECODE_LAUNCH(2, false, kStateBf16);
-  } else {
-    if (vec) KDA_DECODE_LAUNCH(8, true, kStateBf16);
-    else KDA_DECODE_LAUNCH(8, false, kStateBf16);
-  }
+  if (p.state_fmt == kStateFp16) KDA_DECODE_SIZES(true, kStateFp16, 8);
+  else if (p.state_fmt == kStateFp8) KDA_DECODE_SIZES(true, kStateFp8, 16);
+  else if (vec) KDA_DECODE_SIZES(true, kStateBf16, 8);
+  else KDA_DECODE_SIZES(false, kStateBf16, 8);
+#undef KDA_DECODE_SIZES
 #undef KDA_DECODE_LAUNCH
   return hipGetLastError();
 }

@@ -58,43 +58,44 @@ def check_case(orc, case, pool_dev, out_dev):
     assert np.all(ob[~active] == 0), "inactive rows must output +0.0"
 
 
-@pytest.mark.parametrize("gate_mode", [1, 2, 3])
-def test_precomputed_gate_conventions(orc, gate_mode):
+@pytest.mark.parametrize("gate_mode,B", [(1, 512), (2, 512), (3, 512), (3, 32)])
+def test_precomputed_gate_conventions(orc, gate_mode, B):
     """[decode] "T=1 fast path inside recurrent_kda": the pre-computed form
     (log-space g, decay = exp(g); pre-sigmoided beta), alone or together, at
-    B = 512 with 5 % inactive rows; A_log and dt_bias are not passed when the
-    gate is pre-computed."""
-    case = synth.precomputed_gate(synth.decode_case(B=512, H=12), gate_mode,
-                                  synth.seed_for(1, 512, 100 + gate_mode))
+    B = 512 (and 32) with 5 % inactive rows; A_log and dt_bias are not passed
+    when the gate is pre-computed."""
+    case = synth.precomputed_gate(synth.decode_case(B=B, H=12), gate_mode,
+                                  synth.seed_for(1, B, 100 + gate_mode))
     pool, out = run_decode(case)
     check_case(orc, case, pool, out)
 
 
-@pytest.mark.parametrize("B", [1, 512])
+@pytest.mark.parametrize("B", [1, 32, 512])
 def test_fp16_state(orc, B):
-    """An fp16 state pool (state_dtype 1), B = 1 and 512 with inactive rows:
+    """An fp16 state pool (state_dtype 1), B = 1, 32 and 512 (the three tile
+    sizes) with inactive rows:
     the state is read and written as binary16, outputs stay bf16."""
     case = synth.fp16_state(synth.decode_case(B=B, H=12))
     pool, out = run_decode(case)
     check_case(orc, case, pool, out)
 
 
-@pytest.mark.parametrize("B", [1, 512])
+@pytest.mark.parametrize("B", [1, 32, 512])
 def test_fp8_state(orc, B):
-    """An fp8 e4m3 state pool (state_dtype 2), B = 1 and 512 with inactive
-    rows: the state is read and written as one byte per element (round to
+    """An fp8 e4m3 state pool (state_dtype 2), B = 1, 32 and 512 (the three
+    tile sizes) with inactive rows: the state is read and written as one byte per element (round to
     nearest even, saturating), outputs stay bf16."""
     case = synth.fp8_state(synth.decode_case(B=B, H=12))
     pool, out = run_decode(case)
     check_case(orc, case, pool, out)
 
 
-@pytest.mark.parametrize("pre", [False, True])
-def test_per_head_gate(orc, pre):
-    """The per-head (scalar, GDN-style) gate, raw and pre-computed, at B = 512:
-    gate [B, H] and dt_bias [H]."""
-    case = synth.per_head_gate(synth.decode_case(B=512, H=12), pre,
-                               synth.seed_for(1, 512, 120 + int(pre)))
+@pytest.mark.parametrize("pre,B", [(False, 512), (True, 512), (False, 32)])
+def test_per_head_gate(orc, pre, B):
+    """The per-head (scalar, GDN-style) gate, raw and pre-computed, at B = 512
+    (and 32): gate [B, H] and dt_bias [H]."""
+    case = synth.per_head_gate(synth.decode_case(B=B, H=12), pre,
+                               synth.seed_for(1, B, 120 + int(pre)))
     pool, out = run_decode(case)
     check_case(orc, case, pool, out)
 
@@ -177,11 +178,12 @@ def test_read_out_scale_and_other_head_counts(orc):
     check_case(orc, case, pool, out)
 
 
-def test_misaligned_views_odd_strides_and_padded_pool(orc):
-    """Unaligned bases and odd strides take the scalar path; the pool has
-    padded slots (slot stride > H*128*128, odd)."""
-    B, H, N = 9, 12, 6
-    case = synth.decode_case(B=B, N=N, H=H, seed=15, inactive_frac=0.2)
+@pytest.mark.parametrize("B,N", [(4, 6), (9, 6), (350, 360)])
+def test_misaligned_views_odd_strides_and_padded_pool(orc, B, N):
+    """Unaligned bases and odd strides take the scalar path (at each of its
+    tile sizes); the pool has padded slots (slot stride > H*128*128, odd)."""
+    H = 12
+    case = synth.decode_case(B=B, N=N, H=H, seed=15 + B, inactive_frac=0.2)
     W = H * HD
     rs = 3 * W + 3  # odd row stride
     buf = torch.zeros(B * rs + 8, dtype=torch.bfloat16, device="cuda")

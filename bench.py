@@ -50,7 +50,7 @@ N_SLOTS = 1024
 # only for the kernel sources the counters were taken on: the digest below
 # turns it into null once those sources change.
 COUNTED_TRAFFIC = {
-    "kda::decode_kernel<8, true, 0, 0>": dict(
+    "kda::decode_kernel<4, true, 0, 0>": dict(
         sources=("gated_delta_rule_step_amd/csrc/kda_decode.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
@@ -593,8 +593,8 @@ def main():
                    "B": B, "H": H, "T": 1, "pool_slots": N_SLOTS, "device": dev_name},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": wm.HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / wm.HBM_PEAK_GBS, 4),
-                     "traffic": counted_traffic("kda::decode_kernel<8, true, 0, 0>"),
-                     "kernel": "kda::decode_kernel<8, true, 0, 0>",
+                     "traffic": counted_traffic("kda::decode_kernel<4, true, 0, 0>"),
+                     "kernel": "kda::decode_kernel<4, true, 0, 0>",
                      "kernel_us_avg": round(us_ev, 3), "algorithmic_bytes": nbytes},
         "cpu_baseline": cpu,
         "points": points,

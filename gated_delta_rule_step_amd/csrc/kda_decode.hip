@@ -10,13 +10,15 @@
 // The kernel is HBM-bound (32 KiB read + 32 KiB written per head for ~115
 // kflop), so the design is about streaming the state:
 //  * one wave owns a tile of ROWS = 4 * LOADS value rows of one (row, head);
-//    a 256-thread workgroup holds 4 waves, so the (row, head) inputs are
-//    fetched into one L2;
+//    the tile, row, head and slot are wave-uniform, so addressing runs on
+//    the scalar unit;
 //  * lane l covers key channels 8*(l%16) .. +7 of value rows
 //    vbase + 4*i + l/16 (i < LOADS): every state access is a 128-bit load or
 //    store (64-bit with fp8 elements) and one load instruction covers four
 //    full rows;
-//  * all LOADS state loads are issued before any prologue math, and each
+//  * the token inputs are loaded together with the slot index, the LOADS
+//    state loads follow as soon as the index is known, and the prologue
+//    (on the hardware exp/log) runs while the state is in flight; each
 //    updated 4-row group is stored as soon as it is computed (holding all
 //    stores back to the end measured ~15% slower);
 //  * the two dot products S'k_hat and S'q_hat of a row are reduced over the
@@ -36,9 +38,9 @@ namespace kda {
 // one gate value (and dt_bias) per head for all key channels.
 // SF: the pool's element format (kStateBf16, kStateFp16, kStateFp8); the
 // 16-bit formats move 8 elements per 128-bit access, fp8 per 64-bit access.
-// Five waves per SIMD (at most 96 VGPRs: the register allocation rounds to 8,
-// so 97..104 would leave four); the fp8 64-row tile holds twice the state
-// words and keeps four.
+// A register budget that keeps at least five waves per SIMD (at most 96
+// VGPRs; the allocation rounds to 8). The 8- and 16-row tiles need far
+// fewer; the fp8 64-row tile holds twice the state words and keeps four.
 template <int LOADS, int SF>
 constexpr int kDecodeWaves = (SF == kStateFp8 && LOADS == 16) ? 4 : 5;
 
@@ -184,16 +186,20 @@ void decode_kernel(DecodeParams p) {
   if (kb < LOADS) outp[4 * kb + rg] = to_bf16(osel);
 }
 
-// Launch shape: 256-thread workgroups of four independent waves. The tile
-// shrinks with the batch so that a few heads still spread over many CUs:
-// up to 64 heads take 8-row tiles (2 loads per lane), up to 4095 heads
-// 16-row tiles (4 loads), larger batches 32-row tiles (8 loads, four waves =
-// one head), or with fp8 state 64-row tiles (16 loads of 8 bytes: the same
-// 32 registers of state and bytes in flight per wave).
+// Launch shape: 256-thread workgroups of four independent waves. A wave
+// lives for one tile, so the bytes in flight per CU grow with the waves a
+// SIMD holds: 16-row tiles (4 loads per lane, ~67 VGPRs, seven waves per
+// SIMD) streamed the B = 512 pool ~4% faster than 32-row tiles at five
+// waves, and as fast at B = 128. Up to 64 heads take 8-row tiles (2 loads)
+// so that a few heads still spread over many CUs. fp8 states move 8 bytes
+// per load; from 4096 heads they take 64-row tiles (16 loads of 8 bytes,
+// the same 32 registers of state per wave as the 32-row bf16 tile), which
+// measured faster than 16- or 32-row fp8 tiles.
 hipError_t launch_decode(const DecodeParams& p, bool vec, hipStream_t stream) {
   const int64_t heads = int64_t(p.B) * p.H;
-  const int size = heads <= 64 ? 0 : (heads < 4096 ? 1 : 2);
-  const int loads = size == 0 ? 2 : size == 1 ? 4 : (p.state_fmt == kStateFp8 ? 16 : 8);
+  const bool fp8 = p.state_fmt == kStateFp8;
+  const int size = heads <= 64 ? 0 : (fp8 && heads >= 4096 ? 2 : 1);
+  const int loads = size == 0 ? 2 : (size == 1 ? 4 : 16);
   const int64_t tiles = heads * (D / (4 * loads));
   const int64_t blocks = (tiles + 3) / 4;
   if (blocks == 0) return hipSuccess;
@@ -209,18 +215,23 @@ hipError_t launch_decode(const DecodeParams& p, bool vec, hipStream_t stream) {
       default: hipLaunchKernelGGL((decode_kernel<L, V, 5, F>), grid, block, 0, stream, p);      \
     }                                                                                           \
   } while (0)
-#define KDA_DECODE_SIZES(V, F, BIG)                 \
-  do {                                              \
-    if (size == 0) KDA_DECODE_LAUNCH(2, V, F);      \
-    else if (size == 1) KDA_DECODE_LAUNCH(4, V, F); \
-    else KDA_DECODE_LAUNCH(BIG, V, F);              \
+#define KDA_DECODE_SIZES(V, F)                 \
+  do {                                         \
+    if (size == 0) KDA_DECODE_LAUNCH(2, V, F); \
+    else KDA_DECODE_LAUNCH(4, V, F);           \
   } while (0)
   // fp16 and fp8 states run on the vectorised path only (the host requires it)
   if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
-  if (p.state_fmt == kStateFp16) KDA_DECODE_SIZES(true, kStateFp16, 8);
-  else if (p.state_fmt == kStateFp8) KDA_DECODE_SIZES(true, kStateFp8, 16);
-  else if (vec) KDA_DECODE_SIZES(true, kStateBf16, 8);
-  else KDA_DECODE_SIZES(false, kStateBf16, 8);
+  if (p.state_fmt == kStateFp16) {
+    KDA_DECODE_SIZES(true, kStateFp16);
+  } else if (fp8) {
+    if (size == 2) KDA_DECODE_LAUNCH(16, true, kStateFp8);
+    else KDA_DECODE_SIZES(true, kStateFp8);
+  } else if (vec) {
+    KDA_DECODE_SIZES(true, kStateBf16);
+  } else {
+    KDA_DECODE_SIZES(false, kStateBf16);
+  }
 #undef KDA_DECODE_SIZES
 #undef KDA_DECODE_LAUNCH
   return hipGetLastError();

@@ -54,19 +54,19 @@ COUNTED_TRAFFIC = {
         sources=("gated_delta_rule_step_amd/csrc/kda_decode.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
-        sha256=("5fc6dbbe227b21c1bbfa022fa4099bd0330f023e2646621c398ceb364d31e1b0",
-                "cda213427d916f818aebd6bcc05ca7e0e545ccd7080776d630b4730289efa3ce",
+        sha256=("e67926d244fc1e182e056403b430d539c96d6e425f5c17f0745a57a5a2674f8a",
+                "2fe55975814488bcd43f46e6ffd9805dc1139ce860b017fe31783558c0e3b22e",
                 "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
-        fetch_kib=96396.047, write_kib=188167.164, fetch_scale=2.0, write_scale=1.0),
+        fetch_kib=96502.734, write_kib=188161.195, fetch_scale=2.0, write_scale=1.0),
     # T = 8 verify, B = 512, bare checkpoint (the --mode profile sequence)
     "kda::verify_kernel<true, true, 0, 0>": dict(
         sources=("gated_delta_rule_step_amd/csrc/kda_verify.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
-        sha256=("304ada24daf4f0aea7a15054f2bc92a43e8764a3f4cd75d7d6ba240724007c88",
-                "cda213427d916f818aebd6bcc05ca7e0e545ccd7080776d630b4730289efa3ce",
+        sha256=("9ae9ae92ae3ac8f4a7d8464057097d9e35d4b6b80ce669d46d805356eaa84060",
+                "2fe55975814488bcd43f46e6ffd9805dc1139ce860b017fe31783558c0e3b22e",
                 "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
-        fetch_kib=123810.797, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),
+        fetch_kib=123907.617, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),
 }
 
 

@@ -17,6 +17,11 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// Buffer resources (raw, gfx9 family descriptor word 3) and the cache-policy
+// bits of a buffer store that mark it non-temporal.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kStoreNontemporal = 2;
+
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32. Widening is exact (bits move to the top half). Narrowing uses
 // the gfx950 hardware conversion v_cvt_pk_bf16_f32 (round to nearest even),

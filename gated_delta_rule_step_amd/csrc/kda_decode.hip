@@ -56,7 +56,14 @@ void decode_kernel(DecodeParams p) {
   // said so with readfirstlane, the address arithmetic runs on the scalar
   // unit and the slot index is a scalar load.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t tile = int64_t(blockIdx.x) * (blockDim.x >> 6) + wave;
+  // Workgroups go to the eight XCDs round-robin by block index. The grid is a
+  // multiple of 16 blocks and block p runs logical block
+  // 16*(p/16) + 2*(p%8) + (p/8)%2: logical blocks 2j and 2j+1 (the two
+  // workgroups of one head with 16-row tiles) run on one XCD and fetch the
+  // head's token inputs into one L2.
+  const unsigned pb = blockIdx.x;
+  const unsigned lb = (pb & ~15u) | ((pb & 7u) << 1) | ((pb >> 3) & 1u);
+  const int64_t tile = int64_t(lb) * (blockDim.x >> 6) + wave;
   const int vb = int(tile % VBLOCKS);
   const int64_t bh = tile / VBLOCKS;
   if (bh >= int64_t(p.B) * p.H) return;
@@ -201,8 +208,8 @@ hipError_t launch_decode(const DecodeParams& p, bool vec, hipStream_t stream) {
   const int size = heads <= 64 ? 0 : (fp8 && heads >= 4096 ? 2 : 1);
   const int loads = size == 0 ? 2 : (size == 1 ? 4 : 16);
   const int64_t tiles = heads * (D / (4 * loads));
-  const int64_t blocks = (tiles + 3) / 4;
-  if (blocks == 0) return hipSuccess;
+  const int64_t blocks = ((tiles + 3) / 4 + 15) / 16 * 16;  // padding blocks exit at once
+  if (tiles == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
   const int gk = p.gate_mode & kGateKindMask;

@@ -72,8 +72,6 @@ constexpr int RS = D + 4;      // padded row (fp32) of the [token][channel] LDS 
                                // 16 rows read by one MFMA fragment load hit different banks
 constexpr int XLD = D + 4;     // padded row (bf16) of W as bf16 hi / lo
 constexpr int kMaxOrderedDocs = 256;
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
-constexpr int kStoreNontemporal = 2;      // cache-policy bits of a buffer store: nt
 
 // chunk record, bytes
 constexpr int kRecW = 0;

@@ -176,7 +176,7 @@ __device__ __forceinline__ void load_tokens(const VerifyParams& p, int64_t item,
 // widened to bf16 (exactly) as B fragments of the bf16 product. The rings
 // stay bf16.
 template <bool VEC, bool FACT, int GK, int SF>
-__global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
+__global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm, int fold_nt) {
   constexpr bool GRAW = !(GK & kGatePrecomputed);
   constexpr int MF = SF == kStateFp16 ? kStateFp16 : kStateBf16;  // MFMA operand format
   static_assert(VEC || SF == kStateBf16, "fp16 and fp8 checkpoints use the vectorised layout");
@@ -394,6 +394,10 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   // for phase 6.) With no history S_cur is the checkpoint itself and nothing
   // is rewritten.
   if (fold && hist > 0) {
+    // the head's checkpoint as a buffer range (non-temporal stores)
+    const __amdgpu_buffer_rsrc_t fold_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<uint8_t*>(p.state_pool) + ce * kStateBytes<SF>, 0, HEAD_ELEMS * kStateBytes<SF>,
+        kBufferWord3);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int v = 32 * wave + 16 * blk + fv;
@@ -418,14 +422,27 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
           for (int e = 0; e < 8; ++e) x[e] = fmaf(uj, s.dh[j * D + k0 + e], x[e]);
         }
         const St8<SF> w = st8_pack<SF>(x);
-        // A plain (cached) store: one instruction covers 64 of the 128 bytes of
-        // each of 16 checkpoint rows (32 of 64 for fp8), and the st + 1 store
-        // fills the other half; in L2 the halves merge into whole lines before
-        // they reach memory (non-temporal stores measured 9 % slower at 100 %
-        // fold).
-        if constexpr (SF == kStateFp8) st8_store<SF>(p.state_pool, ce + int64_t(v) * D + k0, w);
-        else if constexpr (VEC) *reinterpret_cast<u32x4*>(ckpt + int64_t(v) * D + k0) = w;
-        else store8_raw<VEC>(ckpt + int64_t(v) * D + k0, w);
+        // One instruction covers 64 of the 128 bytes of each of 16 checkpoint
+        // rows (32 of 64 for fp8), and the st + 1 store fills the other half.
+        // Large grids use plain (cached) stores: the halves merge in L2 into
+        // whole lines before they reach memory (non-temporal stores measured
+        // 9 % slower at B = 512, 100 % fold). Small grids (fold_nt) use
+        // non-temporal stores: there the lines left dirty in L2 are written
+        // back at the end of the kernel, on its critical path (B = 32, 100 %
+        // fold: 18.1 us plain, 16.4 us non-temporal).
+        // (The non-temporal stores are buffer stores: a generic store with a
+        // non-temporal hint would be merged with the plain one across the
+        // branch, losing the hint.)
+        const int eo = v * D + k0;  // element offset inside the head
+        if constexpr (SF == kStateFp8) {
+          if (fold_nt) __builtin_amdgcn_raw_buffer_store_b64(w, fold_rsrc, eo, 0, kStoreNontemporal);
+          else st8_store<SF>(p.state_pool, ce + eo, w);
+        } else if constexpr (VEC) {
+          if (fold_nt) __builtin_amdgcn_raw_buffer_store_b128(w, fold_rsrc, 2 * eo, 0, kStoreNontemporal);
+          else *reinterpret_cast<u32x4*>(ckpt + eo) = w;
+        } else {
+          store8_raw<VEC>(ckpt + eo, w);
+        }
       }
     }
   }
@@ -667,21 +684,23 @@ hipError_t launch_verify(const VerifyParams& p, bool vec, hipStream_t stream) {
   const size_t lds = smem_bytes(hm);
   // exp(Gam_r) * exp(-Gam_j) stays finite when |Gam| <= T * |lower_bound| < 80.
   const bool fact = p.lower_bound > -80.0f / float(p.T) && p.lower_bound <= 0.0f;
+  // fold stores: non-temporal below 2048 (row, head) items (see the fold)
+  const int fold_nt = blocks < 2048 ? 1 : 0;
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
   const int gk = p.gate_mode & kGateKindMask;
 #define KDA_VERIFY_LAUNCH(V, F, S)                                                            \
   do {                                                                                        \
     switch (gk) {                                                                             \
       case 0:                                                                                 \
-        hipLaunchKernelGGL((verify_kernel<V, F, 0, S>), grid, block, lds, stream, p, hm);     \
+        hipLaunchKernelGGL((verify_kernel<V, F, 0, S>), grid, block, lds, stream, p, hm, fold_nt);     \
         break;                                                                                \
       case 1:                                                                                 \
-        hipLaunchKernelGGL((verify_kernel<V, F, 1, S>), grid, block, lds, stream, p, hm);     \
+        hipLaunchKernelGGL((verify_kernel<V, F, 1, S>), grid, block, lds, stream, p, hm, fold_nt);     \
         break;                                                                                \
       case 4:                                                                                 \
-        hipLaunchKernelGGL((verify_kernel<V, F, 4, S>), grid, block, lds, stream, p, hm);     \
+        hipLaunchKernelGGL((verify_kernel<V, F, 4, S>), grid, block, lds, stream, p, hm, fold_nt);     \
         break;                                                                                \
-      default: hipLaunchKernelGGL((verify_kernel<V, F, 5, S>), grid, block, lds, stream, p, hm); \
+      default: hipLaunchKernelGGL((verify_kernel<V, F, 5, S>), grid, block, lds, stream, p, hm, fold_nt); \
     }                                                                                         \
   } while (0)
   // fp16 and fp8 checkpoints run on the vectorised path only (the host requires it)

@@ -209,22 +209,28 @@ def test_precomputed_gate_conventions(orc, T, fm, p, gate_mode):
     verify_roundtrip(orc, case)
 
 
-@pytest.mark.parametrize("T,fm,p,hist_max,w", [(8, 9, 0.5, None, 16), (8, 9, 0.0, 0, 16),
-                                              (8, 25, 0.0, 24, 32)])
-def test_fp16_checkpoints(orc, T, fm, p, hist_max, w):
-    """fp16 checkpoints (state_dtype 1) at B = 512: the checkpoint product on
-    fp16 MFMA operands, folds stored as binary16, rings still bf16."""
-    case = build_case(orc, 512, T, w_ring=w, flush_min=fm, fold_p=p, hist_max=hist_max,
+@pytest.mark.parametrize("T,fm,p,hist_max,w,B", [(8, 9, 0.5, None, 16, 512),
+                                                (8, 9, 0.0, 0, 16, 512),
+                                                (8, 25, 0.0, 24, 32, 512),
+                                                (8, 9, 1.0, None, 16, 32)])
+def test_fp16_checkpoints(orc, T, fm, p, hist_max, w, B):
+    """fp16 checkpoints (state_dtype 1) at B = 512 (and 32, where folds use
+    non-temporal stores): the checkpoint product on fp16 MFMA operands, folds
+    stored as binary16, rings still bf16."""
+    case = build_case(orc, B, T, w_ring=w, flush_min=fm, fold_p=p, hist_max=hist_max,
                       state_dtype=1)
     verify_roundtrip(orc, case)
 
 
-@pytest.mark.parametrize("T,fm,p,hist_max,w", [(8, 9, 0.5, None, 16), (8, 9, 0.0, 0, 16),
-                                              (8, 25, 0.0, 24, 32)])
-def test_fp8_checkpoints(orc, T, fm, p, hist_max, w):
-    """fp8 e4m3 checkpoints (state_dtype 2) at B = 512: the checkpoint widened
-    to bf16 B operands (exactly), folds stored as fp8, rings still bf16."""
-    case = build_case(orc, 512, T, w_ring=w, flush_min=fm, fold_p=p, hist_max=hist_max,
+@pytest.mark.parametrize("T,fm,p,hist_max,w,B", [(8, 9, 0.5, None, 16, 512),
+                                                (8, 9, 0.0, 0, 16, 512),
+                                                (8, 25, 0.0, 24, 32, 512),
+                                                (8, 9, 1.0, None, 16, 32)])
+def test_fp8_checkpoints(orc, T, fm, p, hist_max, w, B):
+    """fp8 e4m3 checkpoints (state_dtype 2) at B = 512 (and 32, where folds use
+    non-temporal stores): the checkpoint widened to bf16 B operands (exactly),
+    folds stored as fp8, rings still bf16."""
+    case = build_case(orc, B, T, w_ring=w, flush_min=fm, fold_p=p, hist_max=hist_max,
                       state_dtype=2)
     verify_roundtrip(orc, case)
 

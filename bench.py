@@ -54,10 +54,10 @@ COUNTED_TRAFFIC = {
         sources=("gated_delta_rule_step_amd/csrc/kda_decode.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
-        sha256=("e67926d244fc1e182e056403b430d539c96d6e425f5c17f0745a57a5a2674f8a",
+        sha256=("4029b6b78d8c29b3f122b4dc5489c7da83b124ec12e53c4359c8eadfa5ba3820",
                 "2fe55975814488bcd43f46e6ffd9805dc1139ce860b017fe31783558c0e3b22e",
                 "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
-        fetch_kib=96502.734, write_kib=188161.195, fetch_scale=2.0, write_scale=1.0),
+        fetch_kib=96508.367, write_kib=188160.684, fetch_scale=2.0, write_scale=1.0),
     # T = 8 verify, B = 512, bare checkpoint (the --mode profile sequence)
     "kda::verify_kernel<true, true, 0, 0>": dict(
         sources=("gated_delta_rule_step_amd/csrc/kda_verify.hip",

@@ -46,7 +46,7 @@ constexpr int kDecodeWaves = (SF == kStateFp8 && LOADS == 16) ? 4 : 5;
 
 template <int LOADS, bool VEC, int GK, int SF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDecodeWaves<LOADS, SF>)))
-void decode_kernel(DecodeParams p) {
+void decode_kernel(DecodeParams p, int group) {
   constexpr bool GRAW = !(GK & kGatePrecomputed);
   constexpr bool GHEAD = (GK & kGatePerHead) != 0;
   constexpr int ROWS = 4 * LOADS;
@@ -57,12 +57,15 @@ void decode_kernel(DecodeParams p) {
   // unit and the slot index is a scalar load.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Workgroups go to the eight XCDs round-robin by block index. The grid is a
-  // multiple of 16 blocks and block p runs logical block
-  // 16*(p/16) + 2*(p%8) + (p/8)%2: logical blocks 2j and 2j+1 (the two
-  // workgroups of one head with 16-row tiles) run on one XCD and fetch the
-  // head's token inputs into one L2.
+  // multiple of 8 * group blocks, and block p runs logical block
+  // (8*(k/group) + p%8)*group + k%group with k = p/8, so that every run of
+  // `group` consecutive logical blocks shares one XCD: at least the two
+  // workgroups of one head (16-row tiles), which then fetch the head's token
+  // inputs into one L2, and with large batches all workgroups of one row, so
+  // that an XCD works on an eighth of the slots at a time.
   const unsigned pb = blockIdx.x;
-  const unsigned lb = (pb & ~15u) | ((pb & 7u) << 1) | ((pb >> 3) & 1u);
+  const unsigned xk = pb >> 3, xg = xk / unsigned(group), xr = xk - xg * unsigned(group);
+  const unsigned lb = (xg * 8u + (pb & 7u)) * unsigned(group) + xr;
   const int64_t tile = int64_t(lb) * (blockDim.x >> 6) + wave;
   const int vb = int(tile % VBLOCKS);
   const int64_t bh = tile / VBLOCKS;
@@ -208,7 +211,14 @@ hipError_t launch_decode(const DecodeParams& p, bool vec, hipStream_t stream) {
   const int size = heads <= 64 ? 0 : (fp8 && heads >= 4096 ? 2 : 1);
   const int loads = size == 0 ? 2 : (size == 1 ? 4 : 16);
   const int64_t tiles = heads * (D / (4 * loads));
-  const int64_t blocks = ((tiles + 3) / 4 + 15) / 16 * 16;  // padding blocks exit at once
+  // XCD groups (see the kernel): one row's workgroups from 64 rows on with
+  // 16-bit states (B = 512: 70.7 against 72.1 us for head pairs; neutral at
+  // B = 128, 3 % slower for fp8 at B = 128), else head pairs. Padding blocks
+  // exit at once.
+  const int64_t row_blocks = int64_t(p.H) * (D / (4 * loads)) / 4;
+  const int group =
+      (!fp8 && p.B >= 64 && row_blocks > 2 && row_blocks <= 4096) ? int(row_blocks) : 2;
+  const int64_t blocks = ((tiles + 3) / 4 + 8 * group - 1) / (8 * group) * (8 * group);
   if (tiles == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
@@ -216,10 +226,10 @@ hipError_t launch_decode(const DecodeParams& p, bool vec, hipStream_t stream) {
 #define KDA_DECODE_LAUNCH(L, V, F)                                                              \
   do {                                                                                          \
     switch (gk) {                                                                               \
-      case 0: hipLaunchKernelGGL((decode_kernel<L, V, 0, F>), grid, block, 0, stream, p); break; \
-      case 1: hipLaunchKernelGGL((decode_kernel<L, V, 1, F>), grid, block, 0, stream, p); break; \
-      case 4: hipLaunchKernelGGL((decode_kernel<L, V, 4, F>), grid, block, 0, stream, p); break; \
-      default: hipLaunchKernelGGL((decode_kernel<L, V, 5, F>), grid, block, 0, stream, p);      \
+      case 0: hipLaunchKernelGGL((decode_kernel<L, V, 0, F>), grid, block, 0, stream, p, group); break; \
+      case 1: hipLaunchKernelGGL((decode_kernel<L, V, 1, F>), grid, block, 0, stream, p, group); break; \
+      case 4: hipLaunchKernelGGL((decode_kernel<L, V, 4, F>), grid, block, 0, stream, p, group); break; \
+      default: hipLaunchKernelGGL((decode_kernel<L, V, 5, F>), grid, block, 0, stream, p, group);      \
     }                                                                                           \
   } while (0)
 #define KDA_DECODE_SIZES(V, F)                 \

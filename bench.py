@@ -63,10 +63,10 @@ COUNTED_TRAFFIC = {
         sources=("gated_delta_rule_step_amd/csrc/kda_verify.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
-        sha256=("9ae9ae92ae3ac8f4a7d8464057097d9e35d4b6b80ce669d46d805356eaa84060",
+        sha256=("7fe53cc592c6786ba0e5ed88b14a596b0786507d8bff7b01050d1b3ba6aec005",
                 "2fe55975814488bcd43f46e6ffd9805dc1139ce860b017fe31783558c0e3b22e",
                 "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
-        fetch_kib=123907.617, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),
+        fetch_kib=123884.531, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),
 }
 
 

@@ -398,50 +398,79 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm, int
     const __amdgpu_buffer_rsrc_t fold_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<uint8_t*>(p.state_pool) + ce * kStateBytes<SF>, 0, HEAD_ELEMS * kStateBytes<SF>,
         kBufferWord3);
+    // S_cur for fragment (blk, st) of this lane, packed in the state format
+    auto fold_piece = [&](int blk, int st, int v) {
+      const int k0 = 32 * st + fk;
+      float x[8];
+      if constexpr (SF == kStateFp8) {
+        st8_unpack<SF>(sf[blk][st], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= s.egl[k0 + e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = st_lo<SF>(sf[blk][st][e]) * s.egl[k0 + 2 * e];
+          x[2 * e + 1] = st_hi<SF>(sf[blk][st][e]) * s.egl[k0 + 2 * e + 1];
+        }
+      }
+      for (int j = 0; j < hist; ++j) {
+        const float uj = bf1(s.uh[j * D + v]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = fmaf(uj, s.dh[j * D + k0 + e], x[e]);
+      }
+      return st8_pack<SF>(x);
+    };
+    // Stores: 16-bit formats write whole 128-byte lines, non-temporally
+    // (B = 512, 100 % fold: 127.6 us with half lines through L2, 123.6 us
+    // with whole lines through L2, 117.7 us whole lines non-temporal). fp8
+    // writes 32 of the 128 bytes of each row per store: through L2 on large
+    // grids, where the pieces merge, non-temporally on small grids (fold_nt),
+    // where lines left dirty in L2 would be written back at the end of the
+    // kernel, on its critical path. The non-temporal stores are buffer
+    // stores: a generic store with a non-temporal hint is merged by the
+    // compiler with a plain one across a branch, losing the hint.
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int v = 32 * wave + 16 * blk + fv;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int k0 = 32 * st + fk;
-        float x[8];
-        if constexpr (SF == kStateFp8) {
-          st8_unpack<SF>(sf[blk][st], x);
+      for (int pp = 0; pp < 2; ++pp) {
+        const St8<SF> w0 = fold_piece(blk, 2 * pp, v);
+        const St8<SF> w1 = fold_piece(blk, 2 * pp + 1, v);
+        if constexpr (SF != kStateFp8 && VEC) {
+          // Whole 128-byte lines: a fragment holds 64 bytes of each of 16
+          // rows, so lanes fv and fv ^ 8 swap their st = 2pp + 1 pieces (DPP
+          // row_ror:8) and each store then writes channels 64pp .. 64pp + 63
+          // of 8 rows: rows 0-7 of the block (lanes fv < 8 their own st = 2pp
+          // piece, lanes fv >= 8 the received st = 2pp + 1 piece of row
+          // v - 8), then rows 8-15 the other way round.
+          const bool low = fv < 8;
+          u32x4 r;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] *= s.egl[k0 + e];
+          for (int i = 0; i < 4; ++i)
+            r[i] = static_cast<uint32_t>(
+                __builtin_amdgcn_update_dpp(0, static_cast<int>(w1[i]), 0x128, 0xF, 0xF, false));
+          const int eA = (low ? v : v - 8) * D + 64 * pp + (low ? 0 : 32) + fk;
+          const int eB = (low ? v + 8 : v) * D + 64 * pp + (low ? 32 : 0) + fk;
+          const u32x4 dA = low ? w0 : r;
+          const u32x4 dB = low ? r : w0;
+          __builtin_amdgcn_raw_buffer_store_b128(dA, fold_rsrc, 2 * eA, 0, kStoreNontemporal);
+          __builtin_amdgcn_raw_buffer_store_b128(dB, fold_rsrc, 2 * eB, 0, kStoreNontemporal);
         } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[2 * e] = st_lo<SF>(sf[blk][st][e]) * s.egl[k0 + 2 * e];
-            x[2 * e + 1] = st_hi<SF>(sf[blk][st][e]) * s.egl[k0 + 2 * e + 1];
+          // fp8 (32 bytes of each 128-byte row per fragment) and the scalar
+          // path: one store per fragment.
+          const int e0 = v * D + 64 * pp + fk, e1 = e0 + 32;  // element offsets in the head
+          if constexpr (SF == kStateFp8) {
+            if (fold_nt) {
+              __builtin_amdgcn_raw_buffer_store_b64(w0, fold_rsrc, e0, 0, kStoreNontemporal);
+              __builtin_amdgcn_raw_buffer_store_b64(w1, fold_rsrc, e1, 0, kStoreNontemporal);
+            } else {
+              st8_store<SF>(p.state_pool, ce + e0, w0);
+              st8_store<SF>(p.state_pool, ce + e1, w1);
+            }
+          } else {
+            store8_raw<VEC>(ckpt + e0, w0);
+            store8_raw<VEC>(ckpt + e1, w1);
           }
-        }
-        for (int j = 0; j < hist; ++j) {
-          const float uj = bf1(s.uh[j * D + v]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = fmaf(uj, s.dh[j * D + k0 + e], x[e]);
-        }
-        const St8<SF> w = st8_pack<SF>(x);
-        // One instruction covers 64 of the 128 bytes of each of 16 checkpoint
-        // rows (32 of 64 for fp8), and the st + 1 store fills the other half.
-        // Large grids use plain (cached) stores: the halves merge in L2 into
-        // whole lines before they reach memory (non-temporal stores measured
-        // 9 % slower at B = 512, 100 % fold). Small grids (fold_nt) use
-        // non-temporal stores: there the lines left dirty in L2 are written
-        // back at the end of the kernel, on its critical path (B = 32, 100 %
-        // fold: 18.1 us plain, 16.4 us non-temporal).
-        // (The non-temporal stores are buffer stores: a generic store with a
-        // non-temporal hint would be merged with the plain one across the
-        // branch, losing the hint.)
-        const int eo = v * D + k0;  // element offset inside the head
-        if constexpr (SF == kStateFp8) {
-          if (fold_nt) __builtin_amdgcn_raw_buffer_store_b64(w, fold_rsrc, eo, 0, kStoreNontemporal);
-          else st8_store<SF>(p.state_pool, ce + eo, w);
-        } else if constexpr (VEC) {
-          if (fold_nt) __builtin_amdgcn_raw_buffer_store_b128(w, fold_rsrc, 2 * eo, 0, kStoreNontemporal);
-          else *reinterpret_cast<u32x4*>(ckpt + eo) = w;
-        } else {
-          store8_raw<VEC>(ckpt + eo, w);
         }
       }
     }
@@ -684,7 +713,7 @@ hipError_t launch_verify(const VerifyParams& p, bool vec, hipStream_t stream) {
   const size_t lds = smem_bytes(hm);
   // exp(Gam_r) * exp(-Gam_j) stays finite when |Gam| <= T * |lower_bound| < 80.
   const bool fact = p.lower_bound > -80.0f / float(p.T) && p.lower_bound <= 0.0f;
-  // fold stores: non-temporal below 2048 (row, head) items (see the fold)
+  // fp8 fold stores: non-temporal below 2048 (row, head) items (see the fold)
   const int fold_nt = blocks < 2048 ? 1 : 0;
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
   const int gk = p.gate_mode & kGateKindMask;

@@ -68,16 +68,21 @@ struct Smem {
   float* beta;    // [TMAX]
   float* egl;     // [D] exp(G_L)
   float* cm;      // [2*TMAX][hm]
-  float* dh;      // [hm][D] exp(G_L - G_j) * k_j
-  uint16_t* uh;   // [hm][D] u_j (bf16 bits)
-  uint16_t* kr;   // [hm][D] k_j (bf16 bits) as read from the ring
+  // History rows j < hm, 1 KiB each (kHistF floats): G_j, then
+  // exp(G_L - G_j) * k_j (fp32, in place) | k_j (bf16 bits, as read from the
+  // ring) | u_j (bf16 bits). One 16-byte direct-to-LDS load per lane moves a
+  // whole row.
+  float* dh;      // row j at dh + j * kHistF
+  uint16_t* kr;   // row j at kr + j * kHistU
+  uint16_t* uh;   // row j at uh + j * kHistU
 };
+constexpr int kHistF = 256;  // floats per history row (1 KiB)
+constexpr int kHistU = 512;  // 16-bit words per history row
 
 __host__ __device__ inline size_t smem_bytes(int hm) {
   const size_t f = size_t(4) * TMAX * XS + 2 * TMAX * TMAX + TMAX + D + size_t(2 * TMAX) * hm +
-                   size_t(hm) * D;
-  const size_t bytes = f * 4 + size_t(2) * hm * D * 2;
-  return (bytes + 15) & ~size_t(15);
+                   size_t(hm) * kHistF;
+  return f * 4;
 }
 
 __device__ inline Smem carve(float* base, int hm) {
@@ -93,9 +98,11 @@ __device__ inline Smem carve(float* base, int hm) {
   s.beta = p; p += TMAX;
   s.egl = p; p += D;
   s.cm = p; p += 2 * TMAX * hm;
-  s.dh = p; p += size_t(hm) * D;
-  s.uh = reinterpret_cast<uint16_t*>(p);
-  s.kr = s.uh + size_t(hm) * D;
+  // 16-byte aligned: 4 * TMAX * XS + 2 * TMAX * TMAX + TMAX + D and 2 * TMAX
+  // floats are multiples of 4
+  s.dh = p;
+  s.kr = reinterpret_cast<uint16_t*>(p + D);
+  s.uh = reinterpret_cast<uint16_t*>(p + D) + D;
   return s;
 }
 
@@ -228,25 +235,20 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm, int
   // (blk, st) holds v = 32w + 16*blk + lane%16, key channels
   // 32*st + 8*(lane/16) .. +7).
   // History rows j < hist go straight from the ring into LDS (no register
-  // destinations) in waves 2 and 3. Wave 2 + half owns key / value channels
-  // 64 half .. +63: G_j (64 lanes x 4 B) into dh, k_j and u_j (32 lanes x
-  // 4 B each) into kr and uh. Like every other load of the item they are
-  // issued before the checkpoint loads and covered by the explicit vmcnt(8)
-  // at the start of the prologue math.
+  // destinations), one row per instruction: lanes 0-31 move G_j (512 B),
+  // lanes 32-47 k_j and lanes 48-63 u_j (256 B each), 16 bytes per lane, into
+  // the row's 1 KiB LDS block; wave w takes rows j = w mod 4. Like every
+  // other load of the item they are issued before the checkpoint loads and
+  // covered by the explicit vmcnt(8) at the start of the prologue math (and
+  // the barrier after it, for the rows of the other waves).
   if constexpr (VEC) {
-    if (hist > 0 && wave >= 2) {
-      const int half = wave - 2;
-      for (int j = 0; j < hist; ++j) {
-        const int64_t row = ring_row(j);
-        __builtin_amdgcn_global_load_lds(gc + row * D + 64 * half + lane, s.dh + j * D + 64 * half,
-                                         4, 0, 0);
-        if (lane < 32) {
-          __builtin_amdgcn_global_load_lds(kc + row * D + 64 * half + 2 * lane,
-                                           s.kr + j * D + 64 * half, 4, 0, 0);
-          __builtin_amdgcn_global_load_lds(uc + row * D + 64 * half + 2 * lane,
-                                           s.uh + j * D + 64 * half, 4, 0, 0);
-        }
-      }
+    const float* src_g = gc + 4 * lane;
+    const uint16_t* src_k = (lane < 48 ? kc : uc) + 8 * (lane & 15);
+    for (int j = wave; j < hist; j += 4) {
+      const int64_t row = ring_row(j);
+      const void* src = lane < 32 ? static_cast<const void*>(src_g + row * D)
+                                  : static_cast<const void*>(src_k + row * D);
+      __builtin_amdgcn_global_load_lds(src, s.dh + j * kHistF, 16, 0, 0);
     }
   }
   // G_{hist-1} of key channel tid % 128 (phase 3).
@@ -347,14 +349,14 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm, int
     for (int t = 0; t < TMAX; ++t) gcol[t] = t < T ? s.kb[t * XS + c] : 0.f;
     if (half == 1 && hist > 0) {
       if constexpr (VEC) {
-        // this wave's history rows are in LDS (waited for in phase 2)
+        // the history rows are in LDS (waited for in phase 2, barrier above)
         for (int j = 0; j < hist; ++j)
-          s.dh[j * D + c] = fexp(gl - s.dh[j * D + c]) * bf1(s.kr[j * D + c]);
+          s.dh[j * kHistF + c] = fexp(gl - s.dh[j * kHistF + c]) * bf1(s.kr[j * kHistU + c]);
       } else {
         for (int j = 0; j < hist; ++j) {
           const int64_t row = ring_row(j);
-          s.dh[j * D + c] = fexp(gl - gc[row * D + c]) * bf1(kc[row * D + c]);
-          s.uh[j * D + c] = uc[row * D + c];
+          s.dh[j * kHistF + c] = fexp(gl - gc[row * D + c]) * bf1(kc[row * D + c]);
+          s.uh[j * kHistU + c] = uc[row * D + c];
         }
       }
     }
@@ -414,9 +416,9 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm, int
         }
       }
       for (int j = 0; j < hist; ++j) {
-        const float uj = bf1(s.uh[j * D + v]);
+        const float uj = bf1(s.uh[j * kHistU + v]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = fmaf(uj, s.dh[j * D + k0 + e], x[e]);
+        for (int e = 0; e < 8; ++e) x[e] = fmaf(uj, s.dh[j * kHistF + k0 + e], x[e]);
       }
       return st8_pack<SF>(x);
     };
@@ -569,7 +571,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm, int
       lds_read8(xrow, kb, x);
       for (int j = 0; j < hist; ++j) {
         float d[8];
-        lds_read8(s.dh + j * D, kb, d);
+        lds_read8(s.dh + j * kHistF, kb, d);
         float a = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) a = fmaf(x[c], d[c], a);
@@ -663,8 +665,8 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm, int
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = fk + 2 * i;
-          const uint32_t u0 = j < hist ? s.uh[j * D + v] : 0u;
-          const uint32_t u1 = j + 1 < hist ? s.uh[(j + 1) * D + v] : 0u;
+          const uint32_t u0 = j < hist ? s.uh[j * kHistU + v] : 0u;
+          const uint32_t u1 = j + 1 < hist ? s.uh[(j + 1) * kHistU + v] : 0u;
           ub[i] = u0 | (u1 << 16);
         }
         const bf16x8 bu = __builtin_bit_cast(bf16x8, ub);

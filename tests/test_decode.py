@@ -150,6 +150,16 @@ def test_batch_sweep_packed_rows(orc, B):
     check_case(orc, case, pool, out)
 
 
+@pytest.mark.parametrize("B", [64, 255, 513])
+def test_two_heads_large_pool(orc, B):
+    """Two heads (four workgroups per row, all on one XCD from 64 rows on),
+    a 3000-slot pool, 5 % inactive rows and INT32_MIN / INT32_MAX indices."""
+    case = synth.decode_case(B=B, N=3000, H=2, seed=synth.seed_for(1, B, 130))
+    case["idx"][[3, 10]] = [INT32_MIN, INT32_MAX]
+    pool, out = run_decode(case)
+    check_case(orc, case, pool, out)
+
+
 def test_extreme_indices_and_all_inactive(orc):
     case = synth.decode_case(B=6, N=8, H=12, seed=11, idx=[INT32_MIN, 3, INT32_MAX, 8, -1, 0])
     pool, out = run_decode(case)

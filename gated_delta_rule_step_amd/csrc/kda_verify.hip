@@ -182,7 +182,7 @@ __device__ __forceinline__ void load_tokens(const VerifyParams& p, int64_t item,
 // v_mfma_f32_16x16x32_f16 with fp16 hi / lo A fragments; fp8 checkpoints are
 // widened to bf16 (exactly) as B fragments of the bf16 product. The rings
 // stay bf16.
-template <bool VEC, bool FACT, int GK, int SF>
+template <bool VEC, bool FACT, int GK, int SF, bool DEEP>
 __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm, int fold_nt) {
   constexpr bool GRAW = !(GK & kGatePrecomputed);
   constexpr int MF = SF == kStateFp16 ? kStateFp16 : kStateBf16;  // MFMA operand format
@@ -401,6 +401,65 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm, int
         static_cast<uint8_t*>(p.state_pool) + ce * kStateBytes<SF>, 0, HEAD_ELEMS * kStateBytes<SF>,
         kBufferWord3);
     // S_cur for fragment (blk, st) of this lane, packed in the state format
+    // DEEP (rings holding 16 or more history rows): with hist >= 8 the sum
+    // over the history rows, sum_j u_j D_j, runs on MFMA as one K = 32 step
+    // (rows j >= hist zero on both sides): A = D^T with its 16 rows permuted
+    // so that row m is key channel 32 st + 8 (m / 4) + 4 half + m % 4, split
+    // into three bf16 terms (24 significant bits), B = the ring's u rows
+    // (bf16, exact). The result lands in each lane's own checkpoint row and
+    // key channels 32 st + fk + 4 half + i, the layout of the fragments.
+    f32x4 hs[2][4][2];
+    const bool mfma_hist = DEEP && hist >= 8;
+    if constexpr (DEEP) {
+      if (mfma_hist) {
+        bf16x8 ub[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          const int v = 32 * wave + 16 * blk + fv;
+          u32x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = fk + 2 * i;
+            const uint32_t u0 = j < hist ? s.uh[j * kHistU + v] : 0u;
+            const uint32_t u1 = j + 1 < hist ? s.uh[(j + 1) * kHistU + v] : 0u;
+            w[i] = u0 | (u1 << 16);
+          }
+          ub[blk] = __builtin_bit_cast(bf16x8, w);
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int kk = 32 * st + 8 * (fv >> 2) + 4 * half + (fv & 3);
+            float a[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int j = fk + e;
+              a[e] = j < hist ? s.dh[j * kHistF + kk] : 0.f;
+            }
+            u32x4 t1, t2, t3;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              t1[i] = pack_bf16x2(a[2 * i], a[2 * i + 1]);
+              const float r0 = a[2 * i] - bf_lo(t1[i]), r1 = a[2 * i + 1] - bf_hi(t1[i]);
+              t2[i] = pack_bf16x2(r0, r1);
+              t3[i] = pack_bf16x2(r0 - bf_lo(t2[i]), r1 - bf_hi(t2[i]));
+            }
+            const bf16x8 a1 = __builtin_bit_cast(bf16x8, t1);
+            const bf16x8 a2 = __builtin_bit_cast(bf16x8, t2);
+            const bf16x8 a3 = __builtin_bit_cast(bf16x8, t3);
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+              f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ub[blk], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, ub[blk], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, ub[blk], acc, 0, 0, 0);
+              hs[blk][st][half] = acc;
+            }
+          }
+        }
+      }
+    }
     auto fold_piece = [&](int blk, int st, int v) {
       const int k0 = 32 * st + fk;
       float x[8];
@@ -415,10 +474,15 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm, int
           x[2 * e + 1] = st_hi<SF>(sf[blk][st][e]) * s.egl[k0 + 2 * e + 1];
         }
       }
-      for (int j = 0; j < hist; ++j) {
-        const float uj = bf1(s.uh[j * kHistU + v]);
+      if (mfma_hist) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = fmaf(uj, s.dh[j * kHistF + k0 + e], x[e]);
+        for (int e = 0; e < 8; ++e) x[e] += hs[blk][st][e >> 2][e & 3];
+      } else {
+        for (int j = 0; j < hist; ++j) {
+          const float uj = bf1(s.uh[j * kHistU + v]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = fmaf(uj, s.dh[j * kHistF + k0 + e], x[e]);
+        }
       }
       return st8_pack<SF>(x);
     };
@@ -719,35 +783,44 @@ hipError_t launch_verify(const VerifyParams& p, bool vec, hipStream_t stream) {
   const int fold_nt = blocks < 2048 ? 1 : 0;
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
   const int gk = p.gate_mode & kGateKindMask;
-#define KDA_VERIFY_LAUNCH(V, F, S)                                                            \
-  do {                                                                                        \
-    switch (gk) {                                                                             \
-      case 0:                                                                                 \
-        hipLaunchKernelGGL((verify_kernel<V, F, 0, S>), grid, block, lds, stream, p, hm, fold_nt);     \
-        break;                                                                                \
-      case 1:                                                                                 \
-        hipLaunchKernelGGL((verify_kernel<V, F, 1, S>), grid, block, lds, stream, p, hm, fold_nt);     \
-        break;                                                                                \
-      case 4:                                                                                 \
-        hipLaunchKernelGGL((verify_kernel<V, F, 4, S>), grid, block, lds, stream, p, hm, fold_nt);     \
-        break;                                                                                \
-      default: hipLaunchKernelGGL((verify_kernel<V, F, 5, S>), grid, block, lds, stream, p, hm, fold_nt); \
-    }                                                                                         \
+#define KDA_VERIFY_LAUNCH(V, F, S, DP)                                                             \
+  do {                                                                                             \
+    switch (gk) {                                                                                  \
+      case 0:                                                                                      \
+        hipLaunchKernelGGL((verify_kernel<V, F, 0, S, DP>), grid, block, lds, stream, p, hm, fold_nt); \
+        break;                                                                                     \
+      case 1:                                                                                      \
+        hipLaunchKernelGGL((verify_kernel<V, F, 1, S, DP>), grid, block, lds, stream, p, hm, fold_nt); \
+        break;                                                                                     \
+      case 4:                                                                                      \
+        hipLaunchKernelGGL((verify_kernel<V, F, 4, S, DP>), grid, block, lds, stream, p, hm, fold_nt); \
+        break;                                                                                     \
+      default:                                                                                     \
+        hipLaunchKernelGGL((verify_kernel<V, F, 5, S, DP>), grid, block, lds, stream, p, hm, fold_nt); \
+    }                                                                                              \
   } while (0)
+  // Deep rings (16 or more history rows, the 32-row window): the fold's
+  // history sum on MFMA (see the kernel). These workgroups already hold
+  // three per CU for their LDS, so the extra registers cost no occupancy;
+  // built for the vectorised path with factored exponentials only.
+  const bool deep = hm >= 16 && vec && fact;
   // fp16 and fp8 checkpoints run on the vectorised path only (the host requires it)
   if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
   if (p.state_fmt == kStateFp16) {
-    if (fact) KDA_VERIFY_LAUNCH(true, true, kStateFp16);
-    else KDA_VERIFY_LAUNCH(true, false, kStateFp16);
+    if (deep) KDA_VERIFY_LAUNCH(true, true, kStateFp16, true);
+    else if (fact) KDA_VERIFY_LAUNCH(true, true, kStateFp16, false);
+    else KDA_VERIFY_LAUNCH(true, false, kStateFp16, false);
   } else if (p.state_fmt == kStateFp8) {
-    if (fact) KDA_VERIFY_LAUNCH(true, true, kStateFp8);
-    else KDA_VERIFY_LAUNCH(true, false, kStateFp8);
+    if (deep) KDA_VERIFY_LAUNCH(true, true, kStateFp8, true);
+    else if (fact) KDA_VERIFY_LAUNCH(true, true, kStateFp8, false);
+    else KDA_VERIFY_LAUNCH(true, false, kStateFp8, false);
   } else if (vec) {
-    if (fact) KDA_VERIFY_LAUNCH(true, true, kStateBf16);
-    else KDA_VERIFY_LAUNCH(true, false, kStateBf16);
+    if (deep) KDA_VERIFY_LAUNCH(true, true, kStateBf16, true);
+    else if (fact) KDA_VERIFY_LAUNCH(true, true, kStateBf16, false);
+    else KDA_VERIFY_LAUNCH(true, false, kStateBf16, false);
   } else {
-    if (fact) KDA_VERIFY_LAUNCH(false, true, kStateBf16);
-    else KDA_VERIFY_LAUNCH(false, false, kStateBf16);
+    if (fact) KDA_VERIFY_LAUNCH(false, true, kStateBf16, false);
+    else KDA_VERIFY_LAUNCH(false, false, kStateBf16, false);
   }
 #undef KDA_VERIFY_LAUNCH
   return hipGetLastError();

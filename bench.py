@@ -59,14 +59,14 @@ COUNTED_TRAFFIC = {
                 "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
         fetch_kib=96508.367, write_kib=188160.684, fetch_scale=2.0, write_scale=1.0),
     # T = 8 verify, B = 512, bare checkpoint (the --mode profile sequence)
-    "kda::verify_kernel<true, true, 0, 0>": dict(
+    "kda::verify_kernel<true, true, 0, 0, false>": dict(
         sources=("gated_delta_rule_step_amd/csrc/kda_verify.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
-        sha256=("81e1c2e8504d35acb16a1df67aca811e2c9d9d5bada137b728bdc1bf803bd0c5",
+        sha256=("8546014c33fc98b821bee98caf9ca82558913e7190024a71e8065f65d6018c2a",
                 "2fe55975814488bcd43f46e6ffd9805dc1139ce860b017fe31783558c0e3b22e",
                 "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
-        fetch_kib=123877.078, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),
+        fetch_kib=123890.523, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),
 }
 
 
@@ -539,7 +539,7 @@ def main():
                 fl = wm.verify_flops(cfg["T"], vs.hist)
                 extra = {}
                 if Bv == 512 and cfg["label"] == "T=8 bare (0% fold)":
-                    extra["traffic_bytes"] = counted_traffic("kda::verify_kernel<true, true, 0, 0>")
+                    extra["traffic_bytes"] = counted_traffic("kda::verify_kernel<true, true, 0, 0, false>")
                 points.append(dict(kind="verify", B=Bv, label=cfg["label"],
                                    fold_frac=round(float(np.mean(vs.fold)), 3),
                                    mean_hist=round(float(np.mean(vs.hist)), 2),

@@ -252,6 +252,17 @@ def test_deep_window_w32(orc, B):
     verify_roundtrip(orc, case)
 
 
+@pytest.mark.parametrize("T,fm,state_dtype", [(1, 32, 0), (2, 31, 0), (1, 32, 2)])
+def test_deep_window_full_capacity(orc, T, fm, state_dtype):
+    """w_ring = 32 at full capacity: every row folds with hist = 31 (T = 1) or
+    29-30 (T = 2), so the deep-ring fold's history product uses its whole
+    K = 32 step; bf16 and fp8 checkpoints."""
+    case = build_case(orc, 32, T, w_ring=32, flush_min=fm, fold_p=1.0,
+                      state_dtype=state_dtype)
+    assert case["hist_len"].min() >= fm - T
+    verify_roundtrip(orc, case)
+
+
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 7])
 def test_other_draft_lengths(orc, T):
     case = build_case(orc, 24, T, w_ring=16, flush_min=16 - T + 1, fold_p=0.5, N=64)

@@ -183,7 +183,7 @@ __device__ __forceinline__ void load_tokens(const VerifyParams& p, int64_t item,
 // widened to bf16 (exactly) as B fragments of the bf16 product. The rings
 // stay bf16.
 template <bool VEC, bool FACT, int GK, int SF, bool DEEP>
-__global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm, int fold_nt) {
+__global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   constexpr bool GRAW = !(GK & kGatePrecomputed);
   constexpr int MF = SF == kStateFp16 ? kStateFp16 : kStateBf16;  // MFMA operand format
   static_assert(VEC || SF == kStateBf16, "fp16 and fp8 checkpoints use the vectorised layout");
@@ -486,56 +486,79 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm, int
       }
       return st8_pack<SF>(x);
     };
-    // Stores: 16-bit formats write whole 128-byte lines, non-temporally
-    // (B = 512, 100 % fold: 127.6 us with half lines through L2, 123.6 us
-    // with whole lines through L2, 117.7 us whole lines non-temporal). fp8
-    // writes 32 of the 128 bytes of each row per store: through L2 on large
-    // grids, where the pieces merge, non-temporally on small grids (fold_nt),
-    // where lines left dirty in L2 would be written back at the end of the
-    // kernel, on its critical path. The non-temporal stores are buffer
-    // stores: a generic store with a non-temporal hint is merged by the
-    // compiler with a plain one across a branch, losing the hint.
+    // Stores: whole 128-byte lines, non-temporally (B = 512, 100 % fold,
+    // bf16: 127.6 us with half lines through L2, 123.6 us with whole lines
+    // through L2, 117.7 us whole lines non-temporal; at B = 32 non-temporal
+    // stores also avoid writing back dirty L2 lines at the end of the
+    // kernel). They are buffer stores: a generic store with a non-temporal
+    // hint was merged by the compiler with a plain one across a branch,
+    // losing the hint.
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int v = 32 * wave + 16 * blk + fv;
+      const bool low = fv < 8;
+      if constexpr (SF == kStateFp8) {
+        // Whole 128-byte lines from 8-byte fp8 pieces, in two exchanges.
+        // (1) Lane groups g and g ^ 1 (lanes l and l ^ 16, ds_swizzle) trade
+        // one piece per fragment pair pp, so that each lane holds 16
+        // contiguous bytes of its row: g even the st = 2pp piece of channel
+        // blocks g and g + 1, g odd the st = 2pp + 1 piece of blocks g - 1
+        // and g; the four lanes of a row then cover bytes 64pp .. 64pp + 63
+        // (lane offset og). (2) Lanes fv and fv ^ 8 swap their pp = 1 halves
+        // (DPP row_ror:8), and each store writes whole lines of 8 rows, as
+        // for the 16-bit formats.
+        const bool godd = (lane >> 4) & 1;
+        u32x4 d[2];
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const St8<SF> w0 = fold_piece(blk, 2 * pp, v);
-        const St8<SF> w1 = fold_piece(blk, 2 * pp + 1, v);
-        if constexpr (SF != kStateFp8 && VEC) {
-          // Whole 128-byte lines: a fragment holds 64 bytes of each of 16
-          // rows, so lanes fv and fv ^ 8 swap their st = 2pp + 1 pieces (DPP
-          // row_ror:8) and each store then writes channels 64pp .. 64pp + 63
-          // of 8 rows: rows 0-7 of the block (lanes fv < 8 their own st = 2pp
-          // piece, lanes fv >= 8 the received st = 2pp + 1 piece of row
-          // v - 8), then rows 8-15 the other way round.
-          const bool low = fv < 8;
-          u32x4 r;
+        for (int pp = 0; pp < 2; ++pp) {
+          const St8<SF> a = fold_piece(blk, 2 * pp, v);
+          const St8<SF> b = fold_piece(blk, 2 * pp + 1, v);
+          const St8<SF> send = godd ? a : b;
+          u32x2 recv;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            r[i] = static_cast<uint32_t>(
-                __builtin_amdgcn_update_dpp(0, static_cast<int>(w1[i]), 0x128, 0xF, 0xF, false));
-          const int eA = (low ? v : v - 8) * D + 64 * pp + (low ? 0 : 32) + fk;
-          const int eB = (low ? v + 8 : v) * D + 64 * pp + (low ? 32 : 0) + fk;
-          const u32x4 dA = low ? w0 : r;
-          const u32x4 dB = low ? r : w0;
-          __builtin_amdgcn_raw_buffer_store_b128(dA, fold_rsrc, 2 * eA, 0, kStoreNontemporal);
-          __builtin_amdgcn_raw_buffer_store_b128(dB, fold_rsrc, 2 * eB, 0, kStoreNontemporal);
-        } else {
-          // fp8 (32 bytes of each 128-byte row per fragment) and the scalar
-          // path: one store per fragment.
-          const int e0 = v * D + 64 * pp + fk, e1 = e0 + 32;  // element offsets in the head
-          if constexpr (SF == kStateFp8) {
-            if (fold_nt) {
-              __builtin_amdgcn_raw_buffer_store_b64(w0, fold_rsrc, e0, 0, kStoreNontemporal);
-              __builtin_amdgcn_raw_buffer_store_b64(w1, fold_rsrc, e1, 0, kStoreNontemporal);
-            } else {
-              st8_store<SF>(p.state_pool, ce + e0, w0);
-              st8_store<SF>(p.state_pool, ce + e1, w1);
-            }
+          for (int i = 0; i < 2; ++i)  // bit mode: lane l reads lane l ^ 16
+            recv[i] = static_cast<uint32_t>(
+                __builtin_amdgcn_ds_swizzle(static_cast<int>(send[i]), 0x401F));
+          d[pp] = godd ? u32x4{recv[0], recv[1], b[0], b[1]} : u32x4{a[0], a[1], recv[0], recv[1]};
+        }
+        const int og = 16 * (lane >> 5) + 32 * ((lane >> 4) & 1);  // byte offset in 64pp..64pp+63
+        u32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          r[i] = static_cast<uint32_t>(
+              __builtin_amdgcn_update_dpp(0, static_cast<int>(d[1][i]), 0x128, 0xF, 0xF, false));
+        const int bA = (low ? v : v - 8) * D + (low ? 0 : 64) + og;  // byte offsets in the head
+        const int bB = (low ? v + 8 : v) * D + (low ? 64 : 0) + og;
+        __builtin_amdgcn_raw_buffer_store_b128(low ? d[0] : r, fold_rsrc, bA, 0, kStoreNontemporal);
+        __builtin_amdgcn_raw_buffer_store_b128(low ? r : d[0], fold_rsrc, bB, 0, kStoreNontemporal);
+      } else {
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const St8<SF> w0 = fold_piece(blk, 2 * pp, v);
+          const St8<SF> w1 = fold_piece(blk, 2 * pp + 1, v);
+          if constexpr (VEC) {
+            // Whole 128-byte lines: a fragment holds 64 bytes of each of 16
+            // rows, so lanes fv and fv ^ 8 swap their st = 2pp + 1 pieces
+            // (DPP row_ror:8) and each store then writes channels 64pp ..
+            // 64pp + 63 of 8 rows: rows 0-7 of the block (lanes fv < 8 their
+            // own st = 2pp piece, lanes fv >= 8 the received st = 2pp + 1
+            // piece of row v - 8), then rows 8-15 the other way round.
+            u32x4 r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              r[i] = static_cast<uint32_t>(
+                  __builtin_amdgcn_update_dpp(0, static_cast<int>(w1[i]), 0x128, 0xF, 0xF, false));
+            const int eA = (low ? v : v - 8) * D + 64 * pp + (low ? 0 : 32) + fk;
+            const int eB = (low ? v + 8 : v) * D + 64 * pp + (low ? 32 : 0) + fk;
+            const u32x4 dA = low ? w0 : r;
+            const u32x4 dB = low ? r : w0;
+            __builtin_amdgcn_raw_buffer_store_b128(dA, fold_rsrc, 2 * eA, 0, kStoreNontemporal);
+            __builtin_amdgcn_raw_buffer_store_b128(dB, fold_rsrc, 2 * eB, 0, kStoreNontemporal);
           } else {
+            // the scalar path: one store per fragment
+            const int e0 = v * D + 64 * pp + fk;  // element offset in the head
             store8_raw<VEC>(ckpt + e0, w0);
-            store8_raw<VEC>(ckpt + e1, w1);
+            store8_raw<VEC>(ckpt + e0 + 32, w1);
           }
         }
       }
@@ -779,24 +802,22 @@ hipError_t launch_verify(const VerifyParams& p, bool vec, hipStream_t stream) {
   const size_t lds = smem_bytes(hm);
   // exp(Gam_r) * exp(-Gam_j) stays finite when |Gam| <= T * |lower_bound| < 80.
   const bool fact = p.lower_bound > -80.0f / float(p.T) && p.lower_bound <= 0.0f;
-  // fp8 fold stores: non-temporal below 2048 (row, head) items (see the fold)
-  const int fold_nt = blocks < 2048 ? 1 : 0;
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
   const int gk = p.gate_mode & kGateKindMask;
 #define KDA_VERIFY_LAUNCH(V, F, S, DP)                                                             \
   do {                                                                                             \
     switch (gk) {                                                                                  \
       case 0:                                                                                      \
-        hipLaunchKernelGGL((verify_kernel<V, F, 0, S, DP>), grid, block, lds, stream, p, hm, fold_nt); \
+        hipLaunchKernelGGL((verify_kernel<V, F, 0, S, DP>), grid, block, lds, stream, p, hm); \
         break;                                                                                     \
       case 1:                                                                                      \
-        hipLaunchKernelGGL((verify_kernel<V, F, 1, S, DP>), grid, block, lds, stream, p, hm, fold_nt); \
+        hipLaunchKernelGGL((verify_kernel<V, F, 1, S, DP>), grid, block, lds, stream, p, hm); \
         break;                                                                                     \
       case 4:                                                                                      \
-        hipLaunchKernelGGL((verify_kernel<V, F, 4, S, DP>), grid, block, lds, stream, p, hm, fold_nt); \
+        hipLaunchKernelGGL((verify_kernel<V, F, 4, S, DP>), grid, block, lds, stream, p, hm); \
         break;                                                                                     \
       default:                                                                                     \
-        hipLaunchKernelGGL((verify_kernel<V, F, 5, S, DP>), grid, block, lds, stream, p, hm, fold_nt); \
+        hipLaunchKernelGGL((verify_kernel<V, F, 5, S, DP>), grid, block, lds, stream, p, hm); \
     }                                                                                              \
   } while (0)
   // Deep rings (16 or more history rows, the 32-row window): the fold's

@@ -63,7 +63,7 @@ COUNTED_TRAFFIC = {
         sources=("gated_delta_rule_step_amd/csrc/kda_verify.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
-        sha256=("a20efdef338c5c275db6f70cb570d83fdc5d3e6c381bbfcdcfa174dbb156637b",
+        sha256=("074013727313ef29af8be130e243434316d1f5a4764da5dd3234cffb21402e58",
                 "2fe55975814488bcd43f46e6ffd9805dc1139ce860b017fe31783558c0e3b22e",
                 "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
         fetch_kib=123866.664, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),

@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   __syncthreads();
 
   // ---- 3b. fold: S_cur = exp(G_L) * S_ckpt + sum_j u_j D_j over this wave's
-  // fragments, stored in bf16 over the checkpoint. It needs only the
+  // fragments, stored in the state format over the checkpoint. It needs only the
   // checkpoint fragments, exp(G_L), D_j and u_j, all ready here, so its stores
   // drain while phases 4-7 run. (The checkpoint fragments stay in registers
   // for phase 6.) With no history S_cur is the checkpoint itself and nothing
@@ -400,7 +400,6 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
     const __amdgpu_buffer_rsrc_t fold_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<uint8_t*>(p.state_pool) + ce * kStateBytes<SF>, 0, HEAD_ELEMS * kStateBytes<SF>,
         kBufferWord3);
-    // S_cur for fragment (blk, st) of this lane, packed in the state format
     // DEEP (rings holding 16 or more history rows): with hist >= 8 the sum
     // over the history rows, sum_j u_j D_j, runs on MFMA as one K = 32 step
     // (rows j >= hist zero on both sides): A = D^T with its 16 rows permuted
@@ -460,6 +459,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
         }
       }
     }
+    // S_cur for fragment (blk, st) of this lane, packed in the state format
     auto fold_piece = [&](int blk, int st, int v) {
       const int k0 = 32 * st + fk;
       float x[8];

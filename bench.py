@@ -54,7 +54,7 @@ COUNTED_TRAFFIC = {
         sources=("gated_delta_rule_step_amd/csrc/kda_decode.hip",
                  "gated_delta_rule_step_amd/csrc/kda_common.h",
                  "gated_delta_rule_step_amd/build.py"),
-        sha256=("4029b6b78d8c29b3f122b4dc5489c7da83b124ec12e53c4359c8eadfa5ba3820",
+        sha256=("84c78a8d6498618efb1a4d7b64592ce8060e9db6d865bb021275a99a6dec8ae7",
                 "2fe55975814488bcd43f46e6ffd9805dc1139ce860b017fe31783558c0e3b22e",
                 "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
         fetch_kib=96508.367, write_kib=188160.684, fetch_scale=2.0, write_scale=1.0),

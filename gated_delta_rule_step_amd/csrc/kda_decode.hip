@@ -57,8 +57,8 @@ void decode_kernel(DecodeParams p, int group) {
   // unit and the slot index is a scalar load.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Workgroups go to the eight XCDs round-robin by block index. The grid is a
-  // multiple of 8 * group blocks, and block p runs logical block
-  // (8*(k/group) + p%8)*group + k%group with k = p/8, so that every run of
+  // multiple of 8 * group blocks, and block i runs logical block
+  // (8*(k/group) + i%8)*group + k%group with k = i/8, so that every run of
   // `group` consecutive logical blocks shares one XCD: at least the two
   // workgroups of one head (16-row tiles), which then fetch the head's token
   // inputs into one L2, and with large batches all workgroups of one row, so

@@ -150,11 +150,12 @@ def test_batch_sweep_packed_rows(orc, B):
     check_case(orc, case, pool, out)
 
 
-@pytest.mark.parametrize("B", [64, 255, 513])
-def test_two_heads_large_pool(orc, B):
-    """Two heads (four workgroups per row, all on one XCD from 64 rows on),
-    a 3000-slot pool, 5 % inactive rows and INT32_MIN / INT32_MAX indices."""
-    case = synth.decode_case(B=B, N=3000, H=2, seed=synth.seed_for(1, B, 130))
+@pytest.mark.parametrize("B,H", [(64, 2), (255, 2), (513, 2), (70, 5)])
+def test_two_heads_large_pool(orc, B, H):
+    """Two (or five) heads: four (ten) workgroups per row, all on one XCD from
+    64 rows on; a 3000-slot pool, 5 % inactive rows and INT32_MIN / INT32_MAX
+    indices."""
+    case = synth.decode_case(B=B, N=3000, H=H, seed=synth.seed_for(1, B, 130 + H))
     case["idx"][[3, 10]] = [INT32_MIN, INT32_MAX]
     pool, out = run_decode(case)
     check_case(orc, case, pool, out)

@@ -263,6 +263,18 @@ def test_deep_window_full_capacity(orc, T, fm, state_dtype):
     verify_roundtrip(orc, case)
 
 
+@pytest.mark.parametrize("gate_mode", [3, 4])
+def test_deep_window_gate_kinds(orc, gate_mode):
+    """w_ring = 32 (the deep-ring instance, hist ~ U{0..24}) with the
+    pre-computed gate and beta (3) and with one gate per head (4)."""
+    case = build_case(orc, 32, 8, w_ring=32, flush_min=25, hist_max=24)
+    if gate_mode == 4:
+        case = synth.per_head_gate(case, False, synth.seed_for(3, 32, 140))
+    else:
+        case = synth.precomputed_gate(case, gate_mode, synth.seed_for(3, 32, 141))
+    verify_roundtrip(orc, case)
+
+
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 7])
 def test_other_draft_lengths(orc, T):
     case = build_case(orc, 24, T, w_ring=16, flush_min=16 - T + 1, fold_p=0.5, N=64)

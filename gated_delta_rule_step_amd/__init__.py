@@ -144,6 +144,17 @@ def _pool_geometry(state_pool, H):
     return n, (state_pool.stride(0) if n > 0 else H * HEAD_DIM * HEAD_DIM)
 
 
+def _ring_rows(k_cache, u_cache, g_cache, N, H) -> int:
+    """The three ring tensors must each be [N, H, R, 128] with one R; returns R."""
+    shapes = [tuple(t.shape) for t in (k_cache, u_cache, g_cache)]
+    R = shapes[0][2] if len(shapes[0]) == 4 else -1
+    for name, sh in zip(("k_cache", "u_cache", "g_cache"), shapes):
+        if sh != (N, H, R, HEAD_DIM):
+            raise ValueError(f"{name} must be [N={N}, H={H}, R, 128] with the same R as "
+                             f"k_cache, got {list(sh)}")
+    return R
+
+
 def kda_decode(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_indices, out,
                lower_bound: float = -5.0, scale: float = 1.0, gate_mode: int = 0,
                stream=None) -> None:
@@ -194,10 +205,7 @@ def kda_verify_ucache_flush(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool
     if not (k_cache.is_contiguous() and u_cache.is_contiguous()):
         raise ValueError("ring caches must be contiguous")
     N, slot_stride = _pool_geometry(state_pool, H)
-    if N and (k_cache.shape[:2] != (N, H) or u_cache.shape[:2] != (N, H) or
-              g_cache.shape[:2] != (N, H)):
-        raise ValueError("ring caches must be [N, H, R, 128]")
-    R = k_cache.shape[2]
+    R = _ring_rows(k_cache, u_cache, g_cache, N, H)
     st = lib().kda_verify_ucache_flush(
         B, T, H, HEAD_DIM, HEAD_DIM,
         _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1),
@@ -275,9 +283,7 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
         _i32("cache_base", cache_base)
         if not (kc.is_contiguous() and uc.is_contiguous() and gc.is_contiguous()):
             raise ValueError("ring caches must be contiguous")
-        if N and (kc.shape[:2] != (N, H) or uc.shape[:2] != (N, H) or gc.shape[:2] != (N, H)):
-            raise ValueError("ring caches must be [N, H, R, 128]")
-        R = kc.shape[2]
+        R = _ring_rows(kc, uc, gc, N, H)
     cu_h = _P(cu_seqlens_host.data_ptr())
     st = lib().kda_prefill_varlen(
         n_docs, Ttot, H, HEAD_DIM, HEAD_DIM, cu_h, _ptr(cu_seqlens),

@@ -273,7 +273,9 @@ extern "C" kda_status kda_prefill_varlen(
   if (q_tok_stride < 0 || k_tok_stride < 0 || v_tok_stride < 0 || g_tok_stride < 0 ||
       beta_tok_stride < 0 || out_tok_stride < 0 || slot_stride < 0)
     return KDA_ERR_BAD_STRIDE;
-  if (total_tokens > 1 && out_tok_stride < W) return KDA_ERR_BAD_STRIDE;
+  // also for a single token: a chunk's padding rows must fall outside the
+  // output rows it stores
+  if (total_tokens >= 1 && out_tok_stride < W) return KDA_ERR_BAD_STRIDE;
   // a 16-token chunk of outputs is stored through one 32-bit buffer range
   if (out_tok_stride > (int64_t(1) << 25)) return KDA_ERR_UNSUPPORTED;
   if (num_slots > 1 && slot_stride < W * D) return KDA_ERR_BAD_STRIDE;

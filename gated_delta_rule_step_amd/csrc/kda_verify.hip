@@ -202,8 +202,10 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   const int32_t slot = p.state_indices[b];
   const int hist = p.hist_len[b];
   const int base = p.cache_base[b];
+  // hist <= w_ring - T rather than hist + T <= w_ring: a hist_len near
+  // INT32_MAX must not wrap into an active row
   const bool active = slot >= 0 && int64_t(slot) < p.num_slots && hist >= 0 &&
-                      hist + T <= p.w_ring && base >= 0 && base < R;
+                      hist <= p.w_ring - T && base >= 0 && base < R;
   uint16_t* outb = p.out + b * p.out_row_stride + int64_t(h) * D;
   if (!active) {
     for (int e = tid; e < T * D; e += 256) outb[int64_t(e >> 7) * p.out_tok_stride + (e & 127)] = 0;

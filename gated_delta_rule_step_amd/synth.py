@@ -103,16 +103,17 @@ def state_indices(rng, B: int, N: int, inactive_frac: float = 0.05) -> np.ndarra
     return idx.astype(np.int32)
 
 
-def precomputed_gate(case: dict, gate_mode: int, seed: int) -> dict:
+def precomputed_gate(case: dict, gate_mode: int, seed: int, g_low: float = -6.0) -> dict:
     """A copy of a decode, verify or prefill case whose gate and / or beta
     inputs follow the pre-computed convention (gate_mode bit 1: the log-decay
-    itself, drawn U(-6, 0.5) so that some values lie outside [-5, 0]; bit 2:
-    beta itself, drawn U(0, 1)), as bf16 bits; case["gate_mode"] records it."""
+    itself, drawn U(g_low, 0.5), by default U(-6, 0.5) so that some values lie
+    outside [-5, 0]; bit 2: beta itself, drawn U(0, 1)), as bf16 bits;
+    case["gate_mode"] records it."""
     rng = np.random.Generator(np.random.PCG64(seed))
     c = dict(case)
     c["gate_mode"] = int(gate_mode)
     if gate_mode & 1:
-        c["gate"] = bf16_bits(rng.uniform(-6.0, 0.5, case["gate"].shape).astype(np.float32))
+        c["gate"] = bf16_bits(rng.uniform(g_low, 0.5, case["gate"].shape).astype(np.float32))
     if gate_mode & 2:
         c["beta"] = bf16_bits(rng.uniform(0.0, 1.0, case["beta"].shape).astype(np.float32))
     return c

@@ -43,25 +43,38 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the same source (host
+# code only), loaded instead of _LIB when KDA_ORACLE_LIB names it; the process
+# must then preload gcc's libasan (see tests/test_sanitizers.py).
+SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
 _lib = None
 
 _I32P = ctypes.POINTER(ctypes.c_int32)
 
 
-def build(force: bool = True) -> str:
-    """Compile kda_oracle.cpp into liboracle.so with g++ (OpenMP, IEEE math)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile kda_oracle.cpp into liboracle.so with g++ (OpenMP, IEEE math);
+    sanitize=True builds liboracle_san.so with -fsanitize=address,undefined
+    (aborting on the first report) instead."""
+    out = SAN_LIB if sanitize else _LIB
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        tmp = out + ".tmp"
+        extra = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                 "-fno-omit-frame-pointer", "-g"] if sanitize else []
         cmd = ["g++", "-std=c++17", "-O2", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
-               "-ffp-contract=off", _SRC, "-o", tmp]
+               "-ffp-contract=off", *extra, _SRC, "-o", tmp]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, out)
+    return out
 
 
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
+        path = os.environ.get("KDA_ORACLE_LIB")
+        if path:  # an alternative build of the same source (the sanitizer leg)
+            _lib = ctypes.CDLL(path)
+            return _lib
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
         _lib = ctypes.CDLL(_LIB)

@@ -412,7 +412,8 @@ void verify(int B, int T, int H, int K, int V, const Real* q, const Real* k, con
   for (int b = 0; b < B; ++b) {
     for (int h = 0; h < H; ++h) {
       const int hist = hist_len[b], base = cache_base[b];
-      const bool active = slot_active(idx[b], N) && hist >= 0 && hist + T <= w_ring &&
+      // hist <= w_ring - T: the sum hist + T would overflow for hist near INT32_MAX
+      const bool active = slot_active(idx[b], N) && hist >= 0 && hist <= w_ring - T &&
                           base >= 0 && base < R;
       if (!active) {
         for (int t = 0; t < T; ++t)

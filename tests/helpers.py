@@ -15,6 +15,14 @@ HD = 128
 #    max(|ref|, 2^-12) (the floor covers elements that cancel to ~0);
 #  * cumulative log-decay (fp32): |got - ref| <= 1e-5 + 1e-5 |ref|.
 OUT_ATOL, OUT_RTOL = 1e-2, 1.6e-2
+# Next to the element-wise test, a normwise one: ||got - ref||_2 <= NORM * ||ref||_2
+# over the outputs compared. At the configs' inputs the outputs are small (median
+# |o| ~ 0.025), where the element-wise bound is dominated by OUT_ATOL; the normwise
+# bound is the one that sees a systematic error of a few per mille. Decode and
+# verify keep fp32 (or split-bf16) state products: 2e-3, about one bf16 rounding of
+# every element; prefill's output path takes single-term bf16 products: 5e-3.
+OUT_NORM = 2e-3
+OUT_NORM_PREFILL = 5e-3
 STATE_ULPS, STATE_FLOOR = 2, 2.0 ** -12
 
 
@@ -108,7 +116,16 @@ def check_pool(case, got_bits, ref, what="state"):
                              f"ref {ref[i]!r}")
 
 
-def check_out(got_bits, ref, what="output"):
+def normwise_error(got, ref) -> float:
+    """||got - ref||_2 / ||ref||_2 (0 when both are zero)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = float(np.linalg.norm(ref))
+    num = float(np.linalg.norm(got - ref))
+    return num / den if den > 0 else (0.0 if num == 0 else np.inf)
+
+
+def check_out(got_bits, ref, what="output", norm=OUT_NORM):
     got = f32(got_bits).astype(np.float64).reshape(ref.shape)
     ref = ref.astype(np.float64)
     excess = np.abs(got - ref) - (OUT_ATOL + OUT_RTOL * np.abs(ref))
@@ -117,6 +134,9 @@ def check_out(got_bits, ref, what="output"):
         i = np.unravel_index(np.argmax(np.where(bad, excess, -np.inf)), ref.shape)
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements out of tolerance; "
                              f"worst at {i}: got {got[i]!r} ref {ref[i]!r}")
+    e = normwise_error(got, ref)
+    if not e <= norm:
+        raise AssertionError(f"{what}: normwise error {e:.3e} above {norm:.1e}")
 
 
 def check_state(got_bits, ref, what="state"):
@@ -177,3 +197,16 @@ def oracle_decode(orc, case, pool_bits=None):
                      case["lower_bound"], case["scale"], cpool, cidx, bf16_storage=True,
                      real=np.float32, gate_mode=gm, state_dtype=case.get("state_dtype", 0))
     return out, slots, cpool
+
+
+def report_accuracy(name: str, **figures) -> None:
+    """Append accuracy figures (e.g. normwise errors against an fp64 oracle run)
+    as one JSON line to the file named by KDA_ACCURACY_LOG, if set, and print them."""
+    import json
+    import os
+    line = json.dumps(dict(test=name, **{k: float(v) for k, v in figures.items()}))
+    print(line)
+    path = os.environ.get("KDA_ACCURACY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(line + "\n")

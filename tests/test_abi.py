@@ -187,6 +187,7 @@ def test_prefill_workspace_and_validation(lib):
     assert call([0, 5, 7], 9) == SEQ    # must end at total_tokens
     assert call([0, 5], 5, K=64) == UNSUP
     assert call([0, 5], 5, ots=8) == STRIDE
+    assert call([0, 1], 1, ots=0) == STRIDE   # one token: out rows still H*128 apart
     # 16-token chunks need |lower_bound| <= 5.5 (each decay factor within e^44)
     assert call([0, 5], 5, lb=-5.6) == UNSUP
     assert call([0, 5], 5, lb=float("nan")) == UNSUP

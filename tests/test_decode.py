@@ -70,6 +70,23 @@ def test_precomputed_gate_conventions(orc, gate_mode, B):
     check_case(orc, case, pool, out)
 
 
+@pytest.mark.parametrize("gate_mode,B", [(1, 64), (3, 512), (5, 64)])
+def test_no_decay_floor(orc, gate_mode, B):
+    """lower_bound = -INFINITY with pre-computed log-decays drawn U(-20, 0.5):
+    no floor, decays down to exp(-20) (per channel, and per head with bit 4)."""
+    case = synth.decode_case(B=B, H=12)
+    if gate_mode & 4:
+        case = synth.per_head_gate(case, True, synth.seed_for(1, B, 170))
+        rng = np.random.Generator(np.random.PCG64(synth.seed_for(1, B, 171)))
+        case["gate"] = synth.bf16_bits(rng.uniform(-20.0, 0.5, case["gate"].shape)
+                                       .astype(np.float32))
+    else:
+        case = synth.precomputed_gate(case, gate_mode, synth.seed_for(1, B, 172), g_low=-20.0)
+    case["lower_bound"] = -np.inf
+    pool, out = run_decode(case)
+    check_case(orc, case, pool, out)
+
+
 @pytest.mark.parametrize("B", [1, 32, 512])
 def test_fp16_state(orc, B):
     """An fp16 state pool (state_dtype 1), B = 1, 32 and 512 (the three tile

@@ -12,7 +12,8 @@ import pytest
 
 from gated_delta_rule_step_amd import synth
 from tests.helpers import (HD, bits, check_gcache, check_out, check_pool, check_state,
-                           compact_slots, dev, dev_bf16, f32, pool_dev, pool_vals, split_qkv)
+                           compact_slots, dev, dev_bf16, f32, normwise_error, pool_dev, pool_vals,
+                           report_accuracy, split_qkv)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -134,8 +135,9 @@ def check_all(case, st, ref_out, pool0, kc0, uc0, gc0, T=None, hist=None, base=N
     torch.cuda.synchronize()
     B, H, R = case["B"], case["H"], case["R"]
     T = case["T"] if T is None else T
-    hist = case["hist_len"] if hist is None else hist
-    base = case["cache_base"] if base is None else base
+    # int64 copies: hist + T must not wrap for hist_len near INT32_MAX
+    hist = np.asarray(case["hist_len"] if hist is None else hist, np.int64)
+    base = np.asarray(case["cache_base"] if base is None else base, np.int64)
     fm = case["flush_min"] if flush_min is None else flush_min
     slots, cidx = case["slots"], case["cidx"]
     check_out(bits(st["out"]), ref_out.reshape(B, T, H * HD), "verify output")
@@ -275,6 +277,89 @@ def test_deep_window_gate_kinds(orc, gate_mode):
     verify_roundtrip(orc, case)
 
 
+@pytest.mark.parametrize("T,fm,w,gate_mode,lb,misaligned", [
+    (8, 9, 16, 0, -12.0, False),        # raw gate, T |lb| = 96 >= 80
+    (8, 9, 16, 1, -np.inf, False),      # pre-computed log-decay down to -20, no floor
+    (4, 13, 16, 3, -np.inf, False),     # and pre-sigmoided beta
+    (8, 25, 32, 1, -np.inf, False),     # 32-row window (hist ~ U{0..24})
+    (8, 9, 16, 0, -12.0, True),         # the scalar (unaligned) path
+    (4, 13, 16, 1, -np.inf, True)])
+def test_unfactored_exponentials(orc, T, fm, w, gate_mode, lb, misaligned):
+    """lower_bound <= -80 / T selects the instance that forms each weight
+    exp(Gam_r - Gam_j) directly instead of as exp(Gam_r) * exp(-Gam_j) (whose
+    factors could overflow): ring history and folding rows, B = 64, vector
+    and scalar paths; pre-computed log-decays drawn U(-20, 0.5), so that the
+    cumulative decay of a draft reaches well past exp(-80)."""
+    B = 64
+    if w == 32:
+        case = build_case(orc, B, T, w_ring=32, flush_min=fm, hist_max=24, N=96)
+    else:
+        case = build_case(orc, B, T, w_ring=w, flush_min=fm, fold_p=0.5, N=96)
+    if gate_mode:
+        case = synth.precomputed_gate(case, gate_mode, synth.seed_for(3, B, 160 + T),
+                                      g_low=-20.0)
+    case["lower_bound"] = float(lb)
+    if not misaligned:
+        verify_roundtrip(orc, case)
+        return
+    snap = (case["pool"].copy(), case["k_cache"].copy(), case["u_cache"].copy(),
+            case["g_cache"].copy())
+    H = case["H"]
+    W = H * HD
+    rs = T * (3 * W + 1)
+    buf = torch.zeros(B * rs + 2, dtype=torch.bfloat16, device="cuda")
+    rows = buf[1:1 + B * rs].view(B, T, 3 * W + 1)
+    rows[..., :3 * W] = dev_bf16(case["qkv"])
+    obuf = torch.full((B * T * (W + 1) + 1,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = obuf[1:].view(B, T, W + 1)[..., :W]
+    st = dict(pool=dev_bf16(case["pool"]), kc=dev_bf16(case["k_cache"]),
+              uc=dev_bf16(case["u_cache"]), gc=dev(case["g_cache"]), out=out)
+    pre = gate_mode & 1
+    _kda().kda_verify_ucache_flush(
+        rows[..., :W], rows[..., W:2 * W], rows[..., 2 * W:3 * W], dev_bf16(case["gate"]),
+        dev_bf16(case["beta"]), None if pre else dev(case["a_log"]),
+        None if pre else dev(case["dt_bias"]), st["pool"], dev(case["idx"]), st["kc"],
+        st["uc"], st["gc"], dev(case["hist_len"]), dev(case["cache_base"]), out,
+        flush_min=fm, w_ring=w, lower_bound=float(lb), gate_mode=gate_mode)
+    ref = run_oracle(orc, case)
+    check_all(case, st, ref, *snap)
+
+
+@pytest.mark.parametrize("T,fm,w,hist_max,p", [(8, 9, 16, None, 0.5), (4, 13, 16, None, 1.0),
+                                               (8, 25, 32, 24, 0.0)])
+def test_accuracy_against_fp64(orc, T, fm, w, hist_max, p):
+    """Outputs and folded checkpoints against an fp64 oracle run on the same
+    inputs (the same bf16 checkpoint and ring rows) with no storage rounding:
+    what the bf16 MFMA products (split operands) and the bf16 stores cost.
+    Reported, and bounded normwise (outputs 3e-3, folded checkpoints 3e-3)."""
+    B = 128
+    case = build_case(orc, B, T, w_ring=w, flush_min=fm, fold_p=p, hist_max=hist_max, N=256)
+    st = run_gpu(case)
+    H = case["H"]
+    q, k, v, g, be = _tok_arrays(case["qkv"], case["gate"], case["beta"], H)
+    d = np.float64
+    pool64 = case["opool"].astype(d)
+    kc64, uc64, gc64 = (case[n].astype(d) for n in ("okc", "ouc", "ogc"))
+    ref = orc.verify(q.astype(d), k.astype(d), v.astype(d), g.astype(d), be.astype(d),
+                     case["a_log"].astype(d), case["dt_bias"].astype(d), case["lower_bound"],
+                     case["scale"], pool64, case["cidx"], kc64, uc64, gc64, case["hist_len"],
+                     case["cache_base"], fm, w, bf16_storage=False, real=d)
+    torch.cuda.synchronize()
+    got = f32(bits(st["out"])).reshape(ref.shape).astype(d)
+    e_out = normwise_error(got, ref)
+    folds = [b for b in range(B) if case["cidx"][b] >= 0 and case["hist_len"][b] + T >= fm]
+    pool = f32(bits(st["pool"]))
+    if folds:
+        gs = np.stack([pool[case["slots"][case["cidx"][b]]] for b in folds])
+        rs = np.stack([pool64[case["cidx"][b]] for b in folds])
+        e_ck = normwise_error(gs, rs)
+    else:
+        e_ck = 0.0
+    report_accuracy(f"verify T={T} w={w} fm={fm}", out_normwise=e_out, fold_normwise=e_ck,
+                    folds=len(folds))
+    assert e_out <= 3e-3 and e_ck <= 3e-3, (e_out, e_ck)
+
+
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 7])
 def test_other_draft_lengths(orc, T):
     case = build_case(orc, 24, T, w_ring=16, flush_min=16 - T + 1, fold_p=0.5, N=64)
@@ -319,6 +404,9 @@ def test_inactive_rows_and_bad_ring_metadata(orc):
     case["hist_len"][4] = 13          # hist + T > w_ring
     case["cache_base"][5] = 32        # base outside the ring
     case["cache_base"][6] = -1
+    imax = np.iinfo(np.int32).max     # hist + T would wrap to a negative int32
+    case["hist_len"][7] = imax
+    case["hist_len"][8] = imax - 3
     slots, cidx = compact_slots(case["idx"], case["N"])
     case["slots"], case["cidx"] = slots, cidx
     case["opool"] = np.ascontiguousarray(f32(case["pool"][slots]))

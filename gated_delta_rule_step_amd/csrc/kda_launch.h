@@ -104,9 +104,18 @@ struct PrefillParams {
 hipError_t launch_decode(const DecodeParams& p, bool vec, hipStream_t stream);
 hipError_t launch_verify(const VerifyParams& p, bool vec, hipStream_t stream);
 
-// Prefill needs the host copy of cu_seqlens to plan its launches.
+// Prefill needs the host copy of cu_seqlens to plan its launches. Calls with
+// at least kFusedMinChains (document, head) chains -- one per CU of the chip,
+// a fixed count so that the workspace size does not depend on the device --
+// run the fused 64-token kernel (no workspace); calls with fewer run the
+// two-stage form (a preparation kernel over all 16-token chunks, then the
+// chain), which needs a workspace.
+constexpr int64_t kFusedMinChains = 256;
 size_t prefill_workspace_bytes(int32_t n_docs, int64_t total_tokens, int32_t H);
 hipError_t launch_prefill(const PrefillParams& p, const int32_t* cu_host, bool vec,
                           hipStream_t stream);
+size_t prefill_split_workspace_bytes(int32_t n_docs, int64_t total_tokens, int32_t H);
+hipError_t launch_prefill_split(const PrefillParams& p, const int32_t* cu_host, bool vec,
+                                hipStream_t stream);
 
 }  // namespace kda

@@ -1,62 +1,52 @@
-// Chunked varlen prefill of the KDA recurrence (gfx950): a preparation
-// kernel over every (chunk, head) and a chain kernel over every
-// (document, head).
+// Chunked varlen prefill of the KDA recurrence (gfx950): one fused kernel,
+// one 512-thread workgroup per (document, head), 64-token chunks.
 //
 // Operation: "feat(kda): add CuTe DSL recurrent prefill backend" -- packed
-// documents delimited by cu_seqlens, each (document, head) chain runs the
+// documents delimited by cu_seqlens; each (document, head) chain runs the
 // gated delta-rule recurrence over its tokens from an optional initial state
-// and leaves its final state in the pool; the work is chunked (BT = 16 on
-// that page) into an intra-chunk preparation and a sequential chain over
-// chunks, the two stages of that page's prefill. The result equals the
-// token-by-token recurrence.
+// and leaves its final state in the pool; the work splits into an intra-chunk
+// preparation and a sequential chain over chunks, the two stages of that
+// page's prefill. The result equals the token-by-token recurrence.
 //
-// Chunkwise form used here (WY representation of the delta rule with the
-// decay carried per key channel; Yang et al., "Parallelizing Linear
-// Transformers with the Delta Rule over Sequence Length", 2024). For a chunk
-// of c <= 16 tokens r entering with state S (S[v][k]: value channel v, key
-// channel k), Gam_r = g_0 + ... + g_r per key channel:
-//   A[r,j] = sum_k k_r k_j exp(Gam_r - Gam_j)         (j < r)
-//   P[r,j] = sum_k q_r k_j exp(Gam_r - Gam_j)         (j <= r)
-//   W_r    = beta_r (exp(Gam_r) k_r - sum_{j<r} A[r,j] W_j)
-//   U0_r   = beta_r (v_r - sum_{j<r} A[r,j] U0_j)
-//   U      = U0 - W S^T         (rows are the per-token corrections u_r)
-//   O      = scale ((exp(Gam) q) S^T + P U)
-//   S      = S diag(exp(Gam_c)) + U^T (exp(Gam_c - Gam) k)
-// Everything but the last three lines is independent of the state, so it runs
-// for all chunks of all documents at once (prep_kernel); only the last three
-// lines are sequential (chain_kernel).
+// Chunkwise form (WY representation of the delta rule, Yang et al.,
+// "Parallelizing Linear Transformers with the Delta Rule over Sequence
+// Length", 2024, with the decay carried per key channel). For a chunk of
+// c <= 64 tokens r entering with state S (S[k][v] here: key channel k, value
+// channel v), Gam_r = g_0 + ... + g_r per key channel:
+//   A[r,j] = sum_k k_r k_j exp(Gam_r - Gam_j)            (j < r)
+//   P[r,j] = sum_k q_r k_j exp(Gam_r - Gam_j)            (j <= r)
+//   T      = (I + diag(beta) A)^-1,  T' = T diag(beta)
+//   W      = T' (exp(Gam) k),  U0 = T' V
+//   U      = U0 - W S             (rows are the per-token corrections u_r)
+//   O      = scale ((exp(Gam) q) S + P U)
+//   S      = diag(exp(Gam_e)) S + (exp(Gam_e - Gam) k)^T U
+// with Gam_e the prefix at the last token that enters the state (the chunk's
+// last token, or the last one before a hand-off tail). The lines up to U0 do
+// not depend on the state ("preparation"); the last three are the chain.
 //
-// Every weight exp(Gam_r - Gam_j) of A and P factors into
-// exp(Gam_r - m) * exp(m - Gam_j) with m = Gam_last / 2 per key channel: over
-// 16 tokens |Gam_r - m| <= 8 |lower_bound| <= 44 (the host requires
-// |lower_bound| <= 5.5), so both factors, and a key channel scaled by either,
-// stay far from fp32 overflow and from denormals. W is solved for the
-// right-hand side exp(Gam_r - m) k_r and scaled by exp(m) afterwards (the solve
-// is linear per key channel).
+// Precision. Every product the state depends on (A, W, U0, W S, the state
+// update) runs on bf16 MFMA with its fp32 operands split into bf16 hi + lo
+// parts and three terms (hi hi + hi lo + lo hi; V is exact in bf16, so U0
+// needs two); T is formed in fp32 on fp32 MFMA (diagonal 16 x 16 blocks as
+// the finite product (I + N)(I + N^2)(I + N^4)(I + N^8) of their strictly
+// lower part N = -diag(beta) A, the others by block substitution). P takes
+// three terms as well and is stored in bf16; the read-out products take the
+// state and U in two terms against the bf16 exp(Gam) q and P; O is stored in
+// bf16.
 //
-// Chunk record. The preparation leaves, per (chunk, head), the chain's
-// operands in the workspace already in MFMA fragment order, so the chain
-// moves them with 16-byte loads and reads them with one LDS read per
-// fragment. Lane l = n16 + 16 g4 of a wave:
-//   W   [kt 4][hi, lo][lane][8 bf16]  W[n16][32kt + 4g4 + 0..3, 32kt + 16 + 4g4 + 0..3]
-//   Q   [kt 4][lane][8 bf16]          (exp(Gam) q_hat) at the same positions, bf16
-//   KT  [mt 8][lane][4 hi, 4 lo bf16] (exp(Gam_c - Gam) k_hat)[4g4 + 0..3][16mt + n16]
-//   U0  [vt 8][lane][4 fp32]          U0[4g4 + 0..3][16vt + n16]
-//   P   [lane][4 bf16]                P[n16][4g4 + 0..3]
-//   EG  [128 fp32]                    exp(Gam_c)
-// The chain's state S[v][k] sits in the MFMA accumulator layout: wave w, tile
-// (mt, nt) holds key channels 16mt + 4g4 + i and value channel 32w + 16nt + n16,
-// so the B fragment of v_mfma_f32_16x16x32_bf16 takes its 8 key channels as two
-// runs of 4 from accumulator tiles 2kt and 2kt+1 (the order the W and Q
-// fragments are written in), and U = U0 - W S^T comes out in the accumulator
-// layout, which is the B fragment of v_mfma_f32_16x16x16_bf16 with the chunk's
-// tokens as the contraction.
+// Decay factoring. A chunk is four 16-token blocks b (block-local prefix
+// lam_r, block total tau_b, block start o_b = Gam at the token before it).
+// Diagonal blocks of A and P factor exp(Gam_r - Gam_j) around the block's
+// midpoint (both factors within exp(+-8 |lower_bound|), |lower_bound| <= 5.5);
+// off-diagonal blocks around a block boundary between the two tokens, so both
+// factors are at most 1 and a factor underflows only where the weight is
+// negligible: pairs (1,0), (2,1) at o_1, o_2; (3,2) at o_3; (2,0), (3,0),
+// (3,1) at o_2.
 //
-// Chunk slots. Chunk j of document d (first token t0) has slot
-// d + floor(t0 / 16) + j: strictly increasing over (d, j), fewer than
-// n_docs + floor(Ttot / 16) in all, and computable by the chain from (d, j)
-// alone; the preparation finds (d, j) from its slot by a search over
-// cu_seqlens.
+// Layouts. Token-owner phases: wave w holds block b = w/2 and key channels
+// 64 (w%2) + 32 s + 8 (lane/16) + i, i < 8, of token 16 b + lane%16; chain
+// phases: wave w owns value channels 16 w .. 16 w + 15 of the fp32 state,
+// held as eight 16 x 16 accumulator tiles (key channels 16 m + 4 (lane/16) + i).
 
 #include "kda_common.h"
 #include "kda_launch.h"
@@ -65,116 +55,160 @@ namespace kda {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));  // bf16 operands of the K = 16 MFMA
+typedef __fp16 f16x8 __attribute__((__vector_size__(8 * sizeof(__fp16))));
 
-constexpr int C = 16;          // tokens per chunk
-constexpr int RS = D + 4;      // padded row (fp32) of the [token][channel] LDS arrays: the
-                               // 16 rows read by one MFMA fragment load hit different banks
-constexpr int XLD = D + 4;     // padded row (bf16) of W as bf16 hi / lo
+constexpr int CH = 64;       // tokens per chunk (at most)
+constexpr int NTHR = 512;    // threads per workgroup
 constexpr int kMaxOrderedDocs = 256;
 
-// chunk record, bytes
-constexpr int kRecW = 0;
-constexpr int kRecQ = 8192;
-constexpr int kRecKT = 12288;
-constexpr int kRecU0 = 20480;
-constexpr int kRecP = 28672;
-constexpr int kRecEG = 29184;
-constexpr int kRecBytes = 29696;
-constexpr int kRecUnits = kRecBytes / 16;  // 16-byte units
-constexpr int kThreads = 256;
-constexpr int kRecRounds = (kRecUnits + kThreads - 1) / kThreads;  // 8
-static_assert(kRecEG + 4 * D == kRecBytes, "record layout");
-static_assert(kRecUnits > (kRecRounds - 1) * kThreads, "every round has work");
+// ---- LDS layout (bytes). Arrays of one phase group alias those of another
+// only when a barrier separates the last read from the first write.
+constexpr int VRS = D + 8;     // bf16 row of v (token-major)
+constexpr int KGS = D + 8;     // bf16 row of the right operands of A / P
+constexpr int TRS = CH + 8;    // bf16 row of channel-major arrays (x^T, k~^T) and of T', P
+constexpr int AMS = CH + 4;    // fp32 row of A (scaled by beta)
+
+constexpr int L_NRM = 0;                                // f32 [2][64][2] norm partials
+constexpr int L_TAU = L_NRM + 2 * CH * 2 * 4;           // f32 [4][128] block totals
+constexpr int L_CUT = L_TAU + 4 * D * 4;                // f32 [128] prefix at the cut
+constexpr int L_BETA = L_CUT + D * 4;                   // f32 [64]
+constexpr int L_EG = L_BETA + CH * 4;                   // f32 [128] exp(Gam_e)
+constexpr int L_SEM = L_EG + D * 4;                     // f32 [4][128] exp(tau_b / 2)
+constexpr int L_SEO = L_SEM + 4 * D * 4;                // f32 [4][128] exp(o_b)
+constexpr int L_SPH = L_SEO + 4 * D * 4;                // f32 [4][128] exp(Gam_e - o_b - tau_b)
+constexpr int L_SO = L_SPH + 4 * D * 4;                 // f32 [4][128] o_b
+constexpr int L_ST1 = L_SO + 4 * D * 4;                 // f32 [128] exp(tau_1)
+constexpr int L_ST2 = L_ST1 + D * 4;                    // f32 [128] exp(tau_2)
+constexpr int L_SGE = L_ST2 + D * 4;                    // f32 [128] Gam_e
+constexpr int L_TD = L_SGE + D * 4;                     // f32 [4][16][17] diagonal blocks of T
+constexpr int L_DTB = L_TD + 4 * 16 * 17 * 4;           // f32 [128] dt_bias of the head
+constexpr int L_DLT = L_DTB + D * 4;                    // f32 [64] beta - bf16 hi - bf16 lo
+constexpr int L_VR = L_DLT + CH * 4;                    // bf16 [64][VRS] v
+constexpr int L_QOP = L_VR + CH * VRS * 2;              // bf16 [4 b][4 kt][64 lane][8]
+constexpr int L_PM = L_QOP + 4 * 4 * 64 * 16;           // fp16 [64][TRS] P
+constexpr int L_TP = L_PM + CH * TRS * 2;               // bf16 [2 hl][64][TRS] T'
+constexpr int L_X1 = L_TP + 2 * CH * TRS * 2;           // region X1 (below)
+constexpr int X1_BYTES = 2 * D * TRS * 2;               //   KGR | AM | WOP | KT
+constexpr int L_X2 = L_X1 + X1_BYTES;                   // region X2: PART | XT | OST
+constexpr int X2_BYTES = 2 * D * TRS * 2;
+constexpr int kLdsBytes = L_X2 + X2_BYTES;
+// region X1 tenants
+constexpr int KGR_BYTES = 4 * 2 * 16 * KGS * 2;         // bf16 [4 slots][2 hl][16][KGS]
+constexpr int AM_BYTES = CH * AMS * 4;                  // f32 [64][AMS]
+constexpr int WOP_BYTES = 4 * 4 * 2 * 64 * 16;          // bf16 [4 b][4 kt][2 hl][64][8]
+constexpr int KT_BYTES = 2 * D * TRS * 2;               // fp16 [2 hl][128][TRS]
+// region X2 tenants
+constexpr int PART_BYTES = 10 * 2 * 256 * 4;            // f32 [10 pairs][A, P][64 lanes][4]
+constexpr int XT_BYTES = 2 * D * TRS * 2;               // bf16 [2 hl][128][TRS]
+constexpr int OSS = D + 8;                              // bf16 row of the staged outputs
+constexpr int OST_BYTES = CH * OSS * 2;                 // bf16 [64][OSS]
+static_assert(KGR_BYTES <= X1_BYTES && AM_BYTES <= X1_BYTES && WOP_BYTES <= X1_BYTES &&
+                  KT_BYTES <= X1_BYTES,
+              "region X1");
+static_assert(PART_BYTES <= X2_BYTES && XT_BYTES <= X2_BYTES && OST_BYTES <= X2_BYTES,
+              "region X2");
+static_assert(kLdsBytes <= 160 * 1024, "LDS of one CU");
+static_assert(L_VR % 16 == 0 && L_QOP % 16 == 0 && L_PM % 16 == 0 && L_TP % 16 == 0 &&
+                  L_X1 % 16 == 0 && L_X2 % 16 == 0 && L_TD % 16 == 0 && L_DTB % 16 == 0 &&
+                  L_DLT % 16 == 0,
+              "16-byte aligned arrays");
 
 struct DocOrder {
   int32_t n;  // 0: natural order
   int32_t doc[kMaxOrderedDocs];
 };
 
-struct PSmem {
-  float* qh;     // [C][RS] q_hat, then exp(Gam - m) q_hat as bf16 hi / lo pairs, then W
-  float* kh;     // [C][RS] k_hat, then exp(Gam - m) k_hat as bf16 hi / lo pairs
-  float* gg;     // [C][RS] g, then exp(Gam_last - Gam) k_hat
-  float* u0;     // [C][RS] U0
-  float* kb;     // [C][RS] exp(m - Gam) k_hat as bf16 hi / lo pairs, in the U0 rows
-                 // (dead by the time U0 is solved)
-  float* kw;     // [C][RS] exp(Gam - m) k_hat in fp32: right-hand side of W
-  float* am;     // [C][C] A
-  float* beta;   // [C]
-  float* egl;    // [D] exp(Gam_last)
-  float* em;     // [D] exp(Gam_last / 2)
-  uint16_t* vv;    // [C][VLD] v (bf16, as loaded)
-  uint16_t* wop;   // [2][C][XLD] W, bf16 hi / lo, in the q rows (dead after A and P)
-  uint16_t* qop;   // [C][QLD] exp(Gam) q_hat, bf16
-  uint16_t* ktop;  // [2][C][D] exp(Gam_last - Gam) k_hat, bf16 hi / lo, in the g rows
-                   // (dead once the prefix sums are taken)
-  uint16_t* pop;   // [C][C] P, bf16
-};
-
-constexpr int VLD = D + 8;  // row (bf16) of v: 16-byte aligned rows
-constexpr int QLD = D + 4;  // row (bf16) of exp(Gam) q_hat
-static_assert(2 * C * XLD * 2 <= C * RS * 4, "W fits in the q rows");
-static_assert(2 * C * D * 2 <= C * RS * 4, "K~ fits in the g rows");
-constexpr size_t kPrepLds = size_t(5 * C * RS + C * C + C + 2 * D) * 4 +
-                            size_t(C * VLD + C * QLD + C * C) * 2;
-
-__device__ inline PSmem pcarve(float* base) {
-  PSmem s;
-  float* p = base;
-  s.qh = p; p += C * RS;
-  s.kh = p; p += C * RS;
-  s.gg = p; p += C * RS;
-  s.u0 = p; p += C * RS;
-  s.kb = s.u0;
-  s.kw = p; p += C * RS;
-  s.am = p; p += C * C;
-  s.beta = p; p += C;
-  s.egl = p; p += D;
-  s.em = p; p += D;
-  uint16_t* b = reinterpret_cast<uint16_t*>(p);
-  s.vv = b; b += C * VLD;
-  s.qop = b; b += C * QLD;
-  s.pop = b;
-  s.wop = reinterpret_cast<uint16_t*>(s.qh);
-  s.ktop = reinterpret_cast<uint16_t*>(s.gg);
-  return s;
+// Pair numbering of the 16 x 16 blocks of A and P computed per chunk.
+// (0,0) (1,1) (1,0) (2,2) (2,0) (2,1) (3,3) (3,2) (3,0) (3,1)
+__device__ __forceinline__ int pair_id(int b, int a) {
+  constexpr int base[4] = {0, 1, 3, 6};
+  if (a == b) return base[b];
+  if (b == 1) return 2;
+  if (b == 2) return a == 0 ? 4 : 5;
+  return a == 2 ? 7 : (a == 0 ? 8 : 9);
 }
 
-__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
-  hi = to_bf16(x);
-  lo = to_bf16(x - bf1(hi));
+// Keeps the scheduler from moving instructions across this point (it would
+// otherwise hoist every LDS fragment load of an unrolled loop to its top).
+__device__ __forceinline__ void fence_sched() { __builtin_amdgcn_sched_barrier(0); }
+
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses complete
+// (lgkmcnt 0), then s_barrier. Unlike __syncthreads() it does not wait for
+// outstanding global loads, so the next chunk's inputs stay in flight across
+// the chain's barriers. No global memory is shared between the waves.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// 8 fp32 -> bf16x8 hi and lo parts.
-__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
-  u32x4 h, l;
+// The value unchanged, but opaque to the compiler: lane-dependent addresses
+// derived from it are recomputed in each phase of each chunk instead of being
+// hoisted out of the chunk loop (hundreds of them would not fit in registers).
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Per-phase copies of the lane's indices (see fresh()).
+#define KDA_PHASE_IDS                                   \
+  const int ln_ = fresh(lane);                          \
+  const int n16 = ln_ & 15, g4 = ln_ >> 4;              \
+  const int tr = 16 * tb + n16, cb = 64 * hc + 8 * g4;  \
+  const int v = 16 * wave + n16;                        \
+  (void)n16; (void)g4; (void)tr; (void)cb; (void)v
+
+__device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_h(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// 8 fp32 -> bf16x8 (round to nearest even), and the hi + lo split.
+__device__ __forceinline__ u32x4 pack8(const float* x) {
+  return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+               pack_bf16x2(x[6], x[7])};
+}
+__device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    h[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
-    const float r0 = x[2 * e] - bf_lo(h[e]);
-    const float r1 = x[2 * e + 1] - bf_hi(h[e]);
-    l[e] = pack_bf16x2(r0, r1);
+    hi[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+    lo[e] = pack_bf16x2(x[2 * e] - bf_lo(hi[e]), x[2 * e + 1] - bf_hi(hi[e]));
   }
-  hi = __builtin_bit_cast(bf16x8, h);
-  lo = __builtin_bit_cast(bf16x8, l);
+}
+__device__ __forceinline__ void split4(const f32x4 x, u32x2& hi, u32x2& lo) {
+  hi[0] = pack_bf16x2(x[0], x[1]);
+  hi[1] = pack_bf16x2(x[2], x[3]);
+  lo[0] = pack_bf16x2(x[0] - bf_lo(hi[0]), x[1] - bf_hi(hi[0]));
+  lo[1] = pack_bf16x2(x[2] - bf_lo(hi[1]), x[3] - bf_hi(hi[1]));
 }
 
-__device__ __forceinline__ void split4(const f32x4 x, s16x4& hi, s16x4& lo) {
-  u32x2 h, l;
-  h[0] = pack_bf16x2(x[0], x[1]);
-  h[1] = pack_bf16x2(x[2], x[3]);
-  l[0] = pack_bf16x2(x[0] - bf_lo(h[0]), x[1] - bf_hi(h[0]));
-  l[1] = pack_bf16x2(x[2] - bf_lo(h[1]), x[3] - bf_hi(h[1]));
-  hi = __builtin_bit_cast(s16x4, h);
-  lo = __builtin_bit_cast(s16x4, l);
+// The same split in fp16 (11-bit halves: the residual is ~2^-22 of |x|, against
+// ~2^-16 for bf16), for operands whose magnitude the fp16 range holds: the
+// state update's k~ and the read-out's P (both at most 1 in magnitude) and U
+// (scaled by a power of two where a wave's tile would not fit).
+__device__ __forceinline__ void split8h(const float* x, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hi[e] = pack_f16x2(x[2 * e], x[2 * e + 1]);
+    lo[e] = pack_f16x2(x[2 * e] - f16_lo(hi[e]), x[2 * e + 1] - f16_hi(hi[e]));
+  }
+}
+__device__ __forceinline__ uint16_t to_f16(float x) {
+  return static_cast<uint16_t>(pack_f16x2(x, 0.0f) & 0xffffu);
 }
 
-// Two runs of 4 bf16 (8 bytes each, 8-byte aligned) as one 16-byte unit.
-__device__ __forceinline__ u32x4 lds_2runs(const uint16_t* p0, const uint16_t* p1) {
-  const u32x2 a = *reinterpret_cast<const u32x2*>(p0);
-  const u32x2 b = *reinterpret_cast<const u32x2*>(p1);
-  return u32x4{a[0], a[1], b[0], b[1]};
+template <int N>
+__device__ __forceinline__ float dpp_shr(float x) {  // row_shr:N, zero shifted in
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x110 + N, 0xF, 0xF, true));
 }
 
 template <bool VEC>
@@ -185,9 +219,6 @@ __device__ __forceinline__ u32x2 gload4(const uint16_t* p) {
     return u32x2{uint32_t(p[0]) | (uint32_t(p[1]) << 16), uint32_t(p[2]) | (uint32_t(p[3]) << 16)};
   }
 }
-
-// State rows leave in 32-byte pieces (16 rows per instruction): plain
-// stores, so that L2 merges the pieces of a row into whole lines.
 template <bool VEC>
 __device__ __forceinline__ void gstore4(uint16_t* p, u32x2 w) {
   if constexpr (VEC) {
@@ -201,7 +232,7 @@ __device__ __forceinline__ void gstore4(uint16_t* p, u32x2 w) {
 }
 
 // Four consecutive state elements (the 4 key channels of one accumulator
-// entry), in the state format SF: 8 bytes (bf16, fp16) or 4 bytes (fp8).
+// entry) in the state format SF.
 template <int SF, bool VEC>
 __device__ __forceinline__ f32x4 st4_load(const void* base, int64_t e) {
   if constexpr (SF == kStateFp8) {
@@ -218,489 +249,125 @@ __device__ __forceinline__ void st4_store(void* base, int64_t e, f32x4 a) {
   if constexpr (SF == kStateFp8) {
     *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(base) + e) = pack_f8x4(a[0], a[1], a[2], a[3]);
   } else {
-    gstore4<VEC>(static_cast<uint16_t*>(base) + e, u32x2{st_pack<SF>(a[0], a[1]), st_pack<SF>(a[2], a[3])});
+    gstore4<VEC>(static_cast<uint16_t*>(base) + e,
+                 u32x2{st_pack<SF>(a[0], a[1]), st_pack<SF>(a[2], a[3])});
   }
 }
 
-// Raw token inputs of one lane: 8 channels of q, k, g, v and the beta logit.
-struct TokRaw {
-  u32x4 q, k, g, v;
-  uint16_t b;
+// Raw token inputs of one lane (token-owner layout): two runs of eight
+// channels (cb + 32 s .. + 7) of q, k, g, v, and the beta bits.
+struct Raw {
+  u32x4 q[2], k[2], g[2], v[2];
+  uint32_t b;
 };
 
+// Token row tb + tr: tb is uniform (a chunk's first token), tr the lane's row;
+// two runs of 8 channels (16-byte loads on the vectorised path).
 template <bool VEC, bool GHEAD>
-__device__ __forceinline__ TokRaw load_tok(const PrefillParams& p, int64_t t, int h, int c0,
-                                           bool valid) {
-  TokRaw r;
+__device__ __forceinline__ void load_raw(const PrefillParams& p, int64_t tb, int tr, int h,
+                                         int cb, bool valid, Raw& r) {
   if (valid) {
-    r.q = load8_raw<VEC>(p.q + t * p.q_tok_stride + h * D + c0);
-    r.k = load8_raw<VEC>(p.k + t * p.k_tok_stride + h * D + c0);
-    if constexpr (GHEAD) {  // one gate value per head, in all eight channel slots
-      const uint32_t gh = p.g[t * p.g_tok_stride + h];
-      r.g = u32x4{gh | (gh << 16), gh | (gh << 16), gh | (gh << 16), gh | (gh << 16)};
-    } else {
-      r.g = load8_raw<VEC>(p.g + t * p.g_tok_stride + h * D + c0);
+    const int64_t t = tb + tr;
+    const uint16_t* q = p.q + tb * p.q_tok_stride + (int64_t(tr) * p.q_tok_stride + h * D + cb);
+    const uint16_t* k = p.k + tb * p.k_tok_stride + (int64_t(tr) * p.k_tok_stride + h * D + cb);
+    const uint16_t* v = p.v + tb * p.v_tok_stride + (int64_t(tr) * p.v_tok_stride + h * D + cb);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      r.q[s] = load8_bits<VEC>(q + 32 * s);
+      r.k[s] = load8_bits<VEC>(k + 32 * s);
+      r.v[s] = load8_bits<VEC>(v + 32 * s);
     }
-    r.v = load8_raw<VEC>(p.v + t * p.v_tok_stride + h * D + c0);
+    if constexpr (GHEAD) {
+      const uint32_t gh = p.g[t * p.g_tok_stride + h];
+      const uint32_t g2 = gh | (gh << 16);  // the value in both halves: all 16 channels
+#pragma unroll
+      for (int s = 0; s < 2; ++s) r.g[s] = u32x4{g2, g2, g2, g2};
+    } else {
+      const uint16_t* g = p.g + t * p.g_tok_stride + h * D + cb;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) r.g[s] = load8_bits<VEC>(g + 32 * s);
+    }
     r.b = p.beta[t * p.beta_tok_stride + h];
   } else {
-    r.q = r.k = r.g = r.v = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) r.q[s] = r.k[s] = r.g[s] = r.v[s] = u32x4{0u, 0u, 0u, 0u};
     r.b = 0;
   }
-  return r;
 }
 
-// First chunk slot of document i (i = n_docs gives the slot count).
-__device__ __forceinline__ int64_t doc_slot0(const int32_t* cu, int i) {
-  return int64_t(i) + (int64_t(cu[i]) >> 4);
-}
-
-// The document owning chunk slot sigma: the largest i in [0, n_docs] with
-// doc_slot0(i) <= sigma (doc_slot0 is strictly increasing and doc_slot0(0) = 0).
-// Every thread of the workgroup calls it; each step narrows the window
-// 256-fold with one load per thread.
-__device__ int find_doc(const int32_t* cu, int n_docs, int64_t sigma, int tid) {
-  int lo = 0;
-  int len = n_docs + 1;  // window [lo, lo + len), doc_slot0(lo) <= sigma
-  while (len > kThreads) {
-    const int stride = (len + kThreads - 1) / kThreads;
-    const int off = tid * stride;
-    const bool le = off < len && doc_slot0(cu, lo + off) <= sigma;
-    const int cnt = __syncthreads_count(le);
-    lo += (cnt - 1) * stride;
-    len = min(stride, n_docs + 1 - lo);
+__device__ __forceinline__ void unpack16(const u32x4 (&w)[2], float (&x)[16]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[8 * s + 2 * i] = bf_lo(w[s][i]);
+      x[8 * s + 2 * i + 1] = bf_hi(w[s][i]);
+    }
   }
-  const bool le = tid < len && doc_slot0(cu, lo + tid) <= sigma;
-  return lo + __syncthreads_count(le) - 1;
+}
+
+// 16 per-channel fp32 values of this lane's channels from an LDS array of 128.
+__device__ __forceinline__ void lds_ch16(const float* a, int cb, float (&x)[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(a + cb + 32 * (j >> 1) + 4 * (j & 1));
+    x[4 * j] = w[0];
+    x[4 * j + 1] = w[1];
+    x[4 * j + 2] = w[2];
+    x[4 * j + 3] = w[3];
+  }
+}
+__device__ __forceinline__ void lds_st16(float* a, int cb, const float (&x)[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<f32x4*>(a + cb + 32 * (j >> 1) + 4 * (j & 1)) =
+        f32x4{x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
 }
 
 }  // namespace
 
-// ---------------------------------------------------------------------------
-// Preparation: one 256-thread workgroup per (chunk slot, group of up to
-// kPrepHeads heads). Everything of the chunk that does not depend on the
-// state, written to the chunk record of each head; the next head's token
-// inputs are loaded while the current head is processed.
-constexpr int kPrepHeads = 4;
-
-// GK, the gate kind: kGatePrecomputed clear = raw gate logits, set = the
-// log-decay itself; kGatePerHead set = one gate value per head.
-template <bool VEC, int GK>
-__global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillParams p) {
+// SF: state element format of the pool and the checkpoints; GK: gate kind
+// (kGatePrecomputed / kGatePerHead bits).
+template <bool VEC, int GK, int SF>
+__global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOrder ord) {
   constexpr bool GRAW = !(GK & kGatePrecomputed);
   constexpr bool GHEAD = (GK & kGatePerHead) != 0;
-  extern __shared__ __align__(16) float psmem_raw[];
+  static_assert(VEC || SF == kStateBf16, "fp16 and fp8 states use the vectorised layout");
+  extern __shared__ __align__(16) uint8_t lds[];
+  float* NRM = reinterpret_cast<float*>(lds + L_NRM);
+  float* TAU = reinterpret_cast<float*>(lds + L_TAU);
+  float* CUT = reinterpret_cast<float*>(lds + L_CUT);
+  float* BETA = reinterpret_cast<float*>(lds + L_BETA);
+  float* EG = reinterpret_cast<float*>(lds + L_EG);
+  float* SEM = reinterpret_cast<float*>(lds + L_SEM);
+  float* SEO = reinterpret_cast<float*>(lds + L_SEO);
+  float* SPH = reinterpret_cast<float*>(lds + L_SPH);
+  float* SO = reinterpret_cast<float*>(lds + L_SO);
+  float* ST1 = reinterpret_cast<float*>(lds + L_ST1);
+  float* ST2 = reinterpret_cast<float*>(lds + L_ST2);
+  float* SGE = reinterpret_cast<float*>(lds + L_SGE);
+  float* TD = reinterpret_cast<float*>(lds + L_TD);
+  float* DTB = reinterpret_cast<float*>(lds + L_DTB);
+  float* DLT = reinterpret_cast<float*>(lds + L_DLT);
+  uint16_t* VR = reinterpret_cast<uint16_t*>(lds + L_VR);
+  uint8_t* QOP = lds + L_QOP;
+  uint16_t* PM = reinterpret_cast<uint16_t*>(lds + L_PM);
+  uint16_t* TP = reinterpret_cast<uint16_t*>(lds + L_TP);
+  uint16_t* KGR = reinterpret_cast<uint16_t*>(lds + L_X1);
+  float* AM = reinterpret_cast<float*>(lds + L_X1);
+  uint8_t* WOP = lds + L_X1;
+  uint16_t* KT = reinterpret_cast<uint16_t*>(lds + L_X1);
+  float* PART = reinterpret_cast<float*>(lds + L_X2);
+  uint16_t* XT = reinterpret_cast<uint16_t*>(lds + L_X2);
+  uint16_t* OST = reinterpret_cast<uint16_t*>(lds + L_X2);  // chunk outputs (after P5)
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int g4 = lane >> 4;
   const int n16 = lane & 15;
-  const int64_t sigma = blockIdx.x;
-  const int h0 = int(blockIdx.y) * kPrepHeads;
-  const int h1 = min(h0 + kPrepHeads, p.H);
-
-  const int doc = find_doc(p.cu_seqlens, p.n_docs, sigma, tid);
-  if (doc >= p.n_docs) return;
-  const int64_t t0 = p.cu_seqlens[doc];
-  const int64_t len = int64_t(p.cu_seqlens[doc + 1]) - t0;
-  const int64_t j = sigma - doc_slot0(p.cu_seqlens, doc);
-  if (j * C >= len) return;  // a slot between documents
-  const int32_t slot = p.state_indices[doc];
-  if (slot < 0 || int64_t(slot) >= p.num_slots) return;  // the chain writes zeros
-  const int64_t tc0 = t0 + j * C;
-  const int c = int(min<int64_t>(C, len - j * C));
-  PSmem s = pcarve(psmem_raw);
-
-  const int tt = tid >> 4;        // prologue: token of this lane
-  const int c0 = (tid & 15) * 8;  // prologue: 8 key / value channels of this lane
-  const bool valid = tt < c;
-  TokRaw raw = load_tok<VEC, GHEAD>(p, tc0 + tt, h0, c0, valid);
-
-  for (int h = h0; h < h1; ++h) {
-    // ---- token prologue -> q_hat, k_hat, g, v, beta (rows >= c are zeros)
-    {
-      const TokRaw cur = raw;
-      if (h + 1 < h1) raw = load_tok<VEC, GHEAD>(p, tc0 + tt, h + 1, c0, valid);
-      float neg_ea = 0.f;
-      float dtb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if constexpr (GRAW) {
-        neg_ea = -fexp(p.A_log[h]);
-        if constexpr (GHEAD) {
-          const float dh = p.dt_bias[h];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) dtb[e] = dh;
-        } else {
-          load8_f32<VEC>(p.dt_bias + h * D + c0, dtb);
-        }
-      }
-      float q[8], k[8], gr[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        q[2 * e] = bf_lo(cur.q[e]);  q[2 * e + 1] = bf_hi(cur.q[e]);
-        k[2 * e] = bf_lo(cur.k[e]);  k[2 * e + 1] = bf_hi(cur.k[e]);
-        gr[2 * e] = bf_lo(cur.g[e]); gr[2 * e + 1] = bf_hi(cur.g[e]);
-      }
-      float sq = 0.f, sk = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sq = fmaf(q[e], q[e], sq);
-        sk = fmaf(k[e], k[e], sk);
-      }
-      sq = row16_sum(sq);
-      sk = row16_sum(sk);
-      const float rq = 1.0f / sqrtf(sq + 1e-6f);
-      const float rk = 1.0f / sqrtf(sk + 1e-6f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        s.qh[tt * RS + c0 + e] = q[e] * rq;
-        s.kh[tt * RS + c0 + e] = k[e] * rk;
-        const float ge = GRAW ? fgate(gr[e] + dtb[e], neg_ea, p.lower_bound)
-                              : gate_given(gr[e], p.lower_bound);
-        s.gg[tt * RS + c0 + e] = valid ? ge : 0.f;
-      }
-      *reinterpret_cast<u32x4*>(s.vv + tt * VLD + c0) = cur.v;
-      if ((tid & 15) == 0) {
-        const float braw = bf1(cur.b);
-        const float be = (p.gate_mode & kBetaPresigmoid) ? braw : fsigmoid(braw);
-        s.beta[tt] = valid ? be : 0.f;
-      }
-    }
-    __syncthreads();
-
-    // ---- thread (c, half) owns key channel c = tid % 128 and tokens
-    // 8 half .. 8 half + 7: Gam prefix (every thread sums all 16 gates of its
-    // channel), the scaled rows for A and P as bf16 hi / lo pairs (MFMA
-    // operands, written over the fp32 rows they come from: hi in the first
-    // 128 bf16 of a row, lo in the next 128), the fp32 right-hand side of W,
-    // and the chain's bf16 operands exp(Gam) q_hat and exp(Gam_last - Gam) k_hat.
-    {
-      const int cc = tid & 127;
-      const int r0 = (tid >> 7) * 8;
-      float gam[C];
-      float acc_g = 0.f;
-#pragma unroll
-      for (int r = 0; r < C; ++r) {
-        acc_g += s.gg[r * RS + cc];
-        gam[r] = acc_g;
-      }
-      const float mid = 0.5f * acc_g;  // padded rows carry g = 0
-      const float em = fexp(mid);
-      float kq[8], qq[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        kq[i] = s.kh[(r0 + i) * RS + cc];
-        qq[i] = s.qh[(r0 + i) * RS + cc];
-      }
-      __syncthreads();  // every fp32 row and every gate is read before any is rewritten
-      if (r0 == 0) {
-        s.egl[cc] = fexp(acc_g);
-        s.em[cc] = em;
-      }
-      uint16_t* khp = reinterpret_cast<uint16_t*>(s.kh);
-      uint16_t* qhp = reinterpret_cast<uint16_t*>(s.qh);
-      uint16_t* kbp = reinterpret_cast<uint16_t*>(s.kb);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = r0 + i;
-        const float g_first = gam[i], g_second = gam[8 + i];  // both loaded: a select of
-        const float gr_ = r0 == 0 ? g_first : g_second;         // values, not of addresses
-        const float ea = fexp(gr_ - mid), eb = fexp(mid - gr_);
-        const float kb = kq[i] * eb;
-        uint16_t hi, lo;
-        split_bf16(qq[i] * ea, hi, lo);
-        qhp[r * 2 * RS + cc] = hi;
-        qhp[r * 2 * RS + D + cc] = lo;
-        s.kw[r * RS + cc] = kq[i] * ea;
-        split_bf16(kq[i] * ea, hi, lo);
-        khp[r * 2 * RS + cc] = hi;
-        khp[r * 2 * RS + D + cc] = lo;
-        split_bf16(kb, hi, lo);
-        kbp[r * 2 * RS + cc] = hi;
-        kbp[r * 2 * RS + D + cc] = lo;
-        s.qop[r * QLD + cc] = to_bf16(qq[i] * ea * em);
-        split_bf16(em * kb, hi, lo);  // exp(Gam_last - m) = exp(m)
-        s.ktop[r * D + cc] = hi;
-        s.ktop[C * D + r * D + cc] = lo;
-      }
-    }
-    __syncthreads();
-
-    // ---- A = (e^(Gam-m) k)(e^(m-Gam) k)^T on wave 0, P = (e^(Gam-m) q)(e^(m-Gam) k)^T on
-    // wave 1 (three hi/lo terms each, fragments read straight from the bf16
-    // pairs; one accumulator per term so the products do not wait on each other).
-    if (wave < 2) {
-      const uint16_t* left = reinterpret_cast<const uint16_t*>(wave == 0 ? s.kh : s.qh);
-      const uint16_t* right = reinterpret_cast<const uint16_t*>(s.kb);
-      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int off = n16 * 2 * RS + 32 * kt + 8 * g4;
-        const bf16x8 xh = *reinterpret_cast<const bf16x8*>(left + off);
-        const bf16x8 xl = *reinterpret_cast<const bf16x8*>(left + off + D);
-        const bf16x8 yh = *reinterpret_cast<const bf16x8*>(right + off);
-        const bf16x8 yl = *reinterpret_cast<const bf16x8*>(right + off + D);
-        a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yh, a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yl, a1, 0, 0, 0);
-        a2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, yh, a2, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g4 + i, jj = n16;
-        const float a = a0[i] + (a1[i] + a2[i]);
-        if (wave == 0) s.am[r * C + jj] = jj < r ? a : 0.f;
-        else s.pop[r * C + jj] = to_bf16(jj <= r ? a : 0.f);
-      }
-    }
-    __syncthreads();
-
-    // ---- forward substitution. Threads 0..127: W (key channel c), stored as
-    // bf16 hi / lo; threads 128..255: U0 (value channel v).
-    {
-      const int cc = tid & 127;
-      // Right-looking: once x_j is known it is taken off every later row's
-      // remainder; each row still accumulates its terms in the order j = 0, 1, ...
-      float x[C];
-      if (tid < 128) {
-#pragma unroll
-        for (int r = 0; r < C; ++r) x[r] = s.kw[r * RS + cc];
-      } else {
-#pragma unroll
-        for (int r = 0; r < C; ++r) x[r] = bf1(s.vv[r * VLD + cc]);
-      }
-#pragma unroll
-      for (int jj = 0; jj < C; ++jj) {
-        x[jj] *= s.beta[jj];
-#pragma unroll
-        for (int r = jj + 1; r < C; ++r) x[r] = fmaf(-s.am[r * C + jj], x[jj], x[r]);
-      }
-      if (tid < 128) {
-        const float em = s.em[cc];
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-          uint16_t hi, lo;
-          split_bf16(x[r] * em, hi, lo);
-          s.wop[r * XLD + cc] = hi;
-          s.wop[C * XLD + r * XLD + cc] = lo;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < C; ++r) s.u0[r * RS + cc] = x[r];
-      }
-    }
-    __syncthreads();
-
-    // ---- the chunk record, one 16-byte unit per thread and round
-    u32x4* rec = reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.workspace) +
-                                          (sigma * p.H + h) * int64_t(kRecBytes));
-#pragma unroll
-    for (int rd = 0; rd < kRecRounds; ++rd) {
-      const int u = tid + kThreads * rd;
-      u32x4 w;
-      if (u < kRecQ / 16) {  // W
-        const int kt = u >> 7, part = (u >> 6) & 1, l = u & 63;
-        const uint16_t* row = s.wop + part * C * XLD + (l & 15) * XLD + 32 * kt + 4 * (l >> 4);
-        w = lds_2runs(row, row + 16);
-      } else if (u < kRecKT / 16) {  // Q
-        const int kt = (u - kRecQ / 16) >> 6, l = u & 63;
-        const uint16_t* row = s.qop + (l & 15) * QLD + 32 * kt + 4 * (l >> 4);
-        w = lds_2runs(row, row + 16);
-      } else if (u < kRecU0 / 16) {  // KT: tokens 4g4 .. 4g4+3 of key channel 16mt + n16
-        const int mt = (u - kRecKT / 16) >> 6, l = u & 63;
-        const uint16_t* col = s.ktop + 4 * (l >> 4) * D + 16 * mt + (l & 15);
-#pragma unroll
-        for (int part = 0; part < 2; ++part) {
-          const uint16_t* cp = col + part * C * D;
-          w[2 * part] = uint32_t(cp[0]) | (uint32_t(cp[D]) << 16);
-          w[2 * part + 1] = uint32_t(cp[2 * D]) | (uint32_t(cp[3 * D]) << 16);
-        }
-      } else if (u < kRecP / 16) {  // U0
-        const int vt = (u - kRecU0 / 16) >> 6, l = u & 63;
-        const float* col = s.u0 + 4 * (l >> 4) * RS + 16 * vt + (l & 15);
-        w = u32x4{__float_as_uint(col[0]), __float_as_uint(col[RS]),
-                  __float_as_uint(col[2 * RS]), __float_as_uint(col[3 * RS])};
-      } else if (u < kRecEG / 16) {  // P: lanes 2q and 2q+1
-        const int l0 = 2 * (u - kRecP / 16);
-        w = lds_2runs(s.pop + (l0 & 15) * C + 4 * (l0 >> 4),
-                      s.pop + ((l0 + 1) & 15) * C + 4 * ((l0 + 1) >> 4));
-      } else if (u < kRecUnits) {  // EG
-        w = *reinterpret_cast<const u32x4*>(s.egl + 4 * (u - kRecEG / 16));
-      } else {
-        continue;
-      }
-      rec[u] = w;
-    }
-    __syncthreads();  // the record is read out before the next head rewrites the arrays
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Hand-off to the verify ring: one 256-thread workgroup per (document, head),
-// run between the preparation and the chain when ring_tail > 0. In a
-// document's last chunk (c tokens, of which the last `tail` are handed off,
-// pe = c - tail) only tokens 0 .. pe-1 may enter the state the chain passes
-// on, so this kernel rewrites that chunk record's state-update operands,
-//   K~_r = exp(Gam_e - Gam_r) k_hat_r (r < pe, else 0),  EG = exp(Gam_e),
-// with Gam_e = Gam_{pe-1} (0 when pe = 0), and writes the tail tokens' ring
-// rows: k_hat (bf16) and G, the log-decay summed from the first tail token.
-// The chain then leaves S after pe tokens, and writes the tail's u rows.
-// k_hat and the gate are computed as the preparation computes them.
-template <bool VEC, int GK>
-__global__ __launch_bounds__(kThreads) void handoff_kernel(PrefillParams p) {
-  constexpr bool GRAW = !(GK & kGatePrecomputed);
-  constexpr bool GHEAD = (GK & kGatePerHead) != 0;
-  __shared__ float kh[C][D];
-  __shared__ float gg[C][D];
-  const int tid = threadIdx.x;
-  const int doc = blockIdx.x;
-  const int h = blockIdx.y;
-  const int64_t t0 = p.cu_seqlens[doc];
-  const int64_t len = int64_t(p.cu_seqlens[doc + 1]) - t0;
-  const int32_t slot = p.state_indices[doc];
-  const int32_t rbase = p.cache_base[doc];
-  if (len == 0 || slot < 0 || int64_t(slot) >= p.num_slots || rbase < 0 ||
-      rbase >= p.ring_rows)
-    return;  // nothing to hand off, or an inactive document
-  const int nchunks = int((len + C - 1) / C);
-  const int c = int(len - int64_t(nchunks - 1) * C);
-  const int tail = min(p.ring_tail, c);
-  const int pe = c - tail;
-
-  // ---- k_hat and g of the chunk's tokens (rows >= c: zeros)
-  {
-    const int tt = tid >> 4;
-    const int c0 = (tid & 15) * 8;
-    const bool valid = tt < c;
-    const TokRaw raw =
-        load_tok<VEC, GHEAD>(p, t0 + int64_t(nchunks - 1) * C + tt, h, c0, valid);
-    float neg_ea = 0.f;
-    float dtb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if constexpr (GRAW) {
-      neg_ea = -fexp(p.A_log[h]);
-      if constexpr (GHEAD) {
-        const float dh = p.dt_bias[h];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dtb[e] = dh;
-      } else {
-        load8_f32<VEC>(p.dt_bias + h * D + c0, dtb);
-      }
-    }
-    float k[8], gr[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      k[2 * e] = bf_lo(raw.k[e]);  k[2 * e + 1] = bf_hi(raw.k[e]);
-      gr[2 * e] = bf_lo(raw.g[e]); gr[2 * e + 1] = bf_hi(raw.g[e]);
-    }
-    float sk = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sk = fmaf(k[e], k[e], sk);
-    sk = row16_sum(sk);
-    const float rk = 1.0f / sqrtf(sk + 1e-6f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kh[tt][c0 + e] = k[e] * rk;
-      const float ge = GRAW ? fgate(gr[e] + dtb[e], neg_ea, p.lower_bound)
-                            : gate_given(gr[e], p.lower_bound);
-      gg[tt][c0 + e] = valid ? ge : 0.f;
-    }
-  }
-  __syncthreads();
-  if (tid >= D) return;
-
-  // ---- thread cc: one key channel
-  const int cc = tid;
-  float gam_e = 0.f, acc = 0.f;
-  for (int r = 0; r < pe; ++r) {
-    acc += gg[r][cc];
-    gam_e = acc;
-  }
-  uint8_t* rec = static_cast<uint8_t*>(p.workspace) +
-                 ((doc_slot0(p.cu_seqlens, doc) + nchunks - 1) * p.H + h) * int64_t(kRecBytes);
-  // KT unit (mt, lane = n16 + 16 g4): tokens 4 g4 .. 4 g4 + 3 of key channel
-  // 16 mt + n16, four bf16 hi then four bf16 lo
-  const int mt = cc >> 4, n16 = cc & 15;
-  float gam = 0.f;
-#pragma unroll
-  for (int g4 = 0; g4 < 4; ++g4) {
-    uint16_t hi[4], lo[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g4 + i;
-      gam += gg[r][cc];
-      const float x = r < pe ? fexp(gam_e - gam) * kh[r][cc] : 0.f;
-      split_bf16(x, hi[i], lo[i]);
-    }
-    const u32x4 w = {uint32_t(hi[0]) | (uint32_t(hi[1]) << 16),
-                     uint32_t(hi[2]) | (uint32_t(hi[3]) << 16),
-                     uint32_t(lo[0]) | (uint32_t(lo[1]) << 16),
-                     uint32_t(lo[2]) | (uint32_t(lo[3]) << 16)};
-    *reinterpret_cast<u32x4*>(rec + kRecKT + (mt * 64 + n16 + 16 * g4) * 16) = w;
-  }
-  reinterpret_cast<float*>(rec + kRecEG)[cc] = fexp(gam_e);
-
-  // ---- ring rows of the tail tokens
-  const int64_t ring0 = (int64_t(slot) * p.H + h) * p.ring_rows;
-  float gt = 0.f;
-  for (int r = pe; r < c; ++r) {
-    gt += gg[r][cc];
-    const int64_t row = ring0 + (rbase + r - pe) % p.ring_rows;
-    p.k_cache[row * D + cc] = to_bf16(kh[r][cc]);
-    p.g_cache[row * D + cc] = gt;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Chain: one 512-thread workgroup per (document, head), documents longest
-// first. Wave w keeps value channels 16w .. 16w+15 of the fp32 state in
-// registers (two waves per SIMD, so one wave's MFMA and LDS latencies overlap
-// the other's arithmetic). Chunk records move HBM -> registers one chunk
-// ahead of use and registers -> LDS (double buffer) one chunk ahead, so a
-// chunk's operands are in LDS when it starts and the next record's loads
-// overlap its arithmetic.
-//
-// With few chains (documents x heads below the CU count) each chain is split
-// by value channels over VS = 2 workgroups of 4 waves on different CUs: the
-// value channels of the state evolve independently, and a CU then holds one
-// wave per SIMD instead of two, so a chunk's VALU and MFMA issue per SIMD
-// halves. Each part stages the record's shared operands (W, Q, K~, P,
-// exp(Gam_c)) and only its own U0 tiles.
-template <int VS>
-struct ChainShape {
-  static constexpr int kThreads = 512 / VS;
-  static constexpr int kWaves = 8 / VS;                     // value tiles of 16 channels
-  static constexpr int kShared = kRecU0 / 16;               // W, Q, K~ units
-  static constexpr int kOwnU0 = kWaves * 64;                // this part's U0 units
-  static constexpr int kTail = kRecUnits - kRecP / 16;      // P, exp(Gam_c) units
-  static constexpr int kUnits = kShared + kOwnU0 + kTail;   // units staged per chunk
-  static constexpr int kRounds = (kUnits + kThreads - 1) / kThreads;
-  static_assert(kUnits > (kRounds - 1) * kThreads, "every round has work");
-  // record unit of staged unit i (< kUnits) of part `part`
-  __device__ static int unit(int i, int part) {
-    if (i < kShared) return i;
-    if (i < kShared + kOwnU0) return kRecU0 / 16 + part * kOwnU0 + (i - kShared);
-    return kRecP / 16 + (i - kShared - kOwnU0);
-  }
-};
-static_assert(ChainShape<1>::kUnits == kRecUnits, "the whole record");
-
-// SF: the element format of the pool (initial and final states) and the
-// checkpoints (kStateBf16, kStateFp16, kStateFp8). VS: workgroups per chain.
-template <bool VEC, int SF, int VS>
-__global__ __launch_bounds__(ChainShape<VS>::kThreads) void chain_kernel(PrefillParams p,
-                                                                        DocOrder ord) {
-  using Shape = ChainShape<VS>;
-  constexpr int kChainThreads = Shape::kThreads;
-  constexpr int kChainRounds = Shape::kRounds;
-  __shared__ __align__(16) uint8_t rbuf[2][kRecBytes];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int g4 = lane >> 4;
-  const int n16 = lane & 15;
-  const int part = int(blockIdx.x % VS);
-  const int vt = part * Shape::kWaves + wave;  // value tile of this wave
-  const int v = 16 * vt + n16;                 // value channel of this lane
-  const int h = int((blockIdx.x / VS) % p.H);
-  const int rank = int(blockIdx.x / VS / p.H);
+  const int h = int(blockIdx.x % p.H);
+  const int rank = int(blockIdx.x / p.H);
   const int doc = ord.n > 0 ? ord.doc[rank] : rank;
   const int64_t t0 = p.cu_seqlens[doc];
   const int64_t len = int64_t(p.cu_seqlens[doc + 1]) - t0;
@@ -708,195 +375,760 @@ __global__ __launch_bounds__(ChainShape<VS>::kThreads) void chain_kernel(Prefill
   const int32_t rbase = p.ring_tail > 0 ? p.cache_base[doc] : 0;
   const bool active = slot >= 0 && int64_t(slot) < p.num_slots && rbase >= 0 &&
                       (p.ring_tail == 0 || rbase < p.ring_rows);
-
-  constexpr int kPartCh = D / VS;  // value channels (state rows) of this part
   if (!active) {  // zero outputs, no state access
-    for (int64_t e = tid; e < len * kPartCh; e += kChainThreads)
-      p.out[(t0 + e / kPartCh) * p.out_tok_stride + h * D + part * kPartCh + (e % kPartCh)] = 0;
+    for (int64_t e = tid; e < len * D; e += NTHR)
+      p.out[(t0 + e / D) * p.out_tok_stride + h * D + (e % D)] = 0;
     return;
   }
-  static_assert(VEC || SF == kStateBf16, "fp16 and fp8 states use the vectorised layout");
   const int64_t se = int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS;  // element offset
   if (len == 0) {  // final state = initial state: untouched, or zeros without one
-    if (!p.use_initial_state) {  // this part's state rows
-      uint16_t* z = reinterpret_cast<uint16_t*>(
-          static_cast<uint8_t*>(p.state_pool) + (se + part * kPartCh * D) * kStateBytes<SF>);
-      for (int e = tid; e < kPartCh * D * kStateBytes<SF> / 2; e += kChainThreads) z[e] = 0;
+    if (!p.use_initial_state) {
+      uint16_t* z = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(p.state_pool) +
+                                                se * kStateBytes<SF>);
+      for (int e = tid; e < HEAD_ELEMS * kStateBytes<SF> / 2; e += NTHR) z[e] = 0;
     }
     return;
   }
 
-  const int nchunks = int((len + C - 1) / C);
-  // hand-off: the last chunk's last `tail` tokens go to the ring; the state
-  // passed on (checkpoints, final) covers the first `kept` tokens
-  const int c_last = int(len - int64_t(nchunks - 1) * C);
-  const int tail = p.ring_tail > 0 ? min(p.ring_tail, c_last) : 0;
+  // hand-off: the last `tail` tokens go to the ring; the state passed on
+  // (checkpoints, final) covers the first `kept` tokens
+  const int c_last16 = int(len - 16 * ((len - 1) / 16));
+  const int tail = p.ring_tail > 0 ? min(p.ring_tail, c_last16) : 0;
   const int64_t kept = len - tail;
-  const int64_t sigma0 = doc_slot0(p.cu_seqlens, doc);
-  // first checkpoint row of this document (checkpoints after every
-  // ckpt_interval tokens, a multiple of the chunk)
   const int64_t ckpt_row0 = p.ckpt ? p.ckpt_starts[doc] : 0;
-  const int ckpt_every = p.ckpt_interval / C;
-  const uint8_t* ws = static_cast<const uint8_t*>(p.workspace);
-  auto rec_of = [&](int ch) {
-    return reinterpret_cast<const u32x4*>(ws + ((sigma0 + ch) * p.H + h) * int64_t(kRecBytes));
-  };
-  // Thread tid moves staged units tid + kChainThreads rd (to the record's
-  // own offsets in LDS); the units past the staged set in the last round load
-  // a staged unit again (a fixed load count per chunk) and are not stored.
-  u32x4 pre[kChainRounds];
-  auto load_rec = [&](int ch) {
-    const u32x4* r = rec_of(ch);
-#pragma unroll
-    for (int rd = 0; rd < kChainRounds; ++rd) {
-      const int i = tid + kChainThreads * rd;
-      pre[rd] = __builtin_nontemporal_load(
-          r + Shape::unit(i < Shape::kUnits ? i : i - Shape::kUnits, part));
-    }
-  };
-  auto store_rec = [&](int b) {
-    u32x4* d = reinterpret_cast<u32x4*>(&rbuf[b][0]);
-#pragma unroll
-    for (int rd = 0; rd < kChainRounds; ++rd) {
-      const int i = tid + kChainThreads * rd;
-      if (rd < kChainRounds - 1 || i < Shape::kUnits) d[Shape::unit(i, part)] = pre[rd];
-    }
-  };
+  const int ivl = p.ckpt ? p.ckpt_interval : 0;
+  const int64_t ring0 = (int64_t(slot) * p.H + h) * int64_t(p.ring_rows);
 
-  load_rec(0);
+  // token-owner identity
+  const int tb = wave >> 1, hc = wave & 1;
+  const int tr = 16 * tb + n16;        // token of this lane within the chunk
+  const int cb = 64 * hc + 8 * g4;     // first channel of the lane's two runs of 8
+  // chain identity: value channel of this lane
+  const int v = 16 * wave + n16;
 
-  // ---- initial state into the accumulator layout (all 8 loads issued
-  // before any is waited for)
+  // T' and P above their block diagonal: the blocks a chunk's products read
+  // that are always zero ((0,1) and (2,3)); nothing else writes them.
+  for (int e = tid; e < 2 * 256; e += NTHR) {
+    const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;
+    const int row = 32 * blk + r, col = 32 * blk + 16 + cc;
+    TP[row * TRS + col] = 0;
+    TP[CH * TRS + row * TRS + col] = 0;
+    PM[row * TRS + col] = 0;
+  }
+
+  // ---- initial state in the accumulator layout
   f32x4 acc[8];
   if (p.use_initial_state) {
-    if constexpr (SF == kStateFp8) {
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-        acc[mt] = st4_load<SF, VEC>(p.state_pool, se + v * D + 16 * mt + 4 * g4);
-    } else {
-      const uint16_t* sp = static_cast<const uint16_t*>(p.state_pool) + se;
-      u32x2 w[8];
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) w[mt] = gload4<VEC>(sp + v * D + 16 * mt + 4 * g4);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-        acc[mt] = f32x4{st_lo<SF>(w[mt][0]), st_hi<SF>(w[mt][0]), st_lo<SF>(w[mt][1]),
-                        st_hi<SF>(w[mt][1])};
-    }
+    for (int m = 0; m < 8; ++m)
+      acc[m] = st4_load<SF, VEC>(p.state_pool, se + int64_t(v) * D + 16 * m + 4 * g4);
   } else {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 8; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  store_rec(0);
-  load_rec(min(1, nchunks - 1));
+
+  const int len32 = int(len);  // cu_seqlens is int32: a document holds < 2^31 tokens
+  auto chunk_len = [&](int pos) {
+    int c = min(CH, len32 - pos);
+    if (ivl) c = min(c, ivl - pos % ivl);
+    return c;
+  };
+  Raw raw;
+  {
+    const int c0 = chunk_len(0);
+    load_raw<VEC, GHEAD>(p, t0, tr, h, cb, tr < c0, raw);
+  }
+  const float neg_ea = GRAW ? -fexp(p.A_log[h]) : 0.f;
+  if constexpr (GRAW) {  // the head's dt_bias, read by every chunk's prologue
+    if (tid < D) DTB[tid] = GHEAD ? p.dt_bias[h] : p.dt_bias[h * D + tid];
+  }
   __syncthreads();
+  const bool presig = (p.gate_mode & kBetaPresigmoid) != 0;
 
-  const int ots32 = static_cast<int>(p.out_tok_stride);  // host-checked to fit a buffer range
-  f32x4 u_last = {0.f, 0.f, 0.f, 0.f};  // U of the last chunk (rows 4 g4 + i)
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int64_t tc0 = t0 + int64_t(ch) * C;
-    const int c = int(min<int64_t>(C, len - int64_t(ch) * C));
-    const uint8_t* R = &rbuf[ch & 1][0];
+  for (int pos = 0; pos < len32;) {
+    const int c = chunk_len(pos);
+    const bool last = pos + c == len32;
+    const int pe = last ? c - tail : c;  // tokens of this chunk that enter the state
+    const bool cut = pe < c;
+    const bool valid = tr < c;
 
-    // Output rows of this chunk as a buffer range of exactly c rows: a store
-    // to a padded row (r >= c) is out of range and discarded, so the number
-    // of store instructions does not depend on c.
-    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-        p.out + tc0 * p.out_tok_stride + h * D, 0,
-        static_cast<int>(((c - 1) * p.out_tok_stride + D) * 2), kBufferWord3);
-    // W S^T in three hi/lo terms (one accumulator each, so the products do
-    // not wait on each other) and (e^Gam q) S^T in one
-    f32x4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = y0, y2 = y0, yq = y0;
+    // ================= P1: token prologue (token-owner layout)
+    float qf[16], kf[16], lam[16];
+    {
+      KDA_PHASE_IDS;
+      float gr[16], dtb[16];
+      if constexpr (GRAW) lds_ch16(DTB, cb, dtb);
+      unpack16(raw.q, qf);
+      unpack16(raw.k, kf);
+      unpack16(raw.g, gr);
+      float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const bf16x8 whi = *reinterpret_cast<const bf16x8*>(R + kRecW + ((2 * kt) * 64 + lane) * 16);
-      const bf16x8 wlo =
-          *reinterpret_cast<const bf16x8*>(R + kRecW + ((2 * kt + 1) * 64 + lane) * 16);
-      const bf16x8 qhi = *reinterpret_cast<const bf16x8*>(R + kRecQ + (kt * 64 + lane) * 16);
-      const f32x4 s0 = acc[2 * kt], s1 = acc[2 * kt + 1];
-      const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-      bf16x8 shi, slo;
-      split8(sv, shi, slo);
-      y0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, shi, y0, 0, 0, 0);
-      y1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, slo, y1, 0, 0, 0);
-      y2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, shi, y2, 0, 0, 0);
-      yq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi, shi, yq, 0, 0, 0);
-    }
-    // U = U0 - W S^T (accumulator layout: rows 4*g4 + i, value channel of the lane)
-    const f32x4 u0 = *reinterpret_cast<const f32x4*>(R + kRecU0 + (vt * 64 + lane) * 16);
-    const f32x4 uf = u0 - (y0 + (y1 + y2));
-    s16x4 uhi, ulo;
-    split4(uf, uhi, ulo);
-    u_last = uf;
-    // O = scale ((e^Gam q) S^T + P U); rows r >= c fall outside the buffer
-    // range and are dropped by the store itself
-    const s16x4 pfr = *reinterpret_cast<const s16x4*>(R + kRecP + lane * 8);
-    const f32x4 o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pfr, uhi, yq, 0, 0, 0);
+      for (int e = 0; e < 16; ++e) {
+        sq = fmaf(qf[e], qf[e], sq);
+        sk = fmaf(kf[e], kf[e], sk);
+      }
+      sq += __shfl_xor(sq, 16);
+      sq += __shfl_xor(sq, 32);
+      sk += __shfl_xor(sk, 16);
+      sk += __shfl_xor(sk, 32);
+      if (g4 == 0) {
+        NRM[(hc * CH + tr) * 2] = sq;
+        NRM[(hc * CH + tr) * 2 + 1] = sk;
+      }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g4 + i;
-      __builtin_amdgcn_raw_buffer_store_b16(to_bf16(p.scale * o[i]), orsrc, (r * ots32 + v) * 2,
-                                            0, kStoreNontemporal);
-    }
-    // S = S diag(e^Gam_last) + U^T K~  (contraction over the chunk's tokens)
+      for (int e = 0; e < 16; ++e) {
+        float ge;
+        if constexpr (GRAW) ge = fgate(gr[e] + dtb[e], neg_ea, p.lower_bound);
+        else ge = gate_given(gr[e], p.lower_bound);
+        ge = valid ? ge : 0.f;
+        // inclusive prefix over the 16 tokens of the block (one DPP row)
+        ge += dpp_shr<1>(ge);
+        ge += dpp_shr<2>(ge);
+        ge += dpp_shr<4>(ge);
+        ge += dpp_shr<8>(ge);
+        lam[e] = ge;
+      }
+      if (n16 == 15) lds_st16(TAU + tb * D, cb, lam);
+      if (cut && pe > 0 && tr == pe - 1) lds_st16(CUT, cb, lam);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const u32x4 kk = *reinterpret_cast<const u32x4*>(R + kRecKT + (mt * 64 + lane) * 16);
-      const s16x4 khi = __builtin_bit_cast(s16x4, u32x2{kk[0], kk[1]});
-      const s16x4 klo = __builtin_bit_cast(s16x4, u32x2{kk[2], kk[3]});
-      const f32x4 e4 = *reinterpret_cast<const f32x4*>(R + kRecEG + (16 * mt + 4 * g4) * 4);
-      f32x4 a = acc[mt] * e4;
-      a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(khi, uhi, a, 0, 0, 0);
-      a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(khi, ulo, a, 0, 0, 0);
-      a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(klo, uhi, a, 0, 0, 0);
-      acc[mt] = a;
+      for (int s = 0; s < 2; ++s)
+        *reinterpret_cast<u32x4*>(VR + tr * VRS + cb + 32 * s) = raw.v[s];
+      if (hc == 0 && g4 == 0) {
+        const float braw = bf1(uint16_t(raw.b));
+        const float bt = valid ? (presig ? braw : fsigmoid(braw)) : 0.f;
+        BETA[tr] = bt;
+        // what the bf16 hi + lo pair of T'[t][t] = beta_t leaves out; U0 adds
+        // (this residual) v_t, the largest term of its split error
+        const uint16_t bh = to_bf16(bt);
+        const float br = bt - bf1(bh);
+        DLT[tr] = br - bf1(to_bf16(br));
+      }
     }
-    // record ch+1 (its loads were issued a chunk ago) into the other buffer,
-    // last read before the previous barrier; then the loads of record ch+2
-    store_rec((ch + 1) & 1);
-    load_rec(min(ch + 2, nchunks - 1));
-    // intermediate checkpoint after this chunk, after the record loads
-    if (p.ckpt && (ch + 1) % ckpt_every == 0 && int64_t(ch + 1) * C <= kept) {
-      const int64_t row = ckpt_row0 + (ch + 1) / ckpt_every - 1;
+    lds_barrier();  // b1
+
+    // ================= P1.5: per (block, channel) scalars
+    {
+      const int tid_ = fresh(tid);
+      const int bb = tid_ >> 7, cc = tid_ & 127;
+      const float t0_ = TAU[cc], t1_ = TAU[D + cc], t2_ = TAU[2 * D + cc], t3_ = TAU[3 * D + cc];
+      const float tau[4] = {t0_, t1_, t2_, t3_};
+      float o = 0.f;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        if (a < bb) o += tau[a];
+      const float tbb = tau[bb];
+      const float glast = ((t0_ + t1_) + t2_) + t3_;
+      float gend = glast;
+      if (cut) {
+        if (pe == 0) {
+          gend = 0.f;
+        } else {
+          const int bc = (pe - 1) >> 4;
+          float oc = 0.f;
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            if (a < bc) oc += tau[a];
+          gend = oc + CUT[cc];
+        }
+      }
+      SEM[bb * D + cc] = fexp(0.5f * tbb);
+      SEO[bb * D + cc] = fexp(o);
+      SPH[bb * D + cc] = fexp(gend - o - tbb);
+      SO[bb * D + cc] = o;
+      if (bb == 0) {
+        EG[cc] = fexp(gend);
+        ST1[cc] = fexp(t1_);
+        ST2[cc] = fexp(t2_);
+        SGE[cc] = gend;
+      }
+    }
+    lds_barrier();  // b1.5
+
+    // ================= P2: operands (token-owner layout), one slice of 8 channels
+    // at a time; diagonal blocks of A and P from the wave's own registers
+    u32x4 kFh[2], kFl[2], qFh[2], qFl[2];     // left operands of the off-diagonal pairs
+    u32x4 kF2h[2], kF2l[2], qF2h[2], qF2l[2];  // block 3 towards blocks 0 and 1 (reference o_2)
+    u32x4 xh[2], xl[2];               // exp(Gam) k_hat, for W
+    u32x4 kth[2], ktl[2];             // exp(Gam_e - Gam) k_hat (fp16), for the state update
+    f32x4 accA[4], accP[4];           // this wave's partial sums of its pairs
+    {
+      KDA_PHASE_IDS;
+      const float rq = 1.0f / sqrtf(NRM[tr * 2] + NRM[(CH + tr) * 2] + 1e-6f);
+      const float rk = 1.0f / sqrtf(NRM[tr * 2 + 1] + NRM[(CH + tr) * 2 + 1] + 1e-6f);
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) accA[i] = accP[i] = z;
+      f32x4 a0 = z, a1 = z, a2 = z, pp = z;  // diagonal block (tb, tb)
+      const bool ring_row = cut && tr >= pe && tr < c;
+      // ring row (rbase + tr - pe) mod R: rbase < R and tr - pe < tail <= R
+      int rr = rbase + tr - pe;
+      rr = rr >= p.ring_rows ? rr - p.ring_rows : rr;
+      const int64_t rrow = ring0 + rr;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        // per-channel scalars of this slice: runs (s, 0) and (s, 1)
+        float tau[8], em[8], eo[8], ph[8];
+        auto ch8 = [&](const float* a, float (&x)[8]) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const f32x4 w = *reinterpret_cast<const f32x4*>(a + cb + 32 * s + 4 * h2);
+            x[4 * h2] = w[0]; x[4 * h2 + 1] = w[1]; x[4 * h2 + 2] = w[2]; x[4 * h2 + 3] = w[3];
+          }
+        };
+        ch8(TAU + tb * D, tau);
+        ch8(SEM + tb * D, em);
+        ch8(SEO + tb * D, eo);
+        ch8(SPH + tb * D, ph);
+        float kL[8], kR[8], qL[8], kF[8], qF[8], kG[8], y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int E8 = 8 * s + e;
+          const float qh = qf[E8] * rq, kh = kf[E8] * rk;
+          // exp(lam - tau/2) and its reciprocal: the midpoint factors (within e^+-44)
+          const float E = fexp(lam[E8] - 0.5f * tau[e]);
+          const float Ei = __builtin_amdgcn_rcpf(E);
+          const float F = E * em[e];   // exp(lam)        <= 1
+          const float G = Ei * em[e];  // exp(tau - lam)  <= 1
+          kL[e] = kh * E;
+          kR[e] = kh * Ei;
+          qL[e] = qh * E;
+          kF[e] = kh * F;
+          qF[e] = qh * F;
+          kG[e] = kh * G;
+        }
+        {  // diagonal block: three hi / lo terms for A and for P
+          u32x4 lh, ll, rh, rl, qh8, ql8;
+          split8(kL, lh, ll);
+          split8(kR, rh, rl);
+          split8(qL, qh8, ql8);
+          a0 = mma(lh, rh, a0);
+          a1 = mma(lh, rl, a1);
+          a2 = mma(ll, rh, a2);
+          pp = mma(qh8, rh, pp);
+          pp = mma(qh8, rl, pp);
+          pp = mma(ql8, rh, pp);
+        }
+        split8(kF, kFh[s], kFl[s]);
+        split8(qF, qFh[s], qFl[s]);
+        // Q~ = exp(Gam) q_hat -> the chain's fragment (block tb, kt = 2 hc + s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = qF[e] * eo[e];
+        {  // channels 8 g4 .. +7 of the slice go to the fragments of chain lanes
+           // g = 2 (g4 % 2) and g + 1 (key channels 4 g + i in the first half of a
+           // fragment, 16 + 4 g + i in the second; half g4 / 2)
+          const u32x4 w = pack8(y);
+          uint8_t* base = QOP + (tb * 4 + 2 * hc + s) * 64 * 16 + (g4 >> 1) * 8;
+          const int gq = 2 * (g4 & 1);
+          *reinterpret_cast<u32x2*>(base + (n16 + 16 * gq) * 16) = u32x2{w[0], w[1]};
+          *reinterpret_cast<u32x2*>(base + (n16 + 16 * (gq + 1)) * 16) = u32x2{w[2], w[3]};
+        }
+        // x = exp(Gam) k_hat
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = kF[e] * eo[e];
+        split8(y, xh[s], xl[s]);
+        // k~ = exp(Gam_e - Gam) k_hat (zero for tokens that do not enter the state)
+        if (!cut) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = kG[e] * ph[e];
+        } else {
+          float so[8], sge[8];
+          ch8(SO + tb * D, so);
+          ch8(SGE, sge);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int E8 = 8 * s + e;
+            y[e] = tr < pe ? kf[E8] * rk * fexp(sge[e] - so[e] - lam[E8]) : 0.f;
+          }
+          if (ring_row) {  // hand-off: ring rows of the tail tokens (k_hat, G)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int E8 = 8 * s + e;
+              const int ch = cb + 32 * s + e;
+              p.k_cache[rrow * D + ch] = to_bf16(kf[E8] * rk);
+              p.g_cache[rrow * D + ch] = so[e] + lam[E8] - sge[e];
+            }
+          }
+        }
+        split8h(y, kth[s], ktl[s]);
+        if (tb == 3) {  // left operands towards blocks 0 and 1: reference o_2 (x exp(tau_2))
+          float t2[8], b2[8];
+          ch8(ST2, t2);  // one value per channel
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            y[e] = kF[e] * t2[e];
+            b2[e] = qF[e] * t2[e];
+          }
+          split8(y, kF2h[s], kF2l[s]);
+          split8(b2, qF2h[s], qF2l[s]);
+        }
+        // right operands of the off-diagonal pairs -> LDS, slots 0..2: exp(tau_b - lam) k_hat
+        auto put_right = [&](int sl, const float* x) {
+          u32x4 hi, lo;
+          split8(x, hi, lo);
+          *reinterpret_cast<u32x4*>(KGR + ((sl * 2 + 0) * 16 + n16) * KGS + cb + 32 * s) = hi;
+          *reinterpret_cast<u32x4*>(KGR + ((sl * 2 + 1) * 16 + n16) * KGS + cb + 32 * s) = lo;
+        };
+        if (tb <= 2) put_right(tb, kG);
+        if (tb == 0) {  // slot 3: block 0 towards reference o_2 (x exp(tau_1))
+          float t1[8];
+          ch8(ST1, t1);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = kG[e] * t1[e];
+          put_right(3, y);
+        }
+      }
+      accA[0] = a0 + (a1 + a2);
+      accP[0] = pp;
+    }
+    lds_barrier();  // b2
+
+    // ================= P3: off-diagonal blocks of A and P (partials over this half)
+    {
+      KDA_PHASE_IDS;
+      auto offdiag = [&](int slot_r, const u32x4 (&lh)[2], const u32x4 (&ll)[2],
+                         const u32x4 (&qh)[2], const u32x4 (&ql)[2], f32x4& A, f32x4& P) {
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, pp = a0;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const u32x4 rh = *reinterpret_cast<const u32x4*>(
+              KGR + ((slot_r * 2 + 0) * 16 + n16) * KGS + cb + 32 * s);
+          const u32x4 rl = *reinterpret_cast<const u32x4*>(
+              KGR + ((slot_r * 2 + 1) * 16 + n16) * KGS + cb + 32 * s);
+          a0 = mma(lh[s], rh, a0);
+          a1 = mma(lh[s], rl, a1);
+          a2 = mma(ll[s], rh, a2);
+          pp = mma(qh[s], rh, pp);
+          pp = mma(qh[s], rl, pp);
+          pp = mma(ql[s], rh, pp);
+        }
+        A = a0 + (a1 + a2);
+        P = pp;
+      };
+      if (tb == 1) {
+        offdiag(0, kFh, kFl, qFh, qFl, accA[1], accP[1]);            // (1,0)
+      } else if (tb == 2) {
+        offdiag(3, kFh, kFl, qFh, qFl, accA[1], accP[1]);            // (2,0)
+        offdiag(1, kFh, kFl, qFh, qFl, accA[2], accP[2]);            // (2,1)
+      } else if (tb == 3) {
+        offdiag(2, kFh, kFl, qFh, qFl, accA[1], accP[1]);            // (3,2)
+        offdiag(3, kF2h, kF2l, qF2h, qF2l, accA[2], accP[2]);        // (3,0)
+        offdiag(1, kF2h, kF2l, qF2h, qF2l, accA[3], accP[3]);        // (3,1)
+      }
+      if (hc == 1) {
+        const int np = tb + 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i < np) {
+            const int a = i == 0 ? tb : (tb == 1 ? 0 : (tb == 2 ? i - 1 : (i == 1 ? 2 : i - 2)));
+            const int pid = pair_id(tb, a);
+            *reinterpret_cast<f32x4*>(PART + ((pid * 2 + 0) * 64 + ln_) * 4) = accA[i];
+            *reinterpret_cast<f32x4*>(PART + ((pid * 2 + 1) * 64 + ln_) * 4) = accP[i];
+          }
+        }
+      }
+    }
+    lds_barrier();  // b3
+
+    // ================= P3b: A (scaled by beta) and P, whole sums, masked
+    if (hc == 0) {
+      KDA_PHASE_IDS;
+      const int np = tb + 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < np) {
+          const int a = i == 0 ? tb : (tb == 1 ? 0 : (tb == 2 ? i - 1 : (i == 1 ? 2 : i - 2)));
+          const int pid = pair_id(tb, a);
+          const f32x4 A = accA[i] + *reinterpret_cast<const f32x4*>(PART + ((pid * 2 + 0) * 64 + ln_) * 4);
+          const f32x4 P = accP[i] + *reinterpret_cast<const f32x4*>(PART + ((pid * 2 + 1) * 64 + ln_) * 4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int rl = 4 * g4 + q;  // row within the block; column n16
+            const int r = 16 * tb + rl, j = 16 * a + n16;
+            const float av = (a < tb || n16 < rl) ? A[q] * BETA[r] : 0.f;
+            const float pv = (a < tb || n16 <= rl) ? P[q] : 0.f;
+            AM[r * AMS + j] = av;
+            PM[r * TRS + j] = to_f16(pv);
+          }
+        }
+      }
+    }
+    lds_barrier();  // b4
+
+    // ================= P4a: x^T -> LDS (every wave); diagonal blocks of T (waves 0-3)
+    {
+      KDA_PHASE_IDS;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int e = 8 * s + 2 * w + hf;
+            const int ch = cb + 32 * (e >> 3) + (e & 7);
+            XT[ch * TRS + tr] = uint16_t(hf ? xh[s][w] >> 16 : xh[s][w] & 0xffffu);
+            XT[D * TRS + ch * TRS + tr] = uint16_t(hf ? xl[s][w] >> 16 : xl[s][w] & 0xffffu);
+          }
+        }
+      }
+      if (wave < 4) {
+        // T_bb = (I + L_bb)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8), N = -L_bb
+        // (strictly lower, so N^16 = 0), on fp32 MFMA; wave b takes block b.
+        // A matrix is held in the accumulator layout (Z: rows 4 g4 + i, column
+        // n16), and where it enters as a left factor also transposed (Zt): a
+        // 16 x 16 x 4 step ks contracts the index 4 g4 + ks, which both forms
+        // hold in element ks.
+        const int b = wave;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 Nz, Nt, Id;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          Nz[q] = -AM[(16 * b + 4 * g4 + q) * AMS + 16 * b + n16];
+          Id[q] = (4 * g4 + q == n16) ? 1.f : 0.f;
+        }
+        Nt = -*reinterpret_cast<const f32x4*>(AM + (16 * b + n16) * AMS + 16 * b + 4 * g4);
+        auto prod = [&](f32x4 Xt, f32x4 Y) {  // (X Y) in the Z layout
+          f32x4 r = z;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) r = mma_f32(Xt[ks], Y[ks], r);
+          return r;
+        };
+        auto prodT = [&](f32x4 Xt, f32x4 Y) {  // (X Y)^T in the Z layout
+          f32x4 r = z;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) r = mma_f32(Y[ks], Xt[ks], r);
+          return r;
+        };
+        const f32x4 N2z = prod(Nt, Nz), N2t = prodT(Nt, Nz);
+        const f32x4 N4z = prod(N2t, N2z), N4t = prodT(N2t, N2z);
+        const f32x4 N8z = prod(N4t, N4z);
+        const f32x4 N3z = prod(Nt, N2z), N3t = prodT(Nt, N2z);
+        const f32x4 X1z = ((Id + Nz) + N2z) + N3z, X1t = ((Id + Nt) + N2t) + N3t;
+        const f32x4 X2z = X1z + prod(X1t, N4z), X2t = X1t + prodT(X1t, N4z);
+        const f32x4 Tz = X2z + prod(X2t, N8z);
+        const float bj = BETA[16 * b + n16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = 4 * g4 + q;
+          TD[(b * 16 + r) * 17 + n16] = Tz[q];
+          const float t = Tz[q] * bj;  // T' = T diag(beta)
+          const uint16_t hi = to_bf16(t);
+          TP[(16 * b + r) * TRS + 16 * b + n16] = hi;
+          TP[CH * TRS + (16 * b + r) * TRS + 16 * b + n16] = to_bf16(t - bf1(hi));
+        }
+      }
+    }
+    lds_barrier();  // b5
+
+    // ================= P4b: off-diagonal blocks of T (fp32 MFMA), three chains
+    if (wave < 3) {
+      KDA_PHASE_IDS;
+      // k of the 16 x 16 x 4 steps: slot g4 of step ks is index 4 g4 + ks
+      auto L_a = [&](int b, int cc, int ks) { return AM[(16 * b + n16) * AMS + 16 * cc + 4 * g4 + ks]; };
+      auto TD_b = [&](int a, int ks) { return TD[(a * 16 + 4 * g4 + ks) * 17 + n16]; };  // T_aa[k][n]
+      auto TD_a = [&](int b, int ks) { return TD[(b * 16 + n16) * 17 + 4 * g4 + ks]; };  // T_bb[m][k]
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      // M += L_bc T_cc (diagonal T block from LDS)
+      auto mul_Ld = [&](f32x4 M, int b, int cc) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) M = mma_f32(L_a(b, cc, ks), TD_b(cc, ks), M);
+        return M;
+      };
+      // M += L_bc X (X an off-diagonal T block in the accumulator layout)
+      auto mul_Lx = [&](f32x4 M, int b, int cc, f32x4 X) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) M = mma_f32(L_a(b, cc, ks), X[ks], M);
+        return M;
+      };
+      // -T_bb M
+      auto neg_Tb = [&](int b, f32x4 M) {
+        f32x4 r = z;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) r = mma_f32(TD_a(b, ks), M[ks], r);
+        return -r;
+      };
+      auto put = [&](int b, int a, f32x4 T) {
+        const float bj = BETA[16 * a + n16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = 16 * b + 4 * g4 + q, j = 16 * a + n16;
+          const float t = T[q] * bj;
+          const uint16_t hi = to_bf16(t);
+          TP[r * TRS + j] = hi;
+          TP[CH * TRS + r * TRS + j] = to_bf16(t - bf1(hi));
+        }
+      };
+      if (wave == 0) {
+        const f32x4 T10 = neg_Tb(1, mul_Ld(z, 1, 0));
+        put(1, 0, T10);
+        const f32x4 T20 = neg_Tb(2, mul_Lx(mul_Ld(z, 2, 0), 2, 1, T10));
+        put(2, 0, T20);
+        const f32x4 T30 = neg_Tb(3, mul_Lx(mul_Lx(mul_Ld(z, 3, 0), 3, 1, T10), 3, 2, T20));
+        put(3, 0, T30);
+      } else if (wave == 1) {
+        const f32x4 T21 = neg_Tb(2, mul_Ld(z, 2, 1));
+        put(2, 1, T21);
+        const f32x4 T31 = neg_Tb(3, mul_Lx(mul_Ld(z, 3, 1), 3, 2, T21));
+        put(3, 1, T31);
+      } else {
+        const f32x4 T32 = neg_Tb(3, mul_Ld(z, 3, 2));
+        put(3, 2, T32);
+      }
+    }
+    lds_barrier();  // b6
+
+    // ================= P5: W^T = x^T T'^T (wave: channel tile) and U0 = T' V (wave: value tile)
+    f32x4 u0[4];
+    {
+      KDA_PHASE_IDS;
+      u32x4 vb[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int r0 = 32 * s + 8 * g4 + 2 * w;
+          vb[s][w] = uint32_t(VR[r0 * VRS + v]) | (uint32_t(VR[(r0 + 1) * VRS + v]) << 16);
+        }
+      }
+      const uint16_t* xtr_h = XT + (16 * wave + n16) * TRS;
+      const uint16_t* xtr_l = XT + D * TRS + (16 * wave + n16) * TRS;
+      const u32x4 xa_h0 = *reinterpret_cast<const u32x4*>(xtr_h + 8 * g4);
+      const u32x4 xa_l0 = *reinterpret_cast<const u32x4*>(xtr_l + 8 * g4);
+      const u32x4 xa_h1 = *reinterpret_cast<const u32x4*>(xtr_h + 32 + 8 * g4);
+      const u32x4 xa_l1 = *reinterpret_cast<const u32x4*>(xtr_l + 32 + 8 * g4);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 w0 = z, w1 = z, w2 = z, uu = z;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          if (s == 1 && b < 2) continue;
+          const u32x4 th = *reinterpret_cast<const u32x4*>(TP + (16 * b + n16) * TRS + 32 * s + 8 * g4);
+          const u32x4 tl =
+              *reinterpret_cast<const u32x4*>(TP + CH * TRS + (16 * b + n16) * TRS + 32 * s + 8 * g4);
+          const u32x4 xh8 = s ? xa_h1 : xa_h0;
+          const u32x4 xl8 = s ? xa_l1 : xa_l0;
+          w0 = mma(xh8, th, w0);
+          w1 = mma(xh8, tl, w1);
+          w2 = mma(xl8, th, w2);
+          uu = mma(th, vb[s], uu);
+          uu = mma(tl, vb[s], uu);
+        }
+        {  // + (beta_t - its bf16 hi + lo) v_t, the diagonal's split residual
+          const f32x4 dl = *reinterpret_cast<const f32x4*>(DLT + 16 * b + 4 * g4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            uu[q] = fmaf(dl[q], bf1(VR[(16 * b + 4 * g4 + q) * VRS + v]), uu[q]);
+        }
+        u0[b] = uu;
+        // W^T[16 wave + 4 g4 + i][16 b + n16] -> the chain's W fragment (b, kt = wave / 2)
+        const f32x4 wv = w0 + (w1 + w2);
+        u32x2 hi, lo;
+        split4(wv, hi, lo);
+        uint8_t* dst = WOP + ((b * 4 + (wave >> 1)) * 2 * 64 + ln_) * 16 + 8 * (wave & 1);
+        *reinterpret_cast<u32x2*>(dst) = hi;
+        *reinterpret_cast<u32x2*>(dst + 64 * 16) = lo;
+      }
+    }
+    lds_barrier();  // b7
+
+    // ================= C1: U = U0 - W S, O = Q~ S (chain; wave: value tile)
+    const int npos = pos + c;
+    f32x4 oo[4];
+    u32x4 uh[2], ul[2];  // this wave's U tile in fp16 hi + lo, times u_sc
+    bool u_big = false;  // wave-uniform: u_sc = 2^-s, u_isc = 2^s, else both 1
+    float u_sc = 1.f, u_isc = 1.f;
+    {
+      KDA_PHASE_IDS;
+      u32x4 sh[4], sl[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const float sv[8] = {acc[2 * kt][0],     acc[2 * kt][1],     acc[2 * kt][2],
+                             acc[2 * kt][3],     acc[2 * kt + 1][0], acc[2 * kt + 1][1],
+                             acc[2 * kt + 1][2], acc[2 * kt + 1][3]};
+        split8(sv, sh[kt], sl[kt]);
+      }
+      f32x4 uu[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        fence_sched();
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 y0 = z, y1 = z, y2 = z, yq = z;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const uint8_t* wf = WOP + ((b * 4 + kt) * 2 * 64 + ln_) * 16;
+          const u32x4 wh = *reinterpret_cast<const u32x4*>(wf);
+          const u32x4 wl = *reinterpret_cast<const u32x4*>(wf + 64 * 16);
+          const u32x4 qq = *reinterpret_cast<const u32x4*>(QOP + ((b * 4 + kt) * 64 + ln_) * 16);
+          y0 = mma(wh, sh[kt], y0);
+          y1 = mma(wh, sl[kt], y1);
+          y2 = mma(wl, sh[kt], y2);
+          yq = mma(qq, sh[kt], yq);
+          yq = mma(qq, sl[kt], yq);  // the state's low part: only q~'s rounding remains
+        }
+        uu[b] = u0[b] - (y0 + (y1 + y2));
+        oo[b] = yq;
+      }
+      // U goes to the fp16 products below. A tile with an element of 2^14 or
+      // more (inputs far outside the usual range) is scaled by 2^-s first, so
+      // that hi + lo stay finite; the products are scaled back by 2^s.
+      float um = 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) um = fmaxf(um, fabsf(uu[b][q]));
+      u_big = __builtin_amdgcn_ballot_w64(um >= 16384.f) != 0;
+      if (u_big) {
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) um = fmaxf(um, __shfl_xor(um, o));
+        const int ex = int((__float_as_uint(um) >> 23) & 0xffu) - 127;  // >= 14
+        const int sh = __builtin_amdgcn_readfirstlane(min(ex - 13, 126));
+        u_sc = __uint_as_float(uint32_t(127 - sh) << 23);
+        u_isc = __uint_as_float(uint32_t(127 + sh) << 23);
+      }
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const float x8[8] = {uu[2 * pp][0] * u_sc,     uu[2 * pp][1] * u_sc,
+                             uu[2 * pp][2] * u_sc,     uu[2 * pp][3] * u_sc,
+                             uu[2 * pp + 1][0] * u_sc, uu[2 * pp + 1][1] * u_sc,
+                             uu[2 * pp + 1][2] * u_sc, uu[2 * pp + 1][3] * u_sc};
+        split8h(x8, uh[pp], ul[pp]);
+      }
+      if (cut) {  // hand-off: ring rows of the tail tokens receive u (bf16)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          fence_sched();
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 16 * b + 4 * g4 + q;
+            if (r >= pe && r < c) {
+              int rr = rbase + r - pe;
+              rr = rr >= p.ring_rows ? rr - p.ring_rows : rr;
+              p.u_cache[(ring0 + rr) * D + v] = to_bf16(uu[b][q]);
+            }
+          }
+        }
+      }
+    }
+    lds_barrier();  // b8: W fragments read; k~^T may overwrite them
+
+    {  // next chunk's raw inputs, in flight during C2 and C3 (always assigned, zeros
+       // past the document's end, so that they are dead from P1 to here)
+      KDA_PHASE_IDS;
+      const int cn = npos < len32 ? chunk_len(npos) : 0;
+      load_raw<VEC, GHEAD>(p, t0 + npos, tr, h, cb, tr < cn, raw);
+    }
+
+    // ================= k~^T -> LDS (token-owner registers); C2: O += P U, output
+    {
+      KDA_PHASE_IDS;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int e = 8 * s + 2 * w + hf;
+            const int ch = cb + 32 * (e >> 3) + (e & 7);
+            KT[ch * TRS + tr] = uint16_t(hf ? kth[s][w] >> 16 : kth[s][w] & 0xffffu);
+            KT[D * TRS + ch * TRS + tr] = uint16_t(hf ? ktl[s][w] >> 16 : ktl[s][w] & 0xffffu);
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (u_big) oo[b] *= u_sc;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          if (pp == 1 && b < 2) continue;
+          const uint16_t* prow = PM + (16 * b + n16) * TRS + 32 * pp;
+          const u32x2 a0 = *reinterpret_cast<const u32x2*>(prow + 4 * g4);
+          const u32x2 a1 = *reinterpret_cast<const u32x2*>(prow + 16 + 4 * g4);
+          const u32x4 pa = {a0[0], a0[1], a1[0], a1[1]};
+          oo[b] = mma_h(pa, uh[pp], oo[b]);
+          oo[b] = mma_h(pa, ul[pp], oo[b]);
+        }
+        if (u_big) oo[b] *= u_isc;
+        // outputs staged in LDS (the x^T region, free until the next chunk's
+        // A / P partials), stored below as whole 16-byte pieces of token rows
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          OST[(16 * b + 4 * g4 + q) * OSS + v] = to_bf16(p.scale * oo[b][q]);
+      }
+    }
+    lds_barrier();  // b9
+
+    {  // this chunk's output rows: 64 rows x 16 pieces of 8 channels, two per thread
+      const int t_ = fresh(tid);
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int id = t_ + NTHR * k2;
+        const int r = id >> 4, c8 = 8 * (id & 15);
+        if (r < c) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(OST + r * OSS + c8);
+          store8_raw<VEC>(p.out + (t0 + pos + r) * p.out_tok_stride + h * D + c8, w);
+        }
+      }
+    }
+
+    // ================= C3: S = diag(exp(Gam_e)) S + k~^T U
+    {
+      KDA_PHASE_IDS;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        fence_sched();
+        const f32x4 eg = *reinterpret_cast<const f32x4*>(EG + 16 * m + 4 * g4);
+        f32x4 a = acc[m] * eg;
+        if (u_big) a *= u_sc;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const uint16_t* kr_h = KT + (16 * m + n16) * TRS + 32 * pp;
+          const uint16_t* kr_l = KT + D * TRS + (16 * m + n16) * TRS + 32 * pp;
+          const u32x2 h0 = *reinterpret_cast<const u32x2*>(kr_h + 4 * g4);
+          const u32x2 h1 = *reinterpret_cast<const u32x2*>(kr_h + 16 + 4 * g4);
+          const u32x2 l0 = *reinterpret_cast<const u32x2*>(kr_l + 4 * g4);
+          const u32x2 l1 = *reinterpret_cast<const u32x2*>(kr_l + 16 + 4 * g4);
+          const u32x4 kh8 = {h0[0], h0[1], h1[0], h1[1]};
+          const u32x4 kl8 = {l0[0], l0[1], l1[0], l1[1]};
+          a = mma_h(kh8, uh[pp], a);
+          a = mma_h(kh8, ul[pp], a);
+          a = mma_h(kl8, uh[pp], a);
+        }
+        if (u_big) a *= u_isc;
+        acc[m] = a;
+      }
+    }
+    // intermediate checkpoint after this chunk
+    if (ivl && npos % ivl == 0 && npos <= kept) {
+      KDA_PHASE_IDS;
+      const int64_t row = ckpt_row0 + npos / ivl - 1;  // (32-bit division)
       if (row >= 0 && row < p.ckpt_rows) {
         const int64_t ce = (row * p.H + h) * int64_t(HEAD_ELEMS);
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-          st4_store<SF, VEC>(p.ckpt, ce + v * D + 16 * mt + 4 * g4, acc[mt]);
+        for (int m = 0; m < 8; ++m)
+          st4_store<SF, VEC>(p.ckpt, ce + int64_t(v) * D + 16 * m + 4 * g4, acc[m]);
       }
     }
-    __syncthreads();  // this chunk's buffer is read; the next one is written
-  }
-
-  if (tail > 0) {  // hand-off: ring rows of the tail tokens receive u (bf16)
-    uint16_t* ur = p.u_cache + (int64_t(slot) * p.H + h) * p.ring_rows * int64_t(D) + v;
-    const int pe = c_last - tail;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g4 + i;
-      if (r >= pe && r < c_last)
-        ur[int64_t((rbase + r - pe) % p.ring_rows) * D] = to_bf16(u_last[i]);
-    }
+    pos = npos;
   }
 
   // ---- final state (the state after the first `kept` tokens)
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
-    st4_store<SF, VEC>(p.state_pool, se + v * D + 16 * mt + 4 * g4, acc[mt]);
+  for (int m = 0; m < 8; ++m)
+    st4_store<SF, VEC>(p.state_pool, se + int64_t(v) * D + 16 * m + 4 * g4, acc[m]);
 }
 
 size_t prefill_workspace_bytes(int32_t n_docs, int64_t total_tokens, int32_t H) {
-  if (n_docs <= 0 || total_tokens <= 0 || H <= 0) return 0;
-  return size_t(int64_t(n_docs) + (total_tokens >> 4)) * size_t(H) * size_t(kRecBytes);
+  if (int64_t(n_docs) * H < kFusedMinChains)
+    return prefill_split_workspace_bytes(n_docs, total_tokens, H);
+  return 0;  // the fused kernel keeps every chunk's operands in LDS
 }
 
 hipError_t launch_prefill(const PrefillParams& p, const int32_t* cu_host, bool vec,
                           hipStream_t stream) {
   const int64_t blocks = int64_t(p.n_docs) * p.H;
   if (blocks == 0) return hipSuccess;
-  if (2 * blocks > 0x7fffffff || p.H > 65535) return hipErrorInvalidValue;
-  const int64_t slots = int64_t(p.n_docs) + (p.total_tokens >> 4);
-  if (slots > 0x7fffffff) return hipErrorInvalidValue;
+  if (blocks < kFusedMinChains) return launch_prefill_split(p, cu_host, vec, stream);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   // Longest documents first: their chains bound the makespan.
   DocOrder ord;
   ord.n = 0;
@@ -914,84 +1146,42 @@ hipError_t launch_prefill(const PrefillParams& p, const int32_t* cu_host, bool v
       ord.doc[j + 1] = d;
     }
   }
+  // fp16 and fp8 states run on the vectorised path only (the host requires it)
+  if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
+  const int gk = p.gate_mode & kGateKindMask;
+  const void* fn = nullptr;
+#define KDA_PF(V, G, S) reinterpret_cast<const void*>(&prefill_kernel<V, G, S>)
+#define KDA_PF_G(V, S)                                                   \
+  (gk == 0 ? KDA_PF(V, 0, S) : gk == 1 ? KDA_PF(V, 1, S) : gk == 4 ? KDA_PF(V, 4, S) \
+                                                                   : KDA_PF(V, 5, S))
+  if (p.state_fmt == kStateFp16) fn = KDA_PF_G(true, kStateFp16);
+  else if (p.state_fmt == kStateFp8) fn = KDA_PF_G(true, kStateFp8);
+  else if (vec) fn = KDA_PF_G(true, kStateBf16);
+  else fn = KDA_PF_G(false, kStateBf16);
+#define KDA_PF_ALL                                                                      \
+  KDA_PF(true, 0, kStateBf16), KDA_PF(true, 1, kStateBf16), KDA_PF(true, 4, kStateBf16),     \
+      KDA_PF(true, 5, kStateBf16), KDA_PF(true, 0, kStateFp16), KDA_PF(true, 1, kStateFp16), \
+      KDA_PF(true, 4, kStateFp16), KDA_PF(true, 5, kStateFp16), KDA_PF(true, 0, kStateFp8),  \
+      KDA_PF(true, 1, kStateFp8), KDA_PF(true, 4, kStateFp8), KDA_PF(true, 5, kStateFp8),    \
+      KDA_PF(false, 0, kStateBf16), KDA_PF(false, 1, kStateBf16),                           \
+      KDA_PF(false, 4, kStateBf16), KDA_PF(false, 5, kStateBf16)
+  // the dynamic LDS limit of every instance is raised once per process
   static const hipError_t attr = [] {
-    const void* fns[] = {reinterpret_cast<const void*>(&prep_kernel<true, 0>),
-                         reinterpret_cast<const void*>(&prep_kernel<true, 1>),
-                         reinterpret_cast<const void*>(&prep_kernel<true, 4>),
-                         reinterpret_cast<const void*>(&prep_kernel<true, 5>),
-                         reinterpret_cast<const void*>(&prep_kernel<false, 0>),
-                         reinterpret_cast<const void*>(&prep_kernel<false, 1>),
-                         reinterpret_cast<const void*>(&prep_kernel<false, 4>),
-                         reinterpret_cast<const void*>(&prep_kernel<false, 5>)};
+    const void* fns[] = {KDA_PF_ALL};
     for (const void* f : fns) {
-      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               static_cast<int>(kPrepLds));
+      const hipError_t e =
+          hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
   }();
   if (attr != hipSuccess) return attr;
-  if (p.total_tokens > 0) {
-    dim3 pgrid(static_cast<unsigned>(slots),
-               static_cast<unsigned>((p.H + kPrepHeads - 1) / kPrepHeads)),
-        block(kThreads);
-    const int gk = p.gate_mode & kGateKindMask;
-#define KDA_PREP_LAUNCH(V)                                                                    \
-  do {                                                                                        \
-    switch (gk) {                                                                             \
-      case 0: hipLaunchKernelGGL((prep_kernel<V, 0>), pgrid, block, kPrepLds, stream, p); break; \
-      case 1: hipLaunchKernelGGL((prep_kernel<V, 1>), pgrid, block, kPrepLds, stream, p); break; \
-      case 4: hipLaunchKernelGGL((prep_kernel<V, 4>), pgrid, block, kPrepLds, stream, p); break; \
-      default: hipLaunchKernelGGL((prep_kernel<V, 5>), pgrid, block, kPrepLds, stream, p);      \
-    }                                                                                         \
-  } while (0)
-    if (vec) KDA_PREP_LAUNCH(true);
-    else KDA_PREP_LAUNCH(false);
-#undef KDA_PREP_LAUNCH
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (p.ring_tail > 0) {
-    dim3 hgrid(static_cast<unsigned>(p.n_docs), static_cast<unsigned>(p.H)), hblock(kThreads);
-    const int gk = p.gate_mode & kGateKindMask;
-#define KDA_HANDOFF_LAUNCH(V)                                                                  \
-  do {                                                                                         \
-    switch (gk) {                                                                              \
-      case 0: hipLaunchKernelGGL((handoff_kernel<V, 0>), hgrid, hblock, 0, stream, p); break; \
-      case 1: hipLaunchKernelGGL((handoff_kernel<V, 1>), hgrid, hblock, 0, stream, p); break; \
-      case 4: hipLaunchKernelGGL((handoff_kernel<V, 4>), hgrid, hblock, 0, stream, p); break; \
-      default: hipLaunchKernelGGL((handoff_kernel<V, 5>), hgrid, hblock, 0, stream, p);       \
-    }                                                                                          \
-  } while (0)
-    if (vec) KDA_HANDOFF_LAUNCH(true);
-    else KDA_HANDOFF_LAUNCH(false);
-#undef KDA_HANDOFF_LAUNCH
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  // Fewer chains than CUs: two workgroups per chain (by value channels).
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 0;
-  const bool split = blocks < cus;
-  // fp16 and fp8 states run on the vectorised path only (the host requires it)
-  if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
-#define KDA_CHAIN_LAUNCH(V, S)                                                              \
-  do {                                                                                      \
-    if (split)                                                                              \
-      hipLaunchKernelGGL((chain_kernel<V, S, 2>), dim3(static_cast<unsigned>(2 * blocks)),  \
-                         dim3(ChainShape<2>::kThreads), 0, stream, p, ord);                 \
-    else                                                                                    \
-      hipLaunchKernelGGL((chain_kernel<V, S, 1>), dim3(static_cast<unsigned>(blocks)),      \
-                         dim3(ChainShape<1>::kThreads), 0, stream, p, ord);                 \
-  } while (0)
-  if (p.state_fmt == kStateFp16) KDA_CHAIN_LAUNCH(true, kStateFp16);
-  else if (p.state_fmt == kStateFp8) KDA_CHAIN_LAUNCH(true, kStateFp8);
-  else if (vec) KDA_CHAIN_LAUNCH(true, kStateBf16);
-  else KDA_CHAIN_LAUNCH(false, kStateBf16);
-#undef KDA_CHAIN_LAUNCH
-  return hipGetLastError();
+#undef KDA_PF_ALL
+#undef KDA_PF_G
+#undef KDA_PF
+  void* args[] = {const_cast<PrefillParams*>(&p), &ord};
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(NTHR), args,
+                         static_cast<size_t>(kLdsBytes), stream);
 }
 
 }  // namespace kda

@@ -1,0 +1,999 @@
+// Chunked varlen prefill of the KDA recurrence (gfx950), the two-stage form
+// for calls with few (document, head) chains: a preparation kernel over every
+// (16-token chunk, head) and a chain kernel over every (document, head),
+// joined by a caller-provided workspace. With fewer chains than compute units
+// the chains alone cannot fill the chip, so the state-independent preparation
+// runs first on every CU, and the chain then takes the recurrence alone,
+// split by value channels over two workgroups. (Calls with more chains run
+// the fused kernel of kda_prefill.hip instead.)
+//
+// Operation: "feat(kda): add CuTe DSL recurrent prefill backend" -- packed
+// documents delimited by cu_seqlens, each (document, head) chain runs the
+// gated delta-rule recurrence over its tokens from an optional initial state
+// and leaves its final state in the pool; the work is chunked (BT = 16 on
+// that page) into an intra-chunk preparation and a sequential chain over
+// chunks, the two stages of that page's prefill. The result equals the
+// token-by-token recurrence.
+//
+// Chunkwise form used here (WY representation of the delta rule with the
+// decay carried per key channel; Yang et al., "Parallelizing Linear
+// Transformers with the Delta Rule over Sequence Length", 2024). For a chunk
+// of c <= 16 tokens r entering with state S (S[v][k]: value channel v, key
+// channel k), Gam_r = g_0 + ... + g_r per key channel:
+//   A[r,j] = sum_k k_r k_j exp(Gam_r - Gam_j)         (j < r)
+//   P[r,j] = sum_k q_r k_j exp(Gam_r - Gam_j)         (j <= r)
+//   W_r    = beta_r (exp(Gam_r) k_r - sum_{j<r} A[r,j] W_j)
+//   U0_r   = beta_r (v_r - sum_{j<r} A[r,j] U0_j)
+//   U      = U0 - W S^T         (rows are the per-token corrections u_r)
+//   O      = scale ((exp(Gam) q) S^T + P U)
+//   S      = S diag(exp(Gam_c)) + U^T (exp(Gam_c - Gam) k)
+// Everything but the last three lines is independent of the state, so it runs
+// for all chunks of all documents at once (prep_kernel); only the last three
+// lines are sequential (chain_kernel).
+//
+// Every weight exp(Gam_r - Gam_j) of A and P factors into
+// exp(Gam_r - m) * exp(m - Gam_j) with m = Gam_last / 2 per key channel: over
+// 16 tokens |Gam_r - m| <= 8 |lower_bound| <= 44 (the host requires
+// |lower_bound| <= 5.5), so both factors, and a key channel scaled by either,
+// stay far from fp32 overflow and from denormals. W is solved for the
+// right-hand side exp(Gam_r - m) k_r and scaled by exp(m) afterwards (the solve
+// is linear per key channel).
+//
+// Chunk record. The preparation leaves, per (chunk, head), the chain's
+// operands in the workspace already in MFMA fragment order, so the chain
+// moves them with 16-byte loads and reads them with one LDS read per
+// fragment. Lane l = n16 + 16 g4 of a wave:
+//   W   [kt 4][hi, lo][lane][8 bf16]  W[n16][32kt + 4g4 + 0..3, 32kt + 16 + 4g4 + 0..3]
+//   Q   [kt 4][lane][8 bf16]          (exp(Gam) q_hat) at the same positions, bf16
+//   KT  [mt 8][lane][4 hi, 4 lo bf16] (exp(Gam_c - Gam) k_hat)[4g4 + 0..3][16mt + n16]
+//   U0  [vt 8][lane][4 fp32]          U0[4g4 + 0..3][16vt + n16]
+//   P   [lane][4 bf16]                P[n16][4g4 + 0..3]
+//   EG  [128 fp32]                    exp(Gam_c)
+// The chain's state S[v][k] sits in the MFMA accumulator layout: wave w, tile
+// (mt, nt) holds key channels 16mt + 4g4 + i and value channel 32w + 16nt + n16,
+// so the B fragment of v_mfma_f32_16x16x32_bf16 takes its 8 key channels as two
+// runs of 4 from accumulator tiles 2kt and 2kt+1 (the order the W and Q
+// fragments are written in), and U = U0 - W S^T comes out in the accumulator
+// layout, which is the B fragment of v_mfma_f32_16x16x16_bf16 with the chunk's
+// tokens as the contraction.
+//
+// Chunk slots. Chunk j of document d (first token t0) has slot
+// d + floor(t0 / 16) + j: strictly increasing over (d, j), fewer than
+// n_docs + floor(Ttot / 16) in all, and computable by the chain from (d, j)
+// alone; the preparation finds (d, j) from its slot by a search over
+// cu_seqlens.
+
+#include "kda_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));  // bf16 operands of the K = 16 MFMA
+
+constexpr int C = 16;          // tokens per chunk
+constexpr int RS = D + 4;      // padded row (fp32) of the [token][channel] LDS arrays: the
+                               // 16 rows read by one MFMA fragment load hit different banks
+constexpr int XLD = D + 4;     // padded row (bf16) of W as bf16 hi / lo
+constexpr int kMaxOrderedDocs = 256;
+
+// chunk record, bytes
+constexpr int kRecW = 0;
+constexpr int kRecQ = 8192;
+constexpr int kRecKT = 12288;
+constexpr int kRecU0 = 20480;
+constexpr int kRecP = 28672;
+constexpr int kRecEG = 29184;
+constexpr int kRecBytes = 29696;
+constexpr int kRecUnits = kRecBytes / 16;  // 16-byte units
+constexpr int kThreads = 256;
+constexpr int kRecRounds = (kRecUnits + kThreads - 1) / kThreads;  // 8
+static_assert(kRecEG + 4 * D == kRecBytes, "record layout");
+static_assert(kRecUnits > (kRecRounds - 1) * kThreads, "every round has work");
+
+struct DocOrder {
+  int32_t n;  // 0: natural order
+  int32_t doc[kMaxOrderedDocs];
+};
+
+struct PSmem {
+  float* qh;     // [C][RS] q_hat, then exp(Gam - m) q_hat as bf16 hi / lo pairs, then W
+  float* kh;     // [C][RS] k_hat, then exp(Gam - m) k_hat as bf16 hi / lo pairs
+  float* gg;     // [C][RS] g, then exp(Gam_last - Gam) k_hat
+  float* u0;     // [C][RS] U0
+  float* kb;     // [C][RS] exp(m - Gam) k_hat as bf16 hi / lo pairs, in the U0 rows
+                 // (dead by the time U0 is solved)
+  float* kw;     // [C][RS] exp(Gam - m) k_hat in fp32: right-hand side of W
+  float* am;     // [C][C] A
+  float* beta;   // [C]
+  float* egl;    // [D] exp(Gam_last)
+  float* em;     // [D] exp(Gam_last / 2)
+  uint16_t* vv;    // [C][VLD] v (bf16, as loaded)
+  uint16_t* wop;   // [2][C][XLD] W, bf16 hi / lo, in the q rows (dead after A and P)
+  uint16_t* qop;   // [C][QLD] exp(Gam) q_hat, bf16
+  uint16_t* ktop;  // [2][C][D] exp(Gam_last - Gam) k_hat, bf16 hi / lo, in the g rows
+                   // (dead once the prefix sums are taken)
+  uint16_t* pop;   // [C][C] P, bf16
+};
+
+constexpr int VLD = D + 8;  // row (bf16) of v: 16-byte aligned rows
+constexpr int QLD = D + 4;  // row (bf16) of exp(Gam) q_hat
+static_assert(2 * C * XLD * 2 <= C * RS * 4, "W fits in the q rows");
+static_assert(2 * C * D * 2 <= C * RS * 4, "K~ fits in the g rows");
+constexpr size_t kPrepLds = size_t(5 * C * RS + C * C + C + 2 * D) * 4 +
+                            size_t(C * VLD + C * QLD + C * C) * 2;
+
+__device__ inline PSmem pcarve(float* base) {
+  PSmem s;
+  float* p = base;
+  s.qh = p; p += C * RS;
+  s.kh = p; p += C * RS;
+  s.gg = p; p += C * RS;
+  s.u0 = p; p += C * RS;
+  s.kb = s.u0;
+  s.kw = p; p += C * RS;
+  s.am = p; p += C * C;
+  s.beta = p; p += C;
+  s.egl = p; p += D;
+  s.em = p; p += D;
+  uint16_t* b = reinterpret_cast<uint16_t*>(p);
+  s.vv = b; b += C * VLD;
+  s.qop = b; b += C * QLD;
+  s.pop = b;
+  s.wop = reinterpret_cast<uint16_t*>(s.qh);
+  s.ktop = reinterpret_cast<uint16_t*>(s.gg);
+  return s;
+}
+
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = to_bf16(x);
+  lo = to_bf16(x - bf1(hi));
+}
+
+// 8 fp32 -> bf16x8 hi and lo parts.
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+    const float r0 = x[2 * e] - bf_lo(h[e]);
+    const float r1 = x[2 * e + 1] - bf_hi(h[e]);
+    l[e] = pack_bf16x2(r0, r1);
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
+__device__ __forceinline__ void split4(const f32x4 x, s16x4& hi, s16x4& lo) {
+  u32x2 h, l;
+  h[0] = pack_bf16x2(x[0], x[1]);
+  h[1] = pack_bf16x2(x[2], x[3]);
+  l[0] = pack_bf16x2(x[0] - bf_lo(h[0]), x[1] - bf_hi(h[0]));
+  l[1] = pack_bf16x2(x[2] - bf_lo(h[1]), x[3] - bf_hi(h[1]));
+  hi = __builtin_bit_cast(s16x4, h);
+  lo = __builtin_bit_cast(s16x4, l);
+}
+
+// Two runs of 4 bf16 (8 bytes each, 8-byte aligned) as one 16-byte unit.
+__device__ __forceinline__ u32x4 lds_2runs(const uint16_t* p0, const uint16_t* p1) {
+  const u32x2 a = *reinterpret_cast<const u32x2*>(p0);
+  const u32x2 b = *reinterpret_cast<const u32x2*>(p1);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+template <bool VEC>
+__device__ __forceinline__ u32x2 gload4(const uint16_t* p) {
+  if constexpr (VEC) {
+    return *reinterpret_cast<const u32x2*>(p);
+  } else {
+    return u32x2{uint32_t(p[0]) | (uint32_t(p[1]) << 16), uint32_t(p[2]) | (uint32_t(p[3]) << 16)};
+  }
+}
+
+// State rows leave in 32-byte pieces (16 rows per instruction): plain
+// stores, so that L2 merges the pieces of a row into whole lines.
+template <bool VEC>
+__device__ __forceinline__ void gstore4(uint16_t* p, u32x2 w) {
+  if constexpr (VEC) {
+    *reinterpret_cast<u32x2*>(p) = w;
+  } else {
+    p[0] = uint16_t(w[0] & 0xffffu);
+    p[1] = uint16_t(w[0] >> 16);
+    p[2] = uint16_t(w[1] & 0xffffu);
+    p[3] = uint16_t(w[1] >> 16);
+  }
+}
+
+// Four consecutive state elements (the 4 key channels of one accumulator
+// entry), in the state format SF: 8 bytes (bf16, fp16) or 4 bytes (fp8).
+template <int SF, bool VEC>
+__device__ __forceinline__ f32x4 st4_load(const void* base, int64_t e) {
+  if constexpr (SF == kStateFp8) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(base) + e);
+    const f32x2 a = f8x2_lo(w), b = f8x2_hi(w);
+    return f32x4{a[0], a[1], b[0], b[1]};
+  } else {
+    const u32x2 w = gload4<VEC>(static_cast<const uint16_t*>(base) + e);
+    return f32x4{st_lo<SF>(w[0]), st_hi<SF>(w[0]), st_lo<SF>(w[1]), st_hi<SF>(w[1])};
+  }
+}
+template <int SF, bool VEC>
+__device__ __forceinline__ void st4_store(void* base, int64_t e, f32x4 a) {
+  if constexpr (SF == kStateFp8) {
+    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(base) + e) = pack_f8x4(a[0], a[1], a[2], a[3]);
+  } else {
+    gstore4<VEC>(static_cast<uint16_t*>(base) + e, u32x2{st_pack<SF>(a[0], a[1]), st_pack<SF>(a[2], a[3])});
+  }
+}
+
+// Raw token inputs of one lane: 8 channels of q, k, g, v and the beta logit.
+struct TokRaw {
+  u32x4 q, k, g, v;
+  uint16_t b;
+};
+
+template <bool VEC, bool GHEAD>
+__device__ __forceinline__ TokRaw load_tok(const PrefillParams& p, int64_t t, int h, int c0,
+                                           bool valid) {
+  TokRaw r;
+  if (valid) {
+    r.q = load8_raw<VEC>(p.q + t * p.q_tok_stride + h * D + c0);
+    r.k = load8_raw<VEC>(p.k + t * p.k_tok_stride + h * D + c0);
+    if constexpr (GHEAD) {  // one gate value per head, in all eight channel slots
+      const uint32_t gh = p.g[t * p.g_tok_stride + h];
+      r.g = u32x4{gh | (gh << 16), gh | (gh << 16), gh | (gh << 16), gh | (gh << 16)};
+    } else {
+      r.g = load8_raw<VEC>(p.g + t * p.g_tok_stride + h * D + c0);
+    }
+    r.v = load8_raw<VEC>(p.v + t * p.v_tok_stride + h * D + c0);
+    r.b = p.beta[t * p.beta_tok_stride + h];
+  } else {
+    r.q = r.k = r.g = r.v = u32x4{0u, 0u, 0u, 0u};
+    r.b = 0;
+  }
+  return r;
+}
+
+// First chunk slot of document i (i = n_docs gives the slot count).
+__device__ __forceinline__ int64_t doc_slot0(const int32_t* cu, int i) {
+  return int64_t(i) + (int64_t(cu[i]) >> 4);
+}
+
+// The document owning chunk slot sigma: the largest i in [0, n_docs] with
+// doc_slot0(i) <= sigma (doc_slot0 is strictly increasing and doc_slot0(0) = 0).
+// Every thread of the workgroup calls it; each step narrows the window
+// 256-fold with one load per thread.
+__device__ int find_doc(const int32_t* cu, int n_docs, int64_t sigma, int tid) {
+  int lo = 0;
+  int len = n_docs + 1;  // window [lo, lo + len), doc_slot0(lo) <= sigma
+  while (len > kThreads) {
+    const int stride = (len + kThreads - 1) / kThreads;
+    const int off = tid * stride;
+    const bool le = off < len && doc_slot0(cu, lo + off) <= sigma;
+    const int cnt = __syncthreads_count(le);
+    lo += (cnt - 1) * stride;
+    len = min(stride, n_docs + 1 - lo);
+  }
+  const bool le = tid < len && doc_slot0(cu, lo + tid) <= sigma;
+  return lo + __syncthreads_count(le) - 1;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Preparation: one 256-thread workgroup per (chunk slot, group of up to
+// kPrepHeads heads). Everything of the chunk that does not depend on the
+// state, written to the chunk record of each head; the next head's token
+// inputs are loaded while the current head is processed.
+constexpr int kPrepHeads = 4;
+
+// GK, the gate kind: kGatePrecomputed clear = raw gate logits, set = the
+// log-decay itself; kGatePerHead set = one gate value per head.
+template <bool VEC, int GK>
+__global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillParams p) {
+  constexpr bool GRAW = !(GK & kGatePrecomputed);
+  constexpr bool GHEAD = (GK & kGatePerHead) != 0;
+  extern __shared__ __align__(16) float psmem_raw[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g4 = lane >> 4;
+  const int n16 = lane & 15;
+  const int64_t sigma = blockIdx.x;
+  const int h0 = int(blockIdx.y) * kPrepHeads;
+  const int h1 = min(h0 + kPrepHeads, p.H);
+
+  const int doc = find_doc(p.cu_seqlens, p.n_docs, sigma, tid);
+  if (doc >= p.n_docs) return;
+  const int64_t t0 = p.cu_seqlens[doc];
+  const int64_t len = int64_t(p.cu_seqlens[doc + 1]) - t0;
+  const int64_t j = sigma - doc_slot0(p.cu_seqlens, doc);
+  if (j * C >= len) return;  // a slot between documents
+  const int32_t slot = p.state_indices[doc];
+  if (slot < 0 || int64_t(slot) >= p.num_slots) return;  // the chain writes zeros
+  const int64_t tc0 = t0 + j * C;
+  const int c = int(min<int64_t>(C, len - j * C));
+  PSmem s = pcarve(psmem_raw);
+
+  const int tt = tid >> 4;        // prologue: token of this lane
+  const int c0 = (tid & 15) * 8;  // prologue: 8 key / value channels of this lane
+  const bool valid = tt < c;
+  TokRaw raw = load_tok<VEC, GHEAD>(p, tc0 + tt, h0, c0, valid);
+
+  for (int h = h0; h < h1; ++h) {
+    // ---- token prologue -> q_hat, k_hat, g, v, beta (rows >= c are zeros)
+    {
+      const TokRaw cur = raw;
+      if (h + 1 < h1) raw = load_tok<VEC, GHEAD>(p, tc0 + tt, h + 1, c0, valid);
+      float neg_ea = 0.f;
+      float dtb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if constexpr (GRAW) {
+        neg_ea = -fexp(p.A_log[h]);
+        if constexpr (GHEAD) {
+          const float dh = p.dt_bias[h];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dtb[e] = dh;
+        } else {
+          load8_f32<VEC>(p.dt_bias + h * D + c0, dtb);
+        }
+      }
+      float q[8], k[8], gr[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        q[2 * e] = bf_lo(cur.q[e]);  q[2 * e + 1] = bf_hi(cur.q[e]);
+        k[2 * e] = bf_lo(cur.k[e]);  k[2 * e + 1] = bf_hi(cur.k[e]);
+        gr[2 * e] = bf_lo(cur.g[e]); gr[2 * e + 1] = bf_hi(cur.g[e]);
+      }
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sq = fmaf(q[e], q[e], sq);
+        sk = fmaf(k[e], k[e], sk);
+      }
+      sq = row16_sum(sq);
+      sk = row16_sum(sk);
+      const float rq = 1.0f / sqrtf(sq + 1e-6f);
+      const float rk = 1.0f / sqrtf(sk + 1e-6f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s.qh[tt * RS + c0 + e] = q[e] * rq;
+        s.kh[tt * RS + c0 + e] = k[e] * rk;
+        const float ge = GRAW ? fgate(gr[e] + dtb[e], neg_ea, p.lower_bound)
+                              : gate_given(gr[e], p.lower_bound);
+        s.gg[tt * RS + c0 + e] = valid ? ge : 0.f;
+      }
+      *reinterpret_cast<u32x4*>(s.vv + tt * VLD + c0) = cur.v;
+      if ((tid & 15) == 0) {
+        const float braw = bf1(cur.b);
+        const float be = (p.gate_mode & kBetaPresigmoid) ? braw : fsigmoid(braw);
+        s.beta[tt] = valid ? be : 0.f;
+      }
+    }
+    __syncthreads();
+
+    // ---- thread (c, half) owns key channel c = tid % 128 and tokens
+    // 8 half .. 8 half + 7: Gam prefix (every thread sums all 16 gates of its
+    // channel), the scaled rows for A and P as bf16 hi / lo pairs (MFMA
+    // operands, written over the fp32 rows they come from: hi in the first
+    // 128 bf16 of a row, lo in the next 128), the fp32 right-hand side of W,
+    // and the chain's bf16 operands exp(Gam) q_hat and exp(Gam_last - Gam) k_hat.
+    {
+      const int cc = tid & 127;
+      const int r0 = (tid >> 7) * 8;
+      float gam[C];
+      float acc_g = 0.f;
+#pragma unroll
+      for (int r = 0; r < C; ++r) {
+        acc_g += s.gg[r * RS + cc];
+        gam[r] = acc_g;
+      }
+      const float mid = 0.5f * acc_g;  // padded rows carry g = 0
+      const float em = fexp(mid);
+      float kq[8], qq[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        kq[i] = s.kh[(r0 + i) * RS + cc];
+        qq[i] = s.qh[(r0 + i) * RS + cc];
+      }
+      __syncthreads();  // every fp32 row and every gate is read before any is rewritten
+      if (r0 == 0) {
+        s.egl[cc] = fexp(acc_g);
+        s.em[cc] = em;
+      }
+      uint16_t* khp = reinterpret_cast<uint16_t*>(s.kh);
+      uint16_t* qhp = reinterpret_cast<uint16_t*>(s.qh);
+      uint16_t* kbp = reinterpret_cast<uint16_t*>(s.kb);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = r0 + i;
+        const float g_first = gam[i], g_second = gam[8 + i];  // both loaded: a select of
+        const float gr_ = r0 == 0 ? g_first : g_second;         // values, not of addresses
+        const float ea = fexp(gr_ - mid), eb = fexp(mid - gr_);
+        const float kb = kq[i] * eb;
+        uint16_t hi, lo;
+        split_bf16(qq[i] * ea, hi, lo);
+        qhp[r * 2 * RS + cc] = hi;
+        qhp[r * 2 * RS + D + cc] = lo;
+        s.kw[r * RS + cc] = kq[i] * ea;
+        split_bf16(kq[i] * ea, hi, lo);
+        khp[r * 2 * RS + cc] = hi;
+        khp[r * 2 * RS + D + cc] = lo;
+        split_bf16(kb, hi, lo);
+        kbp[r * 2 * RS + cc] = hi;
+        kbp[r * 2 * RS + D + cc] = lo;
+        s.qop[r * QLD + cc] = to_bf16(qq[i] * ea * em);
+        split_bf16(em * kb, hi, lo);  // exp(Gam_last - m) = exp(m)
+        s.ktop[r * D + cc] = hi;
+        s.ktop[C * D + r * D + cc] = lo;
+      }
+    }
+    __syncthreads();
+
+    // ---- A = (e^(Gam-m) k)(e^(m-Gam) k)^T on wave 0, P = (e^(Gam-m) q)(e^(m-Gam) k)^T on
+    // wave 1 (three hi/lo terms each, fragments read straight from the bf16
+    // pairs; one accumulator per term so the products do not wait on each other).
+    if (wave < 2) {
+      const uint16_t* left = reinterpret_cast<const uint16_t*>(wave == 0 ? s.kh : s.qh);
+      const uint16_t* right = reinterpret_cast<const uint16_t*>(s.kb);
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int off = n16 * 2 * RS + 32 * kt + 8 * g4;
+        const bf16x8 xh = *reinterpret_cast<const bf16x8*>(left + off);
+        const bf16x8 xl = *reinterpret_cast<const bf16x8*>(left + off + D);
+        const bf16x8 yh = *reinterpret_cast<const bf16x8*>(right + off);
+        const bf16x8 yl = *reinterpret_cast<const bf16x8*>(right + off + D);
+        a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yh, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yl, a1, 0, 0, 0);
+        a2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, yh, a2, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i, jj = n16;
+        const float a = a0[i] + (a1[i] + a2[i]);
+        if (wave == 0) s.am[r * C + jj] = jj < r ? a : 0.f;
+        else s.pop[r * C + jj] = to_bf16(jj <= r ? a : 0.f);
+      }
+    }
+    __syncthreads();
+
+    // ---- forward substitution. Threads 0..127: W (key channel c), stored as
+    // bf16 hi / lo; threads 128..255: U0 (value channel v).
+    {
+      const int cc = tid & 127;
+      // Right-looking: once x_j is known it is taken off every later row's
+      // remainder; each row still accumulates its terms in the order j = 0, 1, ...
+      float x[C];
+      if (tid < 128) {
+#pragma unroll
+        for (int r = 0; r < C; ++r) x[r] = s.kw[r * RS + cc];
+      } else {
+#pragma unroll
+        for (int r = 0; r < C; ++r) x[r] = bf1(s.vv[r * VLD + cc]);
+      }
+#pragma unroll
+      for (int jj = 0; jj < C; ++jj) {
+        x[jj] *= s.beta[jj];
+#pragma unroll
+        for (int r = jj + 1; r < C; ++r) x[r] = fmaf(-s.am[r * C + jj], x[jj], x[r]);
+      }
+      if (tid < 128) {
+        const float em = s.em[cc];
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+          uint16_t hi, lo;
+          split_bf16(x[r] * em, hi, lo);
+          s.wop[r * XLD + cc] = hi;
+          s.wop[C * XLD + r * XLD + cc] = lo;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < C; ++r) s.u0[r * RS + cc] = x[r];
+      }
+    }
+    __syncthreads();
+
+    // ---- the chunk record, one 16-byte unit per thread and round
+    u32x4* rec = reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.workspace) +
+                                          (sigma * p.H + h) * int64_t(kRecBytes));
+#pragma unroll
+    for (int rd = 0; rd < kRecRounds; ++rd) {
+      const int u = tid + kThreads * rd;
+      u32x4 w;
+      if (u < kRecQ / 16) {  // W
+        const int kt = u >> 7, part = (u >> 6) & 1, l = u & 63;
+        const uint16_t* row = s.wop + part * C * XLD + (l & 15) * XLD + 32 * kt + 4 * (l >> 4);
+        w = lds_2runs(row, row + 16);
+      } else if (u < kRecKT / 16) {  // Q
+        const int kt = (u - kRecQ / 16) >> 6, l = u & 63;
+        const uint16_t* row = s.qop + (l & 15) * QLD + 32 * kt + 4 * (l >> 4);
+        w = lds_2runs(row, row + 16);
+      } else if (u < kRecU0 / 16) {  // KT: tokens 4g4 .. 4g4+3 of key channel 16mt + n16
+        const int mt = (u - kRecKT / 16) >> 6, l = u & 63;
+        const uint16_t* col = s.ktop + 4 * (l >> 4) * D + 16 * mt + (l & 15);
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          const uint16_t* cp = col + part * C * D;
+          w[2 * part] = uint32_t(cp[0]) | (uint32_t(cp[D]) << 16);
+          w[2 * part + 1] = uint32_t(cp[2 * D]) | (uint32_t(cp[3 * D]) << 16);
+        }
+      } else if (u < kRecP / 16) {  // U0
+        const int vt = (u - kRecU0 / 16) >> 6, l = u & 63;
+        const float* col = s.u0 + 4 * (l >> 4) * RS + 16 * vt + (l & 15);
+        w = u32x4{__float_as_uint(col[0]), __float_as_uint(col[RS]),
+                  __float_as_uint(col[2 * RS]), __float_as_uint(col[3 * RS])};
+      } else if (u < kRecEG / 16) {  // P: lanes 2q and 2q+1
+        const int l0 = 2 * (u - kRecP / 16);
+        w = lds_2runs(s.pop + (l0 & 15) * C + 4 * (l0 >> 4),
+                      s.pop + ((l0 + 1) & 15) * C + 4 * ((l0 + 1) >> 4));
+      } else if (u < kRecUnits) {  // EG
+        w = *reinterpret_cast<const u32x4*>(s.egl + 4 * (u - kRecEG / 16));
+      } else {
+        continue;
+      }
+      rec[u] = w;
+    }
+    __syncthreads();  // the record is read out before the next head rewrites the arrays
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Hand-off to the verify ring: one 256-thread workgroup per (document, head),
+// run between the preparation and the chain when ring_tail > 0. In a
+// document's last chunk (c tokens, of which the last `tail` are handed off,
+// pe = c - tail) only tokens 0 .. pe-1 may enter the state the chain passes
+// on, so this kernel rewrites that chunk record's state-update operands,
+//   K~_r = exp(Gam_e - Gam_r) k_hat_r (r < pe, else 0),  EG = exp(Gam_e),
+// with Gam_e = Gam_{pe-1} (0 when pe = 0), and writes the tail tokens' ring
+// rows: k_hat (bf16) and G, the log-decay summed from the first tail token.
+// The chain then leaves S after pe tokens, and writes the tail's u rows.
+// k_hat and the gate are computed as the preparation computes them.
+template <bool VEC, int GK>
+__global__ __launch_bounds__(kThreads) void handoff_kernel(PrefillParams p) {
+  constexpr bool GRAW = !(GK & kGatePrecomputed);
+  constexpr bool GHEAD = (GK & kGatePerHead) != 0;
+  __shared__ float kh[C][D];
+  __shared__ float gg[C][D];
+  const int tid = threadIdx.x;
+  const int doc = blockIdx.x;
+  const int h = blockIdx.y;
+  const int64_t t0 = p.cu_seqlens[doc];
+  const int64_t len = int64_t(p.cu_seqlens[doc + 1]) - t0;
+  const int32_t slot = p.state_indices[doc];
+  const int32_t rbase = p.cache_base[doc];
+  if (len == 0 || slot < 0 || int64_t(slot) >= p.num_slots || rbase < 0 ||
+      rbase >= p.ring_rows)
+    return;  // nothing to hand off, or an inactive document
+  const int nchunks = int((len + C - 1) / C);
+  const int c = int(len - int64_t(nchunks - 1) * C);
+  const int tail = min(p.ring_tail, c);
+  const int pe = c - tail;
+
+  // ---- k_hat and g of the chunk's tokens (rows >= c: zeros)
+  {
+    const int tt = tid >> 4;
+    const int c0 = (tid & 15) * 8;
+    const bool valid = tt < c;
+    const TokRaw raw =
+        load_tok<VEC, GHEAD>(p, t0 + int64_t(nchunks - 1) * C + tt, h, c0, valid);
+    float neg_ea = 0.f;
+    float dtb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if constexpr (GRAW) {
+      neg_ea = -fexp(p.A_log[h]);
+      if constexpr (GHEAD) {
+        const float dh = p.dt_bias[h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dtb[e] = dh;
+      } else {
+        load8_f32<VEC>(p.dt_bias + h * D + c0, dtb);
+      }
+    }
+    float k[8], gr[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      k[2 * e] = bf_lo(raw.k[e]);  k[2 * e + 1] = bf_hi(raw.k[e]);
+      gr[2 * e] = bf_lo(raw.g[e]); gr[2 * e + 1] = bf_hi(raw.g[e]);
+    }
+    float sk = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sk = fmaf(k[e], k[e], sk);
+    sk = row16_sum(sk);
+    const float rk = 1.0f / sqrtf(sk + 1e-6f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kh[tt][c0 + e] = k[e] * rk;
+      const float ge = GRAW ? fgate(gr[e] + dtb[e], neg_ea, p.lower_bound)
+                            : gate_given(gr[e], p.lower_bound);
+      gg[tt][c0 + e] = valid ? ge : 0.f;
+    }
+  }
+  __syncthreads();
+  if (tid >= D) return;
+
+  // ---- thread cc: one key channel
+  const int cc = tid;
+  float gam_e = 0.f, acc = 0.f;
+  for (int r = 0; r < pe; ++r) {
+    acc += gg[r][cc];
+    gam_e = acc;
+  }
+  uint8_t* rec = static_cast<uint8_t*>(p.workspace) +
+                 ((doc_slot0(p.cu_seqlens, doc) + nchunks - 1) * p.H + h) * int64_t(kRecBytes);
+  // KT unit (mt, lane = n16 + 16 g4): tokens 4 g4 .. 4 g4 + 3 of key channel
+  // 16 mt + n16, four bf16 hi then four bf16 lo
+  const int mt = cc >> 4, n16 = cc & 15;
+  float gam = 0.f;
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g4 + i;
+      gam += gg[r][cc];
+      const float x = r < pe ? fexp(gam_e - gam) * kh[r][cc] : 0.f;
+      split_bf16(x, hi[i], lo[i]);
+    }
+    const u32x4 w = {uint32_t(hi[0]) | (uint32_t(hi[1]) << 16),
+                     uint32_t(hi[2]) | (uint32_t(hi[3]) << 16),
+                     uint32_t(lo[0]) | (uint32_t(lo[1]) << 16),
+                     uint32_t(lo[2]) | (uint32_t(lo[3]) << 16)};
+    *reinterpret_cast<u32x4*>(rec + kRecKT + (mt * 64 + n16 + 16 * g4) * 16) = w;
+  }
+  reinterpret_cast<float*>(rec + kRecEG)[cc] = fexp(gam_e);
+
+  // ---- ring rows of the tail tokens
+  const int64_t ring0 = (int64_t(slot) * p.H + h) * p.ring_rows;
+  float gt = 0.f;
+  for (int r = pe; r < c; ++r) {
+    gt += gg[r][cc];
+    const int64_t row = ring0 + (rbase + r - pe) % p.ring_rows;
+    p.k_cache[row * D + cc] = to_bf16(kh[r][cc]);
+    p.g_cache[row * D + cc] = gt;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chain: one 512-thread workgroup per (document, head), documents longest
+// first. Wave w keeps value channels 16w .. 16w+15 of the fp32 state in
+// registers (two waves per SIMD, so one wave's MFMA and LDS latencies overlap
+// the other's arithmetic). Chunk records move HBM -> registers one chunk
+// ahead of use and registers -> LDS (double buffer) one chunk ahead, so a
+// chunk's operands are in LDS when it starts and the next record's loads
+// overlap its arithmetic.
+//
+// With few chains (documents x heads below the CU count) each chain is split
+// by value channels over VS = 2 workgroups of 4 waves on different CUs: the
+// value channels of the state evolve independently, and a CU then holds one
+// wave per SIMD instead of two, so a chunk's VALU and MFMA issue per SIMD
+// halves. Each part stages the record's shared operands (W, Q, K~, P,
+// exp(Gam_c)) and only its own U0 tiles.
+template <int VS>
+struct ChainShape {
+  static constexpr int kThreads = 512 / VS;
+  static constexpr int kWaves = 8 / VS;                     // value tiles of 16 channels
+  static constexpr int kShared = kRecU0 / 16;               // W, Q, K~ units
+  static constexpr int kOwnU0 = kWaves * 64;                // this part's U0 units
+  static constexpr int kTail = kRecUnits - kRecP / 16;      // P, exp(Gam_c) units
+  static constexpr int kUnits = kShared + kOwnU0 + kTail;   // units staged per chunk
+  static constexpr int kRounds = (kUnits + kThreads - 1) / kThreads;
+  static_assert(kUnits > (kRounds - 1) * kThreads, "every round has work");
+  // record unit of staged unit i (< kUnits) of part `part`
+  __device__ static int unit(int i, int part) {
+    if (i < kShared) return i;
+    if (i < kShared + kOwnU0) return kRecU0 / 16 + part * kOwnU0 + (i - kShared);
+    return kRecP / 16 + (i - kShared - kOwnU0);
+  }
+};
+static_assert(ChainShape<1>::kUnits == kRecUnits, "the whole record");
+
+// SF: the element format of the pool (initial and final states) and the
+// checkpoints (kStateBf16, kStateFp16, kStateFp8). VS: workgroups per chain.
+template <bool VEC, int SF, int VS>
+__global__ __launch_bounds__(ChainShape<VS>::kThreads) void chain_kernel(PrefillParams p,
+                                                                        DocOrder ord) {
+  using Shape = ChainShape<VS>;
+  constexpr int kChainThreads = Shape::kThreads;
+  constexpr int kChainRounds = Shape::kRounds;
+  __shared__ __align__(16) uint8_t rbuf[2][kRecBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g4 = lane >> 4;
+  const int n16 = lane & 15;
+  const int part = int(blockIdx.x % VS);
+  const int vt = part * Shape::kWaves + wave;  // value tile of this wave
+  const int v = 16 * vt + n16;                 // value channel of this lane
+  const int h = int((blockIdx.x / VS) % p.H);
+  const int rank = int(blockIdx.x / VS / p.H);
+  const int doc = ord.n > 0 ? ord.doc[rank] : rank;
+  const int64_t t0 = p.cu_seqlens[doc];
+  const int64_t len = int64_t(p.cu_seqlens[doc + 1]) - t0;
+  const int32_t slot = p.state_indices[doc];
+  const int32_t rbase = p.ring_tail > 0 ? p.cache_base[doc] : 0;
+  const bool active = slot >= 0 && int64_t(slot) < p.num_slots && rbase >= 0 &&
+                      (p.ring_tail == 0 || rbase < p.ring_rows);
+
+  constexpr int kPartCh = D / VS;  // value channels (state rows) of this part
+  if (!active) {  // zero outputs, no state access
+    for (int64_t e = tid; e < len * kPartCh; e += kChainThreads)
+      p.out[(t0 + e / kPartCh) * p.out_tok_stride + h * D + part * kPartCh + (e % kPartCh)] = 0;
+    return;
+  }
+  static_assert(VEC || SF == kStateBf16, "fp16 and fp8 states use the vectorised layout");
+  const int64_t se = int64_t(slot) * p.slot_stride + int64_t(h) * HEAD_ELEMS;  // element offset
+  if (len == 0) {  // final state = initial state: untouched, or zeros without one
+    if (!p.use_initial_state) {  // this part's state rows
+      uint16_t* z = reinterpret_cast<uint16_t*>(
+          static_cast<uint8_t*>(p.state_pool) + (se + part * kPartCh * D) * kStateBytes<SF>);
+      for (int e = tid; e < kPartCh * D * kStateBytes<SF> / 2; e += kChainThreads) z[e] = 0;
+    }
+    return;
+  }
+
+  const int nchunks = int((len + C - 1) / C);
+  // hand-off: the last chunk's last `tail` tokens go to the ring; the state
+  // passed on (checkpoints, final) covers the first `kept` tokens
+  const int c_last = int(len - int64_t(nchunks - 1) * C);
+  const int tail = p.ring_tail > 0 ? min(p.ring_tail, c_last) : 0;
+  const int64_t kept = len - tail;
+  const int64_t sigma0 = doc_slot0(p.cu_seqlens, doc);
+  // first checkpoint row of this document (checkpoints after every
+  // ckpt_interval tokens, a multiple of the chunk)
+  const int64_t ckpt_row0 = p.ckpt ? p.ckpt_starts[doc] : 0;
+  const int ckpt_every = p.ckpt_interval / C;
+  const uint8_t* ws = static_cast<const uint8_t*>(p.workspace);
+  auto rec_of = [&](int ch) {
+    return reinterpret_cast<const u32x4*>(ws + ((sigma0 + ch) * p.H + h) * int64_t(kRecBytes));
+  };
+  // Thread tid moves staged units tid + kChainThreads rd (to the record's
+  // own offsets in LDS); the units past the staged set in the last round load
+  // a staged unit again (a fixed load count per chunk) and are not stored.
+  u32x4 pre[kChainRounds];
+  auto load_rec = [&](int ch) {
+    const u32x4* r = rec_of(ch);
+#pragma unroll
+    for (int rd = 0; rd < kChainRounds; ++rd) {
+      const int i = tid + kChainThreads * rd;
+      pre[rd] = __builtin_nontemporal_load(
+          r + Shape::unit(i < Shape::kUnits ? i : i - Shape::kUnits, part));
+    }
+  };
+  auto store_rec = [&](int b) {
+    u32x4* d = reinterpret_cast<u32x4*>(&rbuf[b][0]);
+#pragma unroll
+    for (int rd = 0; rd < kChainRounds; ++rd) {
+      const int i = tid + kChainThreads * rd;
+      if (rd < kChainRounds - 1 || i < Shape::kUnits) d[Shape::unit(i, part)] = pre[rd];
+    }
+  };
+
+  load_rec(0);
+
+  // ---- initial state into the accumulator layout (all 8 loads issued
+  // before any is waited for)
+  f32x4 acc[8];
+  if (p.use_initial_state) {
+    if constexpr (SF == kStateFp8) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        acc[mt] = st4_load<SF, VEC>(p.state_pool, se + v * D + 16 * mt + 4 * g4);
+    } else {
+      const uint16_t* sp = static_cast<const uint16_t*>(p.state_pool) + se;
+      u32x2 w[8];
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) w[mt] = gload4<VEC>(sp + v * D + 16 * mt + 4 * g4);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        acc[mt] = f32x4{st_lo<SF>(w[mt][0]), st_hi<SF>(w[mt][0]), st_lo<SF>(w[mt][1]),
+                        st_hi<SF>(w[mt][1])};
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  store_rec(0);
+  load_rec(min(1, nchunks - 1));
+  __syncthreads();
+
+  const int ots32 = static_cast<int>(p.out_tok_stride);  // host-checked to fit a buffer range
+  f32x4 u_last = {0.f, 0.f, 0.f, 0.f};  // U of the last chunk (rows 4 g4 + i)
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int64_t tc0 = t0 + int64_t(ch) * C;
+    const int c = int(min<int64_t>(C, len - int64_t(ch) * C));
+    const uint8_t* R = &rbuf[ch & 1][0];
+
+    // Output rows of this chunk as a buffer range of exactly c rows: a store
+    // to a padded row (r >= c) is out of range and discarded, so the number
+    // of store instructions does not depend on c.
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        p.out + tc0 * p.out_tok_stride + h * D, 0,
+        static_cast<int>(((c - 1) * p.out_tok_stride + D) * 2), kBufferWord3);
+    // W S^T in three hi/lo terms (one accumulator each, so the products do
+    // not wait on each other) and (e^Gam q) S^T in one
+    f32x4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = y0, y2 = y0, yq = y0;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const bf16x8 whi = *reinterpret_cast<const bf16x8*>(R + kRecW + ((2 * kt) * 64 + lane) * 16);
+      const bf16x8 wlo =
+          *reinterpret_cast<const bf16x8*>(R + kRecW + ((2 * kt + 1) * 64 + lane) * 16);
+      const bf16x8 qhi = *reinterpret_cast<const bf16x8*>(R + kRecQ + (kt * 64 + lane) * 16);
+      const f32x4 s0 = acc[2 * kt], s1 = acc[2 * kt + 1];
+      const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      bf16x8 shi, slo;
+      split8(sv, shi, slo);
+      y0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, shi, y0, 0, 0, 0);
+      y1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, slo, y1, 0, 0, 0);
+      y2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, shi, y2, 0, 0, 0);
+      yq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi, shi, yq, 0, 0, 0);
+    }
+    // U = U0 - W S^T (accumulator layout: rows 4*g4 + i, value channel of the lane)
+    const f32x4 u0 = *reinterpret_cast<const f32x4*>(R + kRecU0 + (vt * 64 + lane) * 16);
+    const f32x4 uf = u0 - (y0 + (y1 + y2));
+    s16x4 uhi, ulo;
+    split4(uf, uhi, ulo);
+    u_last = uf;
+    // O = scale ((e^Gam q) S^T + P U); rows r >= c fall outside the buffer
+    // range and are dropped by the store itself
+    const s16x4 pfr = *reinterpret_cast<const s16x4*>(R + kRecP + lane * 8);
+    const f32x4 o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pfr, uhi, yq, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g4 + i;
+      __builtin_amdgcn_raw_buffer_store_b16(to_bf16(p.scale * o[i]), orsrc, (r * ots32 + v) * 2,
+                                            0, kStoreNontemporal);
+    }
+    // S = S diag(e^Gam_last) + U^T K~  (contraction over the chunk's tokens)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const u32x4 kk = *reinterpret_cast<const u32x4*>(R + kRecKT + (mt * 64 + lane) * 16);
+      const s16x4 khi = __builtin_bit_cast(s16x4, u32x2{kk[0], kk[1]});
+      const s16x4 klo = __builtin_bit_cast(s16x4, u32x2{kk[2], kk[3]});
+      const f32x4 e4 = *reinterpret_cast<const f32x4*>(R + kRecEG + (16 * mt + 4 * g4) * 4);
+      f32x4 a = acc[mt] * e4;
+      a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(khi, uhi, a, 0, 0, 0);
+      a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(khi, ulo, a, 0, 0, 0);
+      a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(klo, uhi, a, 0, 0, 0);
+      acc[mt] = a;
+    }
+    // record ch+1 (its loads were issued a chunk ago) into the other buffer,
+    // last read before the previous barrier; then the loads of record ch+2
+    store_rec((ch + 1) & 1);
+    load_rec(min(ch + 2, nchunks - 1));
+    // intermediate checkpoint after this chunk, after the record loads
+    if (p.ckpt && (ch + 1) % ckpt_every == 0 && int64_t(ch + 1) * C <= kept) {
+      const int64_t row = ckpt_row0 + (ch + 1) / ckpt_every - 1;
+      if (row >= 0 && row < p.ckpt_rows) {
+        const int64_t ce = (row * p.H + h) * int64_t(HEAD_ELEMS);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+          st4_store<SF, VEC>(p.ckpt, ce + v * D + 16 * mt + 4 * g4, acc[mt]);
+      }
+    }
+    __syncthreads();  // this chunk's buffer is read; the next one is written
+  }
+
+  if (tail > 0) {  // hand-off: ring rows of the tail tokens receive u (bf16)
+    uint16_t* ur = p.u_cache + (int64_t(slot) * p.H + h) * p.ring_rows * int64_t(D) + v;
+    const int pe = c_last - tail;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g4 + i;
+      if (r >= pe && r < c_last)
+        ur[int64_t((rbase + r - pe) % p.ring_rows) * D] = to_bf16(u_last[i]);
+    }
+  }
+
+  // ---- final state (the state after the first `kept` tokens)
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+    st4_store<SF, VEC>(p.state_pool, se + v * D + 16 * mt + 4 * g4, acc[mt]);
+}
+
+size_t prefill_split_workspace_bytes(int32_t n_docs, int64_t total_tokens, int32_t H) {
+  if (n_docs <= 0 || total_tokens <= 0 || H <= 0) return 0;
+  return size_t(int64_t(n_docs) + (total_tokens >> 4)) * size_t(H) * size_t(kRecBytes);
+}
+
+hipError_t launch_prefill_split(const PrefillParams& p, const int32_t* cu_host, bool vec,
+                                hipStream_t stream) {
+  const int64_t blocks = int64_t(p.n_docs) * p.H;
+  if (blocks == 0) return hipSuccess;
+  if (2 * blocks > 0x7fffffff || p.H > 65535) return hipErrorInvalidValue;
+  const int64_t slots = int64_t(p.n_docs) + (p.total_tokens >> 4);
+  if (slots > 0x7fffffff) return hipErrorInvalidValue;
+  // Longest documents first: their chains bound the makespan.
+  DocOrder ord;
+  ord.n = 0;
+  if (p.n_docs <= kMaxOrderedDocs) {
+    ord.n = p.n_docs;
+    for (int d = 0; d < p.n_docs; ++d) ord.doc[d] = d;
+    for (int i = 1; i < p.n_docs; ++i) {  // stable insertion sort, descending length
+      const int d = ord.doc[i];
+      const int32_t ld = cu_host[d + 1] - cu_host[d];
+      int j = i - 1;
+      while (j >= 0 && cu_host[ord.doc[j] + 1] - cu_host[ord.doc[j]] < ld) {
+        ord.doc[j + 1] = ord.doc[j];
+        --j;
+      }
+      ord.doc[j + 1] = d;
+    }
+  }
+  static const hipError_t attr = [] {
+    const void* fns[] = {reinterpret_cast<const void*>(&prep_kernel<true, 0>),
+                         reinterpret_cast<const void*>(&prep_kernel<true, 1>),
+                         reinterpret_cast<const void*>(&prep_kernel<true, 4>),
+                         reinterpret_cast<const void*>(&prep_kernel<true, 5>),
+                         reinterpret_cast<const void*>(&prep_kernel<false, 0>),
+                         reinterpret_cast<const void*>(&prep_kernel<false, 1>),
+                         reinterpret_cast<const void*>(&prep_kernel<false, 4>),
+                         reinterpret_cast<const void*>(&prep_kernel<false, 5>)};
+    for (const void* f : fns) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               static_cast<int>(kPrepLds));
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }();
+  if (attr != hipSuccess) return attr;
+  if (p.total_tokens > 0) {
+    dim3 pgrid(static_cast<unsigned>(slots),
+               static_cast<unsigned>((p.H + kPrepHeads - 1) / kPrepHeads)),
+        block(kThreads);
+    const int gk = p.gate_mode & kGateKindMask;
+#define KDA_PREP_LAUNCH(V)                                                                    \
+  do {                                                                                        \
+    switch (gk) {                                                                             \
+      case 0: hipLaunchKernelGGL((prep_kernel<V, 0>), pgrid, block, kPrepLds, stream, p); break; \
+      case 1: hipLaunchKernelGGL((prep_kernel<V, 1>), pgrid, block, kPrepLds, stream, p); break; \
+      case 4: hipLaunchKernelGGL((prep_kernel<V, 4>), pgrid, block, kPrepLds, stream, p); break; \
+      default: hipLaunchKernelGGL((prep_kernel<V, 5>), pgrid, block, kPrepLds, stream, p);      \
+    }                                                                                         \
+  } while (0)
+    if (vec) KDA_PREP_LAUNCH(true);
+    else KDA_PREP_LAUNCH(false);
+#undef KDA_PREP_LAUNCH
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.ring_tail > 0) {
+    dim3 hgrid(static_cast<unsigned>(p.n_docs), static_cast<unsigned>(p.H)), hblock(kThreads);
+    const int gk = p.gate_mode & kGateKindMask;
+#define KDA_HANDOFF_LAUNCH(V)                                                                  \
+  do {                                                                                         \
+    switch (gk) {                                                                              \
+      case 0: hipLaunchKernelGGL((handoff_kernel<V, 0>), hgrid, hblock, 0, stream, p); break; \
+      case 1: hipLaunchKernelGGL((handoff_kernel<V, 1>), hgrid, hblock, 0, stream, p); break; \
+      case 4: hipLaunchKernelGGL((handoff_kernel<V, 4>), hgrid, hblock, 0, stream, p); break; \
+      default: hipLaunchKernelGGL((handoff_kernel<V, 5>), hgrid, hblock, 0, stream, p);       \
+    }                                                                                          \
+  } while (0)
+    if (vec) KDA_HANDOFF_LAUNCH(true);
+    else KDA_HANDOFF_LAUNCH(false);
+#undef KDA_HANDOFF_LAUNCH
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // Fewer chains than CUs (always the case on this path): two workgroups per
+  // chain, by value channels.
+  const bool split = blocks < kFusedMinChains;
+  // fp16 and fp8 states run on the vectorised path only (the host requires it)
+  if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
+#define KDA_CHAIN_LAUNCH(V, S)                                                              \
+  do {                                                                                      \
+    if (split)                                                                              \
+      hipLaunchKernelGGL((chain_kernel<V, S, 2>), dim3(static_cast<unsigned>(2 * blocks)),  \
+                         dim3(ChainShape<2>::kThreads), 0, stream, p, ord);                 \
+    else                                                                                    \
+      hipLaunchKernelGGL((chain_kernel<V, S, 1>), dim3(static_cast<unsigned>(blocks)),      \
+                         dim3(ChainShape<1>::kThreads), 0, stream, p, ord);                 \
+  } while (0)
+  if (p.state_fmt == kStateFp16) KDA_CHAIN_LAUNCH(true, kStateFp16);
+  else if (p.state_fmt == kStateFp8) KDA_CHAIN_LAUNCH(true, kStateFp8);
+  else if (vec) KDA_CHAIN_LAUNCH(true, kStateBf16);
+  else KDA_CHAIN_LAUNCH(false, kStateBf16);
+#undef KDA_CHAIN_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -160,10 +160,14 @@ def test_verify_host_validation(lib):
 
 def test_prefill_workspace_and_validation(lib):
     P = ctypes.c_void_p
-    # one 29,696-byte chunk record per (chunk slot, head); chunk slots number
-    # fewer than n_docs + floor(total_tokens / 16)
+    # calls with at least 256 (document, head) chains run the fused kernel and
+    # need no workspace; with fewer, the two-stage form keeps one 29,696-byte
+    # chunk record per (chunk slot, head), and chunk slots number fewer than
+    # n_docs + floor(total_tokens / 16)
     rec = 29696
-    assert lib.kda_prefill_workspace_size(4, 13888, 64, 128, 128) == (4 + 868) * 64 * rec
+    assert lib.kda_prefill_workspace_size(4, 13888, 64, 128, 128) == 0
+    assert lib.kda_prefill_workspace_size(14, 16384, 64, 128, 128) == 0
+    assert lib.kda_prefill_workspace_size(3, 13888, 64, 128, 128) == (3 + 868) * 64 * rec
     assert lib.kda_prefill_workspace_size(14, 16384, 12, 128, 128) == (14 + 1024) * 12 * rec
     assert lib.kda_prefill_workspace_size(3, 0, 12, 128, 128) == 0
     assert lib.kda_prefill_workspace_size(4, 13888, 64, 64, 128) == 0

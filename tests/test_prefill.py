@@ -11,7 +11,8 @@ import pytest
 
 from gated_delta_rule_step_amd import synth
 from tests.helpers import (HD, OUT_NORM_PREFILL, bits, check_gcache, check_out, check_pool,
-                           check_state, dev, dev_bf16, f32, pool_dev, pool_vals)
+                           check_state, dev, dev_bf16, f32, normwise_error, pool_dev, pool_vals,
+                           report_accuracy)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -24,13 +25,23 @@ def _kda():
 
 def run_prefill(case, pool=None, packed=False, use_initial_state=None, lower_bound=None,
                 checkpoints=None, ckpt_starts=None, ckpt_interval=16, ring=None, cache_base=None,
-                ring_tail=0):
-    gm = case.get("gate_mode", 0)
+                ring_tail=0, misaligned=False):
     """Launch kda_prefill_varlen on a case. packed: q/k/v are strided views of
-    one [Ttot, 3*H*128] buffer and out is a view with a padded row."""
+    one [Ttot, 3*H*128] buffer and out is a view with a padded row. misaligned:
+    q/k/v/out start one element into rows of W + 1 elements (2-byte aligned
+    bases, odd strides: the scalar path)."""
+    gm = case.get("gate_mode", 0)
     H, Ttot = case["H"], case["Ttot"]
     W = H * HD
-    if packed:
+    if misaligned:
+        def view(a):
+            buf = torch.full((Ttot, W + 1), float("nan"), dtype=torch.bfloat16, device="cuda")
+            if a is not None:
+                buf[:, 1:] = dev_bf16(a.reshape(Ttot, W))
+            return buf[:, 1:]
+        q, k, v = (view(case[n]) for n in ("q", "k", "v"))
+        out = view(None)
+    elif packed:
         qkv = np.concatenate([case["q"].reshape(Ttot, W), case["k"].reshape(Ttot, W),
                               case["v"].reshape(Ttot, W)], axis=1)
         qkv_d = dev_bf16(qkv)
@@ -121,25 +132,43 @@ def check_prefill(orc, case, pool_dev, out_dev, heads=None, use_initial_state=No
 
 SMALL_DOCS = (1, 15, 16, 17, 0, 33, 50, 2, 64, 31)
 
+# The library runs the fused 64-token kernel when a call has at least 256
+# (document, head) chains and the two-stage form (16-token preparation kernel,
+# then the chain) below that; the small cases run on both, the "fused" variant
+# with enough heads.
+PATHS = ["split", "fused"]
+FUSED_MIN_CHAINS = 256
 
-@pytest.mark.parametrize("H", [1, 3])
-def test_small_docs_ragged(orc, H):
+
+def heads_for(path, n_docs, H_split):
+    if path == "split":
+        assert n_docs * H_split < FUSED_MIN_CHAINS
+        return H_split
+    return max(H_split, -(-FUSED_MIN_CHAINS // max(n_docs, 1)))
+
+
+@pytest.mark.parametrize("path,H0", [("split", 1), ("split", 3), ("fused", 3)])
+def test_small_docs_ragged(orc, path, H0):
+    H = heads_for(path, len(SMALL_DOCS), H0)
     case = synth.prefill_case(SMALL_DOCS, H=H, seed=synth.seed_for(4, H, 1))
     pool, out = run_prefill(case)
     check_prefill(orc, case, pool, out)
 
 
-def test_single_token_doc(orc):
-    """One token, one head: the prefill equals one decode step."""
-    case = synth.prefill_case((1,), H=1, seed=synth.seed_for(4, 1, 2))
+@pytest.mark.parametrize("path", PATHS)
+def test_single_token_doc(orc, path):
+    """One token: the prefill equals one decode step."""
+    H = heads_for(path, 1, 1)
+    case = synth.prefill_case((1,), H=H, seed=synth.seed_for(4, 1, 2))
     pool, out = run_prefill(case)
     check_prefill(orc, case, pool, out)
 
 
-def test_no_initial_state(orc):
+@pytest.mark.parametrize("path", PATHS)
+def test_no_initial_state(orc, path):
     """use_initial_state = 0: chains start from zeros; a zero-length document
     leaves a zero state in its slot."""
-    case = synth.prefill_case((20, 0, 37, 16), H=2, seed=synth.seed_for(4, 2, 3),
+    case = synth.prefill_case((20, 0, 37, 16), H=heads_for(path, 4, 2), seed=synth.seed_for(4, 2, 3),
                               use_initial_state=False)
     pool, out = run_prefill(case)
     check_prefill(orc, case, pool, out)
@@ -147,9 +176,10 @@ def test_no_initial_state(orc):
     assert np.all(bits(pool)[z] == 0), "zero-length document without initial state: zeros"
 
 
-def test_zero_length_keeps_state(orc):
+@pytest.mark.parametrize("path", PATHS)
+def test_zero_length_keeps_state(orc, path):
     """use_initial_state = 1: a zero-length document leaves its slot bitwise."""
-    case = synth.prefill_case((0, 5, 0), H=2, seed=synth.seed_for(4, 2, 4))
+    case = synth.prefill_case((0, 5, 0), H=heads_for(path, 3, 2), seed=synth.seed_for(4, 2, 4))
     pool, out = run_prefill(case)
     check_prefill(orc, case, pool, out)
     for d in (0, 2):
@@ -157,24 +187,36 @@ def test_zero_length_keeps_state(orc):
         assert np.array_equal(bits(pool)[s], case["pool"][s])
 
 
-def test_inactive_docs(orc):
+@pytest.mark.parametrize("path", PATHS)
+def test_inactive_docs(orc, path):
     """Documents whose slot is -1 or >= N: zero outputs, pool untouched."""
-    case = synth.prefill_case((18, 40, 7, 23), H=2, seed=synth.seed_for(4, 2, 5),
+    case = synth.prefill_case((18, 40, 7, 23), H=heads_for(path, 4, 2), seed=synth.seed_for(4, 2, 5),
                               inactive_docs=(1,))
     case["idx"][3] = case["N"] + 5
     pool, out = run_prefill(case)
     check_prefill(orc, case, pool, out)
 
 
-def test_packed_views_and_padded_out(orc):
+@pytest.mark.parametrize("path", PATHS)
+def test_packed_views_and_padded_out(orc, path):
     """q / k / v as strided views of one packed row, out with a padded row."""
-    case = synth.prefill_case((29, 16, 3), H=2, seed=synth.seed_for(4, 2, 6))
+    case = synth.prefill_case((29, 16, 3, 130), H=heads_for(path, 4, 2), seed=synth.seed_for(4, 2, 6))
     pool, out = run_prefill(case, packed=True)
     check_prefill(orc, case, pool, out)
 
 
+@pytest.mark.parametrize("path", PATHS)
+def test_misaligned_views(orc, path):
+    """Unaligned q / k / v / out bases and odd token strides: the scalar-load
+    form of each kernel, over ragged documents with checkpoints."""
+    case = synth.prefill_case(SMALL_DOCS, H=heads_for(path, 10, 2), seed=synth.seed_for(4, 2, 60))
+    counts = np.diff(case["cu_seqlens"]) // 16
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
+    _ckpt_roundtrip(orc, case, 16, starts, int(counts.sum()), misaligned=True)
+
+
 def test_many_docs_natural_order(orc):
-    """More documents than the launch orders by length (300)."""
+    """More documents than the launch orders by length (300; the fused kernel)."""
     rng = np.random.Generator(np.random.PCG64(synth.seed_for(4, 1, 7)))
     lens = tuple(int(x) for x in rng.integers(0, 24, size=300))
     case = synth.prefill_case(lens, H=1, seed=synth.seed_for(4, 1, 8))
@@ -182,19 +224,21 @@ def test_many_docs_natural_order(orc):
     check_prefill(orc, case, pool, out)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("gate_mode", [1, 2, 3])
-def test_precomputed_gate_conventions(orc, gate_mode):
+def test_precomputed_gate_conventions(orc, gate_mode, path):
     """The pre-computed gate and / or beta convention over ragged documents."""
-    case = synth.prefill_case(SMALL_DOCS, H=3, seed=synth.seed_for(4, 3, 12))
+    case = synth.prefill_case(SMALL_DOCS, H=heads_for(path, 10, 3), seed=synth.seed_for(4, 3, 12))
     case = synth.precomputed_gate(case, gate_mode, synth.seed_for(4, 3, 100 + gate_mode))
     pool, out = run_prefill(case)
     check_prefill(orc, case, pool, out)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("pre", [False, True])
-def test_per_head_gate(orc, pre):
+def test_per_head_gate(orc, pre, path):
     """The per-head (scalar) gate, raw and pre-computed, over ragged documents."""
-    case = synth.prefill_case(SMALL_DOCS, H=3, seed=synth.seed_for(4, 3, 13))
+    case = synth.prefill_case(SMALL_DOCS, H=heads_for(path, 10, 3), seed=synth.seed_for(4, 3, 13))
     case = synth.per_head_gate(case, pre, synth.seed_for(4, 3, 120 + int(pre)))
     pool, out = run_prefill(case)
     check_prefill(orc, case, pool, out)
@@ -208,7 +252,7 @@ def test_precomputed_gate_full_h12(orc):
     check_prefill(orc, case, pool, out)
 
 
-def _ckpt_roundtrip(orc, case, interval, starts, rows, heads=None):
+def _ckpt_roundtrip(orc, case, interval, starts, rows, heads=None, misaligned=False):
     """Prefill with intermediate checkpoints; compare written rows with the
     oracle's, check that every other row is untouched and that outputs and
     final states match as without checkpoints."""
@@ -218,7 +262,8 @@ def _ckpt_roundtrip(orc, case, interval, starts, rows, heads=None):
     if case.get("state_dtype", 0) == 2:  # one-byte elements
         fill = (fill & 0xFF).astype(np.uint8)
     ck = pool_dev(case, fill)
-    pool, out = run_prefill(case, checkpoints=ck, ckpt_starts=starts, ckpt_interval=interval)
+    pool, out = run_prefill(case, checkpoints=ck, ckpt_starts=starts, ckpt_interval=interval,
+                            misaligned=misaligned)
     check_prefill(orc, case, pool, out, heads=heads)
     ref_ck = np.zeros((rows, len(hs), HD, HD), np.float32)
     oracle_prefill(orc, case, heads=heads, ckpt=ref_ck, ckpt_starts=starts,
@@ -239,10 +284,11 @@ def _ckpt_roundtrip(orc, case, interval, starts, rows, heads=None):
     return written
 
 
-def test_checkpoints_small_docs(orc):
+@pytest.mark.parametrize("path", PATHS)
+def test_checkpoints_small_docs(orc, path):
     """Checkpoints every 16 tokens over ragged documents: one inactive
     document, a gap row, and a last row outside the buffer (skipped)."""
-    case = synth.prefill_case(SMALL_DOCS, H=3, seed=synth.seed_for(4, 3, 20))
+    case = synth.prefill_case(SMALL_DOCS, H=heads_for(path, 10, 3), seed=synth.seed_for(4, 3, 20))
     case["idx"][5] = -1  # the 33-token document: inactive, no checkpoints
     lens = np.diff(case["cu_seqlens"])
     counts = lens // 16
@@ -253,21 +299,23 @@ def test_checkpoints_small_docs(orc):
     assert written.sum() == counts[np.arange(len(lens)) != 5].sum() - 1
 
 
-@pytest.mark.parametrize("interval", [48, 64])
-def test_checkpoints_longer_interval(orc, interval):
-    case = synth.prefill_case((100, 47, 96, 130), H=2, seed=synth.seed_for(4, 2, 21),
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("interval", [48, 64, 80])
+def test_checkpoints_longer_interval(orc, interval, path):
+    case = synth.prefill_case((100, 47, 96, 130), H=heads_for(path, 4, 2), seed=synth.seed_for(4, 2, 21),
                               use_initial_state=False)
     counts = np.diff(case["cu_seqlens"]) // interval
     starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
     _ckpt_roundtrip(orc, case, interval, starts, int(counts.sum()))
 
 
-@pytest.mark.parametrize("docs", ["small", "docs4"])
+@pytest.mark.parametrize("docs", ["small", "small-fused", "docs4"])
 def test_fp16_state(orc, docs):
     """fp16 initial and final states (state_dtype 1): ragged documents with
-    checkpoints every 16 tokens, and the 4-document set at H = 12."""
-    if docs == "small":
-        case = synth.fp16_state(synth.prefill_case(SMALL_DOCS, H=3, seed=synth.seed_for(4, 3, 22)))
+    checkpoints every 16 tokens (both paths), and the 4-document set at H = 12."""
+    if docs.startswith("small"):
+        H = heads_for("fused" if docs == "small-fused" else "split", 10, 3)
+        case = synth.fp16_state(synth.prefill_case(SMALL_DOCS, H=H, seed=synth.seed_for(4, 3, 22)))
         counts = np.diff(case["cu_seqlens"]) // 16
         starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
         _ckpt_roundtrip(orc, case, 16, starts, int(counts.sum()))
@@ -277,17 +325,20 @@ def test_fp16_state(orc, docs):
         check_prefill(orc, case, pool, out)
 
 
-@pytest.mark.parametrize("docs", ["small", "docs4"])
+@pytest.mark.parametrize("docs", ["small", "small-fused", "docs4"])
 def test_fp8_state(orc, docs):
     """fp8 e4m3 initial and final states (state_dtype 2): ragged documents
     with checkpoints every 16 tokens, a zero-length document started from
-    zeros, and the 4-document set at H = 12."""
-    if docs == "small":
-        case = synth.fp8_state(synth.prefill_case(SMALL_DOCS, H=3, seed=synth.seed_for(4, 3, 23)))
+    zeros (both paths), and the 4-document set at H = 12."""
+    if docs.startswith("small"):
+        path = "fused" if docs == "small-fused" else "split"
+        case = synth.fp8_state(synth.prefill_case(SMALL_DOCS, H=heads_for(path, 10, 3),
+                                                  seed=synth.seed_for(4, 3, 23)))
         counts = np.diff(case["cu_seqlens"]) // 16
         starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
         _ckpt_roundtrip(orc, case, 16, starts, int(counts.sum()))
-        case = synth.fp8_state(synth.prefill_case((20, 0, 37), H=2, seed=synth.seed_for(4, 2, 24),
+        case = synth.fp8_state(synth.prefill_case((20, 0, 37), H=heads_for(path, 3, 2),
+                                                  seed=synth.seed_for(4, 2, 24),
                                                   use_initial_state=False))
         pool, out = run_prefill(case)
         check_prefill(orc, case, pool, out)
@@ -306,10 +357,11 @@ def test_checkpoints_full_h12(orc):
     _ckpt_roundtrip(orc, case, 256, starts, int(counts.sum()))
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("lb", [-5.5, -1.0, 0.0])
-def test_lower_bound_range(orc, lb):
+def test_lower_bound_range(orc, lb, path):
     """The accepted range of lower_bound, including its end (|lb| = 5.5)."""
-    case = synth.prefill_case((40, 9), H=2, seed=synth.seed_for(4, 2, 9))
+    case = synth.prefill_case((40, 9, 70), H=heads_for(path, 3, 2), seed=synth.seed_for(4, 2, 9))
     case["a_log"] = np.full_like(case["a_log"], 1.0)  # strong decay: the clamp is active
     pool, out = run_prefill(case, lower_bound=lb)
     check_prefill(orc, case, pool, out, lower_bound=lb)
@@ -321,8 +373,9 @@ def test_lower_bound_rejected():
         run_prefill(case, lower_bound=-6.0)
 
 
-def test_deterministic(orc):
-    case = synth.prefill_case((70, 33), H=2, seed=synth.seed_for(4, 2, 11))
+@pytest.mark.parametrize("path", PATHS)
+def test_deterministic(orc, path):
+    case = synth.prefill_case((70, 33), H=heads_for(path, 2, 2), seed=synth.seed_for(4, 2, 11))
     _, out1 = run_prefill(case)
     pool2, out2 = run_prefill(case)
     torch.cuda.synchronize()
@@ -347,6 +400,37 @@ def test_full_h64_sampled_heads(orc, docs):
     case = synth.prefill_case(lens, H=64)
     pool, out = run_prefill(case)
     check_prefill(orc, case, pool, out, heads=[0, 9, 21, 33, 47, 63])
+
+
+@pytest.mark.parametrize("docs,H,heads", [("docs4", 12, None), ("docs14", 64, [0, 17, 40, 63])])
+def test_accuracy_against_fp64(orc, docs, H, heads):
+    """Outputs and final states against an fp64 oracle run on the same inputs
+    with no storage rounding: what the chunked bf16 MFMA products and the bf16
+    stores cost over whole documents. Reported, and bounded normwise (outputs
+    5e-3, final states 3e-3)."""
+    lens = synth.DOCS_4 if docs == "docs4" else synth.DOCS_14
+    case = synth.prefill_case(lens, H=H)
+    pool_d, out_d = run_prefill(case)
+    hs = np.arange(H) if heads is None else np.asarray(heads)
+    d = np.float64
+    Ttot = case["Ttot"]
+    c = np.ascontiguousarray
+    pool64 = c(pool_vals(case, case["pool"])[:, hs].astype(d))
+    ref = orc.prefill(case["cu_seqlens"], c(f32(case["q"])[:, hs].astype(d)),
+                      c(f32(case["k"])[:, hs].astype(d)), c(f32(case["v"])[:, hs].astype(d)),
+                      c(f32(case["gate"]).reshape(Ttot, H, HD)[:, hs].astype(d)),
+                      c(f32(case["beta"])[:, hs].astype(d)), c(case["a_log"][hs].astype(d)),
+                      c(case["dt_bias"].reshape(H, -1)[hs].astype(d)), case["lower_bound"],
+                      case["scale"], pool64, case["idx"], use_initial_state=True,
+                      bf16_storage=False, real=d)
+    torch.cuda.synchronize()
+    got_out = f32(bits(out_d)).reshape(Ttot, H, HD)[:, hs].astype(d)
+    e_out = normwise_error(got_out, ref)
+    slots = case["idx"].astype(np.int64)
+    got_st = f32(bits(pool_d))[slots][:, hs].astype(d)
+    e_st = normwise_error(got_st, pool64[slots])
+    report_accuracy(f"prefill {docs} H={H}", out_normwise=e_out, state_normwise=e_st)
+    assert e_out <= 5e-3 and e_st <= 3e-3, (e_out, e_st)
 
 
 # ---------------------------------------------------------------------------
@@ -441,12 +525,14 @@ def _handoff_check(orc, case, ring_tail, base, ckpt_interval=None):
     return n_rows, 0
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("ring_tail", [16, 5, 1])
-def test_handoff_small_docs(orc, ring_tail):
+def test_handoff_small_docs(orc, ring_tail, path):
     """Ragged documents (every chunk-boundary case, a zero-length document),
     ring rows wrapping past the ring's end, one document with a ring base
     out of range (inactive)."""
-    case = synth.prefill_case(SMALL_DOCS, H=3, seed=synth.seed_for(4, 3, 30 + ring_tail))
+    case = synth.prefill_case(SMALL_DOCS, H=heads_for(path, 10, 3),
+                              seed=synth.seed_for(4, 3, 30 + ring_tail))
     base = np.array([0, 31, 20, 17, 5, 30, -1, 9, 28, 3], np.int32)
     n_rows, _ = _handoff_check(orc, case, ring_tail, base)
     expect = sum(min(ring_tail, n - 16 * ((n - 1) // 16)) for i, n in enumerate(SMALL_DOCS)
@@ -454,11 +540,13 @@ def test_handoff_small_docs(orc, ring_tail):
     assert n_rows == expect
 
 
-def test_handoff_with_checkpoints_fp16_and_no_initial_state(orc):
+@pytest.mark.parametrize("path", PATHS)
+def test_handoff_with_checkpoints_fp16_and_no_initial_state(orc, path):
     """Hand-off with checkpoints every 16 tokens (a checkpoint at a
     document's end is not written when tokens were handed off), fp16
     states, chains from zeros, a ring base of R (inactive)."""
-    case = synth.fp16_state(synth.prefill_case(SMALL_DOCS, H=2, seed=synth.seed_for(4, 2, 40),
+    case = synth.fp16_state(synth.prefill_case(SMALL_DOCS, H=heads_for(path, 10, 2),
+                                               seed=synth.seed_for(4, 2, 40),
                                                use_initial_state=False))
     base = np.array([4, 8, 12, 16, 20, 24, 28, RING_R, 1, 2], np.int32)
     _, skipped = _handoff_check(orc, case, 16, base, ckpt_interval=16)
@@ -475,13 +563,14 @@ def test_handoff_full_h12(orc):
     assert n_rows == 8 * 4
 
 
-def test_handoff_then_verify(orc):
+@pytest.mark.parametrize("path", PATHS)
+def test_handoff_then_verify(orc, path):
     """Prefill hands off to the ring, then a verify call of 8 draft tokens
     (flush_min 9, 16-row window) resumes from it with hist_len = the tail:
     GPU prefill + GPU verify against oracle prefill + oracle verify."""
     kda = _kda()
     lens = (40, 37, 3, 16, 0, 32, 7)
-    H, T, fm = 3, 8, 9
+    H, T, fm = heads_for(path, 7, 3), 8, 9
     case = synth.prefill_case(lens, H=H, seed=synth.seed_for(4, H, 50))
     N = case["N"]
     base = np.array([5, 31, 0, 12, 7, 20, 27], np.int32)

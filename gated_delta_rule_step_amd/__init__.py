@@ -43,7 +43,16 @@ _SIGS = {
                                       _P, _P, _F, _F, _I32, _I32, _P, _I64, _I64, _P, _I32,
                                       _P, _I64, _P, _I64, _P, _I32, _P, _P, _P, _I32, _P,
                                       _I32, _P, _c.c_size_t, _P]),
+    "kda_prefill_varlen_noalloc": (_c.c_int, [_I32, _I64, _I32, _I32, _I32, _P, _P,
+                                              _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
+                                              _P, _P, _F, _F, _I32, _I32, _P, _I64, _I64, _P,
+                                              _I32, _P, _I64, _P, _I64, _P, _I32, _P, _P, _P,
+                                              _I32, _P, _I32, _P]),
 }
+
+# Scratch held by the library per device for kda_prefill_varlen_noalloc
+# (KDA_NOALLOC_SCRATCH_BYTES in include/kda.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 # gate_mode bits (include/kda.h): g_raw holds the log-decay g itself (A_log and
@@ -242,6 +251,46 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
     document hands its last prefill_handoff_hist(...)[d] tokens to the ring at
     rows cache_base[d] onwards, and its slot receives the state before them."""
     import torch
+    args = _prefill_args(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_log, dt_bias,
+                         state_pool, state_indices, out, use_initial_state, lower_bound, scale,
+                         gate_mode, checkpoints, checkpoint_cu_starts, checkpoint_interval, ring,
+                         cache_base, ring_tail)
+    if workspace is None:
+        need = kda_prefill_workspace_size(args[0], args[1], args[2])
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().kda_prefill_varlen(*args, _ptr(workspace), ws_bytes, _stream(stream))
+    _check("kda_prefill_varlen", st)
+
+
+def kda_prefill_varlen_noalloc(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_log,
+                               dt_bias, state_pool, state_indices, out,
+                               use_initial_state: bool = True, lower_bound: float = -5.0,
+                               scale: float = 1.0, gate_mode: int = 0, checkpoints=None,
+                               checkpoint_cu_starts=None, checkpoint_interval: int = 16,
+                               ring=None, cache_base=None, ring_tail: int = 0,
+                               stream=None) -> None:
+    """kda_prefill_varlen without a workspace: allocates nothing (here or in the
+    library). Where a workspace is needed the library's per-device scratch of
+    NOALLOC_SCRATCH_BYTES serves; a call needing more raises KdaError
+    (KDA_ERR_SCRATCH_LIMIT). Calls on one device share that scratch, so calls
+    on different streams must be ordered."""
+    args = _prefill_args(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_log, dt_bias,
+                         state_pool, state_indices, out, use_initial_state, lower_bound, scale,
+                         gate_mode, checkpoints, checkpoint_cu_starts, checkpoint_interval, ring,
+                         cache_base, ring_tail)
+    st = lib().kda_prefill_varlen_noalloc(*args, _stream(stream))
+    _check("kda_prefill_varlen_noalloc", st)
+
+
+def _prefill_args(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_log, dt_bias,
+                  state_pool, state_indices, out, use_initial_state, lower_bound, scale,
+                  gate_mode, checkpoints, checkpoint_cu_starts, checkpoint_interval, ring,
+                  cache_base, ring_tail):
+    """Checks and the C arguments shared by both prefill entry points, up to
+    (not including) the workspace and the stream."""
+    import torch
     if cu_seqlens_host.dtype != torch.int32 or cu_seqlens_host.is_cuda or \
             not cu_seqlens_host.is_contiguous():
         raise ValueError("cu_seqlens_host must be a contiguous int32 CPU tensor")
@@ -257,11 +306,6 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
     _f32("A_log", A_log, optional=pre)
     _f32("dt_bias", dt_bias, optional=pre)
     N, slot_stride = _pool_geometry(state_pool, H)
-    if workspace is None:
-        need = kda_prefill_workspace_size(n_docs, Ttot, H)
-        if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     ck_rows = 0
     if checkpoints is not None:
         if checkpoints.dtype != state_pool.dtype or not checkpoints.is_cuda:
@@ -285,7 +329,7 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
             raise ValueError("ring caches must be contiguous")
         R = _ring_rows(kc, uc, gc, N, H)
     cu_h = _P(cu_seqlens_host.data_ptr())
-    st = lib().kda_prefill_varlen(
+    return (
         n_docs, Ttot, H, HEAD_DIM, HEAD_DIM, cu_h, _ptr(cu_seqlens),
         _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
         _ptr(g_raw), g_raw.stride(0), _ptr(beta_raw), beta_raw.stride(0),
@@ -293,9 +337,7 @@ def kda_prefill_varlen(cu_seqlens_host, cu_seqlens, q, k, v, g_raw, beta_raw, A_
         _state_dtype(state_pool), _ptr(state_pool) if N else _P(0), N, slot_stride,
         _ptr(state_indices), 1 if use_initial_state else 0, _ptr(out), out.stride(0),
         _ptr(checkpoints), ck_rows, _ptr(checkpoint_cu_starts), int(checkpoint_interval),
-        _ptr(kc), _ptr(uc), _ptr(gc), R, _ptr(cache_base), int(ring_tail),
-        _ptr(workspace), ws_bytes, _stream(stream))
-    _check("kda_prefill_varlen", st)
+        _ptr(kc), _ptr(uc), _ptr(gc), R, _ptr(cache_base), int(ring_tail))
 
 
 def prefill_handoff_hist(cu_seqlens_host, ring_tail: int):

@@ -1,7 +1,10 @@
 // C ABI of the KDA step library: host-side validation, variant choice and
-// kernel launch. Nothing here allocates, synchronises or keeps state.
+// kernel launch. Nothing here allocates or synchronises; the only state kept
+// is the per-device address of the allocation-free prefill's scratch array.
 
 #include <stdint.h>
+
+#include <mutex>
 
 #include "../../include/kda.h"
 #include "kda_launch.h"
@@ -66,6 +69,9 @@ extern "C" const char* kda_status_string(kda_status s) {
     case KDA_ERR_BAD_SEQLENS: return "cu_seqlens must start at 0, never decrease and end at total_tokens";
     case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than kda_prefill_workspace_size()";
     case KDA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case KDA_ERR_SCRATCH_LIMIT:
+      return "the call needs more workspace than the library's fixed scratch "
+             "(KDA_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -228,7 +234,9 @@ extern "C" size_t kda_prefill_workspace_size(int32_t n_docs, int64_t total_token
   return kda::prefill_workspace_bytes(n_docs, total_tokens, H);
 }
 
-extern "C" kda_status kda_prefill_varlen(
+namespace {
+
+kda_status prefill_impl(
     int32_t n_docs, int64_t total_tokens, int32_t H, int32_t K, int32_t V,
     const int32_t* cu_seqlens_host, const int32_t* cu_seqlens, const void* q,
     int64_t q_tok_stride, const void* k, int64_t k_tok_stride, const void* v,
@@ -332,4 +340,84 @@ extern "C" kda_status kda_prefill_varlen(
   // multiples of 8)
   if (p.state_fmt != KDA_STATE_BF16 && !vec) return KDA_ERR_UNSUPPORTED;
   return launch_status(kda::launch_prefill(p, cu_seqlens_host, vec, stream));
+}
+
+// Scratch of kda_prefill_varlen_noalloc: one copy per device, created when the
+// library's code object is loaded there and held until the process ends. Host
+// code never uses the symbol itself as an address (on the host it names a
+// stand-in): each device's address comes from hipGetSymbolAddress, taken once
+// with that device current and kept in scratch_addr.
+constexpr size_t kScratchBytes = KDA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices];
+
+// The current device's scratch address (looked up on its first call).
+hipError_t scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    scratch_addr[dev] = ptr;
+  }
+  *out = scratch_addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" kda_status kda_prefill_varlen(
+    int32_t n_docs, int64_t total_tokens, int32_t H, int32_t K, int32_t V,
+    const int32_t* cu_seqlens_host, const int32_t* cu_seqlens, const void* q,
+    int64_t q_tok_stride, const void* k, int64_t k_tok_stride, const void* v,
+    int64_t v_tok_stride, const void* g_raw, int64_t g_tok_stride, const void* beta_raw,
+    int64_t beta_tok_stride, const float* A_log, const float* dt_bias, float lower_bound,
+    float scale, int32_t gate_mode, int32_t state_dtype, void* state_pool, int64_t num_slots,
+    int64_t slot_stride, const int32_t* state_indices, int32_t use_initial_state, void* out,
+    int64_t out_tok_stride, void* checkpoints, int64_t checkpoint_rows,
+    const int64_t* checkpoint_cu_starts, int32_t checkpoint_interval, void* k_cache,
+    void* u_cache, float* g_cache, int32_t ring_rows, const int32_t* cache_base,
+    int32_t ring_tail, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return prefill_impl(n_docs, total_tokens, H, K, V, cu_seqlens_host, cu_seqlens, q,
+                      q_tok_stride, k, k_tok_stride, v, v_tok_stride, g_raw, g_tok_stride,
+                      beta_raw, beta_tok_stride, A_log, dt_bias, lower_bound, scale, gate_mode,
+                      state_dtype, state_pool, num_slots, slot_stride, state_indices,
+                      use_initial_state, out, out_tok_stride, checkpoints, checkpoint_rows,
+                      checkpoint_cu_starts, checkpoint_interval, k_cache, u_cache, g_cache,
+                      ring_rows, cache_base, ring_tail, workspace, workspace_bytes, stream);
+}
+
+extern "C" kda_status kda_prefill_varlen_noalloc(
+    int32_t n_docs, int64_t total_tokens, int32_t H, int32_t K, int32_t V,
+    const int32_t* cu_seqlens_host, const int32_t* cu_seqlens, const void* q,
+    int64_t q_tok_stride, const void* k, int64_t k_tok_stride, const void* v,
+    int64_t v_tok_stride, const void* g_raw, int64_t g_tok_stride, const void* beta_raw,
+    int64_t beta_tok_stride, const float* A_log, const float* dt_bias, float lower_bound,
+    float scale, int32_t gate_mode, int32_t state_dtype, void* state_pool, int64_t num_slots,
+    int64_t slot_stride, const int32_t* state_indices, int32_t use_initial_state, void* out,
+    int64_t out_tok_stride, void* checkpoints, int64_t checkpoint_rows,
+    const int64_t* checkpoint_cu_starts, int32_t checkpoint_interval, void* k_cache,
+    void* u_cache, float* g_cache, int32_t ring_rows, const int32_t* cache_base,
+    int32_t ring_tail, hipStream_t stream) {
+  if (n_docs < 0 || total_tokens < 0 || H < 1) return KDA_ERR_BAD_SHAPE;
+  if (K != D || V != D) return KDA_ERR_UNSUPPORTED;
+  const size_t need = kda::prefill_workspace_bytes(n_docs, total_tokens, H);
+  if (need > kScratchBytes) return KDA_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if (scratch_ptr(&ws) != hipSuccess) return KDA_ERR_LAUNCH;
+  return prefill_impl(n_docs, total_tokens, H, K, V, cu_seqlens_host, cu_seqlens, q,
+                      q_tok_stride, k, k_tok_stride, v, v_tok_stride, g_raw, g_tok_stride,
+                      beta_raw, beta_tok_stride, A_log, dt_bias, lower_bound, scale, gate_mode,
+                      state_dtype, state_pool, num_slots, slot_stride, state_indices,
+                      use_initial_state, out, out_tok_stride, checkpoints, checkpoint_rows,
+                      checkpoint_cu_starts, checkpoint_interval, k_cache, u_cache, g_cache,
+                      ring_rows, cache_base, ring_tail, ws, kScratchBytes, stream);
 }

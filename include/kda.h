@@ -117,7 +117,9 @@ typedef enum {
   KDA_ERR_UNSUPPORTED = 4,
   KDA_ERR_BAD_SEQLENS = 5,
   KDA_ERR_WORKSPACE_TOO_SMALL = 6,
-  KDA_ERR_LAUNCH = 7
+  KDA_ERR_LAUNCH = 7,
+  KDA_ERR_SCRATCH_LIMIT = 8  /* kda_prefill_varlen_noalloc: the call needs more
+                                than KDA_NOALLOC_SCRATCH_BYTES of workspace */
 } kda_status;
 
 /* Static, NUL-terminated description of a status code ("unknown status" for
@@ -369,6 +371,52 @@ kda_status kda_prefill_varlen(int32_t n_docs, int64_t total_tokens, int32_t H, i
                               const int32_t* cache_base, int32_t ring_tail,
                               void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/*
+ * kda_prefill_varlen_noalloc -- kda_prefill_varlen without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Every argument means what it means for kda_prefill_varlen. Where that call
+ * needs a workspace (kda_prefill_workspace_size(...) > 0: fewer than 256
+ * (document, head) chains), this one uses a scratch array of
+ * KDA_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * (created when its code object is loaded there, kept until the process
+ * ends); calls with 256 chains or more need none and have no size limit here.
+ * Nothing is allocated and nothing in the scratch needs clearing (every
+ * record the chain reads is written by the same call's preparation kernel).
+ * The first call on a device looks up that device's scratch address (with the
+ * device current) and keeps it.
+ * All calls on one device share its scratch: two calls whose kernels may
+ * overlap (different streams without ordering between them) race and give
+ * wrong results; order them on one stream or with events.
+ * KDA_ERR_SCRATCH_LIMIT when kda_prefill_workspace_size(...) exceeds
+ * KDA_NOALLOC_SCRATCH_BYTES (nothing is read or launched); KDA_ERR_LAUNCH when
+ * the scratch address cannot be obtained; otherwise the statuses of
+ * kda_prefill_varlen.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+kda_status kda_prefill_varlen_noalloc(int32_t n_docs, int64_t total_tokens, int32_t H,
+                                      int32_t K, int32_t V,
+                                      const int32_t* cu_seqlens_host, const int32_t* cu_seqlens,
+                                      const void* q, int64_t q_tok_stride,
+                                      const void* k, int64_t k_tok_stride,
+                                      const void* v, int64_t v_tok_stride,
+                                      const void* g_raw, int64_t g_tok_stride,
+                                      const void* beta_raw, int64_t beta_tok_stride,
+                                      const float* A_log, const float* dt_bias,
+                                      float lower_bound, float scale, int32_t gate_mode,
+                                      int32_t state_dtype,
+                                      void* state_pool, int64_t num_slots, int64_t slot_stride,
+                                      const int32_t* state_indices, int32_t use_initial_state,
+                                      void* out, int64_t out_tok_stride,
+                                      void* checkpoints, int64_t checkpoint_rows,
+                                      const int64_t* checkpoint_cu_starts,
+                                      int32_t checkpoint_interval,
+                                      void* k_cache, void* u_cache, float* g_cache,
+                                      int32_t ring_rows, const int32_t* cache_base,
+                                      int32_t ring_tail, hipStream_t stream);
 
 #ifdef __cplusplus
 }

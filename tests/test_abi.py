@@ -11,7 +11,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, NULLP, SHAPE, STRIDE, UNSUP, SEQ, WS, LAUNCH = range(8)
+OK, NULLP, SHAPE, STRIDE, UNSUP, SEQ, WS, LAUNCH, SCRATCH = range(9)
 
 
 @pytest.fixture(scope="module")
@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "kda_status_string", "kda_decode", "kda_verify_ucache_flush",
-        "kda_prefill_workspace_size", "kda_prefill_varlen"])
+        "kda_prefill_workspace_size", "kda_prefill_varlen", "kda_prefill_varlen_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -49,11 +49,11 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     import gated_delta_rule_step_amd as kda
     seen = set()
-    for s in range(8):
+    for s in range(9):
         txt = kda.kda_status_string(s)
         assert txt and txt != "unknown status"
         seen.add(txt)
-    assert len(seen) == 8
+    assert len(seen) == 9
     assert kda.kda_status_string(99) == "unknown status"
 
 
@@ -219,3 +219,26 @@ def test_prefill_workspace_and_validation(lib):
     assert call([0, 5], 5, ws=2 * rec - 1) == WS   # one slot, two heads
     assert call([0, 5], 5, ws=2 * rec, ws_ptr=P(0)) == NULLP
     assert call([0, 5], 5, ws=2 * rec, ws_ptr=P((1 << 20) + 128)) == UNSUP  # 256-byte aligned
+
+
+def test_prefill_noalloc_validation(lib):
+    """The allocation-free prefill refuses, before any device call, a call whose
+    workspace would exceed its fixed scratch (and bad shapes)."""
+    import gated_delta_rule_step_amd as kda
+    P = ctypes.c_void_p
+    assert kda.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+    def call(n, total, H=1, K=128):
+        cu = (ctypes.c_int32 * 2)(0, total)
+        p = P(1 << 20)
+        return lib.kda_prefill_varlen_noalloc(n, total, H, K, 128, cu, p, p, 128, p, 128, p, 128,
+                                              p, 128, p, 1, p, p, -5.0, 1.0, 0, 0, p, 1,
+                                              128 * 128, p, 1, p, 128, P(0), 0, P(0), 16, P(0),
+                                              P(0), P(0), 0, P(0), 0, P(0))
+
+    # one chain of 36,800 tokens: (1 + 2300) records of 29,696 bytes > 64 MiB
+    assert kda.kda_prefill_workspace_size(1, 36800, 1) > kda.NOALLOC_SCRATCH_BYTES
+    assert call(1, 36800) == SCRATCH
+    assert call(-1, 0) == SHAPE
+    assert call(1, 16, H=0) == SHAPE
+    assert call(1, 16, K=64) == UNSUP

@@ -20,9 +20,10 @@ the verify workloads (T = 8 / 4, bare checkpoint, fold rates, deep window)
 and the varlen prefill workloads (4 documents and the 14-document mix of
 16384 tokens, H = 64 and 12).
 
---mode profile runs a short fixed sequence (decode B = 512, verify T = 8
-B = 512, and a known-size device copy for counter calibration) for rocprofv3;
---mode profile-prefill runs 4 prefill calls on each H = 64 document set.
+--mode profile runs a short fixed sequence (decode B = 512, the verify
+workloads at B = 512 whose traffic is counted, and a known-size device copy for
+counter calibration) for rocprofv3; --mode profile-prefill runs 4 prefill
+calls on each document set at H = 64 and at H = 12, then the same copies.
 """
 from __future__ import annotations
 
@@ -43,36 +44,50 @@ H = 12
 N_SLOTS = 1024
 
 
-# HBM bytes per launch of the headline kernel from two rocprofv3 --pmc passes
-# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over `bench.py --mode
-# profile`, scaled by what the same counters read for a device copy of known
-# size (FETCH x 2.0, WRITE x 1.0); the summary is in profiles/. The figure holds
-# only for the kernel sources the counters were taken on: the digest below
-# turns it into null once those sources change.
+# HBM bytes per call of a workload from two rocprofv3 --pmc passes (FETCH_SIZE,
+# then WRITE_SIZE, KiB per dispatch, summed over the call's kernels) over
+# `bench.py --mode profile` / `--mode profile-prefill`, scaled by what the same
+# counters read for a device copy of known size in the same run (FETCH x 2.0,
+# WRITE x 1.0); the summaries are in profiles/. A figure holds only for the
+# kernel sources the counters were taken on: the digests turn it into null
+# once those sources change.
+_DEC_SRC = ("gated_delta_rule_step_amd/csrc/kda_decode.hip",
+            "gated_delta_rule_step_amd/csrc/kda_common.h", "gated_delta_rule_step_amd/build.py")
+_DEC_SHA = ("84c78a8d6498618efb1a4d7b64592ce8060e9db6d865bb021275a99a6dec8ae7",
+            "2fe55975814488bcd43f46e6ffd9805dc1139ce860b017fe31783558c0e3b22e",
+            "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f")
+_VER_SRC = ("gated_delta_rule_step_amd/csrc/kda_verify.hip",) + _DEC_SRC[1:]
+_VER_SHA = ("6b5678d54deedbcc8fd3c7d8dea5d0606841d637a9a3c0a9f333ceec8a7ff1e5",) + _DEC_SHA[1:]
+_PF_SRC = ("gated_delta_rule_step_amd/csrc/kda_prefill.hip",
+           "gated_delta_rule_step_amd/csrc/kda_prefill_split.hip",
+           "gated_delta_rule_step_amd/csrc/kda_launch.h") + _DEC_SRC[1:]
+_PF_SHA = ("78a5c65edc4fd3035d5ac2d80d3467b277a6e6dc72cae3ebbedb498b5bbf675b",
+           "b117e4105b28e420c0234832137a686d2016770084423480d5efccc326405fcd",
+           "f0d19f52b61dfbe88a4f7021b78ca69e8965e900fcdf2a3b68436948e8179958") + _DEC_SHA[1:]
+
+
+def _ct(src, sha, fetch_kib, write_kib):
+    return dict(sources=src, sha256=sha, fetch_kib=fetch_kib, write_kib=write_kib,
+                fetch_scale=2.0, write_scale=1.0)
+
+
 COUNTED_TRAFFIC = {
-    "kda::decode_kernel<4, true, 0, 0>": dict(
-        sources=("gated_delta_rule_step_amd/csrc/kda_decode.hip",
-                 "gated_delta_rule_step_amd/csrc/kda_common.h",
-                 "gated_delta_rule_step_amd/build.py"),
-        sha256=("84c78a8d6498618efb1a4d7b64592ce8060e9db6d865bb021275a99a6dec8ae7",
-                "2fe55975814488bcd43f46e6ffd9805dc1139ce860b017fe31783558c0e3b22e",
-                "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
-        fetch_kib=96508.367, write_kib=188160.684, fetch_scale=2.0, write_scale=1.0),
-    # T = 8 verify, B = 512, bare checkpoint (the --mode profile sequence)
-    "kda::verify_kernel<true, true, 0, 0, false>": dict(
-        sources=("gated_delta_rule_step_amd/csrc/kda_verify.hip",
-                 "gated_delta_rule_step_amd/csrc/kda_common.h",
-                 "gated_delta_rule_step_amd/build.py"),
-        sha256=("074013727313ef29af8be130e243434316d1f5a4764da5dd3234cffb21402e58",
-                "2fe55975814488bcd43f46e6ffd9805dc1139ce860b017fe31783558c0e3b22e",
-                "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f"),
-        fetch_kib=123866.664, write_kib=61440.0, fetch_scale=2.0, write_scale=1.0),
+    "decode B=512": _ct(_DEC_SRC, _DEC_SHA, 96508.461, 188160.848),
+    "verify T=8 B=512 bare": _ct(_VER_SRC, _VER_SHA, 123878.797, 61440.0),
+    "verify T=8 B=512 fm=9 100% fold": _ct(_VER_SRC, _VER_SHA, 138502.297, 258048.031),
+    "verify T=4 B=512 fm=13 100% fold": _ct(_VER_SRC, _VER_SHA, 143792.086, 227328.0),
+    "verify T=8 B=512 W32 fm=25 hist~U{0..24}": _ct(_VER_SRC, _VER_SHA, 160186.586, 124416.0),
+    # the fused kernel (H = 64), or the preparation + chain kernels summed (H = 12)
+    "prefill 4 docs (3840, 3776, 3200, 3072) H=64": _ct(_PF_SRC, _PF_SHA, 455753.922, 230400.0),
+    "prefill 4 docs (3840, 3776, 3200, 3072) H=12": _ct(_PF_SRC, _PF_SHA, 346268.328, 345548.641),
+    "prefill 14-doc mix, 16384 tokens H=64": _ct(_PF_SRC, _PF_SHA, 547235.656, 290816.0),
+    "prefill 14-doc mix, 16384 tokens H=12": _ct(_PF_SRC, _PF_SHA, 415585.219, 414533.008),
 }
 
 
-def counted_traffic(kernel):
+def counted_traffic(workload):
     import hashlib
-    ent = COUNTED_TRAFFIC.get(kernel)
+    ent = COUNTED_TRAFFIC.get(workload)
     if ent is None:
         return None
     for rel, digest in zip(ent["sources"], ent["sha256"]):
@@ -81,6 +96,30 @@ def counted_traffic(kernel):
                 return None
     return int(round((ent["fetch_kib"] * ent["fetch_scale"]
                       + ent["write_kib"] * ent["write_scale"]) * 1024))
+
+
+# verify points (B = 512) whose counted traffic the profile sequence measures
+VERIFY_TRAFFIC = {
+    "T=8 bare (0% fold)": "verify T=8 B=512 bare",
+    "T=8 fm=9 100% fold": "verify T=8 B=512 fm=9 100% fold",
+    "T=4 fm=13 100% fold": "verify T=4 B=512 fm=13 100% fold",
+    "T=8 W32 fm=25 hist~U{0..24}": "verify T=8 B=512 W32 fm=25 hist~U{0..24}",
+}
+# the verify configurations of the points (label -> VerifySetup arguments)
+VERIFY_CFGS = [
+    dict(label="T=8 bare (0% fold)", T=8, hist_max=0),
+    dict(label="T=4 bare (0% fold)", T=4, hist_max=0),
+    dict(label="T=8 fm=9 50% fold", T=8, fold_p=0.5),
+    dict(label="T=8 fm=9 100% fold", T=8, fold_p=1.0),
+    dict(label="T=4 fm=13 100% fold", T=4, fold_p=1.0),
+    dict(label="T=8 W32 fm=25 hist~U{0..24}", T=8, w_ring=32, flush_min=25, hist_max=24),
+    dict(label="T=8 bare, pre-computed gate and beta", T=8, hist_max=0, gate_mode=3),
+    dict(label="T=8 fm=9 50% fold, per-head gate", T=8, fold_p=0.5, gate_mode=4),
+    dict(label="T=8 bare, fp16 checkpoints", T=8, hist_max=0, state="fp16"),
+    dict(label="T=8 fm=9 100% fold, fp16 checkpoints", T=8, fold_p=1.0, state="fp16"),
+    dict(label="T=8 bare, fp8 checkpoints", T=8, hist_max=0, state="fp8"),
+    dict(label="T=8 fm=9 100% fold, fp8 checkpoints", T=8, fold_p=1.0, state="fp8"),
+]
 
 
 def log(msg):
@@ -211,13 +250,50 @@ def index_sets(synth, B, tag, inactive_frac=0.05):
     return sets
 
 
+def cold_sets(synth, B, tag, inactive_frac=0.05):
+    """All 1024 slots split into 1024 // B disjoint sets of B rows, each with
+    round(inactive_frac * B) rows set to -1 or >= 1024."""
+    rng = np.random.Generator(np.random.PCG64(synth.seed_for(1, B, tag + 1000)))
+    perm = rng.permutation(N_SLOTS)
+    sets = []
+    for s in range(N_SLOTS // B):
+        idx = perm[s * B:(s + 1) * B].astype(np.int64)
+        n_bad = int(round(inactive_frac * B))
+        for i, pos in enumerate(sorted(rng.choice(B, size=n_bad, replace=False))):
+            idx[pos] = -1 if i % 2 == 0 else N_SLOTS + int(rng.integers(0, 1000))
+        sets.append(idx.astype(np.int32))
+    return sets
+
+
 class DecodeSetup:
-    def __init__(self, B, torch, kda, synth, pools, gate_mode=0):
+    """Decode workload. Default: four (pool, slot set, inputs) combinations
+    (two pools x two disjoint slot sets). cold=True: every slot of both pools
+    once per pass, 2 * 1024 // B combinations with inputs of their own, so a
+    combination's state was last touched ~800 MB of traffic earlier (past the
+    256 MB Infinity Cache): the small batches are timed cold."""
+
+    def __init__(self, B, torch, kda, synth, pools, gate_mode=0, cold=False):
         self.B, self.gate_mode = B, gate_mode
         W = H * 128
+        self.combos = []
+        if cold:
+            sets = cold_sets(synth, B, 99)
+            n = 2 * len(sets)
+            c = synth.decode_case(B=B * n, N=1, H=H, seed=synth.seed_for(1, B, 7))
+            qkv, gate, beta = (bf16_dev(torch, c[x]) for x in ("qkv", "gate", "beta"))
+            a_log, dtb = torch.from_numpy(c["a_log"]).cuda(), torch.from_numpy(c["dt_bias"]).cuda()
+            for j in range(n):
+                r = slice(j * B, (j + 1) * B)
+                self.combos.append(dict(
+                    q=qkv[r, :W], k=qkv[r, W:2 * W], v=qkv[r, 2 * W:], g=gate[r], b=beta[r],
+                    a_log=a_log, dtb=dtb, pool=pools[j % 2],
+                    idx=torch.from_numpy(sets[j // 2]).cuda(),
+                    out=torch.empty((B, W), dtype=torch.bfloat16, device="cuda")))
+            self.n_active = int(np.mean([((x >= 0) & (x < N_SLOTS)).sum() for x in sets]))
+            self.kda = kda
+            return
         sets = index_sets(synth, B, 99)
         self.n_active = int(((sets[0] >= 0) & (sets[0] < N_SLOTS)).sum())
-        self.combos = []
         for j in range(4):
             c = synth.decode_case(B=B, N=1, H=H, seed=synth.seed_for(1, B) + j)
             if gate_mode & 4:
@@ -252,11 +328,35 @@ class VerifySetup:
     the tests (fold probability p, or hist ~ U{0..hist_max})."""
 
     def __init__(self, B, T, torch, kda, synth, pools, rings, w_ring=16, flush_min=None,
-                 fold_p=0.0, hist_max=None, gate_mode=0):
+                 fold_p=0.0, hist_max=None, gate_mode=0, cold=False):
         self.B, self.T, self.w_ring, self.gate_mode = B, T, w_ring, gate_mode
         W = H * 128
-        sets = index_sets(synth, B, 77, inactive_frac=0.0)
         self.combos = []
+        if cold:  # as DecodeSetup(cold=True); the rows share one hist / fold pattern
+            assert gate_mode == 0
+            sets = cold_sets(synth, B, 77, inactive_frac=0.0)
+            n = 2 * len(sets)
+            c = synth.verify_case(B=B * n, T=T, N=1, H=H, w_ring=w_ring, flush_min=flush_min,
+                                  fold_p=fold_p, hist_max=hist_max,
+                                  seed=synth.seed_for(3, B, T) + 7)
+            self.flush_min = c["flush_min"]
+            self.hist = c["hist_len"][:B].copy()
+            self.fold = (self.hist + T >= c["flush_min"])
+            qkv, gate, beta = (bf16_dev(torch, c[x]) for x in ("qkv", "gate", "beta"))
+            a_log, dtb = torch.from_numpy(c["a_log"]).cuda(), torch.from_numpy(c["dt_bias"]).cuda()
+            hist = torch.from_numpy(self.hist).cuda()
+            for j in range(n):
+                r = slice(j * B, (j + 1) * B)
+                kc, uc, gc = rings[j % 2]
+                self.combos.append(dict(
+                    q=qkv[r, :, :W], k=qkv[r, :, W:2 * W], v=qkv[r, :, 2 * W:], g=gate[r],
+                    b=beta[r], a_log=a_log, dtb=dtb, pool=pools[j % 2],
+                    idx=torch.from_numpy(sets[j // 2]).cuda(), kc=kc, uc=uc, gc=gc, hist=hist,
+                    base=torch.from_numpy(c["cache_base"][r].copy()).cuda(),
+                    out=torch.empty((B, T, W), dtype=torch.bfloat16, device="cuda")))
+            self.kda = kda
+            return
+        sets = index_sets(synth, B, 77, inactive_frac=0.0)
         for j in range(4):
             c = synth.verify_case(B=B, T=T, N=1, H=H, w_ring=w_ring, flush_min=flush_min,
                                   fold_p=fold_p, hist_max=hist_max,
@@ -414,25 +514,62 @@ def cpu_baseline_decode(B, budget_s, synth):
                        f"host {platform.machine()} with {os.cpu_count()} logical CPUs")
 
 
+def cpu_single_row(synth):
+    """The oracle on the single-row workload (B = 1, H = 12, a 4-slot pool,
+    state index 2): one T = 1 call, and a 16-step rollout (16 calls in
+    sequence on the same slot, each with a token of its own); seconds, median
+    of 5 runs each."""
+    import oracle
+    f32 = synth.f32_from_bits
+    case = synth.decode_case(B=16, N=4, H=H, seed=synth.seed_for(0, 1))
+    W = H * 128
+    q, k, v = (np.ascontiguousarray(f32(case["qkv"][:, i * W:(i + 1) * W]).reshape(16, H, 128))
+               for i in range(3))
+    gate = np.ascontiguousarray(f32(case["gate"]).reshape(16, H, 128))
+    beta = np.ascontiguousarray(f32(case["beta"]))
+    base_pool = np.ascontiguousarray(f32(case["pool"]))
+    idx = np.array([2], np.int32)
+
+    def steps(n):
+        pool = base_pool.copy()
+        t0 = time.perf_counter()
+        for t in range(n):
+            oracle.decode(q[t:t + 1], k[t:t + 1], v[t:t + 1], gate[t:t + 1], beta[t:t + 1],
+                          case["a_log"], case["dt_bias"], -5.0, 1.0, pool, idx)
+        return time.perf_counter() - t0
+    one = float(np.median([steps(1) for _ in range(5)]))
+    roll = float(np.median([steps(16) for _ in range(5)]))
+    return dict(single_call_s=round(one, 6), rollout_16_steps_s=round(roll, 6),
+                sample="B=1, H=12, 4-slot pool, state index 2; one T=1 call and a 16-step "
+                       "rollout, fp32 oracle, median of 5 runs each")
+
+
 # ---------------------------------------------------------------------------
 
 def run_profile(torch, kda, synth, pools):
-    """Fixed short sequence for rocprofv3: 8 decode calls (B = 512), 8 verify
-    calls (T = 8, B = 512, bare checkpoint), 4 device copies of 402,653,184 B."""
+    """Fixed short sequence for rocprofv3, in this dispatch order: 8 decode
+    calls (B = 512), then 8 verify calls (B = 512) of each workload in
+    VERIFY_TRAFFIC (in its order), then 4 device copies of 402,653,184 B."""
     dec = DecodeSetup(512, torch, kda, synth, pools)
     for c in dec.calls() * 2:
         c()
     torch.cuda.synchronize()
     rings = make_rings(torch, synth)
-    ver = VerifySetup(512, 8, torch, kda, synth, pools, rings, hist_max=0)
-    for c in ver.calls() * 2:
-        c()
-    torch.cuda.synchronize()
+    for cfg in VERIFY_CFGS:
+        if cfg["label"] not in VERIFY_TRAFFIC:
+            continue
+        kw = {k: v for k, v in cfg.items() if k not in ("label", "T")}
+        ver = VerifySetup(512, cfg["T"], torch, kda, synth, pools, rings, **kw)
+        for c in ver.calls() * 2:
+            c()
+        torch.cuda.synchronize()
+        del ver
     src, dst = pools
     for _ in range(4):
         dst.copy_(src)
     torch.cuda.synchronize()
-    log("profile: 8 x decode B=512, 8 x verify T=8 B=512 bare, 4 x copy 402653184 B")
+    log("profile: 8 x decode B=512; 8 x verify B=512 of each of " + ", ".join(VERIFY_TRAFFIC)
+        + "; 4 x copy 402653184 B")
 
 
 def main():
@@ -463,7 +600,12 @@ def main():
                     c()
                 torch.cuda.synchronize()
                 del ps
-        log("profile: 4 x prefill at H=64 then H=12, on the 4-document set, then the 14-doc mix")
+        src, dst = pools
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("profile: 4 x prefill at H=64 then H=12, on the 4-document set, then the 14-doc "
+            "mix; 4 x copy 402653184 B")
         return
 
     B = 512
@@ -482,14 +624,17 @@ def main():
     points = []
     if args.points == "all":
         for Bp in (1, 8, 32, 128):
-            sp = DecodeSetup(Bp, torch, kda, synth, pools)
-            st = max(args.steps, 256)
+            sp = DecodeSetup(Bp, torch, kda, synth, pools, cold=True)
+            n = len(sp.combos)
+            st = max(256, n)
             _, e = time_graphs(sp.calls(), st, args.warmup, torch, min_warm_s=0.3)
             us = e * 1e3 / st
             nb = wm.decode_bytes(sp.n_active, Bp - sp.n_active)
             points.append(dict(kind="decode", B=Bp, T=1, us_per_call=round(us, 3),
                                GBps=round(nb / (us * 1e-6) / 1e9, 1),
-                               hbm_frac=round(nb / (us * 1e-6) / 1e9 / wm.HBM_PEAK_GBS, 4)))
+                               hbm_frac=round(nb / (us * 1e-6) / 1e9 / wm.HBM_PEAK_GBS, 4),
+                               cold=f"{n} combinations rotated, ~{(n - 1) * nb / 1e6:.0f} MB "
+                                    "touched between reuses"))
             log(f"bench: {points[-1]}")
         points.append(dict(kind="decode", B=B, T=1, us_per_call=round(us_ev, 3),
                            GBps=round(gbs, 1), hbm_frac=round(gbs / wm.HBM_PEAK_GBS, 4)))
@@ -509,20 +654,7 @@ def main():
             log(f"bench: {points[-1]}")
         del f16, f8
         rings = make_rings(torch, synth)
-        vcfgs = [
-            dict(label="T=8 bare (0% fold)", T=8, hist_max=0),
-            dict(label="T=4 bare (0% fold)", T=4, hist_max=0),
-            dict(label="T=8 fm=9 50% fold", T=8, fold_p=0.5),
-            dict(label="T=8 fm=9 100% fold", T=8, fold_p=1.0),
-            dict(label="T=4 fm=13 100% fold", T=4, fold_p=1.0),
-            dict(label="T=8 W32 fm=25 hist~U{0..24}", T=8, w_ring=32, flush_min=25, hist_max=24),
-            dict(label="T=8 bare, pre-computed gate and beta", T=8, hist_max=0, gate_mode=3),
-            dict(label="T=8 fm=9 50% fold, per-head gate", T=8, fold_p=0.5, gate_mode=4),
-            dict(label="T=8 bare, fp16 checkpoints", T=8, hist_max=0, state="fp16"),
-            dict(label="T=8 fm=9 100% fold, fp16 checkpoints", T=8, fold_p=1.0, state="fp16"),
-            dict(label="T=8 bare, fp8 checkpoints", T=8, hist_max=0, state="fp8"),
-            dict(label="T=8 fm=9 100% fold, fp8 checkpoints", T=8, fold_p=1.0, state="fp8"),
-        ]
+        vcfgs = VERIFY_CFGS
         low = {"fp16": fp16_pools(torch, pools), "fp8": fp8_pools(torch, pools)}
         for Bv in (1, 32, 512):
             for cfg in vcfgs:
@@ -530,16 +662,20 @@ def main():
                     continue
                 kw = {k: v for k, v in cfg.items() if k not in ("label", "T", "state")}
                 vs = VerifySetup(Bv, cfg["T"], torch, kda, synth, low.get(cfg.get("state"), pools),
-                                 rings, **kw)
-                st = max(args.steps, 256 if Bv < 512 else 100)
+                                 rings, cold=Bv < 512, **kw)
+                st = max(args.steps, 256 if Bv < 512 else 100, len(vs.combos))
                 _, e = time_graphs(vs.calls(), st, args.warmup, torch, min_warm_s=0.3)
                 us = e * 1e3 / st
                 nb = wm.verify_bytes(cfg["T"], vs.hist, vs.fold,
                                      state_bytes=1 if cfg.get("state") == "fp8" else 2)
                 fl = wm.verify_flops(cfg["T"], vs.hist)
                 extra = {}
-                if Bv == 512 and cfg["label"] == "T=8 bare (0% fold)":
-                    extra["traffic_bytes"] = counted_traffic("kda::verify_kernel<true, true, 0, 0, false>")
+                if Bv < 512:
+                    extra["cold"] = (f"{len(vs.combos)} combinations rotated, "
+                                     f"~{(len(vs.combos) - 1) * nb / 1e6:.0f} MB touched between "
+                                     "reuses")
+                if Bv == 512 and cfg["label"] in VERIFY_TRAFFIC:
+                    extra["traffic_bytes"] = counted_traffic(VERIFY_TRAFFIC[cfg["label"]])
                 points.append(dict(kind="verify", B=Bv, label=cfg["label"],
                                    fold_frac=round(float(np.mean(vs.fold)), 3),
                                    mean_hist=round(float(np.mean(vs.hist)), 2),
@@ -577,6 +713,11 @@ def main():
                 extra["state"] = sdt
             if rt:
                 extra["handoff"] = f"last {rt} tokens of each document to the verify ring"
+            if not (gm or cki or rt) and sdt == "bf16":
+                extra["kernels"] = ("fused 64-token chunk kernel"
+                                    if len(lens) * Hp >= kda.FUSED_MIN_CHAINS
+                                    else "preparation + chain (16-token chunks, workspace)")
+                extra["traffic_bytes"] = counted_traffic(f"prefill {name} H={Hp}")
             points.append(dict(kind="prefill", H=Hp, docs=name, tokens=int(sum(lens)),
                                **extra, us_per_call=round(us, 1),
                                Mtok_per_s=round(sum(lens) / (us * 1e-6) / 1e6, 2),
@@ -593,6 +734,7 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
         cpu = cpu_baseline_decode(B, args.cpu_budget_s, synth)
+        cpu["single_row_workload"] = cpu_single_row(synth)
         log(f"bench: cpu baseline {cpu}")
 
     line = {
@@ -613,7 +755,7 @@ def main():
                    "B": B, "H": H, "T": 1, "pool_slots": N_SLOTS, "device": dev_name},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": wm.HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / wm.HBM_PEAK_GBS, 4),
-                     "traffic": counted_traffic("kda::decode_kernel<4, true, 0, 0>"),
+                     "traffic": counted_traffic("decode B=512"),
                      "kernel": "kda::decode_kernel<4, true, 0, 0>",
                      "kernel_us_avg": round(us_ev, 3), "kernel_us_percentiles": dist,
                      "algorithmic_bytes": nbytes},

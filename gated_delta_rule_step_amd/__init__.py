@@ -53,6 +53,9 @@ _SIGS = {
 # Scratch held by the library per device for kda_prefill_varlen_noalloc
 # (KDA_NOALLOC_SCRATCH_BYTES in include/kda.h).
 NOALLOC_SCRATCH_BYTES = 64 << 20
+# Prefill calls with at least this many (document, head) chains run the fused
+# 64-token chunk kernel (no workspace); fewer run the two-stage form.
+FUSED_MIN_CHAINS = 256
 
 
 # gate_mode bits (include/kda.h): g_raw holds the log-decay g itself (A_log and

@@ -382,6 +382,64 @@ def test_deterministic(orc, path):
     assert np.array_equal(bits(out1), bits(out2))
 
 
+@pytest.mark.parametrize("path", PATHS)
+def test_graph_replay_after_replanning_lengths(orc, path):
+    """A graph captured with one set of document lengths, replayed after the
+    device cu_seqlens was rewritten with other lengths of the same count and
+    total (the host copy, which plans the launch order, is stale): each replay
+    equals an eager call with the new lengths bit for bit, and that call
+    matches the oracle. Replays alternate with eager work and synchronisation."""
+    kda = _kda()
+    L1, L2 = (40, 0, 97, 19), (100, 33, 0, 23)
+    H = heads_for(path, 4, 2)
+    case = synth.prefill_case(L2, H=H, seed=synth.seed_for(4, H, 50))
+    Ttot, W = case["Ttot"], H * HD
+    assert sum(L1) == Ttot
+    q, k, v = (dev_bf16(case[n].reshape(Ttot, W)) for n in ("q", "k", "v"))
+    g, b = dev_bf16(case["gate"]), dev_bf16(case["beta"])
+    a_log, dtb, idx = dev(case["a_log"]), dev(case["dt_bias"]), dev(case["idx"])
+    pool0 = pool_dev(case, case["pool"])
+    cu1 = np.concatenate([[0], np.cumsum(L1)]).astype(np.int32)
+    cu2 = case["cu_seqlens"]
+    ws = torch.empty(max(kda.kda_prefill_workspace_size(4, Ttot, H), 1), dtype=torch.uint8,
+                     device="cuda")
+
+    def call(cu_h, cu_d, pool, out):
+        kda.kda_prefill_varlen(cu_h, cu_d, q, k, v, g, b, a_log, dtb, pool, idx, out,
+                               workspace=ws, lower_bound=case["lower_bound"],
+                               scale=case["scale"])
+
+    # eager reference with the new lengths
+    pool_e = pool0.clone()
+    out_e = torch.full((Ttot, W), float("nan"), dtype=torch.bfloat16, device="cuda")
+    call(torch.from_numpy(cu2.copy()), dev(cu2), pool_e, out_e)
+    torch.cuda.synchronize()
+    check_prefill(orc, case, pool_e, out_e)
+    # capture with the old lengths (host and device copies)
+    cu_d = dev(cu1)
+    pool_g = pool0.clone()
+    out_g = torch.full((Ttot, W), float("nan"), dtype=torch.bfloat16, device="cuda")
+    call(torch.from_numpy(cu1.copy()), cu_d, pool_g, out_g)  # warm-up outside the graph
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            call(torch.from_numpy(cu1.copy()), cu_d, pool_g, out_g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    cu_d.copy_(dev(cu2))
+    for rep in range(3):
+        pool_g.copy_(pool0)
+        out_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out_g), bits(out_e)), f"replay {rep}: outputs differ"
+        assert np.array_equal(bits(pool_g), bits(pool_e)), f"replay {rep}: states differ"
+
+
 # ---------------------------------------------------------------------------
 # full sizes: 4 documents (3840, 3776, 3200, 3072) and the 14-document mix
 # (16384 tokens each), H = 12 (all heads) and H = 64 (sampled heads)

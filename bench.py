@@ -62,7 +62,7 @@ _PF_SRC = ("gated_delta_rule_step_amd/csrc/kda_prefill.hip",
            "gated_delta_rule_step_amd/csrc/kda_prefill_split.hip",
            "gated_delta_rule_step_amd/csrc/kda_launch.h") + _DEC_SRC[1:]
 _PF_SHA = ("78a5c65edc4fd3035d5ac2d80d3467b277a6e6dc72cae3ebbedb498b5bbf675b",
-           "b117e4105b28e420c0234832137a686d2016770084423480d5efccc326405fcd",
+           "7ed314bbe81927c13096a85d78a0d1b52dc5a77399d84ed3928b223cf0d88f51",
            "f0d19f52b61dfbe88a4f7021b78ca69e8965e900fcdf2a3b68436948e8179958") + _DEC_SHA[1:]
 
 

@@ -976,18 +976,11 @@ hipError_t launch_prefill_split(const PrefillParams& p, const int32_t* cu_host, 
   }
   // Fewer chains than CUs (always the case on this path): two workgroups per
   // chain, by value channels.
-  const bool split = blocks < kFusedMinChains;
   // fp16 and fp8 states run on the vectorised path only (the host requires it)
   if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
-#define KDA_CHAIN_LAUNCH(V, S)                                                              \
-  do {                                                                                      \
-    if (split)                                                                              \
-      hipLaunchKernelGGL((chain_kernel<V, S, 2>), dim3(static_cast<unsigned>(2 * blocks)),  \
-                         dim3(ChainShape<2>::kThreads), 0, stream, p, ord);                 \
-    else                                                                                    \
-      hipLaunchKernelGGL((chain_kernel<V, S, 1>), dim3(static_cast<unsigned>(blocks)),      \
-                         dim3(ChainShape<1>::kThreads), 0, stream, p, ord);                 \
-  } while (0)
+#define KDA_CHAIN_LAUNCH(V, S)                                                            \
+  hipLaunchKernelGGL((chain_kernel<V, S, 2>), dim3(static_cast<unsigned>(2 * blocks)),    \
+                     dim3(ChainShape<2>::kThreads), 0, stream, p, ord)
   if (p.state_fmt == kStateFp16) KDA_CHAIN_LAUNCH(true, kStateFp16);
   else if (p.state_fmt == kStateFp8) KDA_CHAIN_LAUNCH(true, kStateFp8);
   else if (vec) KDA_CHAIN_LAUNCH(true, kStateBf16);

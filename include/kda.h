@@ -255,8 +255,10 @@ kda_status kda_verify_ucache_flush(int32_t B, int32_t T, int32_t H, int32_t K, i
 /*
  * kda_prefill_workspace_size -- bytes of device workspace kda_prefill_varlen
  * needs for these sizes (0 when nothing is needed, or when K or V is not 128).
- * Pure host arithmetic: one 29,696-byte chunk record per (chunk slot, head),
- * with (n_docs + floor(total_tokens / 16)) chunk slots, since a document's
+ * Pure host arithmetic. 0 when n_docs * H >= 256: those calls run the fused
+ * kernel, which keeps every chunk's operands on chip. Below that, one
+ * 29,696-byte chunk record per (chunk slot, head), with
+ * (n_docs + floor(total_tokens / 16)) chunk slots, since a document's
  * 16-token chunks are numbered from its index plus floor(first token / 16).
  */
 size_t kda_prefill_workspace_size(int32_t n_docs, int64_t total_tokens, int32_t H, int32_t K,
@@ -271,6 +273,12 @@ size_t kda_prefill_workspace_size(int32_t n_docs, int64_t total_tokens, int32_t 
  * states in a pool addressed by state indices; chunked recurrence in two
  * stages, an intra-chunk preparation and a sequential chain over chunks).
  * The result is the token-by-token recurrence of every (document, head) chain.
+ * Two forms, chosen from n_docs * H alone: with at least 256 (document, head)
+ * chains, one fused kernel (a workgroup per chain prepares each 64-token
+ * chunk and advances the state through it, no workspace); with fewer, a
+ * preparation kernel over every 16-token chunk of every chain writes records
+ * to the workspace and a chain kernel consumes them. Both give the same
+ * recurrence within rounding.
  *
  *  n_docs             documents (>= 0)
  *  total_tokens       tokens over all documents (>= 0)
@@ -344,10 +352,12 @@ size_t kda_prefill_workspace_size(int32_t n_docs, int64_t total_tokens, int32_t 
  * workspace_bytes is short; KDA_ERR_NULL_POINTER when a workspace is needed
  * and NULL; KDA_ERR_UNSUPPORTED when the workspace is not 256-byte aligned,
  * when out_tok_stride exceeds 2^25 elements (16 output rows must span less
- * than 2^31 bytes) or when |lower_bound| > 5.5 (the 16-token chunks factor
- * each decay weight exp(G_r - G_j) into two exps of at most 8 |lower_bound|
- * each, which must stay well inside the fp32 range). The call launches a
- * preparation kernel and then a chain kernel on the stream.
+ * than 2^31 bytes) or when |lower_bound| > 5.5 (both forms factor each decay
+ * weight exp(G_r - G_j) within a 16-token block into two exps of at most
+ * 8 |lower_bound| each, which must stay well inside the fp32 range). The call
+ * launches the fused kernel, or a preparation kernel and then a chain kernel,
+ * on the stream; the longest documents are started first (for up to 256
+ * documents; natural order beyond).
  * Outputs are written in bf16 (round to nearest even); the final states are
  * rounded to bf16 once, at the end of each chain.
  */

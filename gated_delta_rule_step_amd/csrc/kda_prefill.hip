@@ -977,22 +977,6 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
 #pragma unroll
         for (int q = 0; q < 4; ++q) um = fmaxf(um, fabsf(uu[b][q]));
       u_big = __builtin_amdgcn_ballot_w64(um >= 16384.f) != 0;
-      if (u_big) {
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) um = fmaxf(um, __shfl_xor(um, o));
-        const int ex = int((__float_as_uint(um) >> 23) & 0xffu) - 127;  // >= 14
-        const int sh = __builtin_amdgcn_readfirstlane(min(ex - 13, 126));
-        u_sc = __uint_as_float(uint32_t(127 - sh) << 23);
-        u_isc = __uint_as_float(uint32_t(127 + sh) << 23);
-      }
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const float x8[8] = {uu[2 * pp][0] * u_sc,     uu[2 * pp][1] * u_sc,
-                             uu[2 * pp][2] * u_sc,     uu[2 * pp][3] * u_sc,
-                             uu[2 * pp + 1][0] * u_sc, uu[2 * pp + 1][1] * u_sc,
-                             uu[2 * pp + 1][2] * u_sc, uu[2 * pp + 1][3] * u_sc};
-        split8h(x8, uh[pp], ul[pp]);
-      }
       if (cut) {  // hand-off: ring rows of the tail tokens receive u (bf16)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -1007,6 +991,25 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
             }
           }
         }
+      }
+      // The scaling lives in branches of its own (around the products, not in
+      // them), so that the usual case runs none of it.
+      if (__builtin_expect(u_big, 0)) {
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) um = fmaxf(um, __shfl_xor(um, o));
+        const int ex = int((__float_as_uint(um) >> 23) & 0xffu) - 127;  // >= 14
+        const int sh = __builtin_amdgcn_readfirstlane(min(ex - 13, 126));
+        u_sc = __uint_as_float(uint32_t(127 - sh) << 23);
+        u_isc = __uint_as_float(uint32_t(127 + sh) << 23);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) uu[b] *= u_sc;
+      }
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const float x8[8] = {uu[2 * pp][0],     uu[2 * pp][1],     uu[2 * pp][2],
+                             uu[2 * pp][3],     uu[2 * pp + 1][0], uu[2 * pp + 1][1],
+                             uu[2 * pp + 1][2], uu[2 * pp + 1][3]};
+        split8h(x8, uh[pp], ul[pp]);
       }
     }
     lds_barrier();  // b8: W fragments read; k~^T may overwrite them
@@ -1034,9 +1037,13 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
           }
         }
       }
+      if (__builtin_expect(u_big, 0)) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) oo[b] *= u_sc;
+      }
+      const float osc = p.scale * u_isc;  // undoes the scaling of U (1 as a rule)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        if (u_big) oo[b] *= u_sc;
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           if (pp == 1 && b < 2) continue;
@@ -1047,12 +1054,11 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
           oo[b] = mma_h(pa, uh[pp], oo[b]);
           oo[b] = mma_h(pa, ul[pp], oo[b]);
         }
-        if (u_big) oo[b] *= u_isc;
         // outputs staged in LDS (the x^T region, free until the next chunk's
         // A / P partials), stored below as whole 16-byte pieces of token rows
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          OST[(16 * b + 4 * g4 + q) * OSS + v] = to_bf16(p.scale * oo[b][q]);
+          OST[(16 * b + 4 * g4 + q) * OSS + v] = to_bf16(osc * oo[b][q]);
       }
     }
     lds_barrier();  // b9
@@ -1071,6 +1077,10 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
     }
 
     // ================= C3: S = diag(exp(Gam_e)) S + k~^T U
+    if (__builtin_expect(u_big, 0)) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[m] *= u_sc;
+    }
     {
       KDA_PHASE_IDS;
 #pragma unroll
@@ -1078,7 +1088,6 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
         fence_sched();
         const f32x4 eg = *reinterpret_cast<const f32x4*>(EG + 16 * m + 4 * g4);
         f32x4 a = acc[m] * eg;
-        if (u_big) a *= u_sc;
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           const uint16_t* kr_h = KT + (16 * m + n16) * TRS + 32 * pp;
@@ -1093,9 +1102,12 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
           a = mma_h(kh8, ul[pp], a);
           a = mma_h(kl8, uh[pp], a);
         }
-        if (u_big) a *= u_isc;
         acc[m] = a;
       }
+    }
+    if (__builtin_expect(u_big, 0)) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[m] *= u_isc;
     }
     // intermediate checkpoint after this chunk
     if (ivl && npos % ivl == 0 && npos <= kept) {

@@ -374,6 +374,28 @@ def test_lower_bound_rejected():
 
 
 @pytest.mark.parametrize("path", PATHS)
+def test_large_values(orc, path):
+    """v and the initial states scaled by 2^16 (exact in bf16): the
+    corrections u reach ~1e5, beyond the fp16 range the fused kernel's
+    state-update operands take unscaled, so its waves take their power-of-two
+    scaling path. The recurrence is linear in (initial state, v) and power-of-
+    two scaling commutes with rounding, so the results divided by 2^16 (exact)
+    must meet the usual criteria against the oracle of the unscaled case."""
+    case = synth.prefill_case((70, 9, 64, 33), H=heads_for(path, 4, 2),
+                              seed=synth.seed_for(4, 2, 70))
+    big = dict(case)
+    sc = np.float32(65536.0)
+    for name in ("v", "pool"):
+        x = f32(case[name]) * sc
+        big[name] = synth.bf16_bits(x)
+        assert np.array_equal(f32(big[name]), x)
+    pool, out = run_prefill(big)
+    torch.cuda.synchronize()
+    down = [dev_bf16(synth.bf16_bits(f32(bits(t)) / sc)) for t in (pool, out)]
+    check_prefill(orc, case, down[0], down[1])
+
+
+@pytest.mark.parametrize("path", PATHS)
 def test_deterministic(orc, path):
     case = synth.prefill_case((70, 33), H=heads_for(path, 2, 2), seed=synth.seed_for(4, 2, 11))
     _, out1 = run_prefill(case)

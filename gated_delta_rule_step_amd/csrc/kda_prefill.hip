@@ -262,37 +262,64 @@ struct Raw {
 };
 
 // Token row tb + tr: tb is uniform (a chunk's first token), tr the lane's row;
-// two runs of 8 channels (16-byte loads on the vectorised path).
+// two runs of 8 channels (16-byte loads on the vectorised path). The inputs
+// come in four groups (q; k; g; v and beta). Inside the chunk loop each group
+// is issued at its own point of the previous chunk's chain: the workgroup's
+// 64 KB of loads per chunk issued at once stall every wave at issue behind
+// the vector memory path.
+enum RawPart { kRawQ, kRawK, kRawG, kRawVB };
+
+template <int PART, bool VEC, bool GHEAD>
+__device__ __forceinline__ void load_raw_part(const PrefillParams& p, int64_t tb, int tr, int h,
+                                              int cb, bool valid, Raw& r) {
+  constexpr u32x4 z = {0u, 0u, 0u, 0u};
+  if constexpr (PART == kRawQ || PART == kRawK) {
+    u32x4(&dst)[2] = PART == kRawQ ? r.q : r.k;
+    if (valid) {  // lanes past the document's end issue no load
+      const uint16_t* base = PART == kRawQ ? p.q : p.k;
+      const int64_t ts = PART == kRawQ ? p.q_tok_stride : p.k_tok_stride;
+      const uint16_t* x = base + tb * ts + (int64_t(tr) * ts + h * D + cb);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) dst[s] = load8_bits<VEC>(x + 32 * s);
+    } else {
+      dst[0] = dst[1] = z;
+    }
+  } else if constexpr (PART == kRawG) {
+    if (valid) {
+      const int64_t t = tb + tr;
+      if constexpr (GHEAD) {
+        const uint32_t gh = p.g[t * p.g_tok_stride + h];
+        const uint32_t g2 = gh | (gh << 16);  // the value in both halves: all 16 channels
+        r.g[0] = r.g[1] = u32x4{g2, g2, g2, g2};
+      } else {
+        const uint16_t* g = p.g + t * p.g_tok_stride + h * D + cb;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) r.g[s] = load8_bits<VEC>(g + 32 * s);
+      }
+    } else {
+      r.g[0] = r.g[1] = z;
+    }
+  } else {
+    if (valid) {
+      const int64_t t = tb + tr;
+      const uint16_t* v = p.v + tb * p.v_tok_stride + (int64_t(tr) * p.v_tok_stride + h * D + cb);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) r.v[s] = load8_bits<VEC>(v + 32 * s);
+      r.b = p.beta[t * p.beta_tok_stride + h];
+    } else {
+      r.v[0] = r.v[1] = z;
+      r.b = 0u;
+    }
+  }
+}
+
 template <bool VEC, bool GHEAD>
 __device__ __forceinline__ void load_raw(const PrefillParams& p, int64_t tb, int tr, int h,
                                          int cb, bool valid, Raw& r) {
-  if (valid) {
-    const int64_t t = tb + tr;
-    const uint16_t* q = p.q + tb * p.q_tok_stride + (int64_t(tr) * p.q_tok_stride + h * D + cb);
-    const uint16_t* k = p.k + tb * p.k_tok_stride + (int64_t(tr) * p.k_tok_stride + h * D + cb);
-    const uint16_t* v = p.v + tb * p.v_tok_stride + (int64_t(tr) * p.v_tok_stride + h * D + cb);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      r.q[s] = load8_bits<VEC>(q + 32 * s);
-      r.k[s] = load8_bits<VEC>(k + 32 * s);
-      r.v[s] = load8_bits<VEC>(v + 32 * s);
-    }
-    if constexpr (GHEAD) {
-      const uint32_t gh = p.g[t * p.g_tok_stride + h];
-      const uint32_t g2 = gh | (gh << 16);  // the value in both halves: all 16 channels
-#pragma unroll
-      for (int s = 0; s < 2; ++s) r.g[s] = u32x4{g2, g2, g2, g2};
-    } else {
-      const uint16_t* g = p.g + t * p.g_tok_stride + h * D + cb;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) r.g[s] = load8_bits<VEC>(g + 32 * s);
-    }
-    r.b = p.beta[t * p.beta_tok_stride + h];
-  } else {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) r.q[s] = r.k[s] = r.g[s] = r.v[s] = u32x4{0u, 0u, 0u, 0u};
-    r.b = 0;
-  }
+  load_raw_part<kRawQ, VEC, GHEAD>(p, tb, tr, h, cb, valid, r);
+  load_raw_part<kRawK, VEC, GHEAD>(p, tb, tr, h, cb, valid, r);
+  load_raw_part<kRawG, VEC, GHEAD>(p, tb, tr, h, cb, valid, r);
+  load_raw_part<kRawVB, VEC, GHEAD>(p, tb, tr, h, cb, valid, r);
 }
 
 __device__ __forceinline__ void unpack16(const u32x4 (&w)[2], float (&x)[16]) {
@@ -933,6 +960,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
 
     // ================= C1: U = U0 - W S, O = Q~ S (chain; wave: value tile)
     const int npos = pos + c;
+    const int cn_next = npos < len32 ? chunk_len(npos) : 0;  // the next chunk's length (0: none)
     f32x4 oo[4];
     u32x4 uh[2], ul[2];  // this wave's U tile in fp16 hi + lo, times u_sc
     bool u_big = false;  // wave-uniform: u_sc = 2^-s, u_isc = 2^s, else both 1
@@ -1015,10 +1043,9 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
     lds_barrier();  // b8: W fragments read; k~^T may overwrite them
 
     {  // next chunk's raw inputs, in flight during C2 and C3 (always assigned, zeros
-       // past the document's end, so that they are dead from P1 to here)
+       // past the document's end, so that they are dead from P1 to here): q
       KDA_PHASE_IDS;
-      const int cn = npos < len32 ? chunk_len(npos) : 0;
-      load_raw<VEC, GHEAD>(p, t0 + npos, tr, h, cb, tr < cn, raw);
+      load_raw_part<kRawQ, VEC, GHEAD>(p, t0 + npos, tr, h, cb, tr < cn_next, raw);
     }
 
     // ================= k~^T -> LDS (token-owner registers); C2: O += P U, output
@@ -1037,6 +1064,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
           }
         }
       }
+      load_raw_part<kRawK, VEC, GHEAD>(p, t0 + npos, tr, h, cb, tr < cn_next, raw);
       if (__builtin_expect(u_big, 0)) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) oo[b] *= u_sc;
@@ -1060,6 +1088,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
         for (int q = 0; q < 4; ++q)
           OST[(16 * b + 4 * g4 + q) * OSS + v] = to_bf16(osc * oo[b][q]);
       }
+      load_raw_part<kRawG, VEC, GHEAD>(p, t0 + npos, tr, h, cb, tr < cn_next, raw);
     }
     lds_barrier();  // b9
 
@@ -1103,6 +1132,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
           a = mma_h(kl8, uh[pp], a);
         }
         acc[m] = a;
+        if (m == 0) load_raw_part<kRawVB, VEC, GHEAD>(p, t0 + npos, tr, h, cb, tr < cn_next, raw);
       }
     }
     if (__builtin_expect(u_big, 0)) {

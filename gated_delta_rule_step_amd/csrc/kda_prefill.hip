@@ -741,23 +741,24 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
         offdiag(3, kF2h, kF2l, qF2h, qF2l, accA[2], accP[2]);        // (3,0)
         offdiag(1, kF2h, kF2l, qF2h, qF2l, accA[3], accP[3]);        // (3,1)
       }
-      if (hc == 1) {
+      {  // the half that combines A below publishes P, and the other way round
         const int np = tb + 1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (i < np) {
             const int a = i == 0 ? tb : (tb == 1 ? 0 : (tb == 2 ? i - 1 : (i == 1 ? 2 : i - 2)));
             const int pid = pair_id(tb, a);
-            *reinterpret_cast<f32x4*>(PART + ((pid * 2 + 0) * 64 + ln_) * 4) = accA[i];
-            *reinterpret_cast<f32x4*>(PART + ((pid * 2 + 1) * 64 + ln_) * 4) = accP[i];
+            *reinterpret_cast<f32x4*>(PART + ((pid * 2 + (hc ^ 1)) * 64 + ln_) * 4) =
+                hc ? accA[i] : accP[i];
           }
         }
       }
     }
     lds_barrier();  // b3
 
-    // ================= P3b: A (scaled by beta) and P, whole sums, masked
-    if (hc == 0) {
+    // ================= P3b: A (scaled by beta) and P, whole sums, masked; the
+    // channel half hc = 0 completes A, hc = 1 completes P
+    {
       KDA_PHASE_IDS;
       const int np = tb + 1;
 #pragma unroll
@@ -765,16 +766,23 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
         if (i < np) {
           const int a = i == 0 ? tb : (tb == 1 ? 0 : (tb == 2 ? i - 1 : (i == 1 ? 2 : i - 2)));
           const int pid = pair_id(tb, a);
-          const f32x4 A = accA[i] + *reinterpret_cast<const f32x4*>(PART + ((pid * 2 + 0) * 64 + ln_) * 4);
-          const f32x4 P = accP[i] + *reinterpret_cast<const f32x4*>(PART + ((pid * 2 + 1) * 64 + ln_) * 4);
+          const f32x4 part = *reinterpret_cast<const f32x4*>(PART + ((pid * 2 + hc) * 64 + ln_) * 4);
+          if (hc == 0) {
+            const f32x4 A = accA[i] + part;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int rl = 4 * g4 + q;  // row within the block; column n16
-            const int r = 16 * tb + rl, j = 16 * a + n16;
-            const float av = (a < tb || n16 < rl) ? A[q] * BETA[r] : 0.f;
-            const float pv = (a < tb || n16 <= rl) ? P[q] : 0.f;
-            AM[r * AMS + j] = av;
-            PM[r * TRS + j] = to_f16(pv);
+            for (int q = 0; q < 4; ++q) {
+              const int rl = 4 * g4 + q;  // row within the block; column n16
+              const int r = 16 * tb + rl, j = 16 * a + n16;
+              AM[r * AMS + j] = (a < tb || n16 < rl) ? A[q] * BETA[r] : 0.f;
+            }
+          } else {
+            const f32x4 P = accP[i] + part;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int rl = 4 * g4 + q;
+              const int r = 16 * tb + rl, j = 16 * a + n16;
+              PM[r * TRS + j] = to_f16((a < tb || n16 <= rl) ? P[q] : 0.f);
+            }
           }
         }
       }

@@ -80,37 +80,38 @@ constexpr int L_SO = L_SPH + 4 * D * 4;                 // f32 [4][128] o_b
 constexpr int L_ST1 = L_SO + 4 * D * 4;                 // f32 [128] exp(tau_1)
 constexpr int L_ST2 = L_ST1 + D * 4;                    // f32 [128] exp(tau_2)
 constexpr int L_SGE = L_ST2 + D * 4;                    // f32 [128] Gam_e
-constexpr int L_TD = L_SGE + D * 4;                     // f32 [4][16][17] diagonal blocks of T
-constexpr int L_DTB = L_TD + 4 * 16 * 17 * 4;           // f32 [128] dt_bias of the head
-constexpr int L_DLT = L_DTB + D * 4;                    // f32 [64] beta - bf16 hi - bf16 lo
-constexpr int L_VR = L_DLT + CH * 4;                    // bf16 [64][VRS] v
+constexpr int L_NF = L_SGE + D * 4;                     // bf16 [4 b][2 hl][64 lane][4] T_bb - I
+constexpr int L_LF = L_NF + 4 * 2 * 64 * 8;             // bf16 [6][2 hl][64 lane][4] L_ba, a < b
+constexpr int L_DTB = L_LF + 6 * 2 * 64 * 8;            // f32 [128] dt_bias of the head
+constexpr int L_VR = L_DTB + D * 4;                     // bf16 [64][VRS] v
 constexpr int L_QOP = L_VR + CH * VRS * 2;              // bf16 [4 b][4 kt][64 lane][8]
 constexpr int L_PM = L_QOP + 4 * 4 * 64 * 16;           // fp16 [64][TRS] P
-constexpr int L_TP = L_PM + CH * TRS * 2;               // bf16 [2 hl][64][TRS] T'
-constexpr int L_X1 = L_TP + 2 * CH * TRS * 2;           // region X1 (below)
-constexpr int X1_BYTES = 2 * D * TRS * 2;               //   KGR | AM | WOP | KT
+constexpr int WTS = D + 8;     // bf16 row of W (token-major)
+constexpr int L_WTH = L_PM + CH * TRS * 2;              // bf16 [64][WTS] W, hi part
+constexpr int L_X1 = L_WTH + CH * WTS * 2;              // region X1 (below)
+constexpr int X1_BYTES = 2 * D * TRS * 2;               //   KGR | AM + WTL | KT
 constexpr int L_X2 = L_X1 + X1_BYTES;                   // region X2: PART | XT | OST
 constexpr int X2_BYTES = 2 * D * TRS * 2;
 constexpr int kLdsBytes = L_X2 + X2_BYTES;
 // region X1 tenants
 constexpr int KGR_BYTES = 4 * 2 * 16 * KGS * 2;         // bf16 [4 slots][2 hl][16][KGS]
 constexpr int AM_BYTES = CH * AMS * 4;                  // f32 [64][AMS]
-constexpr int WOP_BYTES = 4 * 4 * 2 * 64 * 16;          // bf16 [4 b][4 kt][2 hl][64][8]
 constexpr int KT_BYTES = 2 * D * TRS * 2;               // fp16 [2 hl][128][TRS]
+constexpr int WTL_BYTES = CH * WTS * 2;                 // bf16 [64][WTS] W, lo part, after AM
 // region X2 tenants
 constexpr int PART_BYTES = 10 * 2 * 256 * 4;            // f32 [10 pairs][A, P][64 lanes][4]
 constexpr int XT_BYTES = 2 * D * TRS * 2;               // bf16 [2 hl][128][TRS]
 constexpr int OSS = D + 8;                              // bf16 row of the staged outputs
 constexpr int OST_BYTES = CH * OSS * 2;                 // bf16 [64][OSS]
-static_assert(KGR_BYTES <= X1_BYTES && AM_BYTES <= X1_BYTES && WOP_BYTES <= X1_BYTES &&
-                  KT_BYTES <= X1_BYTES,
+static_assert(KGR_BYTES <= X1_BYTES && KT_BYTES <= X1_BYTES && AM_BYTES + WTL_BYTES <= X1_BYTES,
               "region X1");
 static_assert(PART_BYTES <= X2_BYTES && XT_BYTES <= X2_BYTES && OST_BYTES <= X2_BYTES,
               "region X2");
 static_assert(kLdsBytes <= 160 * 1024, "LDS of one CU");
-static_assert(L_VR % 16 == 0 && L_QOP % 16 == 0 && L_PM % 16 == 0 && L_TP % 16 == 0 &&
-                  L_X1 % 16 == 0 && L_X2 % 16 == 0 && L_TD % 16 == 0 && L_DTB % 16 == 0 &&
-                  L_DLT % 16 == 0,
+static_assert(L_VR % 16 == 0 && L_QOP % 16 == 0 && L_PM % 16 == 0 && L_WTH % 16 == 0 &&
+                  L_X1 % 16 == 0 && L_X2 % 16 == 0 && L_NF % 16 == 0 && L_LF % 16 == 0 &&
+                  L_DTB % 16 == 0 &&
+                  AM_BYTES % 16 == 0,
               "16-byte aligned arrays");
 
 struct DocOrder {
@@ -167,6 +168,10 @@ __device__ __forceinline__ f32x4 mma_h(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
+typedef short s16x4 __attribute__((ext_vector_type(4)));  // bf16 operands of the K = 16 MFMA
+__device__ __forceinline__ f32x4 mma16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -203,6 +208,13 @@ __device__ __forceinline__ void split8h(const float* x, u32x4& hi, u32x4& lo) {
 }
 __device__ __forceinline__ uint16_t to_f16(float x) {
   return static_cast<uint16_t>(pack_f16x2(x, 0.0f) & 0xffffu);
+}
+
+__device__ __forceinline__ void split4s(const f32x4 x, s16x4& hi, s16x4& lo) {
+  u32x2 h, l;
+  split4(x, h, l);
+  hi = __builtin_bit_cast(s16x4, h);
+  lo = __builtin_bit_cast(s16x4, l);
 }
 
 template <int N>
@@ -373,16 +385,16 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
   float* ST1 = reinterpret_cast<float*>(lds + L_ST1);
   float* ST2 = reinterpret_cast<float*>(lds + L_ST2);
   float* SGE = reinterpret_cast<float*>(lds + L_SGE);
-  float* TD = reinterpret_cast<float*>(lds + L_TD);
+  s16x4* NF = reinterpret_cast<s16x4*>(lds + L_NF);  // A fragments of the K = 16 MFMA
+  s16x4* LF = reinterpret_cast<s16x4*>(lds + L_LF);
   float* DTB = reinterpret_cast<float*>(lds + L_DTB);
-  float* DLT = reinterpret_cast<float*>(lds + L_DLT);
   uint16_t* VR = reinterpret_cast<uint16_t*>(lds + L_VR);
   uint8_t* QOP = lds + L_QOP;
   uint16_t* PM = reinterpret_cast<uint16_t*>(lds + L_PM);
-  uint16_t* TP = reinterpret_cast<uint16_t*>(lds + L_TP);
+  uint16_t* WTH = reinterpret_cast<uint16_t*>(lds + L_WTH);
   uint16_t* KGR = reinterpret_cast<uint16_t*>(lds + L_X1);
   float* AM = reinterpret_cast<float*>(lds + L_X1);
-  uint8_t* WOP = lds + L_X1;
+  uint16_t* WTL = reinterpret_cast<uint16_t*>(lds + L_X1 + AM_BYTES);  // W lo, beside AM
   uint16_t* KT = reinterpret_cast<uint16_t*>(lds + L_X1);
   float* PART = reinterpret_cast<float*>(lds + L_X2);
   uint16_t* XT = reinterpret_cast<uint16_t*>(lds + L_X2);
@@ -433,14 +445,11 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
   // chain identity: value channel of this lane
   const int v = 16 * wave + n16;
 
-  // T' and P above their block diagonal: the blocks a chunk's products read
-  // that are always zero ((0,1) and (2,3)); nothing else writes them.
+  // P above its block diagonal: the blocks the read-out's products read that
+  // are always zero ((0,1) and (2,3)); nothing else writes them.
   for (int e = tid; e < 2 * 256; e += NTHR) {
     const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-    const int row = 32 * blk + r, col = 32 * blk + 16 + cc;
-    TP[row * TRS + col] = 0;
-    TP[CH * TRS + row * TRS + col] = 0;
-    PM[row * TRS + col] = 0;
+    PM[(32 * blk + r) * TRS + 32 * blk + 16 + cc] = 0;
   }
 
   // ---- initial state in the accumulator layout
@@ -524,11 +533,6 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
         const float braw = bf1(uint16_t(raw.b));
         const float bt = valid ? (presig ? braw : fsigmoid(braw)) : 0.f;
         BETA[tr] = bt;
-        // what the bf16 hi + lo pair of T'[t][t] = beta_t leaves out; U0 adds
-        // (this residual) v_t, the largest term of its split error
-        const uint16_t bh = to_bf16(bt);
-        const float br = bt - bf1(bh);
-        DLT[tr] = br - bf1(to_bf16(br));
       }
     }
     lds_barrier();  // b1
@@ -836,132 +840,104 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
         const f32x4 N2z = prod(Nt, Nz), N2t = prodT(Nt, Nz);
         const f32x4 N4z = prod(N2t, N2z), N4t = prodT(N2t, N2z);
         const f32x4 N8z = prod(N4t, N4z);
-        const f32x4 N3z = prod(Nt, N2z), N3t = prodT(Nt, N2z);
-        const f32x4 X1z = ((Id + Nz) + N2z) + N3z, X1t = ((Id + Nt) + N2t) + N3t;
-        const f32x4 X2z = X1z + prod(X1t, N4z), X2t = X1t + prodT(X1t, N4z);
-        const f32x4 Tz = X2z + prod(X2t, N8z);
-        const float bj = BETA[16 * b + n16];
+        const f32x4 N3t = prodT(Nt, N2z);
+        const f32x4 X1t = ((Id + Nt) + N2t) + N3t;
+        const f32x4 X2t = X1t + prodT(X1t, N4z);
+        // T_bb^T in the Z layout is T_bb in the A-operand layout of the K = 16
+        // MFMA (lane: row n16, k = 4 g4 + i); the substitution below takes T_bb - I
+        const f32x4 Nb = (X2t + prodT(X2t, N8z)) - Id;
+        split4s(Nb, NF[(2 * b) * 64 + ln_], NF[(2 * b + 1) * 64 + ln_]);
+      } else if (wave < 7) {
+        // the blocks L_ba (a < b) in the same layout, two per wave:
+        // 0 (1,0), 1 (2,0), 2 (2,1), 3 (3,0), 4 (3,1), 5 (3,2)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = 4 * g4 + q;
-          TD[(b * 16 + r) * 17 + n16] = Tz[q];
-          const float t = Tz[q] * bj;  // T' = T diag(beta)
-          const uint16_t hi = to_bf16(t);
-          TP[(16 * b + r) * TRS + 16 * b + n16] = hi;
-          TP[CH * TRS + (16 * b + r) * TRS + 16 * b + n16] = to_bf16(t - bf1(hi));
+        for (int k = 0; k < 2; ++k) {
+          const int li = 2 * (wave - 4) + k;
+          const int b = li == 0 ? 1 : (li < 3 ? 2 : 3);
+          const int a = li - (b == 1 ? 0 : (b == 2 ? 1 : 3));
+          const f32x4 x = *reinterpret_cast<const f32x4*>(AM + (16 * b + n16) * AMS + 16 * a + 4 * g4);
+          split4s(x, LF[(2 * li) * 64 + ln_], LF[(2 * li + 1) * 64 + ln_]);
         }
       }
     }
     lds_barrier();  // b5
 
-    // ================= P4b: off-diagonal blocks of T (fp32 MFMA), three chains
-    if (wave < 3) {
-      KDA_PHASE_IDS;
-      // k of the 16 x 16 x 4 steps: slot g4 of step ks is index 4 g4 + ks
-      auto L_a = [&](int b, int cc, int ks) { return AM[(16 * b + n16) * AMS + 16 * cc + 4 * g4 + ks]; };
-      auto TD_b = [&](int a, int ks) { return TD[(a * 16 + 4 * g4 + ks) * 17 + n16]; };  // T_aa[k][n]
-      auto TD_a = [&](int b, int ks) { return TD[(b * 16 + n16) * 17 + 4 * g4 + ks]; };  // T_bb[m][k]
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      // M += L_bc T_cc (diagonal T block from LDS)
-      auto mul_Ld = [&](f32x4 M, int b, int cc) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) M = mma_f32(L_a(b, cc, ks), TD_b(cc, ks), M);
-        return M;
-      };
-      // M += L_bc X (X an off-diagonal T block in the accumulator layout)
-      auto mul_Lx = [&](f32x4 M, int b, int cc, f32x4 X) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) M = mma_f32(L_a(b, cc, ks), X[ks], M);
-        return M;
-      };
-      // -T_bb M
-      auto neg_Tb = [&](int b, f32x4 M) {
-        f32x4 r = z;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) r = mma_f32(TD_a(b, ks), M[ks], r);
-        return -r;
-      };
-      auto put = [&](int b, int a, f32x4 T) {
-        const float bj = BETA[16 * a + n16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = 16 * b + 4 * g4 + q, j = 16 * a + n16;
-          const float t = T[q] * bj;
-          const uint16_t hi = to_bf16(t);
-          TP[r * TRS + j] = hi;
-          TP[CH * TRS + r * TRS + j] = to_bf16(t - bf1(hi));
-        }
-      };
-      if (wave == 0) {
-        const f32x4 T10 = neg_Tb(1, mul_Ld(z, 1, 0));
-        put(1, 0, T10);
-        const f32x4 T20 = neg_Tb(2, mul_Lx(mul_Ld(z, 2, 0), 2, 1, T10));
-        put(2, 0, T20);
-        const f32x4 T30 = neg_Tb(3, mul_Lx(mul_Lx(mul_Ld(z, 3, 0), 3, 1, T10), 3, 2, T20));
-        put(3, 0, T30);
-      } else if (wave == 1) {
-        const f32x4 T21 = neg_Tb(2, mul_Ld(z, 2, 1));
-        put(2, 1, T21);
-        const f32x4 T31 = neg_Tb(3, mul_Lx(mul_Ld(z, 3, 1), 3, 2, T21));
-        put(3, 1, T31);
-      } else {
-        const f32x4 T32 = neg_Tb(3, mul_Ld(z, 3, 2));
-        put(3, 2, T32);
-      }
-    }
-    lds_barrier();  // b6
-
-    // ================= P5: W^T = x^T T'^T (wave: channel tile) and U0 = T' V (wave: value tile)
+    // ================= P5: W = T' X and U0 = T' V, T' = (I + L)^-1 diag(beta), by
+    // blocked forward substitution: Y_b = T_bb (beta_b R_b - sum_{a<b} L_ba Y_a).
+    // Wave w takes the channel tile 16 w.. of X (W, to LDS token-major) and the
+    // value tile 16 w.. of V (U0, kept for C1); the blocks are 16 x 16 x 16 bf16
+    // MFMAs with hi + lo operands (three terms). beta enters in fp32 and the unit
+    // diagonal of T_bb exactly: only the products L_ba Y_a and (T_bb - I) Z_b
+    // are split.
     f32x4 u0[4];
     {
       KDA_PHASE_IDS;
-      u32x4 vb[2];
+      // A operands (lane: row n16, k = 4 g4 + e): L_10, L_20, L_21, L_30, L_31, L_32
+      // and N_b = T_bb - I
+      s16x4 lh[6], ll[6], nh[4], nl[4];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int r0 = 32 * s + 8 * g4 + 2 * w;
-          vb[s][w] = uint32_t(VR[r0 * VRS + v]) | (uint32_t(VR[(r0 + 1) * VRS + v]) << 16);
-        }
+      for (int li = 0; li < 6; ++li) {
+        lh[li] = LF[(2 * li) * 64 + ln_];
+        ll[li] = LF[(2 * li + 1) * 64 + ln_];
       }
-      const uint16_t* xtr_h = XT + (16 * wave + n16) * TRS;
-      const uint16_t* xtr_l = XT + D * TRS + (16 * wave + n16) * TRS;
-      const u32x4 xa_h0 = *reinterpret_cast<const u32x4*>(xtr_h + 8 * g4);
-      const u32x4 xa_l0 = *reinterpret_cast<const u32x4*>(xtr_l + 8 * g4);
-      const u32x4 xa_h1 = *reinterpret_cast<const u32x4*>(xtr_h + 32 + 8 * g4);
-      const u32x4 xa_l1 = *reinterpret_cast<const u32x4*>(xtr_l + 32 + 8 * g4);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 w0 = z, w1 = z, w2 = z, uu = z;
+        nh[b] = NF[(2 * b) * 64 + ln_];
+        nl[b] = NF[(2 * b + 1) * 64 + ln_];
+      }
+      // the solved blocks Y_a of both tiles, split (B operands of the later blocks)
+      s16x4 yh[2][4], yl[2][4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          if (s == 1 && b < 2) continue;
-          const u32x4 th = *reinterpret_cast<const u32x4*>(TP + (16 * b + n16) * TRS + 32 * s + 8 * g4);
-          const u32x4 tl =
-              *reinterpret_cast<const u32x4*>(TP + CH * TRS + (16 * b + n16) * TRS + 32 * s + 8 * g4);
-          const u32x4 xh8 = s ? xa_h1 : xa_h0;
-          const u32x4 xl8 = s ? xa_l1 : xa_l0;
-          w0 = mma(xh8, th, w0);
-          w1 = mma(xh8, tl, w1);
-          w2 = mma(xl8, th, w2);
-          uu = mma(th, vb[s], uu);
-          uu = mma(tl, vb[s], uu);
-        }
-        {  // + (beta_t - its bf16 hi + lo) v_t, the diagonal's split residual
-          const f32x4 dl = *reinterpret_cast<const f32x4*>(DLT + 16 * b + 4 * g4);
+      for (int b = 0; b < 4; ++b) {
+        const f32x4 bet = *reinterpret_cast<const f32x4*>(BETA + 16 * b + 4 * g4);
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            uu[q] = fmaf(dl[q], bf1(VR[(16 * b + 4 * g4 + q) * VRS + v]), uu[q]);
+        for (int tile = 0; tile < 2; ++tile) {
+          f32x4 r;  // R rows 16 b + 4 g4 + i, column n16 of the tile
+          if (tile == 0) {  // X = hi + lo of x^T, channel 16 wave + n16
+            const u32x2 h2 = *reinterpret_cast<const u32x2*>(XT + (16 * wave + n16) * TRS + 16 * b + 4 * g4);
+            const u32x2 l2 =
+                *reinterpret_cast<const u32x2*>(XT + D * TRS + (16 * wave + n16) * TRS + 16 * b + 4 * g4);
+            r = f32x4{bf_lo(h2[0]) + bf_lo(l2[0]), bf_hi(h2[0]) + bf_hi(l2[0]),
+                      bf_lo(h2[1]) + bf_lo(l2[1]), bf_hi(h2[1]) + bf_hi(l2[1])};
+          } else {  // V, value channel v
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[i] = bf1(VR[(16 * b + 4 * g4 + i) * VRS + v]);
+          }
+          f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+          const int l0 = b == 1 ? 0 : (b == 2 ? 1 : 3);  // first L block of row b
+#pragma unroll
+          for (int a = 0; a < b; ++a) {
+            sum = mma16(lh[l0 + a], yh[tile][a], sum);
+            sum = mma16(lh[l0 + a], yl[tile][a], sum);
+            sum = mma16(ll[l0 + a], yh[tile][a], sum);
+          }
+          const f32x4 z = r * bet - sum;
+          s16x4 zh, zl;
+          split4s(z, zh, zl);
+          f32x4 t = {0.f, 0.f, 0.f, 0.f};
+          t = mma16(nh[b], zh, t);
+          t = mma16(nh[b], zl, t);
+          t = mma16(nl[b], zh, t);
+          const f32x4 y = z + t;
+          split4s(y, yh[tile][b], yl[tile][b]);
+          if (tile == 1) {
+            u0[b] = y;
+          } else {
+            // W rows 16 b + 4 g4 + i, key channel c = 16 wave + n16, stored at
+            // 32 (c >> 5) + 8 ((c & 15) >> 2) + 4 ((c >> 4) & 1) + (c & 3): C1's
+            // eight channels of one operand (the state fragment's order) are
+            // then one contiguous 16-byte piece
+            const u32x2 hb = __builtin_bit_cast(u32x2, yh[0][b]);
+            const u32x2 lb = __builtin_bit_cast(u32x2, yl[0][b]);
+            const int pc = 32 * (wave >> 1) + 8 * (n16 >> 2) + 4 * (wave & 1) + (n16 & 3);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int o = (16 * b + 4 * g4 + i) * WTS + pc;
+              WTH[o] = uint16_t(i & 1 ? hb[i >> 1] >> 16 : hb[i >> 1] & 0xffffu);
+              WTL[o] = uint16_t(i & 1 ? lb[i >> 1] >> 16 : lb[i >> 1] & 0xffffu);
+            }
+          }
         }
-        u0[b] = uu;
-        // W^T[16 wave + 4 g4 + i][16 b + n16] -> the chain's W fragment (b, kt = wave / 2)
-        const f32x4 wv = w0 + (w1 + w2);
-        u32x2 hi, lo;
-        split4(wv, hi, lo);
-        uint8_t* dst = WOP + ((b * 4 + (wave >> 1)) * 2 * 64 + ln_) * 16 + 8 * (wave & 1);
-        *reinterpret_cast<u32x2*>(dst) = hi;
-        *reinterpret_cast<u32x2*>(dst + 64 * 16) = lo;
       }
     }
     lds_barrier();  // b7
@@ -991,9 +967,11 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
         f32x4 y0 = z, y1 = z, y2 = z, yq = z;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          const uint8_t* wf = WOP + ((b * 4 + kt) * 2 * 64 + ln_) * 16;
-          const u32x4 wh = *reinterpret_cast<const u32x4*>(wf);
-          const u32x4 wl = *reinterpret_cast<const u32x4*>(wf + 64 * 16);
+          // W row 16 b + n16, key channels 32 kt + 4 g4 .. +3 and 32 kt + 16 + 4 g4 .. +3
+          // (the order of the state's B fragment), stored contiguously
+          const int wo = (16 * b + n16) * WTS + 32 * kt + 8 * g4;
+          const u32x4 wh = *reinterpret_cast<const u32x4*>(WTH + wo);
+          const u32x4 wl = *reinterpret_cast<const u32x4*>(WTL + wo);
           const u32x4 qq = *reinterpret_cast<const u32x4*>(QOP + ((b * 4 + kt) * 64 + ln_) * 16);
           y0 = mma(wh, sh[kt], y0);
           y1 = mma(wh, sl[kt], y1);

@@ -885,6 +885,18 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
         nh[b] = NF[(2 * b) * 64 + ln_];
         nl[b] = NF[(2 * b + 1) * 64 + ln_];
       }
+      // R rows 16 b + 4 g4 + i, column n16 of the tile, all read up front (the
+      // blocks below form one dependent chain): X as hi + lo of x^T (channel
+      // 16 wave + n16), V (value channel v)
+      u32x2 xh2[4], xl2[4];
+      uint16_t vr[4][4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        xh2[b] = *reinterpret_cast<const u32x2*>(XT + (16 * wave + n16) * TRS + 16 * b + 4 * g4);
+        xl2[b] = *reinterpret_cast<const u32x2*>(XT + D * TRS + (16 * wave + n16) * TRS + 16 * b + 4 * g4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vr[b][i] = VR[(16 * b + 4 * g4 + i) * VRS + v];
+      }
       // the solved blocks Y_a of both tiles, split (B operands of the later blocks)
       s16x4 yh[2][4], yl[2][4];
 #pragma unroll
@@ -892,25 +904,41 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
         const f32x4 bet = *reinterpret_cast<const f32x4*>(BETA + 16 * b + 4 * g4);
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile) {
-          f32x4 r;  // R rows 16 b + 4 g4 + i, column n16 of the tile
-          if (tile == 0) {  // X = hi + lo of x^T, channel 16 wave + n16
-            const u32x2 h2 = *reinterpret_cast<const u32x2*>(XT + (16 * wave + n16) * TRS + 16 * b + 4 * g4);
-            const u32x2 l2 =
-                *reinterpret_cast<const u32x2*>(XT + D * TRS + (16 * wave + n16) * TRS + 16 * b + 4 * g4);
+          f32x4 r;
+          if (tile == 0) {
+            const u32x2 h2 = xh2[b], l2 = xl2[b];
             r = f32x4{bf_lo(h2[0]) + bf_lo(l2[0]), bf_hi(h2[0]) + bf_hi(l2[0]),
                       bf_lo(h2[1]) + bf_lo(l2[1]), bf_hi(h2[1]) + bf_hi(l2[1])};
-          } else {  // V, value channel v
+          } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) r[i] = bf1(VR[(16 * b + 4 * g4 + i) * VRS + v]);
+            for (int i = 0; i < 4; ++i) r[i] = bf1(vr[b][i]);
           }
-          f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+          // Blocks 0 and 1 go into one K = 32 product (operands concatenated). The
+          // 16 x 16 x 32 and 16 x 16 x 16 products keep separate accumulators,
+          // summed on the VALU: a chain in which one shape's result is the
+          // other's accumulator input gave wrong results.
+          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+          f32x4 sum = zero, s16 = zero;
           const int l0 = b == 1 ? 0 : (b == 2 ? 1 : 3);  // first L block of row b
+          if (b >= 2) {
+            auto cat = [](s16x4 x, s16x4 y) {
+              const u32x2 a = __builtin_bit_cast(u32x2, x), c = __builtin_bit_cast(u32x2, y);
+              return u32x4{a[0], a[1], c[0], c[1]};
+            };
+            const u32x4 lh2 = cat(lh[l0], lh[l0 + 1]), ll2 = cat(ll[l0], ll[l0 + 1]);
+            const u32x4 yh2 = cat(yh[tile][0], yh[tile][1]), yl2 = cat(yl[tile][0], yl[tile][1]);
+            sum = mma(lh2, yh2, sum);
+            sum = mma(lh2, yl2, sum);
+            sum = mma(ll2, yh2, sum);
+          }
 #pragma unroll
           for (int a = 0; a < b; ++a) {
-            sum = mma16(lh[l0 + a], yh[tile][a], sum);
-            sum = mma16(lh[l0 + a], yl[tile][a], sum);
-            sum = mma16(ll[l0 + a], yh[tile][a], sum);
+            if (b >= 2 && a < 2) continue;
+            s16 = mma16(lh[l0 + a], yh[tile][a], s16);
+            s16 = mma16(lh[l0 + a], yl[tile][a], s16);
+            s16 = mma16(ll[l0 + a], yh[tile][a], s16);
           }
+          sum += s16;
           const f32x4 z = r * bet - sum;
           s16x4 zh, zl;
           split4s(z, zh, zl);

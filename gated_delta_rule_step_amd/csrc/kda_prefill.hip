@@ -439,7 +439,9 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
   const int64_t ring0 = (int64_t(slot) * p.H + h) * int64_t(p.ring_rows);
 
   // token-owner identity
-  const int tb = wave >> 1, hc = wave & 1;
+  // waves w and w + 4 share a SIMD: blocks 0 and 3 (the lightest and the
+  // heaviest operand and pair work) pair up, and blocks 1 and 2
+  const int tb = (wave >> 1) ^ (wave >> 2), hc = wave & 1;
   const int tr = 16 * tb + n16;        // token of this lane within the chunk
   const int cb = 64 * hc + 8 * g4;     // first channel of the lane's two runs of 8
   // chain identity: value channel of this lane
@@ -584,8 +586,8 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_kernel(PrefillParams p, DocOr
     f32x4 accA[4], accP[4];           // this wave's partial sums of its pairs
     {
       KDA_PHASE_IDS;
-      const float rq = 1.0f / sqrtf(NRM[tr * 2] + NRM[(CH + tr) * 2] + 1e-6f);
-      const float rk = 1.0f / sqrtf(NRM[tr * 2 + 1] + NRM[(CH + tr) * 2 + 1] + 1e-6f);
+      const float rq = __builtin_amdgcn_rsqf(NRM[tr * 2] + NRM[(CH + tr) * 2] + 1e-6f);
+      const float rk = __builtin_amdgcn_rsqf(NRM[tr * 2 + 1] + NRM[(CH + tr) * 2 + 1] + 1e-6f);
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i) accA[i] = accP[i] = z;

@@ -24,15 +24,16 @@
 // last token, or the last one before a hand-off tail). The lines up to U0 do
 // not depend on the state ("preparation"); the last three are the chain.
 //
-// Precision. Every product the state depends on (A, W, U0, W S, the state
-// update) runs on bf16 MFMA with its fp32 operands split into bf16 hi + lo
-// parts and three terms (hi hi + hi lo + lo hi; V is exact in bf16, so U0
-// needs two); T is formed in fp32 on fp32 MFMA (diagonal 16 x 16 blocks as
-// the finite product (I + N)(I + N^2)(I + N^4)(I + N^8) of their strictly
-// lower part N = -diag(beta) A, the others by block substitution). P takes
-// three terms as well and is stored in bf16; the read-out products take the
-// state and U in two terms against the bf16 exp(Gam) q and P; O is stored in
-// bf16.
+// Precision. The products the state depends on (A, W S) run on bf16 MFMA
+// with their fp32 operands split into bf16 hi + lo parts and three terms
+// (hi hi + hi lo + lo hi). T' is never formed: the diagonal 16 x 16 blocks
+// of T are the finite product (I + N)(I + N^2)(I + N^4)(I + N^8) of their
+// strictly lower part N = -diag(beta) A, on fp32 MFMA; W and U0 then follow
+// by blocked forward substitution over the four 16-token blocks on bf16
+// MFMA, three terms, with beta and the unit diagonals applied exactly in
+// fp32. The state update and P U take fp16 hi + lo (three and two terms),
+// P is stored in fp16 (|P| <= 1); O = (exp(Gam) q) S takes the state in two
+// terms against the bf16 exp(Gam) q. O is stored in bf16.
 //
 // Decay factoring. A chunk is four 16-token blocks b (block-local prefix
 // lam_r, block total tau_b, block start o_b = Gam at the token before it).
@@ -43,8 +44,9 @@
 // negligible: pairs (1,0), (2,1) at o_1, o_2; (3,2) at o_3; (2,0), (3,0),
 // (3,1) at o_2.
 //
-// Layouts. Token-owner phases: wave w holds block b = w/2 and key channels
-// 64 (w%2) + 32 s + 8 (lane/16) + i, i < 8, of token 16 b + lane%16; chain
+// Layouts. Token-owner phases: wave w holds block b = (w/2) xor (w/4) (blocks
+// 0 and 3, and 1 and 2, share a SIMD) and key channels 64 (w%2) + 32 s +
+// 8 (lane/16) + i, i < 8, of token 16 b + lane%16; chain
 // phases: wave w owns value channels 16 w .. 16 w + 15 of the fp32 state,
 // held as eight 16 x 16 accumulator tiles (key channels 16 m + 4 (lane/16) + i).
 

@@ -67,7 +67,7 @@ constexpr int kMaxOrderedDocs = 256;
 // only when a barrier separates the last read from the first write.
 constexpr int VRS = D + 8;     // bf16 row of v (token-major)
 constexpr int KGS = D + 8;     // bf16 row of the right operands of A / P
-constexpr int TRS = CH + 8;    // bf16 row of channel-major arrays (x^T, k~^T) and of T', P
+constexpr int TRS = CH + 4;    // 16-bit row of channel-major arrays (x^T, k~^T) and of P
 constexpr int AMS = CH + 4;    // fp32 row of A (scaled by beta)
 
 constexpr int L_NRM = 0;                                // f32 [2][64][2] norm partials

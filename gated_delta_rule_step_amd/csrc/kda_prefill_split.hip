@@ -654,30 +654,37 @@ __global__ __launch_bounds__(kThreads) void handoff_kernel(PrefillParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Chain: one 512-thread workgroup per (document, head), documents longest
-// first. Wave w keeps value channels 16w .. 16w+15 of the fp32 state in
-// registers (two waves per SIMD, so one wave's MFMA and LDS latencies overlap
-// the other's arithmetic). Chunk records move HBM -> registers one chunk
-// ahead of use and registers -> LDS (double buffer) one chunk ahead, so a
-// chunk's operands are in LDS when it starts and the next record's loads
-// overlap its arithmetic.
-//
-// With few chains (documents x heads below the CU count) each chain is split
-// by value channels over VS = 2 workgroups of 4 waves on different CUs: the
-// value channels of the state evolve independently, and a CU then holds one
-// wave per SIMD instead of two, so a chunk's VALU and MFMA issue per SIMD
-// halves. Each part stages the record's shared operands (W, Q, K~, P,
-// exp(Gam_c)) and only its own U0 tiles.
-template <int VS>
+// Chain: the chunks of one (document, head) in order, documents longest first.
+// The value channels of the state evolve independently given the records, so
+// a chain is split by value channels over VS workgroups (parts), and within a
+// part each 16-channel value tile may be split by key channels over KS = 2
+// waves. A wave keeps its tile of the fp32 state (16 value channels x 128 / KS
+// key channels) in registers, in the MFMA accumulator layout. With KS = 2 the
+// two waves of a tile each form half of the contraction W S over their key
+// channels and exchange the partial sums through LDS (one extra barrier per
+// chunk); both then hold the same U and update their own key channels. Fewer
+// key channels per wave halve its MFMA and VALU issue per chunk, which bounds
+// the chain when each SIMD holds one wave. Chunk records move HBM -> registers
+// one chunk ahead of use and registers -> LDS (double buffer) one chunk
+// ahead; each part stages the record's shared operands (W, Q, K~, P,
+// exp(Gam_c)) and only its own U0 tiles. The VS parts of a chain are blocks
+// b, b + 8, ..., so that they run on one XCD (blocks go to the XCDs in turn)
+// and share its L2 copy of the records.
+template <int VS, int KS>
 struct ChainShape {
-  static constexpr int kThreads = 512 / VS;
-  static constexpr int kWaves = 8 / VS;                     // value tiles of 16 channels
+  static constexpr int kTiles = 8 / VS;                     // value tiles of 16 channels
+  static constexpr int kWaves = kTiles * KS;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kAcc = 8 / KS;                       // state tiles (16 keys) per wave
   static constexpr int kShared = kRecU0 / 16;               // W, Q, K~ units
-  static constexpr int kOwnU0 = kWaves * 64;                // this part's U0 units
+  static constexpr int kOwnU0 = kTiles * 64;                // this part's U0 units
   static constexpr int kTail = kRecUnits - kRecP / 16;      // P, exp(Gam_c) units
   static constexpr int kUnits = kShared + kOwnU0 + kTail;   // units staged per chunk
   static constexpr int kRounds = (kUnits + kThreads - 1) / kThreads;
+  // partial sums exchanged per tile: W S and (e^Gam q) S of both halves
+  static constexpr int kXchBytes = KS == 1 ? 16 : kTiles * 4 * 64 * 16;
   static_assert(kUnits > (kRounds - 1) * kThreads, "every round has work");
+  static_assert(KS == 1 || KS == 2, "key split");
   // record unit of staged unit i (< kUnits) of part `part`
   __device__ static int unit(int i, int part) {
     if (i < kShared) return i;
@@ -685,27 +692,36 @@ struct ChainShape {
     return kRecP / 16 + (i - kShared - kOwnU0);
   }
 };
-static_assert(ChainShape<1>::kUnits == kRecUnits, "the whole record");
+static_assert(ChainShape<1, 1>::kUnits == kRecUnits, "the whole record");
 
 // SF: the element format of the pool (initial and final states) and the
-// checkpoints (kStateBf16, kStateFp16, kStateFp8). VS: workgroups per chain.
-template <bool VEC, int SF, int VS>
-__global__ __launch_bounds__(ChainShape<VS>::kThreads) void chain_kernel(PrefillParams p,
-                                                                        DocOrder ord) {
-  using Shape = ChainShape<VS>;
+// checkpoints (kStateBf16, kStateFp16, kStateFp8). VS: workgroups per chain;
+// KS: waves per value tile.
+template <bool VEC, int SF, int VS, int KS>
+__global__ __launch_bounds__((ChainShape<VS, KS>::kThreads)) void chain_kernel(PrefillParams p,
+                                                                              DocOrder ord) {
+  using Shape = ChainShape<VS, KS>;
   constexpr int kChainThreads = Shape::kThreads;
   constexpr int kChainRounds = Shape::kRounds;
+  constexpr int kAcc = Shape::kAcc;
   __shared__ __align__(16) uint8_t rbuf[2][kRecBytes];
+  __shared__ __align__(16) uint8_t xch[Shape::kXchBytes];
+  // block -> (chain, part): chain c's parts are blocks (c / 8 * VS + part) * 8 + c % 8
+  const int bid = int(blockIdx.x);
+  const int chain = (bid / (8 * VS)) * 8 + (bid & 7);
+  const int part = (bid >> 3) % VS;
+  if (chain >= p.n_docs * p.H) return;  // the grid rounds the chains up to a multiple of 8
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g4 = lane >> 4;
   const int n16 = lane & 15;
-  const int part = int(blockIdx.x % VS);
-  const int vt = part * Shape::kWaves + wave;  // value tile of this wave
+  const int tile = wave / KS;                  // value tile within the part
+  const int kh = wave % KS;                    // key half (KS = 2)
+  const int vt = part * Shape::kTiles + tile;  // value tile of this wave
   const int v = 16 * vt + n16;                 // value channel of this lane
-  const int h = int((blockIdx.x / VS) % p.H);
-  const int rank = int(blockIdx.x / VS / p.H);
+  const int h = chain % p.H;
+  const int rank = chain / p.H;
   const int doc = ord.n > 0 ? ord.doc[rank] : rank;
   const int64_t t0 = p.cu_seqlens[doc];
   const int64_t len = int64_t(p.cu_seqlens[doc + 1]) - t0;
@@ -770,32 +786,35 @@ __global__ __launch_bounds__(ChainShape<VS>::kThreads) void chain_kernel(Prefill
 
   load_rec(0);
 
-  // ---- initial state into the accumulator layout (all 8 loads issued
-  // before any is waited for)
-  f32x4 acc[8];
+  // ---- initial state into the accumulator layout: this wave's state tiles
+  // mt = kAcc kh + m (key channels 16 mt ..), all loads issued before any wait
+  f32x4 acc[kAcc];
+  const int mt0 = kAcc * kh;
   if (p.use_initial_state) {
     if constexpr (SF == kStateFp8) {
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-        acc[mt] = st4_load<SF, VEC>(p.state_pool, se + v * D + 16 * mt + 4 * g4);
+      for (int m = 0; m < kAcc; ++m)
+        acc[m] = st4_load<SF, VEC>(p.state_pool, se + v * D + 16 * (mt0 + m) + 4 * g4);
     } else {
       const uint16_t* sp = static_cast<const uint16_t*>(p.state_pool) + se;
-      u32x2 w[8];
+      u32x2 w[kAcc];
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) w[mt] = gload4<VEC>(sp + v * D + 16 * mt + 4 * g4);
+      for (int m = 0; m < kAcc; ++m) w[m] = gload4<VEC>(sp + v * D + 16 * (mt0 + m) + 4 * g4);
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-        acc[mt] = f32x4{st_lo<SF>(w[mt][0]), st_hi<SF>(w[mt][0]), st_lo<SF>(w[mt][1]),
-                        st_hi<SF>(w[mt][1])};
+      for (int m = 0; m < kAcc; ++m)
+        acc[m] = f32x4{st_lo<SF>(w[m][0]), st_hi<SF>(w[m][0]), st_lo<SF>(w[m][1]),
+                       st_hi<SF>(w[m][1])};
     }
   } else {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < kAcc; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   store_rec(0);
   load_rec(min(1, nchunks - 1));
   __syncthreads();
 
+  // the exchanged partial sums of this wave's tile: W S [half][lane], then (e^Gam q) S
+  f32x4* xw = reinterpret_cast<f32x4*>(xch) + tile * 4 * 64;
   const int ots32 = static_cast<int>(p.out_tok_stride);  // host-checked to fit a buffer range
   f32x4 u_last = {0.f, 0.f, 0.f, 0.f};  // U of the last chunk (rows 4 g4 + i)
   for (int ch = 0; ch < nchunks; ++ch) {
@@ -809,16 +828,18 @@ __global__ __launch_bounds__(ChainShape<VS>::kThreads) void chain_kernel(Prefill
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
         p.out + tc0 * p.out_tok_stride + h * D, 0,
         static_cast<int>(((c - 1) * p.out_tok_stride + D) * 2), kBufferWord3);
-    // W S^T in three hi/lo terms (one accumulator each, so the products do
-    // not wait on each other) and (e^Gam q) S^T in one
+    // W S^T over this wave's key channels in three hi/lo terms (one
+    // accumulator each, so the products do not wait on each other) and
+    // (e^Gam q) S^T in one
     f32x4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = y0, y2 = y0, yq = y0;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int j = 0; j < kAcc / 2; ++j) {
+      const int kt = kAcc / 2 * kh + j;  // 32 key channels: state tiles 2 kt, 2 kt + 1
       const bf16x8 whi = *reinterpret_cast<const bf16x8*>(R + kRecW + ((2 * kt) * 64 + lane) * 16);
       const bf16x8 wlo =
           *reinterpret_cast<const bf16x8*>(R + kRecW + ((2 * kt + 1) * 64 + lane) * 16);
       const bf16x8 qhi = *reinterpret_cast<const bf16x8*>(R + kRecQ + (kt * 64 + lane) * 16);
-      const f32x4 s0 = acc[2 * kt], s1 = acc[2 * kt + 1];
+      const f32x4 s0 = acc[2 * j], s1 = acc[2 * j + 1];
       const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
       bf16x8 shi, slo;
       split8(sv, shi, slo);
@@ -829,32 +850,47 @@ __global__ __launch_bounds__(ChainShape<VS>::kThreads) void chain_kernel(Prefill
     }
     // U = U0 - W S^T (accumulator layout: rows 4*g4 + i, value channel of the lane)
     const f32x4 u0 = *reinterpret_cast<const f32x4*>(R + kRecU0 + (vt * 64 + lane) * 16);
-    const f32x4 uf = u0 - (y0 + (y1 + y2));
+    f32x4 ws_ = y0 + (y1 + y2);
+    if constexpr (KS == 2) {
+      // both halves publish their partial sums and add the other's: the
+      // totals are the same in both waves (addition commutes exactly)
+      xw[kh * 64 + lane] = ws_;
+      xw[(2 + kh) * 64 + lane] = yq;
+      __syncthreads();
+      ws_ += xw[(kh ^ 1) * 64 + lane];
+      yq += xw[(2 + (kh ^ 1)) * 64 + lane];
+    }
+    const f32x4 uf = u0 - ws_;
     s16x4 uhi, ulo;
     split4(uf, uhi, ulo);
     u_last = uf;
     // O = scale ((e^Gam q) S^T + P U); rows r >= c fall outside the buffer
-    // range and are dropped by the store itself
-    const s16x4 pfr = *reinterpret_cast<const s16x4*>(R + kRecP + lane * 8);
-    const f32x4 o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pfr, uhi, yq, 0, 0, 0);
+    // range and are dropped by the store itself. With KS = 2 each wave of the
+    // tile stores half of the lane's rows: every wave issues the same stores,
+    // so the wait for the next record's loads need not cover them.
+    {
+      const s16x4 pfr = *reinterpret_cast<const s16x4*>(R + kRecP + lane * 8);
+      const f32x4 o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pfr, uhi, yq, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g4 + i;
-      __builtin_amdgcn_raw_buffer_store_b16(to_bf16(p.scale * o[i]), orsrc, (r * ots32 + v) * 2,
-                                            0, kStoreNontemporal);
+      for (int i = 0; i < 4 / KS; ++i) {
+        const int r = 4 * g4 + 4 / KS * kh + i;
+        __builtin_amdgcn_raw_buffer_store_b16(to_bf16(p.scale * o[4 / KS * kh + i]), orsrc,
+                                              (r * ots32 + v) * 2, 0, kStoreNontemporal);
+      }
     }
     // S = S diag(e^Gam_last) + U^T K~  (contraction over the chunk's tokens)
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
+    for (int m = 0; m < kAcc; ++m) {
+      const int mt = mt0 + m;
       const u32x4 kk = *reinterpret_cast<const u32x4*>(R + kRecKT + (mt * 64 + lane) * 16);
       const s16x4 khi = __builtin_bit_cast(s16x4, u32x2{kk[0], kk[1]});
       const s16x4 klo = __builtin_bit_cast(s16x4, u32x2{kk[2], kk[3]});
       const f32x4 e4 = *reinterpret_cast<const f32x4*>(R + kRecEG + (16 * mt + 4 * g4) * 4);
-      f32x4 a = acc[mt] * e4;
+      f32x4 a = acc[m] * e4;
       a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(khi, uhi, a, 0, 0, 0);
       a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(khi, ulo, a, 0, 0, 0);
       a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(klo, uhi, a, 0, 0, 0);
-      acc[mt] = a;
+      acc[m] = a;
     }
     // record ch+1 (its loads were issued a chunk ago) into the other buffer,
     // last read before the previous barrier; then the loads of record ch+2
@@ -866,14 +902,15 @@ __global__ __launch_bounds__(ChainShape<VS>::kThreads) void chain_kernel(Prefill
       if (row >= 0 && row < p.ckpt_rows) {
         const int64_t ce = (row * p.H + h) * int64_t(HEAD_ELEMS);
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-          st4_store<SF, VEC>(p.ckpt, ce + v * D + 16 * mt + 4 * g4, acc[mt]);
+        for (int m = 0; m < kAcc; ++m)
+          st4_store<SF, VEC>(p.ckpt, ce + v * D + 16 * (mt0 + m) + 4 * g4, acc[m]);
       }
     }
-    __syncthreads();  // this chunk's buffer is read; the next one is written
+    // this chunk's buffer and exchange slots are read; the next ones are written
+    __syncthreads();
   }
 
-  if (tail > 0) {  // hand-off: ring rows of the tail tokens receive u (bf16)
+  if (tail > 0 && kh == 0) {  // hand-off: ring rows of the tail tokens receive u (bf16)
     uint16_t* ur = p.u_cache + (int64_t(slot) * p.H + h) * p.ring_rows * int64_t(D) + v;
     const int pe = c_last - tail;
 #pragma unroll
@@ -886,8 +923,8 @@ __global__ __launch_bounds__(ChainShape<VS>::kThreads) void chain_kernel(Prefill
 
   // ---- final state (the state after the first `kept` tokens)
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
-    st4_store<SF, VEC>(p.state_pool, se + v * D + 16 * mt + 4 * g4, acc[mt]);
+  for (int m = 0; m < kAcc; ++m)
+    st4_store<SF, VEC>(p.state_pool, se + v * D + 16 * (mt0 + m) + 4 * g4, acc[m]);
 }
 
 size_t prefill_split_workspace_bytes(int32_t n_docs, int64_t total_tokens, int32_t H) {
@@ -899,7 +936,7 @@ hipError_t launch_prefill_split(const PrefillParams& p, const int32_t* cu_host, 
                                 hipStream_t stream) {
   const int64_t blocks = int64_t(p.n_docs) * p.H;
   if (blocks == 0) return hipSuccess;
-  if (2 * blocks > 0x7fffffff || p.H > 65535) return hipErrorInvalidValue;
+  if (blocks > (int64_t(0x7fffffff) >> 5) || p.H > 65535) return hipErrorInvalidValue;
   const int64_t slots = int64_t(p.n_docs) + (p.total_tokens >> 4);
   if (slots > 0x7fffffff) return hipErrorInvalidValue;
   // Longest documents first: their chains bound the makespan.
@@ -974,13 +1011,15 @@ hipError_t launch_prefill_split(const PrefillParams& p, const int32_t* cu_host, 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // Fewer chains than CUs (always the case on this path): two workgroups per
-  // chain, by value channels.
+  // Fewer chains than CUs (always the case on this path): four workgroups per
+  // chain (by value channels) of two waves per value tile (by key channels),
+  // one wave per SIMD. Beyond 64 chains two workgroups share a CU.
   // fp16 and fp8 states run on the vectorised path only (the host requires it)
   if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
-#define KDA_CHAIN_LAUNCH(V, S)                                                            \
-  hipLaunchKernelGGL((chain_kernel<V, S, 2>), dim3(static_cast<unsigned>(2 * blocks)),    \
-                     dim3(ChainShape<2>::kThreads), 0, stream, p, ord)
+  const int64_t groups = (blocks + 7) / 8;  // chains, in groups of 8 (one per XCD)
+#define KDA_CHAIN_LAUNCH(V, S)                                                              \
+  hipLaunchKernelGGL((chain_kernel<V, S, 4, 2>), dim3(static_cast<unsigned>(groups * 32)), \
+                     dim3(ChainShape<4, 2>::kThreads), 0, stream, p, ord)
   if (p.state_fmt == kStateFp16) KDA_CHAIN_LAUNCH(true, kStateFp16);
   else if (p.state_fmt == kStateFp8) KDA_CHAIN_LAUNCH(true, kStateFp8);
   else if (vec) KDA_CHAIN_LAUNCH(true, kStateBf16);

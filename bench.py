@@ -61,8 +61,8 @@ _VER_SHA = ("6b5678d54deedbcc8fd3c7d8dea5d0606841d637a9a3c0a9f333ceec8a7ff1e5",)
 _PF_SRC = ("gated_delta_rule_step_amd/csrc/kda_prefill.hip",
            "gated_delta_rule_step_amd/csrc/kda_prefill_split.hip",
            "gated_delta_rule_step_amd/csrc/kda_launch.h") + _DEC_SRC[1:]
-_PF_SHA = ("d6dcc29233140d82069cadfd49c366d66fec4984b4a4fb29cb1dc614d2beae30",
-           "7ed314bbe81927c13096a85d78a0d1b52dc5a77399d84ed3928b223cf0d88f51",
+_PF_SHA = ("c15ff32ad2c76e94ffed06bc44b615ffca296dab0f3fe35f4712ccc00384cdc6",
+           "35ceb19282cf1250c814c505e17179d704db80898ab955a283e45d10e93326cc",
            "f0d19f52b61dfbe88a4f7021b78ca69e8965e900fcdf2a3b68436948e8179958") + _DEC_SHA[1:]
 
 
@@ -78,10 +78,10 @@ COUNTED_TRAFFIC = {
     "verify T=4 B=512 fm=13 100% fold": _ct(_VER_SRC, _VER_SHA, 143792.086, 227328.0),
     "verify T=8 B=512 W32 fm=25 hist~U{0..24}": _ct(_VER_SRC, _VER_SHA, 160186.586, 124416.0),
     # the fused kernel (H = 64), or the preparation + chain kernels summed (H = 12)
-    "prefill 4 docs (3840, 3776, 3200, 3072) H=64": _ct(_PF_SRC, _PF_SHA, 455751.078, 230400.0),
-    "prefill 4 docs (3840, 3776, 3200, 3072) H=12": _ct(_PF_SRC, _PF_SHA, 346266.547, 345588.516),
-    "prefill 14-doc mix, 16384 tokens H=64": _ct(_PF_SRC, _PF_SHA, 547239.906, 290816.0),
-    "prefill 14-doc mix, 16384 tokens H=12": _ct(_PF_SRC, _PF_SHA, 415622.891, 414562.633),
+    "prefill 4 docs (3840, 3776, 3200, 3072) H=64": _ct(_PF_SRC, _PF_SHA, 455747.328, 230400.0),
+    "prefill 4 docs (3840, 3776, 3200, 3072) H=12": _ct(_PF_SRC, _PF_SHA, 250622.047, 360312.883),
+    "prefill 14-doc mix, 16384 tokens H=64": _ct(_PF_SRC, _PF_SHA, 547233.297, 290816.0),
+    "prefill 14-doc mix, 16384 tokens H=12": _ct(_PF_SRC, _PF_SHA, 428745.719, 423618.984),
 }
 
 

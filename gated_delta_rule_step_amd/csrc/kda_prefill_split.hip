@@ -353,8 +353,8 @@ __global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillParams p) {
       }
       sq = row16_sum(sq);
       sk = row16_sum(sk);
-      const float rq = 1.0f / sqrtf(sq + 1e-6f);
-      const float rk = 1.0f / sqrtf(sk + 1e-6f);
+      const float rq = __builtin_amdgcn_rsqf(sq + 1e-6f);  // hardware 1/sqrt
+      const float rk = __builtin_amdgcn_rsqf(sk + 1e-6f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         s.qh[tt * RS + c0 + e] = q[e] * rq;
@@ -462,8 +462,9 @@ __global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillParams p) {
     // bf16 hi / lo; threads 128..255: U0 (value channel v).
     {
       const int cc = tid & 127;
-      // Right-looking: once x_j is known it is taken off every later row's
-      // remainder; each row still accumulates its terms in the order j = 0, 1, ...
+      // Row by row: x_r -= A[r][j] x_j in the order j = 0, 1, ..., r - 1, then
+      // x_r *= beta_r; each row of A is read as 16-byte pieces (one broadcast
+      // LDS read per four terms).
       float x[C];
       if (tid < 128) {
 #pragma unroll
@@ -473,10 +474,15 @@ __global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillParams p) {
         for (int r = 0; r < C; ++r) x[r] = bf1(s.vv[r * VLD + cc]);
       }
 #pragma unroll
-      for (int jj = 0; jj < C; ++jj) {
-        x[jj] *= s.beta[jj];
+      for (int r = 0; r < C; ++r) {
 #pragma unroll
-        for (int r = jj + 1; r < C; ++r) x[r] = fmaf(-s.am[r * C + jj], x[jj], x[r]);
+        for (int j4 = 0; j4 < r; j4 += 4) {
+          const f32x4 a4 = *reinterpret_cast<const f32x4*>(s.am + r * C + j4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j4 + e < r) x[r] = fmaf(-a4[e], x[j4 + e], x[r]);
+        }
+        x[r] *= s.beta[r];
       }
       if (tid < 128) {
         const float em = s.em[cc];
@@ -599,7 +605,7 @@ __global__ __launch_bounds__(kThreads) void handoff_kernel(PrefillParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) sk = fmaf(k[e], k[e], sk);
     sk = row16_sum(sk);
-    const float rk = 1.0f / sqrtf(sk + 1e-6f);
+    const float rk = __builtin_amdgcn_rsqf(sk + 1e-6f);  // as the preparation computes it
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       kh[tt][c0 + e] = k[e] * rk;

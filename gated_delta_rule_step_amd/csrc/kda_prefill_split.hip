@@ -284,9 +284,12 @@ __device__ int find_doc(const int32_t* cu, int n_docs, int64_t sigma, int tid) {
 // ---------------------------------------------------------------------------
 // Preparation: one 256-thread workgroup per (chunk slot, group of up to
 // kPrepHeads heads). Everything of the chunk that does not depend on the
-// state, written to the chunk record of each head; the next head's token
-// inputs are loaded while the current head is processed.
-constexpr int kPrepHeads = 4;
+// state, written to the chunk record of each head; with several heads per
+// workgroup the next head's token inputs are loaded while the current head is
+// processed. One head per workgroup measured fastest (more, shorter
+// workgroups fill the CUs more evenly: set A at H = 12, 329 us against 339 us
+// with four heads and 330 us with two).
+constexpr int kPrepHeads = 1;
 
 // GK, the gate kind: kGatePrecomputed clear = raw gate logits, set = the
 // log-decay itself; kGatePerHead set = one gate value per head.

@@ -651,8 +651,58 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p, int hm) {
   }
   __syncthreads();
 
-  // ---- 5b. C[m, j] = X_m . D_j (history correction); group grp owns row m.
-  if (hist > 0) {
+  // ---- 5b. C[m, j] = X_m . D_j (history correction), rows m < 2T, entries j < hist.
+  // Deep rings, from 8 entries on: one MFMA product per 16 entries (wave w
+  // takes entries 16 w ..): A = the X rows (lane row m = lane % 16, zero from
+  // 2T on), B = the D_j rows (zero from hist on), four 32-channel steps, both
+  // split into bf16 hi and lo, three terms. Otherwise one 16-lane group per
+  // row m and a dot product per entry (in the 16-row-window instance the
+  // product's registers would cost occupancy on every call).
+  if (DEEP && hist >= 8) {
+    if (16 * wave < hist) {
+      const int m = fv, j = 16 * wave + fv;
+      const float* xrow = m < T ? s.ka + m * XS : s.qa + (m - T) * XS;
+      const float* drow = s.dh + j * kHistF;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      f32x4 c0 = z, c1 = z, c2 = z;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int k0 = 32 * st + fk;
+        f32x4 x0 = z, x1 = z, d0 = z, d1 = z;
+        if (m < 2 * T) {
+          x0 = *reinterpret_cast<const f32x4*>(xrow + k0);
+          x1 = *reinterpret_cast<const f32x4*>(xrow + k0 + 4);
+        }
+        if (j < hist) {
+          d0 = *reinterpret_cast<const f32x4*>(drow + k0);
+          d1 = *reinterpret_cast<const f32x4*>(drow + k0 + 4);
+        }
+        u32x4 xh, xl, dhi, dlo;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          xh[i] = pack_bf16x2(x0[2 * i], x0[2 * i + 1]);
+          xh[2 + i] = pack_bf16x2(x1[2 * i], x1[2 * i + 1]);
+          xl[i] = pack_bf16x2(x0[2 * i] - bf_lo(xh[i]), x0[2 * i + 1] - bf_hi(xh[i]));
+          xl[2 + i] = pack_bf16x2(x1[2 * i] - bf_lo(xh[2 + i]), x1[2 * i + 1] - bf_hi(xh[2 + i]));
+          dhi[i] = pack_bf16x2(d0[2 * i], d0[2 * i + 1]);
+          dhi[2 + i] = pack_bf16x2(d1[2 * i], d1[2 * i + 1]);
+          dlo[i] = pack_bf16x2(d0[2 * i] - bf_lo(dhi[i]), d0[2 * i + 1] - bf_hi(dhi[i]));
+          dlo[2 + i] = pack_bf16x2(d1[2 * i] - bf_lo(dhi[2 + i]), d1[2 * i + 1] - bf_hi(dhi[2 + i]));
+        }
+        const bf16x8 axh = __builtin_bit_cast(bf16x8, xh), axl = __builtin_bit_cast(bf16x8, xl);
+        const bf16x8 bdh = __builtin_bit_cast(bf16x8, dhi), bdl = __builtin_bit_cast(bf16x8, dlo);
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(axh, bdh, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(axh, bdl, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(axl, bdh, c2, 0, 0, 0);
+      }
+      const f32x4 c = c0 + (c1 + c2);  // rows 4 (lane / 16) + i, entry 16 wave + lane % 16
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int mr = 4 * (lane >> 4) + i;
+        if (mr < 2 * T && j < hist) s.cm[mr * hm + j] = c[i];
+      }
+    }
+  } else if (hist > 0) {
     const int grp = tid >> 4;
     if (grp < 2 * T) {
       const float* xrow = grp < T ? s.ka + grp * XS : s.qa + (grp - T) * XS;

@@ -57,12 +57,12 @@ _DEC_SHA = ("84c78a8d6498618efb1a4d7b64592ce8060e9db6d865bb021275a99a6dec8ae7",
             "2fe55975814488bcd43f46e6ffd9805dc1139ce860b017fe31783558c0e3b22e",
             "90c1cd82031d88b6ff81e4330b9f109c95bf3e9b0f031a3208f41099dfb3fb5f")
 _VER_SRC = ("gated_delta_rule_step_amd/csrc/kda_verify.hip",) + _DEC_SRC[1:]
-_VER_SHA = ("6b5678d54deedbcc8fd3c7d8dea5d0606841d637a9a3c0a9f333ceec8a7ff1e5",) + _DEC_SHA[1:]
+_VER_SHA = ("3e6ca5522e82c662fc18e380962fbbb2c1895663a619f60314014b129b10ac5b",) + _DEC_SHA[1:]
 _PF_SRC = ("gated_delta_rule_step_amd/csrc/kda_prefill.hip",
            "gated_delta_rule_step_amd/csrc/kda_prefill_split.hip",
            "gated_delta_rule_step_amd/csrc/kda_launch.h") + _DEC_SRC[1:]
 _PF_SHA = ("c15ff32ad2c76e94ffed06bc44b615ffca296dab0f3fe35f4712ccc00384cdc6",
-           "35ceb19282cf1250c814c505e17179d704db80898ab955a283e45d10e93326cc",
+           "595c89c04b359ac1cf45bb99010f2fabda48f35d47f7d445a4fdbac3eb279e31",
            "f0d19f52b61dfbe88a4f7021b78ca69e8965e900fcdf2a3b68436948e8179958") + _DEC_SHA[1:]
 
 
@@ -72,16 +72,16 @@ def _ct(src, sha, fetch_kib, write_kib):
 
 
 COUNTED_TRAFFIC = {
-    "decode B=512": _ct(_DEC_SRC, _DEC_SHA, 96508.461, 188160.848),
-    "verify T=8 B=512 bare": _ct(_VER_SRC, _VER_SHA, 123878.797, 61440.0),
-    "verify T=8 B=512 fm=9 100% fold": _ct(_VER_SRC, _VER_SHA, 138502.297, 258048.031),
-    "verify T=4 B=512 fm=13 100% fold": _ct(_VER_SRC, _VER_SHA, 143792.086, 227328.0),
-    "verify T=8 B=512 W32 fm=25 hist~U{0..24}": _ct(_VER_SRC, _VER_SHA, 160186.586, 124416.0),
+    "decode B=512": _ct(_DEC_SRC, _DEC_SHA, 96508.344, 188160.961),
+    "verify T=8 B=512 bare": _ct(_VER_SRC, _VER_SHA, 123843.391, 61440.0),
+    "verify T=8 B=512 fm=9 100% fold": _ct(_VER_SRC, _VER_SHA, 138465.023, 258048.188),
+    "verify T=4 B=512 fm=13 100% fold": _ct(_VER_SRC, _VER_SHA, 143754.445, 227328.0),
+    "verify T=8 B=512 W32 fm=25 hist~U{0..24}": _ct(_VER_SRC, _VER_SHA, 160222.203, 124416.0),
     # the fused kernel (H = 64), or the preparation + chain kernels summed (H = 12)
-    "prefill 4 docs (3840, 3776, 3200, 3072) H=64": _ct(_PF_SRC, _PF_SHA, 455747.328, 230400.0),
-    "prefill 4 docs (3840, 3776, 3200, 3072) H=12": _ct(_PF_SRC, _PF_SHA, 250622.047, 360312.883),
-    "prefill 14-doc mix, 16384 tokens H=64": _ct(_PF_SRC, _PF_SHA, 547233.297, 290816.0),
-    "prefill 14-doc mix, 16384 tokens H=12": _ct(_PF_SRC, _PF_SHA, 428745.719, 423618.984),
+    "prefill 4 docs (3840, 3776, 3200, 3072) H=64": _ct(_PF_SRC, _PF_SHA, 455748.047, 230400.0),
+    "prefill 4 docs (3840, 3776, 3200, 3072) H=12": _ct(_PF_SRC, _PF_SHA, 246238.797, 360245.961),
+    "prefill 14-doc mix, 16384 tokens H=64": _ct(_PF_SRC, _PF_SHA, 547232.453, 290816.0),
+    "prefill 14-doc mix, 16384 tokens H=12": _ct(_PF_SRC, _PF_SHA, 429454.453, 424229.984),
 }
 
 

@@ -62,7 +62,7 @@ _PF_SRC = ("gated_delta_rule_step_amd/csrc/kda_prefill.hip",
            "gated_delta_rule_step_amd/csrc/kda_prefill_split.hip",
            "gated_delta_rule_step_amd/csrc/kda_launch.h") + _DEC_SRC[1:]
 _PF_SHA = ("c15ff32ad2c76e94ffed06bc44b615ffca296dab0f3fe35f4712ccc00384cdc6",
-           "595c89c04b359ac1cf45bb99010f2fabda48f35d47f7d445a4fdbac3eb279e31",
+           "2dc90c9dcfa9fe0f2dedae2b76fe029b65df6163ee4d25d9484c933fa1407a52",
            "f0d19f52b61dfbe88a4f7021b78ca69e8965e900fcdf2a3b68436948e8179958") + _DEC_SHA[1:]
 
 

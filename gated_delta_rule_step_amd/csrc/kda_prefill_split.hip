@@ -4,8 +4,9 @@
 // joined by a caller-provided workspace. With fewer chains than compute units
 // the chains alone cannot fill the chip, so the state-independent preparation
 // runs first on every CU, and the chain then takes the recurrence alone,
-// split by value channels over two workgroups. (Calls with more chains run
-// the fused kernel of kda_prefill.hip instead.)
+// split by value channels over four workgroups and, within each, by key
+// channels over two waves per value tile. (Calls with more chains run the
+// fused kernel of kda_prefill.hip instead.)
 //
 // Operation: "feat(kda): add CuTe DSL recurrent prefill backend" -- packed
 // documents delimited by cu_seqlens, each (document, head) chain runs the
@@ -49,13 +50,14 @@
 //   U0  [vt 8][lane][4 fp32]          U0[4g4 + 0..3][16vt + n16]
 //   P   [lane][4 bf16]                P[n16][4g4 + 0..3]
 //   EG  [128 fp32]                    exp(Gam_c)
-// The chain's state S[v][k] sits in the MFMA accumulator layout: wave w, tile
-// (mt, nt) holds key channels 16mt + 4g4 + i and value channel 32w + 16nt + n16,
-// so the B fragment of v_mfma_f32_16x16x32_bf16 takes its 8 key channels as two
-// runs of 4 from accumulator tiles 2kt and 2kt+1 (the order the W and Q
-// fragments are written in), and U = U0 - W S^T comes out in the accumulator
-// layout, which is the B fragment of v_mfma_f32_16x16x16_bf16 with the chunk's
-// tokens as the contraction.
+// The chain's state S[v][k] sits in the MFMA accumulator layout: the wave of
+// value tile vt and key half kh holds, in tile m, key channels
+// 16 (4 kh + m) + 4g4 + i and value channel 16 vt + n16, so the B fragment of
+// v_mfma_f32_16x16x32_bf16 takes its 8 key channels as two runs of 4 from
+// accumulator tiles 2kt and 2kt+1 (the order the W and Q fragments are written
+// in), and U = U0 - W S^T comes out in the accumulator layout, which is the B
+// fragment of v_mfma_f32_16x16x16_bf16 with the chunk's tokens as the
+// contraction.
 //
 // Chunk slots. Chunk j of document d (first token t0) has slot
 // d + floor(t0 / 16) + j: strictly increasing over (d, j), fewer than

@@ -1024,13 +1024,21 @@ hipError_t launch_prefill_split(const PrefillParams& p, const int32_t* cu_host, 
   }
   // Fewer chains than CUs (always the case on this path): four workgroups per
   // chain (by value channels) of two waves per value tile (by key channels),
-  // one wave per SIMD. Beyond 64 chains two workgroups share a CU.
+  // one wave per SIMD. Each workgroup takes a CU of its own: an unused
+  // dynamic LDS block lifts it past half of the CU's LDS, so that beyond 64
+  // chains the longest chains (dispatched first) do not share their CUs and
+  // the rest follow as CUs free up (the 14-document set at H = 12: 367 us
+  // against 395 us with two workgroups per CU).
   // fp16 and fp8 states run on the vectorised path only (the host requires it)
   if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
   const int64_t groups = (blocks + 7) / 8;  // chains, in groups of 8 (one per XCD)
+  constexpr size_t kChainStaticLds = 2 * kRecBytes + ChainShape<4, 2>::kXchBytes;
+  constexpr size_t kChainPadLds = 81 * 1024 - kChainStaticLds;
+  static_assert(kChainStaticLds < 81 * 1024 && kChainStaticLds + kChainPadLds <= 160 * 1024,
+                "one chain workgroup per CU");
 #define KDA_CHAIN_LAUNCH(V, S)                                                              \
   hipLaunchKernelGGL((chain_kernel<V, S, 4, 2>), dim3(static_cast<unsigned>(groups * 32)), \
-                     dim3(ChainShape<4, 2>::kThreads), 0, stream, p, ord)
+                     dim3(ChainShape<4, 2>::kThreads), kChainPadLds, stream, p, ord)
   if (p.state_fmt == kStateFp16) KDA_CHAIN_LAUNCH(true, kStateFp16);
   else if (p.state_fmt == kStateFp8) KDA_CHAIN_LAUNCH(true, kStateFp8);
   else if (vec) KDA_CHAIN_LAUNCH(true, kStateBf16);

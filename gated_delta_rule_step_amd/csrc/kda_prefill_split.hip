@@ -675,12 +675,22 @@ __global__ __launch_bounds__(kThreads) void handoff_kernel(PrefillParams p) {
 // channels and exchange the partial sums through LDS (one extra barrier per
 // chunk); both then hold the same U and update their own key channels. Fewer
 // key channels per wave halve its MFMA and VALU issue per chunk, which bounds
-// the chain when each SIMD holds one wave. Chunk records move HBM -> registers
-// one chunk ahead of use and registers -> LDS (double buffer) one chunk
-// ahead; each part stages the record's shared operands (W, Q, K~, P,
+// the chain when each SIMD holds one wave. Chunk records move HBM -> LDS
+// directly (global_load_lds, no registers), two chunks ahead of use, into three
+// LDS buffers; each part stages the record's shared operands (W, Q, K~, P,
 // exp(Gam_c)) and only its own U0 tiles. The VS parts of a chain are blocks
 // b, b + 8, ..., so that they run on one XCD (blocks go to the XCDs in turn)
 // and share its L2 copy of the records.
+
+// Workgroup barrier for LDS traffic only (lgkmcnt 0, then s_barrier), so that
+// the record loads stay in flight; their own waits are explicit vmcnt counts.
+__device__ __forceinline__ void lds_barrier_c() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int VS, int KS>
 struct ChainShape {
   static constexpr int kTiles = 8 / VS;                     // value tiles of 16 channels
@@ -691,10 +701,8 @@ struct ChainShape {
   static constexpr int kOwnU0 = kTiles * 64;                // this part's U0 units
   static constexpr int kTail = kRecUnits - kRecP / 16;      // P, exp(Gam_c) units
   static constexpr int kUnits = kShared + kOwnU0 + kTail;   // units staged per chunk
-  static constexpr int kRounds = (kUnits + kThreads - 1) / kThreads;
   // partial sums exchanged per tile: W S and (e^Gam q) S of both halves
   static constexpr int kXchBytes = KS == 1 ? 16 : kTiles * 4 * 64 * 16;
-  static_assert(kUnits > (kRounds - 1) * kThreads, "every round has work");
   static_assert(KS == 1 || KS == 2, "key split");
   // record unit of staged unit i (< kUnits) of part `part`
   __device__ static int unit(int i, int part) {
@@ -713,9 +721,14 @@ __global__ __launch_bounds__((ChainShape<VS, KS>::kThreads)) void chain_kernel(P
                                                                               DocOrder ord) {
   using Shape = ChainShape<VS, KS>;
   constexpr int kChainThreads = Shape::kThreads;
-  constexpr int kChainRounds = Shape::kRounds;
   constexpr int kAcc = Shape::kAcc;
-  __shared__ __align__(16) uint8_t rbuf[2][kRecBytes];
+  // Three record buffers, declared apart: every access below names its buffer
+  // statically (the chunk loop is unrolled by three), so the compiler can tell
+  // a read of one buffer from the loads in flight into another and adds no
+  // wait of its own for them.
+  __shared__ __align__(16) uint8_t rb0[kRecBytes];
+  __shared__ __align__(16) uint8_t rb1[kRecBytes];
+  __shared__ __align__(16) uint8_t rb2[kRecBytes];
   __shared__ __align__(16) uint8_t xch[Shape::kXchBytes];
   // block -> (chain, part): chain c's parts are blocks (c / 8 * VS + part) * 8 + c % 8
   const int bid = int(blockIdx.x);
@@ -773,29 +786,28 @@ __global__ __launch_bounds__((ChainShape<VS, KS>::kThreads)) void chain_kernel(P
   auto rec_of = [&](int ch) {
     return reinterpret_cast<const u32x4*>(ws + ((sigma0 + ch) * p.H + h) * int64_t(kRecBytes));
   };
-  // Thread tid moves staged units tid + kChainThreads rd (to the record's
-  // own offsets in LDS); the units past the staged set in the last round load
-  // a staged unit again (a fixed load count per chunk) and are not stored.
-  u32x4 pre[kChainRounds];
-  auto load_rec = [&](int ch) {
+  // Records go HBM -> LDS directly: a global_load_lds moves 64 consecutive
+  // 16-byte units (one per lane) to consecutive LDS. The staged set is
+  // kUnits / 64 such runs; wave w issues runs w, w + kWaves, ... (kDmaPerWave
+  // per wave, the last run issued again by the waves that run out, with the
+  // same bytes to the same place), so every wave issues the same count and the
+  // waits below are fixed counts. Record indices past the last chunk are
+  // clamped to it, for the same reason.
+  constexpr int kRuns = Shape::kUnits / 64;
+  constexpr int kDmaPerWave = (kRuns + Shape::kWaves - 1) / Shape::kWaves;
+  static_assert(Shape::kUnits % 64 == 0 && Shape::kShared % 64 == 0 && Shape::kOwnU0 % 64 == 0,
+                "whole runs");
+  auto dma_rec = [&](int ch, uint8_t* dst) {
     const u32x4* r = rec_of(ch);
 #pragma unroll
-    for (int rd = 0; rd < kChainRounds; ++rd) {
-      const int i = tid + kChainThreads * rd;
-      pre[rd] = __builtin_nontemporal_load(
-          r + Shape::unit(i < Shape::kUnits ? i : i - Shape::kUnits, part));
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const int run = min(wave + Shape::kWaves * i, kRuns - 1);
+      const int u = Shape::unit(64 * run, part);
+      __builtin_amdgcn_global_load_lds(r + u + lane, dst + 16 * u, 16, 0, 0);
     }
   };
-  auto store_rec = [&](int b) {
-    u32x4* d = reinterpret_cast<u32x4*>(&rbuf[b][0]);
-#pragma unroll
-    for (int rd = 0; rd < kChainRounds; ++rd) {
-      const int i = tid + kChainThreads * rd;
-      if (rd < kChainRounds - 1 || i < Shape::kUnits) d[Shape::unit(i, part)] = pre[rd];
-    }
-  };
-
-  load_rec(0);
+  dma_rec(0, rb0);
+  dma_rec(min(1, nchunks - 1), rb1);
 
   // ---- initial state into the accumulator layout: this wave's state tiles
   // mt = kAcc kh + m (key channels 16 mt ..), all loads issued before any wait
@@ -820,18 +832,17 @@ __global__ __launch_bounds__((ChainShape<VS, KS>::kThreads)) void chain_kernel(P
 #pragma unroll
     for (int m = 0; m < kAcc; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  store_rec(0);
-  load_rec(min(1, nchunks - 1));
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: records 0, 1 and the state
+  lds_barrier_c();
 
   // the exchanged partial sums of this wave's tile: W S [half][lane], then (e^Gam q) S
   f32x4* xw = reinterpret_cast<f32x4*>(xch) + tile * 4 * 64;
   const int ots32 = static_cast<int>(p.out_tok_stride);  // host-checked to fit a buffer range
   f32x4 u_last = {0.f, 0.f, 0.f, 0.f};  // U of the last chunk (rows 4 g4 + i)
-  for (int ch = 0; ch < nchunks; ++ch) {
+  auto step = [&](const int ch, const uint8_t* R, uint8_t* D2) __attribute__((always_inline)) {
+    dma_rec(min(ch + 2, nchunks - 1), D2);  // into the buffer read by chunk ch - 1
     const int64_t tc0 = t0 + int64_t(ch) * C;
     const int c = int(min<int64_t>(C, len - int64_t(ch) * C));
-    const uint8_t* R = &rbuf[ch & 1][0];
 
     // Output rows of this chunk as a buffer range of exactly c rows: a store
     // to a padded row (r >= c) is out of range and discarded, so the number
@@ -867,7 +878,7 @@ __global__ __launch_bounds__((ChainShape<VS, KS>::kThreads)) void chain_kernel(P
       // totals are the same in both waves (addition commutes exactly)
       xw[kh * 64 + lane] = ws_;
       xw[(2 + kh) * 64 + lane] = yq;
-      __syncthreads();
+      lds_barrier_c();
       ws_ += xw[(kh ^ 1) * 64 + lane];
       yq += xw[(2 + (kh ^ 1)) * 64 + lane];
     }
@@ -903,10 +914,10 @@ __global__ __launch_bounds__((ChainShape<VS, KS>::kThreads)) void chain_kernel(P
       a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(klo, uhi, a, 0, 0, 0);
       acc[m] = a;
     }
-    // record ch+1 (its loads were issued a chunk ago) into the other buffer,
-    // last read before the previous barrier; then the loads of record ch+2
-    store_rec((ch + 1) & 1);
-    load_rec(min(ch + 2, nchunks - 1));
+    // record ch + 1 is in LDS: only record ch + 2 (kDmaPerWave loads) and this
+    // chunk's output stores (4 / KS) were issued after it
+    static_assert(kDmaPerWave + 4 / KS <= 15, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (kDmaPerWave + 4 / KS));
     // intermediate checkpoint after this chunk, after the record loads
     if (p.ckpt && (ch + 1) % ckpt_every == 0 && int64_t(ch + 1) * C <= kept) {
       const int64_t row = ckpt_row0 + (ch + 1) / ckpt_every - 1;
@@ -918,7 +929,15 @@ __global__ __launch_bounds__((ChainShape<VS, KS>::kThreads)) void chain_kernel(P
       }
     }
     // this chunk's buffer and exchange slots are read; the next ones are written
-    __syncthreads();
+    lds_barrier_c();
+  };
+  for (int ch = 0;;) {
+    step(ch, rb0, rb2);
+    if (++ch >= nchunks) break;
+    step(ch, rb1, rb0);
+    if (++ch >= nchunks) break;
+    step(ch, rb2, rb1);
+    if (++ch >= nchunks) break;
   }
 
   if (tail > 0 && kh == 0) {  // hand-off: ring rows of the tail tokens receive u (bf16)
@@ -1024,21 +1043,19 @@ hipError_t launch_prefill_split(const PrefillParams& p, const int32_t* cu_host, 
   }
   // Fewer chains than CUs (always the case on this path): four workgroups per
   // chain (by value channels) of two waves per value tile (by key channels),
-  // one wave per SIMD. Each workgroup takes a CU of its own: an unused
-  // dynamic LDS block lifts it past half of the CU's LDS, so that beyond 64
-  // chains the longest chains (dispatched first) do not share their CUs and
-  // the rest follow as CUs free up (the 14-document set at H = 12: 367 us
-  // against 395 us with two workgroups per CU).
+  // one wave per SIMD. Each workgroup takes a CU of its own: its three record
+  // buffers take more than half of the CU's LDS, so that beyond 64 chains the
+  // longest chains (dispatched first) do not share their CUs and the rest
+  // follow as CUs free up (with two record buffers, one workgroup per CU was
+  // worth 395 -> 367 us on the 14-document set at H = 12).
   // fp16 and fp8 states run on the vectorised path only (the host requires it)
   if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
   const int64_t groups = (blocks + 7) / 8;  // chains, in groups of 8 (one per XCD)
-  constexpr size_t kChainStaticLds = 2 * kRecBytes + ChainShape<4, 2>::kXchBytes;
-  constexpr size_t kChainPadLds = 81 * 1024 - kChainStaticLds;
-  static_assert(kChainStaticLds < 81 * 1024 && kChainStaticLds + kChainPadLds <= 160 * 1024,
-                "one chain workgroup per CU");
+  constexpr size_t kChainLds = 3 * kRecBytes + ChainShape<4, 2>::kXchBytes;
+  static_assert(kChainLds > 80 * 1024 && kChainLds <= 160 * 1024, "one chain workgroup per CU");
 #define KDA_CHAIN_LAUNCH(V, S)                                                              \
   hipLaunchKernelGGL((chain_kernel<V, S, 4, 2>), dim3(static_cast<unsigned>(groups * 32)), \
-                     dim3(ChainShape<4, 2>::kThreads), kChainPadLds, stream, p, ord)
+                     dim3(ChainShape<4, 2>::kThreads), 0, stream, p, ord)
   if (p.state_fmt == kStateFp16) KDA_CHAIN_LAUNCH(true, kStateFp16);
   else if (p.state_fmt == kStateFp8) KDA_CHAIN_LAUNCH(true, kStateFp8);
   else if (vec) KDA_CHAIN_LAUNCH(true, kStateBf16);

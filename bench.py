@@ -62,7 +62,7 @@ _PF_SRC = ("gated_delta_rule_step_amd/csrc/kda_prefill.hip",
            "gated_delta_rule_step_amd/csrc/kda_prefill_split.hip",
            "gated_delta_rule_step_amd/csrc/kda_launch.h") + _DEC_SRC[1:]
 _PF_SHA = ("c15ff32ad2c76e94ffed06bc44b615ffca296dab0f3fe35f4712ccc00384cdc6",
-           "d13f42b923ca987efaf6786bbf57eefbeee8869ec714c68c616db84521649da2",
+           "56d23d48060d6748b978f99b8377d85a35c1744186d8f7bb1ec2bc1b3669faaa",
            "f0d19f52b61dfbe88a4f7021b78ca69e8965e900fcdf2a3b68436948e8179958") + _DEC_SHA[1:]
 
 
@@ -78,10 +78,10 @@ COUNTED_TRAFFIC = {
     "verify T=4 B=512 fm=13 100% fold": _ct(_VER_SRC, _VER_SHA, 143754.445, 227328.0),
     "verify T=8 B=512 W32 fm=25 hist~U{0..24}": _ct(_VER_SRC, _VER_SHA, 160222.203, 124416.0),
     # the fused kernel (H = 64), or the preparation + chain kernels summed (H = 12)
-    "prefill 4 docs (3840, 3776, 3200, 3072) H=64": _ct(_PF_SRC, _PF_SHA, 455751.047, 230400.0),
-    "prefill 4 docs (3840, 3776, 3200, 3072) H=12": _ct(_PF_SRC, _PF_SHA, 247280.812, 359825.219),
-    "prefill 14-doc mix, 16384 tokens H=64": _ct(_PF_SRC, _PF_SHA, 547234.219, 290816.031),
-    "prefill 14-doc mix, 16384 tokens H=12": _ct(_PF_SRC, _PF_SHA, 301441.672, 428194.711),
+    "prefill 4 docs (3840, 3776, 3200, 3072) H=64": _ct(_PF_SRC, _PF_SHA, 455747.391, 230400.0),
+    "prefill 4 docs (3840, 3776, 3200, 3072) H=12": _ct(_PF_SRC, _PF_SHA, 235868.531, 357119.508),
+    "prefill 14-doc mix, 16384 tokens H=64": _ct(_PF_SRC, _PF_SHA, 547233.688, 290816.0),
+    "prefill 14-doc mix, 16384 tokens H=12": _ct(_PF_SRC, _PF_SHA, 282825.203, 423161.594),
 }
 
 

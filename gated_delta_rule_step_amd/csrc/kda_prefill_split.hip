@@ -797,17 +797,19 @@ __global__ __launch_bounds__((ChainShape<VS, KS>::kThreads)) void chain_kernel(P
   constexpr int kDmaPerWave = (kRuns + Shape::kWaves - 1) / Shape::kWaves;
   static_assert(Shape::kUnits % 64 == 0 && Shape::kShared % 64 == 0 && Shape::kOwnU0 % 64 == 0,
                 "whole runs");
-  auto dma_rec = [&](int ch, uint8_t* dst) {
+  auto dma_runs = [&](int ch, uint8_t* dst, int i0, int i1) {
     const u32x4* r = rec_of(ch);
 #pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int run = min(wave + Shape::kWaves * i, kRuns - 1);
       const int u = Shape::unit(64 * run, part);
       __builtin_amdgcn_global_load_lds(r + u + lane, dst + 16 * u, 16, 0, 0);
     }
   };
-  dma_rec(0, rb0);
-  dma_rec(min(1, nchunks - 1), rb1);
+  static_assert(kDmaPerWave % 3 == 0, "three groups of loads per chunk");
+  constexpr int kDma1 = kDmaPerWave / 3, kDma2 = 2 * kDmaPerWave / 3;
+  dma_runs(0, rb0, 0, kDmaPerWave);
+  dma_runs(min(1, nchunks - 1), rb1, 0, kDmaPerWave);
 
   // ---- initial state into the accumulator layout: this wave's state tiles
   // mt = kAcc kh + m (key channels 16 mt ..), all loads issued before any wait
@@ -840,7 +842,11 @@ __global__ __launch_bounds__((ChainShape<VS, KS>::kThreads)) void chain_kernel(P
   const int ots32 = static_cast<int>(p.out_tok_stride);  // host-checked to fit a buffer range
   f32x4 u_last = {0.f, 0.f, 0.f, 0.f};  // U of the last chunk (rows 4 g4 + i)
   auto step = [&](const int ch, const uint8_t* R, uint8_t* D2) __attribute__((always_inline)) {
-    dma_rec(min(ch + 2, nchunks - 1), D2);  // into the buffer read by chunk ch - 1
+    // Record ch + 2 goes into the buffer read by chunk ch - 1, in three groups
+    // spread over the chunk: issued back to back, the loads held up the
+    // wave's own instructions (292 against 309 us at set A, H = 12).
+    const int chn = min(ch + 2, nchunks - 1);
+    dma_runs(chn, D2, 0, kDma1);
     const int64_t tc0 = t0 + int64_t(ch) * C;
     const int c = int(min<int64_t>(C, len - int64_t(ch) * C));
 
@@ -879,6 +885,7 @@ __global__ __launch_bounds__((ChainShape<VS, KS>::kThreads)) void chain_kernel(P
       xw[kh * 64 + lane] = ws_;
       xw[(2 + kh) * 64 + lane] = yq;
       lds_barrier_c();
+      dma_runs(chn, D2, kDma1, kDma2);
       ws_ += xw[(kh ^ 1) * 64 + lane];
       yq += xw[(2 + (kh ^ 1)) * 64 + lane];
     }
@@ -914,6 +921,7 @@ __global__ __launch_bounds__((ChainShape<VS, KS>::kThreads)) void chain_kernel(P
       a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(klo, uhi, a, 0, 0, 0);
       acc[m] = a;
     }
+    dma_runs(chn, D2, kDma2, kDmaPerWave);
     // record ch + 1 is in LDS: only record ch + 2 (kDmaPerWave loads) and this
     // chunk's output stores (4 / KS) were issued after it
     static_assert(kDmaPerWave + 4 / KS <= 15, "vmcnt field");

@@ -62,7 +62,7 @@ _PF_SRC = ("gated_delta_rule_step_amd/csrc/kda_prefill.hip",
            "gated_delta_rule_step_amd/csrc/kda_prefill_split.hip",
            "gated_delta_rule_step_amd/csrc/kda_launch.h") + _DEC_SRC[1:]
 _PF_SHA = ("c15ff32ad2c76e94ffed06bc44b615ffca296dab0f3fe35f4712ccc00384cdc6",
-           "56d23d48060d6748b978f99b8377d85a35c1744186d8f7bb1ec2bc1b3669faaa",
+           "5e7aa29c6b822a0400ee3401e6840a3c44a1d957ed360c4688ee6b02b8b09b9f",
            "f0d19f52b61dfbe88a4f7021b78ca69e8965e900fcdf2a3b68436948e8179958") + _DEC_SHA[1:]
 
 

@@ -289,8 +289,9 @@ __device__ int find_doc(const int32_t* cu, int n_docs, int64_t sigma, int tid) {
 // state, written to the chunk record of each head; with several heads per
 // workgroup the next head's token inputs are loaded while the current head is
 // processed. One head per workgroup measured fastest (more, shorter
-// workgroups fill the CUs more evenly: set A at H = 12, 329 us against 339 us
-// with four heads and 330 us with two).
+// workgroups fill the CUs more evenly: documents of 3840, 3776, 3200 and
+// 3072 tokens at H = 12, 329 us against 339 us with four heads and 330 us
+// with two).
 constexpr int kPrepHeads = 1;
 
 // GK, the gate kind: kGatePrecomputed clear = raw gate logits, set = the
@@ -844,7 +845,8 @@ __global__ __launch_bounds__((ChainShape<VS, KS>::kThreads)) void chain_kernel(P
   auto step = [&](const int ch, const uint8_t* R, uint8_t* D2) __attribute__((always_inline)) {
     // Record ch + 2 goes into the buffer read by chunk ch - 1, in three groups
     // spread over the chunk: issued back to back, the loads held up the
-    // wave's own instructions (292 against 309 us at set A, H = 12).
+    // wave's own instructions (292 against 309 us for documents of 3840, 3776,
+    // 3200 and 3072 tokens at H = 12).
     const int chn = min(ch + 2, nchunks - 1);
     dma_runs(chn, D2, 0, kDma1);
     const int64_t tc0 = t0 + int64_t(ch) * C;
@@ -1055,7 +1057,7 @@ hipError_t launch_prefill_split(const PrefillParams& p, const int32_t* cu_host, 
   // buffers take more than half of the CU's LDS, so that beyond 64 chains the
   // longest chains (dispatched first) do not share their CUs and the rest
   // follow as CUs free up (with two record buffers, one workgroup per CU was
-  // worth 395 -> 367 us on the 14-document set at H = 12).
+  // worth 395 -> 367 us on a 14-document mix of 16384 tokens at H = 12).
   // fp16 and fp8 states run on the vectorised path only (the host requires it)
   if (p.state_fmt != kStateBf16 && !vec) return hipErrorInvalidValue;
   const int64_t groups = (blocks + 7) / 8;  // chains, in groups of 8 (one per XCD)

@@ -309,6 +309,18 @@ def test_checkpoints_longer_interval(orc, interval, path):
     _ckpt_roundtrip(orc, case, interval, starts, int(counts.sum()))
 
 
+def test_checkpoints_every_chunk_long_docs(orc):
+    """Two-stage form: a checkpoint after every 16 tokens over documents of 20
+    to 40 chunks, so the chain's record loads, output stores and checkpoint
+    stores interleave over many chunks and every position of its unrolled
+    chunk loop."""
+    case = synth.prefill_case((640, 333, 481), H=heads_for("split", 3, 2),
+                              seed=synth.seed_for(4, 2, 23))
+    counts = np.diff(case["cu_seqlens"]) // 16
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
+    _ckpt_roundtrip(orc, case, 16, starts, int(counts.sum()))
+
+
 @pytest.mark.parametrize("docs", ["small", "small-fused", "docs4"])
 def test_fp16_state(orc, docs):
     """fp16 initial and final states (state_dtype 1): ragged documents with
